@@ -1,0 +1,137 @@
+"""Exact value decoders for the KV-cache storage formats (oracle, test-only).
+
+The cache stores keys and values as 16-bit floats (bf16 / fp16), as 32-bit
+floats, or as 8-bit codes (INT8 or FP8).  "KV Cache Engineering for LLM
+Serving", section "The cache formula", fixes two bytes per value for BF16 and
+one for FP8; section 8 "Quantization" describes storing a small code plus a
+scale.  The FP8 flavour here is OCP E4M3 (the "fn" variant: no infinities,
+one NaN pattern per sign), the FP8 format the gfx950 matrix cores consume.
+
+Nothing here rounds except ``e4m3_encode``; every decoder is exact.
+"""
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# bf16 / fp16 / fp32
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits_to_f32(bits):
+    """bf16 bit patterns (uint16) -> exact float32 values.
+
+    A bf16 number is the upper half of an IEEE binary32 number, so placing the
+    16 bits in the high half of a 32-bit word gives the same value exactly.
+    """
+    b = np.asarray(bits).astype(np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f16_bits_to_f32(bits):
+    """IEEE binary16 bit patterns (uint16) -> exact float32 values."""
+    return np.asarray(bits).astype(np.uint16).view(np.float16).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 (OCP "fn" flavour)
+# ---------------------------------------------------------------------------
+
+E4M3_BIAS = 7
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """Value of one FP8-E4M3 code, from the format definition.
+
+    Bit layout S.EEEE.MMM, exponent bias 7.  Exponent field 0 encodes
+    subnormals m * 2^-9; fields 1..15 encode (1 + m/8) * 2^(e-7), except
+    S.1111.111 which is NaN.  There is no infinity, so the largest finite
+    magnitude is 1.75 * 2^8 = 448.
+    """
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        mag = m * 2.0 ** (1 - E4M3_BIAS - 3)
+    else:
+        mag = (1.0 + m / 8.0) * 2.0 ** (e - E4M3_BIAS)
+    return sign * mag
+
+
+# All 256 code values; every finite one is exactly representable in fp32.
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+# Non-negative finite magnitudes, indexed by code 0x00..0x7E (increasing).
+_E4M3_MAGS = E4M3_TABLE[:0x7F].copy()
+
+
+def e4m3_to_f32(codes):
+    """FP8-E4M3 codes (uint8) -> exact float32 values (table lookup)."""
+    c = np.asarray(codes).astype(np.uint8)
+    return E4M3_TABLE[c].astype(np.float32)
+
+
+def e4m3_encode(x):
+    """float32 values -> FP8-E4M3 codes, round to nearest, ties to even.
+
+    Brute force: for each |x| the distance to every one of the 127 finite
+    non-negative magnitudes is computed and the nearest is taken; on an
+    exact tie the candidate whose code integer is even wins (codes are
+    monotonic in magnitude, so a tie is always between neighbours c, c+1 and
+    exactly one is even).  Magnitudes above 448 saturate to 448 (code 0x7E).
+    The sign bit of x is kept, so a negative value that rounds to zero gives
+    0x80.  Distances are taken in float64, which is exact wherever a tie can
+    occur (x and both neighbours lie within a few binades of each other).
+    """
+    xf = np.asarray(x, dtype=np.float32)
+    flat = xf.reshape(-1)
+    if np.isnan(flat).any():
+        raise ValueError("e4m3_encode: NaN input is outside the quantiser's domain")
+    mag = np.abs(flat.astype(np.float64))
+    out = np.empty(flat.shape, dtype=np.uint8)
+    chunk = 1 << 16
+    for lo in range(0, flat.size, chunk):
+        m = mag[lo:lo + chunk]
+        d = np.abs(m[:, None] - _E4M3_MAGS[None, :])          # [n, 127]
+        best = d.min(axis=1, keepdims=True)
+        is_best = d == best
+        # among the (one or two) nearest codes, prefer the even code integer
+        even = (np.arange(0x7F) % 2 == 0)[None, :]
+        pick_even = is_best & even
+        has_even = pick_even.any(axis=1)
+        first_best = is_best.argmax(axis=1)
+        first_even = pick_even.argmax(axis=1)
+        code = np.where(has_even, first_even, first_best).astype(np.uint8)
+        code[m > E4M3_MAX] = 0x7E
+        out[lo:lo + chunk] = code
+    sign = np.signbit(flat)
+    out = out | np.where(sign, np.uint8(0x80), np.uint8(0))
+    return out.reshape(xf.shape)
+
+
+# ---------------------------------------------------------------------------
+# dispatch by storage dtype name
+# ---------------------------------------------------------------------------
+
+def decode(raw, dtype):
+    """Raw stored data -> exact float32 values, for dtype in
+    {"f32", "bf16", "f16", "i8", "fp8e4m3"}.
+
+    ``raw`` holds the storage words: float32 for "f32", uint16 bit patterns
+    for "bf16"/"f16", int8 codes for "i8", uint8 codes for "fp8e4m3".
+    Integer and FP8 codes decode to the code's own value (the scale is
+    applied separately, see ``quant.dequantize``).
+    """
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits_to_f32(raw)
+    if dtype == "f16":
+        return f16_bits_to_f32(raw)
+    if dtype == "i8":
+        return np.asarray(raw).astype(np.int8).astype(np.float32)
+    if dtype == "fp8e4m3":
+        return e4m3_to_f32(raw)
+    raise ValueError(f"unknown dtype {dtype!r}")

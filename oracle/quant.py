@@ -1,0 +1,104 @@
+"""Symmetric absmax KV quantiser (oracle, test-only).
+
+"KV Cache Engineering for LLM Serving", section 8 "Quantization": one scale
+for a group of values, ``scale = max|x| / largest_code`` with
+``largest_code = 2^(bits-1) - 1``; codes are ``x / scale`` rounded half to even
+and clipped to ``[-largest_code, largest_code]``; the restored value is
+``code * scale``.  The page's example uses bits = 4 (codes -7..7); the INT8
+cache uses bits = 8 (largest code 127).  "Chapter 18", section "KV-Cache
+Quantization", lists INT8 storage at one byte per value.
+
+FP8-E4M3 storage follows the same rule with the largest finite E4M3 magnitude
+(448) as the largest code and FP8 round-to-nearest-even in place of integer
+rounding.
+
+Group: one scale per (physical block, KV head) over the ``[block_size, d_k]``
+tile, separately for K and V.
+
+Precision: the page's example runs in float64; here every step is a single
+IEEE float32 operation (absmax is exact, then one fp32 division for the scale,
+one fp32 division per element, one rounding to the code grid), which is what
+a GPU kernel computes.  The page's 4-bit example gives the same codes either
+way.  An all-zero group has scale 0 and all codes 0.
+"""
+
+import numpy as np
+
+from . import codecs
+
+INT8_QMAX = 127
+FP8E4M3_QMAX = 448.0
+
+
+def largest_code(bits):
+    """``2^(bits-1) - 1``: 7 for 4-bit, 127 for 8-bit codes."""
+    return 2 ** (bits - 1) - 1
+
+
+def absmax_scale(x, qmax):
+    """fp32(max|x| / qmax) for one group (x float32)."""
+    a = np.float32(np.max(np.abs(np.asarray(x, dtype=np.float32)))) if np.size(x) else np.float32(0)
+    return np.float32(a / np.float32(qmax))
+
+
+def quantize_int(x, bits):
+    """Integer codes and scale for one group (float32 arithmetic).
+
+    Returns (codes int array, scale float32).  Half-to-even rounding is
+    ``np.rint``.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    qmax = largest_code(bits)
+    sc = absmax_scale(x, qmax)
+    if sc == 0:
+        return np.zeros(x.shape, dtype=np.int32), np.float32(0)
+    y = (x / sc).astype(np.float32)
+    codes = np.clip(np.rint(y), -qmax, qmax).astype(np.int32)
+    return codes, sc
+
+
+def quantize_fp8(x):
+    """FP8-E4M3 codes and scale for one group (float32 arithmetic)."""
+    x = np.asarray(x, dtype=np.float32)
+    sc = absmax_scale(x, FP8E4M3_QMAX)
+    if sc == 0:
+        return np.zeros(x.shape, dtype=np.uint8), np.float32(0)
+    y = (x / sc).astype(np.float32)
+    return codecs.e4m3_encode(y), sc
+
+
+def dequantize(code_values, scale):
+    """Restored value ``fp32(code * scale)``: one float32 multiply, rounded to
+    nearest even.  ``code_values`` are the codes' own values (float32)."""
+    return (np.asarray(code_values, dtype=np.float32) * np.asarray(scale, dtype=np.float32)).astype(np.float32)
+
+
+def quantize_cache_blocks(cache_vals, code_dtype, block_ids=None):
+    """Quantise whole blocks of a decoded float32 cache.
+
+    ``cache_vals``: [NB, BS, Hkv, D] float32 values.  For every block in
+    ``block_ids`` (all blocks if None) and every KV head, the
+    ``[BS, D]`` tile gets its own scale.  Returns (codes, scales) where
+    ``codes`` has the cache's shape (int8 for "i8", uint8 for "fp8e4m3") and
+    ``scales`` is [NB, Hkv] float32; blocks not listed keep code 0 / scale 0.
+    """
+    NB, BS, Hkv, D = cache_vals.shape
+    ids = range(NB) if block_ids is None else [int(b) for b in block_ids]
+    if code_dtype == "i8":
+        codes = np.zeros(cache_vals.shape, dtype=np.int8)
+    elif code_dtype == "fp8e4m3":
+        codes = np.zeros(cache_vals.shape, dtype=np.uint8)
+    else:
+        raise ValueError(code_dtype)
+    scales = np.zeros((NB, Hkv), dtype=np.float32)
+    for b in ids:
+        for h in range(Hkv):
+            tile = cache_vals[b, :, h, :]
+            if code_dtype == "i8":
+                c, sc = quantize_int(tile, 8)
+                codes[b, :, h, :] = c.astype(np.int8)
+            else:
+                c, sc = quantize_fp8(tile)
+                codes[b, :, h, :] = c
+            scales[b, h] = sc
+    return codes, scales

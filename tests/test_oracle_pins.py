@@ -1,0 +1,284 @@
+"""Pins the CPU oracle to what the pages print and to closed forms.
+
+Every fixture under tests/golden/ names the page and section it comes from.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, codecs, paging, pool, quant, sizes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# addressing (t13_4 block-table example)
+# --------------------------------------------------------------------------
+
+def test_block_table_example():
+    g = golden("block_table_example.json")
+    bs, L, table = g["block_size"], g["seq_len"], g["block_table"]
+    assert paging.blocks_needed(L, bs) == g["num_blocks_used"]
+    assert L - (g["num_blocks_used"] - 1) * bs == g["tokens_in_last_block"]
+    for logical, (t0, t1) in enumerate(g["logical_token_ranges"]):
+        for t in range(t0, t1 + 1):
+            slot = paging.slot_of(table, t, bs)
+            assert slot // bs == table[logical]
+            assert slot % bs == t - t0
+    # slots of the whole sequence: 112..127, 32..47, 224..231
+    slots = paging.slot_mapping(np.array([table]), [0] * L, list(range(L)), bs)
+    expect = list(range(112, 128)) + list(range(32, 48)) + list(range(224, 232))
+    assert slots.tolist() == expect
+    # waste lives only in the last block, and is below one block
+    assert paging.wasted_slots(L, bs) == bs - g["tokens_in_last_block"]
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 40, 64, 65, 4096, 131072])
+def test_waste_bound(L):
+    assert 0 <= paging.wasted_slots(L, 16) < 16
+
+
+def test_gather_follows_logical_order():
+    """Rows come back in logical order whatever the physical placement."""
+    bs, Hkv, D = 16, 1, 2
+    cache = np.zeros((20, bs, Hkv, D), dtype=np.float32)
+    table = [7, 2, 14]
+    for t in range(40):
+        cache[table[t // bs], t % bs, 0, :] = [t, -t]
+    rows = paging.gather_sequence(cache, table, 40, bs)
+    assert rows[:, 0, 0].tolist() == list(range(40))
+    assert rows[:, 0, 1].tolist() == [-t for t in range(40)]
+
+
+# --------------------------------------------------------------------------
+# GQA mapping and scalar counts (KV Cache Engineering, section 1)
+# --------------------------------------------------------------------------
+
+def test_gqa_mapping_and_scalars():
+    g = golden("gqa_mapping.json")
+    for case in g["cases"]:
+        m = [attention.kv_head_of(h, g["query_heads"], case["kv_heads"]) for h in range(g["query_heads"])]
+        assert m == case["mapping"], case["name"]
+        scalars = sizes.kv_cache_bytes(1, case["kv_heads"], g["head_size"], g["tokens"], 1)
+        assert scalars == case["cached_scalars"], case["name"]
+
+
+# --------------------------------------------------------------------------
+# sizes
+# --------------------------------------------------------------------------
+
+def test_cache_sizes():
+    g = golden("cache_sizes.json")
+    for c in g["cases"]:
+        if c["kind"] == "block":
+            assert sizes.block_bytes(c["block_size"], c["kv_heads"], c["head_dim"], c["bytes"]) == c["expect_bytes"]
+        elif c["kind"] == "sequence":
+            b = sizes.kv_cache_bytes(c["layers"], c["kv_heads"], c["head_dim"], c["tokens"], c["bytes"])
+            assert b == c["expect_gib"] * 2 ** 30, c["source"]
+        elif c["kind"] == "scalars":
+            one = sizes.kv_cache_bytes(c["layers"], c["kv_heads"], c["head_dim"], c["tokens"], 1)
+            assert one == c["expect_scalars"]
+            assert 2 * one == 2048
+        elif c["kind"] == "hybrid_kb":
+            for tokens, kb in c["tokens_to_kb"]:
+                assert sizes.kv_cache_bytes(1, 1, c["width"], tokens, c["bytes"]) // 1024 == kb
+            assert c["width"] * c["width"] * c["bytes"] // 1024 == c["recurrent_kb"]
+    p = g["pool"]
+    per_tok = sizes.kv_bytes_per_token(80, 8, 128, 2)
+    assert per_tok == 320 * 1024
+    assert sizes.kv_bytes_per_token(80, 8, 128, 1) == 160 * 1024
+    for kib, tokens in p["per_token_kib"]:
+        assert sizes.tokens_in_pool(p["pool_bytes"], kib * 1024) == tokens
+
+
+def test_page_13b_example_is_not_consistent():
+    """t13_4 quotes ~800 MB for a 13B FP16 model at 2048 tokens.  With the
+    usual 13B attention shape (40 layers, 40 heads of 128) the formula gives
+    about 1.6 GiB, so that figure is not used as a pin."""
+    b = sizes.kv_cache_bytes(40, 40, 128, 2048, 2)
+    assert b / 2 ** 30 > 1.5
+
+
+# --------------------------------------------------------------------------
+# sliding window and StreamingLLM keep-mask
+# --------------------------------------------------------------------------
+
+def test_sliding_window_example():
+    g = golden("sliding_window.json")
+    for pos, expect in enumerate(g["retained_after_token"]):
+        assert attention.kept_positions(pos + 1, sink=0, window=g["window"]).tolist() == expect
+
+
+def test_streaming_llm_layout():
+    g = golden("streaming_llm_layout.json")
+    L = 131072
+    kept = attention.kept_positions(L, g["sink_tokens"], g["window_tokens"])
+    assert kept.size == g["total_entries"]
+    assert kept[:4].tolist() == [0, 1, 2, 3]
+    assert kept[4:].tolist() == list(range(L - 4092, L))
+    # short sequences keep every token
+    for L in (1, 4, 4095, 4096):
+        assert attention.kept_positions(L, 4, 4092).tolist() == list(range(L))
+    assert attention.kept_positions(4097, 4, 4092).tolist() == [0, 1, 2, 3] + list(range(5, 4097))
+
+
+# --------------------------------------------------------------------------
+# quantiser (KV Cache Engineering, section 8)
+# --------------------------------------------------------------------------
+
+def test_quantizer_4bit_example():
+    g = golden("quant4_example.json")
+    codes, sc = quant.quantize_int(np.array(g["values"]), g["bits"])
+    assert codes.tolist() == g["codes"]
+    restored = quant.dequantize(codes, sc)
+    assert np.round(restored.astype(np.float64), 3).tolist() == g["restored_3dp"]
+    assert len(g["values"]) * 16 == g["payload_bits"][0]
+    assert len(g["values"]) * g["bits"] == g["payload_bits"][1]
+    # the page's float64 arithmetic gives the same codes
+    v = np.array(g["values"])
+    s64 = np.max(np.abs(v)) / 7
+    assert np.clip(np.rint(v / s64), -7, 7).astype(int).tolist() == g["codes"]
+
+
+def test_int8_quantizer_properties():
+    rng = np.random.default_rng(0)
+    for trial in range(50):
+        x = (rng.standard_normal((16, 128)) * rng.uniform(0.01, 100)).astype(np.float32)
+        codes, sc = quant.quantize_int(x, 8)
+        assert sc == np.float32(np.float32(np.abs(x).max()) / np.float32(127))
+        i = np.unravel_index(np.abs(x).argmax(), x.shape)
+        assert abs(int(codes[i])) == 127 and np.sign(codes[i]) == np.sign(x[i])
+        assert codes.min() >= -127 and codes.max() <= 127
+        err = np.abs(x.astype(np.float64) - codes * np.float64(sc))
+        assert (err <= np.float64(sc) * (0.5 + 2 ** -20)).all()
+    codes, sc = quant.quantize_int(np.zeros((16, 128), np.float32), 8)
+    assert sc == 0 and (codes == 0).all()
+
+
+def test_int8_half_even_ties():
+    # x/sc lands exactly on .5: 127 * [0.5/127 ...] -- construct ties directly
+    x = np.array([127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5], dtype=np.float32)
+    codes, sc = quant.quantize_int(x, 8)
+    assert sc == 1.0
+    assert codes.tolist() == [127, 0, 2, 2, 0, -2, -2]
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 codec against torch's float8_e4m3fn (a library routine)
+# --------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch():
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    ours = codecs.E4M3_TABLE.astype(np.float32)
+    nan = np.isnan(t)
+    assert (np.isnan(ours) == nan).all()
+    assert nan.sum() == 2                       # 0x7F and 0xFF only
+    assert (ours[~nan] == t[~nan]).all()
+    assert np.signbit(ours[0x80]) and ours[0x80] == 0
+    assert codecs.E4M3_TABLE[0x7E] == 448.0
+    assert codecs.E4M3_TABLE[0x01] == 2.0 ** -9
+    assert codecs.E4M3_TABLE[0x38] == 1.0
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(1)
+    mags = codecs.E4M3_TABLE[:0x7F]
+    mids = (mags[:-1] + mags[1:]) / 2           # exact ties
+    x = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        rng.standard_normal(20000) * 0.01,
+        mags, -mags, mids, -mids,
+        np.nextafter(mids, 0), np.nextafter(mids, 1000),
+        [0.0, -0.0, 2.0 ** -10, -2.0 ** -10, 2.0 ** -11, 448.0, -448.0, 460.0],
+    ]).astype(np.float32)
+    ours = codecs.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (ours == ref).all(), np.nonzero(ours != ref)[0][:10]
+
+
+def test_e4m3_roundtrip_and_saturation():
+    finite = [c for c in range(256) if not np.isnan(codecs.E4M3_TABLE[c])]
+    vals = codecs.E4M3_TABLE[finite].astype(np.float32)
+    assert codecs.e4m3_encode(vals).tolist() == finite
+    assert codecs.e4m3_encode(np.array([465.0, 1e30, -1e30], np.float32)).tolist() == [0x7E, 0x7E, 0xFE]
+    assert codecs.e4m3_encode(np.array([-1e-30], np.float32)).tolist() == [0x80]
+
+
+def test_fp8_quantizer_properties():
+    rng = np.random.default_rng(2)
+    for trial in range(20):
+        x = (rng.standard_normal((16, 128)) * rng.uniform(0.01, 100)).astype(np.float32)
+        codes, sc = quant.quantize_fp8(x)
+        assert sc == np.float32(np.float32(np.abs(x).max()) / np.float32(448))
+        i = np.unravel_index(np.abs(x).argmax(), x.shape)
+        assert codes[i] & 0x7F == 0x7E
+        restored = codecs.e4m3_to_f32(codes).astype(np.float64) * sc
+        # within half an e4m3 ulp of the scaled value's binade (3 mantissa bits)
+        y = np.abs(x.astype(np.float64) / sc)
+        ulp = np.where(y < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3))
+        assert (np.abs(restored / sc - x / sc) <= ulp / 2 * (1 + 1e-6) + 1e-7).all()
+
+
+def test_bf16_decode_matches_torch():
+    x = torch.randn(10000).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    assert (codecs.bf16_bits_to_f32(bits) == x.float().numpy()).all()
+    y = torch.randn(10000).to(torch.float16)
+    assert (codecs.f16_bits_to_f32(y.view(torch.int16).numpy().view(np.uint16)) == y.float().numpy()).all()
+
+
+# --------------------------------------------------------------------------
+# pool (KV Cache Engineering, section 10; t13_4 copy-on-write)
+# --------------------------------------------------------------------------
+
+def test_paging_free_list_example():
+    g = golden("paging_free_list.json")
+    p = pool.BlockPool(g["num_blocks"])
+    a = p.allocate_sequence(3, 1)
+    b = p.allocate_sequence(2, 1)
+    assert a == g["request_a"] and b == g["request_b"]
+    p.release(a)
+    assert list(p.free_list) == g["free_after_a"]
+    c = p.allocate_sequence(2, 1)
+    assert c == g["request_c"]
+
+
+def test_append_allocates_exactly_at_block_boundary():
+    p = pool.BlockPool(8)
+    table = []
+    for L in range(0, 50):
+        before = len(table)
+        slot, cow = p.append(table, L, 16)
+        assert cow is None
+        assert (len(table) > before) == (L % 16 == 0)
+        assert slot == paging.slot_of(table, L, 16)
+    assert len(table) == 4
+
+
+def test_copy_on_write_only_when_shared():
+    p = pool.BlockPool(10)
+    parent = p.allocate_sequence(40, 16)          # 3 blocks, last partial
+    child = p.fork(parent)
+    assert p.stats()["shared"] == 3
+    slot, cow = p.append(parent, 40, 16)          # shared partial block -> copy
+    assert cow is not None and cow[0] == child[2] and parent[2] == cow[1]
+    assert p.refcount[cow[0]] == 1 and p.refcount[cow[1]] == 1
+    slot2, cow2 = p.append(child, 40, 16)         # no longer shared -> in place
+    assert cow2 is None and slot2 == child[2] * 16 + 8
+    slot3, cow3 = p.append(parent, 41, 16)
+    assert cow3 is None
+    with pytest.raises(ValueError):
+        p.decref(p.free_list[0])
+    q = pool.BlockPool(1)
+    q.alloc()
+    with pytest.raises(pool.PoolExhausted):
+        q.alloc()
