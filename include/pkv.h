@@ -1,0 +1,321 @@
+/*
+ * pkv.h - paged-KV decode attention for AMD MI355X (gfx950): the C ABI.
+ *
+ * The operations follow three pages on KV-cache management:
+ *   [P1] "Chapter 18 - KV-Cache Optimization Strategies" (Language Modelling -
+ *        The Complete Guide), sections "How PagedAttention Works" (with the
+ *        "Physical KV Block" figure), "Prefix Caching", "KV-Cache
+ *        Quantization", "Token Eviction and Pruning".
+ *   [P2] "KV Cache Engineering for LLM Serving, clearly explained", sections
+ *        "The cache formula", 1 "GQA and MQA cache fewer heads", 3 "Sliding
+ *        windows", 8 "Quantization", 10 "Paging".
+ *   [P3] Learning-AI topic t13_4 (KV cache management): block-table and
+ *        copy-on-write paragraphs.
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * Layout.  K and V caches are separate C-contiguous arrays
+ *   k_cache, v_cache : [num_blocks][block_size][num_kv_heads][head_dim]
+ * i.e. one physical block holds [block_size, n_kv_heads, d_k] keys and the
+ * same for values ([P1] "Physical KV Block").  A flat slot number
+ * slot = physical_block * block_size + offset names one row
+ * cache[slot / block_size][slot % block_size][:][:] ([P3] block table).
+ *   query, out      : [num_seqs][num_q_heads][head_dim]
+ *   block_tables    : [num_seqs][max_blocks_per_seq] int32, row s maps logical
+ *                     block i of sequence s to a physical block
+ *   seq_lens        : [num_seqs] int32, tokens of each sequence that attention
+ *                     reads (the newest token included)
+ *   k_scales,
+ *   v_scales        : [num_blocks][num_kv_heads] fp32, one scale per (physical
+ *                     block, KV head), used only when the cache holds codes.
+ * GQA: query head h reads KV head h / (num_q_heads / num_kv_heads) ([P2] s.1).
+ *
+ * Pointers.  Every tensor pointer is a DEVICE pointer unless the argument is
+ * documented as host memory; the caller owns all memory.  No entry point
+ * allocates device memory: scratch comes in through a caller-provided
+ * workspace.  Integers in device arrays are int32.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Every device entry point only enqueues work on it and returns; it
+ * never synchronises.
+ *
+ * Errors.  Every call returns a pkv_status.  Argument errors detectable on the
+ * host return PKV_EINVAL / PKV_EUNSUPPORTED / PKV_EWORKSPACE before anything is
+ * enqueued; a failed launch returns PKV_EHIP.  pkv_last_error() returns a
+ * thread-local message for the last failing call on the calling thread.  No
+ * C++ exception crosses this interface.
+ *
+ * Device-resident contents (block_tables, seq_lens, slot_mapping) are not
+ * inspected on the fast path, because that would need a synchronisation.
+ * Their preconditions:
+ *   0 <= seq_lens[s] <= max_blocks_per_seq * block_size;
+ *   block_tables[s][i] in [0, num_blocks) for i < ceil(seq_lens[s]/block_size)
+ *     (later entries are never read);
+ *   slot_mapping entries unique among non-negative ones and < num_blocks *
+ *     block_size (negative = skip the token).
+ * Kernels clamp out-of-range values so that a bad table never makes them
+ * access memory outside the arrays, but the results are then unspecified.
+ * pkv_validate_tables() checks the preconditions on host copies; setting the
+ * environment variable PKV_CHECK=1 makes the device entry points copy the
+ * arrays to the host, synchronise the stream and check them before launching.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,       /* bad argument (shape, null pointer, value out of range) */
+  PKV_EUNSUPPORTED = 2, /* dtype / head_dim / block_size / group combination not built */
+  PKV_EWORKSPACE = 3,   /* workspace missing or smaller than required */
+  PKV_EHIP = 4,         /* the HIP runtime reported an error */
+  PKV_ENOMEM = 5        /* host block pool: no free block */
+} pkv_status;
+
+/* Storage types of query / cache / output elements. */
+typedef enum pkv_dtype {
+  PKV_F32 = 0,     /* IEEE binary32 */
+  PKV_BF16 = 1,    /* bfloat16 */
+  PKV_F16 = 2,     /* IEEE binary16 */
+  PKV_I8 = 3,      /* signed 8-bit integer code, value = code * scale */
+  PKV_FP8E4M3 = 4  /* OCP FP8 E4M3 ("fn": no inf, NaN = S.1111.111) code, value = code * scale */
+} pkv_dtype;
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char* pkv_last_error(void);
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Number of KV partitions the decode uses per sequence for a given bound on
+ * the sequence length.  partition_size 0 lets the library choose (see
+ * pkv_paged_attn_partition_size); otherwise it must be a positive multiple of
+ * block_size.  Returns 0 on bad arguments.
+ */
+int pkv_paged_attn_num_partitions(int num_seqs, int num_kv_heads, int max_seq_len,
+                                  int block_size, int partition_size);
+
+/*
+ * The partition size (tokens) the library picks when the caller passes 0,
+ * given the launch shape.  One workgroup runs per (sequence, KV head,
+ * partition); the choice keeps the grid large enough to fill 256 compute
+ * units.  A result equal to or above max_seq_len means a single pass (no
+ * partials, no merge).
+ */
+int pkv_paged_attn_partition_size(int num_seqs, int num_kv_heads, int max_seq_len, int block_size);
+
+/*
+ * Bytes of scratch pkv_paged_attn_decode needs: fp32 partial results
+ * (running max m, sum l and unnormalised accumulator acc[head_dim]) per
+ * (sequence, query head, partition).  0 when a single pass suffices.
+ * max_seq_len must be max_blocks_per_seq * block_size of the later call.
+ */
+size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int max_seq_len, int partition_size);
+
+/*
+ * Paged decode attention: one query token per sequence attends over the
+ * sequence's cached keys and values, read block by block through its block
+ * table ([P1] "How PagedAttention Works"; [P3] block table; [P2] s.10: the
+ * blocks are read in logical order).  For every sequence s and query head h:
+ *   out[s][h] = sum_t softmax_t(sm_scale * q[s][h] . K_s[t][kvh]) V_s[t][kvh]
+ * over the kept positions t: all t < seq_lens[s]; with sink_tokens /
+ * window_tokens not both 0, only t < sink_tokens or t >= seq_lens[s] -
+ * window_tokens ([P1] "Token Eviction and Pruning": attention sinks plus a
+ * recent window).  Scores accumulate in fp32; the result is rounded to
+ * q_dtype (nearest even).  A sequence with no kept position gets zeros.
+ *
+ * q_dtype:  PKV_F32, PKV_BF16 or PKV_F16; out has the same dtype.
+ * kv_dtype: equal to q_dtype, or PKV_I8 / PKV_FP8E4M3 with a bf16 or f16
+ *           query (dequantised in registers with k_scales / v_scales,
+ *           [P2] s.8).  k_scales/v_scales are ignored (may be NULL) otherwise.
+ * head_dim: 64 or 128.  block_size: 16.  num_q_heads % num_kv_heads == 0.
+ * partition_size: 0 = library's choice, else a positive multiple of
+ *           block_size.  When the sequence bound max_blocks_per_seq *
+ *           block_size exceeds the partition size, each partition writes
+ *           partial results to the workspace and a merge kernel combines them
+ *           by log-sum-exp.
+ * workspace: device scratch of at least pkv_paged_attn_workspace_bytes(...)
+ *           bytes (may be NULL when that is 0).  Its contents on entry do not
+ *           matter and are undefined on exit.
+ * Calls on the same stream that share a workspace are ordered; calls on
+ * different streams must not share one.
+ */
+pkv_status pkv_paged_attn_decode(
+    void* out, const void* query, int q_dtype,
+    const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* seq_lens, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+    float sm_scale, int partition_size, int sink_tokens, int window_tokens,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two kernels pkv_paged_attn_decode launches, exposed so that each can be
+ * timed on its own.  pkv_paged_attn_partition takes the same arguments and
+ * writes the partials to the workspace (or `out` directly when one partition
+ * covers max_blocks_per_seq * block_size); pkv_paged_attn_merge then combines
+ * them into `out`.  Calling partition then merge on one stream with the same
+ * arguments is exactly pkv_paged_attn_decode.  With a single partition,
+ * pkv_paged_attn_merge does nothing and returns PKV_OK.  For the merge,
+ * max_seq_len is max_blocks_per_seq * block_size of the partition call.
+ */
+pkv_status pkv_paged_attn_partition(
+    void* out, const void* query, int q_dtype,
+    const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* seq_lens, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+    float sm_scale, int partition_size, int sink_tokens, int window_tokens,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+pkv_status pkv_paged_attn_merge(
+    void* out, int q_dtype, const int32_t* seq_lens, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len, int partition_size,
+    const void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Cache writes                                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Slot of each new token: slot_mapping[j] = block_tables[s][p / block_size] *
+ * block_size + p % block_size with s = seq_ids[j] (or j when seq_ids is
+ * NULL) and p = positions[j] ([P3] block table; [P1] new tokens fill the
+ * current block).  Bit-exact integer arithmetic.  A token whose sequence id
+ * is outside [0, num_seqs), whose position is negative or past the table, or
+ * whose table entry is outside [0, num_blocks) gets slot -1.
+ * All arrays are device int32 of length num_tokens (block_tables as above).
+ */
+pkv_status pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* seq_ids,
+                            const int32_t* positions, int num_tokens, int num_seqs,
+                            int block_size, int num_blocks, void* stream);
+
+/*
+ * The slot write ([P1] "How PagedAttention Works"; [P3] new entries are
+ * appended as tokens are generated): for each token j with
+ * slot_mapping[j] >= 0, copies key[j][:][:] into k_cache at that slot and
+ * value[j][:][:] into v_cache.  key/value: [num_tokens][num_kv_heads][head_dim]
+ * of `dtype`, which must equal the caches' dtype (PKV_F32, PKV_BF16, PKV_F16).
+ * A bit copy.  Slots >= num_blocks * block_size are skipped.
+ */
+pkv_status pkv_reshape_and_cache(const void* key, const void* value,
+                                 void* k_cache, void* v_cache, int dtype,
+                                 const int32_t* slot_mapping, int num_tokens,
+                                 int num_blocks, int block_size, int num_kv_heads,
+                                 int head_dim, void* stream);
+
+/*
+ * Copy-on-write block duplication ([P3] copy-on-write: a shared block is
+ * duplicated when a sequence diverges; [P1] "Prefix Caching"): for each pair
+ * i, copies every slot and head of physical block src_dst[2i] onto block
+ * src_dst[2i+1] in k_cache and v_cache, and, when k_scales / v_scales are not
+ * NULL, their [num_kv_heads] scale rows.  src_dst is device int32 [n][2].
+ * Pairs must not overlap (no block is both a destination and another pair's
+ * source).  Indices outside [0, num_blocks) are skipped.  Bit copy.
+ */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                           const int32_t* src_dst, int n, int dtype, int num_blocks,
+                           int block_size, int num_kv_heads, int head_dim, void* stream);
+
+/*
+ * Symmetric absmax quantisation of whole cache blocks ([P2] s.8;
+ * [P1] "KV-Cache Quantization"), one scale per (block, KV head) over its
+ * [block_size, head_dim] tile:
+ *   a = max |x|;  scale = fp32(a / qmax)  (IEEE division; qmax = 127 for
+ *   PKV_I8, 448 for PKV_FP8E4M3);
+ *   code = round_half_even(fp32(x / scale)) clipped to [-127, 127]   (I8)
+ *   code = FP8-E4M3 round-to-nearest-even of fp32(x / scale), saturating at
+ *          +-448, sign of zero kept                                     (FP8)
+ *   a == 0 gives scale 0 and all codes 0.
+ * src_cache: [num_blocks][block_size][num_kv_heads][head_dim] of src_dtype
+ * (PKV_F32, PKV_BF16, PKV_F16); dst_codes: same shape of code_dtype
+ * (PKV_I8 or PKV_FP8E4M3); dst_scales: [num_blocks][num_kv_heads] fp32.
+ * block_ids: device int32 [n_blocks] of blocks to quantise, or NULL for
+ * blocks 0..n_blocks-1.  Call once for K and once for V.  Every slot of a
+ * quantised block must hold data.  Bit-exact.
+ */
+pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
+                           float* dst_scales, const int32_t* block_ids, int n_blocks,
+                           int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                           void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host-side checks                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Checks the device-array preconditions listed above on HOST copies:
+ * block_tables [num_seqs][max_blocks_per_seq], seq_lens [num_seqs] and,
+ * when not NULL, slot_mapping [num_tokens].  Returns PKV_EINVAL with a
+ * message naming the first violation.
+ */
+pkv_status pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int num_seqs, int block_size,
+                               int num_blocks, const int32_t* slot_mapping, int num_tokens);
+
+/* ------------------------------------------------------------------------ */
+/* Host block pool ([P2] s.10 free list; [P1] on-demand blocks; [P3] CoW)    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * A pool of physical block ids with a FIFO free list and a reference count
+ * per block.  Host memory only; not thread-safe (one owner thread).
+ */
+typedef struct pkv_pool pkv_pool;
+
+/* Creates a pool of num_blocks blocks.  initial_order (host, may be NULL =
+ * 0..num_blocks-1) gives the initial free-list order and must be a
+ * permutation.  Returns NULL on bad arguments (see pkv_last_error). */
+pkv_pool* pkv_pool_create(int num_blocks, const int32_t* initial_order);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* Takes the block at the front of the free list; its count becomes 1.
+ * PKV_ENOMEM when the list is empty. */
+pkv_status pkv_pool_alloc(pkv_pool* pool, int32_t* block_out);
+/* Adds a reference to a block in use (sharing, e.g. a forked sequence). */
+pkv_status pkv_pool_incref(pkv_pool* pool, int32_t block);
+/* Drops a reference; a block whose count reaches 0 goes to the back of the
+ * free list.  PKV_EINVAL for a free block. */
+pkv_status pkv_pool_decref(pkv_pool* pool, int32_t block);
+/* Reference count of a block (0 = free, -1 = out of range). */
+int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t block);
+
+/*
+ * Reserves the slot of token number seq_len of a sequence whose host table
+ * table[0 .. *table_len) covers seq_len tokens.  If seq_len % block_size == 0
+ * a new block is appended to the table (table_capacity bounds it).
+ * Otherwise, if the current last block is shared (count > 1), a new block is
+ * taken, the old block loses one reference and the table entry is repointed;
+ * *cow_src / *cow_dst then name the block to copy before writing (else both
+ * are -1).  *slot_out receives the slot.  PKV_ENOMEM if no block is free (the
+ * table is unchanged), PKV_EINVAL on inconsistent arguments.
+ */
+pkv_status pkv_pool_append(pkv_pool* pool, int32_t* table, int32_t table_capacity,
+                           int32_t* table_len, int32_t seq_len, int block_size,
+                           int32_t* slot_out, int32_t* cow_src, int32_t* cow_dst);
+
+/* Pool occupancy: free blocks, blocks in use, blocks with count > 1. */
+pkv_status pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* used_blocks,
+                          int32_t* shared_blocks);
+/* Copies the free list, front first, into out[0 .. min(n, cap)); *n = its length. */
+pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,359 @@
+// The C ABI: argument validation, partition choice, workspace layout and
+// kernel dispatch on the caller's stream.  Host code only.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static pkv_status hip_status(int err, const char* where) {
+  if (err == hipSuccess) return PKV_OK;
+  return fail(PKV_EHIP, "%s: %s", where, hipGetErrorString((hipError_t)err));
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int num_partitions) {
+  const size_t n = (size_t)num_seqs * num_q_heads * num_partitions;
+  WsLayout w;
+  w.m_off = 0;
+  w.l_off = align256(n * sizeof(float));
+  w.acc_off = w.l_off + align256(n * sizeof(float));
+  w.total = w.acc_off + align256(n * head_dim * sizeof(float));
+  return w;
+}
+
+static bool check_env() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("PKV_CHECK");
+    v = (e && e[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+// Resolve a user partition size (0 = auto) for the given shape.
+static int resolve_partition(int num_seqs, int num_kv_heads, int max_len, int block_size, int psize) {
+  if (psize > 0) return psize;
+  (void)num_seqs;
+  (void)num_kv_heads;
+  // One workgroup (4 waves) per 512-token partition keeps >= 8 blocks per
+  // wave and, for the long-context shapes, thousands of workgroups.  Shorter
+  // bounds run as one pass without partials.
+  const int single = ((max_len + block_size - 1) / block_size) * block_size;
+  if (max_len <= 512) return single > 0 ? single : block_size;
+  return 512;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" const char* pkv_last_error(void) { return g_err; }
+extern "C" const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+
+extern "C" int pkv_paged_attn_partition_size(int num_seqs, int num_kv_heads, int max_seq_len, int block_size) {
+  if (block_size <= 0 || max_seq_len < 0) return 0;
+  return resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, 0);
+}
+
+extern "C" int pkv_paged_attn_num_partitions(int num_seqs, int num_kv_heads, int max_seq_len, int block_size,
+                                             int partition_size) {
+  if (block_size <= 0 || max_seq_len < 0 || partition_size < 0) return 0;
+  if (partition_size > 0 && partition_size % block_size) return 0;
+  const int ps = resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_size);
+  const int n = (max_seq_len + ps - 1) / ps;
+  return n < 1 ? 1 : n;
+}
+
+extern "C" size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                                 int max_seq_len, int partition_size) {
+  const int np = pkv_paged_attn_num_partitions(num_seqs, num_kv_heads, max_seq_len, 16, partition_size);
+  if (np <= 1 || num_seqs <= 0) return 0;
+  return workspace_layout(num_seqs, num_q_heads, head_dim, np).total;
+}
+
+extern "C" pkv_status pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* seq_lens, int num_seqs, int block_size, int num_blocks,
+                                          const int32_t* slot_mapping, int num_tokens) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_blocks < 0)
+    return fail(PKV_EINVAL, "pkv_validate_tables: negative size");
+  if (num_seqs > 0 && (!block_tables || !seq_lens))
+    return fail(PKV_EINVAL, "pkv_validate_tables: null table");
+  for (int s = 0; s < num_seqs; ++s) {
+    const int L = seq_lens[s];
+    if (L < 0 || (long long)L > (long long)max_blocks_per_seq * block_size)
+      return fail(PKV_EINVAL, "seq_lens[%d] = %d outside [0, %d]", s, L, max_blocks_per_seq * block_size);
+    const int nb = (L + block_size - 1) / block_size;
+    for (int i = 0; i < nb; ++i) {
+      const int b = block_tables[(size_t)s * max_blocks_per_seq + i];
+      if (b < 0 || b >= num_blocks)
+        return fail(PKV_EINVAL, "block_tables[%d][%d] = %d outside [0, %d)", s, i, b, num_blocks);
+    }
+  }
+  if (slot_mapping && num_tokens > 0) {
+    const long long nslots = (long long)num_blocks * block_size;
+    std::vector<char> seen((size_t)nslots, 0);
+    for (int j = 0; j < num_tokens; ++j) {
+      const int sl = slot_mapping[j];
+      if (sl < 0) continue;
+      if (sl >= nslots) return fail(PKV_EINVAL, "slot_mapping[%d] = %d outside [0, %lld)", j, sl, nslots);
+      if (seen[sl]) return fail(PKV_EINVAL, "slot_mapping[%d] = %d repeats an earlier slot", j, sl);
+      seen[sl] = 1;
+    }
+  }
+  return PKV_OK;
+}
+
+// Device arrays -> host, then pkv_validate_tables (PKV_CHECK=1 only).
+static pkv_status device_check(const int32_t* block_tables, int mbs, const int32_t* seq_lens, int num_seqs,
+                               int block_size, int num_blocks, const int32_t* slots, int num_tokens,
+                               void* stream) {
+  std::vector<int32_t> bt((size_t)num_seqs * mbs), sl(num_seqs), sm(slots ? num_tokens : 0);
+  hipStream_t st = (hipStream_t)stream;
+  int e = hipSuccess;
+  if (num_seqs > 0 && block_tables)
+    e |= hipMemcpyAsync(bt.data(), block_tables, bt.size() * 4, hipMemcpyDeviceToHost, st);
+  if (num_seqs > 0 && seq_lens) e |= hipMemcpyAsync(sl.data(), seq_lens, sl.size() * 4, hipMemcpyDeviceToHost, st);
+  if (slots && num_tokens > 0) e |= hipMemcpyAsync(sm.data(), slots, sm.size() * 4, hipMemcpyDeviceToHost, st);
+  e |= hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(PKV_EHIP, "PKV_CHECK: copying tables to the host failed");
+  return pkv_validate_tables(block_tables ? bt.data() : nullptr, mbs, seq_lens ? sl.data() : nullptr,
+                             seq_lens ? num_seqs : 0, block_size, num_blocks, slots ? sm.data() : nullptr,
+                             num_tokens);
+}
+
+// ---------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------
+static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, size_t workspace_bytes,
+                               bool need_inputs) {
+  if (a.num_seqs < 0 || a.num_q_heads <= 0 || a.num_kv_heads <= 0 || a.max_blocks_per_seq < 0 || a.num_blocks < 0)
+    return fail(PKV_EINVAL, "%s: negative or zero size", who);
+  if (a.num_q_heads % a.num_kv_heads)
+    return fail(PKV_EINVAL, "%s: num_q_heads %% num_kv_heads != 0", who);
+  if (a.num_q_heads / a.num_kv_heads > 16)
+    return fail(PKV_EUNSUPPORTED, "%s: query group size above 16 is not built", who);
+  if (a.head_dim != 64 && a.head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be 64 or 128", who);
+  if (a.block_size != 16) return fail(PKV_EUNSUPPORTED, "%s: block_size must be 16", who);
+  if (a.q_dtype != PKV_F32 && a.q_dtype != PKV_BF16 && a.q_dtype != PKV_F16)
+    return fail(PKV_EUNSUPPORTED, "%s: query dtype must be f32, bf16 or f16", who);
+  if (need_inputs) {
+    const bool same = a.kv_dtype == a.q_dtype;
+    const bool codes = is_code_storage(a.kv_dtype) && (a.q_dtype == PKV_BF16 || a.q_dtype == PKV_F16);
+    if (!same && !codes)
+      return fail(PKV_EUNSUPPORTED, "%s: kv dtype must equal the query dtype, or be i8/fp8e4m3 with a 16-bit query",
+                  who);
+    if (codes && (!a.k_scales || !a.v_scales)) return fail(PKV_EINVAL, "%s: quantised cache needs k/v scales", who);
+    if (a.sink_tokens < 0 || a.window_tokens < 0) return fail(PKV_EINVAL, "%s: negative sink/window", who);
+  }
+  if (a.partition_size < 0 || (a.partition_size > 0 && a.partition_size % a.block_size))
+    return fail(PKV_EINVAL, "%s: partition_size must be 0 or a positive multiple of block_size", who);
+  const int max_len = a.max_blocks_per_seq * a.block_size;
+  a.partition_size = resolve_partition(a.num_seqs, a.num_kv_heads, max_len, a.block_size, a.partition_size);
+  a.num_partitions = (max_len + a.partition_size - 1) / a.partition_size;
+  if (a.num_partitions < 1) a.num_partitions = 1;
+  if (a.num_seqs == 0) return PKV_OK;
+  if (!a.out || !a.seq_lens) return fail(PKV_EINVAL, "%s: null pointer argument", who);
+  if (need_inputs && (!a.query || !a.k_cache || !a.v_cache || !a.block_tables))
+    return fail(PKV_EINVAL, "%s: null pointer argument", who);
+  a.ws_m = a.ws_l = a.ws_acc = nullptr;
+  if (a.num_partitions > 1) {
+    const WsLayout w = workspace_layout(a.num_seqs, a.num_q_heads, a.head_dim, a.num_partitions);
+    if (!workspace || workspace_bytes < w.total)
+      return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, w.total, workspace_bytes);
+    if (((uintptr_t)workspace) & 15) return fail(PKV_EINVAL, "%s: workspace must be 16-byte aligned", who);
+    char* base = (char*)workspace;
+    a.ws_m = (float*)(base + w.m_off);
+    a.ws_l = (float*)(base + w.l_off);
+    a.ws_acc = (float*)(base + w.acc_off);
+  }
+  return PKV_OK;
+}
+
+#define PKV_ATTN_ARGS                                                                                        \
+  void *out, const void *query, int q_dtype, const void *k_cache, const void *v_cache, int kv_dtype,          \
+      const float *k_scales, const float *v_scales, const int32_t *block_tables, int max_blocks_per_seq,      \
+      const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size, \
+      int num_blocks, float sm_scale, int partition_size, int sink_tokens, int window_tokens, void *workspace, \
+      size_t workspace_bytes, void *stream
+
+static AttnArgs fill_args(void* out, const void* query, int q_dtype, const void* k_cache, const void* v_cache,
+                          int kv_dtype, const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                          int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                          int num_kv_heads, int head_dim, int block_size, int num_blocks, float sm_scale,
+                          int partition_size, int sink_tokens, int window_tokens, void* stream) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.out = out;
+  a.query = query;
+  a.q_dtype = q_dtype;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_dtype = kv_dtype;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.sm_scale = sm_scale;
+  a.partition_size = partition_size;
+  a.sink_tokens = sink_tokens;
+  a.window_tokens = window_tokens;
+  a.stream = stream;
+  return a;
+}
+
+static pkv_status run_attn(bool do_partition, bool do_merge, PKV_ATTN_ARGS) {
+  AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, block_tables,
+                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, stream);
+  const char* who = do_partition ? (do_merge ? "pkv_paged_attn_decode" : "pkv_paged_attn_partition")
+                                 : "pkv_paged_attn_merge";
+  pkv_status st = prepare_attn(a, who, workspace, workspace_bytes, do_partition);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if (do_partition && check_env()) {
+    st = device_check(block_tables, max_blocks_per_seq, seq_lens, num_seqs, block_size, num_blocks, nullptr, 0,
+                      stream);
+    if (st != PKV_OK) return st;
+  }
+  if (do_partition) {
+    st = hip_status(launch_paged_attn_partition(a), who);
+    if (st != PKV_OK) return st;
+  }
+  if (do_merge) st = hip_status(launch_paged_attn_merge(a), who);
+  return st;
+}
+
+extern "C" pkv_status pkv_paged_attn_decode(PKV_ATTN_ARGS) {
+  return run_attn(true, true, out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, block_tables,
+                  max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                  num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, workspace, workspace_bytes,
+                  stream);
+}
+
+extern "C" pkv_status pkv_paged_attn_partition(PKV_ATTN_ARGS) {
+  return run_attn(true, false, out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales,
+                  block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                  block_size, num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, workspace,
+                  workspace_bytes, stream);
+}
+
+extern "C" pkv_status pkv_paged_attn_merge(void* out, int q_dtype, const int32_t* seq_lens, int num_seqs,
+                                           int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+                                           int partition_size, const void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (max_seq_len < 0 || max_seq_len % 16) return fail(PKV_EINVAL, "pkv_paged_attn_merge: bad max_seq_len");
+  return run_attn(false, true, out, nullptr, q_dtype, nullptr, nullptr, q_dtype, nullptr, nullptr, nullptr,
+                  max_seq_len / 16, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, 16, 0, 1.f,
+                  partition_size, 0, 0, const_cast<void*>(workspace), workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// cache writes
+// ---------------------------------------------------------------------------
+extern "C" pkv_status pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* seq_ids, const int32_t* positions, int num_tokens,
+                                       int num_seqs, int block_size, int num_blocks, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_blocks < 0)
+    return fail(PKV_EINVAL, "pkv_slot_mapping: bad size");
+  if (num_tokens == 0) return PKV_OK;
+  if (!slot_mapping || !block_tables || !positions) return fail(PKV_EINVAL, "pkv_slot_mapping: null pointer");
+  if (!seq_ids && num_tokens > num_seqs)
+    return fail(PKV_EINVAL, "pkv_slot_mapping: without seq_ids, token j belongs to sequence j < num_seqs");
+  return hip_status(launch_slot_mapping(slot_mapping, block_tables, max_blocks_per_seq, seq_ids, positions,
+                                        num_tokens, num_seqs, block_size, num_blocks, stream),
+                    "pkv_slot_mapping");
+}
+
+static pkv_status check_cache_shape(const char* who, int block_size, int num_kv_heads, int head_dim) {
+  if (block_size != 16) return fail(PKV_EUNSUPPORTED, "%s: block_size must be 16", who);
+  if (num_kv_heads <= 0) return fail(PKV_EINVAL, "%s: num_kv_heads must be positive", who);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be 64 or 128", who);
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                            int dtype, const int32_t* slot_mapping, int num_tokens, int num_blocks,
+                                            int block_size, int num_kv_heads, int head_dim, void* stream) {
+  pkv_status st = check_cache_shape("pkv_reshape_and_cache", block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (!is_float_storage(dtype))
+    return fail(PKV_EUNSUPPORTED, "pkv_reshape_and_cache: dtype must be f32, bf16 or f16");
+  if (num_tokens < 0 || num_blocks < 0) return fail(PKV_EINVAL, "pkv_reshape_and_cache: negative size");
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_EINVAL, "pkv_reshape_and_cache: null pointer");
+  if (check_env()) {
+    st = device_check(nullptr, 0, nullptr, 0, block_size, num_blocks, slot_mapping, num_tokens, stream);
+    if (st != PKV_OK) return st;
+  }
+  return hip_status(launch_reshape_and_cache(key, value, k_cache, v_cache, dtype_bytes(dtype), slot_mapping,
+                                             num_tokens, num_blocks, block_size, num_kv_heads, head_dim, stream),
+                    "pkv_reshape_and_cache");
+}
+
+extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                                      const int32_t* src_dst, int n, int dtype, int num_blocks, int block_size,
+                                      int num_kv_heads, int head_dim, void* stream) {
+  pkv_status st = check_cache_shape("pkv_copy_blocks", block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (!dtype_bytes(dtype)) return fail(PKV_EUNSUPPORTED, "pkv_copy_blocks: unknown dtype");
+  if (n < 0 || num_blocks < 0) return fail(PKV_EINVAL, "pkv_copy_blocks: negative size");
+  if (n == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src_dst) return fail(PKV_EINVAL, "pkv_copy_blocks: null pointer");
+  if ((k_scales == nullptr) != (v_scales == nullptr))
+    return fail(PKV_EINVAL, "pkv_copy_blocks: give both scale arrays or neither");
+  return hip_status(launch_copy_blocks(k_cache, v_cache, k_scales, v_scales, src_dst, n, dtype_bytes(dtype),
+                                       num_blocks, block_size, num_kv_heads, head_dim, stream),
+                    "pkv_copy_blocks");
+}
+
+extern "C" pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
+                                      float* dst_scales, const int32_t* block_ids, int n_blocks, int num_blocks,
+                                      int block_size, int num_kv_heads, int head_dim, void* stream) {
+  pkv_status st = check_cache_shape("pkv_quantize_kv", block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (!is_float_storage(src_dtype)) return fail(PKV_EUNSUPPORTED, "pkv_quantize_kv: source must be f32/bf16/f16");
+  if (!is_code_storage(code_dtype)) return fail(PKV_EUNSUPPORTED, "pkv_quantize_kv: codes must be i8 or fp8e4m3");
+  if (n_blocks < 0 || num_blocks < 0) return fail(PKV_EINVAL, "pkv_quantize_kv: negative size");
+  if (!block_ids && n_blocks > num_blocks) return fail(PKV_EINVAL, "pkv_quantize_kv: n_blocks > num_blocks");
+  if (n_blocks == 0) return PKV_OK;
+  if (n_blocks > 2147483647 / 1) return fail(PKV_EINVAL, "pkv_quantize_kv: too many blocks");
+  if (!src_cache || !dst_codes || !dst_scales) return fail(PKV_EINVAL, "pkv_quantize_kv: null pointer");
+  return hip_status(launch_quantize_kv(src_cache, src_dtype, dst_codes, code_dtype, dst_scales, block_ids, n_blocks,
+                                       num_blocks, block_size, num_kv_heads, head_dim, stream),
+                    "pkv_quantize_kv");
+}

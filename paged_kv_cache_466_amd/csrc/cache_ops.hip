@@ -1,0 +1,219 @@
+// Cache-write kernels: slot mapping, the slot write (reshape_and_cache),
+// whole-block copy-on-write, and absmax block quantisation.
+//
+// All four are memory-bound streams over short rows; each thread moves 16
+// bytes per access so that a wave touches whole 64-byte segments.
+#include <hip/hip_runtime.h>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------------------
+// slot = table[s][p / bs] * bs + p % bs   (t13_4 block table; Chapter 18,
+// "How PagedAttention Works")
+// ---------------------------------------------------------------------------
+__global__ void slot_mapping_kernel(int32_t* __restrict__ slots, const int32_t* __restrict__ tables,
+                                    int mbs, const int32_t* __restrict__ seq_ids,
+                                    const int32_t* __restrict__ positions, int num_tokens,
+                                    int num_seqs, int bs, int num_blocks) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= num_tokens) return;
+  const int s = seq_ids ? seq_ids[j] : j;
+  const int p = positions[j];
+  int32_t slot = -1;
+  if (s >= 0 && s < num_seqs && p >= 0) {
+    const int lb = p / bs;
+    if (lb < mbs) {
+      const int32_t pb = tables[(size_t)s * mbs + lb];
+      if (pb >= 0 && pb < num_blocks) slot = pb * bs + p % bs;
+    }
+  }
+  slots[j] = slot;
+}
+
+int launch_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* seq_ids, const int32_t* positions, int num_tokens, int num_seqs,
+                        int block_size, int num_blocks, void* stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int threads = 256;
+  const int grid = (num_tokens + threads - 1) / threads;
+  slot_mapping_kernel<<<grid, threads, 0, (hipStream_t)stream>>>(
+      slot_mapping, block_tables, max_blocks_per_seq, seq_ids, positions, num_tokens, num_seqs,
+      block_size, num_blocks);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// reshape_and_cache: token j's [Hkv, D] row goes to cache row slot_mapping[j].
+// A cache row for slot `slot` starts at slot * row_bytes because a block is
+// [bs][Hkv][D] and blocks are consecutive.
+// ---------------------------------------------------------------------------
+__global__ void reshape_and_cache_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
+                                         uint4* __restrict__ kc, uint4* __restrict__ vc,
+                                         const int32_t* __restrict__ slots, int num_tokens,
+                                         int chunks_per_row, long long num_slots) {
+  const long long total = (long long)num_tokens * chunks_per_row;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int j = (int)(i / chunks_per_row);
+    const int c = (int)(i - (long long)j * chunks_per_row);
+    const long long slot = slots[j];
+    if (slot < 0 || slot >= num_slots) continue;
+    const long long dst = slot * chunks_per_row + c;
+    kc[dst] = key[i];
+    vc[dst] = value[i];
+  }
+}
+
+int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                             int elem_bytes, const int32_t* slot_mapping, int num_tokens,
+                             int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                             void* stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int chunks_per_row = num_kv_heads * head_dim * elem_bytes / 16;
+  const long long total = (long long)num_tokens * chunks_per_row;
+  const int threads = 256;
+  long long grid = (total + threads - 1) / threads;
+  if (grid > 65536) grid = 65536;
+  reshape_and_cache_kernel<<<(int)grid, threads, 0, (hipStream_t)stream>>>(
+      (const uint4*)key, (const uint4*)value, (uint4*)k_cache, (uint4*)v_cache, slot_mapping,
+      num_tokens, chunks_per_row, (long long)num_blocks * block_size);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// copy_blocks: duplicate whole blocks (K, V and their scale rows).
+// ---------------------------------------------------------------------------
+__global__ void copy_blocks_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc,
+                                   float* __restrict__ ks, float* __restrict__ vs,
+                                   const int32_t* __restrict__ src_dst, int chunks_per_block,
+                                   int num_blocks, int num_kv_heads) {
+  const int pair = blockIdx.x;
+  const int src = src_dst[2 * pair];
+  const int dst = src_dst[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const long long s0 = (long long)src * chunks_per_block;
+  const long long d0 = (long long)dst * chunks_per_block;
+  for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < chunks_per_block; c += gridDim.y * blockDim.x) {
+    kc[d0 + c] = kc[s0 + c];
+    vc[d0 + c] = vc[s0 + c];
+  }
+  if (blockIdx.y == 0 && ks) {
+    for (int h = threadIdx.x; h < num_kv_heads; h += blockDim.x) {
+      ks[(size_t)dst * num_kv_heads + h] = ks[(size_t)src * num_kv_heads + h];
+      vs[(size_t)dst * num_kv_heads + h] = vs[(size_t)src * num_kv_heads + h];
+    }
+  }
+}
+
+int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                       const int32_t* src_dst, int n, int elem_bytes, int num_blocks, int block_size,
+                       int num_kv_heads, int head_dim, void* stream) {
+  if (n == 0) return hipSuccess;
+  const int chunks_per_block = block_size * num_kv_heads * head_dim * elem_bytes / 16;
+  const int threads = 256;
+  int gy = (chunks_per_block + threads - 1) / threads;
+  if (gy > 64) gy = 64;
+  copy_blocks_kernel<<<dim3(n, gy), threads, 0, (hipStream_t)stream>>>(
+      (uint4*)k_cache, (uint4*)v_cache, k_scales, v_scales, src_dst, chunks_per_block, num_blocks,
+      num_kv_heads);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// quantize_kv: one wave per (block, KV head) tile of [BS=16][D].
+// Lane l reads token row l/4, quarter l%4 of the head dimension.
+// "KV Cache Engineering", section 8: scale = absmax / largest code, codes
+// rounded half to even and clipped.
+// ---------------------------------------------------------------------------
+template <typename SRC, int D, bool FP8OUT>
+__global__ __launch_bounds__(64) void quantize_kv_kernel(
+    const typename SRC::raw* __restrict__ src, void* __restrict__ dst, float* __restrict__ scales,
+    const int32_t* __restrict__ block_ids, int num_blocks, int num_kv_heads) {
+  constexpr int BS = 16;
+  constexpr int ELEMS = D / 4;                 // per lane
+  constexpr int SRC_CHUNKS = ELEMS * SRC::bytes / 16;
+  constexpr int EL16 = 16 / SRC::bytes;
+  const int b = block_ids ? block_ids[blockIdx.x] : (int)blockIdx.x;
+  const int h = blockIdx.y;
+  if (b < 0 || b >= num_blocks) return;
+  const int lane = threadIdx.x;
+  const int t = lane >> 2, q = lane & 3;
+  const size_t row = ((size_t)b * BS + t) * num_kv_heads + h;   // element row index
+  const uint4* p = reinterpret_cast<const uint4*>(src + row * D + q * ELEMS);
+  float x[ELEMS];
+#pragma unroll
+  for (int c = 0; c < SRC_CHUNKS; ++c) {
+    uint4 v = p[c];
+    decode16<SRC>(v, x + c * EL16);
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
+  a = wave_max(a);
+  const float qmax = FP8OUT ? 448.0f : 127.0f;
+  const float sc = __fdiv_rn(a, qmax);
+  uint8_t codes[ELEMS];
+#pragma unroll
+  for (int i = 0; i < ELEMS; ++i) {
+    if (sc == 0.f) {
+      codes[i] = 0;
+    } else {
+      const float y = __fdiv_rn(x[i], sc);
+      if (FP8OUT) {
+        codes[i] = (uint8_t)f32_to_e4m3(y);
+      } else {
+        float r = rintf(y);
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        codes[i] = (uint8_t)(int8_t)(int)r;
+      }
+    }
+  }
+  uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + row * D + q * ELEMS);
+#pragma unroll
+  for (int c = 0; c < ELEMS / 16; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)codes[c * 16 + 4 * k] | ((uint32_t)codes[c * 16 + 4 * k + 1] << 8) |
+             ((uint32_t)codes[c * 16 + 4 * k + 2] << 16) | ((uint32_t)codes[c * 16 + 4 * k + 3] << 24);
+    o[c] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (lane == 0) scales[(size_t)b * num_kv_heads + h] = sc;
+}
+
+template <typename SRC, int D>
+static int launch_q(const void* src, void* dst, int code_dtype, float* scales, const int32_t* ids,
+                    int n_blocks, int num_blocks, int num_kv_heads, hipStream_t st) {
+  dim3 grid(n_blocks, num_kv_heads);
+  if (code_dtype == PKV_FP8E4M3)
+    quantize_kv_kernel<SRC, D, true><<<grid, 64, 0, st>>>((const typename SRC::raw*)src, dst, scales, ids,
+                                                          num_blocks, num_kv_heads);
+  else
+    quantize_kv_kernel<SRC, D, false><<<grid, 64, 0, st>>>((const typename SRC::raw*)src, dst, scales, ids,
+                                                           num_blocks, num_kv_heads);
+  return hipGetLastError();
+}
+
+int launch_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
+                       float* dst_scales, const int32_t* block_ids, int n_blocks, int num_blocks,
+                       int block_size, int num_kv_heads, int head_dim, void* stream) {
+  (void)block_size;
+  if (n_blocks == 0) return hipSuccess;
+  hipStream_t st = (hipStream_t)stream;
+#define PKV_Q(SRC)                                                                                  \
+  return head_dim == 64 ? launch_q<SRC, 64>(src_cache, dst_codes, code_dtype, dst_scales, block_ids, \
+                                            n_blocks, num_blocks, num_kv_heads, st)                 \
+                        : launch_q<SRC, 128>(src_cache, dst_codes, code_dtype, dst_scales, block_ids, \
+                                             n_blocks, num_blocks, num_kv_heads, st)
+  switch (src_dtype) {
+    case PKV_F32: PKV_Q(F32);
+    case PKV_BF16: PKV_Q(BF16);
+    default: PKV_Q(F16);
+  }
+#undef PKV_Q
+}
+
+}  // namespace pkv

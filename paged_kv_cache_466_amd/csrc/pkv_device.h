@@ -1,0 +1,156 @@
+// Device helpers for gfx950: storage-type conversions, 16-byte vector
+// access and wave64 reductions.
+#ifndef PKV_DEVICE_H_
+#define PKV_DEVICE_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// Storage tags: each holds raw bits; `Elems16` elements fill 16 bytes.
+struct F32 { typedef float raw; static constexpr int bytes = 4; };
+struct BF16 { typedef uint16_t raw; static constexpr int bytes = 2; };
+struct F16 { typedef uint16_t raw; static constexpr int bytes = 2; };
+struct I8 { typedef int8_t raw; static constexpr int bytes = 1; };
+struct FP8 { typedef uint8_t raw; static constexpr int bytes = 1; };
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Decode the 16 bytes `v` holding 16/bytes elements of storage type T into
+// `out` as float.  Exact for every storage type (codes decode to the code's
+// own value; the scale is applied by the caller).
+template <typename T> __device__ __forceinline__ void decode16(const uint4& v, float* out);
+
+template <> __device__ __forceinline__ void decode16<F32>(const uint4& v, float* out) {
+  out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+}
+template <> __device__ __forceinline__ void decode16<BF16>(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <> __device__ __forceinline__ void decode16<F16>(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = f16_to_f32(w[i] & 0xFFFFu);
+    out[2 * i + 1] = f16_to_f32(w[i] >> 16);
+  }
+}
+template <> __device__ __forceinline__ void decode16<I8>(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) out[4 * i + b] = (float)(int8_t)((w[i] >> (8 * b)) & 0xFF);
+  }
+}
+// OCP FP8-E4M3 -> fp32 via the gfx950 converter (exact).
+template <> __device__ __forceinline__ void decode16<FP8>(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+    floatx2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+    out[4 * i + 0] = lo[0]; out[4 * i + 1] = lo[1];
+    out[4 * i + 2] = hi[0]; out[4 * i + 3] = hi[1];
+  }
+}
+
+// Store helpers for the output types.
+template <typename T> __device__ __forceinline__ void store_out(void* base, size_t idx, float x);
+template <> __device__ __forceinline__ void store_out<F32>(void* base, size_t idx, float x) {
+  reinterpret_cast<float*>(base)[idx] = x;
+}
+template <> __device__ __forceinline__ void store_out<BF16>(void* base, size_t idx, float x) {
+  reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16(x);
+}
+template <> __device__ __forceinline__ void store_out<F16>(void* base, size_t idx, float x) {
+  reinterpret_cast<uint16_t*>(base)[idx] = f32_to_f16(x);
+}
+
+template <typename T> __device__ __forceinline__ float load_elem(const void* base, size_t idx);
+template <> __device__ __forceinline__ float load_elem<F32>(const void* base, size_t idx) {
+  return reinterpret_cast<const float*>(base)[idx];
+}
+template <> __device__ __forceinline__ float load_elem<BF16>(const void* base, size_t idx) {
+  return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+}
+template <> __device__ __forceinline__ float load_elem<F16>(const void* base, size_t idx) {
+  return f16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions (butterfly over all 64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// DPP quad permutes: exchange with lane ^1 / ^2 inside groups of four lanes.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+
+// ---------------------------------------------------------------------------
+// FP8-E4M3 (OCP "fn") encoder: round to nearest, ties to even, saturating at
+// +-448, sign of zero kept.  Integer arithmetic on the fp32 bit pattern.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x43E00000u) {                 // |x| > 448: saturate
+    code = 0x7E;
+  } else if (a >= 0x3C800000u) {         // |x| >= 2^-6: normal range
+    // keep exponent and top 3 mantissa bits, round the 20 dropped bits
+    uint32_t q = a >> 20;
+    const uint32_t rem = a & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1;
+    code = q - (120u << 3);              // rebias exponent 127 -> 7
+    if (code > 0x7E) code = 0x7E;
+  } else {                               // subnormal: value = m * 2^-9
+    const float y = __uint_as_float(a) * 512.0f;   // exact power-of-two scaling
+    code = (uint32_t)rintf(y);                     // 0..8; 8 is the smallest normal
+  }
+  return code | sign;
+}
+
+}  // namespace pkv
+
+#endif  // PKV_DEVICE_H_

@@ -1,0 +1,81 @@
+// Internal declarations shared by the host-side translation units.
+#ifndef PKV_INTERNAL_H_
+#define PKV_INTERNAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Records the thread-local error message and returns `st`.
+pkv_status fail(pkv_status st, const char* fmt, ...);
+void set_error(const char* fmt, ...);
+void clear_error();
+
+inline int dtype_bytes(int dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_BF16:
+    case PKV_F16: return 2;
+    case PKV_I8:
+    case PKV_FP8E4M3: return 1;
+    default: return 0;
+  }
+}
+
+inline bool is_float_storage(int dt) { return dt == PKV_F32 || dt == PKV_BF16 || dt == PKV_F16; }
+inline bool is_code_storage(int dt) { return dt == PKV_I8 || dt == PKV_FP8E4M3; }
+
+// Decode-attention launch description shared by the partition and merge passes.
+struct AttnArgs {
+  void* out;
+  const void* query;
+  int q_dtype;
+  const void* k_cache;
+  const void* v_cache;
+  int kv_dtype;
+  const float* k_scales;
+  const float* v_scales;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* seq_lens;
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  float sm_scale;
+  int partition_size;  // resolved (never 0)
+  int num_partitions;  // per sequence, from max_blocks_per_seq * block_size
+  int sink_tokens, window_tokens;
+  float* ws_m;    // [S][Hq][P]
+  float* ws_l;    // [S][Hq][P]
+  float* ws_acc;  // [S][Hq][P][D]
+  void* stream;
+};
+
+// Workspace layout for given sizes: offsets (bytes) of m, l, acc and total.
+struct WsLayout {
+  size_t m_off, l_off, acc_off, total;
+};
+WsLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int num_partitions);
+
+// Kernel launchers (defined in the .hip files).  They assume validated
+// arguments and return a hipError_t cast to int.
+int launch_paged_attn_partition(const AttnArgs& a);
+int launch_paged_attn_merge(const AttnArgs& a);
+int launch_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* seq_ids, const int32_t* positions, int num_tokens,
+                        int num_seqs, int block_size, int num_blocks, void* stream);
+int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                             int elem_bytes, const int32_t* slot_mapping, int num_tokens,
+                             int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                             void* stream);
+int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                       const int32_t* src_dst, int n, int elem_bytes, int num_blocks, int block_size,
+                       int num_kv_heads, int head_dim, void* stream);
+int launch_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
+                       float* dst_scales, const int32_t* block_ids, int n_blocks, int num_blocks,
+                       int block_size, int num_kv_heads, int head_dim, void* stream);
+
+}  // namespace pkv
+
+#endif  // PKV_INTERNAL_H_

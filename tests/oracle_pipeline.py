@@ -15,6 +15,7 @@ import torch
 
 import oracle
 from oracle import attention, paging, quant
+from plan import build_tables
 
 POISON = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "f16": np.uint16(0x7E00),
           "i8": np.int8(-128), "fp8e4m3": np.uint8(0x7F)}
@@ -33,23 +34,6 @@ def to_raw(t, dtype):
     if dtype == "fp8e4m3":
         return t.view(torch.uint8).numpy()
     raise ValueError(dtype)
-
-
-def build_tables(w, pool):
-    """Execute the workload's pool plan; returns a list of python tables."""
-    from workloads.synth import plan_ops
-    tables = [None] * w.S
-    for op in plan_ops(w):
-        kind, s = op[0], op[1]
-        if kind == "new":
-            tables[s] = pool.allocate_sequence(op[2], w.BS)
-        elif kind == "share":
-            tables[s] = pool.fork(tables[op[2]][: op[3]])
-        elif kind == "grow":
-            need = -(-op[2] // w.BS)
-            while len(tables[s]) < need:
-                tables[s].append(pool.alloc())
-    return tables
 
 
 def pad_tables(tables, width, fill=0):
@@ -85,6 +69,9 @@ class OracleRun:
             self.k_src, self.v_src = self.k_cache, self.v_cache
             self.k_cache, self.k_scales = quant.quantize_cache_blocks(kv, w.kv_dtype, used)
             self.v_cache, self.v_scales = quant.quantize_cache_blocks(vv, w.kv_dtype, used)
+            unused = np.setdiff1d(np.arange(w.num_blocks), used)
+            for arr in (self.k_cache, self.v_cache):
+                arr[unused] = POISON[w.kv_dtype]
         self.step_slots = None
         self.cow = []
         if do_step and w.append:
