@@ -168,15 +168,26 @@ __global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams 
   constexpr int WAVE_LDS = 16 * ACC_STRIDE * 4;
   static_assert(kBS * VROW <= WAVE_LDS, "V staging must fit the per-wave region");
   constexpr bool kCodes = KVT::bytes == 1;
+  constexpr int KCH = kCodes ? NC / 2 : NC;            // 16-byte K loads per lane per block
+  constexpr int ROW_BYTES = D * KVT::bytes;
+  constexpr int LANES_PER_ROW = ROW_BYTES / 16;
+  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+  constexpr int VCH = kBS / ROWS_PER_PASS;             // 16-byte V loads per lane per block
+  // Scores may exceed the running max by this much (log2 units) before the
+  // accumulators are rescaled: probabilities stay below 2^8.
+  constexpr float kSlack = 8.0f;
   typedef Mfma<QT> M;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[WAVES * WAVE_LDS + WAVES * 16 * 2 * 4];
-  const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  // kvh fastest: the KV heads of one block are dispatched together, so the
+  // block's 16 x Hkv x D rows are read from HBM close together in time.
+  const int kvh = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int L = clamp_len(p.seq_lens[s], p.mbs);
   const bool single = p.num_partitions == 1;
   const int t_begin = part * p.partition_size;
+  const bool windowed = p.sink != 0 || p.window != 0;
 
   if (t_begin >= L) {
     if (single && part == 0) {
@@ -205,112 +216,141 @@ __global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams 
     }
   }
 
-  float m2 = -INFINITY;          // running max (log2 domain) of head g
+  // ---- this wave's blocks: lb = first + j * WAVES, j < nwb ------------------
+  const int first = lb_begin + wave;
+  const int nwb = first < lb_end ? (lb_end - first + WAVES - 1) / WAVES : 0;
+  // lane i holds the table entry of wave block (chunk * 64 + i)
+  int chunk = 0;
+  int pbv = lane < nwb ? table_entry(p, s, first + lane * WAVES) : 0;
+
+  auto block_needed_j = [&](int j) { return block_needed(first + j * WAVES, L, p.sink, p.window); };
+  auto next_needed = [&](int j) {
+    while (j < nwb && !block_needed_j(j)) ++j;
+    return j;
+  };
+  auto entry = [&](int j) {
+    if ((j >> 6) != chunk) {               // wave-uniform; once per 64 blocks
+      chunk = j >> 6;
+      const int jj = chunk * 64 + lane;
+      pbv = jj < nwb ? table_entry(p, s, first + jj * WAVES) : 0;
+    }
+    return __builtin_amdgcn_readlane(pbv, j & 63);
+  };
+
+  struct Tile {
+    uint4 k[KCH];
+    uint4 v[VCH];
+    int pb;
+    float ks, vs;
+  };
+  const size_t row_elems = (size_t)p.num_kv_heads * D;   // elements between token rows
+  auto load_tile = [&](Tile& t, int j) {
+    const int pb = entry(j);
+    t.pb = pb;
+    const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * D;   // element offset of row 0
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) +
+                           (tile + (size_t)(lane & 15) * row_elems) * KVT::bytes;
+    if constexpr (!kCodes) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kbase + qk_doff<KVT, D>(c, kg) * 2);
+    } else {
+#pragma unroll
+      for (int c2 = 0; c2 < KCH; ++c2) t.k[c2] = *reinterpret_cast<const uint4*>(kbase + (D / 4) * kg + 16 * c2);
+    }
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_cache) + tile * KVT::bytes;
+#pragma unroll
+    for (int pass = 0; pass < VCH; ++pass) {
+      const int r = pass * ROWS_PER_PASS + lane / LANES_PER_ROW;
+      t.v[pass] = *reinterpret_cast<const uint4*>(vbase + (size_t)r * row_elems * KVT::bytes +
+                                                  (lane % LANES_PER_ROW) * 16);
+    }
+    if constexpr (kCodes) {
+      t.ks = p.k_scales[(size_t)pb * p.num_kv_heads + kvh];
+      t.vs = p.v_scales[(size_t)pb * p.num_kv_heads + kvh];
+    } else {
+      t.ks = t.vs = 1.f;
+    }
+  };
+
+  float m2 = -INFINITY;          // running max (log2 domain) of head g, same in all lane groups
   float lsum = 0.f;              // this lane's share of the softmax denominator
   floatx4 acc[NN];
 #pragma unroll
   for (int n = 0; n < NN; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
-
   uint8_t* vstage = lds + wave * WAVE_LDS;
-  const size_t row_elems = (size_t)p.num_kv_heads * D;   // elements between token rows
 
-  for (int lb = lb_begin + wave; lb < lb_end; lb += WAVES) {
-    if (!block_needed(lb, L, p.sink, p.window)) continue;
-    const int pb = table_entry(p, s, lb);
-    const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * D;   // element offset of row 0
+  auto process = [&](const Tile& t, int j) {
+    const int lb = first + j * WAVES;
+    const int t0 = lb * kBS;
+    // every token of the block is kept: no masking work
+    const bool full = t0 + kBS <= L && (!windowed || t0 + kBS <= p.sink || t0 >= L - p.window);
 
-    // ---- K: lane (row = lane%16, group kg) loads its A-operand chunks -----
-    uint4 kraw[NC];
-    {
-      const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) +
-                             (tile + (size_t)(lane & 15) * row_elems) * KVT::bytes;
+    // ---- V rows -> LDS (masked rows as zeros: 0 * NaN must not reach acc) --
+#pragma unroll
+    for (int pass = 0; pass < VCH; ++pass) {
+      const int r = pass * ROWS_PER_PASS + lane / LANES_PER_ROW;
+      const int cchunk = lane % LANES_PER_ROW;
+      uint4 w = t.v[pass];
       if constexpr (!kCodes) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          kraw[c] = *reinterpret_cast<const uint4*>(kbase + qk_doff<KVT, D>(c, kg) * 2);
+        if (!full && !kept(t0 + r, L, p.sink, p.window)) w = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 16) = w;
       } else {
-        // 8 codes per MFMA; the lane's NC chunks are contiguous (qk_doff)
-#pragma unroll
-        for (int c2 = 0; c2 < NC / 2; ++c2) {
-          uint4 w = *reinterpret_cast<const uint4*>(kbase + (D / 4) * kg + 16 * c2);
-          kraw[2 * c2] = to16<QT, KVT>(make_uint2(w.x, w.y));
-          kraw[2 * c2 + 1] = to16<QT, KVT>(make_uint2(w.z, w.w));
-        }
-      }
-    }
-    // ---- V: whole rows, 16 bytes per lane per access, staged in LDS -------
-    {
-      const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_cache) + tile * KVT::bytes;
-      constexpr int ROW_BYTES = D * KVT::bytes;
-      constexpr int LANES_PER_ROW = ROW_BYTES / 16;
-      constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
-#pragma unroll
-      for (int pass = 0; pass < kBS / ROWS_PER_PASS; ++pass) {
-        const int r = pass * ROWS_PER_PASS + lane / LANES_PER_ROW;
-        const int cchunk = lane % LANES_PER_ROW;
-        // Rows of tokens outside the kept set (the unused tail of the last
-        // block, tokens between the sinks and the window) are staged as
-        // zeros: their probability is 0, but 0 * (whatever the slot holds,
-        // e.g. NaN) must not reach the accumulator.
-        const bool keep_row = kept(lb * kBS + r, L, p.sink, p.window);
-        uint4 w = *reinterpret_cast<const uint4*>(vbase + (size_t)r * row_elems * KVT::bytes + cchunk * 16);
-        if constexpr (!kCodes) {
-          if (!keep_row) w = make_uint4(0, 0, 0, 0);
-          *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 16) = w;
-        } else {
-          // 16 codes -> 16 elements of 16 bits (32 bytes)
-          uint4 lo = to16<QT, KVT>(make_uint2(w.x, w.y));
-          uint4 hi = to16<QT, KVT>(make_uint2(w.z, w.w));
-          if (!keep_row) lo = hi = make_uint4(0, 0, 0, 0);
-          *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 32) = lo;
-          *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 32 + 16) = hi;
-        }
+        uint4 lo = to16<QT, KVT>(make_uint2(w.x, w.y));
+        uint4 hi = to16<QT, KVT>(make_uint2(w.z, w.w));
+        if (!full && !kept(t0 + r, L, p.sink, p.window)) lo = hi = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 32) = lo;
+        *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 32 + 16) = hi;
       }
     }
 
-    // ---- S^T = K Q^T ------------------------------------------------------
+    // ---- S^T = K Q^T --------------------------------------------------------
     floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!kCodes) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::vec8, kraw[c]), qop[c], sacc);
-
-    float factor = p.scale_log2;
-    float vscale = 1.f;
-    if constexpr (kCodes) {
-      factor *= p.k_scales[(size_t)pb * p.num_kv_heads + kvh];
-      vscale = p.v_scales[(size_t)pb * p.num_kv_heads + kvh];
+      for (int c = 0; c < NC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::vec8, t.k[c]), qop[c], sacc);
+    } else {
+#pragma unroll
+      for (int c2 = 0; c2 < KCH; ++c2) {
+        const uint4 lo = to16<QT, KVT>(make_uint2(t.k[c2].x, t.k[c2].y));
+        const uint4 hi = to16<QT, KVT>(make_uint2(t.k[c2].z, t.k[c2].w));
+        sacc = M::qk(__builtin_bit_cast(typename M::vec8, lo), qop[2 * c2], sacc);
+        sacc = M::qk(__builtin_bit_cast(typename M::vec8, hi), qop[2 * c2 + 1], sacc);
+      }
     }
+    const float factor = p.scale_log2 * t.ks;
     // lane holds tokens 4*kg + i of this block for head g
     float sc[4];
-    float bmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = lb * kBS + 4 * kg + i;
-      sc[i] = kept(t, L, p.sink, p.window) ? sacc[i] * factor : -INFINITY;
-      bmax = fmaxf(bmax, sc[i]);
+    for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * factor;
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!kept(t0 + 4 * kg + i, L, p.sink, p.window)) sc[i] = -INFINITY;
     }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float mnew = fmaxf(m2, bmax);
-    if (mnew == -INFINITY) continue;           // nothing kept yet (uniform over the wave)
-    const float alpha = exp2f(m2 - mnew);      // 0 when m2 = -inf
+    const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    // ---- online softmax, rescaling only when a score passes m2 + slack -----
+    if (__ballot(lm > m2 + kSlack)) {
+      float bmax = fmaxf(lm, __shfl_xor(lm, 16, 64));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+      const float mnew = fmaxf(m2, bmax);
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);   // 0 while m2 = -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int n = 0; n < NN; ++n) acc[n] *= alpha;
+      m2 = mnew;
+    }
     float pr[4];
-    float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pr[i] = exp2f(sc[i] - mnew);
-      psum += pr[i];
+      pr[i] = __builtin_amdgcn_exp2f(sc[i] - m2);
+      lsum += pr[i];
     }
-    lsum = lsum * alpha + psum;
-    m2 = mnew;
-#pragma unroll
-    for (int n = 0; n < NN; ++n) acc[n] *= alpha;
-
     // P^T as the B operand (tokens 4kg..4kg+3 of head g), V scale folded in
-    const uint32_t p01 = M::pack2(pr[0] * vscale, pr[1] * vscale);
-    const uint32_t p23 = M::pack2(pr[2] * vscale, pr[3] * vscale);
+    const uint32_t p01 = M::pack2(pr[0] * t.vs, pr[1] * t.vs);
+    const uint32_t p23 = M::pack2(pr[2] * t.vs, pr[3] * t.vs);
     const shortx4 pop = __builtin_bit_cast(shortx4, make_uint2(p01, p23));
 
-    // ---- out^T += V^T P^T: V^T chunks through the transposing LDS read -----
+    // ---- out^T += V^T P^T: V^T chunks through the transposing LDS read ----
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -326,6 +366,24 @@ __global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // ---- main loop: block j+1's loads are in flight while block j computes --
+  {
+    Tile ta, tb;
+    int j = next_needed(0);
+    if (j < nwb) load_tile(ta, j);
+    while (j < nwb) {
+      int jn = next_needed(j + 1);
+      if (jn < nwb) load_tile(tb, jn);
+      process(ta, j);
+      j = jn;
+      if (j >= nwb) break;
+      jn = next_needed(j + 1);
+      if (jn < nwb) load_tile(ta, jn);
+      process(tb, j);
+      j = jn;
+    }
   }
 
   // ---- this wave's softmax state -> LDS; combine the waves -----------------
@@ -346,16 +404,16 @@ __global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams 
   const size_t head0 = (size_t)s * p.num_q_heads + kvh * G;
   for (int i = threadIdx.x; i < G * D; i += 64 * WAVES) {
     const int gg = i / D, d = i % D;
-    float M = -INFINITY;
+    float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mlbuf[(w * 16 + gg) * 2]);
+    for (int w = 0; w < WAVES; ++w) Mx = fmaxf(Mx, mlbuf[(w * 16 + gg) * 2]);
     float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
+    if (Mx != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
         const float mw = mlbuf[(w * 16 + gg) * 2];
         if (mw == -INFINITY) continue;
-        const float e = exp2f(mw - M);
+        const float e = exp2f(mw - Mx);
         num += e * reinterpret_cast<float*>(lds + w * WAVE_LDS)[gg * ACC_STRIDE + d];
         den += e * mlbuf[(w * 16 + gg) * 2 + 1];
       }
@@ -366,7 +424,7 @@ __global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams 
       const size_t pi = (head0 + gg) * p.num_partitions + part;
       p.ws_acc[pi * D + d] = num;
       if (d == 0) {
-        p.ws_m[pi] = M;
+        p.ws_m[pi] = Mx;
         p.ws_l[pi] = den;
       }
     }
@@ -385,7 +443,7 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
   __shared__ float qs[MAXG * D];
   __shared__ float sc[MAXG * CH];
   __shared__ float mrow[MAXG], lrow[MAXG], arow[MAXG];
-  const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int kvh = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int L = clamp_len(p.seq_lens[s], p.mbs);
@@ -603,7 +661,7 @@ static int launch_simple(const AttnParams& p, dim3 grid, hipStream_t st) {
 
 int launch_paged_attn_partition(const AttnArgs& a) {
   const AttnParams p = make_params(a);
-  const dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
+  const dim3 grid(a.num_kv_heads, a.num_partitions, a.num_seqs);
   hipStream_t st = (hipStream_t)a.stream;
   const int D = a.head_dim;
   if (a.num_seqs == 0) return hipSuccess;
