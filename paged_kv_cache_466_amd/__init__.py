@@ -3,7 +3,7 @@
 Argument marshalling only: every operation runs in the HIP library through its
 C ABI (``include/pkv.h``).  torch supplies device memory and the current
 stream.  Importing this package fails if the library has not been built
-(``python -m paged_kv_cache_466_amd.build``); there is no fallback.
+(``python paged_kv_cache_466_amd/build.py``); there is no fallback.
 """
 
 import ctypes
@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libpkv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"libpkv.so not found at {LIB_PATH}: build it with `python -m paged_kv_cache_466_amd.build`")
+        f"libpkv.so not found at {LIB_PATH}: build it with `python paged_kv_cache_466_amd/build.py`")
 lib = ctypes.CDLL(LIB_PATH)
 
 # pkv_dtype

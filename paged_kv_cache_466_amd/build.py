@@ -1,6 +1,6 @@
 """Builds libpkv.so (HIP kernels + C ABI + host pool) for gfx950 with hipcc.
 
-Usage: ``python -m paged_kv_cache_466_amd.build`` (or ``build()``).  The
+Usage: ``python paged_kv_cache_466_amd/build.py`` (or ``build()``).  The
 library lands in ``paged_kv_cache_466_amd/_lib/libpkv.so``.  Every call
 recompiles from source.
 """
