@@ -115,9 +115,10 @@ int pkv_paged_attn_num_partitions(int num_seqs, int num_kv_heads, int max_seq_le
 int pkv_paged_attn_partition_size(int num_seqs, int num_kv_heads, int max_seq_len, int block_size);
 
 /*
- * Bytes of scratch pkv_paged_attn_decode needs: fp32 partial results
- * (running max m, sum l and unnormalised accumulator acc[head_dim]) per
- * (sequence, query head, partition).  0 when a single pass suffices.
+ * Bytes of scratch pkv_paged_attn_decode needs: one fp32 partial record per
+ * (sequence, KV head, partition) holding the group's unnormalised
+ * accumulators acc[G][head_dim], running maxima m[16] and softmax sums
+ * l[16] (G = num_q_heads / num_kv_heads).  0 when a single pass suffices.
  * max_seq_len must be max_blocks_per_seq * block_size of the later call.
  */
 size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
@@ -146,8 +147,8 @@ size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_
  *           partial results to the workspace and a merge kernel combines them
  *           by log-sum-exp.
  * workspace: device scratch of at least pkv_paged_attn_workspace_bytes(...)
- *           bytes (may be NULL when that is 0).  Its contents on entry do not
- *           matter and are undefined on exit.
+ *           bytes, 128-byte aligned (may be NULL when that is 0).  Its
+ *           contents on entry do not matter and are undefined on exit.
  * Calls on the same stream that share a workspace are ordered; calls on
  * different streams must not share one.
  */

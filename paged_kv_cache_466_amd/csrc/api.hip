@@ -39,14 +39,10 @@ static pkv_status hip_status(int err, const char* where) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int num_partitions) {
-  const size_t n = (size_t)num_seqs * num_q_heads * num_partitions;
-  WsLayout w;
-  w.m_off = 0;
-  w.l_off = align256(n * sizeof(float));
-  w.acc_off = w.l_off + align256(n * sizeof(float));
-  w.total = w.acc_off + align256(n * head_dim * sizeof(float));
-  return w;
+size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int num_partitions) {
+  const size_t records = (size_t)num_seqs * num_kv_heads * num_partitions;
+  const int G = num_q_heads / num_kv_heads;
+  return align256(records * partial_record_floats(G, head_dim) * sizeof(float));
 }
 
 static bool check_env() {
@@ -96,7 +92,8 @@ extern "C" size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, 
                                                  int max_seq_len, int partition_size) {
   const int np = pkv_paged_attn_num_partitions(num_seqs, num_kv_heads, max_seq_len, 16, partition_size);
   if (np <= 1 || num_seqs <= 0) return 0;
-  return workspace_layout(num_seqs, num_q_heads, head_dim, np).total;
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return 0;
+  return workspace_total(num_seqs, num_q_heads, num_kv_heads, head_dim, np);
 }
 
 extern "C" pkv_status pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
@@ -183,16 +180,13 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
   if (!a.out || !a.seq_lens) return fail(PKV_EINVAL, "%s: null pointer argument", who);
   if (need_inputs && (!a.query || !a.k_cache || !a.v_cache || !a.block_tables))
     return fail(PKV_EINVAL, "%s: null pointer argument", who);
-  a.ws_m = a.ws_l = a.ws_acc = nullptr;
+  a.ws = nullptr;
   if (a.num_partitions > 1) {
-    const WsLayout w = workspace_layout(a.num_seqs, a.num_q_heads, a.head_dim, a.num_partitions);
-    if (!workspace || workspace_bytes < w.total)
-      return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, w.total, workspace_bytes);
-    if (((uintptr_t)workspace) & 15) return fail(PKV_EINVAL, "%s: workspace must be 16-byte aligned", who);
-    char* base = (char*)workspace;
-    a.ws_m = (float*)(base + w.m_off);
-    a.ws_l = (float*)(base + w.l_off);
-    a.ws_acc = (float*)(base + w.acc_off);
+    const size_t total = workspace_total(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.num_partitions);
+    if (!workspace || workspace_bytes < total)
+      return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, total, workspace_bytes);
+    if (((uintptr_t)workspace) & 127) return fail(PKV_EINVAL, "%s: workspace must be 128-byte aligned", who);
+    a.ws = (float*)workspace;
   }
   return PKV_OK;
 }

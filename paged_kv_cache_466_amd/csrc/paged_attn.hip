@@ -1,25 +1,33 @@
 // Paged decode attention for gfx950.
 //
-// One workgroup per (KV partition, KV head, sequence).  The workgroup walks
-// the partition's physical blocks through the sequence's block table, in
-// logical order ("Chapter 18", "How PagedAttention Works"; Learning-AI topic
-// t13_4, block table; "KV Cache Engineering", section 10), computes the
-// grouped query heads' scores against each block's keys (GQA, "KV Cache
-// Engineering" section 1: the G = Hq/Hkv query heads of a group read the
-// same KV head), keeps an online softmax, and accumulates P.V.  Partitions
-// either write the final output (one partition per sequence) or fp32
-// partials (m, l, acc) that a merge kernel combines by log-sum-exp.
+// The decode walks each sequence's physical blocks through its block table,
+// in logical order ("Chapter 18", "How PagedAttention Works"; Learning-AI
+// topic t13_4, block table; "KV Cache Engineering", section 10), scores the
+// grouped query heads against each block's keys (GQA, "KV Cache Engineering"
+// section 1: the G = Hq/Hkv query heads of a group read the same KV head),
+// keeps an online softmax and accumulates P.V.  The tokens of a sequence are
+// split into partitions of partition_size tokens; a partition either writes
+// the final output (one partition per sequence) or fp32 partials (m, l, acc)
+// that a merge kernel combines by log-sum-exp.
 //
-// Two kernels:
-//  * paged_attn_mfma_kernel - bf16 / f16 caches and INT8 / FP8-E4M3 codes
-//    (converted to the query's 16-bit type in registers).  Per 16-token block
-//    and wave: S^T = K Q^T on v_mfma_f32_16x16x32 (K rows go straight from
-//    HBM into the A operand; the query group, padded to 16 heads, is the B
-//    operand), then out^T += V^T P^T on v_mfma_f32_16x16x16 where the score
-//    tile is already in the B-operand layout and V^T is read from an LDS
-//    copy of the block with ds_read_b64_tr_b16.
+// Kernels:
+//  * paged_attn_wave_kernel - bf16 / f16 caches and INT8 / FP8-E4M3 codes
+//    (converted to the query's 16-bit type in registers).  One wave per
+//    (partition, KV head, sequence); the waves never synchronise.  Per
+//    16-token block: S^T = K Q^T on v_mfma_f32_16x16x32 (K rows go straight
+//    from HBM into the A operand; the query group, padded to 16 heads, is the
+//    B operand), then out^T += V^T P^T on v_mfma_f32_16x16x16, where the
+//    score tile already has the B-operand layout and V^T is read from an LDS
+//    copy of the block with the transposing ds_read_b64_tr_b16.  Blocks are
+//    loaded with buffer loads into a ring of DEPTH register tiles, so DEPTH-1
+//    blocks are in flight while one computes.  Rows outside the kept range
+//    and tiles past the end are given an out-of-range buffer offset: the
+//    hardware returns zeros for them without touching memory, which both
+//    masks poisoned slots (no 0 * NaN in the MFMA) and keeps the ring
+//    branch-free.
 //  * paged_attn_simple_kernel - fp32 caches (and any group size): scores in
 //    LDS, plain fp32 FMAs.  Exact fp32 arithmetic, for the fp32 path.
+//  * paged_attn_merge_kernel - log-sum-exp combine of the partials.
 //
 // Scores are kept in the log2 domain: s2 = (q.k) * sm_scale * log2(e), so
 // exp(s - m) = exp2(s2 - m2).
@@ -44,9 +52,8 @@ struct AttnParams {
   const float* v_scales;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* ws_m;
-  float* ws_l;
-  float* ws_acc;
+  float* ws;            // partial records (see AttnArgs)
+  int rec_floats;       // floats per record
   int mbs, num_q_heads, num_kv_heads, num_blocks;
   int partition_size, num_partitions;
   int sink, window;
@@ -59,18 +66,10 @@ __device__ __forceinline__ int clamp_len(int L, int mbs) {
 }
 
 // Is logical token t taken into attention for a sequence of length L?
+// (Evaluated without branches: bitwise, not short-circuit, operators.)
 __device__ __forceinline__ bool kept(int t, int L, int sink, int window) {
-  if (t >= L) return false;
-  if (sink == 0 && window == 0) return true;
-  return t < sink || t >= L - window;
-}
-
-// Does block lb (tokens 16lb .. 16lb+15) hold at least one kept token?
-__device__ __forceinline__ bool block_needed(int lb, int L, int sink, int window) {
-  const int t0 = lb * kBS;
-  if (t0 >= L) return false;
-  if (sink == 0 && window == 0) return true;
-  return t0 < sink || t0 + kBS - 1 >= L - window;
+  const bool all = (sink | window) == 0;
+  return (t < L) & (all | (t < sink) | (t >= L - window));
 }
 
 __device__ __forceinline__ int table_entry(const AttnParams& p, int s, int lb) {
@@ -79,8 +78,21 @@ __device__ __forceinline__ int table_entry(const AttnParams& p, int s, int lb) {
   return (pb < 0 || pb >= p.num_blocks) ? 0 : pb;
 }
 
+// Raw buffer resource over `nbytes` bytes from `base` (gfx9 descriptor word 3).
+// A load whose offset + size exceeds nbytes returns zeros and reads nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+constexpr int kOutOfRange = 0x40000000;    // buffer offset that is always out of range
+
 // ===========================================================================
-// MFMA kernel
+// Wave kernel
 // ===========================================================================
 
 // 16-bit MFMA element type of the query (bf16 or f16) and the converted KV.
@@ -95,6 +107,12 @@ template <> struct Mfma<BF16> {
   }
   __device__ static uint32_t pack2(float x, float y) {
     return (uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(y) << 16);
+  }
+  // sum of the two packed values
+  __device__ static float sum2(uint32_t w) { return __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u); }
+  // two FP8-E4M3 codes (byte pair `hi` of w) -> two values, exactly
+  template <bool HI> __device__ static uint32_t fp8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   }
   __device__ static shortx4 tr_read(const void* lds) {
     bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -115,38 +133,50 @@ template <> struct Mfma<F16> {
   __device__ static uint32_t pack2(float x, float y) {
     return (uint32_t)f32_to_f16(x) | ((uint32_t)f32_to_f16(y) << 16);
   }
+  __device__ static float sum2(uint32_t w) { return f16_to_f32(w & 0xFFFFu) + f16_to_f32(w >> 16); }
+  template <bool HI> __device__ static uint32_t fp8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
   __device__ static shortx4 tr_read(const void* lds) {
     fp16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4*)(lds));
     return __builtin_bit_cast(shortx4, v);
   }
 };
 
-template <typename QT>
-__device__ __forceinline__ uint32_t pack_q(float a, float b) { return Mfma<QT>::pack2(a, b); }
-
 // 8 codes -> 8 elements of the query's 16-bit type, exactly (every INT8 and
 // FP8-E4M3 value is a bf16 and an f16 value).
 template <typename QT, typename KVT>
-__device__ __forceinline__ uint4 to16(const uint2& c) {
-  float f[8];
+__device__ __forceinline__ uint4 to16(uint32_t w0, uint32_t w1) {
+  typedef Mfma<QT> M;
   if constexpr (std::is_same<KVT, I8>::value) {
-    const uint32_t w[2] = {c.x, c.y};
+    float f[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) f[4 * i + b] = (float)(int8_t)((w[i] >> (8 * b)) & 0xFF);
-  } else {
-    const uint32_t w[2] = {c.x, c.y};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-      floatx2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-      f[4 * i] = lo[0]; f[4 * i + 1] = lo[1]; f[4 * i + 2] = hi[0]; f[4 * i + 3] = hi[1];
+    for (int b = 0; b < 4; ++b) {
+      f[b] = (float)(int8_t)((w0 >> (8 * b)) & 0xFF);
+      f[4 + b] = (float)(int8_t)((w1 >> (8 * b)) & 0xFF);
     }
+    return make_uint4(M::pack2(f[0], f[1]), M::pack2(f[2], f[3]), M::pack2(f[4], f[5]), M::pack2(f[6], f[7]));
+  } else {
+    return make_uint4(M::template fp8x2<false>(w0), M::template fp8x2<true>(w0), M::template fp8x2<false>(w1),
+                      M::template fp8x2<true>(w1));
   }
-  return make_uint4(pack_q<QT>(f[0], f[1]), pack_q<QT>(f[2], f[3]), pack_q<QT>(f[4], f[5]),
-                    pack_q<QT>(f[6], f[7]));
 }
+
+template <typename KVT, int D>
+struct WaveCfg {
+  static constexpr bool kCodes = KVT::bytes == 1;
+  static constexpr int NC = D / 32;                    // q.K MFMAs per block (k = 32)
+  static constexpr int NN = D / 16;                    // P.V MFMAs per block (n = 16)
+  static constexpr int ROW_BYTES = D * KVT::bytes;     // one token row of one KV head
+  static constexpr int KCH = kCodes ? NC / 2 : NC;     // 16-byte K loads per lane per block
+  static constexpr int LANES_PER_ROW = ROW_BYTES / 16;
+  static constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+  static constexpr int VCH = kBS / ROWS_PER_PASS;      // 16-byte V loads per lane per block
+  static constexpr int STAGE_VGPRS = 4 * (KCH + VCH);
+  static constexpr int DEPTH = STAGE_VGPRS >= 32 ? 4 : 8;   // ring of register tiles
+  static constexpr int VROW = D * 2 + 16;              // LDS bytes per staged V row (16-bit, padded)
+  static constexpr int VSTAGE = kBS * VROW;            // one staged V block
+};
 
 // d-offset (elements) of the 8-element k-chunk that lane group `kg` feeds to
 // MFMA number `c` of the q.K product.  Any assignment works as long as K and
@@ -159,114 +189,119 @@ __device__ __forceinline__ int qk_doff(int c, int kg) {
   else return (D / 4) * kg + 8 * c;
 }
 
-template <typename QT, typename KVT, int D, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams p) {
-  constexpr int NC = D / 32;                 // q.K MFMAs per block (k = 32)
-  constexpr int NN = D / 16;                 // P.V MFMAs per block (n = 16)
-  constexpr int VROW = D * 2 + 16;           // LDS bytes per staged V row (16-bit, padded)
-  constexpr int ACC_STRIDE = D + 4;          // floats per head row of the merge buffer
-  constexpr int WAVE_LDS = 16 * ACC_STRIDE * 4;
-  static_assert(kBS * VROW <= WAVE_LDS, "V staging must fit the per-wave region");
-  constexpr bool kCodes = KVT::bytes == 1;
-  constexpr int KCH = kCodes ? NC / 2 : NC;            // 16-byte K loads per lane per block
-  constexpr int ROW_BYTES = D * KVT::bytes;
-  constexpr int LANES_PER_ROW = ROW_BYTES / 16;
-  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
-  constexpr int VCH = kBS / ROWS_PER_PASS;             // 16-byte V loads per lane per block
+template <typename QT, typename KVT, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_attn_wave_kernel(AttnParams p) {
+  typedef WaveCfg<KVT, D> C;
+  typedef Mfma<QT> M;
+  constexpr int NC = C::NC, NN = C::NN, KCH = C::KCH, VCH = C::VCH, DEPTH = C::DEPTH;
+  constexpr bool kCodes = C::kCodes;
   // Scores may exceed the running max by this much (log2 units) before the
   // accumulators are rescaled: probabilities stay below 2^8.
   constexpr float kSlack = 8.0f;
-  typedef Mfma<QT> M;
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[WAVES * WAVE_LDS + WAVES * 16 * 2 * 4];
-  // kvh fastest: the KV heads of one block are dispatched together, so the
-  // block's 16 x Hkv x D rows are read from HBM close together in time.
-  const int kvh = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint8_t vstage[2 * C::VSTAGE];
+  const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x;
   const int G = p.num_q_heads / p.num_kv_heads;
-  const int L = clamp_len(p.seq_lens[s], p.mbs);
+  const int g = lane & 15;       // query head in the group (column of S^T / out^T)
+  const int kg = lane >> 4;      // lane group: k-chunk of the operands, 4-row slab of outputs
   const bool single = p.num_partitions == 1;
   const int t_begin = part * p.partition_size;
-  const bool windowed = p.sink != 0 || p.window != 0;
+  const int lb_begin = t_begin / kBS;
+  const int part_blocks = p.partition_size / kBS;
+  const size_t head0 = (size_t)s * p.num_q_heads + kvh * G;
 
+  // block-table entries of this partition (lane i: entry i of the current
+  // 64-entry chunk), issued before anything waits
+  const int tab_end = min(lb_begin + part_blocks, p.mbs);
+  int chunk = 0;
+  int pbv = lb_begin + lane < tab_end ? table_entry(p, s, lb_begin + lane) : 0;
+
+  const int L = clamp_len(p.seq_lens[s], p.mbs);
   if (t_begin >= L) {
-    if (single && part == 0) {
-      // empty sequence: zeros
-      for (int i = threadIdx.x; i < G * D; i += 64 * WAVES)
-        store_out<QT>(p.out, ((size_t)s * p.num_q_heads + kvh * G) * D + i, 0.f);
+    if (single) {   // empty sequence: zeros
+      for (int i = lane; i < G * D; i += 64) store_out<QT>(p.out, head0 * D + i, 0.f);
     }
     return;
   }
-  const int t_end = min(t_begin + p.partition_size, L);
-  const int lb_begin = t_begin / kBS, lb_end = (t_end + kBS - 1) / kBS;
-
-  const int g = lane & 15;       // query head in the group (column of S^T / out^T)
-  const int kg = lane >> 4;      // lane group: k-chunk of the operands, 4-row slab of outputs
 
   // ---- query group as the B operand of S^T = K Q^T (zero rows for g >= G) --
   typename M::vec8 qop[NC];
-  {
-    const size_t qrow = ((size_t)s * p.num_q_heads + kvh * G + g) * D;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (g < G) w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + qrow +
-                                                    qk_doff<KVT, D>(c, kg));
-      qop[c] = __builtin_bit_cast(typename M::vec8, w);
-    }
+  for (int c = 0; c < NC; ++c) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (g < G)
+      w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + (head0 + g) * D +
+                                          qk_doff<KVT, D>(c, kg));
+    qop[c] = __builtin_bit_cast(typename M::vec8, w);
   }
 
-  // ---- this wave's blocks: lb = first + j * WAVES, j < nwb ------------------
-  const int first = lb_begin + wave;
-  const int nwb = first < lb_end ? (lb_end - first + WAVES - 1) / WAVES : 0;
-  // lane i holds the table entry of wave block (chunk * 64 + i)
-  int chunk = 0;
-  int pbv = lane < nwb ? table_entry(p, s, first + lane * WAVES) : 0;
-
-  auto block_needed_j = [&](int j) { return block_needed(first + j * WAVES, L, p.sink, p.window); };
-  auto next_needed = [&](int j) {
-    while (j < nwb && !block_needed_j(j)) ++j;
-    return j;
-  };
-  auto entry = [&](int j) {
-    if ((j >> 6) != chunk) {               // wave-uniform; once per 64 blocks
-      chunk = j >> 6;
-      const int jj = chunk * 64 + lane;
-      pbv = jj < nwb ? table_entry(p, s, first + jj * WAVES) : 0;
-    }
-    return __builtin_amdgcn_readlane(pbv, j & 63);
+  // ---- blocks this partition reads: [a0, a1) then [b0, b1) ----------------
+  const int t_end = min(t_begin + p.partition_size, L);
+  const int lb_end = (t_end + kBS - 1) / kBS;
+  const bool windowed = p.sink != 0 || p.window != 0;
+  int a1 = lb_end, b0 = lb_end;
+  if (windowed) {
+    const int sink_end = min(lb_end, (p.sink + kBS - 1) / kBS);   // blocks holding a sink token
+    a1 = max(lb_begin, sink_end);
+    b0 = p.window > 0 ? min(lb_end, max(max(lb_begin, max(0, L - p.window) / kBS), a1)) : lb_end;
+  }
+  const int n_a = a1 - lb_begin;
+  const int n_need = n_a + (lb_end - b0);
+  auto block_of = [&](int j) { return j < n_a ? lb_begin + j : b0 + (j - n_a); };
+  // every token of block lb is kept
+  auto block_full = [&](int lb) {
+    const int t0 = lb * kBS;
+    return (t0 + kBS <= L) & (!windowed | (t0 + kBS <= p.sink) | (t0 >= L - p.window));
   };
 
   struct Tile {
     uint4 k[KCH];
     uint4 v[VCH];
-    int pb;
     float ks, vs;
   };
-  const size_t row_elems = (size_t)p.num_kv_heads * D;   // elements between token rows
+  const int row_stride = p.num_kv_heads * C::ROW_BYTES;        // bytes between token rows
+  const int krow = lane & 15;
+  const int kcol = kCodes ? (D / 4) * kg : 16 * kg;            // bytes
+  const int k_off = krow * row_stride + kcol;
+  int v_off[VCH], v_row[VCH];
+#pragma unroll
+  for (int ps = 0; ps < VCH; ++ps) {
+    v_row[ps] = ps * C::ROWS_PER_PASS + lane / C::LANES_PER_ROW;
+    v_off[ps] = v_row[ps] * row_stride + (lane % C::LANES_PER_ROW) * 16;
+  }
+  const int tile_bytes = (kBS - 1) * row_stride + C::ROW_BYTES;
+
   auto load_tile = [&](Tile& t, int j) {
-    const int pb = entry(j);
-    t.pb = pb;
-    const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * D;   // element offset of row 0
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_cache) +
-                           (tile + (size_t)(lane & 15) * row_elems) * KVT::bytes;
-    if constexpr (!kCodes) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kbase + qk_doff<KVT, D>(c, kg) * 2);
-    } else {
-#pragma unroll
-      for (int c2 = 0; c2 < KCH; ++c2) t.k[c2] = *reinterpret_cast<const uint4*>(kbase + (D / 4) * kg + 16 * c2);
+    const bool valid = j < n_need;
+    const int lb = valid ? block_of(j) : lb_begin;
+    const int e = lb - lb_begin;
+    if ((e >> 6) != chunk) {             // wave-uniform; once per 64 blocks
+      chunk = e >> 6;
+      const int lbe = lb_begin + chunk * 64 + lane;
+      pbv = lbe < tab_end ? table_entry(p, s, lbe) : 0;
     }
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_cache) + tile * KVT::bytes;
+    const int pb = __builtin_amdgcn_readlane(pbv, e & 63);
+    const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * C::ROW_BYTES;
+    const int nbytes = valid ? tile_bytes : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(p.k_cache) + tile, nbytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v_cache) + tile, nbytes);
+    const int t0 = lb * kBS;
+    const bool full = block_full(lb);
+    const int ko = (full | kept(t0 + krow, L, p.sink, p.window)) ? k_off : kOutOfRange;
 #pragma unroll
-    for (int pass = 0; pass < VCH; ++pass) {
-      const int r = pass * ROWS_PER_PASS + lane / LANES_PER_ROW;
-      t.v[pass] = *reinterpret_cast<const uint4*>(vbase + (size_t)r * row_elems * KVT::bytes +
-                                                  (lane % LANES_PER_ROW) * 16);
+    for (int c = 0; c < KCH; ++c) t.k[c] = buf_load16(kr, ko + (kCodes ? 16 : 64) * c);
+#pragma unroll
+    for (int ps = 0; ps < VCH; ++ps) {
+      const int vo = (full | kept(t0 + v_row[ps], L, p.sink, p.window)) ? v_off[ps] : kOutOfRange;
+      t.v[ps] = buf_load16(vr, vo);
     }
     if constexpr (kCodes) {
-      t.ks = p.k_scales[(size_t)pb * p.num_kv_heads + kvh];
-      t.vs = p.v_scales[(size_t)pb * p.num_kv_heads + kvh];
+      // the scale row of this block: a 4-byte window at its own address
+      const size_t si = (size_t)pb * p.num_kv_heads + kvh;
+      t.ks = buf_load4(make_rsrc(p.k_scales + si, 4), 0);
+      t.vs = buf_load4(make_rsrc(p.v_scales + si, 4), 0);
     } else {
       t.ks = t.vs = 1.f;
     }
@@ -277,29 +312,22 @@ __global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams 
   floatx4 acc[NN];
 #pragma unroll
   for (int n = 0; n < NN; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
-  uint8_t* vstage = lds + wave * WAVE_LDS;
 
-  auto process = [&](const Tile& t, int j) {
-    const int lb = first + j * WAVES;
+  auto process = [&](const Tile& t, int j, uint8_t* vst) {
+    const int lb = block_of(j);
     const int t0 = lb * kBS;
-    // every token of the block is kept: no masking work
-    const bool full = t0 + kBS <= L && (!windowed || t0 + kBS <= p.sink || t0 >= L - p.window);
+    const bool full = block_full(lb);
 
-    // ---- V rows -> LDS (masked rows as zeros: 0 * NaN must not reach acc) --
+    // ---- V rows -> LDS (masked rows arrive as zeros) -----------------------
 #pragma unroll
-    for (int pass = 0; pass < VCH; ++pass) {
-      const int r = pass * ROWS_PER_PASS + lane / LANES_PER_ROW;
-      const int cchunk = lane % LANES_PER_ROW;
-      uint4 w = t.v[pass];
+    for (int ps = 0; ps < VCH; ++ps) {
+      const int cchunk = lane % C::LANES_PER_ROW;
       if constexpr (!kCodes) {
-        if (!full && !kept(t0 + r, L, p.sink, p.window)) w = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 16) = w;
+        *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 16) = t.v[ps];
       } else {
-        uint4 lo = to16<QT, KVT>(make_uint2(w.x, w.y));
-        uint4 hi = to16<QT, KVT>(make_uint2(w.z, w.w));
-        if (!full && !kept(t0 + r, L, p.sink, p.window)) lo = hi = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 32) = lo;
-        *reinterpret_cast<uint4*>(vstage + r * VROW + cchunk * 32 + 16) = hi;
+        *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32) = to16<QT, KVT>(t.v[ps].x, t.v[ps].y);
+        *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32 + 16) =
+            to16<QT, KVT>(t.v[ps].z, t.v[ps].w);
       }
     }
 
@@ -311,10 +339,9 @@ __global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams 
     } else {
 #pragma unroll
       for (int c2 = 0; c2 < KCH; ++c2) {
-        const uint4 lo = to16<QT, KVT>(make_uint2(t.k[c2].x, t.k[c2].y));
-        const uint4 hi = to16<QT, KVT>(make_uint2(t.k[c2].z, t.k[c2].w));
-        sacc = M::qk(__builtin_bit_cast(typename M::vec8, lo), qop[2 * c2], sacc);
-        sacc = M::qk(__builtin_bit_cast(typename M::vec8, hi), qop[2 * c2 + 1], sacc);
+        sacc = M::qk(__builtin_bit_cast(typename M::vec8, to16<QT, KVT>(t.k[c2].x, t.k[c2].y)), qop[2 * c2], sacc);
+        sacc = M::qk(__builtin_bit_cast(typename M::vec8, to16<QT, KVT>(t.k[c2].z, t.k[c2].w)), qop[2 * c2 + 1],
+                     sacc);
       }
     }
     const float factor = p.scale_log2 * t.ks;
@@ -341,92 +368,84 @@ __global__ __launch_bounds__(64 * WAVES) void paged_attn_mfma_kernel(AttnParams 
     }
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(sc[i] - m2);
-      lsum += pr[i];
-    }
+    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m2);
     // P^T as the B operand (tokens 4kg..4kg+3 of head g), V scale folded in
     const uint32_t p01 = M::pack2(pr[0] * t.vs, pr[1] * t.vs);
     const uint32_t p23 = M::pack2(pr[2] * t.vs, pr[3] * t.vs);
+    // the denominator sums the weights the MFMA uses (16-bit rounded), so
+    // they add up to one; with codes the V scale is not part of the weight
+    if constexpr (!kCodes) lsum += M::sum2(p01) + M::sum2(p23);
+    else lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const shortx4 pop = __builtin_bit_cast(shortx4, make_uint2(p01, p23));
 
     // ---- out^T += V^T P^T: V^T chunks through the transposing LDS read ----
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    {
-      // lane i of each 16-lane group reads row 4kg + i/4, columns 4(i%4)..+3
-      const uint8_t* rd = vstage + (4 * kg + (g >> 2)) * VROW + (g & 3) * 8;
+    // lane i of each 16-lane group reads row 4kg + i/4, columns 4(i%4)..+3
+    const uint8_t* rd = vst + (4 * kg + (g >> 2)) * C::VROW + (g & 3) * 8;
 #pragma unroll
-      for (int n = 0; n < NN; ++n) {
-        const shortx4 vop = M::tr_read(rd + n * 32);
-        acc[n] = M::pv(vop, pop, acc[n]);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int n = 0; n < NN; ++n) acc[n] = M::pv(M::tr_read(rd + n * 32), pop, acc[n]);
   };
 
-  // ---- main loop: block j+1's loads are in flight while block j computes --
+  // ---- main loop: a ring of DEPTH tiles; block j + DEPTH is requested as
+  // soon as block j's registers are free.  Loads past the end read nothing.
   {
-    Tile ta, tb;
-    int j = next_needed(0);
-    if (j < nwb) load_tile(ta, j);
-    while (j < nwb) {
-      int jn = next_needed(j + 1);
-      if (jn < nwb) load_tile(tb, jn);
-      process(ta, j);
-      j = jn;
-      if (j >= nwb) break;
-      jn = next_needed(j + 1);
-      if (jn < nwb) load_tile(ta, jn);
-      process(tb, j);
-      j = jn;
+    Tile ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], d);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int j0 = 0; j0 < n_need; j0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        if (j0 + d < n_need) process(ring[d], j0 + d, vstage + (d & 1) * C::VSTAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(ring[d], j0 + d + DEPTH);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
-  // ---- this wave's softmax state -> LDS; combine the waves -----------------
+  // ---- results -------------------------------------------------------------
+  // lane (g, kg) holds out[g][16n + 4kg + i], i = 0..3.  The accumulators go
+  // through LDS (the V staging area, idle now) so that every global store
+  // writes whole, contiguous 128-byte lines: scattered partial-line stores
+  // cost far more HBM time than their bytes.
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
-  float* accbuf = reinterpret_cast<float*>(lds + wave * WAVE_LDS);
-  float* mlbuf = reinterpret_cast<float*>(lds + WAVES * WAVE_LDS);
-  __syncthreads();   // every wave is done with its V staging area
+  constexpr int RSTRIDE = D + 4;                      // floats per padded LDS row
+  static_assert((16 * RSTRIDE + 32) * 4 <= 2 * C::VSTAGE, "result staging must fit the V staging area");
+  float* rl = reinterpret_cast<float*>(vstage);
+  const float scale_out = single ? (lsum > 0.f ? 1.f / lsum : 0.f) : 1.f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int n = 0; n < NN; ++n)
-    *reinterpret_cast<floatx4*>(accbuf + g * ACC_STRIDE + 16 * n + 4 * kg) = acc[n];
+  for (int n = 0; n < NN; ++n) *reinterpret_cast<floatx4*>(rl + g * RSTRIDE + 16 * n + 4 * kg) = acc[n] * scale_out;
   if (kg == 0) {
-    mlbuf[(wave * 16 + g) * 2] = m2;
-    mlbuf[(wave * 16 + g) * 2 + 1] = lsum;
+    rl[16 * RSTRIDE + g] = m2;
+    rl[16 * RSTRIDE + 16 + g] = lsum;
   }
-  __syncthreads();
-
-  const size_t head0 = (size_t)s * p.num_q_heads + kvh * G;
-  for (int i = threadIdx.x; i < G * D; i += 64 * WAVES) {
-    const int gg = i / D, d = i % D;
-    float Mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) Mx = fmaxf(Mx, mlbuf[(w * 16 + gg) * 2]);
-    float num = 0.f, den = 0.f;
-    if (Mx != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        const float mw = mlbuf[(w * 16 + gg) * 2];
-        if (mw == -INFINITY) continue;
-        const float e = exp2f(mw - Mx);
-        num += e * reinterpret_cast<float*>(lds + w * WAVE_LDS)[gg * ACC_STRIDE + d];
-        den += e * mlbuf[(w * 16 + gg) * 2 + 1];
-      }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (single) {
+    // G rows of D outputs, contiguous from head0: 8 elements per lane-store
+    constexpr int CPR = D / 8;
+    for (int c = lane; c < G * CPR; c += 64) {
+      const float* src = rl + (c / CPR) * RSTRIDE + (c % CPR) * 8;
+      const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
+      const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + head0 * D + c * 8) =
+          make_uint4(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]), M::pack2(hi[0], hi[1]), M::pack2(hi[2], hi[3]));
     }
-    if (single) {
-      store_out<QT>(p.out, (head0 + gg) * D + d, den > 0.f ? num / den : 0.f);
-    } else {
-      const size_t pi = (head0 + gg) * p.num_partitions + part;
-      p.ws_acc[pi * D + d] = num;
-      if (d == 0) {
-        p.ws_m[pi] = Mx;
-        p.ws_l[pi] = den;
-      }
+  } else {
+    // record of (s, kvh, part): acc[G][D], then m[16], l[16]
+    float* rec = p.ws + (((size_t)s * p.num_kv_heads + kvh) * p.num_partitions + part) * p.rec_floats;
+    constexpr int CPR = D / 4;
+    for (int c = lane; c < G * CPR + 8; c += 64) {
+      const float* src = c < G * CPR ? rl + (c / CPR) * RSTRIDE + (c % CPR) * 4 : rl + 16 * RSTRIDE + (c - G * CPR) * 4;
+      *reinterpret_cast<floatx4*>(rec + 4 * c) = *reinterpret_cast<const floatx4*>(src);
     }
   }
 }
@@ -542,40 +561,47 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
     if (single) {
       store_out<QT>(p.out, (head0 + gg) * D + d, den > 0.f ? acc[k] / den : 0.f);
     } else {
-      const size_t pi = (head0 + gg) * p.num_partitions + part;
-      p.ws_acc[pi * D + d] = acc[k];
+      float* rec = p.ws + (((size_t)s * p.num_kv_heads + kvh) * p.num_partitions + part) * p.rec_floats;
+      rec[gg * D + d] = acc[k];
       if (d == 0) {
-        p.ws_m[pi] = mrow[gg];
-        p.ws_l[pi] = den;
+        rec[G * D + gg] = mrow[gg];
+        rec[G * D + 16 + gg] = den;
       }
     }
   }
 }
 
 // ===========================================================================
-// Merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
-// One workgroup per (query head, sequence); 8 partition rows in flight, each
-// read by D/4 threads with 16-byte loads.
+// Merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over the
+// partitions p < ceil(L / partition_size); every such partition wrote its
+// record (m = -inf, l = 0, acc = 0 when it kept no token).  One workgroup
+// per (query head, sequence): the max first, then 8 partition rows at a time,
+// each read by D/4 threads with 16-byte loads, 4 rows per thread in flight.
 // ===========================================================================
 template <typename QT, int D>
-__global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const int32_t* seq_lens,
-                                                               const float* ws_m, const float* ws_l,
-                                                               const float* ws_acc, int num_q_heads,
-                                                               int num_partitions, int partition_size,
-                                                               int max_len) {
+__global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const int32_t* seq_lens, const float* ws,
+                                                               int rec_floats, int num_q_heads, int num_kv_heads,
+                                                               int num_partitions, int partition_size, int max_len) {
   constexpr int TPR = D / 4;               // threads per partition row
   constexpr int ROWS = 256 / TPR;
+  constexpr int U = 4;
   __shared__ float red[256];
   __shared__ floatx4 part_num[ROWS][TPR];
   __shared__ float part_den[ROWS];
   const int h = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x;
+  const int G = num_q_heads / num_kv_heads;
+  const int kvh = h / G, g = h % G;
   int L = seq_lens[s];
   L = L < 0 ? 0 : (L > max_len ? max_len : L);
   const int np = (L + partition_size - 1) / partition_size;
-  const size_t base = ((size_t)s * num_q_heads + h) * num_partitions;
+  // record of partition i: rec0 + i * rec_floats; acc row g, then m[16], l[16]
+  const float* rec0 = ws + ((size_t)s * num_kv_heads + kvh) * num_partitions * rec_floats;
+  const float* m_of = rec0 + (size_t)G * D + g;
+  const float* l_of = m_of + 16;
+  const float* a_of = rec0 + (size_t)g * D;
   float mx = -INFINITY;
-  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, ws_m[base + i]);
+  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, m_of[(size_t)i * rec_floats]);
   red[tid] = mx;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -587,13 +613,29 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
   floatx4 num = floatx4{0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (M != -INFINITY) {
-    for (int i = row; i < np; i += ROWS) {
-      const float mi = ws_m[base + i];
-      if (mi == -INFINITY) continue;
-      const float e = exp2f(mi - M);
-      const floatx4 a = *reinterpret_cast<const floatx4*>(ws_acc + (base + i) * D + 4 * c);
-      num += e * a;
-      den += e * ws_l[base + i];
+    int i = row;
+    for (; i + (U - 1) * ROWS < np; i += U * ROWS) {
+      float mi[U], li[U];
+      floatx4 a[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t r = (size_t)(i + u * ROWS) * rec_floats;
+        mi[u] = m_of[r];
+        li[u] = l_of[r];
+        a[u] = *reinterpret_cast<const floatx4*>(a_of + r + 4 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float e = exp2f(mi[u] - M);   // 0 for an empty partition
+        num += e * a[u];
+        den += e * li[u];
+      }
+    }
+    for (; i < np; i += ROWS) {
+      const size_t r = (size_t)i * rec_floats;
+      const float e = exp2f(m_of[r] - M);
+      num += e * *reinterpret_cast<const floatx4*>(a_of + r + 4 * c);
+      den += e * l_of[r];
     }
   }
   part_num[row][c] = num;
@@ -602,6 +644,7 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
   if (tid < TPR) {
     floatx4 n = floatx4{0.f, 0.f, 0.f, 0.f};
     float dn = 0.f;
+#pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       n += part_num[r][tid];
       dn += part_den[r];
@@ -625,9 +668,8 @@ static AttnParams make_params(const AttnArgs& a) {
   p.v_scales = a.v_scales;
   p.block_tables = a.block_tables;
   p.seq_lens = a.seq_lens;
-  p.ws_m = a.ws_m;
-  p.ws_l = a.ws_l;
-  p.ws_acc = a.ws_acc;
+  p.ws = a.ws;
+  p.rec_floats = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads, a.head_dim);
   p.mbs = a.max_blocks_per_seq;
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
@@ -640,17 +682,15 @@ static AttnParams make_params(const AttnArgs& a) {
   return p;
 }
 
-constexpr int kWaves = 4;
-
 template <typename QT, typename KVT, int D>
-static int launch_mfma(const AttnParams& p, dim3 grid, hipStream_t st) {
-  paged_attn_mfma_kernel<QT, KVT, D, kWaves><<<grid, 64 * kWaves, 0, st>>>(p);
+static int launch_wave(const AttnParams& p, dim3 grid, hipStream_t st) {
+  paged_attn_wave_kernel<QT, KVT, D><<<grid, 64, 0, st>>>(p);
   return hipGetLastError();
 }
 
 template <typename QT, typename KVT>
-static int launch_mfma_d(const AttnParams& p, int D, dim3 grid, hipStream_t st) {
-  return D == 64 ? launch_mfma<QT, KVT, 64>(p, grid, st) : launch_mfma<QT, KVT, 128>(p, grid, st);
+static int launch_wave_d(const AttnParams& p, int D, dim3 grid, hipStream_t st) {
+  return D == 64 ? launch_wave<QT, KVT, 64>(p, grid, st) : launch_wave<QT, KVT, 128>(p, grid, st);
 }
 
 template <typename QT, typename KVT, int D>
@@ -660,25 +700,28 @@ static int launch_simple(const AttnParams& p, dim3 grid, hipStream_t st) {
 }
 
 int launch_paged_attn_partition(const AttnArgs& a) {
+  if (a.num_seqs == 0) return hipSuccess;
   const AttnParams p = make_params(a);
-  const dim3 grid(a.num_kv_heads, a.num_partitions, a.num_seqs);
   hipStream_t st = (hipStream_t)a.stream;
   const int D = a.head_dim;
-  if (a.num_seqs == 0) return hipSuccess;
   if (a.kv_dtype == PKV_F32) {
+    const dim3 grid(a.num_kv_heads, a.num_partitions, a.num_seqs);
     return D == 64 ? launch_simple<F32, F32, 64>(p, grid, st) : launch_simple<F32, F32, 128>(p, grid, st);
   }
+  // partition fastest: consecutive workgroups (spread over the XCDs) read
+  // consecutive stretches of one sequence's blocks
+  const dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
   if (a.q_dtype == PKV_BF16) {
     switch (a.kv_dtype) {
-      case PKV_BF16: return launch_mfma_d<BF16, BF16>(p, D, grid, st);
-      case PKV_I8: return launch_mfma_d<BF16, I8>(p, D, grid, st);
-      default: return launch_mfma_d<BF16, FP8>(p, D, grid, st);
+      case PKV_BF16: return launch_wave_d<BF16, BF16>(p, D, grid, st);
+      case PKV_I8: return launch_wave_d<BF16, I8>(p, D, grid, st);
+      default: return launch_wave_d<BF16, FP8>(p, D, grid, st);
     }
   }
   switch (a.kv_dtype) {
-    case PKV_F16: return launch_mfma_d<F16, F16>(p, D, grid, st);
-    case PKV_I8: return launch_mfma_d<F16, I8>(p, D, grid, st);
-    default: return launch_mfma_d<F16, FP8>(p, D, grid, st);
+    case PKV_F16: return launch_wave_d<F16, F16>(p, D, grid, st);
+    case PKV_I8: return launch_wave_d<F16, I8>(p, D, grid, st);
+    default: return launch_wave_d<F16, FP8>(p, D, grid, st);
   }
 }
 
@@ -687,9 +730,10 @@ int launch_paged_attn_merge(const AttnArgs& a) {
   const dim3 grid(a.num_q_heads, a.num_seqs);
   hipStream_t st = (hipStream_t)a.stream;
   const int max_len = a.max_blocks_per_seq * a.block_size;
+  const int rec = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads, a.head_dim);
 #define PKV_MERGE(QT, D)                                                                               \
-  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.seq_lens, a.ws_m, a.ws_l, a.ws_acc,    \
-                                                      a.num_q_heads, a.num_partitions, a.partition_size, \
+  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.seq_lens, a.ws, rec, a.num_q_heads,          \
+                                                      a.num_kv_heads, a.num_partitions, a.partition_size, \
                                                       max_len)
   if (a.head_dim == 64) {
     if (a.q_dtype == PKV_F32) PKV_MERGE(F32, 64);

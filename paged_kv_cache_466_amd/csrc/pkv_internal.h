@@ -46,17 +46,19 @@ struct AttnArgs {
   int partition_size;  // resolved (never 0)
   int num_partitions;  // per sequence, from max_blocks_per_seq * block_size
   int sink_tokens, window_tokens;
-  float* ws_m;    // [S][Hq][P]
-  float* ws_l;    // [S][Hq][P]
-  float* ws_acc;  // [S][Hq][P][D]
+  // Partial results: one record per (sequence, KV head, partition), in that
+  // order (partition fastest).  A record holds acc[G][D] (unnormalised fp32
+  // accumulators of the group's query heads), then m[16] and l[16] (running
+  // max in the log2 domain and softmax denominator; entries >= G unused).
+  float* ws;
   void* stream;
 };
 
-// Workspace layout for given sizes: offsets (bytes) of m, l, acc and total.
-struct WsLayout {
-  size_t m_off, l_off, acc_off, total;
-};
-WsLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int num_partitions);
+// Floats in one partial record for group size G and head_dim D.
+inline size_t partial_record_floats(int G, int D) { return (size_t)G * D + 32; }
+
+// Bytes of workspace the split decode needs.
+size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int num_partitions);
 
 // Kernel launchers (defined in the .hip files).  They assume validated
 // arguments and return a hipError_t cast to int.
