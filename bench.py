@@ -162,7 +162,8 @@ def measure(w, steps, warmup, copies):
                                  window_tokens=w.window, kv_dtype=kvdt)
         if ev is not None:
             ev[1].record()
-        pkv.paged_attn_merge(out, r.lens, w.Hkv, max_len, ws, partition_size=psize)
+        pkv.paged_attn_merge(out, r.lens, w.Hkv, max_len, ws, partition_size=psize, sink_tokens=w.sink,
+                             window_tokens=w.window)
         if ev is not None:
             ev[2].record()
 

@@ -97,29 +97,34 @@ const char* pkv_version(void);
 /* ------------------------------------------------------------------------ */
 
 /*
- * Number of KV partitions the decode uses per sequence for a given bound on
- * the sequence length.  partition_size 0 lets the library choose (see
- * pkv_paged_attn_partition_size); otherwise it must be a positive multiple of
- * block_size.  Returns 0 on bad arguments.
+ * Number of KV partitions per sequence for a given bound on the sequence
+ * length: ceil(max_seq_len / partition_size).  partition_size 0 lets the
+ * library choose (see pkv_paged_attn_partition_size); otherwise it must be a
+ * positive multiple of block_size.  Returns 0 on bad arguments.
  */
 int pkv_paged_attn_num_partitions(int num_seqs, int num_kv_heads, int max_seq_len,
                                   int block_size, int partition_size);
 
 /*
- * The partition size (tokens) the library picks when the caller passes 0,
- * given the launch shape.  One workgroup runs per (sequence, KV head,
- * partition); the choice keeps the grid large enough to fill 256 compute
- * units.  A result equal to or above max_seq_len means a single pass (no
- * partials, no merge).
+ * The partition size (tokens) the library picks when the caller passes 0.
+ * Partitions are the split granularity of the decode: a sequence's tokens
+ * are cut at multiples of partition_size, the decode hands each wave a run of
+ * consecutive partitions of one (sequence, KV head), sized from the actual
+ * lengths so that the waves fill the GPU evenly, and the partial results of
+ * the runs are combined by log-sum-exp.  A result equal to or above
+ * max_seq_len means a single pass (no partials, no merge).
  */
 int pkv_paged_attn_partition_size(int num_seqs, int num_kv_heads, int max_seq_len, int block_size);
 
 /*
- * Bytes of scratch pkv_paged_attn_decode needs: one fp32 partial record per
- * (sequence, KV head, partition) holding the group's unnormalised
- * accumulators acc[G][head_dim], running maxima m[16] and softmax sums
- * l[16] (G = num_q_heads / num_kv_heads).  0 when a single pass suffices.
- * max_seq_len must be max_blocks_per_seq * block_size of the later call.
+ * Bytes of scratch pkv_paged_attn_decode needs for fp32 partial records,
+ * each holding a query group's unnormalised accumulators acc[G][head_dim],
+ * running maxima m[16] and softmax sums l[16] (G = num_q_heads /
+ * num_kv_heads): one per wave for 16-bit and code caches, one per (sequence,
+ * KV head, partition) for fp32 caches; the larger of the two.  0 when no
+ * sequence can be split.  max_seq_len must be max_blocks_per_seq *
+ * block_size of the later call; the size depends on the current device's
+ * compute-unit count.
  */
 size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                       int head_dim, int max_seq_len, int partition_size);
@@ -142,10 +147,11 @@ size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_
  *           [P2] s.8).  k_scales/v_scales are ignored (may be NULL) otherwise.
  * head_dim: 64 or 128.  block_size: 16.  num_q_heads % num_kv_heads == 0.
  * partition_size: 0 = library's choice, else a positive multiple of
- *           block_size.  When the sequence bound max_blocks_per_seq *
- *           block_size exceeds the partition size, each partition writes
- *           partial results to the workspace and a merge kernel combines them
- *           by log-sum-exp.
+ *           block_size: the split granularity (see
+ *           pkv_paged_attn_partition_size).  When a sequence is split over
+ *           several waves, each wave writes a partial record covering whole
+ *           partitions to the workspace and a merge kernel combines them by
+ *           log-sum-exp; a sequence handled by one wave is written directly.
  * workspace: device scratch of at least pkv_paged_attn_workspace_bytes(...)
  *           bytes, 128-byte aligned (may be NULL when that is 0).  Its
  *           contents on entry do not matter and are undefined on exit.
@@ -168,9 +174,11 @@ pkv_status pkv_paged_attn_decode(
  * writes the partials to the workspace (or `out` directly when one partition
  * covers max_blocks_per_seq * block_size); pkv_paged_attn_merge then combines
  * them into `out`.  Calling partition then merge on one stream with the same
- * arguments is exactly pkv_paged_attn_decode.  With a single partition,
- * pkv_paged_attn_merge does nothing and returns PKV_OK.  For the merge,
- * max_seq_len is max_blocks_per_seq * block_size of the partition call.
+ * arguments is exactly pkv_paged_attn_decode.  When no sequence can be
+ * split, pkv_paged_attn_merge does nothing and returns PKV_OK.  For the
+ * merge, max_seq_len is max_blocks_per_seq * block_size of the partition
+ * call, and partition_size, sink_tokens and window_tokens must be the ones
+ * the partition call used (they fix how the work was split).
  */
 pkv_status pkv_paged_attn_partition(
     void* out, const void* query, int q_dtype,
@@ -185,6 +193,7 @@ pkv_status pkv_paged_attn_partition(
 pkv_status pkv_paged_attn_merge(
     void* out, int q_dtype, const int32_t* seq_lens, int num_seqs,
     int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len, int partition_size,
+    int sink_tokens, int window_tokens,
     const void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */

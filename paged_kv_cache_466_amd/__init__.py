@@ -47,7 +47,7 @@ _SIGS = {
     "pkv_paged_attn_workspace_bytes": ([_i, _i, _i, _i, _i, _i], _sz),
     "pkv_paged_attn_decode": (_ATTN, _i),
     "pkv_paged_attn_partition": (_ATTN, _i),
-    "pkv_paged_attn_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
+    "pkv_paged_attn_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
     "pkv_slot_mapping": ([_p, _p, _i, _p, _p, _i, _i, _i, _i, _p], _i),
     "pkv_reshape_and_cache": ([_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_copy_blocks": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p], _i),
@@ -188,13 +188,16 @@ def paged_attn_partition(out, query, k_cache, v_cache, block_tables, seq_lens, s
                       kv_dtype)
 
 
-def paged_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_size=0):
-    """Second pass of the decode (``pkv_paged_attn_merge``)."""
+def paged_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_size=0, sink_tokens=0,
+                     window_tokens=0):
+    """Second pass of the decode (``pkv_paged_attn_merge``); partition_size,
+    sink_tokens and window_tokens must match the partition call."""
     _contig(out, seq_lens, workspace)
     S, Hq, D = out.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pkv_paged_attn_merge(_ptr(out), _dtype(out), _ptr(seq_lens), S, Hq, num_kv_heads, D,
-                                    max_seq_len, partition_size, _ptr(workspace), ws_bytes, _stream(out)))
+                                    max_seq_len, partition_size, int(sink_tokens), int(window_tokens),
+                                    _ptr(workspace), ws_bytes, _stream(out)))
     return out
 
 

@@ -39,10 +39,46 @@ static pkv_status hip_status(int err, const char* where) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int num_partitions) {
-  const size_t records = (size_t)num_seqs * num_kv_heads * num_partitions;
+// Compute units of the current device (256 when none can be queried, e.g.
+// on a host without a GPU, so that sizes computed there match MI355X).
+static int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int decode_waves(int num_seqs, int num_kv_heads) {
+  constexpr int kWavesPerCU = 8;   // two waves per SIMD: the wave kernel's register budget
+  const long long runs = (long long)num_seqs * num_kv_heads;
+  const long long fill = (long long)kWavesPerCU * device_cu_count();
+  long long n = runs > fill ? runs : fill;
+  n = (n + num_kv_heads - 1) / num_kv_heads * num_kv_heads;   // whole chunk slots (one wave per KV head)
+  return n > 0x7FFFFFFF ? 0x7FFFFFFF / num_kv_heads * num_kv_heads : (int)n;
+}
+
+size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int num_partitions,
+                       int partition_size) {
+  if (num_partitions <= 1 || num_seqs <= 0) return 0;
   const int G = num_q_heads / num_kv_heads;
-  return align256(records * partial_record_floats(G, head_dim) * sizeof(float));
+  const size_t rec = partial_record_floats(G, head_dim) * sizeof(float);
+  // fp32 path: a record per (sequence, KV head, partition)
+  const size_t per_part = (size_t)num_seqs * num_kv_heads * num_partitions * rec;
+  // wave path: a record per wave, when a sequence can be split over waves
+  const size_t per_wave =
+      num_partitions > min_units_per_wave(partition_size) ? (size_t)decode_waves(num_seqs, num_kv_heads) * rec : 0;
+  return align256(per_part > per_wave ? per_part : per_wave);
 }
 
 static bool check_env() {
@@ -59,12 +95,13 @@ static int resolve_partition(int num_seqs, int num_kv_heads, int max_len, int bl
   if (psize > 0) return psize;
   (void)num_seqs;
   (void)num_kv_heads;
-  // One workgroup (4 waves) per 512-token partition keeps >= 8 blocks per
-  // wave and, for the long-context shapes, thousands of workgroups.  Shorter
-  // bounds run as one pass without partials.
+  // Bounds up to 512 tokens run as one pass without partials.  Longer ones
+  // are split at 64-token granularity: the decode gives each wave a stretch
+  // of at least 512 tokens of one sequence, and the fine granularity lets it
+  // balance the stretches across waves.
   const int single = ((max_len + block_size - 1) / block_size) * block_size;
   if (max_len <= 512) return single > 0 ? single : block_size;
-  return 512;
+  return 64;
 }
 
 }  // namespace pkv
@@ -93,7 +130,8 @@ extern "C" size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, 
   const int np = pkv_paged_attn_num_partitions(num_seqs, num_kv_heads, max_seq_len, 16, partition_size);
   if (np <= 1 || num_seqs <= 0) return 0;
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return 0;
-  return workspace_total(num_seqs, num_q_heads, num_kv_heads, head_dim, np);
+  const int ps = resolve_partition(num_seqs, num_kv_heads, max_seq_len, 16, partition_size);
+  return workspace_total(num_seqs, num_q_heads, num_kv_heads, head_dim, np, ps);
 }
 
 extern "C" pkv_status pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
@@ -180,9 +218,14 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
   if (!a.out || !a.seq_lens) return fail(PKV_EINVAL, "%s: null pointer argument", who);
   if (need_inputs && (!a.query || !a.k_cache || !a.v_cache || !a.block_tables))
     return fail(PKV_EINVAL, "%s: null pointer argument", who);
+  a.num_waves = decode_waves(a.num_seqs, a.num_kv_heads);
+  a.min_units = min_units_per_wave(a.partition_size);
+  a.may_split = a.num_partitions > a.min_units;
   a.ws = nullptr;
-  if (a.num_partitions > 1) {
-    const size_t total = workspace_total(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.num_partitions);
+  const bool needs_ws = a.q_dtype == PKV_F32 ? a.num_partitions > 1 : a.may_split;
+  if (needs_ws) {
+    const size_t total = workspace_total(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.num_partitions,
+                                         a.partition_size);
     if (!workspace || workspace_bytes < total)
       return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, total, workspace_bytes);
     if (((uintptr_t)workspace) & 127) return fail(PKV_EINVAL, "%s: workspace must be 128-byte aligned", who);
@@ -267,12 +310,14 @@ extern "C" pkv_status pkv_paged_attn_partition(PKV_ATTN_ARGS) {
 
 extern "C" pkv_status pkv_paged_attn_merge(void* out, int q_dtype, const int32_t* seq_lens, int num_seqs,
                                            int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
-                                           int partition_size, const void* workspace, size_t workspace_bytes,
-                                           void* stream) {
+                                           int partition_size, int sink_tokens, int window_tokens,
+                                           const void* workspace, size_t workspace_bytes, void* stream) {
   if (max_seq_len < 0 || max_seq_len % 16) return fail(PKV_EINVAL, "pkv_paged_attn_merge: bad max_seq_len");
+  if (sink_tokens < 0 || window_tokens < 0) return fail(PKV_EINVAL, "pkv_paged_attn_merge: negative sink/window");
   return run_attn(false, true, out, nullptr, q_dtype, nullptr, nullptr, q_dtype, nullptr, nullptr, nullptr,
                   max_seq_len / 16, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, 16, 0, 1.f,
-                  partition_size, 0, 0, const_cast<void*>(workspace), workspace_bytes, stream);
+                  partition_size, sink_tokens, window_tokens, const_cast<void*>(workspace), workspace_bytes,
+                  stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -54,7 +54,7 @@ struct AttnParams {
   const int32_t* seq_lens;
   float* ws;            // partial records (see AttnArgs)
   int rec_floats;       // floats per record
-  int mbs, num_q_heads, num_kv_heads, num_blocks;
+  int num_seqs, mbs, num_q_heads, num_kv_heads, num_blocks;
   int partition_size, num_partitions;
   int sink, window;
   float scale_log2;   // sm_scale * log2(e)
@@ -189,9 +189,124 @@ __device__ __forceinline__ int qk_doff(int c, int kg) {
   else return (D / 4) * kg + 8 * c;
 }
 
+// ===========================================================================
+// Split plan
+//
+// A "unit" is a partition (partition_size tokens from t = 0) that holds at
+// least one kept token.  A sequence with n units is cut into
+// k = ceil(n / Q) near-equal chunks of consecutive units.  One workgroup per
+// (chunk, group of up to 8 KV heads) runs one wave per KV head, so the waves
+// of a workgroup stream the same physical blocks at the same time (each
+// reads its head's rows of every block), and each wave writes one partial
+// record (or the final output when its sequence is a single chunk).  Q, the
+// largest chunk, is the smallest value that keeps the waves within NW:
+//   waves(Q) = Hkv * sum_s ceil(n_s / Q) <= Hkv * (U / Q + S_ne) <= NW
+// for Q >= Hkv * U / (NW - Hkv * S_ne), with U = sum_s n_s and S_ne the
+// sequences with a unit.  Chunks are numbered sequence-major.  The decode
+// and the merge compute the plan the same way from the lengths, so nothing
+// is stored between the kernels.
+// ===========================================================================
+struct SeqUnits {
+  int np;   // partitions covering the sequence
+  int a;    // units [0, a) hold sink tokens
+  int b0;   // units [a, n) are partitions b0 .. np-1 (window tokens)
+  int n;    // units
+};
+
+__device__ __forceinline__ SeqUnits seq_units(int L, int psize, int sink, int window) {
+  SeqUnits u;
+  u.np = (L + psize - 1) / psize;
+  if ((sink | window) == 0) {
+    u.a = u.b0 = u.n = u.np;
+    return u;
+  }
+  u.a = min(u.np, (min(sink, L) + psize - 1) / psize);
+  u.b0 = window > 0 ? min(u.np, max(u.a, max(0, L - window) / psize)) : u.np;
+  u.n = u.a + (u.np - u.b0);
+  return u;
+}
+__device__ __forceinline__ int unit_partition(const SeqUnits& u, int i) { return i < u.a ? i : u.b0 + (i - u.a); }
+
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int num_seqs, mbs, num_kv_heads, psize, sink, window;
+  int num_waves;      // NW
+  int min_units;      // Q never goes below this
+};
+
+__device__ __forceinline__ int lane_scan_incl(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Units per chunk.  Called by a whole wave; the result is wave-uniform.
+__device__ int plan_units_per_chunk(const PlanArgs& a, int lane) {
+  long long U = 0;
+  int s_ne = 0, nmax = 0;
+  for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
+    const int s = s0 + lane;
+    int n = 0;
+    if (s < a.num_seqs) n = seq_units(clamp_len(a.seq_lens[s], a.mbs), a.psize, a.sink, a.window).n;
+    const int incl = lane_scan_incl(n, lane);
+    U += __shfl(incl, 63, 64);
+    s_ne += __popcll(__ballot(n > 0));
+    nmax = max(nmax, n);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
+  const long long room = (long long)a.num_waves - (long long)a.num_kv_heads * s_ne;
+  long long Q = room > 0 ? ((long long)a.num_kv_heads * U + room - 1) / room : (long long)nmax;
+  if (Q > nmax) Q = nmax;                 // one chunk per run is the coarsest split
+  if (Q < a.min_units) Q = a.min_units;
+  return Q < 1 ? 1 : (int)Q;
+}
+
+struct ChunkInfo {
+  int s, c;        // sequence and chunk index within it (s = -1: past the end)
+  int chunks;      // chunks of this sequence (0 for an empty sequence)
+  int first;       // number of the sequence's first chunk
+};
+
+// Locates chunk number `target` (by_chunk) or the chunks of sequence
+// `target`.  Called by a whole wave; the result is wave-uniform.
+__device__ ChunkInfo plan_locate(const PlanArgs& a, int Q, int lane, bool by_chunk, int target) {
+  ChunkInfo r;
+  r.s = -1;
+  r.c = r.chunks = r.first = 0;
+  int base = 0;
+  for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
+    const int s = s0 + lane;
+    int k = 0;   // chunks of sequence s
+    if (s < a.num_seqs) {
+      const int n = seq_units(clamp_len(a.seq_lens[s], a.mbs), a.psize, a.sink, a.window).n;
+      k = (n + Q - 1) / Q;
+    }
+    const int incl = lane_scan_incl(k, lane);
+    const int lo = base + incl - k;
+    const bool hit = by_chunk ? (target >= lo && target < lo + k) : (s == target);
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int ln = __ffsll((long long)m) - 1;
+      r.s = s0 + ln;
+      r.chunks = __shfl(k, ln, 64);
+      r.first = __shfl(lo, ln, 64);
+      r.c = by_chunk ? target - r.first : 0;
+      return r;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return r;
+}
+
+constexpr int kMaxWavesPerGroup = 8;   // KV heads per workgroup
+
 template <typename QT, typename KVT, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-void paged_attn_wave_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
   typedef WaveCfg<KVT, D> C;
   typedef Mfma<QT> M;
   constexpr int NC = C::NC, NN = C::NN, KCH = C::KCH, VCH = C::VCH, DEPTH = C::DEPTH;
@@ -200,46 +315,58 @@ void paged_attn_wave_kernel(AttnParams p) {
   // accumulators are rescaled: probabilities stay below 2^8.
   constexpr float kSlack = 8.0f;
 
-  __shared__ __attribute__((aligned(16))) uint8_t vstage[2 * C::VSTAGE];
-  const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-  const int lane = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMaxWavesPerGroup * C::VSTAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int heads_per_group = blockDim.x >> 6;
+  const int kvh = blockIdx.y * heads_per_group + wave;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int g = lane & 15;       // query head in the group (column of S^T / out^T)
   const int kg = lane >> 4;      // lane group: k-chunk of the operands, 4-row slab of outputs
-  const bool single = p.num_partitions == 1;
-  const int t_begin = part * p.partition_size;
-  const int lb_begin = t_begin / kBS;
-  const int part_blocks = p.partition_size / kBS;
-  const size_t head0 = (size_t)s * p.num_q_heads + kvh * G;
+  uint8_t* vstage = lds + wave * C::VSTAGE;
+  if (kvh >= p.num_kv_heads) return;
 
-  // block-table entries of this partition (lane i: entry i of the current
-  // 64-entry chunk), issued before anything waits
-  const int tab_end = min(lb_begin + part_blocks, p.mbs);
-  int chunk = 0;
-  int pbv = lb_begin + lane < tab_end ? table_entry(p, s, lb_begin + lane) : 0;
-
-  const int L = clamp_len(p.seq_lens[s], p.mbs);
-  if (t_begin >= L) {
-    if (single) {   // empty sequence: zeros
-      for (int i = lane; i < G * D; i += 64) store_out<QT>(p.out, head0 * D + i, 0.f);
+  // an empty sequence gets zeros (the head-0 wave of chunk slot s does it)
+  {
+    const int zs = blockIdx.x;
+    if (kvh == 0 && zs < p.num_seqs && clamp_len(p.seq_lens[zs], p.mbs) == 0) {
+      for (int i = lane; i < p.num_q_heads * D; i += 64)
+        store_out<QT>(p.out, (size_t)zs * p.num_q_heads * D + i, 0.f);
     }
-    return;
   }
+
+  // the plan's results are wave-uniform; say so, so that everything derived
+  // from them stays in scalar registers
+  const int Q = __builtin_amdgcn_readfirstlane(plan_units_per_chunk(pa, lane));
+  const ChunkInfo ci = plan_locate(pa, Q, lane, true, blockIdx.x);
+  const int s = __builtin_amdgcn_readfirstlane(ci.s);
+  if (s < 0) return;
+  const int chunk = __builtin_amdgcn_readfirstlane(ci.c);
+  const int chunks = __builtin_amdgcn_readfirstlane(ci.chunks);
+  const bool single = chunks == 1;
+  const int rec_index = blockIdx.x * p.num_kv_heads + kvh;
+  const size_t head0 = (size_t)s * p.num_q_heads + kvh * G;
+  const int L = clamp_len(p.seq_lens[s], p.mbs);
+  const SeqUnits su = seq_units(L, p.partition_size, p.sink, p.window);
+  // the sequence's n units are cut into `chunks` near-equal pieces
+  const int i0 = (int)((long long)chunk * su.n / chunks), i1 = (int)((long long)(chunk + 1) * su.n / chunks);
+  const int t_begin = unit_partition(su, i0) * p.partition_size;
+  const int t_end = min((unit_partition(su, i1 - 1) + 1) * p.partition_size, L);
+  const int lb_begin = t_begin / kBS;
+  const int lb_end = (t_end + kBS - 1) / kBS;
 
   // ---- query group as the B operand of S^T = K Q^T (zero rows for g >= G) --
   typename M::vec8 qop[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    uint4 w = make_uint4(0, 0, 0, 0);
+    uint4 v = make_uint4(0, 0, 0, 0);
     if (g < G)
-      w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + (head0 + g) * D +
+      v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + (head0 + g) * D +
                                           qk_doff<KVT, D>(c, kg));
-    qop[c] = __builtin_bit_cast(typename M::vec8, w);
+    qop[c] = __builtin_bit_cast(typename M::vec8, v);
   }
 
-  // ---- blocks this partition reads: [a0, a1) then [b0, b1) ----------------
-  const int t_end = min(t_begin + p.partition_size, L);
-  const int lb_end = (t_end + kBS - 1) / kBS;
+  // ---- blocks this wave reads: [lb_begin, a1) then [b0, lb_end) ----------
   const bool windowed = p.sink != 0 || p.window != 0;
   int a1 = lb_end, b0 = lb_end;
   if (windowed) {
@@ -272,17 +399,19 @@ void paged_attn_wave_kernel(AttnParams p) {
     v_off[ps] = v_row[ps] * row_stride + (lane % C::LANES_PER_ROW) * 16;
   }
   const int tile_bytes = (kBS - 1) * row_stride + C::ROW_BYTES;
+  // this sequence's block-table row; entries are fetched 2*DEPTH blocks
+  // ahead as uniform loads, so by the time a tile load needs one it is older
+  // than every load still in flight and no wait stalls the ring
+  const __amdgpu_buffer_rsrc_t tab = make_rsrc(p.block_tables + (size_t)s * p.mbs, p.mbs * 4);
+  auto load_entry = [&](int j) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(tab, j < n_need ? block_of(j) * 4 : kOutOfRange, 0, 0);
+  };
 
-  auto load_tile = [&](Tile& t, int j) {
+  auto load_tile = [&](Tile& t, int j, int entry) {
     const bool valid = j < n_need;
     const int lb = valid ? block_of(j) : lb_begin;
-    const int e = lb - lb_begin;
-    if ((e >> 6) != chunk) {             // wave-uniform; once per 64 blocks
-      chunk = e >> 6;
-      const int lbe = lb_begin + chunk * 64 + lane;
-      pbv = lbe < tab_end ? table_entry(p, s, lbe) : 0;
-    }
-    const int pb = __builtin_amdgcn_readlane(pbv, e & 63);
+    int pb = __builtin_amdgcn_readfirstlane(entry);
+    pb = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the cache arrays
     const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * C::ROW_BYTES;
     const int nbytes = valid ? tile_bytes : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(p.k_cache) + tile, nbytes);
@@ -389,18 +518,28 @@ void paged_attn_wave_kernel(AttnParams p) {
   };
 
   // ---- main loop: a ring of DEPTH tiles; block j + DEPTH is requested as
-  // soon as block j's registers are free.  Loads past the end read nothing.
+  // soon as block j's registers are free, with its table entry fetched
+  // DEPTH steps earlier.  Loads past the end read nothing.
   {
     Tile ring[DEPTH];
+    int ent[DEPTH];
+    {
+      int first[DEPTH];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], d);
+      for (int d = 0; d < DEPTH; ++d) first[d] = load_entry(d);
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) ent[d] = load_entry(DEPTH + d);
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], d, first[d]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     for (int j0 = 0; j0 < n_need; j0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        if (j0 + d < n_need) process(ring[d], j0 + d, vstage + (d & 1) * C::VSTAGE);
+        if (j0 + d < n_need) process(ring[d], j0 + d, vstage);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(ring[d], j0 + d + DEPTH);
+        load_tile(ring[d], j0 + d + DEPTH, ent[d]);
+        ent[d] = load_entry(j0 + d + 2 * DEPTH);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -408,44 +547,50 @@ void paged_attn_wave_kernel(AttnParams p) {
 
   // ---- results -------------------------------------------------------------
   // lane (g, kg) holds out[g][16n + 4kg + i], i = 0..3.  The accumulators go
-  // through LDS (the V staging area, idle now) so that every global store
-  // writes whole, contiguous 128-byte lines: scattered partial-line stores
-  // cost far more HBM time than their bytes.
+  // through LDS (the wave's V staging area, idle now), 8 heads at a time, so
+  // that every global store writes whole, contiguous 128-byte lines.
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   constexpr int RSTRIDE = D + 4;                      // floats per padded LDS row
-  static_assert((16 * RSTRIDE + 32) * 4 <= 2 * C::VSTAGE, "result staging must fit the V staging area");
+  static_assert((8 * RSTRIDE + 32) * 4 <= C::VSTAGE, "result staging must fit the V staging area");
   float* rl = reinterpret_cast<float*>(vstage);
   const float scale_out = single ? (lsum > 0.f ? 1.f / lsum : 0.f) : 1.f;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* rec = p.ws + (size_t)rec_index * p.rec_floats;   // acc[G][D], then m[16], l[16]
+  for (int h0 = 0; h0 < G; h0 += 8) {
+    const int nh = min(8, G - h0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (g >= h0 && g < h0 + 8) {
 #pragma unroll
-  for (int n = 0; n < NN; ++n) *reinterpret_cast<floatx4*>(rl + g * RSTRIDE + 16 * n + 4 * kg) = acc[n] * scale_out;
-  if (kg == 0) {
-    rl[16 * RSTRIDE + g] = m2;
-    rl[16 * RSTRIDE + 16 + g] = lsum;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (single) {
-    // G rows of D outputs, contiguous from head0: 8 elements per lane-store
-    constexpr int CPR = D / 8;
-    for (int c = lane; c < G * CPR; c += 64) {
-      const float* src = rl + (c / CPR) * RSTRIDE + (c % CPR) * 8;
-      const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
-      const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + head0 * D + c * 8) =
-          make_uint4(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]), M::pack2(hi[0], hi[1]), M::pack2(hi[2], hi[3]));
+      for (int n = 0; n < NN; ++n)
+        *reinterpret_cast<floatx4*>(rl + (g - h0) * RSTRIDE + 16 * n + 4 * kg) = acc[n] * scale_out;
     }
-  } else {
-    // record of (s, kvh, part): acc[G][D], then m[16], l[16]
-    float* rec = p.ws + (((size_t)s * p.num_kv_heads + kvh) * p.num_partitions + part) * p.rec_floats;
-    constexpr int CPR = D / 4;
-    for (int c = lane; c < G * CPR + 8; c += 64) {
-      const float* src = c < G * CPR ? rl + (c / CPR) * RSTRIDE + (c % CPR) * 4 : rl + 16 * RSTRIDE + (c - G * CPR) * 4;
-      *reinterpret_cast<floatx4*>(rec + 4 * c) = *reinterpret_cast<const floatx4*>(src);
+    if (h0 == 0 && kg == 0) {
+      rl[8 * RSTRIDE + g] = m2;
+      rl[8 * RSTRIDE + 16 + g] = lsum;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (single) {
+      // nh rows of D outputs, contiguous from head0 + h0: 8 elements per lane-store
+      constexpr int CPR = D / 8;
+      for (int c = lane; c < nh * CPR; c += 64) {
+        const float* src = rl + (c / CPR) * RSTRIDE + (c % CPR) * 8;
+        const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
+        const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (head0 + h0) * D + c * 8) = make_uint4(
+            M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]), M::pack2(hi[0], hi[1]), M::pack2(hi[2], hi[3]));
+      }
+    } else {
+      constexpr int CPR = D / 4;
+      for (int c = lane; c < nh * CPR; c += 64)
+        *reinterpret_cast<floatx4*>(rec + (size_t)h0 * D + 4 * c) =
+            *reinterpret_cast<const floatx4*>(rl + (c / CPR) * RSTRIDE + (c % CPR) * 4);
+      if (h0 == 0 && lane < 8)
+        *reinterpret_cast<floatx4*>(rec + (size_t)G * D + 4 * lane) =
+            *reinterpret_cast<const floatx4*>(rl + 8 * RSTRIDE + 4 * lane);
     }
   }
 }
@@ -572,14 +717,109 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 }
 
 // ===========================================================================
-// Merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over the
+// Merge of the wave kernel's records: for each (query head, sequence) that
+// was cut into several chunks, out = sum_c 2^(m_c - M) acc_c /
+// sum_c 2^(m_c - M) l_c over its records (one per chunk, in chunk order).
+// Sequences of one chunk were finished by their waves; empty sequences were
+// zeroed.  The first wave of the workgroup recomputes the split plan to
+// find the records; then 8 record rows at a time are read by D/4 threads with
+// 16-byte loads, 4 rows per thread in flight.
+// ===========================================================================
+template <typename QT, int D>
+__global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const float* ws, int rec_floats,
+                                                               int num_q_heads, PlanArgs pa) {
+  constexpr int TPR = D / 4;               // threads per record row
+  constexpr int ROWS = 256 / TPR;
+  constexpr int U = 4;
+  __shared__ float red[256];
+  __shared__ floatx4 part_num[ROWS][TPR];
+  __shared__ float part_den[ROWS];
+  __shared__ int sh_first, sh_chunks;
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int G = num_q_heads / pa.num_kv_heads;
+  const int kvh = h / G, g = h % G;
+  if (tid < 64) {
+    const int Q = plan_units_per_chunk(pa, tid);
+    const ChunkInfo ci = plan_locate(pa, Q, tid, false, s);
+    if (tid == 0) {
+      sh_first = ci.first;
+      sh_chunks = ci.chunks;
+    }
+  }
+  __syncthreads();
+  const int np = sh_chunks;
+  if (np <= 1) return;
+  // record of chunk c of this head: (first + c) * Hkv + kvh
+  const float* rec0 = ws + ((size_t)sh_first * pa.num_kv_heads + kvh) * rec_floats;
+  rec_floats *= pa.num_kv_heads;   // stride between the head's consecutive chunks
+  const float* m_of = rec0 + (size_t)G * D + g;
+  const float* l_of = m_of + 16;
+  const float* a_of = rec0 + (size_t)g * D;
+  float mx = -INFINITY;
+  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, m_of[(size_t)i * rec_floats]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  const int row = tid / TPR, c = tid % TPR;
+  floatx4 num = floatx4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (M != -INFINITY) {
+    int i = row;
+    for (; i + (U - 1) * ROWS < np; i += U * ROWS) {
+      float mi[U], li[U];
+      floatx4 a[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t r = (size_t)(i + u * ROWS) * rec_floats;
+        mi[u] = m_of[r];
+        li[u] = l_of[r];
+        a[u] = *reinterpret_cast<const floatx4*>(a_of + r + 4 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float e = exp2f(mi[u] - M);   // 0 for a chunk that kept no token
+        num += e * a[u];
+        den += e * li[u];
+      }
+    }
+    for (; i < np; i += ROWS) {
+      const size_t r = (size_t)i * rec_floats;
+      const float e = exp2f(m_of[r] - M);
+      num += e * *reinterpret_cast<const floatx4*>(a_of + r + 4 * c);
+      den += e * l_of[r];
+    }
+  }
+  part_num[row][c] = num;
+  if (c == 0) part_den[row] = den;
+  __syncthreads();
+  if (tid < TPR) {
+    floatx4 n = floatx4{0.f, 0.f, 0.f, 0.f};
+    float dn = 0.f;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      n += part_num[r][tid];
+      dn += part_den[r];
+    }
+    const size_t o = ((size_t)s * num_q_heads + h) * D + 4 * tid;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) store_out<QT>(out, o + k, dn > 0.f ? n[k] / dn : 0.f);
+  }
+}
+
+// ===========================================================================
+// Merge of the fp32 kernel's per-partition records: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over the
 // partitions p < ceil(L / partition_size); every such partition wrote its
 // record (m = -inf, l = 0, acc = 0 when it kept no token).  One workgroup
 // per (query head, sequence): the max first, then 8 partition rows at a time,
 // each read by D/4 threads with 16-byte loads, 4 rows per thread in flight.
 // ===========================================================================
 template <typename QT, int D>
-__global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const int32_t* seq_lens, const float* ws,
+__global__ __launch_bounds__(256) void paged_attn_merge_units_kernel(void* out, const int32_t* seq_lens, const float* ws,
                                                                int rec_floats, int num_q_heads, int num_kv_heads,
                                                                int num_partitions, int partition_size, int max_len) {
   constexpr int TPR = D / 4;               // threads per partition row
@@ -670,6 +910,7 @@ static AttnParams make_params(const AttnArgs& a) {
   p.seq_lens = a.seq_lens;
   p.ws = a.ws;
   p.rec_floats = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads, a.head_dim);
+  p.num_seqs = a.num_seqs;
   p.mbs = a.max_blocks_per_seq;
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
@@ -682,15 +923,33 @@ static AttnParams make_params(const AttnArgs& a) {
   return p;
 }
 
+static PlanArgs make_plan(const AttnArgs& a) {
+  PlanArgs pa;
+  pa.seq_lens = a.seq_lens;
+  pa.num_seqs = a.num_seqs;
+  pa.mbs = a.max_blocks_per_seq;
+  pa.num_kv_heads = a.num_kv_heads;
+  pa.psize = a.partition_size;
+  pa.sink = a.sink_tokens;
+  pa.window = a.window_tokens;
+  pa.num_waves = a.num_waves;
+  pa.min_units = a.min_units;
+  return pa;
+}
+
 template <typename QT, typename KVT, int D>
-static int launch_wave(const AttnParams& p, dim3 grid, hipStream_t st) {
-  paged_attn_wave_kernel<QT, KVT, D><<<grid, 64, 0, st>>>(p);
+static int launch_wave(const AttnParams& p, const PlanArgs& pa, hipStream_t st) {
+  // (chunk slot, group of up to 8 KV heads); one wave per KV head
+  const int per_group = pa.num_kv_heads < kMaxWavesPerGroup ? pa.num_kv_heads : kMaxWavesPerGroup;
+  const int groups = (pa.num_kv_heads + per_group - 1) / per_group;
+  const dim3 grid(pa.num_waves / pa.num_kv_heads, groups);
+  paged_attn_wave_kernel<QT, KVT, D><<<grid, 64 * per_group, 0, st>>>(p, pa);
   return hipGetLastError();
 }
 
 template <typename QT, typename KVT>
-static int launch_wave_d(const AttnParams& p, int D, dim3 grid, hipStream_t st) {
-  return D == 64 ? launch_wave<QT, KVT, 64>(p, grid, st) : launch_wave<QT, KVT, 128>(p, grid, st);
+static int launch_wave_d(const AttnParams& p, const PlanArgs& pa, int D, hipStream_t st) {
+  return D == 64 ? launch_wave<QT, KVT, 64>(p, pa, st) : launch_wave<QT, KVT, 128>(p, pa, st);
 }
 
 template <typename QT, typename KVT, int D>
@@ -701,47 +960,54 @@ static int launch_simple(const AttnParams& p, dim3 grid, hipStream_t st) {
 
 int launch_paged_attn_partition(const AttnArgs& a) {
   if (a.num_seqs == 0) return hipSuccess;
-  const AttnParams p = make_params(a);
+  AttnParams p = make_params(a);
   hipStream_t st = (hipStream_t)a.stream;
   const int D = a.head_dim;
   if (a.kv_dtype == PKV_F32) {
     const dim3 grid(a.num_kv_heads, a.num_partitions, a.num_seqs);
     return D == 64 ? launch_simple<F32, F32, 64>(p, grid, st) : launch_simple<F32, F32, 128>(p, grid, st);
   }
-  // partition fastest: consecutive workgroups (spread over the XCDs) read
-  // consecutive stretches of one sequence's blocks
-  const dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
+  const PlanArgs pa = make_plan(a);
   if (a.q_dtype == PKV_BF16) {
     switch (a.kv_dtype) {
-      case PKV_BF16: return launch_wave_d<BF16, BF16>(p, D, grid, st);
-      case PKV_I8: return launch_wave_d<BF16, I8>(p, D, grid, st);
-      default: return launch_wave_d<BF16, FP8>(p, D, grid, st);
+      case PKV_BF16: return launch_wave_d<BF16, BF16>(p, pa, D, st);
+      case PKV_I8: return launch_wave_d<BF16, I8>(p, pa, D, st);
+      default: return launch_wave_d<BF16, FP8>(p, pa, D, st);
     }
   }
   switch (a.kv_dtype) {
-    case PKV_F16: return launch_wave_d<F16, F16>(p, D, grid, st);
-    case PKV_I8: return launch_wave_d<F16, I8>(p, D, grid, st);
-    default: return launch_wave_d<F16, FP8>(p, D, grid, st);
+    case PKV_F16: return launch_wave_d<F16, F16>(p, pa, D, st);
+    case PKV_I8: return launch_wave_d<F16, I8>(p, pa, D, st);
+    default: return launch_wave_d<F16, FP8>(p, pa, D, st);
   }
 }
 
 int launch_paged_attn_merge(const AttnArgs& a) {
-  if (a.num_partitions <= 1 || a.num_seqs == 0) return hipSuccess;
+  if (a.num_seqs == 0) return hipSuccess;
   const dim3 grid(a.num_q_heads, a.num_seqs);
   hipStream_t st = (hipStream_t)a.stream;
-  const int max_len = a.max_blocks_per_seq * a.block_size;
   const int rec = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads, a.head_dim);
-#define PKV_MERGE(QT, D)                                                                               \
-  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.seq_lens, a.ws, rec, a.num_q_heads,          \
-                                                      a.num_kv_heads, a.num_partitions, a.partition_size, \
-                                                      max_len)
+  if (a.q_dtype == PKV_F32) {
+    if (a.num_partitions <= 1) return hipSuccess;
+    const int max_len = a.max_blocks_per_seq * a.block_size;
+    if (a.head_dim == 64)
+      paged_attn_merge_units_kernel<F32, 64><<<grid, 256, 0, st>>>(a.out, a.seq_lens, a.ws, rec, a.num_q_heads,
+                                                                    a.num_kv_heads, a.num_partitions,
+                                                                    a.partition_size, max_len);
+    else
+      paged_attn_merge_units_kernel<F32, 128><<<grid, 256, 0, st>>>(a.out, a.seq_lens, a.ws, rec, a.num_q_heads,
+                                                                     a.num_kv_heads, a.num_partitions,
+                                                                     a.partition_size, max_len);
+    return hipGetLastError();
+  }
+  if (!a.may_split) return hipSuccess;
+  const PlanArgs pa = make_plan(a);
+#define PKV_MERGE(QT, D) paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.ws, rec, a.num_q_heads, pa)
   if (a.head_dim == 64) {
-    if (a.q_dtype == PKV_F32) PKV_MERGE(F32, 64);
-    else if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 64);
+    if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 64);
     else PKV_MERGE(F16, 64);
   } else {
-    if (a.q_dtype == PKV_F32) PKV_MERGE(F32, 128);
-    else if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 128);
+    if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 128);
     else PKV_MERGE(F16, 128);
   }
 #undef PKV_MERGE

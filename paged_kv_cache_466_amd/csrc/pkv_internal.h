@@ -45,11 +45,16 @@ struct AttnArgs {
   float sm_scale;
   int partition_size;  // resolved (never 0)
   int num_partitions;  // per sequence, from max_blocks_per_seq * block_size
+  // 16-bit / code caches: waves launched, fewest partitions per wave, and
+  // whether any sequence can be split over several waves (merge needed)
+  int num_waves, min_units;
+  bool may_split;
   int sink_tokens, window_tokens;
-  // Partial results: one record per (sequence, KV head, partition), in that
-  // order (partition fastest).  A record holds acc[G][D] (unnormalised fp32
+  // Partial results.  A record holds acc[G][D] (unnormalised fp32
   // accumulators of the group's query heads), then m[16] and l[16] (running
   // max in the log2 domain and softmax denominator; entries >= G unused).
+  // 16-bit / code caches: one record per wave (chunk of a run); fp32 caches:
+  // one per (sequence, KV head, partition), partition fastest.
   float* ws;
   void* stream;
 };
@@ -57,8 +62,19 @@ struct AttnArgs {
 // Floats in one partial record for group size G and head_dim D.
 inline size_t partial_record_floats(int G, int D) { return (size_t)G * D + 32; }
 
-// Bytes of workspace the split decode needs.
-size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int num_partitions);
+// Waves the decode launches for the 16-bit / code caches: enough to fill
+// every compute unit at two waves per SIMD, at least one per (sequence, KV
+// head), and a multiple of num_kv_heads (a chunk slot runs one wave per head).
+int decode_waves(int num_seqs, int num_kv_heads);
+// Fewest partitions a wave takes (so that a wave reads at least 512 tokens).
+inline int min_units_per_wave(int partition_size) {
+  const int m = 512 / partition_size;
+  return m < 1 ? 1 : m;
+}
+// Bytes of workspace the split decode needs (the larger of the fp32 path's
+// per-partition records and the wave path's per-wave records), 0 if none.
+size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int num_partitions,
+                       int partition_size);
 
 // Kernel launchers (defined in the .hip files).  They assume validated
 // arguments and return a hipError_t cast to int.

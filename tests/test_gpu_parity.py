@@ -153,18 +153,20 @@ def test_single_token_and_empty_and_constant_values():
     assert (out[0].float() == 0.375).all() and (out[2].float() == 0.375).all()
 
 
-def test_partition_and_merge_entry_points_compose():
+@pytest.mark.parametrize("sink,window", [(0, 0), (4, 700)])
+def test_partition_and_merge_entry_points_compose(sink, window):
     """pkv_paged_attn_partition followed by pkv_paged_attn_merge is the decode."""
     import paged_kv_cache_466_amd as pkv
     w, t, g, o = run_case("ctx_small")
     q = t["query"]
-    ref = g.decode(q, partition_size=512)
-    nbytes = pkv.paged_attn_workspace_bytes(w.S, w.Hq, w.Hkv, w.D, g.mbs * 16, 512)
+    ref = g.decode(q, partition_size=64, sink=sink, window=window)
+    nbytes = pkv.paged_attn_workspace_bytes(w.S, w.Hq, w.Hkv, w.D, g.mbs * 16, 64)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
     pkv.paged_attn_partition(out, q, g.k_cache, g.v_cache, g.block_tables, g.lens, w.sm_scale, ws,
-                             partition_size=512)
-    pkv.paged_attn_merge(out, g.lens, w.Hkv, g.mbs * 16, ws, partition_size=512)
+                             partition_size=64, sink_tokens=sink, window_tokens=window)
+    pkv.paged_attn_merge(out, g.lens, w.Hkv, g.mbs * 16, ws, partition_size=64, sink_tokens=sink,
+                         window_tokens=window)
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
