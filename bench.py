@@ -148,6 +148,8 @@ def measure(w, steps, warmup, copies):
     slots = torch.empty(S, dtype=torch.int32, device="cuda")
     kvdt = w.kv_dtype if w.kv_dtype == "fp8e4m3" else None
     quant = w.kv_dtype in ("i8", "fp8e4m3")
+    # sequences that share no block are read with the streaming load policy
+    stream_kv = not (w.prefix_tokens or w.fork)
 
     def step(r, ev=None):
         # the slot write of the new token (code caches are written whole by
@@ -159,7 +161,7 @@ def measure(w, steps, warmup, copies):
             ev[0].record()
         pkv.paged_attn_partition(out, t["query"], r.k_cache, r.v_cache, r.block_tables, r.lens, w.sm_scale, ws,
                                  r.k_scales, r.v_scales, partition_size=psize, sink_tokens=w.sink,
-                                 window_tokens=w.window, kv_dtype=kvdt)
+                                 window_tokens=w.window, kv_dtype=kvdt, stream_kv=stream_kv)
         if ev is not None:
             ev[1].record()
         pkv.paged_attn_merge(out, r.lens, w.Hkv, max_len, ws, partition_size=psize, sink_tokens=w.sink,
@@ -190,6 +192,7 @@ def measure(w, steps, warmup, copies):
         "w": w, "t": t, "lens": lens, "kv_bytes": kv_bytes, "psize": psize, "S": S, "Hq": Hq, "D": D,
         "ms_per_step": total_ms / steps, "part_ms": float(part_ms.mean()), "merge_ms": float(merge_ms.mean()),
         "attn_ms": float((part_ms + merge_ms).mean()), "wall": wall, "copies": len(runs),
+        "stream_kv": stream_kv,
     }
 
 
@@ -256,7 +259,7 @@ def main():
             "num_seqs": m["S"], "num_q_heads": m["Hq"], "num_kv_heads": w.Hkv, "head_dim": m["D"],
             "block_size": 16, "seq_len_mean": float(lens.mean()), "seq_len_max": int(lens.max()),
             "kv_dtype": w.kv_dtype, "partition_size": m["psize"], "kv_bytes_per_step": int(kv_bytes),
-            "cache_copies_rotated": m["copies"],
+            "cache_copies_rotated": m["copies"], "stream_kv": m["stream_kv"],
         },
         "steps_per_s": round(1000.0 / ms, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),

@@ -96,6 +96,16 @@ const char* pkv_version(void);
 /* Decode attention                                                          */
 /* ------------------------------------------------------------------------ */
 
+/* Decode flags (bit set). */
+enum {
+  /* Every physical block is read by one sequence of the batch only (no
+   * shared prefix blocks).  The caches are then read with the non-temporal
+   * (streaming) load policy, so the stream does not evict data that is
+   * reused; leave it off when sequences share blocks, whose reuse it would
+   * defeat.  Results are identical either way. */
+  PKV_DECODE_STREAM_KV = 1
+};
+
 /*
  * Number of KV partitions per sequence for a given bound on the sequence
  * length: ceil(max_seq_len / partition_size).  partition_size 0 lets the
@@ -152,6 +162,7 @@ size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_
  *           several waves, each wave writes a partial record covering whole
  *           partitions to the workspace and a merge kernel combines them by
  *           log-sum-exp; a sequence handled by one wave is written directly.
+ * flags:    PKV_DECODE_* bits (0 for none); unknown bits give PKV_EINVAL.
  * workspace: device scratch of at least pkv_paged_attn_workspace_bytes(...)
  *           bytes, 128-byte aligned (may be NULL when that is 0).  Its
  *           contents on entry do not matter and are undefined on exit.
@@ -165,7 +176,7 @@ pkv_status pkv_paged_attn_decode(
     const int32_t* block_tables, int max_blocks_per_seq,
     const int32_t* seq_lens, int num_seqs,
     int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
-    float sm_scale, int partition_size, int sink_tokens, int window_tokens,
+    float sm_scale, int partition_size, int sink_tokens, int window_tokens, unsigned flags,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -187,7 +198,7 @@ pkv_status pkv_paged_attn_partition(
     const int32_t* block_tables, int max_blocks_per_seq,
     const int32_t* seq_lens, int num_seqs,
     int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
-    float sm_scale, int partition_size, int sink_tokens, int window_tokens,
+    float sm_scale, int partition_size, int sink_tokens, int window_tokens, unsigned flags,
     void* workspace, size_t workspace_bytes, void* stream);
 
 pkv_status pkv_paged_attn_merge(

@@ -29,6 +29,8 @@ lib = ctypes.CDLL(LIB_PATH)
 
 # pkv_dtype
 F32, BF16, F16, I8, FP8E4M3 = 0, 1, 2, 3, 4
+# decode flags
+DECODE_STREAM_KV = 1
 DTYPES = {"f32": F32, "bf16": BF16, "f16": F16, "i8": I8, "fp8e4m3": FP8E4M3}
 _TORCH_TO_PKV = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8,
                  torch.float8_e4m3fn: FP8E4M3}
@@ -38,7 +40,8 @@ _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPA
 _p, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
-_ATTN = [_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p, _sz, _p]
+_ATTN = [_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, ctypes.c_uint, _p, _sz,
+         _p]
 _SIGS = {
     "pkv_last_error": ([], ctypes.c_char_p),
     "pkv_version": ([], ctypes.c_char_p),
@@ -133,7 +136,7 @@ def paged_attn_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, ma
 
 
 def _attn_call(fn, out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_scales, v_scales,
-               partition_size, sink_tokens, window_tokens, workspace, kv_dtype):
+               partition_size, sink_tokens, window_tokens, workspace, kv_dtype, stream_kv):
     _contig(out, query, k_cache, v_cache, block_tables, seq_lens, k_scales, v_scales, workspace)
     S, Hq, D = query.shape
     NB, BS, Hkv, D2 = k_cache.shape
@@ -147,8 +150,8 @@ def _attn_call(fn, out, query, k_cache, v_cache, block_tables, seq_lens, sm_scal
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(fn(_ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache, kv_dtype),
               _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), mbs, _ptr(seq_lens), S, Hq, Hkv, D, BS, NB,
-              float(sm_scale), int(partition_size), int(sink_tokens), int(window_tokens), _ptr(workspace),
-              ws_bytes, _stream(query)))
+              float(sm_scale), int(partition_size), int(sink_tokens), int(window_tokens),
+              DECODE_STREAM_KV if stream_kv else 0, _ptr(workspace), ws_bytes, _stream(query)))
     return out
 
 
@@ -165,27 +168,28 @@ def _workspace_for(query, k_cache, block_tables, partition_size, workspace):
 
 def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_scales=None,
                       v_scales=None, partition_size=0, sink_tokens=0, window_tokens=0, workspace=None,
-                      kv_dtype=None):
+                      kv_dtype=None, stream_kv=False):
     """Decode attention over a paged cache (``pkv_paged_attn_decode``).
 
     query/out [S, Hq, D]; caches [NB, 16, Hkv, D]; block_tables [S, MBS] int32;
     seq_lens [S] int32.  A workspace is taken from torch when none is given.
     ``kv_dtype`` ("i8" / "fp8e4m3") names the code type when the caches are
-    uint8 tensors.
+    uint8 tensors.  ``stream_kv`` sets PKV_DECODE_STREAM_KV (no block is
+    shared between the batch's sequences).
     """
     workspace = _workspace_for(query, k_cache, block_tables, partition_size, workspace)
     return _attn_call(lib.pkv_paged_attn_decode, out, query, k_cache, v_cache, block_tables, seq_lens,
                       sm_scale, k_scales, v_scales, partition_size, sink_tokens, window_tokens, workspace,
-                      kv_dtype)
+                      kv_dtype, stream_kv)
 
 
 def paged_attn_partition(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, workspace,
                          k_scales=None, v_scales=None, partition_size=0, sink_tokens=0, window_tokens=0,
-                         kv_dtype=None):
+                         kv_dtype=None, stream_kv=False):
     """First pass of the decode (``pkv_paged_attn_partition``)."""
     return _attn_call(lib.pkv_paged_attn_partition, out, query, k_cache, v_cache, block_tables, seq_lens,
                       sm_scale, k_scales, v_scales, partition_size, sink_tokens, window_tokens, workspace,
-                      kv_dtype)
+                      kv_dtype, stream_kv)
 
 
 def paged_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_size=0, sink_tokens=0,

@@ -75,9 +75,11 @@ size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head
   const size_t rec = partial_record_floats(G, head_dim) * sizeof(float);
   // fp32 path: a record per (sequence, KV head, partition)
   const size_t per_part = (size_t)num_seqs * num_kv_heads * num_partitions * rec;
-  // wave path: a record per wave, when a sequence can be split over waves
-  const size_t per_wave =
-      num_partitions > min_units_per_wave(partition_size) ? (size_t)decode_waves(num_seqs, num_kv_heads) * rec : 0;
+  // wave path, when a sequence can be split over waves: the per-sequence
+  // plan area, then a record per wave
+  const size_t per_wave = num_partitions > min_units_per_wave(partition_size)
+                              ? plan_area_bytes(num_seqs) + (size_t)decode_waves(num_seqs, num_kv_heads) * rec
+                              : 0;
   return align256(per_part > per_wave ? per_part : per_wave);
 }
 
@@ -96,9 +98,8 @@ static int resolve_partition(int num_seqs, int num_kv_heads, int max_len, int bl
   (void)num_seqs;
   (void)num_kv_heads;
   // Bounds up to 512 tokens run as one pass without partials.  Longer ones
-  // are split at 64-token granularity: the decode gives each wave a stretch
-  // of at least 512 tokens of one sequence, and the fine granularity lets it
-  // balance the stretches across waves.
+  // are split at 64-token granularity, fine enough for the decode to balance
+  // its waves' stretches of each sequence.
   const int single = ((max_len + block_size - 1) / block_size) * block_size;
   if (max_len <= 512) return single > 0 ? single : block_size;
   return 64;
@@ -207,6 +208,7 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
                   who);
     if (codes && (!a.k_scales || !a.v_scales)) return fail(PKV_EINVAL, "%s: quantised cache needs k/v scales", who);
     if (a.sink_tokens < 0 || a.window_tokens < 0) return fail(PKV_EINVAL, "%s: negative sink/window", who);
+    if (a.flags & ~(unsigned)PKV_DECODE_STREAM_KV) return fail(PKV_EINVAL, "%s: unknown flags 0x%x", who, a.flags);
   }
   if (a.partition_size < 0 || (a.partition_size > 0 && a.partition_size % a.block_size))
     return fail(PKV_EINVAL, "%s: partition_size must be 0 or a positive multiple of block_size", who);
@@ -222,6 +224,7 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
   a.min_units = min_units_per_wave(a.partition_size);
   a.may_split = a.num_partitions > a.min_units;
   a.ws = nullptr;
+  a.plan = nullptr;
   const bool needs_ws = a.q_dtype == PKV_F32 ? a.num_partitions > 1 : a.may_split;
   if (needs_ws) {
     const size_t total = workspace_total(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.num_partitions,
@@ -229,7 +232,12 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
     if (!workspace || workspace_bytes < total)
       return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, total, workspace_bytes);
     if (((uintptr_t)workspace) & 127) return fail(PKV_EINVAL, "%s: workspace must be 128-byte aligned", who);
-    a.ws = (float*)workspace;
+    if (a.q_dtype == PKV_F32) {
+      a.ws = (float*)workspace;
+    } else {
+      a.plan = (int*)workspace;
+      a.ws = (float*)((char*)workspace + plan_area_bytes(a.num_seqs));
+    }
   }
   return PKV_OK;
 }
@@ -238,14 +246,15 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
   void *out, const void *query, int q_dtype, const void *k_cache, const void *v_cache, int kv_dtype,          \
       const float *k_scales, const float *v_scales, const int32_t *block_tables, int max_blocks_per_seq,      \
       const int32_t *seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size, \
-      int num_blocks, float sm_scale, int partition_size, int sink_tokens, int window_tokens, void *workspace, \
-      size_t workspace_bytes, void *stream
+      int num_blocks, float sm_scale, int partition_size, int sink_tokens, int window_tokens, unsigned flags,  \
+      void *workspace, size_t workspace_bytes, void *stream
 
 static AttnArgs fill_args(void* out, const void* query, int q_dtype, const void* k_cache, const void* v_cache,
                           int kv_dtype, const float* k_scales, const float* v_scales, const int32_t* block_tables,
                           int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
                           int num_kv_heads, int head_dim, int block_size, int num_blocks, float sm_scale,
-                          int partition_size, int sink_tokens, int window_tokens, void* stream) {
+                          int partition_size, int sink_tokens, int window_tokens, unsigned flags,
+                          void* stream) {
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.out = out;
@@ -269,6 +278,7 @@ static AttnArgs fill_args(void* out, const void* query, int q_dtype, const void*
   a.partition_size = partition_size;
   a.sink_tokens = sink_tokens;
   a.window_tokens = window_tokens;
+  a.flags = flags;
   a.stream = stream;
   return a;
 }
@@ -276,7 +286,7 @@ static AttnArgs fill_args(void* out, const void* query, int q_dtype, const void*
 static pkv_status run_attn(bool do_partition, bool do_merge, PKV_ATTN_ARGS) {
   AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, block_tables,
                          max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                         num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, stream);
+                         num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, flags, stream);
   const char* who = do_partition ? (do_merge ? "pkv_paged_attn_decode" : "pkv_paged_attn_partition")
                                  : "pkv_paged_attn_merge";
   pkv_status st = prepare_attn(a, who, workspace, workspace_bytes, do_partition);
@@ -297,14 +307,14 @@ static pkv_status run_attn(bool do_partition, bool do_merge, PKV_ATTN_ARGS) {
 extern "C" pkv_status pkv_paged_attn_decode(PKV_ATTN_ARGS) {
   return run_attn(true, true, out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, block_tables,
                   max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                  num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, workspace, workspace_bytes,
-                  stream);
+                  num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, flags, workspace,
+                  workspace_bytes, stream);
 }
 
 extern "C" pkv_status pkv_paged_attn_partition(PKV_ATTN_ARGS) {
   return run_attn(true, false, out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales,
                   block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                  block_size, num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, workspace,
+                  block_size, num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, flags, workspace,
                   workspace_bytes, stream);
 }
 
@@ -316,7 +326,7 @@ extern "C" pkv_status pkv_paged_attn_merge(void* out, int q_dtype, const int32_t
   if (sink_tokens < 0 || window_tokens < 0) return fail(PKV_EINVAL, "pkv_paged_attn_merge: negative sink/window");
   return run_attn(false, true, out, nullptr, q_dtype, nullptr, nullptr, q_dtype, nullptr, nullptr, nullptr,
                   max_seq_len / 16, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, 16, 0, 1.f,
-                  partition_size, sink_tokens, window_tokens, const_cast<void*>(workspace), workspace_bytes,
+                  partition_size, sink_tokens, window_tokens, 0u, const_cast<void*>(workspace), workspace_bytes,
                   stream);
 }
 

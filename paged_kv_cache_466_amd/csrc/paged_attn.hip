@@ -53,6 +53,7 @@ struct AttnParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   float* ws;            // partial records (see AttnArgs)
+  int* plan;            // per sequence: first chunk, chunk count (wave path, split decodes)
   int rec_floats;       // floats per record
   int num_seqs, mbs, num_q_heads, num_kv_heads, num_blocks;
   int partition_size, num_partitions;
@@ -83,9 +84,12 @@ __device__ __forceinline__ int table_entry(const AttnParams& p, int s, int lb) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
 }
+// POL: cache-policy bits of the load (gfx950: 2 = nt, non-temporal).
+template <int POL = 0>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, POL));
 }
+constexpr int kPolicyStream = 2;   // non-temporal: streamed data does not evict reused data
 __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int voff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
@@ -143,19 +147,33 @@ template <> struct Mfma<F16> {
   }
 };
 
-// 8 codes -> 8 elements of the query's 16-bit type, exactly (every INT8 and
-// FP8-E4M3 value is a bf16 and an f16 value).
+// The 16-bit type the MFMAs use: the query's for 16-bit and FP8 caches; f16
+// for INT8 codes, which convert to f16 in two cheap steps (below).
 template <typename QT, typename KVT>
+struct MmaType { typedef QT type; };
+template <typename QT>
+struct MmaType<QT, I8> { typedef F16 type; };
+
+// Two INT8 codes (bytes 2h, 2h+1 of w) -> two f16 values, exactly.  With
+// u = c + 128 (the code's bits with the top bit flipped), the f16 with bits
+// 0x64 << 8 | u is 1024 + u; subtracting 1152 leaves c.
+template <int H>
+__device__ __forceinline__ uint32_t i8x2_f16(uint32_t u) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  // bytes: u[2H], 0x64, u[2H+1], 0x64
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, H ? 0x04030402u : 0x04010400u);
+  const h2 x = __builtin_bit_cast(h2, b) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+// 8 codes -> 8 elements of the MFMA type, exactly (every INT8 value is an f16
+// value; every FP8-E4M3 value is a bf16 and an f16 value).
+template <typename MT, typename KVT>
 __device__ __forceinline__ uint4 to16(uint32_t w0, uint32_t w1) {
-  typedef Mfma<QT> M;
+  typedef Mfma<MT> M;
   if constexpr (std::is_same<KVT, I8>::value) {
-    float f[8];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      f[b] = (float)(int8_t)((w0 >> (8 * b)) & 0xFF);
-      f[4 + b] = (float)(int8_t)((w1 >> (8 * b)) & 0xFF);
-    }
-    return make_uint4(M::pack2(f[0], f[1]), M::pack2(f[2], f[3]), M::pack2(f[4], f[5]), M::pack2(f[6], f[7]));
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+    return make_uint4(i8x2_f16<0>(u0), i8x2_f16<1>(u0), i8x2_f16<0>(u1), i8x2_f16<1>(u1));
   } else {
     return make_uint4(M::template fp8x2<false>(w0), M::template fp8x2<true>(w0), M::template fp8x2<false>(w1),
                       M::template fp8x2<true>(w1));
@@ -243,7 +261,11 @@ __device__ __forceinline__ int lane_scan_incl(int x, int lane) {
   return x;
 }
 
-// Units per chunk.  Called by a whole wave; the result is wave-uniform.
+// Units per chunk, Q.  Called by a whole wave; the result is wave-uniform.
+// With K = NW / Hkv chunk slots, Q is the smallest value with
+// sum_s ceil(n_s / Q) <= K, found by bisection between U / K (below it the
+// sum exceeds K) and U / (K - S_ne) (at or above it the sum fits); it never
+// goes below min_units, nor above the longest sequence's unit count.
 __device__ int plan_units_per_chunk(const PlanArgs& a, int lane) {
   long long U = 0;
   int s_ne = 0, nmax = 0;
@@ -258,11 +280,31 @@ __device__ int plan_units_per_chunk(const PlanArgs& a, int lane) {
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
-  const long long room = (long long)a.num_waves - (long long)a.num_kv_heads * s_ne;
-  long long Q = room > 0 ? ((long long)a.num_kv_heads * U + room - 1) / room : (long long)nmax;
-  if (Q > nmax) Q = nmax;                 // one chunk per run is the coarsest split
-  if (Q < a.min_units) Q = a.min_units;
-  return Q < 1 ? 1 : (int)Q;
+  const int floor_q = max(1, a.min_units);
+  if (nmax <= floor_q) return floor_q;                  // every sequence is one chunk
+  const long long K = a.num_waves / a.num_kv_heads;     // chunk slots
+  auto chunks = [&](int Q) {
+    long long total = 0;
+    for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
+      const int s = s0 + lane;
+      int k = 0;
+      if (s < a.num_seqs) k = (seq_units(clamp_len(a.seq_lens[s], a.mbs), a.psize, a.sink, a.window).n + Q - 1) / Q;
+      total += __shfl(lane_scan_incl(k, lane), 63, 64);
+    }
+    return total;
+  };
+  long long hi = K > s_ne ? (U + (K - s_ne) - 1) / (K - s_ne) : nmax;
+  if (hi > nmax) hi = nmax;
+  if (hi < floor_q) hi = floor_q;
+  long long lo = (U + K - 1) / K;
+  if (lo < floor_q) lo = floor_q;
+  if (lo > hi) lo = hi;
+  while (lo < hi) {
+    const int mid = (int)((lo + hi) / 2);
+    if (chunks(mid) <= K) hi = mid;
+    else lo = mid + 1;
+  }
+  return (int)hi;
 }
 
 struct ChunkInfo {
@@ -304,13 +346,17 @@ __device__ ChunkInfo plan_locate(const PlanArgs& a, int Q, int lane, bool by_chu
 
 constexpr int kMaxWavesPerGroup = 8;   // KV heads per workgroup
 
-template <typename QT, typename KVT, int D>
+template <typename QT, typename KVT, int D, bool STREAM>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
   typedef WaveCfg<KVT, D> C;
-  typedef Mfma<QT> M;
+  typedef typename MmaType<QT, KVT>::type MT;
+  typedef Mfma<MT> M;     // operands of both products
+  typedef Mfma<QT> MO;    // the output type
   constexpr int NC = C::NC, NN = C::NN, KCH = C::KCH, VCH = C::VCH, DEPTH = C::DEPTH;
   constexpr bool kCodes = C::kCodes;
+  // the query is rescaled into f16 (INT8 caches with a bf16 query)
+  constexpr bool kRescaleQ = !std::is_same<MT, QT>::value;
   // Scores may exceed the running max by this much (log2 units) before the
   // accumulators are rescaled: probabilities stay below 2^8.
   constexpr float kSlack = 8.0f;
@@ -345,6 +391,11 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
   const int chunks = __builtin_amdgcn_readfirstlane(ci.chunks);
   const bool single = chunks == 1;
   const int rec_index = blockIdx.x * p.num_kv_heads + kvh;
+  // where the merge finds this sequence's records
+  if (p.plan && chunk == 0 && kvh == 0 && lane == 0) {
+    p.plan[2 * s] = blockIdx.x;
+    p.plan[2 * s + 1] = chunks;
+  }
   const size_t head0 = (size_t)s * p.num_q_heads + kvh * G;
   const int L = clamp_len(p.seq_lens[s], p.mbs);
   const SeqUnits su = seq_units(L, p.partition_size, p.sink, p.window);
@@ -357,13 +408,47 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
 
   // ---- query group as the B operand of S^T = K Q^T (zero rows for g >= G) --
   typename M::vec8 qop[NC];
+  // log2-domain score factor of this lane's head (times the block's K scale)
+  float qfactor = p.scale_log2;
+  {
+    uint4 v[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (g < G)
-      v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + (head0 + g) * D +
-                                          qk_doff<KVT, D>(c, kg));
-    qop[c] = __builtin_bit_cast(typename M::vec8, v);
+    for (int c = 0; c < NC; ++c) {
+      v[c] = make_uint4(0, 0, 0, 0);
+      if (g < G)
+        v[c] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + (head0 + g) * D +
+                                               qk_doff<KVT, D>(c, kg));
+    }
+    if constexpr (!kRescaleQ) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qop[c] = __builtin_bit_cast(typename M::vec8, v[c]);
+    } else {
+      // bf16 -> f16 with the head's values scaled by 2^e so that the largest
+      // lands in [2^14, 2^15): every bf16 value within 2^29 of the largest
+      // stays exact, and the scores get 2^-e back through the factor
+      float qf[NC][8];
+      float mx = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        decode16<BF16>(v[c], qf[c]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(qf[c][i]));
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      int e = 0;
+      if (mx > 0.f) e = min(100, max(-100, 15 - __builtin_amdgcn_frexp_expf(mx)));
+      qfactor = ldexpf(p.scale_log2, -e);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint4 w;
+        w.x = M::pack2(ldexpf(qf[c][0], e), ldexpf(qf[c][1], e));
+        w.y = M::pack2(ldexpf(qf[c][2], e), ldexpf(qf[c][3], e));
+        w.z = M::pack2(ldexpf(qf[c][4], e), ldexpf(qf[c][5], e));
+        w.w = M::pack2(ldexpf(qf[c][6], e), ldexpf(qf[c][7], e));
+        qop[c] = __builtin_bit_cast(typename M::vec8, w);
+      }
+    }
   }
 
   // ---- blocks this wave reads: [lb_begin, a1) then [b0, lb_end) ----------
@@ -420,11 +505,11 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
     const bool full = block_full(lb);
     const int ko = (full | kept(t0 + krow, L, p.sink, p.window)) ? k_off : kOutOfRange;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) t.k[c] = buf_load16(kr, ko + (kCodes ? 16 : 64) * c);
+    for (int c = 0; c < KCH; ++c) t.k[c] = buf_load16<STREAM ? kPolicyStream : 0>(kr, ko + (kCodes ? 16 : 64) * c);
 #pragma unroll
     for (int ps = 0; ps < VCH; ++ps) {
       const int vo = (full | kept(t0 + v_row[ps], L, p.sink, p.window)) ? v_off[ps] : kOutOfRange;
-      t.v[ps] = buf_load16(vr, vo);
+      t.v[ps] = buf_load16<STREAM ? kPolicyStream : 0>(vr, vo);
     }
     if constexpr (kCodes) {
       // the scale row of this block: a 4-byte window at its own address
@@ -454,9 +539,9 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
       if constexpr (!kCodes) {
         *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 16) = t.v[ps];
       } else {
-        *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32) = to16<QT, KVT>(t.v[ps].x, t.v[ps].y);
+        *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32) = to16<MT, KVT>(t.v[ps].x, t.v[ps].y);
         *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32 + 16) =
-            to16<QT, KVT>(t.v[ps].z, t.v[ps].w);
+            to16<MT, KVT>(t.v[ps].z, t.v[ps].w);
       }
     }
 
@@ -468,12 +553,12 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
     } else {
 #pragma unroll
       for (int c2 = 0; c2 < KCH; ++c2) {
-        sacc = M::qk(__builtin_bit_cast(typename M::vec8, to16<QT, KVT>(t.k[c2].x, t.k[c2].y)), qop[2 * c2], sacc);
-        sacc = M::qk(__builtin_bit_cast(typename M::vec8, to16<QT, KVT>(t.k[c2].z, t.k[c2].w)), qop[2 * c2 + 1],
+        sacc = M::qk(__builtin_bit_cast(typename M::vec8, to16<MT, KVT>(t.k[c2].x, t.k[c2].y)), qop[2 * c2], sacc);
+        sacc = M::qk(__builtin_bit_cast(typename M::vec8, to16<MT, KVT>(t.k[c2].z, t.k[c2].w)), qop[2 * c2 + 1],
                      sacc);
       }
     }
-    const float factor = p.scale_log2 * t.ks;
+    const float factor = qfactor * t.ks;
     // lane holds tokens 4*kg + i of this block for head g
     float sc[4];
 #pragma unroll
@@ -581,7 +666,7 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
         const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
         const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
         *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (head0 + h0) * D + c * 8) = make_uint4(
-            M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]), M::pack2(hi[0], hi[1]), M::pack2(hi[2], hi[3]));
+            MO::pack2(lo[0], lo[1]), MO::pack2(lo[2], lo[3]), MO::pack2(hi[0], hi[1]), MO::pack2(hi[2], hi[3]));
       }
     } else {
       constexpr int CPR = D / 4;
@@ -721,37 +806,29 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 // was cut into several chunks, out = sum_c 2^(m_c - M) acc_c /
 // sum_c 2^(m_c - M) l_c over its records (one per chunk, in chunk order).
 // Sequences of one chunk were finished by their waves; empty sequences were
-// zeroed.  The first wave of the workgroup recomputes the split plan to
-// find the records; then 8 record rows at a time are read by D/4 threads with
+// zeroed.  The decode left each sequence's first chunk and chunk count in
+// the plan area; 8 record rows at a time are read by D/4 threads with
 // 16-byte loads, 4 rows per thread in flight.
 // ===========================================================================
 template <typename QT, int D>
-__global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const float* ws, int rec_floats,
-                                                               int num_q_heads, PlanArgs pa) {
+__global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const float* ws, const int* plan,
+                                                               int rec_floats, int num_q_heads, PlanArgs pa) {
   constexpr int TPR = D / 4;               // threads per record row
   constexpr int ROWS = 256 / TPR;
   constexpr int U = 4;
   __shared__ float red[256];
   __shared__ floatx4 part_num[ROWS][TPR];
   __shared__ float part_den[ROWS];
-  __shared__ int sh_first, sh_chunks;
   const int h = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x;
   const int G = num_q_heads / pa.num_kv_heads;
   const int kvh = h / G, g = h % G;
-  if (tid < 64) {
-    const int Q = plan_units_per_chunk(pa, tid);
-    const ChunkInfo ci = plan_locate(pa, Q, tid, false, s);
-    if (tid == 0) {
-      sh_first = ci.first;
-      sh_chunks = ci.chunks;
-    }
-  }
-  __syncthreads();
-  const int np = sh_chunks;
+  // a sequence without units was zeroed by the decode and wrote no plan entry
+  if (seq_units(clamp_len(pa.seq_lens[s], pa.mbs), pa.psize, pa.sink, pa.window).n == 0) return;
+  const int np = plan[2 * s + 1];
   if (np <= 1) return;
   // record of chunk c of this head: (first + c) * Hkv + kvh
-  const float* rec0 = ws + ((size_t)sh_first * pa.num_kv_heads + kvh) * rec_floats;
+  const float* rec0 = ws + ((size_t)plan[2 * s] * pa.num_kv_heads + kvh) * rec_floats;
   rec_floats *= pa.num_kv_heads;   // stride between the head's consecutive chunks
   const float* m_of = rec0 + (size_t)G * D + g;
   const float* l_of = m_of + 16;
@@ -909,6 +986,7 @@ static AttnParams make_params(const AttnArgs& a) {
   p.block_tables = a.block_tables;
   p.seq_lens = a.seq_lens;
   p.ws = a.ws;
+  p.plan = a.plan;
   p.rec_floats = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads, a.head_dim);
   p.num_seqs = a.num_seqs;
   p.mbs = a.max_blocks_per_seq;
@@ -937,19 +1015,20 @@ static PlanArgs make_plan(const AttnArgs& a) {
   return pa;
 }
 
-template <typename QT, typename KVT, int D>
+template <typename QT, typename KVT, int D, bool STREAM>
 static int launch_wave(const AttnParams& p, const PlanArgs& pa, hipStream_t st) {
   // (chunk slot, group of up to 8 KV heads); one wave per KV head
   const int per_group = pa.num_kv_heads < kMaxWavesPerGroup ? pa.num_kv_heads : kMaxWavesPerGroup;
   const int groups = (pa.num_kv_heads + per_group - 1) / per_group;
   const dim3 grid(pa.num_waves / pa.num_kv_heads, groups);
-  paged_attn_wave_kernel<QT, KVT, D><<<grid, 64 * per_group, 0, st>>>(p, pa);
+  paged_attn_wave_kernel<QT, KVT, D, STREAM><<<grid, 64 * per_group, 0, st>>>(p, pa);
   return hipGetLastError();
 }
 
 template <typename QT, typename KVT>
-static int launch_wave_d(const AttnParams& p, const PlanArgs& pa, int D, hipStream_t st) {
-  return D == 64 ? launch_wave<QT, KVT, 64>(p, pa, st) : launch_wave<QT, KVT, 128>(p, pa, st);
+static int launch_wave_d(const AttnParams& p, const PlanArgs& pa, int D, bool stream, hipStream_t st) {
+  if (stream) return D == 64 ? launch_wave<QT, KVT, 64, true>(p, pa, st) : launch_wave<QT, KVT, 128, true>(p, pa, st);
+  return D == 64 ? launch_wave<QT, KVT, 64, false>(p, pa, st) : launch_wave<QT, KVT, 128, false>(p, pa, st);
 }
 
 template <typename QT, typename KVT, int D>
@@ -968,17 +1047,18 @@ int launch_paged_attn_partition(const AttnArgs& a) {
     return D == 64 ? launch_simple<F32, F32, 64>(p, grid, st) : launch_simple<F32, F32, 128>(p, grid, st);
   }
   const PlanArgs pa = make_plan(a);
+  const bool stream = (a.flags & PKV_DECODE_STREAM_KV) != 0;
   if (a.q_dtype == PKV_BF16) {
     switch (a.kv_dtype) {
-      case PKV_BF16: return launch_wave_d<BF16, BF16>(p, pa, D, st);
-      case PKV_I8: return launch_wave_d<BF16, I8>(p, pa, D, st);
-      default: return launch_wave_d<BF16, FP8>(p, pa, D, st);
+      case PKV_BF16: return launch_wave_d<BF16, BF16>(p, pa, D, stream, st);
+      case PKV_I8: return launch_wave_d<BF16, I8>(p, pa, D, stream, st);
+      default: return launch_wave_d<BF16, FP8>(p, pa, D, stream, st);
     }
   }
   switch (a.kv_dtype) {
-    case PKV_F16: return launch_wave_d<F16, F16>(p, pa, D, st);
-    case PKV_I8: return launch_wave_d<F16, I8>(p, pa, D, st);
-    default: return launch_wave_d<F16, FP8>(p, pa, D, st);
+    case PKV_F16: return launch_wave_d<F16, F16>(p, pa, D, stream, st);
+    case PKV_I8: return launch_wave_d<F16, I8>(p, pa, D, stream, st);
+    default: return launch_wave_d<F16, FP8>(p, pa, D, stream, st);
   }
 }
 
@@ -1002,7 +1082,8 @@ int launch_paged_attn_merge(const AttnArgs& a) {
   }
   if (!a.may_split) return hipSuccess;
   const PlanArgs pa = make_plan(a);
-#define PKV_MERGE(QT, D) paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.ws, rec, a.num_q_heads, pa)
+#define PKV_MERGE(QT, D) \
+  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.ws, a.plan, rec, a.num_q_heads, pa)
   if (a.head_dim == 64) {
     if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 64);
     else PKV_MERGE(F16, 64);

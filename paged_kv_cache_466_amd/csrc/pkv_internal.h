@@ -49,6 +49,7 @@ struct AttnArgs {
   // whether any sequence can be split over several waves (merge needed)
   int num_waves, min_units;
   bool may_split;
+  unsigned flags;  // PKV_DECODE_* bits
   int sink_tokens, window_tokens;
   // Partial results.  A record holds acc[G][D] (unnormalised fp32
   // accumulators of the group's query heads), then m[16] and l[16] (running
@@ -56,6 +57,7 @@ struct AttnArgs {
   // 16-bit / code caches: one record per wave (chunk of a run); fp32 caches:
   // one per (sequence, KV head, partition), partition fastest.
   float* ws;
+  int* plan;   // wave path: [num_seqs][2] (first chunk, chunk count), before the records
   void* stream;
 };
 
@@ -66,9 +68,15 @@ inline size_t partial_record_floats(int G, int D) { return (size_t)G * D + 32; }
 // every compute unit at two waves per SIMD, at least one per (sequence, KV
 // head), and a multiple of num_kv_heads (a chunk slot runs one wave per head).
 int decode_waves(int num_seqs, int num_kv_heads);
-// Fewest partitions a wave takes (so that a wave reads at least 512 tokens).
+// Bytes at the start of the wave path's workspace that hold, per sequence,
+// the number of its first chunk and its chunk count (int32 pairs), written by
+// the decode for the merge; the records follow.
+inline size_t plan_area_bytes(int num_seqs) { return ((size_t)num_seqs * 8 + 255) & ~(size_t)255; }
+// Fewest partitions a wave takes: enough for 128 tokens (8 blocks), so that
+// a wave's fixed costs stay small next to its stream, while small batches
+// still spread over many compute units.
 inline int min_units_per_wave(int partition_size) {
-  const int m = 512 / partition_size;
+  const int m = 128 / partition_size;
   return m < 1 ? 1 : m;
 }
 // Bytes of workspace the split decode needs (the larger of the fp32 path's

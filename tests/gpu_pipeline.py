@@ -92,7 +92,7 @@ class GpuRun:
                               self.step_slots)
         self.lens += 1
 
-    def decode(self, query, partition_size=0, sink=None, window=None, out=None):
+    def decode(self, query, partition_size=0, sink=None, window=None, out=None, stream_kv=False):
         w = self.w
         if out is None:
             out = torch.empty_like(query)
@@ -100,5 +100,6 @@ class GpuRun:
         pkv.paged_attn_decode(out, query, self.k_cache, self.v_cache, self.block_tables, self.lens, w.sm_scale,
                               self.k_scales, self.v_scales, partition_size=partition_size,
                               sink_tokens=w.sink if sink is None else sink,
-                              window_tokens=w.window if window is None else window, kv_dtype=kvdt)
+                              window_tokens=w.window if window is None else window, kv_dtype=kvdt,
+                              stream_kv=stream_kv)
         return out

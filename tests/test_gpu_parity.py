@@ -28,6 +28,9 @@ CASES = {
     "prefix_small": ("shared_prefix_b128", dict(S=6, len_lo=20, len_hi=200, prefix_tokens=64)),
     "quant_i8_small": ("quant_kv_32k_b16", dict(S=3, fixed_len=1024)),
     "quant_fp8_small": ("quant_kv_32k_b16", dict(S=3, fixed_len=1024, kv_dtype="fp8e4m3")),
+    "quant_i8_f16q": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16")),
+    "quant_fp8_f16q": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16",
+                                                 kv_dtype="fp8e4m3")),
     "ctx_small": ("ctx128k_b4", dict(S=2, fixed_len=5000)),
     "mqa_d64": ("llama3_8b_b64", dict(S=4, Hq=8, Hkv=1, D=64, len_lo=1, len_hi=700)),
     "mha_d64": ("llama3_8b_b64", dict(S=4, Hq=4, Hkv=4, D=64, len_lo=1, len_hi=300)),
@@ -93,6 +96,16 @@ def test_decode_parity(name, psize):
     err = np.abs(out - ref).max()
     print(f"[parity] {name} psize={psize} max_abs_err={err:.3e}")
     assert err <= TOL[w.q_dtype], err
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if n != "tiny_fp32"])
+def test_decode_streaming_policy_is_bit_identical(name):
+    """PKV_DECODE_STREAM_KV only changes the cache policy of the loads: the
+    output is bit-identical to the default policy's."""
+    w, t, g, o = run_case(name)
+    a = g.decode(t["query"], partition_size=64)
+    b = g.decode(t["query"], partition_size=64, stream_kv=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 @pytest.mark.parametrize("name", ["ctx_small", "llama_small"])
@@ -168,6 +181,30 @@ def test_partition_and_merge_entry_points_compose(sink, window):
     pkv.paged_attn_merge(out, g.lens, w.Hkv, g.mbs * 16, ws, partition_size=64, sink_tokens=sink,
                          window_tokens=window)
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8e4m3"])
+@pytest.mark.parametrize("k", [20, -30])
+def test_code_cache_with_out_of_f16_range_query(kv, k):
+    """bf16 queries scaled by 2^k with sm_scale scaled by 2^-k (same scores):
+    2^20 overflows f16 and 2^-30 underflows it, so this checks that the
+    INT8 products move each query head into f16 range by a power of two.
+    Results must match the oracle on the same dequantised values."""
+    import paged_kv_cache_466_amd as pkv
+    from oracle import attention
+    w, t, g, o = run_case("quant_i8_small" if kv == "i8" else "quant_fp8_small")
+    q = (t["query"].float() * 2.0 ** k).to(torch.bfloat16)
+    sm = float(np.float32(w.sm_scale) * np.float32(2.0 ** -k))
+    out = torch.empty_like(q)
+    pkv.paged_attn_decode(out, q, g.k_cache, g.v_cache, g.block_tables, g.lens, sm, g.k_scales, g.v_scales,
+                          partition_size=64, kv_dtype=kv if kv == "fp8e4m3" else None)
+    got = out.float().cpu().numpy()
+    ref = attention.paged_decode(to_raw(q, "bf16"), "bf16", o.k_cache, o.v_cache, w.kv_dtype, o.block_tables(),
+                                 o.lens, w.BS, sm, o.k_scales, o.v_scales)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    print(f"[parity] query x 2^{k} kv={kv} max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"], err
 
 
 @pytest.mark.parametrize("qdt", [torch.float16, torch.bfloat16])

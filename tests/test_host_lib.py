@@ -141,35 +141,38 @@ def test_argument_errors_return_before_launch():
     no pointer is dereferenced (all null) and nothing is enqueued."""
     L = pkv.lib
     st = L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 2, 32, 8, 96, 16, 10,
-                                 0.1, 0, 0, 0, None, 0, None)
+                                 0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 2 and "head_dim" in pkv.last_error()
     st = L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 2, 30, 8, 128, 16, 10,
-                                 0.1, 0, 0, 0, None, 0, None)
+                                 0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 1 and "%" in pkv.last_error()
     st = L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 2, 32, 8, 128, 32, 10,
-                                 0.1, 0, 0, 0, None, 0, None)
+                                 0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 2 and "block_size" in pkv.last_error()
     st = L.pkv_paged_attn_decode(None, None, 0, None, None, 3, None, None, None, 4, None, 2, 32, 8, 128, 16, 10,
-                                 0.1, 0, 0, 0, None, 0, None)
+                                 0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 2                       # int8 codes need a 16-bit query
     st = L.pkv_paged_attn_decode(None, None, 1, None, None, 3, None, None, None, 4, None, 2, 32, 8, 128, 16, 10,
-                                 0.1, 0, 0, 0, None, 0, None)
+                                 0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 1 and "scales" in pkv.last_error()
     st = L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 2, 32, 8, 128, 16, 10,
-                                 0.1, 24, 0, 0, None, 0, None)
+                                 0.1, 24, 0, 0, 0, None, 0, None)
     assert st == 1 and "partition_size" in pkv.last_error()
     # a 128K bound needs partials: missing workspace is reported
     st = L.pkv_paged_attn_decode(1, 1, 1, 1, 1, 1, None, None, 1, 8192, 1, 4, 64, 8, 128, 16, 32768,
-                                 0.1, 512, 0, 0, None, 0, None)
+                                 0.1, 512, 0, 0, 0, None, 0, None)
     assert st == 3 and "workspace" in pkv.last_error()
     st = L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 2, 64 * 17, 64, 128, 16,
-                                 10, 0.1, 0, 0, 0, None, 0, None)
+                                 10, 0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 2 and "group" in pkv.last_error()
     assert L.pkv_reshape_and_cache(None, None, None, None, 3, None, 4, 10, 16, 8, 128, None) == 2
     assert L.pkv_quantize_kv(None, 1, None, 1, None, None, 4, 10, 16, 8, 128, None) == 2
     assert L.pkv_copy_blocks(1, 1, 1, None, 1, 1, 1, 10, 16, 8, 128, None) == 1
     assert L.pkv_slot_mapping(1, 1, 4, None, 1, 8, 4, 16, 10, None) == 1
+    st = L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 2, 32, 8, 128, 16, 10,
+                                 0.1, 0, 0, 0, 2, None, 0, None)
+    assert st == 1 and "flags" in pkv.last_error()
     # empty batches are no-ops
     assert L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 0, 32, 8, 128, 16, 10,
-                                   0.1, 0, 0, 0, None, 0, None) == 0
+                                   0.1, 0, 0, 0, 0, None, 0, None) == 0
     assert L.pkv_reshape_and_cache(None, None, None, None, 1, None, 0, 10, 16, 8, 128, None) == 0
