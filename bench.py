@@ -1,9 +1,10 @@
 """Paged-decode benchmark on one MI355X.
 
-A step is one decode step of one attention layer for the whole batch:
-slot mapping of each sequence's new token, the slot write of its K/V, then
-decode attention (partition kernel + log-sum-exp merge) over every
-sequence's cached tokens.  Inputs are resident in HBM before timing starts.
+A step is one decode step of one attention layer for the whole batch: the
+slot mapping and slot write of each sequence's new token K/V (one fused
+launch), then decode attention (partition kernel + log-sum-exp merge) over
+every sequence's cached tokens.  Inputs are resident in HBM before timing
+starts.
 
 Prints one JSON line:
   value        KV-read GB/s over the whole step (algorithmic KV bytes / step time)
@@ -155,8 +156,8 @@ def measure(w, steps, warmup, copies):
         # the slot write of the new token (code caches are written whole by
         # the quantiser at prefill, so their step is attention only)
         if not quant:
-            pkv.slot_mapping(r.block_tables, positions, w.num_blocks, out=slots)
-            pkv.reshape_and_cache(t["new_key"], t["new_value"], r.k_cache, r.v_cache, slots)
+            pkv.append_kv(t["new_key"], t["new_value"], r.k_cache, r.v_cache, r.block_tables, positions,
+                          slot_mapping=slots)
         if ev is not None:
             ev[0].record()
         pkv.paged_attn_partition(out, t["query"], r.k_cache, r.v_cache, r.block_tables, r.lens, w.sm_scale, ws,

@@ -240,6 +240,21 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value,
                                  int head_dim, void* stream);
 
 /*
+ * pkv_slot_mapping and pkv_reshape_and_cache in one launch: token j (of
+ * sequence seq_ids[j], or j when seq_ids is NULL, at position positions[j])
+ * gets slot block_tables[s][p / block_size] * block_size + p % block_size
+ * and its key[j] / value[j] rows are copied there.  A token whose slot would
+ * be -1 under pkv_slot_mapping is skipped.  slot_mapping (device int32
+ * [num_tokens]) receives the slots when not NULL.  Same layouts, dtypes and
+ * bit-exactness as the two calls it combines; the same tokens must not map
+ * to one slot.
+ */
+pkv_status pkv_append_kv(const void* key, const void* value, void* k_cache, void* v_cache, int dtype,
+                         const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_ids,
+                         const int32_t* positions, int32_t* slot_mapping, int num_tokens, int num_seqs,
+                         int num_blocks, int block_size, int num_kv_heads, int head_dim, void* stream);
+
+/*
  * Copy-on-write block duplication ([P3] copy-on-write: a shared block is
  * duplicated when a sequence diverges; [P1] "Prefix Caching"): for each pair
  * i, copies every slot and head of physical block src_dst[2i] onto block

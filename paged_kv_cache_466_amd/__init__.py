@@ -15,7 +15,7 @@ __all__ = [
     "PkvError", "lib", "version", "last_error",
     "paged_attn_decode", "paged_attn_partition", "paged_attn_merge",
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
-    "slot_mapping", "reshape_and_cache", "copy_blocks", "quantize_kv",
+    "slot_mapping", "reshape_and_cache", "append_kv", "copy_blocks", "quantize_kv",
     "validate_tables", "BlockPool", "DTYPES",
 ]
 
@@ -53,6 +53,7 @@ _SIGS = {
     "pkv_paged_attn_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
     "pkv_slot_mapping": ([_p, _p, _i, _p, _p, _i, _i, _i, _i, _p], _i),
     "pkv_reshape_and_cache": ([_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p], _i),
+    "pkv_append_kv": ([_p, _p, _p, _p, _i, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p], _i),
     "pkv_copy_blocks": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p], _i),
     "pkv_quantize_kv": ([_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_validate_tables": ([_p, _i, _p, _i, _i, _i, _p, _i], _i),
@@ -230,6 +231,20 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
         raise ValueError("key/value must be [T, Hkv, D] of the cache's dtype")
     _check(lib.pkv_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache),
                                      _ptr(slot_mapping), T, NB, BS, Hkv, D, _stream(key)))
+
+
+def append_kv(key, value, k_cache, v_cache, block_tables, positions, seq_ids=None, slot_mapping=None):
+    """Slot mapping + slot write in one launch (``pkv_append_kv``); key/value
+    [T, Hkv, D] of the cache's dtype.  ``slot_mapping`` (int32 [T]) receives
+    the slots when given."""
+    _contig(key, value, k_cache, v_cache, block_tables, positions, seq_ids, slot_mapping)
+    T = key.shape[0]
+    NB, BS, Hkv, D = k_cache.shape
+    if tuple(key.shape[1:]) != (Hkv, D) or key.shape != value.shape or key.dtype != k_cache.dtype:
+        raise ValueError("key/value must be [T, Hkv, D] of the cache's dtype")
+    _check(lib.pkv_append_kv(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache),
+                             _ptr(block_tables), block_tables.shape[1], _ptr(seq_ids), _ptr(positions),
+                             _ptr(slot_mapping), T, block_tables.shape[0], NB, BS, Hkv, D, _stream(key)))
 
 
 def copy_blocks(k_cache, v_cache, src_dst, k_scales=None, v_scales=None, dtype=None):

@@ -374,6 +374,26 @@ extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, 
                     "pkv_reshape_and_cache");
 }
 
+extern "C" pkv_status pkv_append_kv(const void* key, const void* value, void* k_cache, void* v_cache, int dtype,
+                                    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_ids,
+                                    const int32_t* positions, int32_t* slot_mapping, int num_tokens, int num_seqs,
+                                    int num_blocks, int block_size, int num_kv_heads, int head_dim, void* stream) {
+  pkv_status st = check_cache_shape("pkv_append_kv", block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (!is_float_storage(dtype)) return fail(PKV_EUNSUPPORTED, "pkv_append_kv: dtype must be f32, bf16 or f16");
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return fail(PKV_EINVAL, "pkv_append_kv: negative size");
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !block_tables || !positions)
+    return fail(PKV_EINVAL, "pkv_append_kv: null pointer");
+  if (!seq_ids && num_tokens > num_seqs)
+    return fail(PKV_EINVAL, "pkv_append_kv: without seq_ids, token j belongs to sequence j < num_seqs");
+  return hip_status(launch_append_kv(key, value, k_cache, v_cache, dtype_bytes(dtype), block_tables,
+                                     max_blocks_per_seq, seq_ids, positions, slot_mapping, num_tokens, num_seqs,
+                                     num_blocks, block_size, num_kv_heads, head_dim, stream),
+                    "pkv_append_kv");
+}
+
 extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
                                       const int32_t* src_dst, int n, int dtype, int num_blocks, int block_size,
                                       int num_kv_heads, int head_dim, void* stream) {

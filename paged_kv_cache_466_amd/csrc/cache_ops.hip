@@ -84,6 +84,51 @@ int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, 
 }
 
 // ---------------------------------------------------------------------------
+// append_kv: slot mapping and slot write in one pass.  Thread group of token
+// j computes its slot from the table (as slot_mapping_kernel), optionally
+// records it, and copies the token's K and V rows there.
+// ---------------------------------------------------------------------------
+__global__ void append_kv_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
+                                 uint4* __restrict__ kc, uint4* __restrict__ vc,
+                                 const int32_t* __restrict__ tables, int mbs, const int32_t* __restrict__ seq_ids,
+                                 const int32_t* __restrict__ positions, int32_t* __restrict__ slots_out,
+                                 int num_tokens, int num_seqs, int bs, int num_blocks, int chunks_per_row) {
+  const int j = blockIdx.x;
+  if (j >= num_tokens) return;
+  const int s = seq_ids ? seq_ids[j] : j;
+  const int pos = positions[j];
+  long long slot = -1;
+  if (s >= 0 && s < num_seqs && pos >= 0) {
+    const int lb = pos / bs;
+    if (lb < mbs) {
+      const int32_t pb = tables[(size_t)s * mbs + lb];
+      if (pb >= 0 && pb < num_blocks) slot = (long long)pb * bs + pos % bs;
+    }
+  }
+  if (slots_out && threadIdx.x == 0) slots_out[j] = (int32_t)slot;
+  if (slot < 0) return;
+  const long long src = (long long)j * chunks_per_row, dst = slot * chunks_per_row;
+  for (int c = threadIdx.x; c < chunks_per_row; c += blockDim.x) {
+    kc[dst + c] = key[src + c];
+    vc[dst + c] = value[src + c];
+  }
+}
+
+int launch_append_kv(const void* key, const void* value, void* k_cache, void* v_cache, int elem_bytes,
+                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_ids,
+                     const int32_t* positions, int32_t* slot_mapping, int num_tokens, int num_seqs,
+                     int num_blocks, int block_size, int num_kv_heads, int head_dim, void* stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int chunks_per_row = num_kv_heads * head_dim * elem_bytes / 16;
+  int threads = 64;
+  while (threads < chunks_per_row && threads < 256) threads *= 2;
+  append_kv_kernel<<<num_tokens, threads, 0, (hipStream_t)stream>>>(
+      (const uint4*)key, (const uint4*)value, (uint4*)k_cache, (uint4*)v_cache, block_tables, max_blocks_per_seq,
+      seq_ids, positions, slot_mapping, num_tokens, num_seqs, block_size, num_blocks, chunks_per_row);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // copy_blocks: duplicate whole blocks (K, V and their scale rows).
 // ---------------------------------------------------------------------------
 __global__ void copy_blocks_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc,

@@ -372,12 +372,17 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
   uint8_t* vstage = lds + wave * C::VSTAGE;
   if (kvh >= p.num_kv_heads) return;
 
-  // an empty sequence gets zeros (the head-0 wave of chunk slot s does it)
+  // an empty sequence gets zeros and a plan entry of no chunks (the head-0
+  // wave of chunk slot s does it)
   {
     const int zs = blockIdx.x;
     if (kvh == 0 && zs < p.num_seqs && clamp_len(p.seq_lens[zs], p.mbs) == 0) {
       for (int i = lane; i < p.num_q_heads * D; i += 64)
         store_out<QT>(p.out, (size_t)zs * p.num_q_heads * D + i, 0.f);
+      if (p.plan && lane == 0) {
+        p.plan[2 * zs] = 0;
+        p.plan[2 * zs + 1] = 0;
+      }
     }
   }
 
@@ -806,7 +811,7 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 // was cut into several chunks, out = sum_c 2^(m_c - M) acc_c /
 // sum_c 2^(m_c - M) l_c over its records (one per chunk, in chunk order).
 // Sequences of one chunk were finished by their waves; empty sequences were
-// zeroed.  The decode left each sequence's first chunk and chunk count in
+// zeroed.  The decode left every sequence's first chunk and chunk count in
 // the plan area; 8 record rows at a time are read by D/4 threads with
 // 16-byte loads, 4 rows per thread in flight.
 // ===========================================================================
@@ -823,8 +828,8 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
   const int tid = threadIdx.x;
   const int G = num_q_heads / pa.num_kv_heads;
   const int kvh = h / G, g = h % G;
-  // a sequence without units was zeroed by the decode and wrote no plan entry
-  if (seq_units(clamp_len(pa.seq_lens[s], pa.mbs), pa.psize, pa.sink, pa.window).n == 0) return;
+  // the decode wrote every sequence's entry: no chunks (empty sequence,
+  // zeroed) or one chunk (finished by its waves) leave nothing to merge
   const int np = plan[2 * s + 1];
   if (np <= 1) return;
   // record of chunk c of this head: (first + c) * Hkv + kvh

@@ -95,6 +95,10 @@ int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, 
                              int elem_bytes, const int32_t* slot_mapping, int num_tokens,
                              int num_blocks, int block_size, int num_kv_heads, int head_dim,
                              void* stream);
+int launch_append_kv(const void* key, const void* value, void* k_cache, void* v_cache, int elem_bytes,
+                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_ids,
+                     const int32_t* positions, int32_t* slot_mapping, int num_tokens, int num_seqs,
+                     int num_blocks, int block_size, int num_kv_heads, int head_dim, void* stream);
 int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
                        const int32_t* src_dst, int n, int elem_bytes, int num_blocks, int block_size,
                        int num_kv_heads, int head_dim, void* stream);

@@ -69,9 +69,10 @@ class GpuRun:
         if do_step and w.append:
             self.decode_step(tensors)
 
-    def decode_step(self, tensors):
+    def decode_step(self, tensors, fused=False):
         """Host pool append -> copy-on-write copies -> device slot mapping ->
-        slot write.  Also returns the host pool's slots for comparison."""
+        slot write (``fused``: both in one pkv_append_kv launch).  Also keeps
+        the host pool's slots for comparison."""
         w = self.w
         host_slots = []
         lens = self.lens.cpu().numpy()
@@ -86,10 +87,15 @@ class GpuRun:
             pkv.copy_blocks(self.k_cache, self.v_cache, pairs, self.k_scales, self.v_scales,
                             dtype=w.kv_dtype if w.kv_dtype in ("i8", "fp8e4m3") else None)
         positions = self.lens.clone()
-        self.step_slots = pkv.slot_mapping(self.block_tables, positions, w.num_blocks)
         self.host_step_slots = np.asarray(host_slots, dtype=np.int64)
-        pkv.reshape_and_cache(tensors["new_key"], tensors["new_value"], self.k_cache, self.v_cache,
-                              self.step_slots)
+        if fused:
+            self.step_slots = torch.empty(w.S, dtype=torch.int32, device=self.device)
+            pkv.append_kv(tensors["new_key"], tensors["new_value"], self.k_cache, self.v_cache, self.block_tables,
+                          positions, slot_mapping=self.step_slots)
+        else:
+            self.step_slots = pkv.slot_mapping(self.block_tables, positions, w.num_blocks)
+            pkv.reshape_and_cache(tensors["new_key"], tensors["new_value"], self.k_cache, self.v_cache,
+                                  self.step_slots)
         self.lens += 1
 
     def decode(self, query, partition_size=0, sink=None, window=None, out=None, stream_kv=False):

@@ -98,6 +98,20 @@ def test_decode_parity(name, psize):
     assert err <= TOL[w.q_dtype], err
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama_small", "prefix_small", "llama_small_f16"])
+def test_fused_append_matches_oracle(name):
+    """pkv_append_kv (slot mapping + slot write in one launch) leaves the same
+    slots and caches as the oracle's step, copy-on-write included."""
+    from gpu_pipeline import GpuRun
+    w, t, g0, o = run_case(name)
+    g = GpuRun(w, t, do_step=False)
+    g.decode_step(t, fused=True)
+    assert (g.step_slots.cpu().numpy().astype(np.int64) == o.step_slots).all()
+    assert g.cow == o.cow and g.tables == o.tables
+    assert raw_cpu(g.k_cache, w.kv_dtype).tobytes() == o.k_cache.tobytes()
+    assert raw_cpu(g.v_cache, w.kv_dtype).tobytes() == o.v_cache.tobytes()
+
+
 @pytest.mark.parametrize("name", [n for n in CASES if n != "tiny_fp32"])
 def test_decode_streaming_policy_is_bit_identical(name):
     """PKV_DECODE_STREAM_KV only changes the cache policy of the loads: the
