@@ -230,6 +230,12 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return
 
+    # the 128K split-K measurement runs first, in a child process of its own,
+    # so that its multi-GiB allocations start from a fresh device heap
+    long_ctx = None
+    if not args.no_long_context and args.workload != "ctx128k_b4":
+        long_ctx = long_context_entry(min(args.steps, 50), min(args.warmup, 20))
+
     from workloads import get_workload
 
     ov = {}
@@ -273,22 +279,29 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, m["t"], lens, args.cpu_seconds)
-    if not args.no_long_context and args.workload != "ctx128k_b4":
-        del m
-        torch.cuda.empty_cache()
-        lw = get_workload("ctx128k_b4")
-        lm = measure(lw, min(args.steps, 50), min(args.warmup, 10), args.copies)
-        lval = lm["kv_bytes"] / (lm["ms_per_step"] * 1e-3) / 1e9
-        result["long_context"] = {
-            "workload": DESCRIPTIONS["ctx128k_b4"],
-            "partition_size": lm["psize"], "kv_bytes_per_step": int(lm["kv_bytes"]),
-            "ms_per_step": round(lm["ms_per_step"], 5), "steps_per_s": round(1000.0 / lm["ms_per_step"], 1),
-            "value_gbps": round(lval, 2), "partition_us": round(lm["part_ms"] * 1e3, 2),
-            "merge_us": round(lm["merge_ms"] * 1e3, 2),
-            "attn_kv_gbps": round(lm["kv_bytes"] / (lm["attn_ms"] * 1e-3) / 1e9, 2),
-            "roofline": roofline(lm),
-        }
+    if long_ctx is not None:
+        result["long_context"] = long_ctx
     print(json.dumps(result), flush=True)
+
+
+def long_context_entry(steps, warmup):
+    """Measures the 128K-context split-K workload in a child process and
+    returns its summary for the long_context field."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", "ctx128k_b4", "--no-cpu-baseline",
+           "--no-long-context", "--steps", str(steps), "--warmup", str(warmup)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr[-2000:])
+        raise RuntimeError(f"long-context measurement failed ({r.returncode})")
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return {
+        "workload": d["config"]["workload"],
+        "partition_size": d["config"]["partition_size"], "kv_bytes_per_step": d["config"]["kv_bytes_per_step"],
+        "ms_per_step": d["ms_per_step"], "steps_per_s": d["steps_per_s"], "value_gbps": d["value"],
+        "partition_us": d["partition_us"], "merge_us": d["merge_us"], "attn_kv_gbps": d["attn_kv_gbps"],
+        "steps": steps, "warmup": warmup, "roofline": d["roofline"],
+    }
 
 
 def cpu_baseline(w, t, lens, budget_s):
