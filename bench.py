@@ -141,8 +141,8 @@ def measure(w, steps, warmup, copies):
     kv_bytes = kv_bytes_per_step(w, lens)
     S, Hq, D = t["query"].shape
     max_len = g0.mbs * 16
-    psize = w.partition_size or pkv.paged_attn_partition_size(S, w.Hkv, max_len)
-    nbytes = pkv.paged_attn_workspace_bytes(S, Hq, w.Hkv, D, max_len, psize)
+    psize = w.partition_size or pkv.paged_attn_partition_size(w.kv_dtype, max_len)
+    nbytes = pkv.paged_attn_workspace_bytes(w.kv_dtype, S, Hq, w.Hkv, D, max_len, psize)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["query"])
     positions = (g0.lens - 1).contiguous()

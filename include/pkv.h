@@ -109,34 +109,38 @@ enum {
 /*
  * Number of KV partitions per sequence for a given bound on the sequence
  * length: ceil(max_seq_len / partition_size).  partition_size 0 lets the
- * library choose (see pkv_paged_attn_partition_size); otherwise it must be a
- * positive multiple of block_size.  Returns 0 on bad arguments.
+ * library choose for a cache of kv_dtype (see
+ * pkv_paged_attn_partition_size); otherwise it must be a positive multiple
+ * of block_size.  Returns 0 on bad arguments.
  */
-int pkv_paged_attn_num_partitions(int num_seqs, int num_kv_heads, int max_seq_len,
-                                  int block_size, int partition_size);
+int pkv_paged_attn_num_partitions(int kv_dtype, int max_seq_len, int block_size, int partition_size);
 
 /*
  * The partition size (tokens) the library picks when the caller passes 0.
  * Partitions are the split granularity of the decode: a sequence's tokens
- * are cut at multiples of partition_size, the decode hands each wave a run of
- * consecutive partitions of one (sequence, KV head), sized from the actual
- * lengths so that the waves fill the GPU evenly, and the partial results of
- * the runs are combined by log-sum-exp.  A result equal to or above
- * max_seq_len means a single pass (no partials, no merge).
+ * are cut only at multiples of partition_size.  For 16-bit and code caches
+ * the decode numbers the partitions that hold a kept token across the whole
+ * batch and gives every workgroup an equal run of them (a run may end
+ * inside one sequence and continue over the next); a sequence cut over
+ * several workgroups gets one partial result per piece, combined by
+ * log-sum-exp.  The choice: one pass (a result >= max_seq_len, no partials)
+ * up to 512 tokens; above, one block for 16-bit and code caches and 64
+ * tokens for fp32 caches.
  */
-int pkv_paged_attn_partition_size(int num_seqs, int num_kv_heads, int max_seq_len, int block_size);
+int pkv_paged_attn_partition_size(int kv_dtype, int max_seq_len, int block_size);
 
 /*
- * Bytes of scratch pkv_paged_attn_decode needs for fp32 partial records,
- * each holding a query group's unnormalised accumulators acc[G][head_dim],
- * running maxima m[16] and softmax sums l[16] (G = num_q_heads /
- * num_kv_heads): one per wave for 16-bit and code caches, one per (sequence,
- * KV head, partition) for fp32 caches; the larger of the two.  0 when no
- * sequence can be split.  max_seq_len must be max_blocks_per_seq *
- * block_size of the later call; the size depends on the current device's
- * compute-unit count.
+ * Bytes of scratch pkv_paged_attn_decode needs for a cache of kv_dtype.
+ * Partial records each hold a query group's unnormalised accumulators
+ * acc[G][head_dim], running maxima m[16] and softmax sums l[16] (G =
+ * num_q_heads / num_kv_heads).  16-bit and code caches: 16 bytes per
+ * sequence (rounded up to 256) for the split plan, then two records per
+ * (workgroup, KV head); the workgroup count depends on the current device's
+ * compute units.  fp32 caches: one record per (sequence, KV head,
+ * partition).  0 when no sequence can be split.  max_seq_len must be
+ * max_blocks_per_seq * block_size of the later call.
  */
-size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+size_t pkv_paged_attn_workspace_bytes(int kv_dtype, int num_seqs, int num_q_heads, int num_kv_heads,
                                       int head_dim, int max_seq_len, int partition_size);
 
 /*
@@ -157,11 +161,14 @@ size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_
  *           [P2] s.8).  k_scales/v_scales are ignored (may be NULL) otherwise.
  * head_dim: 64 or 128.  block_size: 16.  num_q_heads % num_kv_heads == 0.
  * partition_size: 0 = library's choice, else a positive multiple of
- *           block_size: the split granularity (see
- *           pkv_paged_attn_partition_size).  When a sequence is split over
- *           several waves, each wave writes a partial record covering whole
- *           partitions to the workspace and a merge kernel combines them by
- *           log-sum-exp; a sequence handled by one wave is written directly.
+ *           block_size, at most 128 * min(num_kv_heads, 8) blocks for 16-bit
+ *           and code caches: the split granularity (see
+ *           pkv_paged_attn_partition_size).  A sequence split over several
+ *           workgroups gets a partial record per piece in the workspace,
+ *           and a merge kernel combines them by log-sum-exp; a sequence
+ *           handled by one workgroup is written directly.
+ *           16-bit and code caches also need num_seqs * max_blocks_per_seq
+ *           < 2^29 (PKV_EUNSUPPORTED otherwise).
  * flags:    PKV_DECODE_* bits (0 for none); unknown bits give PKV_EINVAL.
  * workspace: device scratch of at least pkv_paged_attn_workspace_bytes(...)
  *           bytes, 128-byte aligned (may be NULL when that is 0).  Its

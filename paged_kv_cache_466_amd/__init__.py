@@ -45,9 +45,9 @@ _ATTN = [_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
 _SIGS = {
     "pkv_last_error": ([], ctypes.c_char_p),
     "pkv_version": ([], ctypes.c_char_p),
-    "pkv_paged_attn_num_partitions": ([_i, _i, _i, _i, _i], _i),
-    "pkv_paged_attn_partition_size": ([_i, _i, _i, _i], _i),
-    "pkv_paged_attn_workspace_bytes": ([_i, _i, _i, _i, _i, _i], _sz),
+    "pkv_paged_attn_num_partitions": ([_i, _i, _i, _i], _i),
+    "pkv_paged_attn_partition_size": ([_i, _i, _i], _i),
+    "pkv_paged_attn_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "pkv_paged_attn_decode": (_ATTN, _i),
     "pkv_paged_attn_partition": (_ATTN, _i),
     "pkv_paged_attn_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
@@ -123,17 +123,27 @@ def _contig(*tensors):
 # decode attention
 # ---------------------------------------------------------------------------
 
-def paged_attn_num_partitions(num_seqs, num_kv_heads, max_seq_len, partition_size=0, block_size=16):
-    return lib.pkv_paged_attn_num_partitions(num_seqs, num_kv_heads, max_seq_len, block_size, partition_size)
+def _dtype_code(dt):
+    """A pkv dtype code from a name ("bf16", "i8", ...), a torch dtype or a code."""
+    if isinstance(dt, str):
+        return DTYPES[dt]
+    if isinstance(dt, torch.dtype):
+        return _TORCH_TO_PKV[dt]
+    return int(dt)
 
 
-def paged_attn_partition_size(num_seqs, num_kv_heads, max_seq_len, block_size=16):
-    return lib.pkv_paged_attn_partition_size(num_seqs, num_kv_heads, max_seq_len, block_size)
+def paged_attn_num_partitions(kv_dtype, max_seq_len, partition_size=0, block_size=16):
+    return lib.pkv_paged_attn_num_partitions(_dtype_code(kv_dtype), max_seq_len, block_size, partition_size)
 
 
-def paged_attn_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size=0):
-    return lib.pkv_paged_attn_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                              partition_size)
+def paged_attn_partition_size(kv_dtype, max_seq_len, block_size=16):
+    return lib.pkv_paged_attn_partition_size(_dtype_code(kv_dtype), max_seq_len, block_size)
+
+
+def paged_attn_workspace_bytes(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                               partition_size=0):
+    return lib.pkv_paged_attn_workspace_bytes(_dtype_code(kv_dtype), num_seqs, num_q_heads, num_kv_heads,
+                                              head_dim, max_seq_len, partition_size)
 
 
 def _attn_call(fn, out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_scales, v_scales,
@@ -156,12 +166,12 @@ def _attn_call(fn, out, query, k_cache, v_cache, block_tables, seq_lens, sm_scal
     return out
 
 
-def _workspace_for(query, k_cache, block_tables, partition_size, workspace):
+def _workspace_for(query, k_cache, block_tables, partition_size, workspace, kv_dtype):
     if workspace is not None:
         return workspace
     S, Hq, D = query.shape
-    nbytes = paged_attn_workspace_bytes(S, Hq, k_cache.shape[2], D, block_tables.shape[1] * k_cache.shape[1],
-                                        partition_size)
+    nbytes = paged_attn_workspace_bytes(_dtype(k_cache, kv_dtype), S, Hq, k_cache.shape[2], D,
+                                        block_tables.shape[1] * k_cache.shape[1], partition_size)
     if nbytes == 0:
         return None
     return torch.empty(nbytes, dtype=torch.uint8, device=query.device)
@@ -178,7 +188,7 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens, sm_s
     uint8 tensors.  ``stream_kv`` sets PKV_DECODE_STREAM_KV (no block is
     shared between the batch's sequences).
     """
-    workspace = _workspace_for(query, k_cache, block_tables, partition_size, workspace)
+    workspace = _workspace_for(query, k_cache, block_tables, partition_size, workspace, kv_dtype)
     return _attn_call(lib.pkv_paged_attn_decode, out, query, k_cache, v_cache, block_tables, seq_lens,
                       sm_scale, k_scales, v_scales, partition_size, sink_tokens, window_tokens, workspace,
                       kv_dtype, stream_kv)

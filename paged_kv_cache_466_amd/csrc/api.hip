@@ -59,28 +59,29 @@ static int device_cu_count() {
   return cache[dev];
 }
 
-int decode_waves(int num_seqs, int num_kv_heads) {
+int decode_slots(int num_seqs, int num_kv_heads, int num_partitions, int partition_size) {
   constexpr int kWavesPerCU = 8;   // two waves per SIMD: the wave kernel's register budget
-  const long long runs = (long long)num_seqs * num_kv_heads;
-  const long long fill = (long long)kWavesPerCU * device_cu_count();
-  long long n = runs > fill ? runs : fill;
-  n = (n + num_kv_heads - 1) / num_kv_heads * num_kv_heads;   // whole chunk slots (one wave per KV head)
-  return n > 0x7FFFFFFF ? 0x7FFFFFFF / num_kv_heads * num_kv_heads : (int)n;
+  long long k = ((long long)kWavesPerCU * device_cu_count() + num_kv_heads - 1) / num_kv_heads;
+  if (k < num_seqs) k = num_seqs;
+  // a workgroup takes at most ceil(units / k) partitions (or the minimum):
+  // both must fit its block list
+  const long long blocks_per_unit = partition_size / 16;
+  const long long units_cap = decode_list_cap(num_kv_heads) / (blocks_per_unit > 0 ? blocks_per_unit : 1);
+  if (units_cap > 0) {
+    const long long need = ((long long)num_seqs * num_partitions + units_cap - 1) / units_cap;
+    if (k < need) k = need;
+  }
+  return k > 0x7FFFFFFF ? 0x7FFFFFFF : (int)k;
 }
 
-size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int num_partitions,
-                       int partition_size) {
+size_t workspace_total(int kv_dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int num_partitions, int partition_size) {
   if (num_partitions <= 1 || num_seqs <= 0) return 0;
   const int G = num_q_heads / num_kv_heads;
   const size_t rec = partial_record_floats(G, head_dim) * sizeof(float);
-  // fp32 path: a record per (sequence, KV head, partition)
-  const size_t per_part = (size_t)num_seqs * num_kv_heads * num_partitions * rec;
-  // wave path, when a sequence can be split over waves: the per-sequence
-  // plan area, then a record per wave
-  const size_t per_wave = num_partitions > min_units_per_wave(partition_size)
-                              ? plan_area_bytes(num_seqs) + (size_t)decode_waves(num_seqs, num_kv_heads) * rec
-                              : 0;
-  return align256(per_part > per_wave ? per_part : per_wave);
+  if (kv_dtype == PKV_F32) return align256((size_t)num_seqs * num_kv_heads * num_partitions * rec);
+  const size_t slots = 2 * (size_t)decode_slots(num_seqs, num_kv_heads, num_partitions, partition_size);
+  return align256(plan_area_bytes(num_seqs) + slots * num_kv_heads * rec);
 }
 
 static bool check_env() {
@@ -93,16 +94,14 @@ static bool check_env() {
 }
 
 // Resolve a user partition size (0 = auto) for the given shape.
-static int resolve_partition(int num_seqs, int num_kv_heads, int max_len, int block_size, int psize) {
+static int resolve_partition(int kv_dtype, int max_len, int block_size, int psize) {
   if (psize > 0) return psize;
-  (void)num_seqs;
-  (void)num_kv_heads;
   // Bounds up to 512 tokens run as one pass without partials.  Longer ones
-  // are split at 64-token granularity, fine enough for the decode to balance
-  // its waves' stretches of each sequence.
+  // are split at block granularity for the 16-bit and code caches, whose
+  // decode balances its workgroups to the block, and at 64 tokens for fp32.
   const int single = ((max_len + block_size - 1) / block_size) * block_size;
   if (max_len <= 512) return single > 0 ? single : block_size;
-  return 64;
+  return kv_dtype == PKV_F32 ? 64 : block_size;
 }
 
 }  // namespace pkv
@@ -112,27 +111,26 @@ using namespace pkv;
 extern "C" const char* pkv_last_error(void) { return g_err; }
 extern "C" const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 
-extern "C" int pkv_paged_attn_partition_size(int num_seqs, int num_kv_heads, int max_seq_len, int block_size) {
+extern "C" int pkv_paged_attn_partition_size(int kv_dtype, int max_seq_len, int block_size) {
   if (block_size <= 0 || max_seq_len < 0) return 0;
-  return resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, 0);
+  return resolve_partition(kv_dtype, max_seq_len, block_size, 0);
 }
 
-extern "C" int pkv_paged_attn_num_partitions(int num_seqs, int num_kv_heads, int max_seq_len, int block_size,
-                                             int partition_size) {
+extern "C" int pkv_paged_attn_num_partitions(int kv_dtype, int max_seq_len, int block_size, int partition_size) {
   if (block_size <= 0 || max_seq_len < 0 || partition_size < 0) return 0;
   if (partition_size > 0 && partition_size % block_size) return 0;
-  const int ps = resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_size);
+  const int ps = resolve_partition(kv_dtype, max_seq_len, block_size, partition_size);
   const int n = (max_seq_len + ps - 1) / ps;
   return n < 1 ? 1 : n;
 }
 
-extern "C" size_t pkv_paged_attn_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                                 int max_seq_len, int partition_size) {
-  const int np = pkv_paged_attn_num_partitions(num_seqs, num_kv_heads, max_seq_len, 16, partition_size);
+extern "C" size_t pkv_paged_attn_workspace_bytes(int kv_dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                                                 int head_dim, int max_seq_len, int partition_size) {
+  const int np = pkv_paged_attn_num_partitions(kv_dtype, max_seq_len, 16, partition_size);
   if (np <= 1 || num_seqs <= 0) return 0;
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return 0;
-  const int ps = resolve_partition(num_seqs, num_kv_heads, max_seq_len, 16, partition_size);
-  return workspace_total(num_seqs, num_q_heads, num_kv_heads, head_dim, np, ps);
+  const int ps = resolve_partition(kv_dtype, max_seq_len, 16, partition_size);
+  return workspace_total(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, np, ps);
 }
 
 extern "C" pkv_status pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
@@ -213,26 +211,36 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
   if (a.partition_size < 0 || (a.partition_size > 0 && a.partition_size % a.block_size))
     return fail(PKV_EINVAL, "%s: partition_size must be 0 or a positive multiple of block_size", who);
   const int max_len = a.max_blocks_per_seq * a.block_size;
-  a.partition_size = resolve_partition(a.num_seqs, a.num_kv_heads, max_len, a.block_size, a.partition_size);
+  a.partition_size = resolve_partition(a.kv_dtype, max_len, a.block_size, a.partition_size);
   a.num_partitions = (max_len + a.partition_size - 1) / a.partition_size;
   if (a.num_partitions < 1) a.num_partitions = 1;
   if (a.num_seqs == 0) return PKV_OK;
   if (!a.out || !a.seq_lens) return fail(PKV_EINVAL, "%s: null pointer argument", who);
   if (need_inputs && (!a.query || !a.k_cache || !a.v_cache || !a.block_tables))
     return fail(PKV_EINVAL, "%s: null pointer argument", who);
-  a.num_waves = decode_waves(a.num_seqs, a.num_kv_heads);
-  a.min_units = min_units_per_wave(a.partition_size);
-  a.may_split = a.num_partitions > a.min_units;
+  const bool wave_path = a.q_dtype != PKV_F32;
+  if (wave_path) {
+    // the decode keeps sequence numbers in 23 bits, table offsets and unit
+    // counts in 31
+    if (a.num_seqs >= (1 << 23) || (long long)a.num_seqs * a.max_blocks_per_seq >= (1LL << 29) ||
+        (long long)a.num_seqs * a.num_partitions >= (1LL << 30))
+      return fail(PKV_EUNSUPPORTED, "%s: batch too large (num_seqs * max_blocks_per_seq >= 2^29)", who);
+    a.list_cap = decode_list_cap(a.num_kv_heads);
+    if (a.partition_size / a.block_size > a.list_cap)
+      return fail(PKV_EINVAL, "%s: partition_size above %d tokens", who, a.list_cap * a.block_size);
+    a.num_slots = decode_slots(a.num_seqs, a.num_kv_heads, a.num_partitions, a.partition_size);
+    a.min_units = min_units_per_wave(a.partition_size);
+  }
+  a.may_split = a.num_partitions > 1;
   a.ws = nullptr;
   a.plan = nullptr;
-  const bool needs_ws = a.q_dtype == PKV_F32 ? a.num_partitions > 1 : a.may_split;
-  if (needs_ws) {
-    const size_t total = workspace_total(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.num_partitions,
-                                         a.partition_size);
+  if (a.may_split) {
+    const size_t total = workspace_total(a.kv_dtype, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim,
+                                         a.num_partitions, a.partition_size);
     if (!workspace || workspace_bytes < total)
       return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, total, workspace_bytes);
     if (((uintptr_t)workspace) & 127) return fail(PKV_EINVAL, "%s: workspace must be 128-byte aligned", who);
-    if (a.q_dtype == PKV_F32) {
+    if (!wave_path) {
       a.ws = (float*)workspace;
     } else {
       a.plan = (int*)workspace;

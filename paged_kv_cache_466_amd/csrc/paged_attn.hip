@@ -6,25 +6,26 @@
 // grouped query heads against each block's keys (GQA, "KV Cache Engineering"
 // section 1: the G = Hq/Hkv query heads of a group read the same KV head),
 // keeps an online softmax and accumulates P.V.  The tokens of a sequence are
-// split into partitions of partition_size tokens; a partition either writes
-// the final output (one partition per sequence) or fp32 partials (m, l, acc)
-// that a merge kernel combines by log-sum-exp.
+// cut only at multiples of partition_size; a piece of a sequence either
+// writes the final output (the whole sequence in one piece) or fp32 partials
+// (m, l, acc) that a merge kernel combines by log-sum-exp.
 //
 // Kernels:
 //  * paged_attn_wave_kernel - bf16 / f16 caches and INT8 / FP8-E4M3 codes
-//    (converted to the query's 16-bit type in registers).  One wave per
-//    (partition, KV head, sequence); the waves never synchronise.  Per
-//    16-token block: S^T = K Q^T on v_mfma_f32_16x16x32 (K rows go straight
-//    from HBM into the A operand; the query group, padded to 16 heads, is the
-//    B operand), then out^T += V^T P^T on v_mfma_f32_16x16x16, where the
-//    score tile already has the B-operand layout and V^T is read from an LDS
-//    copy of the block with the transposing ds_read_b64_tr_b16.  Blocks are
-//    loaded with buffer loads into a ring of DEPTH register tiles, so DEPTH-1
-//    blocks are in flight while one computes.  Rows outside the kept range
-//    and tiles past the end are given an out-of-range buffer offset: the
-//    hardware returns zeros for them without touching memory, which both
-//    masks poisoned slots (no 0 * NaN in the MFMA) and keeps the ring
-//    branch-free.
+//    (converted to the query's 16-bit type in registers).  Each workgroup
+//    takes an equal run of the batch's partitions (stream-K style, crossing
+//    sequence boundaries) and runs one wave per KV head over the same list
+//    of physical blocks.  Per 16-token block: S^T = K Q^T on
+//    v_mfma_f32_16x16x32 (K rows go straight from HBM into the A operand;
+//    the query group, padded to 16 heads, is the B operand), then out^T +=
+//    V^T P^T on v_mfma_f32_16x16x16, where the score tile already has the
+//    B-operand layout and V^T is read from an LDS copy of the block with the
+//    transposing ds_read_b64_tr_b16.  Blocks are loaded with buffer loads
+//    into a ring of DEPTH register tiles, so DEPTH-1 blocks are in flight
+//    while one computes.  Rows outside the kept range and tiles past the end
+//    are given an out-of-range buffer offset: the hardware returns zeros for
+//    them without touching memory, which both masks poisoned slots (no
+//    0 * NaN in the MFMA) and keeps the ring branch-free.
 //  * paged_attn_simple_kernel - fp32 caches (and any group size): scores in
 //    LDS, plain fp32 FMAs.  Exact fp32 arithmetic, for the fp32 path.
 //  * paged_attn_merge_kernel - log-sum-exp combine of the partials.
@@ -53,12 +54,15 @@ struct AttnParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   float* ws;            // partial records (see AttnArgs)
-  int* plan;            // per sequence: first chunk, chunk count (wave path, split decodes)
+  int* plan;            // wave path: per sequence (slot of its first record, first and last workgroup, 0)
   int rec_floats;       // floats per record
   int num_seqs, mbs, num_q_heads, num_kv_heads, num_blocks;
   int partition_size, num_partitions;
   int sink, window;
-  float scale_log2;   // sm_scale * log2(e)
+  int min_units;        // fewest units a workgroup takes
+  int list_cap;         // blocks a workgroup's list holds
+  int table_bytes;      // bytes of block_tables
+  float scale_log2;     // sm_scale * log2(e)
 };
 
 __device__ __forceinline__ int clamp_len(int L, int mbs) {
@@ -208,21 +212,25 @@ __device__ __forceinline__ int qk_doff(int c, int kg) {
 }
 
 // ===========================================================================
-// Split plan
+// Work split
 //
 // A "unit" is a partition (partition_size tokens from t = 0) that holds at
-// least one kept token.  A sequence with n units is cut into
-// k = ceil(n / Q) near-equal chunks of consecutive units.  One workgroup per
-// (chunk, group of up to 8 KV heads) runs one wave per KV head, so the waves
-// of a workgroup stream the same physical blocks at the same time (each
-// reads its head's rows of every block), and each wave writes one partial
-// record (or the final output when its sequence is a single chunk).  Q, the
-// largest chunk, is the smallest value that keeps the waves within NW:
-//   waves(Q) = Hkv * sum_s ceil(n_s / Q) <= Hkv * (U / Q + S_ne) <= NW
-// for Q >= Hkv * U / (NW - Hkv * S_ne), with U = sum_s n_s and S_ne the
-// sequences with a unit.  Chunks are numbered sequence-major.  The decode
-// and the merge compute the plan the same way from the lengths, so nothing
-// is stored between the kernels.
+// least one kept token.  Numbering the units of all sequences one after the
+// other gives U units.  With K workgroups along x, Q = max(min_units,
+// ceil(U / K)) units per workgroup and K_eff = ceil(U / Q) workgroups at
+// work, workgroup w takes units [w U / K_eff, (w + 1) U / K_eff): all get Q
+// or Q - 1 units, and a range may begin or end inside a sequence and may
+// cover several sequences.  A workgroup runs one wave per KV head of its
+// group of heads; the waves walk the same list of physical blocks at the
+// same time, each reading its head's rows.
+//
+// The part of a sequence inside one workgroup is a "segment".  A whole
+// sequence is finished where it is; otherwise each wave writes a partial
+// record: slot 2w for the workgroup's first segment, 2w + 1 for its last (a
+// segment between the two always holds its whole sequence).  The workgroup
+// holding a sequence's first unit leaves in the plan area, for the merge,
+// the slot of that first record and the first and last workgroups the
+// sequence reaches; every later workgroup's record of it sits in its slot 2w.
 // ===========================================================================
 struct SeqUnits {
   int np;   // partitions covering the sequence
@@ -245,13 +253,6 @@ __device__ __forceinline__ SeqUnits seq_units(int L, int psize, int sink, int wi
 }
 __device__ __forceinline__ int unit_partition(const SeqUnits& u, int i) { return i < u.a ? i : u.b0 + (i - u.a); }
 
-struct PlanArgs {
-  const int32_t* seq_lens;
-  int num_seqs, mbs, num_kv_heads, psize, sink, window;
-  int num_waves;      // NW
-  int min_units;      // Q never goes below this
-};
-
 __device__ __forceinline__ int lane_scan_incl(int x, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -261,94 +262,147 @@ __device__ __forceinline__ int lane_scan_incl(int x, int lane) {
   return x;
 }
 
-// Units per chunk, Q.  Called by a whole wave; the result is wave-uniform.
-// With K = NW / Hkv chunk slots, Q is the smallest value with
-// sum_s ceil(n_s / Q) <= K, found by bisection between U / K (below it the
-// sum exceeds K) and U / (K - S_ne) (at or above it the sum fits); it never
-// goes below min_units, nor above the longest sequence's unit count.
-__device__ int plan_units_per_chunk(const PlanArgs& a, int lane) {
-  long long U = 0;
-  int s_ne = 0, nmax = 0;
-  for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
-    const int s = s0 + lane;
-    int n = 0;
-    if (s < a.num_seqs) n = seq_units(clamp_len(a.seq_lens[s], a.mbs), a.psize, a.sink, a.window).n;
-    const int incl = lane_scan_incl(n, lane);
-    U += __shfl(incl, 63, 64);
-    s_ne += __popcll(__ballot(n > 0));
-    nmax = max(nmax, n);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
-  const int floor_q = max(1, a.min_units);
-  if (nmax <= floor_q) return floor_q;                  // every sequence is one chunk
-  const long long K = a.num_waves / a.num_kv_heads;     // chunk slots
-  auto chunks = [&](int Q) {
-    long long total = 0;
-    for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
-      const int s = s0 + lane;
-      int k = 0;
-      if (s < a.num_seqs) k = (seq_units(clamp_len(a.seq_lens[s], a.mbs), a.psize, a.sink, a.window).n + Q - 1) / Q;
-      total += __shfl(lane_scan_incl(k, lane), 63, 64);
-    }
-    return total;
-  };
-  long long hi = K > s_ne ? (U + (K - s_ne) - 1) / (K - s_ne) : nmax;
-  if (hi > nmax) hi = nmax;
-  if (hi < floor_q) hi = floor_q;
-  long long lo = (U + K - 1) / K;
-  if (lo < floor_q) lo = floor_q;
-  if (lo > hi) lo = hi;
-  while (lo < hi) {
-    const int mid = (int)((lo + hi) / 2);
-    if (chunks(mid) <= K) hi = mid;
-    else lo = mid + 1;
-  }
-  return (int)hi;
-}
-
-struct ChunkInfo {
-  int s, c;        // sequence and chunk index within it (s = -1: past the end)
-  int chunks;      // chunks of this sequence (0 for an empty sequence)
-  int first;       // number of the sequence's first chunk
+// 64 consecutive sequences, lane i describing sequence s0 + i.
+struct SeqWindow {
+  int s0;      // first sequence (uniform)
+  int base;    // global number of its first unit (uniform)
+  int total;   // units in the window (uniform)
+  int L;       // this lane's clamped length
+  int n;       // its units
+  int P;       // global number of its first unit
 };
 
-// Locates chunk number `target` (by_chunk) or the chunks of sequence
-// `target`.  Called by a whole wave; the result is wave-uniform.
-__device__ ChunkInfo plan_locate(const PlanArgs& a, int Q, int lane, bool by_chunk, int target) {
-  ChunkInfo r;
-  r.s = -1;
-  r.c = r.chunks = r.first = 0;
-  int base = 0;
-  for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
-    const int s = s0 + lane;
-    int k = 0;   // chunks of sequence s
-    if (s < a.num_seqs) {
-      const int n = seq_units(clamp_len(a.seq_lens[s], a.mbs), a.psize, a.sink, a.window).n;
-      k = (n + Q - 1) / Q;
-    }
-    const int incl = lane_scan_incl(k, lane);
-    const int lo = base + incl - k;
-    const bool hit = by_chunk ? (target >= lo && target < lo + k) : (s == target);
-    const unsigned long long m = __ballot(hit);
-    if (m) {
-      const int ln = __ffsll((long long)m) - 1;
-      r.s = s0 + ln;
-      r.chunks = __shfl(k, ln, 64);
-      r.first = __shfl(lo, ln, 64);
-      r.c = by_chunk ? target - r.first : 0;
-      return r;
-    }
-    base += __shfl(incl, 63, 64);
+__device__ __forceinline__ SeqWindow load_window(const AttnParams& p, int s0, int base, int lane) {
+  SeqWindow w;
+  w.s0 = s0;
+  w.base = base;
+  const int s = s0 + lane;
+  w.L = s < p.num_seqs ? clamp_len(p.seq_lens[s], p.mbs) : 0;
+  w.n = seq_units(w.L, p.partition_size, p.sink, p.window).n;
+  const int incl = lane_scan_incl(w.n, lane);
+  w.P = base + incl - w.n;
+  w.total = __builtin_amdgcn_readlane(incl, 63);
+  return w;
+}
+
+// Blocks of units [i0, i1) of a sequence of length L, in logical order:
+// blocks lb_begin .. lb_begin + n_a - 1, then b0 .. b0 + (n_need - n_a) - 1
+// (the blocks between hold no kept token).
+struct SegBlocks {
+  int lb_begin, n_a, b0, n_need;
+};
+
+__device__ __forceinline__ SegBlocks segment_blocks(const AttnParams& p, int L, int i0, int i1) {
+  const SeqUnits su = seq_units(L, p.partition_size, p.sink, p.window);
+  const int t_begin = unit_partition(su, i0) * p.partition_size;
+  const int t_end = min((unit_partition(su, i1 - 1) + 1) * p.partition_size, L);
+  SegBlocks b;
+  b.lb_begin = t_begin / kBS;
+  const int lb_end = (t_end + kBS - 1) / kBS;
+  int a1 = lb_end, b0 = lb_end;
+  if ((p.sink | p.window) != 0) {
+    const int sink_end = min(lb_end, (p.sink + kBS - 1) / kBS);   // blocks holding a sink token
+    a1 = max(b.lb_begin, sink_end);
+    b0 = p.window > 0 ? min(lb_end, max(max(b.lb_begin, max(0, L - p.window) / kBS), a1)) : lb_end;
   }
-  return r;
+  b.n_a = a1 - b.lb_begin;
+  b.b0 = b0;
+  b.n_need = b.n_a + (lb_end - b0);
+  return b;
 }
 
 constexpr int kMaxWavesPerGroup = 8;   // KV heads per workgroup
+constexpr int kQueryLds = 6144;        // LDS bytes per wave for the queries of its first segments
+constexpr int kMaxQuerySegs = 64;      // segments whose sequence number is kept for that
+constexpr int kEndKey = -1;            // key of the list entry after the last block
+
+// LDS of a workgroup of `waves` waves: per wave a V staging area and a query
+// area, then the block list (list_cap entries and the end entry), the
+// sequences of the first segments and two counters.
+__host__ __device__ constexpr int wave_group_lds(int vstage, int waves, int list_cap) {
+  return waves * (vstage + kQueryLds) + (list_cap + 1) * 16 + kMaxQuerySegs * 4 + 16;
+}
+
+// Writes the workgroup's block list into LDS (one wave calls it).  Entry k:
+// (byte offset of the block's table entry, first token of the block, length
+// of its sequence, segment key); the key packs the sequence (bits 8+), the
+// segment's number in the workgroup (bits 2-7, saturating), whether its
+// record goes to slot 2w + 1 (bit 1) and whether it is the whole sequence
+// (bit 0).  Also zeroes an empty sequence's output and writes the plan
+// entries of the sequences that start here.
+__device__ __forceinline__ void build_block_list(const AttnParams& p, int head_dim, int lane, int4* list, int* segs, int* counts) {
+  const int S = p.num_seqs;
+  const int w = blockIdx.x;
+  // workgroup s of the first head group zeroes sequence s when it is empty
+  // (16-bit outputs: zero bits are zero)
+  if (blockIdx.y == 0 && w < S && clamp_len(p.seq_lens[w], p.mbs) == 0) {
+    const int n16 = p.num_q_heads * head_dim / 8;
+    uint4* o = reinterpret_cast<uint4*>(p.out) + (size_t)w * n16;
+    for (int i = lane; i < n16; i += 64) o[i] = make_uint4(0, 0, 0, 0);
+    if (p.plan && lane == 0) reinterpret_cast<int4*>(p.plan)[w] = make_int4(0, 0, 0, 0);
+  }
+
+  SeqWindow win = load_window(p, 0, 0, lane);
+  int U = win.total;
+  for (int s0 = 64; s0 < S; s0 += 64) U += load_window(p, s0, U, lane).total;
+  int nb = 0, nseg = 0;
+  if (U > 0) {
+    const int K = gridDim.x;
+    const int Q = max(p.min_units, (U + K - 1) / K);
+    const int k_eff = (U + Q - 1) / Q;
+    if (w < k_eff) {
+      const int u0 = (int)((long long)w * U / k_eff);
+      const int u1 = (int)((long long)(w + 1) * U / k_eff);
+      if (S > 64) {
+        win = load_window(p, 0, 0, lane);
+        while (win.base + win.total <= u0 && win.s0 + 64 < S)
+          win = load_window(p, win.s0 + 64, win.base + win.total, lane);
+      }
+      // the sequence holding unit u0: the first with units past it
+      const unsigned long long hit = __ballot(win.n > 0 && win.P + win.n > u0);
+      int s = hit ? win.s0 + (int)__ffsll((long long)hit) - 1 : S;
+      while (s < S) {
+        if (s >= win.s0 + 64) win = load_window(p, win.s0 + 64, win.base + win.total, lane);
+        const int l = s - win.s0;
+        const int n = __builtin_amdgcn_readlane(win.n, l);
+        const int P = __builtin_amdgcn_readlane(win.P, l);
+        const int L = __builtin_amdgcn_readlane(win.L, l);
+        if (P >= u1) break;
+        if (n > 0) {
+          const int i0 = max(u0 - P, 0), i1 = min(u1 - P, n);
+          const SegBlocks sb = segment_blocks(p, L, i0, i1);
+          const int whole = (i0 == 0 && i1 == n) ? 1 : 0;
+          const int upper = (P + i0 == u0) ? 0 : 1;   // not the workgroup's first segment
+          const int key = (s << 8) | (min(nseg, 63) << 2) | (upper << 1) | whole;
+          // the grid is sized so that every range fits; the bound only
+          // keeps a wrong size from writing past the list
+          const int cnt = min(sb.n_need, p.list_cap - nb);
+          for (int j = lane; j < cnt; j += 64) {
+            const int lb = j < sb.n_a ? sb.lb_begin + j : sb.b0 + (j - sb.n_a);
+            list[nb + j] = make_int4((s * p.mbs + lb) * 4, lb * kBS, L, key);
+          }
+          if (lane == 0 && nseg < kMaxQuerySegs) segs[nseg] = s;
+          if (i0 == 0 && p.plan && blockIdx.y == 0 && lane == 0) {
+            const int w_last = (int)(((long long)(P + n) * k_eff - 1) / U);
+            reinterpret_cast<int4*>(p.plan)[s] = make_int4(2 * w + upper, w, w_last, 0);
+          }
+          nb += cnt;
+          ++nseg;
+        }
+        ++s;
+      }
+    }
+  }
+  if (lane == 0) {
+    list[nb] = make_int4(kOutOfRange, 0, 0, kEndKey);
+    counts[0] = nb;
+    counts[1] = nseg;
+  }
+}
 
 template <typename QT, typename KVT, int D, bool STREAM>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
-void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
+void paged_attn_wave_kernel(AttnParams p) {
   typedef WaveCfg<KVT, D> C;
   typedef typename MmaType<QT, KVT>::type MT;
   typedef Mfma<MT> M;     // operands of both products
@@ -360,69 +414,115 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
   // Scores may exceed the running max by this much (log2 units) before the
   // accumulators are rescaled: probabilities stay below 2^8.
   constexpr float kSlack = 8.0f;
+  constexpr int kQRegs = kQueryLds / 1024;   // 16-byte query loads per lane
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kMaxWavesPerGroup * C::VSTAGE];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int heads_per_group = blockDim.x >> 6;
-  const int kvh = blockIdx.y * heads_per_group + wave;
+  const int waves = blockDim.x >> 6;
+  const int kvh = blockIdx.y * waves + wave;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int g = lane & 15;       // query head in the group (column of S^T / out^T)
   const int kg = lane >> 4;      // lane group: k-chunk of the operands, 4-row slab of outputs
   uint8_t* vstage = lds + wave * C::VSTAGE;
+  uint8_t* qlds = lds + waves * C::VSTAGE + wave * kQueryLds;
+  int4* list = reinterpret_cast<int4*>(lds + waves * (C::VSTAGE + kQueryLds));
+  int* segs = reinterpret_cast<int*>(list + p.list_cap + 1);
+  int* counts = segs + kMaxQuerySegs;
+
+  if (wave == 0) build_block_list(p, D, lane, list, segs, counts);
+  __syncthreads();
   if (kvh >= p.num_kv_heads) return;
+  const int nb = __builtin_amdgcn_readfirstlane(counts[0]);
+  const int nseg = __builtin_amdgcn_readfirstlane(counts[1]);
 
-  // an empty sequence gets zeros and a plan entry of no chunks (the head-0
-  // wave of chunk slot s does it)
-  {
-    const int zs = blockIdx.x;
-    if (kvh == 0 && zs < p.num_seqs && clamp_len(p.seq_lens[zs], p.mbs) == 0) {
-      for (int i = lane; i < p.num_q_heads * D; i += 64)
-        store_out<QT>(p.out, (size_t)zs * p.num_q_heads * D + i, 0.f);
-      if (p.plan && lane == 0) {
-        p.plan[2 * zs] = 0;
-        p.plan[2 * zs + 1] = 0;
-      }
-    }
-  }
+  // queries of the first segments, copied to LDS at the start of the ring
+  const int q_chunks = G * D / 8;                      // 16-byte pieces of one group's query
+  const int q_segs = min(min(kQueryLds / (G * D * 2), kMaxQuerySegs), nseg);
 
-  // the plan's results are wave-uniform; say so, so that everything derived
-  // from them stays in scalar registers
-  const int Q = __builtin_amdgcn_readfirstlane(plan_units_per_chunk(pa, lane));
-  const ChunkInfo ci = plan_locate(pa, Q, lane, true, blockIdx.x);
-  const int s = __builtin_amdgcn_readfirstlane(ci.s);
-  if (s < 0) return;
-  const int chunk = __builtin_amdgcn_readfirstlane(ci.c);
-  const int chunks = __builtin_amdgcn_readfirstlane(ci.chunks);
-  const bool single = chunks == 1;
-  const int rec_index = blockIdx.x * p.num_kv_heads + kvh;
-  // where the merge finds this sequence's records
-  if (p.plan && chunk == 0 && kvh == 0 && lane == 0) {
-    p.plan[2 * s] = blockIdx.x;
-    p.plan[2 * s + 1] = chunks;
-  }
-  const size_t head0 = (size_t)s * p.num_q_heads + kvh * G;
-  const int L = clamp_len(p.seq_lens[s], p.mbs);
-  const SeqUnits su = seq_units(L, p.partition_size, p.sink, p.window);
-  // the sequence's n units are cut into `chunks` near-equal pieces
-  const int i0 = (int)((long long)chunk * su.n / chunks), i1 = (int)((long long)(chunk + 1) * su.n / chunks);
-  const int t_begin = unit_partition(su, i0) * p.partition_size;
-  const int t_end = min((unit_partition(su, i1 - 1) + 1) * p.partition_size, L);
-  const int lb_begin = t_begin / kBS;
-  const int lb_end = (t_end + kBS - 1) / kBS;
+  // block-list entry k (the end entry for k >= nb), wave-uniform
+  auto entry_at = [&](int k) {
+    const int4 r = list[min(k, nb)];
+    return make_int4(__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                     __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w));
+  };
+  const __amdgpu_buffer_rsrc_t tab = make_rsrc(p.block_tables, p.table_bytes);
+  auto load_table = [&](int off) { return (int)__builtin_amdgcn_raw_buffer_load_b32(tab, off, 0, 0); };
+  const bool windowed = p.sink != 0 || p.window != 0;
+  // every token of the block starting at t0 is kept
+  auto block_full = [&](int t0, int L) {
+    return (t0 + kBS <= L) & (!windowed | (t0 + kBS <= p.sink) | (t0 >= L - p.window));
+  };
 
-  // ---- query group as the B operand of S^T = K Q^T (zero rows for g >= G) --
-  typename M::vec8 qop[NC];
-  // log2-domain score factor of this lane's head (times the block's K scale)
-  float qfactor = p.scale_log2;
-  {
-    uint4 v[NC];
+  struct Tile {
+    uint4 k[KCH];
+    uint4 v[VCH];
+    float ks, vs;
+  };
+  const int row_stride = p.num_kv_heads * C::ROW_BYTES;        // bytes between token rows
+  const int krow = lane & 15;
+  const int kcol = kCodes ? (D / 4) * kg : 16 * kg;            // bytes
+  const int k_off = krow * row_stride + kcol;
+  int v_off[VCH], v_row[VCH];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      v[c] = make_uint4(0, 0, 0, 0);
-      if (g < G)
-        v[c] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + (head0 + g) * D +
-                                               qk_doff<KVT, D>(c, kg));
+  for (int ps = 0; ps < VCH; ++ps) {
+    v_row[ps] = ps * C::ROWS_PER_PASS + lane / C::LANES_PER_ROW;
+    v_off[ps] = v_row[ps] * row_stride + (lane % C::LANES_PER_ROW) * 16;
+  }
+  const int tile_bytes = (kBS - 1) * row_stride + C::ROW_BYTES;
+
+  // e: list entry of the block, pb_raw: its table entry
+  auto load_tile = [&](Tile& t, int pb_raw, const int4& e) {
+    const bool valid = e.w != kEndKey;
+    int pb = __builtin_amdgcn_readfirstlane(pb_raw);
+    pb = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the cache arrays
+    const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * C::ROW_BYTES;
+    const int nbytes = valid ? tile_bytes : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(p.k_cache) + tile, nbytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v_cache) + tile, nbytes);
+    const int t0 = e.y, L = e.z;
+    const bool full = block_full(t0, L);
+    const int ko = (full | kept(t0 + krow, L, p.sink, p.window)) ? k_off : kOutOfRange;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) t.k[c] = buf_load16<STREAM ? kPolicyStream : 0>(kr, ko + (kCodes ? 16 : 64) * c);
+#pragma unroll
+    for (int ps = 0; ps < VCH; ++ps) {
+      const int vo = (full | kept(t0 + v_row[ps], L, p.sink, p.window)) ? v_off[ps] : kOutOfRange;
+      t.v[ps] = buf_load16<STREAM ? kPolicyStream : 0>(vr, vo);
+    }
+    if constexpr (kCodes) {
+      // the scale row of this block: a 4-byte window at its own address
+      const size_t si = (size_t)pb * p.num_kv_heads + kvh;
+      t.ks = buf_load4(make_rsrc(p.k_scales + si, valid ? 4 : 0), 0);
+      t.vs = buf_load4(make_rsrc(p.v_scales + si, valid ? 4 : 0), 0);
+    } else {
+      t.ks = t.vs = 1.f;
+    }
+  };
+
+  // ---- per-segment state ---------------------------------------------------
+  int cur_key = kEndKey;         // segment being accumulated
+  typename M::vec8 qop[NC];      // query group as the B operand of S^T = K Q^T (zero rows for g >= G)
+  float qfactor = p.scale_log2;  // log2-domain score factor of this lane's head (times the block's K scale)
+  float m2 = -INFINITY;          // running max (log2 domain) of head g, same in all lane groups
+  float lsum = 0.f;              // this lane's share of the softmax denominator
+  floatx4 acc[NN];
+
+  auto start_segment = [&](int key) {
+    const int ord = (key >> 2) & 63;
+    uint4 v[NC];
+    if (ord < q_segs) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        v[c] = g < G ? *reinterpret_cast<const uint4*>(qlds + (size_t)ord * G * D * 2 + (g * D + qk_doff<KVT, D>(c, kg)) * 2)
+                     : make_uint4(0, 0, 0, 0);
+    } else {
+      const size_t head0 = (size_t)(key >> 8) * p.num_q_heads + kvh * G;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        v[c] = g < G ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + (head0 + g) * D +
+                                                       qk_doff<KVT, D>(c, kg))
+                     : make_uint4(0, 0, 0, 0);
     }
     if constexpr (!kRescaleQ) {
 #pragma unroll
@@ -454,88 +554,76 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
         qop[c] = __builtin_bit_cast(typename M::vec8, w);
       }
     }
-  }
-
-  // ---- blocks this wave reads: [lb_begin, a1) then [b0, lb_end) ----------
-  const bool windowed = p.sink != 0 || p.window != 0;
-  int a1 = lb_end, b0 = lb_end;
-  if (windowed) {
-    const int sink_end = min(lb_end, (p.sink + kBS - 1) / kBS);   // blocks holding a sink token
-    a1 = max(lb_begin, sink_end);
-    b0 = p.window > 0 ? min(lb_end, max(max(lb_begin, max(0, L - p.window) / kBS), a1)) : lb_end;
-  }
-  const int n_a = a1 - lb_begin;
-  const int n_need = n_a + (lb_end - b0);
-  auto block_of = [&](int j) { return j < n_a ? lb_begin + j : b0 + (j - n_a); };
-  // every token of block lb is kept
-  auto block_full = [&](int lb) {
-    const int t0 = lb * kBS;
-    return (t0 + kBS <= L) & (!windowed | (t0 + kBS <= p.sink) | (t0 >= L - p.window));
+    m2 = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
   };
 
-  struct Tile {
-    uint4 k[KCH];
-    uint4 v[VCH];
-    float ks, vs;
-  };
-  const int row_stride = p.num_kv_heads * C::ROW_BYTES;        // bytes between token rows
-  const int krow = lane & 15;
-  const int kcol = kCodes ? (D / 4) * kg : 16 * kg;            // bytes
-  const int k_off = krow * row_stride + kcol;
-  int v_off[VCH], v_row[VCH];
+  // Results of the segment with this key.  Lane (g, kg) holds
+  // out[g][16n + 4kg + i], i = 0..3.  The accumulators go through LDS (the
+  // wave's V staging area, idle between blocks), 8 heads at a time, so that
+  // every global store writes whole, contiguous 128-byte lines.
+  auto finish_segment = [&](int key) {
+    const bool whole = (key & 1) != 0;
+    const size_t head0 = (size_t)(key >> 8) * p.num_q_heads + kvh * G;
+    float l = lsum + __shfl_xor(lsum, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    constexpr int RSTRIDE = D + 4;                      // floats per padded LDS row
+    static_assert((8 * RSTRIDE + 32) * 4 <= C::VSTAGE, "result staging must fit the V staging area");
+    float* rl = reinterpret_cast<float*>(vstage);
+    const float scale_out = whole ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
+    // acc[G][D], then m[16], l[16]
+    float* rec = p.ws + ((size_t)(2 * blockIdx.x + ((key >> 1) & 1)) * p.num_kv_heads + kvh) * p.rec_floats;
+    for (int h0 = 0; h0 < G; h0 += 8) {
+      const int nh = min(8, G - h0);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (g >= h0 && g < h0 + 8) {
 #pragma unroll
-  for (int ps = 0; ps < VCH; ++ps) {
-    v_row[ps] = ps * C::ROWS_PER_PASS + lane / C::LANES_PER_ROW;
-    v_off[ps] = v_row[ps] * row_stride + (lane % C::LANES_PER_ROW) * 16;
-  }
-  const int tile_bytes = (kBS - 1) * row_stride + C::ROW_BYTES;
-  // this sequence's block-table row; entries are fetched 2*DEPTH blocks
-  // ahead as uniform loads, so by the time a tile load needs one it is older
-  // than every load still in flight and no wait stalls the ring
-  const __amdgpu_buffer_rsrc_t tab = make_rsrc(p.block_tables + (size_t)s * p.mbs, p.mbs * 4);
-  auto load_entry = [&](int j) {
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(tab, j < n_need ? block_of(j) * 4 : kOutOfRange, 0, 0);
-  };
-
-  auto load_tile = [&](Tile& t, int j, int entry) {
-    const bool valid = j < n_need;
-    const int lb = valid ? block_of(j) : lb_begin;
-    int pb = __builtin_amdgcn_readfirstlane(entry);
-    pb = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the cache arrays
-    const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * C::ROW_BYTES;
-    const int nbytes = valid ? tile_bytes : 0;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(p.k_cache) + tile, nbytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v_cache) + tile, nbytes);
-    const int t0 = lb * kBS;
-    const bool full = block_full(lb);
-    const int ko = (full | kept(t0 + krow, L, p.sink, p.window)) ? k_off : kOutOfRange;
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) t.k[c] = buf_load16<STREAM ? kPolicyStream : 0>(kr, ko + (kCodes ? 16 : 64) * c);
-#pragma unroll
-    for (int ps = 0; ps < VCH; ++ps) {
-      const int vo = (full | kept(t0 + v_row[ps], L, p.sink, p.window)) ? v_off[ps] : kOutOfRange;
-      t.v[ps] = buf_load16<STREAM ? kPolicyStream : 0>(vr, vo);
-    }
-    if constexpr (kCodes) {
-      // the scale row of this block: a 4-byte window at its own address
-      const size_t si = (size_t)pb * p.num_kv_heads + kvh;
-      t.ks = buf_load4(make_rsrc(p.k_scales + si, 4), 0);
-      t.vs = buf_load4(make_rsrc(p.v_scales + si, 4), 0);
-    } else {
-      t.ks = t.vs = 1.f;
+        for (int n = 0; n < NN; ++n)
+          *reinterpret_cast<floatx4*>(rl + (g - h0) * RSTRIDE + 16 * n + 4 * kg) = acc[n] * scale_out;
+      }
+      if (h0 == 0 && kg == 0) {
+        rl[8 * RSTRIDE + g] = m2;
+        rl[8 * RSTRIDE + 16 + g] = l;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (whole) {
+        // nh rows of D outputs, contiguous from head0 + h0: 8 elements per lane-store
+        constexpr int CPR = D / 8;
+        for (int c = lane; c < nh * CPR; c += 64) {
+          const float* src = rl + (c / CPR) * RSTRIDE + (c % CPR) * 8;
+          const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
+          const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (head0 + h0) * D + c * 8) = make_uint4(
+              MO::pack2(lo[0], lo[1]), MO::pack2(lo[2], lo[3]), MO::pack2(hi[0], hi[1]), MO::pack2(hi[2], hi[3]));
+        }
+      } else if (p.ws) {
+        constexpr int CPR = D / 4;
+        for (int c = lane; c < nh * CPR; c += 64)
+          *reinterpret_cast<floatx4*>(rec + (size_t)h0 * D + 4 * c) =
+              *reinterpret_cast<const floatx4*>(rl + (c / CPR) * RSTRIDE + (c % CPR) * 4);
+        if (h0 == 0 && lane < 8)
+          *reinterpret_cast<floatx4*>(rec + (size_t)G * D + 4 * lane) =
+              *reinterpret_cast<const floatx4*>(rl + 8 * RSTRIDE + 4 * lane);
+      }
     }
   };
 
-  float m2 = -INFINITY;          // running max (log2 domain) of head g, same in all lane groups
-  float lsum = 0.f;              // this lane's share of the softmax denominator
-  floatx4 acc[NN];
-#pragma unroll
-  for (int n = 0; n < NN; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  auto process = [&](const Tile& t, int j, uint8_t* vst) {
-    const int lb = block_of(j);
-    const int t0 = lb * kBS;
-    const bool full = block_full(lb);
+  auto process = [&](const Tile& t, const int4& e, uint8_t* vst) {
+    if (e.w != cur_key) {
+      // a new segment: the previous one's results leave first (they are
+      // staged through the V area this block is about to use)
+      if (cur_key != kEndKey) finish_segment(cur_key);
+      start_segment(e.w);
+      cur_key = e.w;
+    }
+    const int t0 = e.y, L = e.z;
+    const bool full = block_full(t0, L);
 
     // ---- V rows -> LDS (masked rows arrive as zeros) -----------------------
 #pragma unroll
@@ -607,82 +695,59 @@ void paged_attn_wave_kernel(AttnParams p, PlanArgs pa) {
     for (int n = 0; n < NN; ++n) acc[n] = M::pv(M::tr_read(rd + n * 32), pop, acc[n]);
   };
 
-  // ---- main loop: a ring of DEPTH tiles; block j + DEPTH is requested as
-  // soon as block j's registers are free, with its table entry fetched
-  // DEPTH steps earlier.  Loads past the end read nothing.
+  // ---- main loop: a ring of DEPTH tiles; block k + DEPTH is requested as
+  // soon as block k's registers are free, with its table entry fetched
+  // DEPTH steps earlier, so that by the time a tile load needs an entry it
+  // is older than every load still in flight and no wait stalls the ring.
+  // Loads past the end of the list read nothing.
   {
     Tile ring[DEPTH];
-    int ent[DEPTH];
+    int tab_ent[DEPTH];
     {
       int first[DEPTH];
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) first[d] = load_entry(d);
+      for (int d = 0; d < DEPTH; ++d) first[d] = load_table(entry_at(d).x);
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) ent[d] = load_entry(DEPTH + d);
+      for (int d = 0; d < DEPTH; ++d) tab_ent[d] = load_table(entry_at(DEPTH + d).x);
+      // The queries' loads overlap the table entries' (no wait comes between
+      // them).  Branch-free, so that the waits stay counted: pieces past the
+      // end load sequence 0's query and land in unused LDS.
+      // c / q_chunks as (c * inv) >> 16: exact for c < 6 * 64 and every
+      // q_chunks = G * D / 8 built (checked exhaustively on the host)
+      const int inv = 0x10000 / q_chunks + 1;
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      u32x4 qv[kQRegs];
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], d, first[d]);
+      for (int r = 0; r < kQRegs; ++r) {
+        const int c = r * 64 + lane;
+        const int i = (c * inv) >> 16;               // < kMaxQuerySegs: q_chunks >= 8
+        const bool used = c < q_segs * q_chunks;
+        const int si = segs[i];                      // read unconditionally, used only when set
+        const int s = used ? si : 0;
+        const int piece = used ? c - i * q_chunks : 0;
+        qv[r] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.query) +
+                                                ((size_t)s * p.num_q_heads + kvh * G) * D + piece * 8);
+      }
+#pragma unroll
+      for (int r = 0; r < kQRegs; ++r) *reinterpret_cast<u32x4*>(qlds + (r * 64 + lane) * 16) = qv[r];
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], first[d], entry_at(d));
     }
     __builtin_amdgcn_sched_barrier(0);
-    for (int j0 = 0; j0 < n_need; j0 += DEPTH) {
+    for (int k0 = 0; k0 < nb; k0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        if (j0 + d < n_need) process(ring[d], j0 + d, vstage);
+        const int k = k0 + d;
+        const int4 e0 = entry_at(k), e1 = entry_at(k + DEPTH), e2 = entry_at(k + 2 * DEPTH);
+        if (k < nb) process(ring[d], e0, vstage);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(ring[d], j0 + d + DEPTH, ent[d]);
-        ent[d] = load_entry(j0 + d + 2 * DEPTH);
+        load_tile(ring[d], tab_ent[d], e1);
+        tab_ent[d] = load_table(e2.x);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
-
-  // ---- results -------------------------------------------------------------
-  // lane (g, kg) holds out[g][16n + 4kg + i], i = 0..3.  The accumulators go
-  // through LDS (the wave's V staging area, idle now), 8 heads at a time, so
-  // that every global store writes whole, contiguous 128-byte lines.
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  constexpr int RSTRIDE = D + 4;                      // floats per padded LDS row
-  static_assert((8 * RSTRIDE + 32) * 4 <= C::VSTAGE, "result staging must fit the V staging area");
-  float* rl = reinterpret_cast<float*>(vstage);
-  const float scale_out = single ? (lsum > 0.f ? 1.f / lsum : 0.f) : 1.f;
-  float* rec = p.ws + (size_t)rec_index * p.rec_floats;   // acc[G][D], then m[16], l[16]
-  for (int h0 = 0; h0 < G; h0 += 8) {
-    const int nh = min(8, G - h0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (g >= h0 && g < h0 + 8) {
-#pragma unroll
-      for (int n = 0; n < NN; ++n)
-        *reinterpret_cast<floatx4*>(rl + (g - h0) * RSTRIDE + 16 * n + 4 * kg) = acc[n] * scale_out;
-    }
-    if (h0 == 0 && kg == 0) {
-      rl[8 * RSTRIDE + g] = m2;
-      rl[8 * RSTRIDE + 16 + g] = lsum;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (single) {
-      // nh rows of D outputs, contiguous from head0 + h0: 8 elements per lane-store
-      constexpr int CPR = D / 8;
-      for (int c = lane; c < nh * CPR; c += 64) {
-        const float* src = rl + (c / CPR) * RSTRIDE + (c % CPR) * 8;
-        const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
-        const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (head0 + h0) * D + c * 8) = make_uint4(
-            MO::pack2(lo[0], lo[1]), MO::pack2(lo[2], lo[3]), MO::pack2(hi[0], hi[1]), MO::pack2(hi[2], hi[3]));
-      }
-    } else {
-      constexpr int CPR = D / 4;
-      for (int c = lane; c < nh * CPR; c += 64)
-        *reinterpret_cast<floatx4*>(rec + (size_t)h0 * D + 4 * c) =
-            *reinterpret_cast<const floatx4*>(rl + (c / CPR) * RSTRIDE + (c % CPR) * 4);
-      if (h0 == 0 && lane < 8)
-        *reinterpret_cast<floatx4*>(rec + (size_t)G * D + 4 * lane) =
-            *reinterpret_cast<const floatx4*>(rl + 8 * RSTRIDE + 4 * lane);
-    }
-  }
+  if (cur_key != kEndKey) finish_segment(cur_key);
 }
 
 // ===========================================================================
@@ -807,17 +872,16 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 }
 
 // ===========================================================================
-// Merge of the wave kernel's records: for each (query head, sequence) that
-// was cut into several chunks, out = sum_c 2^(m_c - M) acc_c /
-// sum_c 2^(m_c - M) l_c over its records (one per chunk, in chunk order).
-// Sequences of one chunk were finished by their waves; empty sequences were
-// zeroed.  The decode left every sequence's first chunk and chunk count in
-// the plan area; 8 record rows at a time are read by D/4 threads with
-// 16-byte loads, 4 rows per thread in flight.
+// Merge of the wave kernel's records: for each (query head, sequence) cut
+// over several workgroups, out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M)
+// l_i over its records, one per workgroup it reaches.  Whole sequences were
+// finished by their waves and empty ones zeroed: their plan entries name one
+// workgroup.  8 record rows at a time are read by D/4 threads with 16-byte
+// loads, 4 rows per thread in flight.
 // ===========================================================================
 template <typename QT, int D>
 __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const float* ws, const int* plan,
-                                                               int rec_floats, int num_q_heads, PlanArgs pa) {
+                                                               int rec_floats, int num_q_heads, int num_kv_heads) {
   constexpr int TPR = D / 4;               // threads per record row
   constexpr int ROWS = 256 / TPR;
   constexpr int U = 4;
@@ -826,20 +890,19 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
   __shared__ float part_den[ROWS];
   const int h = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x;
-  const int G = num_q_heads / pa.num_kv_heads;
+  const int G = num_q_heads / num_kv_heads;
   const int kvh = h / G, g = h % G;
-  // the decode wrote every sequence's entry: no chunks (empty sequence,
-  // zeroed) or one chunk (finished by its waves) leave nothing to merge
-  const int np = plan[2 * s + 1];
-  if (np <= 1) return;
-  // record of chunk c of this head: (first + c) * Hkv + kvh
-  const float* rec0 = ws + ((size_t)plan[2 * s] * pa.num_kv_heads + kvh) * rec_floats;
-  rec_floats *= pa.num_kv_heads;   // stride between the head's consecutive chunks
-  const float* m_of = rec0 + (size_t)G * D + g;
-  const float* l_of = m_of + 16;
-  const float* a_of = rec0 + (size_t)g * D;
+  // (slot of the first record, first workgroup, last workgroup)
+  const int4 e = reinterpret_cast<const int4*>(plan)[s];
+  if (e.z <= e.y) return;
+  const int np = e.z - e.y + 1;
+  // record i: slot e.x for i = 0, then slot 2 (e.y + i) of each later workgroup
+  auto rec_of = [&](int i) {
+    const int slot = i == 0 ? e.x : 2 * (e.y + i);
+    return ws + ((size_t)slot * num_kv_heads + kvh) * rec_floats;
+  };
   float mx = -INFINITY;
-  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, m_of[(size_t)i * rec_floats]);
+  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, rec_of(i)[G * D + g]);
   red[tid] = mx;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -857,23 +920,23 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
       floatx4 a[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const size_t r = (size_t)(i + u * ROWS) * rec_floats;
-        mi[u] = m_of[r];
-        li[u] = l_of[r];
-        a[u] = *reinterpret_cast<const floatx4*>(a_of + r + 4 * c);
+        const float* r = rec_of(i + u * ROWS);
+        mi[u] = r[G * D + g];
+        li[u] = r[G * D + 16 + g];
+        a[u] = *reinterpret_cast<const floatx4*>(r + g * D + 4 * c);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float e = exp2f(mi[u] - M);   // 0 for a chunk that kept no token
-        num += e * a[u];
-        den += e * li[u];
+        const float w = exp2f(mi[u] - M);
+        num += w * a[u];
+        den += w * li[u];
       }
     }
     for (; i < np; i += ROWS) {
-      const size_t r = (size_t)i * rec_floats;
-      const float e = exp2f(m_of[r] - M);
-      num += e * *reinterpret_cast<const floatx4*>(a_of + r + 4 * c);
-      den += e * l_of[r];
+      const float* r = rec_of(i);
+      const float w = exp2f(r[G * D + g] - M);
+      num += w * *reinterpret_cast<const floatx4*>(r + g * D + 4 * c);
+      den += w * r[G * D + 16 + g];
     }
   }
   part_num[row][c] = num;
@@ -1002,38 +1065,39 @@ static AttnParams make_params(const AttnArgs& a) {
   p.num_partitions = a.num_partitions;
   p.sink = a.sink_tokens;
   p.window = a.window_tokens;
+  p.min_units = a.min_units;
+  p.list_cap = a.list_cap;
+  p.table_bytes = (int)((long long)a.num_seqs * a.max_blocks_per_seq * 4);
   p.scale_log2 = a.sm_scale * kLog2e;
   return p;
 }
 
-static PlanArgs make_plan(const AttnArgs& a) {
-  PlanArgs pa;
-  pa.seq_lens = a.seq_lens;
-  pa.num_seqs = a.num_seqs;
-  pa.mbs = a.max_blocks_per_seq;
-  pa.num_kv_heads = a.num_kv_heads;
-  pa.psize = a.partition_size;
-  pa.sink = a.sink_tokens;
-  pa.window = a.window_tokens;
-  pa.num_waves = a.num_waves;
-  pa.min_units = a.min_units;
-  return pa;
-}
-
 template <typename QT, typename KVT, int D, bool STREAM>
-static int launch_wave(const AttnParams& p, const PlanArgs& pa, hipStream_t st) {
-  // (chunk slot, group of up to 8 KV heads); one wave per KV head
-  const int per_group = pa.num_kv_heads < kMaxWavesPerGroup ? pa.num_kv_heads : kMaxWavesPerGroup;
-  const int groups = (pa.num_kv_heads + per_group - 1) / per_group;
-  const dim3 grid(pa.num_waves / pa.num_kv_heads, groups);
-  paged_attn_wave_kernel<QT, KVT, D, STREAM><<<grid, 64 * per_group, 0, st>>>(p, pa);
+static int launch_wave(const AttnParams& p, int num_slots, hipStream_t st) {
+  // (workgroup slot, group of up to 8 KV heads); one wave per KV head
+  const int per_group = wave_group_size(p.num_kv_heads);
+  const int groups = (p.num_kv_heads + per_group - 1) / per_group;
+  const int lds = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, per_group, p.list_cap);
+  auto kernel = paged_attn_wave_kernel<QT, KVT, D, STREAM>;
+  static bool lds_set = false;
+  if (!lds_set) {
+    // above the default dynamic-LDS limit: the largest group needs ~100 KB
+    const int most = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, kMaxWavesPerGroup, 128 * kMaxWavesPerGroup);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, most);
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  kernel<<<dim3(num_slots, groups), 64 * per_group, lds, st>>>(p);
   return hipGetLastError();
 }
 
 template <typename QT, typename KVT>
-static int launch_wave_d(const AttnParams& p, const PlanArgs& pa, int D, bool stream, hipStream_t st) {
-  if (stream) return D == 64 ? launch_wave<QT, KVT, 64, true>(p, pa, st) : launch_wave<QT, KVT, 128, true>(p, pa, st);
-  return D == 64 ? launch_wave<QT, KVT, 64, false>(p, pa, st) : launch_wave<QT, KVT, 128, false>(p, pa, st);
+static int launch_wave_d(const AttnParams& p, int num_slots, int D, bool stream, hipStream_t st) {
+  if (stream)
+    return D == 64 ? launch_wave<QT, KVT, 64, true>(p, num_slots, st) : launch_wave<QT, KVT, 128, true>(p, num_slots, st);
+  return D == 64 ? launch_wave<QT, KVT, 64, false>(p, num_slots, st)
+                 : launch_wave<QT, KVT, 128, false>(p, num_slots, st);
 }
 
 template <typename QT, typename KVT, int D>
@@ -1051,19 +1115,19 @@ int launch_paged_attn_partition(const AttnArgs& a) {
     const dim3 grid(a.num_kv_heads, a.num_partitions, a.num_seqs);
     return D == 64 ? launch_simple<F32, F32, 64>(p, grid, st) : launch_simple<F32, F32, 128>(p, grid, st);
   }
-  const PlanArgs pa = make_plan(a);
+  const int K = a.num_slots;
   const bool stream = (a.flags & PKV_DECODE_STREAM_KV) != 0;
   if (a.q_dtype == PKV_BF16) {
     switch (a.kv_dtype) {
-      case PKV_BF16: return launch_wave_d<BF16, BF16>(p, pa, D, stream, st);
-      case PKV_I8: return launch_wave_d<BF16, I8>(p, pa, D, stream, st);
-      default: return launch_wave_d<BF16, FP8>(p, pa, D, stream, st);
+      case PKV_BF16: return launch_wave_d<BF16, BF16>(p, K, D, stream, st);
+      case PKV_I8: return launch_wave_d<BF16, I8>(p, K, D, stream, st);
+      default: return launch_wave_d<BF16, FP8>(p, K, D, stream, st);
     }
   }
   switch (a.kv_dtype) {
-    case PKV_F16: return launch_wave_d<F16, F16>(p, pa, D, stream, st);
-    case PKV_I8: return launch_wave_d<F16, I8>(p, pa, D, stream, st);
-    default: return launch_wave_d<F16, FP8>(p, pa, D, stream, st);
+    case PKV_F16: return launch_wave_d<F16, F16>(p, K, D, stream, st);
+    case PKV_I8: return launch_wave_d<F16, I8>(p, K, D, stream, st);
+    default: return launch_wave_d<F16, FP8>(p, K, D, stream, st);
   }
 }
 
@@ -1086,9 +1150,8 @@ int launch_paged_attn_merge(const AttnArgs& a) {
     return hipGetLastError();
   }
   if (!a.may_split) return hipSuccess;
-  const PlanArgs pa = make_plan(a);
 #define PKV_MERGE(QT, D) \
-  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.ws, a.plan, rec, a.num_q_heads, pa)
+  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.ws, a.plan, rec, a.num_q_heads, a.num_kv_heads)
   if (a.head_dim == 64) {
     if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 64);
     else PKV_MERGE(F16, 64);

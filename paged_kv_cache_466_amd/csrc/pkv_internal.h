@@ -45,44 +45,52 @@ struct AttnArgs {
   float sm_scale;
   int partition_size;  // resolved (never 0)
   int num_partitions;  // per sequence, from max_blocks_per_seq * block_size
-  // 16-bit / code caches: waves launched, fewest partitions per wave, and
-  // whether any sequence can be split over several waves (merge needed)
-  int num_waves, min_units;
+  // 16-bit / code caches: workgroups along the sequence axis, blocks a
+  // workgroup's list holds, fewest partitions per workgroup, and whether a
+  // sequence can be cut over several workgroups (merge needed)
+  int num_slots, list_cap, min_units;
   bool may_split;
   unsigned flags;  // PKV_DECODE_* bits
   int sink_tokens, window_tokens;
   // Partial results.  A record holds acc[G][D] (unnormalised fp32
   // accumulators of the group's query heads), then m[16] and l[16] (running
   // max in the log2 domain and softmax denominator; entries >= G unused).
-  // 16-bit / code caches: one record per wave (chunk of a run); fp32 caches:
-  // one per (sequence, KV head, partition), partition fastest.
+  // 16-bit / code caches: two record slots per (workgroup, KV head); fp32
+  // caches: one record per (sequence, KV head, partition), partition fastest.
   float* ws;
-  int* plan;   // wave path: [num_seqs][2] (first chunk, chunk count), before the records
+  int* plan;   // wave path: [num_seqs][4] ints for the merge, before the records
   void* stream;
 };
 
 // Floats in one partial record for group size G and head_dim D.
 inline size_t partial_record_floats(int G, int D) { return (size_t)G * D + 32; }
 
-// Waves the decode launches for the 16-bit / code caches: enough to fill
-// every compute unit at two waves per SIMD, at least one per (sequence, KV
-// head), and a multiple of num_kv_heads (a chunk slot runs one wave per head).
-int decode_waves(int num_seqs, int num_kv_heads);
+// KV heads (one wave each) per workgroup of the 16-bit / code-cache decode.
+inline int wave_group_size(int num_kv_heads) { return num_kv_heads < 8 ? num_kv_heads : 8; }
+// Blocks a workgroup of that decode takes at most (its block list in LDS).
+inline int decode_list_cap(int num_kv_heads) { return 128 * wave_group_size(num_kv_heads); }
+// Workgroups along the sequence axis of that decode: enough to fill every
+// compute unit at two waves per SIMD, at least one per sequence, and enough
+// that no workgroup's share of the partitions exceeds its block list.
+int decode_slots(int num_seqs, int num_kv_heads, int num_partitions, int partition_size);
 // Bytes at the start of the wave path's workspace that hold, per sequence,
-// the number of its first chunk and its chunk count (int32 pairs), written by
-// the decode for the merge; the records follow.
-inline size_t plan_area_bytes(int num_seqs) { return ((size_t)num_seqs * 8 + 255) & ~(size_t)255; }
-// Fewest partitions a wave takes: enough for 128 tokens (8 blocks), so that
-// a wave's fixed costs stay small next to its stream, while small batches
+// the slot of its first partial record and the first and last workgroups it
+// reaches (four int32), written by the decode for the merge; the records
+// follow.
+inline size_t plan_area_bytes(int num_seqs) { return ((size_t)num_seqs * 16 + 255) & ~(size_t)255; }
+// Fewest partitions a workgroup takes: enough for 128 tokens (8 blocks), so
+// that its fixed costs stay small next to its stream, while small batches
 // still spread over many compute units.
 inline int min_units_per_wave(int partition_size) {
   const int m = 128 / partition_size;
   return m < 1 ? 1 : m;
 }
-// Bytes of workspace the split decode needs (the larger of the fp32 path's
-// per-partition records and the wave path's per-wave records), 0 if none.
-size_t workspace_total(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int num_partitions,
-                       int partition_size);
+// Bytes of workspace the split decode needs for a cache of kv_dtype: fp32
+// records per (sequence, KV head, partition) for fp32 caches; the plan area
+// and two records per (workgroup, KV head) otherwise; 0 if no sequence can
+// be split.
+size_t workspace_total(int kv_dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int num_partitions, int partition_size);
 
 // Kernel launchers (defined in the .hip files).  They assume validated
 // arguments and return a hipError_t cast to int.

@@ -107,7 +107,7 @@ def test_full_size_sampled(case):
     t = draw_tensors(w, "cuda")
     g = GpuRun(w, t)
     S, Hq, D = t["query"].shape
-    psize = w.partition_size or pkv.paged_attn_partition_size(S, w.Hkv, g.mbs * 16)
+    psize = w.partition_size or pkv.paged_attn_partition_size(w.kv_dtype, g.mbs * 16)
     stream_kv = not (w.prefix_tokens or w.fork)
     out = g.decode(t["query"], partition_size=psize, stream_kv=stream_kv).float().cpu().numpy()
     torch.cuda.synchronize()

@@ -187,7 +187,7 @@ def test_partition_and_merge_entry_points_compose(sink, window):
     w, t, g, o = run_case("ctx_small")
     q = t["query"]
     ref = g.decode(q, partition_size=64, sink=sink, window=window)
-    nbytes = pkv.paged_attn_workspace_bytes(w.S, w.Hq, w.Hkv, w.D, g.mbs * 16, 64)
+    nbytes = pkv.paged_attn_workspace_bytes(w.kv_dtype, w.S, w.Hq, w.Hkv, w.D, g.mbs * 16, 64)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
     pkv.paged_attn_partition(out, q, g.k_cache, g.v_cache, g.block_tables, g.lens, w.sm_scale, ws,

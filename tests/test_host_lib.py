@@ -126,14 +126,23 @@ def test_validate_tables():
 
 def test_partition_and_workspace_sizes():
     # short bounds: one pass, no workspace
-    assert pkv.paged_attn_num_partitions(4, 2, 96) == 1
-    assert pkv.paged_attn_workspace_bytes(4, 8, 2, 64, 96) == 0
+    assert pkv.paged_attn_num_partitions("bf16", 96) == 1
+    assert pkv.paged_attn_workspace_bytes("bf16", 4, 8, 2, 64, 96) == 0
+    # longer bounds: block granularity for 16-bit and code caches, 64 tokens for fp32
+    assert pkv.paged_attn_partition_size("bf16", 4096) == 16
+    assert pkv.paged_attn_partition_size("i8", 4096) == 16
+    assert pkv.paged_attn_partition_size("f32", 4096) == 64
     # 128K tokens in 512-token partitions
-    assert pkv.paged_attn_num_partitions(4, 8, 131072 + 16, 512) == 257
-    nbytes = pkv.paged_attn_workspace_bytes(4, 64, 8, 128, 131072, 512)
-    n = 4 * 64 * 256
-    assert nbytes >= n * 4 * 2 + n * 128 * 4
-    assert pkv.paged_attn_num_partitions(4, 8, 1000, 100) == 0     # not a multiple of 16
+    assert pkv.paged_attn_num_partitions("bf16", 131072 + 16, 512) == 257
+    # fp32: a record per (sequence, KV head, partition)
+    nbytes = pkv.paged_attn_workspace_bytes("f32", 4, 64, 8, 128, 131072, 512)
+    n = 4 * 8 * 256
+    assert nbytes >= n * (8 * 128 + 32) * 4
+    # 16-bit: the plan area and two records per (workgroup, KV head); with 8
+    # KV heads a workgroup per compute unit (256 on a host without a GPU)
+    nbytes = pkv.paged_attn_workspace_bytes("bf16", 4, 64, 8, 128, 131072, 512)
+    assert nbytes == 256 + 2 * 256 * 8 * (8 * 128 + 32) * 4
+    assert pkv.paged_attn_num_partitions("bf16", 1000, 100) == 0     # not a multiple of 16
 
 
 def test_argument_errors_return_before_launch():
