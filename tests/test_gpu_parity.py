@@ -36,6 +36,14 @@ CASES = {
     "mha_d64": ("llama3_8b_b64", dict(S=4, Hq=4, Hkv=4, D=64, len_lo=1, len_hi=300)),
     "g16": ("llama3_8b_b64", dict(S=3, Hq=32, Hkv=2, len_lo=100, len_hi=700)),
     "fp32_d128_g8": ("tiny_fp32", dict(S=3, Hq=16, Hkv=2, D=128, fixed_lens=(300, 33, 129), pool_blocks=64)),
+    # split edge cases: more than 64 sequences (several scan windows), many
+    # sequences per workgroup (past the queries kept in LDS), empty
+    # sequences between others, one sequence cut over many workgroups, and
+    # more KV heads than one workgroup holds
+    "many_short": ("llama3_8b_b64", dict(S=150, len_lo=1, len_hi=40)),
+    "gaps_no_append": ("llama3_8b_b64", dict(S=8, fixed_lens=(0, 37, 0, 0, 300, 1, 0, 64), append=False)),
+    "one_long": ("llama3_8b_b64", dict(S=1, fixed_len=20000)),
+    "hkv16": ("llama3_8b_b64", dict(S=3, Hq=32, Hkv=16, len_lo=200, len_hi=900)),
 }
 
 _runs = {}
