@@ -15,7 +15,8 @@ Sources (cited by page title and section):
   and Pruning" (StreamingLLM cache layout).
 * "KV Cache Engineering for LLM Serving, clearly explained": "The cache
   formula", section 1 "GQA and MQA cache fewer heads", section 3 "Sliding
-  windows", section 8 "Quantization", section 10 "Paging".
+  windows", section 7 "Query-aware sparse reads", section 8 "Quantization",
+  section 10 "Paging".
 * Learning-AI topic t13_4 (KV cache management): the cache-size formula
   paragraph, the block-table paragraph and its example, and the
   copy-on-write paragraph.
@@ -33,6 +34,9 @@ Modules:
 * ``pool``      - FIFO free-block pool with reference counts and
                   copy-on-write append.
 * ``sizes``     - the KV cache-size formula.
+* ``quest``     - query-aware page selection: per-page key minimum /
+                  maximum, the page score, top-budget selection, and decode
+                  over the selected pages.
 
 Every function here is pinned by tests in ``tests/test_oracle_*.py`` against
 values the pages print, closed forms, invariants, library routines
@@ -40,4 +44,4 @@ values the pages print, closed forms, invariants, library routines
 ``float8_e4m3fn`` cast) or brute force.  No function is "parity unpinned".
 """
 
-from . import attention, codecs, paging, pool, quant, sizes  # noqa: F401
+from . import attention, codecs, paging, pool, quant, quest, sizes  # noqa: F401
