@@ -8,7 +8,8 @@
  *        Quantization", "Token Eviction and Pruning".
  *   [P2] "KV Cache Engineering for LLM Serving, clearly explained", sections
  *        "The cache formula", 1 "GQA and MQA cache fewer heads", 3 "Sliding
- *        windows", 8 "Quantization", 10 "Paging".
+ *        windows", 7 "Query-aware sparse reads", 8 "Quantization", 10
+ *        "Paging".
  *   [P3] Learning-AI topic t13_4 (KV cache management): block-table and
  *        copy-on-write paragraphs.
  *
@@ -213,6 +214,71 @@ pkv_status pkv_paged_attn_merge(
     int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len, int partition_size,
     int sink_tokens, int window_tokens,
     const void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Query-aware page selection (Quest)                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * [P2] s.7 "Query-aware sparse reads": each page keeps the minimum and the
+ * maximum of its keys in every key dimension; a query scores a page by the
+ * sum over dimensions of max(q_i * min_i, q_i * max_i), the largest q . k a
+ * key inside the page's box can reach, and only the highest-scoring pages
+ * are read.  Nothing is evicted.  Here a page is one physical block; with
+ * GQA a page's score for a KV head is the largest over the group's query
+ * heads, and pages are chosen per (sequence, KV head).
+ */
+
+/*
+ * Page summaries of the key cache: k_summary[NB][num_kv_heads][2][head_dim]
+ * in kv_dtype (bf16 or f16), minimum first, then maximum, over the rows a
+ * block holds (tokens < seq_lens[s]; a partial last block summarises its
+ * written rows only).  last_only = 0: every block of every sequence (after
+ * a prefill); 1: each sequence's last block only (after a decode step's
+ * slot write).  Blocks no sequence reaches are left alone.  A block shared
+ * by several sequences gets the same summary from each.
+ */
+pkv_status pkv_quest_summarize(const void* k_cache, int kv_dtype, void* k_summary,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int num_seqs, int num_blocks, int block_size,
+                               int num_kv_heads, int head_dim, int last_only, void* stream);
+
+/* Bytes of scratch pkv_quest_select needs (8 per (sequence, KV head, block)). */
+size_t pkv_quest_scratch_bytes(int num_seqs, int num_kv_heads, int max_blocks_per_seq);
+
+/*
+ * Scores every page of every (sequence, KV head) against the query group
+ * (fp64; each product of two 16-bit values is exact) and writes, for each
+ * (s, kvh), the budget_blocks highest-scoring pages in logical order to
+ * selected[S][num_kv_heads][budget_blocks][2] as (physical block, logical
+ * block) int32 pairs.  Equal scores keep the lower logical block.  A
+ * sequence of n <= budget_blocks blocks keeps all n (entries past n are
+ * left alone).  query: [S][Hq][D] bf16 / f16, the cache's 16-bit type.
+ * scratch: pkv_quest_scratch_bytes(...) bytes, 8-byte aligned.
+ */
+pkv_status pkv_quest_select(const void* query, int q_dtype, const void* k_summary,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                            int head_dim, int block_size, int num_blocks, int budget_blocks,
+                            int32_t* selected, void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Decode attention reading only the selected pages: for query head h of
+ * sequence s, softmax attention over the tokens t < seq_lens[s] of the
+ * first min(budget_blocks, ceil(seq_lens[s] / block_size)) entries of
+ * selected[s][h / G] (as pkv_quest_select writes them, or any list of
+ * distinct blocks of the sequence in logical order).  Other arguments as
+ * pkv_paged_attn_decode; 16-bit and code caches.  The workspace is
+ * pkv_paged_attn_workspace_bytes(kv_dtype, num_seqs, num_q_heads,
+ * num_kv_heads, head_dim, budget_blocks * block_size, block_size) bytes.
+ */
+pkv_status pkv_paged_attn_decode_selected(
+    void* out, const void* query, int q_dtype,
+    const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_scales, const float* v_scales,
+    const int32_t* selected, int budget_blocks,
+    const int32_t* seq_lens, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+    float sm_scale, unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Cache writes                                                              */

@@ -15,6 +15,7 @@ __all__ = [
     "PkvError", "lib", "version", "last_error",
     "paged_attn_decode", "paged_attn_partition", "paged_attn_merge",
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
+    "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
     "slot_mapping", "reshape_and_cache", "append_kv", "copy_blocks", "quantize_kv",
     "validate_tables", "BlockPool", "DTYPES",
 ]
@@ -51,6 +52,11 @@ _SIGS = {
     "pkv_paged_attn_decode": (_ATTN, _i),
     "pkv_paged_attn_partition": (_ATTN, _i),
     "pkv_paged_attn_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
+    "pkv_paged_attn_decode_selected": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
+                                        ctypes.c_uint, _p, _sz, _p], _i),
+    "pkv_quest_summarize": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p], _i),
+    "pkv_quest_scratch_bytes": ([_i, _i, _i], _sz),
+    "pkv_quest_select": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p], _i),
     "pkv_slot_mapping": ([_p, _p, _i, _p, _p, _i, _i, _i, _i, _p], _i),
     "pkv_reshape_and_cache": ([_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_append_kv": ([_p, _p, _p, _p, _i, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p], _i),
@@ -201,6 +207,74 @@ def paged_attn_partition(out, query, k_cache, v_cache, block_tables, seq_lens, s
     return _attn_call(lib.pkv_paged_attn_partition, out, query, k_cache, v_cache, block_tables, seq_lens,
                       sm_scale, k_scales, v_scales, partition_size, sink_tokens, window_tokens, workspace,
                       kv_dtype, stream_kv)
+
+
+def paged_attn_decode_selected(out, query, k_cache, v_cache, selected, seq_lens, sm_scale, k_scales=None,
+                               v_scales=None, workspace=None, kv_dtype=None):
+    """Decode reading only the selected pages (``pkv_paged_attn_decode_selected``).
+
+    ``selected`` [S, Hkv, budget, 2] int32 (physical, logical block) as
+    ``quest_select`` returns it."""
+    _contig(out, query, k_cache, v_cache, selected, seq_lens, k_scales, v_scales, workspace)
+    S, Hq, D = query.shape
+    NB, BS, Hkv, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("shape mismatch between query, caches and out")
+    if selected.dtype != torch.int32 or selected.dim() != 4 or tuple(selected.shape[:2]) != (S, Hkv) \
+            or selected.shape[3] != 2:
+        raise ValueError("selected must be int32 [num_seqs, num_kv_heads, budget, 2]")
+    budget = selected.shape[2]
+    kvdt = _dtype(k_cache, kv_dtype)
+    if workspace is None:
+        nbytes = paged_attn_workspace_bytes(kvdt, S, Hq, Hkv, D, budget * BS, BS)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device) if nbytes else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attn_decode_selected(
+        _ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), kvdt, _ptr(k_scales), _ptr(v_scales),
+        _ptr(selected), budget, _ptr(seq_lens), S, Hq, Hkv, D, BS, NB, float(sm_scale), 0, _ptr(workspace),
+        ws_bytes, _stream(query)))
+    return out
+
+
+def quest_summary_like(k_cache):
+    """An empty page-summary tensor for ``k_cache`` [NB, BS, Hkv, D]:
+    [NB, Hkv, 2, D] of the cache's dtype."""
+    NB, BS, Hkv, D = k_cache.shape
+    return torch.empty((NB, Hkv, 2, D), dtype=k_cache.dtype, device=k_cache.device)
+
+
+def quest_summarize(k_cache, k_summary, block_tables, seq_lens, last_only=False):
+    """Page summaries (``pkv_quest_summarize``): per (block, KV head) the
+    minimum and maximum of the written keys."""
+    _contig(k_cache, k_summary, block_tables, seq_lens)
+    NB, BS, Hkv, D = k_cache.shape
+    if tuple(k_summary.shape) != (NB, Hkv, 2, D) or k_summary.dtype != k_cache.dtype:
+        raise ValueError("k_summary must be [num_blocks, num_kv_heads, 2, head_dim] of the cache's dtype")
+    S, mbs = block_tables.shape
+    _check(lib.pkv_quest_summarize(_ptr(k_cache), _dtype(k_cache), _ptr(k_summary), _ptr(block_tables), mbs,
+                                   _ptr(seq_lens), S, NB, BS, Hkv, D, 1 if last_only else 0, _stream(k_cache)))
+    return k_summary
+
+
+def quest_select(query, k_summary, block_tables, seq_lens, budget_blocks, selected=None, scratch=None):
+    """Top-``budget_blocks`` pages per (sequence, KV head) (``pkv_quest_select``).
+    Returns ``selected`` [S, Hkv, budget, 2] int32 (physical, logical block)."""
+    _contig(query, k_summary, block_tables, seq_lens, selected, scratch)
+    S, Hq, D = query.shape
+    NB, Hkv, two, D2 = k_summary.shape
+    if two != 2 or D2 != D:
+        raise ValueError("k_summary must be [num_blocks, num_kv_heads, 2, head_dim]")
+    mbs = block_tables.shape[1]
+    if selected is None:
+        selected = torch.zeros((S, Hkv, budget_blocks, 2), dtype=torch.int32, device=query.device)
+    if scratch is None:
+        nbytes = lib.pkv_quest_scratch_bytes(S, Hkv, mbs)
+        scratch = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=query.device)
+    sb = scratch.numel() * scratch.element_size()
+    _check(lib.pkv_quest_select(_ptr(query), _dtype(query), _ptr(k_summary), _ptr(block_tables), mbs,
+                                _ptr(seq_lens), S, Hq, Hkv, D, 16, NB, budget_blocks, _ptr(selected),
+                                _ptr(scratch), sb, _stream(query)))
+    return selected
 
 
 def paged_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_size=0, sink_tokens=0,

@@ -183,6 +183,13 @@ static pkv_status device_check(const int32_t* block_tables, int mbs, const int32
                              num_tokens);
 }
 
+static pkv_status check_cache_shape(const char* who, int block_size, int num_kv_heads, int head_dim) {
+  if (block_size != 16) return fail(PKV_EUNSUPPORTED, "%s: block_size must be 16", who);
+  if (num_kv_heads <= 0) return fail(PKV_EINVAL, "%s: num_kv_heads must be positive", who);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be 64 or 128", who);
+  return PKV_OK;
+}
+
 // ---------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------
@@ -216,7 +223,7 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
   if (a.num_partitions < 1) a.num_partitions = 1;
   if (a.num_seqs == 0) return PKV_OK;
   if (!a.out || !a.seq_lens) return fail(PKV_EINVAL, "%s: null pointer argument", who);
-  if (need_inputs && (!a.query || !a.k_cache || !a.v_cache || !a.block_tables))
+  if (need_inputs && (!a.query || !a.k_cache || !a.v_cache || (!a.block_tables && !a.selected)))
     return fail(PKV_EINVAL, "%s: null pointer argument", who);
   const bool wave_path = a.q_dtype != PKV_F32;
   if (wave_path) {
@@ -326,6 +333,82 @@ extern "C" pkv_status pkv_paged_attn_partition(PKV_ATTN_ARGS) {
                   workspace_bytes, stream);
 }
 
+extern "C" pkv_status pkv_paged_attn_decode_selected(
+    void* out, const void* query, int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_scales, const float* v_scales, const int32_t* selected, int budget_blocks,
+    const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int num_blocks, float sm_scale, unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "pkv_paged_attn_decode_selected";
+  if (budget_blocks <= 0) return fail(PKV_EINVAL, "%s: budget_blocks must be positive", who);
+  if (q_dtype == PKV_F32) return fail(PKV_EUNSUPPORTED, "%s: fp32 caches are not built for selected reads", who);
+  if (num_seqs > 0 && num_kv_heads > 0 &&
+      (long long)num_seqs * num_kv_heads * budget_blocks * 8 >= (1LL << 31))
+    return fail(PKV_EUNSUPPORTED, "%s: selection of 2^31 bytes or more", who);
+  // the selection's pages are the units: one-block partitions over a bound
+  // of budget_blocks blocks
+  AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, nullptr, budget_blocks,
+                         seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sm_scale,
+                         16, 0, 0, flags, stream);
+  a.selected = selected;
+  a.budget = budget_blocks;
+  if (num_seqs > 0 && !selected) return fail(PKV_EINVAL, "%s: null pointer argument", who);
+  pkv_status st = prepare_attn(a, who, workspace, workspace_bytes, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  st = hip_status(launch_paged_attn_partition(a), who);
+  if (st != PKV_OK) return st;
+  return hip_status(launch_paged_attn_merge(a), who);
+}
+
+extern "C" size_t pkv_quest_scratch_bytes(int num_seqs, int num_kv_heads, int max_blocks_per_seq) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
+  return align256((size_t)num_seqs * num_kv_heads * max_blocks_per_seq * 8);
+}
+
+extern "C" pkv_status pkv_quest_summarize(const void* k_cache, int kv_dtype, void* k_summary,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* seq_lens, int num_seqs, int num_blocks, int block_size,
+                                          int num_kv_heads, int head_dim, int last_only, void* stream) {
+  const char* who = "pkv_quest_summarize";
+  pkv_status st = check_cache_shape(who, block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16) return fail(PKV_EUNSUPPORTED, "%s: cache must be bf16 or f16", who);
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || num_blocks < 0) return fail(PKV_EINVAL, "%s: negative size", who);
+  if (num_seqs == 0 || max_blocks_per_seq == 0) return PKV_OK;
+  if (num_seqs > 2147483647 / 1 || (!last_only && max_blocks_per_seq > 65535))
+    return fail(PKV_EUNSUPPORTED, "%s: max_blocks_per_seq above 65535 needs last_only", who);
+  if (!k_cache || !k_summary || !block_tables || !seq_lens) return fail(PKV_EINVAL, "%s: null pointer", who);
+  return hip_status(launch_quest_summarize(k_cache, kv_dtype, k_summary, block_tables, max_blocks_per_seq, seq_lens,
+                                           num_seqs, num_blocks, num_kv_heads, head_dim, last_only ? 1 : 0, stream),
+                    who);
+}
+
+extern "C" pkv_status pkv_quest_select(const void* query, int q_dtype, const void* k_summary,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks, int budget_blocks,
+                                       int32_t* selected, void* scratch, size_t scratch_bytes, void* stream) {
+  const char* who = "pkv_quest_select";
+  pkv_status st = check_cache_shape(who, block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (q_dtype != PKV_BF16 && q_dtype != PKV_F16) return fail(PKV_EUNSUPPORTED, "%s: query must be bf16 or f16", who);
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads) return fail(PKV_EINVAL, "%s: num_q_heads %% num_kv_heads", who);
+  if (num_q_heads / num_kv_heads > 16) return fail(PKV_EUNSUPPORTED, "%s: query group size above 16", who);
+  if (budget_blocks <= 0) return fail(PKV_EINVAL, "%s: budget_blocks must be positive", who);
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || num_blocks < 0) return fail(PKV_EINVAL, "%s: negative size", who);
+  if (num_seqs == 0) return PKV_OK;
+  if ((long long)num_seqs * num_kv_heads > 2147483647LL || max_blocks_per_seq / 16 >= 65535)
+    return fail(PKV_EUNSUPPORTED, "%s: shape too large", who);
+  const size_t need = pkv_quest_scratch_bytes(num_seqs, num_kv_heads, max_blocks_per_seq);
+  if (!scratch || scratch_bytes < need)
+    return fail(PKV_EWORKSPACE, "%s: scratch of %zu bytes needed, %zu given", who, need, scratch_bytes);
+  if (((uintptr_t)scratch) & 7) return fail(PKV_EINVAL, "%s: scratch must be 8-byte aligned", who);
+  if (!query || !k_summary || !block_tables || !seq_lens || !selected) return fail(PKV_EINVAL, "%s: null pointer", who);
+  return hip_status(launch_quest_select(query, q_dtype, k_summary, block_tables, max_blocks_per_seq, seq_lens,
+                                        num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, budget_blocks,
+                                        selected, scratch, stream),
+                    who);
+}
+
 extern "C" pkv_status pkv_paged_attn_merge(void* out, int q_dtype, const int32_t* seq_lens, int num_seqs,
                                            int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
                                            int partition_size, int sink_tokens, int window_tokens,
@@ -353,13 +436,6 @@ extern "C" pkv_status pkv_slot_mapping(int32_t* slot_mapping, const int32_t* blo
   return hip_status(launch_slot_mapping(slot_mapping, block_tables, max_blocks_per_seq, seq_ids, positions,
                                         num_tokens, num_seqs, block_size, num_blocks, stream),
                     "pkv_slot_mapping");
-}
-
-static pkv_status check_cache_shape(const char* who, int block_size, int num_kv_heads, int head_dim) {
-  if (block_size != 16) return fail(PKV_EUNSUPPORTED, "%s: block_size must be 16", who);
-  if (num_kv_heads <= 0) return fail(PKV_EINVAL, "%s: num_kv_heads must be positive", who);
-  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be 64 or 128", who);
-  return PKV_OK;
 }
 
 extern "C" pkv_status pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,

@@ -61,7 +61,9 @@ struct AttnParams {
   int sink, window;
   int min_units;        // fewest units a workgroup takes
   int list_cap;         // blocks a workgroup's list holds
-  int table_bytes;      // bytes of block_tables
+  int table_bytes;      // bytes of block_tables (of `selected` for a selected decode)
+  const int32_t* selected;   // selected decode: [S][Hkv][budget] (physical, logical block)
+  int budget;                // selected decode: pages per (sequence, KV head)
   float scale_log2;     // sm_scale * log2(e)
 };
 
@@ -272,13 +274,17 @@ struct SeqWindow {
   int P;       // global number of its first unit
 };
 
+// SEL: a selected decode, whose units are the selected pages (at most
+// `budget` blocks of the sequence).
+template <bool SEL>
 __device__ __forceinline__ SeqWindow load_window(const AttnParams& p, int s0, int base, int lane) {
   SeqWindow w;
   w.s0 = s0;
   w.base = base;
   const int s = s0 + lane;
   w.L = s < p.num_seqs ? clamp_len(p.seq_lens[s], p.mbs) : 0;
-  w.n = seq_units(w.L, p.partition_size, p.sink, p.window).n;
+  if constexpr (SEL) w.n = min(p.budget, (w.L + kBS - 1) / kBS);
+  else w.n = seq_units(w.L, p.partition_size, p.sink, p.window).n;
   const int incl = lane_scan_incl(w.n, lane);
   w.P = base + incl - w.n;
   w.total = __builtin_amdgcn_readlane(incl, 63);
@@ -324,13 +330,16 @@ __host__ __device__ constexpr int wave_group_lds(int vstage, int waves, int list
 }
 
 // Writes the workgroup's block list into LDS (one wave calls it).  Entry k:
-// (byte offset of the block's table entry, first token of the block, length
-// of its sequence, segment key); the key packs the sequence (bits 8+), the
+// (byte offset of the block's table entry - of its selection entry for a
+// selected decode -, first token of the block, length of its sequence,
+// segment key); the key packs the sequence (bits 8+), the
 // segment's number in the workgroup (bits 2-7, saturating), whether its
 // record goes to slot 2w + 1 (bit 1) and whether it is the whole sequence
 // (bit 0).  Also zeroes an empty sequence's output and writes the plan
 // entries of the sequences that start here.
-__device__ __forceinline__ void build_block_list(const AttnParams& p, int head_dim, int lane, int4* list, int* segs, int* counts) {
+template <bool SEL>
+__device__ __forceinline__ void build_block_list(const AttnParams& p, int head_dim, int lane, int4* list, int* segs,
+                                                 int* counts) {
   const int S = p.num_seqs;
   const int w = blockIdx.x;
   // workgroup s of the first head group zeroes sequence s when it is empty
@@ -342,9 +351,9 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
     if (p.plan && lane == 0) reinterpret_cast<int4*>(p.plan)[w] = make_int4(0, 0, 0, 0);
   }
 
-  SeqWindow win = load_window(p, 0, 0, lane);
+  SeqWindow win = load_window<SEL>(p, 0, 0, lane);
   int U = win.total;
-  for (int s0 = 64; s0 < S; s0 += 64) U += load_window(p, s0, U, lane).total;
+  for (int s0 = 64; s0 < S; s0 += 64) U += load_window<SEL>(p, s0, U, lane).total;
   int nb = 0, nseg = 0;
   if (U > 0) {
     const int K = gridDim.x;
@@ -354,15 +363,15 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
       const int u0 = (int)((long long)w * U / k_eff);
       const int u1 = (int)((long long)(w + 1) * U / k_eff);
       if (S > 64) {
-        win = load_window(p, 0, 0, lane);
+        win = load_window<SEL>(p, 0, 0, lane);
         while (win.base + win.total <= u0 && win.s0 + 64 < S)
-          win = load_window(p, win.s0 + 64, win.base + win.total, lane);
+          win = load_window<SEL>(p, win.s0 + 64, win.base + win.total, lane);
       }
       // the sequence holding unit u0: the first with units past it
       const unsigned long long hit = __ballot(win.n > 0 && win.P + win.n > u0);
       int s = hit ? win.s0 + (int)__ffsll((long long)hit) - 1 : S;
       while (s < S) {
-        if (s >= win.s0 + 64) win = load_window(p, win.s0 + 64, win.base + win.total, lane);
+        if (s >= win.s0 + 64) win = load_window<SEL>(p, win.s0 + 64, win.base + win.total, lane);
         const int l = s - win.s0;
         const int n = __builtin_amdgcn_readlane(win.n, l);
         const int P = __builtin_amdgcn_readlane(win.P, l);
@@ -370,7 +379,15 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
         if (P >= u1) break;
         if (n > 0) {
           const int i0 = max(u0 - P, 0), i1 = min(u1 - P, n);
-          const SegBlocks sb = segment_blocks(p, L, i0, i1);
+          SegBlocks sb;
+          if constexpr (SEL) {
+            // units are entries i0 .. i1-1 of the sequence's selection
+            sb.lb_begin = i0;
+            sb.n_a = sb.n_need = i1 - i0;
+            sb.b0 = 0;
+          } else {
+            sb = segment_blocks(p, L, i0, i1);
+          }
           const int whole = (i0 == 0 && i1 == n) ? 1 : 0;
           const int upper = (P + i0 == u0) ? 0 : 1;   // not the workgroup's first segment
           const int key = (s << 8) | (min(nseg, 63) << 2) | (upper << 1) | whole;
@@ -379,7 +396,10 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
           const int cnt = min(sb.n_need, p.list_cap - nb);
           for (int j = lane; j < cnt; j += 64) {
             const int lb = j < sb.n_a ? sb.lb_begin + j : sb.b0 + (j - sb.n_a);
-            list[nb + j] = make_int4((s * p.mbs + lb) * 4, lb * kBS, L, key);
+            // SEL: offset of the selection entry (KV head 0); the block's
+            // first token comes with the entry
+            list[nb + j] = SEL ? make_int4((s * p.num_kv_heads * p.budget + lb) * 8, 0, L, key)
+                               : make_int4((s * p.mbs + lb) * 4, lb * kBS, L, key);
           }
           if (lane == 0 && nseg < kMaxQuerySegs) segs[nseg] = s;
           if (i0 == 0 && p.plan && blockIdx.y == 0 && lane == 0) {
@@ -400,7 +420,7 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
   }
 }
 
-template <typename QT, typename KVT, int D, bool STREAM>
+template <typename QT, typename KVT, int D, bool STREAM, bool SEL>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_attn_wave_kernel(AttnParams p) {
   typedef WaveCfg<KVT, D> C;
@@ -430,7 +450,7 @@ void paged_attn_wave_kernel(AttnParams p) {
   int* segs = reinterpret_cast<int*>(list + p.list_cap + 1);
   int* counts = segs + kMaxQuerySegs;
 
-  if (wave == 0) build_block_list(p, D, lane, list, segs, counts);
+  if (wave == 0) build_block_list<SEL>(p, D, lane, list, segs, counts);
   __syncthreads();
   if (kvh >= p.num_kv_heads) return;
   const int nb = __builtin_amdgcn_readfirstlane(counts[0]);
@@ -446,8 +466,20 @@ void paged_attn_wave_kernel(AttnParams p) {
     return make_int4(__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
                      __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w));
   };
-  const __amdgpu_buffer_rsrc_t tab = make_rsrc(p.block_tables, p.table_bytes);
-  auto load_table = [&](int off) { return (int)__builtin_amdgcn_raw_buffer_load_b32(tab, off, 0, 0); };
+  // (physical block, logical block) of a list entry: the table entry, or
+  // this head's selection entry for a selected decode
+  const __amdgpu_buffer_rsrc_t tab = make_rsrc(SEL ? (const void*)p.selected : (const void*)p.block_tables,
+                                               p.table_bytes);
+  const int sel_head = kvh * p.budget * 8;
+  auto load_table = [&](int off) {
+    if constexpr (SEL) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(tab, off + sel_head, 0, 0));
+      return make_int2((int)v[0], (int)v[1]);
+    } else {
+      return make_int2((int)__builtin_amdgcn_raw_buffer_load_b32(tab, off, 0, 0), 0);
+    }
+  };
   const bool windowed = p.sink != 0 || p.window != 0;
   // every token of the block starting at t0 is kept
   auto block_full = [&](int t0, int L) {
@@ -458,6 +490,7 @@ void paged_attn_wave_kernel(AttnParams p) {
     uint4 k[KCH];
     uint4 v[VCH];
     float ks, vs;
+    int t0;   // first token of the block
   };
   const int row_stride = p.num_kv_heads * C::ROW_BYTES;        // bytes between token rows
   const int krow = lane & 15;
@@ -471,16 +504,18 @@ void paged_attn_wave_kernel(AttnParams p) {
   }
   const int tile_bytes = (kBS - 1) * row_stride + C::ROW_BYTES;
 
-  // e: list entry of the block, pb_raw: its table entry
-  auto load_tile = [&](Tile& t, int pb_raw, const int4& e) {
+  // e: list entry of the block, ent: its (physical, logical) block
+  auto load_tile = [&](Tile& t, const int2& ent, const int4& e) {
     const bool valid = e.w != kEndKey;
-    int pb = __builtin_amdgcn_readfirstlane(pb_raw);
+    int pb = __builtin_amdgcn_readfirstlane(ent.x);
     pb = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the cache arrays
     const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * C::ROW_BYTES;
     const int nbytes = valid ? tile_bytes : 0;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(p.k_cache) + tile, nbytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v_cache) + tile, nbytes);
-    const int t0 = e.y, L = e.z;
+    const int t0 = SEL ? __builtin_amdgcn_readfirstlane(ent.y) * kBS : e.y;
+    const int L = e.z;
+    t.t0 = t0;
     const bool full = block_full(t0, L);
     const int ko = (full | kept(t0 + krow, L, p.sink, p.window)) ? k_off : kOutOfRange;
 #pragma unroll
@@ -622,7 +657,7 @@ void paged_attn_wave_kernel(AttnParams p) {
       start_segment(e.w);
       cur_key = e.w;
     }
-    const int t0 = e.y, L = e.z;
+    const int t0 = t.t0, L = e.z;
     const bool full = block_full(t0, L);
 
     // ---- V rows -> LDS (masked rows arrive as zeros) -----------------------
@@ -702,9 +737,9 @@ void paged_attn_wave_kernel(AttnParams p) {
   // Loads past the end of the list read nothing.
   {
     Tile ring[DEPTH];
-    int tab_ent[DEPTH];
+    int2 tab_ent[DEPTH];
     {
-      int first[DEPTH];
+      int2 first[DEPTH];
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) first[d] = load_table(entry_at(d).x);
 #pragma unroll
@@ -1057,7 +1092,8 @@ static AttnParams make_params(const AttnArgs& a) {
   p.plan = a.plan;
   p.rec_floats = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads, a.head_dim);
   p.num_seqs = a.num_seqs;
-  p.mbs = a.max_blocks_per_seq;
+  // a selected decode takes lengths as they are (its pages come with the selection)
+  p.mbs = a.selected ? (1 << 27) - 1 : a.max_blocks_per_seq;
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.num_blocks = a.num_blocks;
@@ -1067,18 +1103,21 @@ static AttnParams make_params(const AttnArgs& a) {
   p.window = a.window_tokens;
   p.min_units = a.min_units;
   p.list_cap = a.list_cap;
-  p.table_bytes = (int)((long long)a.num_seqs * a.max_blocks_per_seq * 4);
+  p.selected = a.selected;
+  p.budget = a.budget;
+  p.table_bytes = a.selected ? (int)((long long)a.num_seqs * a.num_kv_heads * a.budget * 8)
+                             : (int)((long long)a.num_seqs * a.max_blocks_per_seq * 4);
   p.scale_log2 = a.sm_scale * kLog2e;
   return p;
 }
 
-template <typename QT, typename KVT, int D, bool STREAM>
+template <typename QT, typename KVT, int D, bool STREAM, bool SEL>
 static int launch_wave(const AttnParams& p, int num_slots, hipStream_t st) {
   // (workgroup slot, group of up to 8 KV heads); one wave per KV head
   const int per_group = wave_group_size(p.num_kv_heads);
   const int groups = (p.num_kv_heads + per_group - 1) / per_group;
   const int lds = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, per_group, p.list_cap);
-  auto kernel = paged_attn_wave_kernel<QT, KVT, D, STREAM>;
+  auto kernel = paged_attn_wave_kernel<QT, KVT, D, STREAM, SEL>;
   static bool lds_set = false;
   if (!lds_set) {
     // above the default dynamic-LDS limit: the largest group needs ~100 KB
@@ -1094,10 +1133,15 @@ static int launch_wave(const AttnParams& p, int num_slots, hipStream_t st) {
 
 template <typename QT, typename KVT>
 static int launch_wave_d(const AttnParams& p, int num_slots, int D, bool stream, hipStream_t st) {
+  // a selected decode reads scattered pages with the default load policy
+  if (p.selected)
+    return D == 64 ? launch_wave<QT, KVT, 64, false, true>(p, num_slots, st)
+                   : launch_wave<QT, KVT, 128, false, true>(p, num_slots, st);
   if (stream)
-    return D == 64 ? launch_wave<QT, KVT, 64, true>(p, num_slots, st) : launch_wave<QT, KVT, 128, true>(p, num_slots, st);
-  return D == 64 ? launch_wave<QT, KVT, 64, false>(p, num_slots, st)
-                 : launch_wave<QT, KVT, 128, false>(p, num_slots, st);
+    return D == 64 ? launch_wave<QT, KVT, 64, true, false>(p, num_slots, st)
+                   : launch_wave<QT, KVT, 128, true, false>(p, num_slots, st);
+  return D == 64 ? launch_wave<QT, KVT, 64, false, false>(p, num_slots, st)
+                 : launch_wave<QT, KVT, 128, false, false>(p, num_slots, st);
 }
 
 template <typename QT, typename KVT, int D>

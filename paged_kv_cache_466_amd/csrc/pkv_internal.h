@@ -59,6 +59,10 @@ struct AttnArgs {
   // caches: one record per (sequence, KV head, partition), partition fastest.
   float* ws;
   int* plan;   // wave path: [num_seqs][4] ints for the merge, before the records
+  // selected decode: [S][Hkv][budget] (physical block, logical block) pairs
+  // in logical order; the units are these pages (partition_size 16)
+  const int32_t* selected;
+  int budget;
   void* stream;
 };
 
@@ -110,6 +114,13 @@ int launch_append_kv(const void* key, const void* value, void* k_cache, void* v_
 int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
                        const int32_t* src_dst, int n, int elem_bytes, int num_blocks, int block_size,
                        int num_kv_heads, int head_dim, void* stream);
+int launch_quest_summarize(const void* k_cache, int kv_dtype, void* k_summary, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_blocks,
+                           int num_kv_heads, int head_dim, int last_only, void* stream);
+int launch_quest_select(const void* query, int q_dtype, const void* k_summary, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int num_blocks, int budget, int32_t* selected,
+                        void* scratch, void* stream);
 int launch_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
                        float* dst_scales, const int32_t* block_ids, int n_blocks, int num_blocks,
                        int block_size, int num_kv_heads, int head_dim, void* stream);
