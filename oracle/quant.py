@@ -15,6 +15,14 @@ rounding.
 Group: one scale per (physical block, KV head) over the ``[block_size, d_k]``
 tile, separately for K and V.
 
+Appending to a quantised cache (the pages do not say how): a sequence keeps
+the source values of its partial last block (its "tail"); each new token is
+added to the tail and the whole block is quantised again from the tail, with
+the rows not yet written taken as zeros.  Zeros change neither the absmax
+nor any other code, so the block holds, at every step, the codes of its
+written rows, and once full exactly the codes of quantising the block at
+once.
+
 Precision: the page's example runs in float64; here every step is a single
 IEEE float32 operation (absmax is exact, then one fp32 division for the scale,
 one fp32 division per element, one rounding to the code grid), which is what
@@ -101,4 +109,29 @@ def quantize_cache_blocks(cache_vals, code_dtype, block_ids=None):
                 c, sc = quantize_fp8(tile)
                 codes[b, :, h, :] = c
             scales[b, h] = sc
+    return codes, scales
+
+
+def requantize_tail(tail_vals, rows, code_dtype):
+    """Codes and scales of a block quantised from its first ``rows`` written
+    rows, the others taken as zeros.
+
+    ``tail_vals``: [BS, Hkv, D] float32 source values (rows >= ``rows`` are
+    ignored).  Returns (codes [BS, Hkv, D] - int8 for "i8", uint8 for
+    "fp8e4m3" - and scales [Hkv] float32)."""
+    t = np.array(tail_vals, dtype=np.float32)
+    t[rows:] = 0.0
+    BS, Hkv, D = t.shape
+    codes = np.zeros(t.shape, dtype=np.int8 if code_dtype == "i8" else np.uint8)
+    scales = np.zeros(Hkv, dtype=np.float32)
+    for h in range(Hkv):
+        if code_dtype == "i8":
+            c, sc = quantize_int(t[:, h, :], 8)
+            codes[:, h, :] = c.astype(np.int8)
+        elif code_dtype == "fp8e4m3":
+            c, sc = quantize_fp8(t[:, h, :])
+            codes[:, h, :] = c
+        else:
+            raise ValueError(code_dtype)
+        scales[h] = sc
     return codes, scales

@@ -282,3 +282,40 @@ def test_copy_on_write_only_when_shared():
     q.alloc()
     with pytest.raises(pool.PoolExhausted):
         q.alloc()
+
+
+# --------------------------------------------------------------------------
+# appending to a quantised cache
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("code", ["i8", "fp8e4m3"])
+def test_token_by_token_requantisation_ends_at_the_whole_block_codes(code):
+    """A block filled one token at a time, quantised again from its tail after
+    each token, ends with exactly the codes and scales of quantising the
+    whole block at once; in between, every written row is within half a
+    step of its source value (INT8) and unwritten rows hold code 0."""
+    rng = np.random.default_rng(21)
+    tile = rng.standard_normal((16, 2, 32)).astype(np.float32)
+    tile[:, 1, 5] *= 8.0
+    for rows in range(1, 17):
+        codes, scales = quant.requantize_tail(tile, rows, code)
+        assert not codes[rows:].any()
+        if code == "i8":
+            back = quant.dequantize(codecs.decode(codes[:rows], "i8"), scales[None, :, None])
+            assert (np.abs(back - tile[:rows]) <= scales[None, :, None] * 0.5 * (1 + 1e-6)).all()
+    whole, whole_sc = quant.quantize_cache_blocks(tile[None], code)
+    assert codes.tobytes() == whole[0].tobytes()
+    assert scales.view(np.uint32).tolist() == whole_sc[0].view(np.uint32).tolist()
+
+
+def test_page_example_grows_one_value_at_a_time():
+    """The section-8 example's six values entered one by one into a 4-bit
+    group: the last requantisation prints the page's codes."""
+    g = golden("quant4_example.json")
+    vals = np.array(g["values"], dtype=np.float32)
+    codes = None
+    for n in range(1, len(vals) + 1):
+        x = np.zeros_like(vals)
+        x[:n] = vals[:n]
+        codes, sc = quant.quantize_int(x, g["bits"])
+    assert codes.tolist() == g["codes"]
