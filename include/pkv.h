@@ -362,6 +362,30 @@ pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes
                            int num_blocks, int block_size, int num_kv_heads, int head_dim,
                            void* stream);
 
+/*
+ * Appends one token per sequence to a quantised cache (the pages leave the
+ * how open; this is the reading taken).  Each sequence keeps the source
+ * values of its partial last block in a tail, [num_seqs][block_size]
+ * [num_kv_heads][head_dim] of src_dtype (caller-owned, one per K and V).
+ * For sequence s with positions[s] = p >= 0: row p % block_size of its tail
+ * takes key[s] / value[s] ([num_seqs][num_kv_heads][head_dim], src_dtype),
+ * and block block_tables[s][p / block_size] is quantised again from the
+ * tail's rows 0 .. p % block_size, the rows after them taken as zeros
+ * ([P2] s.8 absmax rule, the arithmetic of pkv_quantize_kv): its codes and
+ * its scales per KV head are rewritten, later rows get code 0.  Once a
+ * block is full its codes and scales are exactly pkv_quantize_kv's for its
+ * rows.  Tail rows before p % block_size must hold the block's earlier
+ * tokens (a prefill's partial last block is copied into the tail by the
+ * caller; a fork copies its parent's tail with the block).  positions[s] <
+ * 0 skips sequence s; one token per sequence per call.
+ */
+pkv_status pkv_append_kv_quantized(const void* key, const void* value, int src_dtype,
+                                   void* k_tail, void* v_tail, void* k_codes, void* v_codes,
+                                   int code_dtype, float* k_scales, float* v_scales,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* positions, int num_seqs, int num_blocks, int block_size,
+                                   int num_kv_heads, int head_dim, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host-side checks                                                          */
 /* ------------------------------------------------------------------------ */

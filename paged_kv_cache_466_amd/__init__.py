@@ -16,7 +16,7 @@ __all__ = [
     "paged_attn_decode", "paged_attn_partition", "paged_attn_merge",
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
     "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
-    "slot_mapping", "reshape_and_cache", "append_kv", "copy_blocks", "quantize_kv",
+    "slot_mapping", "reshape_and_cache", "append_kv", "append_kv_quantized", "copy_blocks", "quantize_kv",
     "validate_tables", "BlockPool", "DTYPES",
 ]
 
@@ -60,6 +60,7 @@ _SIGS = {
     "pkv_slot_mapping": ([_p, _p, _i, _p, _p, _i, _i, _i, _i, _p], _i),
     "pkv_reshape_and_cache": ([_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_append_kv": ([_p, _p, _p, _p, _i, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p], _i),
+    "pkv_append_kv_quantized": ([_p, _p, _i, _p, _p, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_copy_blocks": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p], _i),
     "pkv_quantize_kv": ([_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_validate_tables": ([_p, _i, _p, _i, _i, _i, _p, _i], _i),
@@ -329,6 +330,23 @@ def append_kv(key, value, k_cache, v_cache, block_tables, positions, seq_ids=Non
     _check(lib.pkv_append_kv(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache),
                              _ptr(block_tables), block_tables.shape[1], _ptr(seq_ids), _ptr(positions),
                              _ptr(slot_mapping), T, block_tables.shape[0], NB, BS, Hkv, D, _stream(key)))
+
+
+def append_kv_quantized(key, value, k_tail, v_tail, k_codes, v_codes, k_scales, v_scales, block_tables,
+                        positions, code_dtype):
+    """Appends one token per sequence to a quantised cache
+    (``pkv_append_kv_quantized``): key/value [S, Hkv, D] and the tails
+    [S, 16, Hkv, D] in the source dtype; codes [NB, 16, Hkv, D] int8 /
+    uint8, scales [NB, Hkv] fp32; positions int32 [S] (< 0 skips)."""
+    _contig(key, value, k_tail, v_tail, k_codes, v_codes, k_scales, v_scales, block_tables, positions)
+    S, Hkv, D = key.shape
+    NB, BS = k_codes.shape[:2]
+    if tuple(k_tail.shape) != (S, BS, Hkv, D) or k_tail.dtype != key.dtype or value.shape != key.shape:
+        raise ValueError("tails must be [S, block_size, Hkv, D] of the key dtype")
+    _check(lib.pkv_append_kv_quantized(_ptr(key), _ptr(value), _dtype(key), _ptr(k_tail), _ptr(v_tail),
+                                       _ptr(k_codes), _ptr(v_codes), DTYPES[code_dtype], _ptr(k_scales),
+                                       _ptr(v_scales), _ptr(block_tables), block_tables.shape[1], _ptr(positions),
+                                       S, NB, BS, Hkv, D, _stream(key)))
 
 
 def copy_blocks(k_cache, v_cache, src_dst, k_scales=None, v_scales=None, dtype=None):

@@ -261,4 +261,125 @@ int launch_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, in
 #undef PKV_Q
 }
 
+// ---------------------------------------------------------------------------
+// append_kv_quantized: the new token of each sequence goes into the
+// sequence's tail (the source values of its partial last block), and the
+// block is quantised again from the tail, its unwritten rows taken as
+// zeros.  One wave per (sequence, KV head, K or V), with quantize_kv's lane
+// layout (lane l: token row l/4, quarter l%4 of the head dimension) and the
+// same arithmetic, so a full block ends with exactly quantize_kv's codes.
+// ---------------------------------------------------------------------------
+template <typename SRC, int D, bool FP8OUT>
+__global__ __launch_bounds__(64) void append_quantized_kernel(
+    const typename SRC::raw* __restrict__ key, const typename SRC::raw* __restrict__ value,
+    typename SRC::raw* __restrict__ k_tail, typename SRC::raw* __restrict__ v_tail, uint8_t* __restrict__ k_codes,
+    uint8_t* __restrict__ v_codes, float* __restrict__ k_scales, float* __restrict__ v_scales,
+    const int32_t* __restrict__ tables, int mbs, const int32_t* __restrict__ positions, int num_blocks,
+    int num_kv_heads) {
+  constexpr int BS = 16;
+  constexpr int ELEMS = D / 4;                 // per lane
+  constexpr int SRC_CHUNKS = ELEMS * SRC::bytes / 16;
+  constexpr int EL16 = 16 / SRC::bytes;
+  const int s = blockIdx.x, h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int pos = positions[s];
+  if (pos < 0 || pos / BS >= mbs) return;
+  const int row = pos % BS;
+  const int b = tables[(size_t)s * mbs + pos / BS];
+  if (b < 0 || b >= num_blocks) return;
+  const int lane = threadIdx.x;
+  const int t = lane >> 2, q = lane & 3;
+  typename SRC::raw* tail = (is_v ? v_tail : k_tail) + (((size_t)s * BS + t) * num_kv_heads + h) * D + q * ELEMS;
+  float x[ELEMS];
+  if (t < row) {
+    const uint4* p = reinterpret_cast<const uint4*>(tail);
+#pragma unroll
+    for (int c = 0; c < SRC_CHUNKS; ++c) decode16<SRC>(p[c], x + c * EL16);
+  } else if (t == row) {
+    const typename SRC::raw* src = (is_v ? value : key) + ((size_t)s * num_kv_heads + h) * D + q * ELEMS;
+    const uint4* p = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+    for (int c = 0; c < SRC_CHUNKS; ++c) {
+      const uint4 v = p[c];
+      reinterpret_cast<uint4*>(tail)[c] = v;
+      decode16<SRC>(v, x + c * EL16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ELEMS; ++i) x[i] = 0.f;
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
+  a = wave_max(a);
+  const float qmax = FP8OUT ? 448.0f : 127.0f;
+  const float sc = __fdiv_rn(a, qmax);
+  uint8_t codes[ELEMS];
+#pragma unroll
+  for (int i = 0; i < ELEMS; ++i) {
+    if (sc == 0.f) {
+      codes[i] = 0;
+    } else {
+      const float y = __fdiv_rn(x[i], sc);
+      if (FP8OUT) {
+        codes[i] = (uint8_t)f32_to_e4m3(y);
+      } else {
+        float r = rintf(y);
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        codes[i] = (uint8_t)(int8_t)(int)r;
+      }
+    }
+  }
+  uint8_t* dst = is_v ? v_codes : k_codes;
+  uint4* o = reinterpret_cast<uint4*>(dst + (((size_t)b * BS + t) * num_kv_heads + h) * D + q * ELEMS);
+#pragma unroll
+  for (int c = 0; c < ELEMS / 16; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)codes[c * 16 + 4 * k] | ((uint32_t)codes[c * 16 + 4 * k + 1] << 8) |
+             ((uint32_t)codes[c * 16 + 4 * k + 2] << 16) | ((uint32_t)codes[c * 16 + 4 * k + 3] << 24);
+    o[c] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (lane == 0) (is_v ? v_scales : k_scales)[(size_t)b * num_kv_heads + h] = sc;
+}
+
+template <typename SRC, int D>
+static int launch_aq(const void* key, const void* value, void* k_tail, void* v_tail, void* k_codes, void* v_codes,
+                     int code_dtype, float* k_scales, float* v_scales, const int32_t* tables, int mbs,
+                     const int32_t* positions, int num_seqs, int num_blocks, int num_kv_heads, hipStream_t st) {
+  typedef typename SRC::raw R;
+  const dim3 grid(num_seqs, num_kv_heads, 2);
+  if (code_dtype == PKV_FP8E4M3)
+    append_quantized_kernel<SRC, D, true><<<grid, 64, 0, st>>>(
+        (const R*)key, (const R*)value, (R*)k_tail, (R*)v_tail, (uint8_t*)k_codes, (uint8_t*)v_codes, k_scales,
+        v_scales, tables, mbs, positions, num_blocks, num_kv_heads);
+  else
+    append_quantized_kernel<SRC, D, false><<<grid, 64, 0, st>>>(
+        (const R*)key, (const R*)value, (R*)k_tail, (R*)v_tail, (uint8_t*)k_codes, (uint8_t*)v_codes, k_scales,
+        v_scales, tables, mbs, positions, num_blocks, num_kv_heads);
+  return hipGetLastError();
+}
+
+int launch_append_quantized(const void* key, const void* value, int src_dtype, void* k_tail, void* v_tail,
+                            void* k_codes, void* v_codes, int code_dtype, float* k_scales, float* v_scales,
+                            const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
+                            int num_seqs, int num_blocks, int num_kv_heads, int head_dim, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+#define PKV_AQ(SRC)                                                                                          \
+  return head_dim == 64                                                                                      \
+             ? launch_aq<SRC, 64>(key, value, k_tail, v_tail, k_codes, v_codes, code_dtype, k_scales,        \
+                                  v_scales, block_tables, max_blocks_per_seq, positions, num_seqs, num_blocks, \
+                                  num_kv_heads, st)                                                          \
+             : launch_aq<SRC, 128>(key, value, k_tail, v_tail, k_codes, v_codes, code_dtype, k_scales,       \
+                                   v_scales, block_tables, max_blocks_per_seq, positions, num_seqs,          \
+                                   num_blocks, num_kv_heads, st)
+  switch (src_dtype) {
+    case PKV_F32: PKV_AQ(F32);
+    case PKV_BF16: PKV_AQ(BF16);
+    default: PKV_AQ(F16);
+  }
+#undef PKV_AQ
+}
+
 }  // namespace pkv

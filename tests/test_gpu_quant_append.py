@@ -1,0 +1,89 @@
+"""GPU parity of appending to an INT8 / FP8 cache one token at a time
+(``pkv_append_kv_quantized``) against the oracle's ``requantize_tail``:
+codes and scales of every written block bit-exact after each checked step,
+and decode attention over the growing sequences within 2e-2 of the oracle
+run on the same dequantised values."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, codecs, quant
+from oracle_pipeline import to_raw
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+TORCH = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def src_values(rng, shape, dtype, outliers=False):
+    """Seeded N(0,1) values rounded to the source dtype, with two channels x8
+    when ``outliers`` (the keys of the quantised workload have such
+    channels): (torch tensor on the GPU, exact float32 values)."""
+    x = rng.standard_normal(shape).astype(np.float32)
+    if outliers:
+        x[..., 3] *= 8.0
+        x[..., 17] *= 8.0
+    t = torch.from_numpy(x).to(TORCH[dtype])
+    return t.cuda(), codecs.decode(to_raw(t, dtype), dtype)
+
+
+@pytest.mark.parametrize("code,src,D,Hkv", [("i8", "bf16", 128, 4), ("fp8e4m3", "bf16", 128, 2),
+                                            ("i8", "f16", 64, 2), ("fp8e4m3", "f16", 64, 1)])
+def test_append_token_by_token(code, src, D, Hkv):
+    import paged_kv_cache_466_amd as pkv
+    rng = np.random.default_rng(31)
+    S, G, T, BS = 3, 4, 37, 16
+    Hq = Hkv * G
+    mbs = (T + BS - 1) // BS
+    NB = S * mbs + 2
+    order = rng.permutation(NB).astype(np.int32)
+    tables = order[: S * mbs].reshape(S, mbs)
+    bt = torch.from_numpy(tables.copy()).cuda()
+    cdt = torch.int8 if code == "i8" else torch.uint8
+    poison = -128 if code == "i8" else 0x7F
+    kc = torch.full((NB, BS, Hkv, D), poison, dtype=cdt, device="cuda")
+    vc = torch.full_like(kc, poison)
+    ks = torch.full((NB, Hkv), float("nan"), device="cuda")
+    vs = torch.full_like(ks, float("nan"))
+    kt = torch.full((S, BS, Hkv, D), float("nan"), dtype=TORCH[src], device="cuda")
+    vt = torch.full_like(kt, float("nan"))
+    # oracle state
+    o_kc = np.full((NB, BS, Hkv, D), poison, dtype=np.int8 if code == "i8" else np.uint8)
+    o_vc = o_kc.copy()
+    o_ks = np.zeros((NB, Hkv), np.float32)
+    o_vs = np.zeros((NB, Hkv), np.float32)
+    o_kt = np.zeros((S, BS, Hkv, D), np.float32)
+    o_vt = np.zeros((S, BS, Hkv, D), np.float32)
+    sm = np.float32(1.0 / np.sqrt(D))
+    worst = 0.0
+    for step in range(T):
+        k_new, k_val = src_values(rng, (S, Hkv, D), src, outliers=True)
+        v_new, v_val = src_values(rng, (S, Hkv, D), src)
+        pos = torch.full((S,), step, dtype=torch.int32, device="cuda")
+        pkv.append_kv_quantized(k_new, v_new, kt, vt, kc, vc, ks, vs, bt, pos, code)
+        row, lb = step % BS, step // BS
+        for s in range(S):
+            b = tables[s, lb]
+            o_kt[s, row], o_vt[s, row] = k_val[s], v_val[s]
+            o_kc[b], o_ks[b] = quant.requantize_tail(o_kt[s], row + 1, code)
+            o_vc[b], o_vs[b] = quant.requantize_tail(o_vt[s], row + 1, code)
+        if step not in (0, 5, 15, 16, 17, T - 1):
+            continue
+        used = tables[:, : lb + 1].reshape(-1)
+        assert to_raw(kc, code)[used].tobytes() == o_kc[used].tobytes(), step
+        assert to_raw(vc, code)[used].tobytes() == o_vc[used].tobytes(), step
+        assert ks.cpu().numpy()[used].view(np.uint32).tolist() == o_ks[used].view(np.uint32).tolist()
+        assert vs.cpu().numpy()[used].view(np.uint32).tolist() == o_vs[used].view(np.uint32).tolist()
+        # decode over the step + 1 tokens
+        q, q_val = src_values(rng, (S, Hq, D), src)
+        lens = torch.full((S,), step + 1, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(q)
+        pkv.paged_attn_decode(out, q, kc, vc, bt, lens, float(sm), ks, vs, kv_dtype=code)
+        ref = attention.paged_decode(to_raw(q, src), src, o_kc, o_vc, code, tables, [step + 1] * S, BS, sm,
+                                     o_ks, o_vs)
+        err = float(np.abs(out.float().cpu().numpy() - ref).max())
+        worst = max(worst, err)
+        assert err <= TOL, (step, err)
+    print(f"[quant-append] {code} {src} D={D} Hkv={Hkv} max_abs_err={worst:.3e}")
