@@ -16,7 +16,7 @@ Sources (cited by page title and section):
 * "KV Cache Engineering for LLM Serving, clearly explained": "The cache
   formula", section 1 "GQA and MQA cache fewer heads", section 3 "Sliding
   windows", section 7 "Query-aware sparse reads", section 8 "Quantization",
-  section 10 "Paging".
+  section 9 "Eviction", section 10 "Paging", section 11 "Prefix reuse".
 * Learning-AI topic t13_4 (KV cache management): the cache-size formula
   paragraph, the block-table paragraph and its example, and the
   copy-on-write paragraph.
@@ -37,6 +37,8 @@ Modules:
 * ``quest``     - query-aware page selection: per-page key minimum /
                   maximum, the page score, top-budget selection, and decode
                   over the selected pages.
+* ``reuse``     - full-prefix block keys and their cache; H2O retention of
+                  the recent positions plus the older heavy hitters.
 
 Every function here is pinned by tests in ``tests/test_oracle_*.py`` against
 values the pages print, closed forms, invariants, library routines
@@ -44,4 +46,4 @@ values the pages print, closed forms, invariants, library routines
 ``float8_e4m3fn`` cast) or brute force.  No function is "parity unpinned".
 """
 
-from . import attention, codecs, paging, pool, quant, quest, sizes  # noqa: F401
+from . import attention, codecs, paging, pool, quant, quest, reuse, sizes  # noqa: F401
