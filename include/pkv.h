@@ -8,8 +8,8 @@
  *        Quantization", "Token Eviction and Pruning".
  *   [P2] "KV Cache Engineering for LLM Serving, clearly explained", sections
  *        "The cache formula", 1 "GQA and MQA cache fewer heads", 3 "Sliding
- *        windows", 7 "Query-aware sparse reads", 8 "Quantization", 10
- *        "Paging".
+ *        windows", 7 "Query-aware sparse reads", 8 "Quantization", 9
+ *        "Eviction", 10 "Paging", 11 "Prefix reuse".
  *   [P3] Learning-AI topic t13_4 (KV cache management): block-table and
  *        copy-on-write paragraphs.
  *
@@ -446,6 +446,64 @@ pkv_status pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* u
                           int32_t* shared_blocks);
 /* Copies the free list, front first, into out[0 .. min(n, cap)); *n = its length. */
 pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* ------------------------------------------------------------------------ */
+/* Host block reuse                                                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * Prefix cache ([P2] s.11 "Prefix reuse"): a completed block is stored
+ * under its full token prefix (kept as a chain of (parent entry, the
+ * block's own block_size tokens), compared in full: no false match), so a
+ * request starting with the same tokens reuses it.  The cache holds one
+ * reference (pkv_pool_incref) per cached block.  Host only; tokens are
+ * int32 ids.
+ */
+typedef struct pkv_prefix_cache pkv_prefix_cache;
+
+/* A cache over `pool` (not owned; it must outlive the cache).  NULL on error. */
+pkv_prefix_cache* pkv_prefix_cache_create(pkv_pool* pool, int block_size);
+/* Releases the cache's references and frees it. */
+void pkv_prefix_cache_destroy(pkv_prefix_cache* cache);
+
+/*
+ * The leading full blocks of tokens[0 .. n_tokens) that are cached, up to
+ * the first miss and at most max_blocks: their physical blocks go to
+ * blocks_out[0 .. *n_matched), and the caller receives one pool reference
+ * for each (release with pkv_pool_decref when the sequence ends).
+ */
+pkv_status pkv_prefix_cache_match(pkv_prefix_cache* cache, const int32_t* tokens, int n_tokens,
+                                  int32_t* blocks_out, int max_blocks, int* n_matched);
+
+/*
+ * Stores the full blocks of tokens[0 .. n_tokens) held in blocks[0 ..
+ * n_blocks) (a sequence's table); a block whose prefix is already cached
+ * keeps the cached entry.  The cache takes a reference to each block it
+ * adds; *n_added (may be NULL) receives their number.
+ */
+pkv_status pkv_prefix_cache_insert(pkv_prefix_cache* cache, const int32_t* tokens, int n_tokens,
+                                   const int32_t* blocks, int n_blocks, int* n_added);
+
+/*
+ * Drops up to n_wanted entries, least recently used first, among those with
+ * no cached entry after them and whose block only the cache holds; their
+ * blocks go back to the pool's free list.  *n_evicted (may be NULL)
+ * receives the count.
+ */
+pkv_status pkv_prefix_cache_evict(pkv_prefix_cache* cache, int n_wanted, int* n_evicted);
+
+/* Entries in the cache (-1 for NULL). */
+int pkv_prefix_cache_size(const pkv_prefix_cache* cache);
+
+/*
+ * H2O retention ([P2] s.9 "Eviction"): of n positions with accumulated
+ * attention scores, keep the latest min(recent_count, budget) and give the
+ * rest of the budget to the older positions with the largest scores
+ * (earlier position first among equal scores).  kept_out[0 .. *n_kept)
+ * receives the kept positions in increasing order (all n when budget >= n).
+ * NaN scores give PKV_EINVAL.
+ */
+pkv_status pkv_h2o_retain(const float* scores, int n, int budget, int recent_count, int32_t* kept_out,
+                          int* n_kept);
 
 #ifdef __cplusplus
 }

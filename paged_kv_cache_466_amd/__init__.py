@@ -17,7 +17,7 @@ __all__ = [
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
     "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
     "slot_mapping", "reshape_and_cache", "append_kv", "append_kv_quantized", "copy_blocks", "quantize_kv",
-    "validate_tables", "BlockPool", "DTYPES",
+    "validate_tables", "BlockPool", "PrefixCache", "h2o_retain", "DTYPES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,6 +65,13 @@ _SIGS = {
     "pkv_quantize_kv": ([_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_validate_tables": ([_p, _i, _p, _i, _i, _i, _p, _i], _i),
     "pkv_pool_create": ([_i, _p], _p),
+    "pkv_prefix_cache_create": ([_p, _i], _p),
+    "pkv_prefix_cache_destroy": ([_p], None),
+    "pkv_prefix_cache_match": ([_p, _p, _i, _p, _i, _p], _i),
+    "pkv_prefix_cache_insert": ([_p, _p, _i, _p, _i, _p], _i),
+    "pkv_prefix_cache_evict": ([_p, _i, _p], _i),
+    "pkv_prefix_cache_size": ([_p], _i),
+    "pkv_h2o_retain": ([_p, _i, _i, _i, _p, _p], _i),
     "pkv_pool_destroy": ([_p], None),
     "pkv_pool_alloc": ([_p, _i32p], _i),
     "pkv_pool_incref": ([_p, ctypes.c_int32], _i),
@@ -454,3 +461,64 @@ class BlockPool:
     def release(self, table):
         for b in table:
             self.decref(b)
+
+
+class PrefixCache:
+    """The library's prefix cache over a ``BlockPool`` (``pkv_prefix_cache_*``):
+    full blocks stored under their whole token prefix."""
+
+    def __init__(self, pool, block_size=16):
+        self.pool = pool            # kept alive: the cache holds references into it
+        self.block_size = block_size
+        self._h = lib.pkv_prefix_cache_create(pool._h, block_size)
+        if not self._h:
+            raise PkvError(1, last_error())
+
+    def __del__(self, _destroy=lib.pkv_prefix_cache_destroy):
+        h = getattr(self, "_h", None)
+        if h:
+            _destroy(h)
+            self._h = None
+
+    @staticmethod
+    def _tokens(tokens):
+        t = [int(x) for x in tokens]
+        return (ctypes.c_int32 * max(1, len(t)))(*t), len(t)
+
+    def match(self, tokens):
+        """Physical blocks of the cached leading full blocks of ``tokens``;
+        the caller receives one pool reference per block."""
+        buf, n = self._tokens(tokens)
+        cap = n // self.block_size
+        out = (ctypes.c_int32 * max(1, cap))()
+        got = ctypes.c_int()
+        _check(lib.pkv_prefix_cache_match(self._h, buf, n, out, cap, ctypes.byref(got)))
+        return list(out[: got.value])
+
+    def insert(self, tokens, blocks):
+        """Stores the full blocks of ``tokens`` held in ``blocks``; returns the
+        number of entries added."""
+        buf, n = self._tokens(tokens)
+        b = [int(x) for x in blocks]
+        bb = (ctypes.c_int32 * max(1, len(b)))(*b)
+        added = ctypes.c_int()
+        _check(lib.pkv_prefix_cache_insert(self._h, buf, n, bb, len(b), ctypes.byref(added)))
+        return added.value
+
+    def evict(self, n):
+        got = ctypes.c_int()
+        _check(lib.pkv_prefix_cache_evict(self._h, int(n), ctypes.byref(got)))
+        return got.value
+
+    def __len__(self):
+        return lib.pkv_prefix_cache_size(self._h)
+
+
+def h2o_retain(scores, budget, recent_count):
+    """Positions kept by the H2O rule (``pkv_h2o_retain``), in increasing order."""
+    s = [float(x) for x in scores]
+    buf = (ctypes.c_float * max(1, len(s)))(*s)
+    out = (ctypes.c_int32 * max(1, len(s)))()
+    n = ctypes.c_int()
+    _check(lib.pkv_h2o_retain(buf, len(s), int(budget), int(recent_count), out, ctypes.byref(n)))
+    return list(out[: n.value])

@@ -19,7 +19,7 @@ LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libpkv.so")
 OBJDIR = os.path.join(ROOT, "_build", "pkv")
 
-SOURCES = ["api.hip", "cache_ops.hip", "paged_attn.hip", "quest.hip", "pool.cpp"]
+SOURCES = ["api.hip", "cache_ops.hip", "paged_attn.hip", "quest.hip", "pool.cpp", "reuse.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -185,3 +185,86 @@ def test_argument_errors_return_before_launch():
     assert L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 0, 32, 8, 128, 16, 10,
                                    0.1, 0, 0, 0, 0, None, 0, None) == 0
     assert L.pkv_reshape_and_cache(None, None, None, None, 1, None, 0, 10, 16, 8, 128, None) == 0
+
+
+# --------------------------------------------------------------------------
+# host block reuse: prefix cache and H2O retention
+# --------------------------------------------------------------------------
+
+def test_prefix_cache_reproduces_page_example():
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "prefix_reuse_example.json")))
+    pool = pkv.BlockPool(16)
+    c = pkv.PrefixCache(pool, g["block_size"])
+    assert c.match(g["first"]) == []
+    first_blocks = [pool.alloc() for _ in range(3)]
+    assert c.insert(g["first"], first_blocks) == 3
+    hits = c.match(g["second"])
+    assert len(hits) == g["second_reused"] and hits == first_blocks[:2]
+    assert 3 - len(hits) == g["second_new_blocks"]
+    # the lookup handed the caller a reference per block, the cache holds one
+    assert [pool.refcount(b) for b in first_blocks] == [3, 3, 2]
+
+
+def test_prefix_cache_matches_oracle_on_random_requests():
+    """Differential test against the oracle's full-prefix-key dictionary:
+    requests over a small vocabulary (many shared prefixes) look up, take
+    new blocks for the rest, store their full blocks and finish."""
+    rng = random.Random(9)
+    bs = 4
+    pool = pkv.BlockPool(4000)
+    c = pkv.PrefixCache(pool, bs)
+    o = oracle.reuse.PrefixCache(bs)
+    for _ in range(300):
+        n = rng.randint(0, 30)
+        stem = [1, 2, 3, 4, 5, 6, 7, 8][: rng.randint(0, 8)]
+        toks = stem + [rng.randint(0, 3) for _ in range(n)]
+        got = c.match(toks)
+        assert got == o.match(toks)
+        need = -(-len(toks) // bs)
+        blocks = got + [pool.alloc() for _ in range(need - len(got))]
+        added = c.insert(toks, blocks)
+        assert added == o.insert(toks, blocks)
+        for b in blocks:                      # the request finishes
+            pool.decref(b)
+    assert len(c) == len(o.blocks)
+    # every cached block is held by the cache only, so all can be evicted
+    assert c.evict(10 ** 6) == len(o.blocks)
+    assert len(c) == 0 and len(pool.free_list()) == pool.num_blocks
+
+
+def test_prefix_cache_evicts_least_recently_used_leaf():
+    pool = pkv.BlockPool(8)
+    c = pkv.PrefixCache(pool, 2)
+    a, b = [1, 2, 3, 4, 5, 6], [1, 2, 3, 4, 7, 8]
+    ablk = [pool.alloc() for _ in range(3)]
+    c.insert(a, ablk)
+    hit = c.match(b)
+    bblk = hit + [pool.alloc()]
+    c.insert(b, bblk)
+    for blk in ablk + bblk:
+        pool.decref(blk)
+    assert c.evict(1) == 1                    # a's last block: the older leaf
+    ha, hb = c.match(a), c.match(b)
+    assert ha == ablk[:2] and hb == bblk
+    # blocks a running sequence holds are not evicted
+    assert c.evict(10) == 0 and len(c) == 3
+    for blk in ha + hb:
+        pool.decref(blk)
+    assert c.evict(10) == 3 and len(c) == 0
+    assert len(pool.free_list()) == 8
+
+
+def test_h2o_matches_page_and_oracle():
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "h2o_example.json")))
+    assert pkv.h2o_retain(g["scores"], g["budget"], g["recent_count"]) == g["retained"]
+    rng = random.Random(4)
+    for _ in range(300):
+        n = rng.randint(0, 40)
+        scores = [rng.choice([0.0, 0.25, 1.0, 3.5]) for _ in range(n)]
+        budget = rng.randint(0, n + 2)
+        recent = rng.randint(0, budget + 1)
+        assert pkv.h2o_retain(scores, budget, recent) == oracle.reuse.h2o_retain(scores, budget, recent)
+    with pytest.raises(pkv.PkvError):
+        pkv.h2o_retain([1.0, float("nan")], 1, 0)
