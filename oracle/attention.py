@@ -8,6 +8,9 @@ is exactly softmax attention over the sequence's tokens in logical order.
 
 GQA (same section): query head ``h`` reads KV head ``h // (Hq // Hkv)``.
 
+Several query tokens per sequence (``multi_query_decode``): each new token
+sees the cache up to and including its own position.
+
 StreamingLLM keep-mask ("Chapter 18 - KV-Cache Optimization Strategies",
 section "Token Eviction and Pruning"): the first ``sink`` tokens plus the most
 recent ``window`` tokens (4 + 4092 = 4096 entries in the page's layout).
@@ -108,6 +111,31 @@ def paged_decode(query, q_dtype, k_cache, v_cache, kv_dtype, block_tables, seq_l
         K = decoded_cache_rows(k_cache, block_tables[s], L, block_size, kv_dtype, k_scales)
         V = decoded_cache_rows(v_cache, block_tables[s], L, block_size, kv_dtype, v_scales)
         out[s] = decode_sequence(qv[s], K, V, sm_scale, sink, window)
+    return out
+
+
+def multi_query_decode(query, q_dtype, k_cache, v_cache, kv_dtype, block_tables, seq_lens, block_size,
+                       sm_scale, k_scales=None, v_scales=None):
+    """Several new tokens per sequence attending to the paged cache (a
+    speculative-decode check or a short chunk of prefill; the pages stop at
+    one token per step, this is the plain causal reading).
+
+    ``query``: raw [S, T, Hq, D]; ``seq_lens[s]`` counts the T new tokens,
+    whose keys and values are already in the cache at positions
+    L - T .. L - 1.  Token t sees the positions 0 .. L - T + t.  Returns
+    float32 [S, T, Hq, D]."""
+    qv = codecs.decode(query, q_dtype)
+    S, T, Hq, D = qv.shape
+    out = np.zeros((S, T, Hq, D), dtype=np.float32)
+    for s in range(S):
+        L = int(seq_lens[s])
+        K = decoded_cache_rows(k_cache, block_tables[s], L, block_size, kv_dtype, k_scales)
+        V = decoded_cache_rows(v_cache, block_tables[s], L, block_size, kv_dtype, v_scales)
+        for t in range(T):
+            n = L - T + t + 1
+            if n <= 0:
+                continue
+            out[s, t] = decode_sequence(qv[s, t], K[:n], V[:n], sm_scale)
     return out
 
 

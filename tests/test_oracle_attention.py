@@ -2,6 +2,7 @@
 invariants that hold for any correct paged decode."""
 
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -214,3 +215,64 @@ def test_copy_on_write_step_on_shared_prefix():
     q = to_raw(t["query"], "bf16")
     out = run.decode(q)
     assert np.isfinite(out).all()
+
+
+# --------------------------------------------------------------------------
+# several query tokens per sequence
+# --------------------------------------------------------------------------
+
+def _paged_case(rng, S, L, Hq, Hkv, D, bs=16):
+    nb = sum(-(-l // bs) for l in L)
+    order = rng.permutation(nb)
+    k = rng.standard_normal((nb, bs, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((nb, bs, Hkv, D)).astype(np.float32)
+    tables, pos = [], 0
+    for l in L:
+        n = -(-l // bs)
+        tables.append(list(order[pos:pos + n]) + [0])
+        pos += n
+    width = max(len(t) for t in tables)
+    bt = np.array([t + [0] * (width - len(t)) for t in tables], dtype=np.int64)
+    return k, v, bt
+
+
+def test_multi_query_token_t_is_the_decode_of_its_prefix():
+    """Token t of T new tokens gives exactly the one-token decode of the
+    sequence cut after its own position; T = 1 is the decode."""
+    rng = np.random.default_rng(41)
+    S, Hq, Hkv, D, T = 3, 8, 2, 16, 4
+    L = [37, 16, 70]
+    k, v, bt = _paged_case(rng, S, L, Hq, Hkv, D)
+    q = rng.standard_normal((S, T, Hq, D)).astype(np.float32)
+    out = attention.multi_query_decode(q, "f32", k, v, "f32", bt, L, 16, 0.25)
+    for t in range(T):
+        cut = [l - T + t + 1 for l in L]
+        ref = attention.paged_decode(q[:, t], "f32", k, v, "f32", bt, cut, 16, 0.25)
+        assert np.array_equal(out[:, t], ref)
+    one = attention.multi_query_decode(q[:, -1:], "f32", k, v, "f32", bt, L, 16, 0.25)
+    assert np.array_equal(one[:, 0], attention.paged_decode(q[:, -1], "f32", k, v, "f32", bt, L, 16, 0.25))
+
+
+def test_multi_query_against_scalar_loops():
+    """Brute force: explicit loops over positions with the causal limit."""
+    rng = np.random.default_rng(43)
+    S, Hq, Hkv, D, T = 2, 4, 2, 8, 3
+    L = [19, 5]
+    k, v, bt = _paged_case(rng, S, L, Hq, Hkv, D)
+    q = rng.standard_normal((S, T, Hq, D)).astype(np.float32)
+    out = attention.multi_query_decode(q, "f32", k, v, "f32", bt, L, 16, 0.5)
+    G = Hq // Hkv
+    for s in range(S):
+        for t in range(T):
+            for h in range(Hq):
+                n = L[s] - T + t + 1
+                sc, vals = [], []
+                for p in range(n):
+                    blk, off = bt[s][p // 16], p % 16
+                    sc.append(0.5 * sum(float(q[s, t, h, d]) * float(k[blk, off, h // G, d]) for d in range(D)))
+                    vals.append([float(x) for x in v[blk, off, h // G]])
+                m = max(sc)
+                w = [math.exp(x - m) for x in sc]
+                tot = sum(w)
+                ref = [sum(w[i] * vals[i][d] for i in range(n)) / tot for d in range(D)]
+                assert np.abs(out[s, t, h] - np.array(ref)).max() < 1e-5
