@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--query-tokens", type=int, default=1, metavar="T",
+                    help="T query tokens per sequence in one pass (checking speculative drafts)")
     ap.add_argument("--quest", type=int, default=0, metavar="PAGES",
                     help="time query-aware page selection reading PAGES pages per (sequence, KV head) instead")
     ap.add_argument("--no-long-context", action="store_true",
@@ -298,6 +300,83 @@ def measure_quest(w, steps, warmup, copies, budget):
     }
 
 
+def measure_multi(w, steps, warmup, copies, T):
+    """Times `steps` steps in which T query tokens per sequence attend to the
+    cache in one pass (the slot write of one token, then the decode of all
+    T): tokens/s and KV-read GB/s."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_466_amd as pkv
+    from gpu_pipeline import GpuRun
+    from workloads import draw_tensors
+
+    print(f"[bench] multi-query workload={w.name} S={w.S} T={T}", file=sys.stderr, flush=True)
+    t = draw_tensors(w, "cuda")
+    runs = [GpuRun(w, t)]
+    for _ in range(copies - 1):
+        r = GpuRun.__new__(GpuRun)
+        r.__dict__.update(runs[0].__dict__)
+        r.k_cache = runs[0].k_cache.clone()
+        r.v_cache = runs[0].v_cache.clone()
+        runs.append(r)
+    g = runs[0]
+    torch.cuda.synchronize()
+    lens = g.lens.cpu().numpy()
+    kv_bytes = kv_bytes_per_step(w, lens)
+    S, Hq, D = t["query"].shape
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.randn((S, T, Hq, D), generator=gen, device="cuda").to(t["query"].dtype)
+    out = torch.empty_like(q)
+    mbs = g.block_tables.shape[1]
+    psize = w.partition_size
+    nbytes = pkv.paged_attn_workspace_bytes(w.kv_dtype, S, Hq * T, w.Hkv, D, mbs * 16, psize)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    positions = (g.lens - 1).contiguous()
+    slots = torch.empty(S, dtype=torch.int32, device="cuda")
+    stream_kv = not (w.prefix_tokens or w.fork)
+
+    quant = w.kv_dtype in ("i8", "fp8e4m3")
+    kvdt = w.kv_dtype if w.kv_dtype == "fp8e4m3" else None
+
+    def step(r, ev=None):
+        if not quant:
+            pkv.append_kv(t["new_key"], t["new_value"], r.k_cache, r.v_cache, r.block_tables, positions,
+                          slot_mapping=slots)
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_attn_decode_multi(out, q, r.k_cache, r.v_cache, r.block_tables, r.lens, w.sm_scale,
+                                    r.k_scales, r.v_scales, partition_size=psize, workspace=ws, kv_dtype=kvdt,
+                                    stream_kv=stream_kv)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(warmup):
+        step(runs[i % len(runs)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(runs[i % len(runs)], evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    return {
+        "metric": "multi-token paged decode: query tokens/s + KV-read GB/s",
+        "value": round(S * T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype,
+        "data": "synthetic (seeded N(0,1) keys/values/queries, random block placement)",
+        "config": {"workload": DESCRIPTIONS.get(w.name, w.name) + f", {T} query tokens per sequence",
+                   "query_tokens": T, "kv_bytes_per_step": int(kv_bytes)},
+        "attn_us": round(attn_ms * 1e3, 2),
+        "attn_kv_gbps": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 2),
+    }
+
+
 def roofline(m):
     achieved = m["kv_bytes"] / (m["part_ms"] * 1e-3) / 1e9
     return {
@@ -334,7 +413,7 @@ def main():
     # the 128K split-K measurement runs first, in a child process of its own,
     # so that its multi-GiB allocations start from a fresh device heap
     long_ctx = None
-    if not args.no_long_context and not args.quest and args.workload != "ctx128k_b4":
+    if not args.no_long_context and not args.quest and args.query_tokens == 1 and args.workload != "ctx128k_b4":
         long_ctx = long_context_entry(min(args.steps, 50), min(args.warmup, 20))
 
     from workloads import get_workload
@@ -347,6 +426,9 @@ def main():
     w = get_workload(args.workload, streaming=args.streaming, **ov)
     if args.quest:
         print(json.dumps(measure_quest(w, args.steps, args.warmup, args.copies, args.quest)), flush=True)
+        return
+    if args.query_tokens > 1:
+        print(json.dumps(measure_multi(w, args.steps, args.warmup, args.copies, args.query_tokens)), flush=True)
         return
     m = measure(w, args.steps, args.warmup, args.copies)
     kv_bytes, ms = m["kv_bytes"], m["ms_per_step"]

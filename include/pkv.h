@@ -215,6 +215,28 @@ pkv_status pkv_paged_attn_merge(
     int sink_tokens, int window_tokens,
     const void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Several new tokens per sequence at once (checking speculative drafts, or
+ * a short chunk of prefill; the pages stop at one token per step, this is
+ * the plain causal reading): query and out are [num_seqs][num_query_tokens]
+ * [num_q_heads][head_dim]; seq_lens[s] = L counts the new tokens, whose
+ * keys and values are already in the cache at positions L - T .. L - 1 (T =
+ * num_query_tokens), and token t attends to positions 0 .. L - T + t.  One
+ * pass over the cache serves all T tokens: T * (num_q_heads / num_kv_heads)
+ * must be at most 16.  16-bit and code caches; no keep-mask.  The workspace
+ * is pkv_paged_attn_workspace_bytes(kv_dtype, num_seqs, num_q_heads * T,
+ * num_kv_heads, head_dim, max_blocks_per_seq * block_size, partition_size).
+ * Other arguments as pkv_paged_attn_decode; T = 1 is that decode.
+ */
+pkv_status pkv_paged_attn_decode_multi(
+    void* out, const void* query, int q_dtype,
+    const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* seq_lens, int num_seqs, int num_query_tokens,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+    float sm_scale, int partition_size, unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Query-aware page selection (Quest)                                        */
 /* ------------------------------------------------------------------------ */

@@ -15,7 +15,7 @@ __all__ = [
     "PkvError", "lib", "version", "last_error",
     "paged_attn_decode", "paged_attn_partition", "paged_attn_merge",
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
-    "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
+    "paged_attn_decode_multi", "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
     "slot_mapping", "reshape_and_cache", "append_kv", "append_kv_quantized", "copy_blocks", "quantize_kv",
     "validate_tables", "BlockPool", "PrefixCache", "h2o_retain", "DTYPES",
 ]
@@ -52,6 +52,8 @@ _SIGS = {
     "pkv_paged_attn_decode": (_ATTN, _i),
     "pkv_paged_attn_partition": (_ATTN, _i),
     "pkv_paged_attn_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
+    "pkv_paged_attn_decode_multi": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                                     ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_selected": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                         ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_quest_summarize": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p], _i),
@@ -215,6 +217,29 @@ def paged_attn_partition(out, query, k_cache, v_cache, block_tables, seq_lens, s
     return _attn_call(lib.pkv_paged_attn_partition, out, query, k_cache, v_cache, block_tables, seq_lens,
                       sm_scale, k_scales, v_scales, partition_size, sink_tokens, window_tokens, workspace,
                       kv_dtype, stream_kv)
+
+
+def paged_attn_decode_multi(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_scales=None,
+                            v_scales=None, partition_size=0, workspace=None, kv_dtype=None, stream_kv=False):
+    """Several new tokens per sequence (``pkv_paged_attn_decode_multi``):
+    query/out [S, T, Hq, D]; seq_lens count the T new tokens (already in
+    the cache); token t sees positions up to L - T + t."""
+    _contig(out, query, k_cache, v_cache, block_tables, seq_lens, k_scales, v_scales, workspace)
+    S, T, Hq, D = query.shape
+    NB, BS, Hkv, D2 = k_cache.shape
+    if D2 != D or tuple(out.shape) != tuple(query.shape) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between query, caches and out")
+    kvdt = _dtype(k_cache, kv_dtype)
+    mbs = block_tables.shape[1]
+    if workspace is None:
+        nbytes = paged_attn_workspace_bytes(kvdt, S, Hq * T, Hkv, D, mbs * BS, partition_size)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=query.device) if nbytes else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attn_decode_multi(
+        _ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), kvdt, _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), mbs, _ptr(seq_lens), S, T, Hq, Hkv, D, BS, NB, float(sm_scale), int(partition_size),
+        DECODE_STREAM_KV if stream_kv else 0, _ptr(workspace), ws_bytes, _stream(query)))
+    return out
 
 
 def paged_attn_decode_selected(out, query, k_cache, v_cache, selected, seq_lens, sm_scale, k_scales=None,

@@ -199,8 +199,16 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
     return fail(PKV_EINVAL, "%s: negative or zero size", who);
   if (a.num_q_heads % a.num_kv_heads)
     return fail(PKV_EINVAL, "%s: num_q_heads %% num_kv_heads != 0", who);
+  if (a.qtok < 1) a.qtok = 1;
   if (a.num_q_heads / a.num_kv_heads > 16)
     return fail(PKV_EUNSUPPORTED, "%s: query group size above 16 is not built", who);
+  if (a.qtok > 1) {
+    if ((long long)(a.num_q_heads / a.num_kv_heads) * a.qtok > 16)
+      return fail(PKV_EUNSUPPORTED, "%s: query tokens x group size above 16 is not built", who);
+    if (a.q_dtype == PKV_F32) return fail(PKV_EUNSUPPORTED, "%s: several query tokens need a 16-bit query", who);
+    if (a.sink_tokens || a.window_tokens || a.selected)
+      return fail(PKV_EUNSUPPORTED, "%s: several query tokens take neither a keep-mask nor a selection", who);
+  }
   if (a.head_dim != 64 && a.head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be 64 or 128", who);
   if (a.block_size != 16) return fail(PKV_EUNSUPPORTED, "%s: block_size must be 16", who);
   if (a.q_dtype != PKV_F32 && a.q_dtype != PKV_BF16 && a.q_dtype != PKV_F16)
@@ -242,8 +250,9 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
   a.ws = nullptr;
   a.plan = nullptr;
   if (a.may_split) {
-    const size_t total = workspace_total(a.kv_dtype, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim,
-                                         a.num_partitions, a.partition_size);
+    // records hold one row per (query token, query head) of a group
+    const size_t total = workspace_total(a.kv_dtype, a.num_seqs, a.num_q_heads * a.qtok, a.num_kv_heads,
+                                         a.head_dim, a.num_partitions, a.partition_size);
     if (!workspace || workspace_bytes < total)
       return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, total, workspace_bytes);
     if (((uintptr_t)workspace) & 127) return fail(PKV_EINVAL, "%s: workspace must be 128-byte aligned", who);
@@ -331,6 +340,25 @@ extern "C" pkv_status pkv_paged_attn_partition(PKV_ATTN_ARGS) {
                   block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                   block_size, num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, flags, workspace,
                   workspace_bytes, stream);
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_multi(
+    void* out, const void* query, int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_scales, const float* v_scales, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* seq_lens, int num_seqs, int num_query_tokens, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, float sm_scale, int partition_size, unsigned flags, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* who = "pkv_paged_attn_decode_multi";
+  if (num_query_tokens < 1) return fail(PKV_EINVAL, "%s: num_query_tokens must be positive", who);
+  AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, block_tables,
+                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         num_blocks, sm_scale, partition_size, 0, 0, flags, stream);
+  a.qtok = num_query_tokens;
+  pkv_status st = prepare_attn(a, who, workspace, workspace_bytes, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  st = hip_status(launch_paged_attn_partition(a), who);
+  if (st != PKV_OK) return st;
+  return hip_status(launch_paged_attn_merge(a), who);
 }
 
 extern "C" pkv_status pkv_paged_attn_decode_selected(

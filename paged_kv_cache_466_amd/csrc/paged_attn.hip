@@ -64,6 +64,7 @@ struct AttnParams {
   int table_bytes;      // bytes of block_tables (of `selected` for a selected decode)
   const int32_t* selected;   // selected decode: [S][Hkv][budget] (physical, logical block)
   int budget;                // selected decode: pages per (sequence, KV head)
+  int qtok;                  // query tokens per sequence (the last qtok positions, causal)
   float scale_log2;     // sm_scale * log2(e)
 };
 
@@ -345,7 +346,7 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
   // workgroup s of the first head group zeroes sequence s when it is empty
   // (16-bit outputs: zero bits are zero)
   if (blockIdx.y == 0 && w < S && clamp_len(p.seq_lens[w], p.mbs) == 0) {
-    const int n16 = p.num_q_heads * head_dim / 8;
+    const int n16 = p.num_q_heads * p.qtok * head_dim / 8;
     uint4* o = reinterpret_cast<uint4*>(p.out) + (size_t)w * n16;
     for (int i = lane; i < n16; i += 64) o[i] = make_uint4(0, 0, 0, 0);
     if (p.plan && lane == 0) reinterpret_cast<int4*>(p.plan)[w] = make_int4(0, 0, 0, 0);
@@ -442,8 +443,20 @@ void paged_attn_wave_kernel(AttnParams p) {
   const int waves = blockDim.x >> 6;
   const int kvh = blockIdx.y * waves + wave;
   const int G = p.num_q_heads / p.num_kv_heads;
-  const int g = lane & 15;       // query head in the group (column of S^T / out^T)
+  const int T = p.qtok;
+  // Columns of S^T / out^T: (query token t, head gh of the group), col =
+  // t * G + gh, NCOL = G * T <= 16.  col / G as (col * inv_g) >> 16, exact
+  // for col < 16 and every G <= 16.
+  const int NCOL = G * T;
+  const int inv_g = 0x10000 / G + 1;
+  const int g = lane & 15;       // this lane's column
   const int kg = lane >> 4;      // lane group: k-chunk of the operands, 4-row slab of outputs
+  const int lane_t = g < NCOL ? (g * inv_g) >> 16 : 0;   // its query token
+  // query / output row of column col of sequence s
+  auto qrow = [&](size_t s, int col) {
+    const int t = (col * inv_g) >> 16;
+    return (s * T + t) * p.num_q_heads + kvh * G + (col - t * G);
+  };
   uint8_t* vstage = lds + wave * C::VSTAGE;
   uint8_t* qlds = lds + waves * C::VSTAGE + wave * kQueryLds;
   int4* list = reinterpret_cast<int4*>(lds + waves * (C::VSTAGE + kQueryLds));
@@ -457,8 +470,8 @@ void paged_attn_wave_kernel(AttnParams p) {
   const int nseg = __builtin_amdgcn_readfirstlane(counts[1]);
 
   // queries of the first segments, copied to LDS at the start of the ring
-  const int q_chunks = G * D / 8;                      // 16-byte pieces of one group's query
-  const int q_segs = min(min(kQueryLds / (G * D * 2), kMaxQuerySegs), nseg);
+  const int q_chunks = NCOL * D / 8;                   // 16-byte pieces of one segment's query columns
+  const int q_segs = min(min(kQueryLds / (NCOL * D * 2), kMaxQuerySegs), nseg);
 
   // block-list entry k (the end entry for k >= nb), wave-uniform
   auto entry_at = [&](int k) {
@@ -549,15 +562,16 @@ void paged_attn_wave_kernel(AttnParams p) {
     if (ord < q_segs) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        v[c] = g < G ? *reinterpret_cast<const uint4*>(qlds + (size_t)ord * G * D * 2 + (g * D + qk_doff<KVT, D>(c, kg)) * 2)
-                     : make_uint4(0, 0, 0, 0);
+        v[c] = g < NCOL ? *reinterpret_cast<const uint4*>(qlds + (size_t)ord * NCOL * D * 2 +
+                                                          (g * D + qk_doff<KVT, D>(c, kg)) * 2)
+                        : make_uint4(0, 0, 0, 0);
     } else {
-      const size_t head0 = (size_t)(key >> 8) * p.num_q_heads + kvh * G;
+      const size_t row = qrow((size_t)(key >> 8), g < NCOL ? g : 0);
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        v[c] = g < G ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + (head0 + g) * D +
-                                                       qk_doff<KVT, D>(c, kg))
-                     : make_uint4(0, 0, 0, 0);
+        v[c] = g < NCOL ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.query) + row * D +
+                                                          qk_doff<KVT, D>(c, kg))
+                        : make_uint4(0, 0, 0, 0);
     }
     if constexpr (!kRescaleQ) {
 #pragma unroll
@@ -601,17 +615,17 @@ void paged_attn_wave_kernel(AttnParams p) {
   // every global store writes whole, contiguous 128-byte lines.
   auto finish_segment = [&](int key) {
     const bool whole = (key & 1) != 0;
-    const size_t head0 = (size_t)(key >> 8) * p.num_q_heads + kvh * G;
+    const size_t seq = (size_t)(key >> 8);
     float l = lsum + __shfl_xor(lsum, 16, 64);
     l += __shfl_xor(l, 32, 64);
     constexpr int RSTRIDE = D + 4;                      // floats per padded LDS row
     static_assert((8 * RSTRIDE + 32) * 4 <= C::VSTAGE, "result staging must fit the V staging area");
     float* rl = reinterpret_cast<float*>(vstage);
     const float scale_out = whole ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
-    // acc[G][D], then m[16], l[16]
+    // acc[NCOL][D], then m[16], l[16]
     float* rec = p.ws + ((size_t)(2 * blockIdx.x + ((key >> 1) & 1)) * p.num_kv_heads + kvh) * p.rec_floats;
-    for (int h0 = 0; h0 < G; h0 += 8) {
-      const int nh = min(8, G - h0);
+    for (int h0 = 0; h0 < NCOL; h0 += 8) {
+      const int nh = min(8, NCOL - h0);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -628,14 +642,16 @@ void paged_attn_wave_kernel(AttnParams p) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if (whole) {
-        // nh rows of D outputs, contiguous from head0 + h0: 8 elements per lane-store
+        // nh output rows of D elements (rows of one query token are
+        // contiguous): 8 elements per lane-store
         constexpr int CPR = D / 8;
         for (int c = lane; c < nh * CPR; c += 64) {
           const float* src = rl + (c / CPR) * RSTRIDE + (c % CPR) * 8;
           const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
           const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (head0 + h0) * D + c * 8) = make_uint4(
-              MO::pack2(lo[0], lo[1]), MO::pack2(lo[2], lo[3]), MO::pack2(hi[0], hi[1]), MO::pack2(hi[2], hi[3]));
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + qrow(seq, h0 + c / CPR) * D + (c % CPR) * 8) =
+              make_uint4(MO::pack2(lo[0], lo[1]), MO::pack2(lo[2], lo[3]), MO::pack2(hi[0], hi[1]),
+                         MO::pack2(hi[2], hi[3]));
         }
       } else if (p.ws) {
         constexpr int CPR = D / 4;
@@ -643,7 +659,7 @@ void paged_attn_wave_kernel(AttnParams p) {
           *reinterpret_cast<floatx4*>(rec + (size_t)h0 * D + 4 * c) =
               *reinterpret_cast<const floatx4*>(rl + (c / CPR) * RSTRIDE + (c % CPR) * 4);
         if (h0 == 0 && lane < 8)
-          *reinterpret_cast<floatx4*>(rec + (size_t)G * D + 4 * lane) =
+          *reinterpret_cast<floatx4*>(rec + (size_t)NCOL * D + 4 * lane) =
               *reinterpret_cast<const floatx4*>(rl + 8 * RSTRIDE + 4 * lane);
       }
     }
@@ -687,14 +703,19 @@ void paged_attn_wave_kernel(AttnParams p) {
       }
     }
     const float factor = qfactor * t.ks;
-    // lane holds tokens 4*kg + i of this block for head g
+    // lane holds tokens 4*kg + i of this block for column g
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * factor;
-    if (!full) {
+    // query token t sees positions up to L - T + t: blocks reaching past
+    // L - T are masked per column
+    if (!full | (t0 + kBS - 1 > L - T)) {
+      const int lim = L - T + lane_t;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!kept(t0 + 4 * kg + i, L, p.sink, p.window)) sc[i] = -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int pos = t0 + 4 * kg + i;
+        if (!kept(pos, L, p.sink, p.window) | (pos > lim)) sc[i] = -INFINITY;
+      }
     }
     const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     // ---- online softmax, rescaling only when a score passes m2 + slack -----
@@ -748,7 +769,7 @@ void paged_attn_wave_kernel(AttnParams p) {
       // them).  Branch-free, so that the waits stay counted: pieces past the
       // end load sequence 0's query and land in unused LDS.
       // c / q_chunks as (c * inv) >> 16: exact for c < 6 * 64 and every
-      // q_chunks = G * D / 8 built (checked exhaustively on the host)
+      // q_chunks = NCOL * D / 8 built (checked exhaustively on the host)
       const int inv = 0x10000 / q_chunks + 1;
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       u32x4 qv[kQRegs];
@@ -760,8 +781,9 @@ void paged_attn_wave_kernel(AttnParams p) {
         const int si = segs[i];                      // read unconditionally, used only when set
         const int s = used ? si : 0;
         const int piece = used ? c - i * q_chunks : 0;
+        // piece of column piece / (D / 8)
         qv[r] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.query) +
-                                                ((size_t)s * p.num_q_heads + kvh * G) * D + piece * 8);
+                                                qrow((size_t)s, piece / (D / 8)) * D + (piece % (D / 8)) * 8);
       }
 #pragma unroll
       for (int r = 0; r < kQRegs; ++r) *reinterpret_cast<u32x4*>(qlds + (r * 64 + lane) * 16) = qv[r];
@@ -916,17 +938,21 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 // ===========================================================================
 template <typename QT, int D>
 __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const float* ws, const int* plan,
-                                                               int rec_floats, int num_q_heads, int num_kv_heads) {
+                                                               int rec_floats, int num_q_heads, int num_kv_heads,
+                                                               int qtok) {
   constexpr int TPR = D / 4;               // threads per record row
   constexpr int ROWS = 256 / TPR;
   constexpr int U = 4;
   __shared__ float red[256];
   __shared__ floatx4 part_num[ROWS][TPR];
   __shared__ float part_den[ROWS];
-  const int h = blockIdx.x, s = blockIdx.y;
+  // x: (query token, query head); y: sequence
+  const int t = blockIdx.x / num_q_heads, h = blockIdx.x % num_q_heads, s = blockIdx.y;
   const int tid = threadIdx.x;
   const int G = num_q_heads / num_kv_heads;
-  const int kvh = h / G, g = h % G;
+  const int kvh = h / G;
+  const int g = t * G + h % G;             // the record column
+  const int NCOL = G * qtok;
   // (slot of the first record, first workgroup, last workgroup)
   const int4 e = reinterpret_cast<const int4*>(plan)[s];
   if (e.z <= e.y) return;
@@ -937,7 +963,7 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
     return ws + ((size_t)slot * num_kv_heads + kvh) * rec_floats;
   };
   float mx = -INFINITY;
-  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, rec_of(i)[G * D + g]);
+  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, rec_of(i)[NCOL * D + g]);
   red[tid] = mx;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -956,8 +982,8 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float* r = rec_of(i + u * ROWS);
-        mi[u] = r[G * D + g];
-        li[u] = r[G * D + 16 + g];
+        mi[u] = r[NCOL * D + g];
+        li[u] = r[NCOL * D + 16 + g];
         a[u] = *reinterpret_cast<const floatx4*>(r + g * D + 4 * c);
       }
 #pragma unroll
@@ -969,9 +995,9 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
     }
     for (; i < np; i += ROWS) {
       const float* r = rec_of(i);
-      const float w = exp2f(r[G * D + g] - M);
+      const float w = exp2f(r[NCOL * D + g] - M);
       num += w * *reinterpret_cast<const floatx4*>(r + g * D + 4 * c);
-      den += w * r[G * D + 16 + g];
+      den += w * r[NCOL * D + 16 + g];
     }
   }
   part_num[row][c] = num;
@@ -985,7 +1011,7 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
       n += part_num[r][tid];
       dn += part_den[r];
     }
-    const size_t o = ((size_t)s * num_q_heads + h) * D + 4 * tid;
+    const size_t o = (((size_t)s * qtok + t) * num_q_heads + h) * D + 4 * tid;
 #pragma unroll
     for (int k = 0; k < 4; ++k) store_out<QT>(out, o + k, dn > 0.f ? n[k] / dn : 0.f);
   }
@@ -1090,7 +1116,7 @@ static AttnParams make_params(const AttnArgs& a) {
   p.seq_lens = a.seq_lens;
   p.ws = a.ws;
   p.plan = a.plan;
-  p.rec_floats = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads, a.head_dim);
+  p.rec_floats = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads * (a.qtok > 0 ? a.qtok : 1), a.head_dim);
   p.num_seqs = a.num_seqs;
   // a selected decode takes lengths as they are (its pages come with the selection)
   p.mbs = a.selected ? (1 << 27) - 1 : a.max_blocks_per_seq;
@@ -1105,6 +1131,7 @@ static AttnParams make_params(const AttnArgs& a) {
   p.list_cap = a.list_cap;
   p.selected = a.selected;
   p.budget = a.budget;
+  p.qtok = a.qtok > 0 ? a.qtok : 1;
   p.table_bytes = a.selected ? (int)((long long)a.num_seqs * a.num_kv_heads * a.budget * 8)
                              : (int)((long long)a.num_seqs * a.max_blocks_per_seq * 4);
   p.scale_log2 = a.sm_scale * kLog2e;
@@ -1177,9 +1204,10 @@ int launch_paged_attn_partition(const AttnArgs& a) {
 
 int launch_paged_attn_merge(const AttnArgs& a) {
   if (a.num_seqs == 0) return hipSuccess;
-  const dim3 grid(a.num_q_heads, a.num_seqs);
+  const int T = a.qtok > 0 ? a.qtok : 1;
+  const dim3 grid(a.num_q_heads * T, a.num_seqs);
   hipStream_t st = (hipStream_t)a.stream;
-  const int rec = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads, a.head_dim);
+  const int rec = (int)partial_record_floats(a.num_q_heads / a.num_kv_heads * T, a.head_dim);
   if (a.q_dtype == PKV_F32) {
     if (a.num_partitions <= 1) return hipSuccess;
     const int max_len = a.max_blocks_per_seq * a.block_size;
@@ -1195,7 +1223,7 @@ int launch_paged_attn_merge(const AttnArgs& a) {
   }
   if (!a.may_split) return hipSuccess;
 #define PKV_MERGE(QT, D) \
-  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.ws, a.plan, rec, a.num_q_heads, a.num_kv_heads)
+  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.ws, a.plan, rec, a.num_q_heads, a.num_kv_heads, T)
   if (a.head_dim == 64) {
     if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 64);
     else PKV_MERGE(F16, 64);

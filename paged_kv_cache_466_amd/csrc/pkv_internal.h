@@ -63,6 +63,7 @@ struct AttnArgs {
   // in logical order; the units are these pages (partition_size 16)
   const int32_t* selected;
   int budget;
+  int qtok;    // query tokens per sequence (0 or 1: one)
   void* stream;
 };
 
