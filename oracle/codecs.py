@@ -112,15 +112,52 @@ def e4m3_encode(x):
 
 
 # ---------------------------------------------------------------------------
+# INT4: two signed 4-bit codes per byte
+# ---------------------------------------------------------------------------
+# "KV Cache Engineering", section 8 "Quantization": a 4-bit format keeps a
+# quarter of the BF16 payload; its codes are -7..7.  Storage here: element
+# 2i in the low nibble of byte i, element 2i + 1 in the high nibble, each a
+# two's-complement 4-bit number.
+
+
+def i4_pack(codes):
+    """Signed codes in [-8, 7], last dimension even -> packed uint8 bytes
+    (last dimension halved)."""
+    c = np.asarray(codes).astype(np.int64)
+    if c.shape[-1] % 2:
+        raise ValueError("i4_pack: last dimension must be even")
+    if (c < -8).any() or (c > 7).any():
+        raise ValueError("i4_pack: code outside [-8, 7]")
+    lo = c[..., 0::2] & 0xF
+    hi = c[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def i4_unpack(raw):
+    """Packed uint8 bytes -> signed codes (int8), last dimension doubled."""
+    b = np.asarray(raw).astype(np.uint8).astype(np.int64)
+    lo = b & 0xF
+    hi = b >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# ---------------------------------------------------------------------------
 # dispatch by storage dtype name
 # ---------------------------------------------------------------------------
 
 def decode(raw, dtype):
     """Raw stored data -> exact float32 values, for dtype in
-    {"f32", "bf16", "f16", "i8", "fp8e4m3"}.
+    {"f32", "bf16", "f16", "i8", "i4", "fp8e4m3"}.
 
     ``raw`` holds the storage words: float32 for "f32", uint16 bit patterns
-    for "bf16"/"f16", int8 codes for "i8", uint8 codes for "fp8e4m3".
+    for "bf16"/"f16", int8 codes for "i8", packed uint8 nibbles for "i4"
+    (the last dimension holds half the elements), uint8 codes for
+    "fp8e4m3".
     Integer and FP8 codes decode to the code's own value (the scale is
     applied separately, see ``quant.dequantize``).
     """
@@ -132,6 +169,8 @@ def decode(raw, dtype):
         return f16_bits_to_f32(raw)
     if dtype == "i8":
         return np.asarray(raw).astype(np.int8).astype(np.float32)
+    if dtype == "i4":
+        return i4_unpack(raw).astype(np.float32)
     if dtype == "fp8e4m3":
         return e4m3_to_f32(raw)
     raise ValueError(f"unknown dtype {dtype!r}")

@@ -4,8 +4,9 @@
 for a group of values, ``scale = max|x| / largest_code`` with
 ``largest_code = 2^(bits-1) - 1``; codes are ``x / scale`` rounded half to even
 and clipped to ``[-largest_code, largest_code]``; the restored value is
-``code * scale``.  The page's example uses bits = 4 (codes -7..7); the INT8
-cache uses bits = 8 (largest code 127).  "Chapter 18", section "KV-Cache
+``code * scale``.  The page's example uses bits = 4 (codes -7..7), which is
+also the INT4 cache's rule (two codes per byte, ``codecs.i4_pack``); the
+INT8 cache uses bits = 8 (largest code 127).  "Chapter 18", section "KV-Cache
 Quantization", lists INT8 storage at one byte per value.
 
 FP8-E4M3 storage follows the same rule with the largest finite E4M3 magnitude
@@ -35,6 +36,7 @@ import numpy as np
 from . import codecs
 
 INT8_QMAX = 127
+INT4_QMAX = 7
 FP8E4M3_QMAX = 448.0
 
 
@@ -87,13 +89,16 @@ def quantize_cache_blocks(cache_vals, code_dtype, block_ids=None):
     ``cache_vals``: [NB, BS, Hkv, D] float32 values.  For every block in
     ``block_ids`` (all blocks if None) and every KV head, the
     ``[BS, D]`` tile gets its own scale.  Returns (codes, scales) where
-    ``codes`` has the cache's shape (int8 for "i8", uint8 for "fp8e4m3") and
+    ``codes`` has the cache's shape (int8 for "i8", uint8 for "fp8e4m3",
+    packed uint8 with D / 2 bytes per row for "i4") and
     ``scales`` is [NB, Hkv] float32; blocks not listed keep code 0 / scale 0.
     """
     NB, BS, Hkv, D = cache_vals.shape
     ids = range(NB) if block_ids is None else [int(b) for b in block_ids]
     if code_dtype == "i8":
         codes = np.zeros(cache_vals.shape, dtype=np.int8)
+    elif code_dtype == "i4":
+        codes = np.zeros(cache_vals.shape[:-1] + (D // 2,), dtype=np.uint8)
     elif code_dtype == "fp8e4m3":
         codes = np.zeros(cache_vals.shape, dtype=np.uint8)
     else:
@@ -105,6 +110,9 @@ def quantize_cache_blocks(cache_vals, code_dtype, block_ids=None):
             if code_dtype == "i8":
                 c, sc = quantize_int(tile, 8)
                 codes[b, :, h, :] = c.astype(np.int8)
+            elif code_dtype == "i4":
+                c, sc = quantize_int(tile, 4)
+                codes[b, :, h, :] = codecs.i4_pack(c)
             else:
                 c, sc = quantize_fp8(tile)
                 codes[b, :, h, :] = c
@@ -122,6 +130,9 @@ def requantize_tail(tail_vals, rows, code_dtype):
     t = np.array(tail_vals, dtype=np.float32)
     t[rows:] = 0.0
     BS, Hkv, D = t.shape
+    if code_dtype == "i4":
+        codes, scales = quantize_cache_blocks(t[None], "i4")
+        return codes[0], scales[0]
     codes = np.zeros(t.shape, dtype=np.int8 if code_dtype == "i8" else np.uint8)
     scales = np.zeros(Hkv, dtype=np.float32)
     for h in range(Hkv):

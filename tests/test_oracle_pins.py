@@ -319,3 +319,32 @@ def test_page_example_grows_one_value_at_a_time():
         x[:n] = vals[:n]
         codes, sc = quant.quantize_int(x, g["bits"])
     assert codes.tolist() == g["codes"]
+
+
+# --------------------------------------------------------------------------
+# INT4 storage: the page's 4-bit rule, two codes per byte
+# --------------------------------------------------------------------------
+
+def test_i4_packing_round_trip_and_layout():
+    codes = np.array([[-7, -4, -1, 2, 4, 7, 0, -8]])
+    packed = codecs.i4_pack(codes)
+    # element 2i in the low nibble, 2i + 1 in the high nibble, two's complement
+    assert packed.tolist() == [[0xC9, 0x2F, 0x74, 0x80]]
+    assert codecs.i4_unpack(packed).tolist() == codes.tolist()
+    every = np.array([[a, b] for a in range(-8, 8) for b in range(-8, 8)])
+    assert (codecs.i4_unpack(codecs.i4_pack(every)) == every).all()
+
+
+def test_i4_cache_blocks_follow_the_page_example_rule():
+    """An INT4 block is the page's 4-bit quantiser over the [16, D] tile,
+    packed: decoding and rescaling gives back the rule's restored values."""
+    g = golden("quant4_example.json")
+    tile = np.zeros((1, 16, 1, 8), dtype=np.float32)
+    tile[0, 0, 0, :6] = g["values"]
+    codes, scales = quant.quantize_cache_blocks(tile, "i4")
+    assert codes.shape == (1, 16, 1, 4)
+    vals = codecs.decode(codes, "i4")
+    assert vals[0, 0, 0, :6].tolist() == g["codes"]
+    back = quant.dequantize(vals[0, 0, 0, :6], scales[0, 0]).astype(np.float64)
+    assert np.round(back, 3).tolist() == g["restored_3dp"]
+    assert (vals[0, 1:] == 0).all()
