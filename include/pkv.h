@@ -85,7 +85,10 @@ typedef enum pkv_dtype {
   PKV_BF16 = 1,    /* bfloat16 */
   PKV_F16 = 2,     /* IEEE binary16 */
   PKV_I8 = 3,      /* signed 8-bit integer code, value = code * scale */
-  PKV_FP8E4M3 = 4  /* OCP FP8 E4M3 ("fn": no inf, NaN = S.1111.111) code, value = code * scale */
+  PKV_FP8E4M3 = 4, /* OCP FP8 E4M3 ("fn": no inf, NaN = S.1111.111) code, value = code * scale */
+  PKV_I4 = 5       /* signed 4-bit integer code in -7..7, two per byte (element 2i in the low
+                      nibble, 2i + 1 in the high nibble, two's complement); a cache row holds
+                      head_dim / 2 bytes; value = code * scale */
 } pkv_dtype;
 
 /* Thread-local text of the last error on this thread ("" if none). */

@@ -29,10 +29,10 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 # pkv_dtype
-F32, BF16, F16, I8, FP8E4M3 = 0, 1, 2, 3, 4
+F32, BF16, F16, I8, FP8E4M3, I4 = 0, 1, 2, 3, 4, 5
 # decode flags
 DECODE_STREAM_KV = 1
-DTYPES = {"f32": F32, "bf16": BF16, "f16": F16, "i8": I8, "fp8e4m3": FP8E4M3}
+DTYPES = {"f32": F32, "bf16": BF16, "f16": F16, "i8": I8, "fp8e4m3": FP8E4M3, "i4": I4}
 _TORCH_TO_PKV = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8,
                  torch.float8_e4m3fn: FP8E4M3}
 _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP",
@@ -129,6 +129,11 @@ def _dtype(t, override=None):
     return _TORCH_TO_PKV[t.dtype]
 
 
+def _head_dim(cache, kvdt):
+    """head_dim of a cache tensor: an INT4 cache holds two elements per byte."""
+    return cache.shape[-1] * 2 if kvdt == I4 else cache.shape[-1]
+
+
 def _contig(*tensors):
     for t in tensors:
         if t is not None and not t.is_contiguous():
@@ -166,8 +171,9 @@ def _attn_call(fn, out, query, k_cache, v_cache, block_tables, seq_lens, sm_scal
                partition_size, sink_tokens, window_tokens, workspace, kv_dtype, stream_kv):
     _contig(out, query, k_cache, v_cache, block_tables, seq_lens, k_scales, v_scales, workspace)
     S, Hq, D = query.shape
-    NB, BS, Hkv, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(query.shape):
+    NB, BS, Hkv = k_cache.shape[:3]
+    if _head_dim(k_cache, _dtype(k_cache, kv_dtype)) != D or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or tuple(out.shape) != tuple(query.shape):
         raise ValueError("shape mismatch between query, caches and out")
     if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_tables and seq_lens must be int32")
@@ -200,7 +206,7 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens, sm_s
 
     query/out [S, Hq, D]; caches [NB, 16, Hkv, D]; block_tables [S, MBS] int32;
     seq_lens [S] int32.  A workspace is taken from torch when none is given.
-    ``kv_dtype`` ("i8" / "fp8e4m3") names the code type when the caches are
+    ``kv_dtype`` ("i8" / "fp8e4m3" / "i4") names the code type when the caches are
     uint8 tensors.  ``stream_kv`` sets PKV_DECODE_STREAM_KV (no block is
     shared between the batch's sequences).
     """
@@ -226,10 +232,11 @@ def paged_attn_decode_multi(out, query, k_cache, v_cache, block_tables, seq_lens
     the cache); token t sees positions up to L - T + t."""
     _contig(out, query, k_cache, v_cache, block_tables, seq_lens, k_scales, v_scales, workspace)
     S, T, Hq, D = query.shape
-    NB, BS, Hkv, D2 = k_cache.shape
-    if D2 != D or tuple(out.shape) != tuple(query.shape) or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("shape mismatch between query, caches and out")
+    NB, BS, Hkv = k_cache.shape[:3]
     kvdt = _dtype(k_cache, kv_dtype)
+    if _head_dim(k_cache, kvdt) != D or tuple(out.shape) != tuple(query.shape) \
+            or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between query, caches and out")
     mbs = block_tables.shape[1]
     if workspace is None:
         nbytes = paged_attn_workspace_bytes(kvdt, S, Hq * T, Hkv, D, mbs * BS, partition_size)
@@ -250,8 +257,9 @@ def paged_attn_decode_selected(out, query, k_cache, v_cache, selected, seq_lens,
     ``quest_select`` returns it."""
     _contig(out, query, k_cache, v_cache, selected, seq_lens, k_scales, v_scales, workspace)
     S, Hq, D = query.shape
-    NB, BS, Hkv, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(query.shape):
+    NB, BS, Hkv = k_cache.shape[:3]
+    if _head_dim(k_cache, _dtype(k_cache, kv_dtype)) != D or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or tuple(out.shape) != tuple(query.shape):
         raise ValueError("shape mismatch between query, caches and out")
     if selected.dtype != torch.int32 or selected.dim() != 4 or tuple(selected.shape[:2]) != (S, Hkv) \
             or selected.shape[3] != 2:
@@ -369,12 +377,15 @@ def append_kv_quantized(key, value, k_tail, v_tail, k_codes, v_codes, k_scales, 
     """Appends one token per sequence to a quantised cache
     (``pkv_append_kv_quantized``): key/value [S, Hkv, D] and the tails
     [S, 16, Hkv, D] in the source dtype; codes [NB, 16, Hkv, D] int8 /
-    uint8, scales [NB, Hkv] fp32; positions int32 [S] (< 0 skips)."""
+    uint8 ([NB, 16, Hkv, D / 2] uint8 for "i4"), scales [NB, Hkv] fp32;
+    positions int32 [S] (< 0 skips)."""
     _contig(key, value, k_tail, v_tail, k_codes, v_codes, k_scales, v_scales, block_tables, positions)
     S, Hkv, D = key.shape
     NB, BS = k_codes.shape[:2]
     if tuple(k_tail.shape) != (S, BS, Hkv, D) or k_tail.dtype != key.dtype or value.shape != key.shape:
         raise ValueError("tails must be [S, block_size, Hkv, D] of the key dtype")
+    if _head_dim(k_codes, DTYPES[code_dtype]) != D or k_codes.shape != v_codes.shape:
+        raise ValueError("codes must be [NB, block_size, Hkv, D] (D / 2 bytes for i4)")
     _check(lib.pkv_append_kv_quantized(_ptr(key), _ptr(value), _dtype(key), _ptr(k_tail), _ptr(v_tail),
                                        _ptr(k_codes), _ptr(v_codes), DTYPES[code_dtype], _ptr(k_scales),
                                        _ptr(v_scales), _ptr(block_tables), block_tables.shape[1], _ptr(positions),
@@ -384,17 +395,21 @@ def append_kv_quantized(key, value, k_tail, v_tail, k_codes, v_codes, k_scales, 
 def copy_blocks(k_cache, v_cache, src_dst, k_scales=None, v_scales=None, dtype=None):
     """Copy-on-write block copies (``pkv_copy_blocks``); src_dst int32 [n, 2]."""
     _contig(k_cache, v_cache, src_dst, k_scales, v_scales)
-    NB, BS, Hkv, D = k_cache.shape
+    NB, BS, Hkv = k_cache.shape[:3]
     dt = _dtype(k_cache, dtype) if k_cache.dtype != torch.uint8 or dtype else FP8E4M3
+    D = _head_dim(k_cache, dt)
     _check(lib.pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(src_dst),
                                src_dst.shape[0], dt, NB, BS, Hkv, D, _stream(k_cache)))
 
 
 def quantize_kv(src_cache, dst_codes, dst_scales, code_dtype, block_ids=None, n_blocks=None):
-    """Absmax block quantisation (``pkv_quantize_kv``).  code_dtype "i8" or
-    "fp8e4m3"; dst_codes has the cache's shape (int8 / uint8)."""
+    """Absmax block quantisation (``pkv_quantize_kv``).  code_dtype "i8",
+    "fp8e4m3" or "i4"; dst_codes has the cache's shape (int8 / uint8), with
+    D / 2 bytes per row for "i4" (element 2i in the low nibble of byte i)."""
     _contig(src_cache, dst_codes, dst_scales, block_ids)
     NB, BS, Hkv, D = src_cache.shape
+    if _head_dim(dst_codes, DTYPES[code_dtype]) != D or tuple(dst_codes.shape[:3]) != (NB, BS, Hkv):
+        raise ValueError("dst_codes must be [NB, block_size, Hkv, D] (D / 2 bytes for i4)")
     if n_blocks is None:
         n_blocks = block_ids.numel() if block_ids is not None else NB
     _check(lib.pkv_quantize_kv(_ptr(src_cache), _dtype(src_cache), _ptr(dst_codes), DTYPES[code_dtype],

@@ -217,9 +217,11 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
     const bool same = a.kv_dtype == a.q_dtype;
     const bool codes = is_code_storage(a.kv_dtype) && (a.q_dtype == PKV_BF16 || a.q_dtype == PKV_F16);
     if (!same && !codes)
-      return fail(PKV_EUNSUPPORTED, "%s: kv dtype must equal the query dtype, or be i8/fp8e4m3 with a 16-bit query",
+      return fail(PKV_EUNSUPPORTED, "%s: kv dtype must equal the query dtype, or be i8/i4/fp8e4m3 with a 16-bit query",
                   who);
     if (codes && (!a.k_scales || !a.v_scales)) return fail(PKV_EINVAL, "%s: quantised cache needs k/v scales", who);
+    if (a.kv_dtype == PKV_I4 && a.head_dim != 128)
+      return fail(PKV_EUNSUPPORTED, "%s: INT4 caches are built for head_dim 128", who);
     if (a.sink_tokens < 0 || a.window_tokens < 0) return fail(PKV_EINVAL, "%s: negative sink/window", who);
     if (a.flags & ~(unsigned)PKV_DECODE_STREAM_KV) return fail(PKV_EINVAL, "%s: unknown flags 0x%x", who, a.flags);
   }
@@ -517,8 +519,10 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_sca
   if (!k_cache || !v_cache || !src_dst) return fail(PKV_EINVAL, "pkv_copy_blocks: null pointer");
   if ((k_scales == nullptr) != (v_scales == nullptr))
     return fail(PKV_EINVAL, "pkv_copy_blocks: give both scale arrays or neither");
+  // INT4 rows: head_dim / 2 bytes
   return hip_status(launch_copy_blocks(k_cache, v_cache, k_scales, v_scales, src_dst, n, dtype_bytes(dtype),
-                                       num_blocks, block_size, num_kv_heads, head_dim, stream),
+                                       num_blocks, block_size, num_kv_heads,
+                                       dtype == PKV_I4 ? head_dim / 2 : head_dim, stream),
                     "pkv_copy_blocks");
 }
 
@@ -532,7 +536,7 @@ extern "C" pkv_status pkv_append_kv_quantized(const void* key, const void* value
   pkv_status st = check_cache_shape(who, block_size, num_kv_heads, head_dim);
   if (st != PKV_OK) return st;
   if (!is_float_storage(src_dtype)) return fail(PKV_EUNSUPPORTED, "%s: source must be f32/bf16/f16", who);
-  if (!is_code_storage(code_dtype)) return fail(PKV_EUNSUPPORTED, "%s: codes must be i8 or fp8e4m3", who);
+  if (!is_code_storage(code_dtype)) return fail(PKV_EUNSUPPORTED, "%s: codes must be i8, i4 or fp8e4m3", who);
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0) return fail(PKV_EINVAL, "%s: negative size", who);
   if (num_seqs == 0) return PKV_OK;
   if (num_seqs > 2147483647 / 1 || num_kv_heads > 65535) return fail(PKV_EUNSUPPORTED, "%s: shape too large", who);
@@ -551,7 +555,8 @@ extern "C" pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void
   pkv_status st = check_cache_shape("pkv_quantize_kv", block_size, num_kv_heads, head_dim);
   if (st != PKV_OK) return st;
   if (!is_float_storage(src_dtype)) return fail(PKV_EUNSUPPORTED, "pkv_quantize_kv: source must be f32/bf16/f16");
-  if (!is_code_storage(code_dtype)) return fail(PKV_EUNSUPPORTED, "pkv_quantize_kv: codes must be i8 or fp8e4m3");
+  if (!is_code_storage(code_dtype))
+    return fail(PKV_EUNSUPPORTED, "pkv_quantize_kv: codes must be i8, i4 or fp8e4m3");
   if (n_blocks < 0 || num_blocks < 0) return fail(PKV_EINVAL, "pkv_quantize_kv: negative size");
   if (!block_ids && n_blocks > num_blocks) return fail(PKV_EINVAL, "pkv_quantize_kv: n_blocks > num_blocks");
   if (n_blocks == 0) return PKV_OK;

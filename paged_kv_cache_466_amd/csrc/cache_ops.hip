@@ -167,13 +167,69 @@ int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_s
   return hipGetLastError();
 }
 
+// Code type of the quantisers: INT8, FP8-E4M3 or packed INT4.
+enum CodeKind { kCodeI8 = 0, kCodeFP8 = 1, kCodeI4 = 2 };
+
+template <int CODE> struct CodeTraits;
+template <> struct CodeTraits<kCodeI8> { static constexpr float qmax = 127.f; static constexpr int bits = 8; };
+template <> struct CodeTraits<kCodeFP8> { static constexpr float qmax = 448.f; static constexpr int bits = 8; };
+template <> struct CodeTraits<kCodeI4> { static constexpr float qmax = 7.f; static constexpr int bits = 4; };
+
+// Codes of N values x with scale sc ("KV Cache Engineering", section 8:
+// x / scale rounded half to even and clipped to the largest code; FP8
+// rounds to the E4M3 grid), stored at dst as N * bits / 8 bytes (INT4:
+// element 2i in the low nibble of byte i).
+template <int CODE, int N>
+__device__ __forceinline__ void encode_store(const float* x, float sc, uint8_t* dst) {
+  constexpr float qmax = CodeTraits<CODE>::qmax;
+  uint8_t codes[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (sc == 0.f) {
+      codes[i] = 0;
+    } else {
+      const float y = __fdiv_rn(x[i], sc);
+      if constexpr (CODE == kCodeFP8) {
+        codes[i] = (uint8_t)f32_to_e4m3(y);
+      } else {
+        float r = rintf(y);
+        r = fminf(fmaxf(r, -qmax), qmax);
+        codes[i] = (uint8_t)(int8_t)(int)r;
+      }
+    }
+  }
+  if constexpr (CODE == kCodeI4) {
+    constexpr int NB = N / 2;   // bytes
+    uint32_t w[NB / 4];
+#pragma unroll
+    for (int k = 0; k < NB / 4; ++k) {
+      w[k] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[k] |= (uint32_t)((codes[8 * k + 2 * j] & 0xF) | ((codes[8 * k + 2 * j + 1] & 0xF) << 4)) << (8 * j);
+    }
+    if constexpr (NB == 16) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < N / 16; ++c) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)codes[c * 16 + 4 * k] | ((uint32_t)codes[c * 16 + 4 * k + 1] << 8) |
+               ((uint32_t)codes[c * 16 + 4 * k + 2] << 16) | ((uint32_t)codes[c * 16 + 4 * k + 3] << 24);
+      reinterpret_cast<uint4*>(dst)[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // quantize_kv: one wave per (block, KV head) tile of [BS=16][D].
 // Lane l reads token row l/4, quarter l%4 of the head dimension.
 // "KV Cache Engineering", section 8: scale = absmax / largest code, codes
 // rounded half to even and clipped.
 // ---------------------------------------------------------------------------
-template <typename SRC, int D, bool FP8OUT>
+template <typename SRC, int D, int CODE>
 __global__ __launch_bounds__(64) void quantize_kv_kernel(
     const typename SRC::raw* __restrict__ src, void* __restrict__ dst, float* __restrict__ scales,
     const int32_t* __restrict__ block_ids, int num_blocks, int num_kv_heads) {
@@ -181,6 +237,7 @@ __global__ __launch_bounds__(64) void quantize_kv_kernel(
   constexpr int ELEMS = D / 4;                 // per lane
   constexpr int SRC_CHUNKS = ELEMS * SRC::bytes / 16;
   constexpr int EL16 = 16 / SRC::bytes;
+  constexpr int ROWB = D * CodeTraits<CODE>::bits / 8;   // code bytes per row
   const int b = block_ids ? block_ids[blockIdx.x] : (int)blockIdx.x;
   const int h = blockIdx.y;
   if (b < 0 || b >= num_blocks) return;
@@ -198,34 +255,8 @@ __global__ __launch_bounds__(64) void quantize_kv_kernel(
 #pragma unroll
   for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
   a = wave_max(a);
-  const float qmax = FP8OUT ? 448.0f : 127.0f;
-  const float sc = __fdiv_rn(a, qmax);
-  uint8_t codes[ELEMS];
-#pragma unroll
-  for (int i = 0; i < ELEMS; ++i) {
-    if (sc == 0.f) {
-      codes[i] = 0;
-    } else {
-      const float y = __fdiv_rn(x[i], sc);
-      if (FP8OUT) {
-        codes[i] = (uint8_t)f32_to_e4m3(y);
-      } else {
-        float r = rintf(y);
-        r = fminf(fmaxf(r, -127.f), 127.f);
-        codes[i] = (uint8_t)(int8_t)(int)r;
-      }
-    }
-  }
-  uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + row * D + q * ELEMS);
-#pragma unroll
-  for (int c = 0; c < ELEMS / 16; ++c) {
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = (uint32_t)codes[c * 16 + 4 * k] | ((uint32_t)codes[c * 16 + 4 * k + 1] << 8) |
-             ((uint32_t)codes[c * 16 + 4 * k + 2] << 16) | ((uint32_t)codes[c * 16 + 4 * k + 3] << 24);
-    o[c] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  const float sc = __fdiv_rn(a, CodeTraits<CODE>::qmax);
+  encode_store<CODE, ELEMS>(x, sc, reinterpret_cast<uint8_t*>(dst) + row * ROWB + q * (ROWB / 4));
   if (lane == 0) scales[(size_t)b * num_kv_heads + h] = sc;
 }
 
@@ -233,12 +264,16 @@ template <typename SRC, int D>
 static int launch_q(const void* src, void* dst, int code_dtype, float* scales, const int32_t* ids,
                     int n_blocks, int num_blocks, int num_kv_heads, hipStream_t st) {
   dim3 grid(n_blocks, num_kv_heads);
+  typedef typename SRC::raw R;
   if (code_dtype == PKV_FP8E4M3)
-    quantize_kv_kernel<SRC, D, true><<<grid, 64, 0, st>>>((const typename SRC::raw*)src, dst, scales, ids,
-                                                          num_blocks, num_kv_heads);
+    quantize_kv_kernel<SRC, D, kCodeFP8><<<grid, 64, 0, st>>>((const R*)src, dst, scales, ids, num_blocks,
+                                                              num_kv_heads);
+  else if (code_dtype == PKV_I4)
+    quantize_kv_kernel<SRC, D, kCodeI4><<<grid, 64, 0, st>>>((const R*)src, dst, scales, ids, num_blocks,
+                                                             num_kv_heads);
   else
-    quantize_kv_kernel<SRC, D, false><<<grid, 64, 0, st>>>((const typename SRC::raw*)src, dst, scales, ids,
-                                                           num_blocks, num_kv_heads);
+    quantize_kv_kernel<SRC, D, kCodeI8><<<grid, 64, 0, st>>>((const R*)src, dst, scales, ids, num_blocks,
+                                                             num_kv_heads);
   return hipGetLastError();
 }
 
@@ -269,7 +304,7 @@ int launch_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, in
 // layout (lane l: token row l/4, quarter l%4 of the head dimension) and the
 // same arithmetic, so a full block ends with exactly quantize_kv's codes.
 // ---------------------------------------------------------------------------
-template <typename SRC, int D, bool FP8OUT>
+template <typename SRC, int D, int CODE>
 __global__ __launch_bounds__(64) void append_quantized_kernel(
     const typename SRC::raw* __restrict__ key, const typename SRC::raw* __restrict__ value,
     typename SRC::raw* __restrict__ k_tail, typename SRC::raw* __restrict__ v_tail, uint8_t* __restrict__ k_codes,
@@ -280,6 +315,7 @@ __global__ __launch_bounds__(64) void append_quantized_kernel(
   constexpr int ELEMS = D / 4;                 // per lane
   constexpr int SRC_CHUNKS = ELEMS * SRC::bytes / 16;
   constexpr int EL16 = 16 / SRC::bytes;
+  constexpr int ROWB = D * CodeTraits<CODE>::bits / 8;   // code bytes per row
   const int s = blockIdx.x, h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
   const int pos = positions[s];
@@ -312,35 +348,9 @@ __global__ __launch_bounds__(64) void append_quantized_kernel(
 #pragma unroll
   for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
   a = wave_max(a);
-  const float qmax = FP8OUT ? 448.0f : 127.0f;
-  const float sc = __fdiv_rn(a, qmax);
-  uint8_t codes[ELEMS];
-#pragma unroll
-  for (int i = 0; i < ELEMS; ++i) {
-    if (sc == 0.f) {
-      codes[i] = 0;
-    } else {
-      const float y = __fdiv_rn(x[i], sc);
-      if (FP8OUT) {
-        codes[i] = (uint8_t)f32_to_e4m3(y);
-      } else {
-        float r = rintf(y);
-        r = fminf(fmaxf(r, -127.f), 127.f);
-        codes[i] = (uint8_t)(int8_t)(int)r;
-      }
-    }
-  }
+  const float sc = __fdiv_rn(a, CodeTraits<CODE>::qmax);
   uint8_t* dst = is_v ? v_codes : k_codes;
-  uint4* o = reinterpret_cast<uint4*>(dst + (((size_t)b * BS + t) * num_kv_heads + h) * D + q * ELEMS);
-#pragma unroll
-  for (int c = 0; c < ELEMS / 16; ++c) {
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = (uint32_t)codes[c * 16 + 4 * k] | ((uint32_t)codes[c * 16 + 4 * k + 1] << 8) |
-             ((uint32_t)codes[c * 16 + 4 * k + 2] << 16) | ((uint32_t)codes[c * 16 + 4 * k + 3] << 24);
-    o[c] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  encode_store<CODE, ELEMS>(x, sc, dst + (((size_t)b * BS + t) * num_kv_heads + h) * ROWB + q * (ROWB / 4));
   if (lane == 0) (is_v ? v_scales : k_scales)[(size_t)b * num_kv_heads + h] = sc;
 }
 
@@ -350,14 +360,14 @@ static int launch_aq(const void* key, const void* value, void* k_tail, void* v_t
                      const int32_t* positions, int num_seqs, int num_blocks, int num_kv_heads, hipStream_t st) {
   typedef typename SRC::raw R;
   const dim3 grid(num_seqs, num_kv_heads, 2);
-  if (code_dtype == PKV_FP8E4M3)
-    append_quantized_kernel<SRC, D, true><<<grid, 64, 0, st>>>(
-        (const R*)key, (const R*)value, (R*)k_tail, (R*)v_tail, (uint8_t*)k_codes, (uint8_t*)v_codes, k_scales,
-        v_scales, tables, mbs, positions, num_blocks, num_kv_heads);
-  else
-    append_quantized_kernel<SRC, D, false><<<grid, 64, 0, st>>>(
-        (const R*)key, (const R*)value, (R*)k_tail, (R*)v_tail, (uint8_t*)k_codes, (uint8_t*)v_codes, k_scales,
-        v_scales, tables, mbs, positions, num_blocks, num_kv_heads);
+#define PKV_AQK(CODE)                                                                                      \
+  append_quantized_kernel<SRC, D, CODE><<<grid, 64, 0, st>>>(                                              \
+      (const R*)key, (const R*)value, (R*)k_tail, (R*)v_tail, (uint8_t*)k_codes, (uint8_t*)v_codes, k_scales, \
+      v_scales, tables, mbs, positions, num_blocks, num_kv_heads)
+  if (code_dtype == PKV_FP8E4M3) PKV_AQK(kCodeFP8);
+  else if (code_dtype == PKV_I4) PKV_AQK(kCodeI4);
+  else PKV_AQK(kCodeI8);
+#undef PKV_AQK
   return hipGetLastError();
 }
 

@@ -160,6 +160,8 @@ template <typename QT, typename KVT>
 struct MmaType { typedef QT type; };
 template <typename QT>
 struct MmaType<QT, I8> { typedef F16 type; };
+template <typename QT>
+struct MmaType<QT, I4> { typedef F16 type; };
 
 // Two INT8 codes (bytes 2h, 2h+1 of w) -> two f16 values, exactly.  With
 // u = c + 128 (the code's bits with the top bit flipped), the f16 with bits
@@ -171,6 +173,24 @@ __device__ __forceinline__ uint32_t i8x2_f16(uint32_t u) {
   const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, H ? 0x04030402u : 0x04010400u);
   const h2 x = __builtin_bit_cast(h2, b) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
   return __builtin_bit_cast(uint32_t, x);
+}
+
+// Eight INT4 codes (the nibbles of w, element 2i in the low nibble of byte
+// i) -> eight f16 values, exactly: with u = code + 8, bytes 0x64, u are the
+// f16 1024 + u, and subtracting 1032 leaves the code.
+__device__ __forceinline__ uint4 i4x8_f16(uint32_t w) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t lo = u & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // elements 0..3, one per byte
+  const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // elements 4..7
+  auto pair = [](uint32_t x, uint32_t sel) {
+    const h2 v = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, sel)) -
+                 h2{(_Float16)1032.0f, (_Float16)1032.0f};
+    return __builtin_bit_cast(uint32_t, v);
+  };
+  return make_uint4(pair(a, 0x04010400u), pair(a, 0x04030402u), pair(b, 0x04010400u), pair(b, 0x04030402u));
 }
 
 // 8 codes -> 8 elements of the MFMA type, exactly (every INT8 value is an f16
@@ -189,11 +209,13 @@ __device__ __forceinline__ uint4 to16(uint32_t w0, uint32_t w1) {
 
 template <typename KVT, int D>
 struct WaveCfg {
-  static constexpr bool kCodes = KVT::bytes == 1;
+  static constexpr bool kCodes = KVT::bits < 16;
   static constexpr int NC = D / 32;                    // q.K MFMAs per block (k = 32)
   static constexpr int NN = D / 16;                    // P.V MFMAs per block (n = 16)
-  static constexpr int ROW_BYTES = D * KVT::bytes;     // one token row of one KV head
-  static constexpr int KCH = kCodes ? NC / 2 : NC;     // 16-byte K loads per lane per block
+  static constexpr int ROW_BYTES = D * KVT::bits / 8;  // one token row of one KV head
+  // 16-byte K loads per lane per block: codes take a quarter row per lane group
+  static constexpr int KCH = kCodes ? ROW_BYTES / 4 / 16 : NC;
+  static_assert(KCH >= 1, "a lane group's quarter row must fill a 16-byte load");
   static constexpr int LANES_PER_ROW = ROW_BYTES / 16;
   static constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
   static constexpr int VCH = kBS / ROWS_PER_PASS;      // 16-byte V loads per lane per block
@@ -507,7 +529,7 @@ void paged_attn_wave_kernel(AttnParams p) {
   };
   const int row_stride = p.num_kv_heads * C::ROW_BYTES;        // bytes between token rows
   const int krow = lane & 15;
-  const int kcol = kCodes ? (D / 4) * kg : 16 * kg;            // bytes
+  const int kcol = kCodes ? (C::ROW_BYTES / 4) * kg : 16 * kg;   // bytes
   const int k_off = krow * row_stride + kcol;
   int v_off[VCH], v_row[VCH];
 #pragma unroll
@@ -682,6 +704,13 @@ void paged_attn_wave_kernel(AttnParams p) {
       const int cchunk = lane % C::LANES_PER_ROW;
       if constexpr (!kCodes) {
         *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 16) = t.v[ps];
+      } else if constexpr (KVT::bits == 4) {
+        // 32 codes -> 64 bytes of f16
+        uint8_t* dst = vst + v_row[ps] * C::VROW + cchunk * 64;
+        *reinterpret_cast<uint4*>(dst) = i4x8_f16(t.v[ps].x);
+        *reinterpret_cast<uint4*>(dst + 16) = i4x8_f16(t.v[ps].y);
+        *reinterpret_cast<uint4*>(dst + 32) = i4x8_f16(t.v[ps].z);
+        *reinterpret_cast<uint4*>(dst + 48) = i4x8_f16(t.v[ps].w);
       } else {
         *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32) = to16<MT, KVT>(t.v[ps].x, t.v[ps].y);
         *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32 + 16) =
@@ -694,6 +723,15 @@ void paged_attn_wave_kernel(AttnParams p) {
     if constexpr (!kCodes) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::vec8, t.k[c]), qop[c], sacc);
+    } else if constexpr (KVT::bits == 4) {
+      // each 16-byte load holds 32 codes: four k-chunks of 8
+#pragma unroll
+      for (int c2 = 0; c2 < KCH; ++c2) {
+        const uint32_t w[4] = {t.k[c2].x, t.k[c2].y, t.k[c2].z, t.k[c2].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sacc = M::qk(__builtin_bit_cast(typename M::vec8, i4x8_f16(w[j])), qop[4 * c2 + j], sacc);
+      }
     } else {
 #pragma unroll
       for (int c2 = 0; c2 < KCH; ++c2) {
@@ -1171,6 +1209,14 @@ static int launch_wave_d(const AttnParams& p, int num_slots, int D, bool stream,
                  : launch_wave<QT, KVT, 128, false, false>(p, num_slots, st);
 }
 
+// INT4 caches: head_dim 128 only (a lane group's quarter row is one 16-byte load)
+template <typename QT>
+static int launch_wave_i4(const AttnParams& p, int num_slots, bool stream, hipStream_t st) {
+  if (p.selected) return launch_wave<QT, I4, 128, false, true>(p, num_slots, st);
+  if (stream) return launch_wave<QT, I4, 128, true, false>(p, num_slots, st);
+  return launch_wave<QT, I4, 128, false, false>(p, num_slots, st);
+}
+
 template <typename QT, typename KVT, int D>
 static int launch_simple(const AttnParams& p, dim3 grid, hipStream_t st) {
   paged_attn_simple_kernel<QT, KVT, D><<<grid, 256, 0, st>>>(p);
@@ -1192,12 +1238,14 @@ int launch_paged_attn_partition(const AttnArgs& a) {
     switch (a.kv_dtype) {
       case PKV_BF16: return launch_wave_d<BF16, BF16>(p, K, D, stream, st);
       case PKV_I8: return launch_wave_d<BF16, I8>(p, K, D, stream, st);
+      case PKV_I4: return launch_wave_i4<BF16>(p, K, stream, st);
       default: return launch_wave_d<BF16, FP8>(p, K, D, stream, st);
     }
   }
   switch (a.kv_dtype) {
     case PKV_F16: return launch_wave_d<F16, F16>(p, K, D, stream, st);
     case PKV_I8: return launch_wave_d<F16, I8>(p, K, D, stream, st);
+    case PKV_I4: return launch_wave_i4<F16>(p, K, stream, st);
     default: return launch_wave_d<F16, FP8>(p, K, D, stream, st);
   }
 }

@@ -17,11 +17,13 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 // Storage tags: each holds raw bits; `Elems16` elements fill 16 bytes.
-struct F32 { typedef float raw; static constexpr int bytes = 4; };
-struct BF16 { typedef uint16_t raw; static constexpr int bytes = 2; };
-struct F16 { typedef uint16_t raw; static constexpr int bytes = 2; };
-struct I8 { typedef int8_t raw; static constexpr int bytes = 1; };
-struct FP8 { typedef uint8_t raw; static constexpr int bytes = 1; };
+struct F32 { typedef float raw; static constexpr int bytes = 4; static constexpr int bits = 32; };
+struct BF16 { typedef uint16_t raw; static constexpr int bytes = 2; static constexpr int bits = 16; };
+struct F16 { typedef uint16_t raw; static constexpr int bytes = 2; static constexpr int bits = 16; };
+struct I8 { typedef int8_t raw; static constexpr int bytes = 1; static constexpr int bits = 8; };
+struct FP8 { typedef uint8_t raw; static constexpr int bytes = 1; static constexpr int bits = 8; };
+// two signed 4-bit codes per byte: element 2i in the low nibble
+struct I4 { typedef uint8_t raw; static constexpr int bytes = 1; static constexpr int bits = 4; };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {

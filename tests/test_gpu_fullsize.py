@@ -33,6 +33,7 @@ CASES = {
     "shared_prefix_b128": ("shared_prefix_b128", {}, [0, 1, 77], None),
     "quant_kv_32k_b16_i8": ("quant_kv_32k_b16", {}, [5], [0, 7]),
     "quant_kv_32k_b16_fp8": ("quant_kv_32k_b16", {"kv_dtype": "fp8e4m3"}, [11], [3]),
+    "quant_kv_32k_b16_i4": ("quant_kv_32k_b16", {"kv_dtype": "i4"}, [2], [1, 6]),
     "ctx128k_b4": ("ctx128k_b4", {}, [1, 3], None),
     "ctx128k_b4_streaming": ("ctx128k_b4", {"streaming": True}, [2], None),
 }
@@ -80,11 +81,15 @@ def quantised_tiles(vals, kv_dtype, heads):
     deq = np.zeros_like(vals)
     for h in heads:
         tiles = vals[:, h, :].reshape(nb, 16, D)
-        c_all = np.empty((nb, 16, D), dtype=np.int8 if kv_dtype == "i8" else np.uint8)
+        row_bytes = D // 2 if kv_dtype == "i4" else D
+        c_all = np.empty((nb, 16, row_bytes), dtype=np.int8 if kv_dtype == "i8" else np.uint8)
         for b in range(nb):
             if kv_dtype == "i8":
                 c, sc = quant.quantize_int(tiles[b], 8)
                 c_all[b] = c.astype(np.int8)
+            elif kv_dtype == "i4":
+                c, sc = quant.quantize_int(tiles[b], 4)
+                c_all[b] = codecs.i4_pack(c)
             else:
                 c, sc = quant.quantize_fp8(tiles[b])
                 c_all[b] = c
@@ -125,7 +130,7 @@ def test_full_size_sampled(case):
         # cache contents of sequence s, read through the GPU's own table
         nb = -(-L // 16)
         blocks = torch.as_tensor(bt[s, :nb].astype(np.int64), device="cuda")
-        if w.kv_dtype in ("i8", "fp8e4m3"):
+        if w.kv_dtype in ("i8", "fp8e4m3", "i4"):
             kv = codecs.decode(k_raw, w.src_dtype)
             vv = codecs.decode(v_raw, w.src_dtype)
             kc, ks, K = quantised_tiles(kv, w.kv_dtype, kv_heads)

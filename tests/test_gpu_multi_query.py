@@ -22,9 +22,10 @@ CASES = {
                                           kv_dtype="f16", src_dtype="f16")),
     "i8": ("quant_kv_32k_b16", dict(S=3, fixed_len=704)),
     "fp8": ("quant_kv_32k_b16", dict(S=2, fixed_len=512, kv_dtype="fp8e4m3")),
+    "i4": ("quant_kv_32k_b16", dict(S=2, fixed_len=576, kv_dtype="i4")),
     "d64_g8": ("llama3_8b_b64", dict(S=3, Hq=8, Hkv=1, D=64, len_lo=5, len_hi=300)),
 }
-TOKENS = {"llama_shape": [1, 2, 4], "g8_f16": [2], "i8": [4], "fp8": [3], "d64_g8": [2]}
+TOKENS = {"llama_shape": [1, 2, 4], "g8_f16": [2], "i8": [4], "fp8": [3], "i4": [2], "d64_g8": [2]}
 
 _runs = {}
 
@@ -46,13 +47,14 @@ def run_case(name):
 @pytest.mark.parametrize("psize", [0, 64])
 def test_multi_query_parity(name, T, psize):
     import paged_kv_cache_466_amd as pkv
+    from gpu_pipeline import uint8_kind
     w, t, g, o = run_case(name)
     print(f"[multi] case={name} T={T} psize={psize} lens={g.lens.tolist()}", flush=True)
     gen = torch.Generator(device="cuda").manual_seed(1000 + T)
     qdt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.q_dtype]
     q = torch.randn((w.S, T, w.Hq, w.D), generator=gen, device="cuda").to(qdt)
     out = torch.empty_like(q)
-    kvdt = w.kv_dtype if w.kv_dtype == "fp8e4m3" else None
+    kvdt = uint8_kind(w.kv_dtype)
     pkv.paged_attn_decode_multi(out, q, g.k_cache, g.v_cache, g.block_tables, g.lens, w.sm_scale, g.k_scales,
                                 g.v_scales, partition_size=psize, kv_dtype=kvdt)
     torch.cuda.synchronize()

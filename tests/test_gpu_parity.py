@@ -31,6 +31,9 @@ CASES = {
     "quant_i8_f16q": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16")),
     "quant_fp8_f16q": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16",
                                                  kv_dtype="fp8e4m3")),
+    "quant_i4_small": ("quant_kv_32k_b16", dict(S=3, fixed_len=1024, kv_dtype="i4")),
+    "quant_i4_f16q": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16",
+                                                kv_dtype="i4")),
     "ctx_small": ("ctx128k_b4", dict(S=2, fixed_len=5000)),
     "mqa_d64": ("llama3_8b_b64", dict(S=4, Hq=8, Hkv=1, D=64, len_lo=1, len_hi=700)),
     "mha_d64": ("llama3_8b_b64", dict(S=4, Hq=4, Hkv=4, D=64, len_lo=1, len_hi=300)),
@@ -205,7 +208,7 @@ def test_partition_and_merge_entry_points_compose(sink, window):
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("kv", ["i8", "fp8e4m3"])
+@pytest.mark.parametrize("kv", ["i8", "fp8e4m3", "i4"])
 @pytest.mark.parametrize("k", [20, -30])
 def test_code_cache_with_out_of_f16_range_query(kv, k):
     """bf16 queries scaled by 2^k with sm_scale scaled by 2^-k (same scores):
@@ -214,12 +217,12 @@ def test_code_cache_with_out_of_f16_range_query(kv, k):
     Results must match the oracle on the same dequantised values."""
     import paged_kv_cache_466_amd as pkv
     from oracle import attention
-    w, t, g, o = run_case("quant_i8_small" if kv == "i8" else "quant_fp8_small")
+    w, t, g, o = run_case({"i8": "quant_i8_small", "fp8e4m3": "quant_fp8_small", "i4": "quant_i4_small"}[kv])
     q = (t["query"].float() * 2.0 ** k).to(torch.bfloat16)
     sm = float(np.float32(w.sm_scale) * np.float32(2.0 ** -k))
     out = torch.empty_like(q)
     pkv.paged_attn_decode(out, q, g.k_cache, g.v_cache, g.block_tables, g.lens, sm, g.k_scales, g.v_scales,
-                          partition_size=64, kv_dtype=kv if kv == "fp8e4m3" else None)
+                          partition_size=64, kv_dtype=None if kv == "i8" else kv)
     got = out.float().cpu().numpy()
     ref = attention.paged_decode(to_raw(q, "bf16"), "bf16", o.k_cache, o.v_cache, w.kv_dtype, o.block_tables(),
                                  o.lens, w.BS, sm, o.k_scales, o.v_scales)
@@ -252,3 +255,25 @@ def test_fp8_decoder_matches_format_table(qdt):
     got = out.float().cpu().numpy().reshape(2, D)
     # every e4m3 value is exactly representable in f16 and in bf16
     assert (got == expect).all()
+
+
+@pytest.mark.parametrize("qdt", [torch.float16, torch.bfloat16])
+def test_int4_decoder_reads_every_code(qdt):
+    """Every INT4 code, in either nibble of a byte, decodes to its own value
+    (two's complement, element 2i in the low nibble of byte i): a one-token
+    sequence with V scale 1 returns V[0]."""
+    import paged_kv_cache_466_amd as pkv
+    from oracle import codecs
+    D, Hkv = 128, 1
+    vals = np.array([(i * 5) % 16 - 8 for i in range(D)], dtype=np.int32)    # all 16 codes, both nibbles
+    rows = np.stack([vals, vals[::-1].copy()])
+    packed = codecs.i4_pack(rows)                                    # [2, D / 2]
+    vc = torch.from_numpy(packed).view(2, 1, 1, D // 2).repeat(1, 16, 1, 1).contiguous().cuda()
+    kc = torch.zeros_like(vc)
+    q = torch.ones(2, 1, D, dtype=qdt, device="cuda")
+    bt = torch.tensor([[0], [1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([1, 1], dtype=torch.int32, device="cuda")
+    one = torch.ones(2, Hkv, device="cuda")
+    out = torch.empty_like(q)
+    pkv.paged_attn_decode(out, q, kc, vc, bt, lens, 0.1, one, one, kv_dtype="i4")
+    assert (out.float().cpu().numpy().reshape(2, D) == rows).all()

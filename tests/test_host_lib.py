@@ -181,6 +181,11 @@ def test_argument_errors_return_before_launch():
     st = L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 2, 32, 8, 128, 16, 10,
                                  0.1, 0, 0, 0, 2, None, 0, None)
     assert st == 1 and "flags" in pkv.last_error()
+    # INT4 caches: head_dim 128 only; no raw slot write into codes
+    st = L.pkv_paged_attn_decode(None, None, 1, None, None, 5, 1, 1, None, 4, None, 2, 32, 8, 64, 16, 10,
+                                 0.1, 0, 0, 0, 0, None, 0, None)
+    assert st == 2 and "INT4" in pkv.last_error()
+    assert L.pkv_reshape_and_cache(None, None, None, None, 5, None, 4, 10, 16, 8, 128, None) == 2
     # empty batches are no-ops
     assert L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 0, 32, 8, 128, 16, 10,
                                    0.1, 0, 0, 0, 0, None, 0, None) == 0
