@@ -242,6 +242,9 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
     if (a.num_seqs >= (1 << 23) || (long long)a.num_seqs * a.max_blocks_per_seq >= (1LL << 29) ||
         (long long)a.num_seqs * a.num_partitions >= (1LL << 30))
       return fail(PKV_EUNSUPPORTED, "%s: batch too large (num_seqs * max_blocks_per_seq >= 2^29)", who);
+    // block offsets are formed as num_blocks * num_kv_heads * 4 in 31 bits
+    if ((long long)a.num_blocks * a.num_kv_heads >= (1LL << 29))
+      return fail(PKV_EUNSUPPORTED, "%s: pool too large (num_blocks * num_kv_heads >= 2^29)", who);
     a.list_cap = decode_list_cap(a.num_kv_heads);
     if (a.partition_size / a.block_size > a.list_cap)
       return fail(PKV_EINVAL, "%s: partition_size above %d tokens", who, a.list_cap * a.block_size);

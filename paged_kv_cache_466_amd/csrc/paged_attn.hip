@@ -97,8 +97,8 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, POL));
 }
 constexpr int kPolicyStream = 2;   // non-temporal: streamed data does not evict reused data
-__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int voff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff = 0) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 constexpr int kOutOfRange = 0x40000000;    // buffer offset that is always out of range
 
@@ -354,7 +354,8 @@ __host__ __device__ constexpr int wave_group_lds(int vstage, int waves, int list
 
 // Writes the workgroup's block list into LDS (one wave calls it).  Entry k:
 // (byte offset of the block's table entry - of its selection entry for a
-// selected decode -, first token of the block, length of its sequence,
+// selected decode -, first token of the block with bit 31 set when some
+// token of the block is masked for some query, length of its sequence,
 // segment key); the key packs the sequence (bits 8+), the
 // segment's number in the workgroup (bits 2-7, saturating), whether its
 // record goes to slot 2w + 1 (bit 1) and whether it is the whole sequence
@@ -417,12 +418,18 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
           // the grid is sized so that every range fits; the bound only
           // keeps a wrong size from writing past the list
           const int cnt = min(sb.n_need, p.list_cap - nb);
+          const bool windowed = (p.sink | p.window) != 0;
           for (int j = lane; j < cnt; j += 64) {
             const int lb = j < sb.n_a ? sb.lb_begin + j : sb.b0 + (j - sb.n_a);
+            // masked: past L - T (the first query token's last position), or
+            // partly outside the keep-mask
+            const int t0 = lb * kBS;
+            const bool masked = (t0 + kBS - 1 > L - p.qtok) |
+                                (windowed & (t0 + kBS > p.sink) & (t0 < L - p.window));
             // SEL: offset of the selection entry (KV head 0); the block's
             // first token comes with the entry
             list[nb + j] = SEL ? make_int4((s * p.num_kv_heads * p.budget + lb) * 8, 0, L, key)
-                               : make_int4((s * p.mbs + lb) * 4, lb * kBS, L, key);
+                               : make_int4((s * p.mbs + lb) * 4, t0 | (masked ? (int)0x80000000u : 0), L, key);
           }
           if (lane == 0 && nseg < kMaxQuerySegs) segs[nseg] = s;
           if (i0 == 0 && p.plan && blockIdx.y == 0 && lane == 0) {
@@ -515,11 +522,13 @@ void paged_attn_wave_kernel(AttnParams p) {
       return make_int2((int)__builtin_amdgcn_raw_buffer_load_b32(tab, off, 0, 0), 0);
     }
   };
-  const bool windowed = p.sink != 0 || p.window != 0;
-  // every token of the block starting at t0 is kept
-  auto block_full = [&](int t0, int L) {
-    return (t0 + kBS <= L) & (!windowed | (t0 + kBS <= p.sink) | (t0 >= L - p.window));
+  // first token of an entry's block, and whether some token of it is
+  // masked for some query (a selected decode has one query token and no
+  // keep-mask)
+  auto block_start = [&](const int2& ent, const int4& e) {
+    return SEL ? (int)__builtin_amdgcn_readfirstlane(ent.y) * kBS : (e.y & 0x7fffffff);
   };
+  auto block_masked = [&](int t0, const int4& e) { return SEL ? t0 + kBS > e.z : e.y < 0; };
 
   struct Tile {
     uint4 k[KCH];
@@ -531,40 +540,59 @@ void paged_attn_wave_kernel(AttnParams p) {
   const int krow = lane & 15;
   const int kcol = kCodes ? (C::ROW_BYTES / 4) * kg : 16 * kg;   // bytes
   const int k_off = krow * row_stride + kcol;
+  // This head's rows of block 0.  Block b starts b * kBS * Hkv * ROW_BYTES
+  // bytes further on, which is (b * Hkv * 4) << kTileShift: the byte offset
+  // of its scale row, shifted.
+  const uint8_t* k_head = reinterpret_cast<const uint8_t*>(p.k_cache) + (size_t)kvh * C::ROW_BYTES;
+  const uint8_t* v_head = reinterpret_cast<const uint8_t*>(p.v_cache) + (size_t)kvh * C::ROW_BYTES;
+  constexpr int kTileShift = __builtin_ctz(kBS * C::ROW_BYTES / 4);
+  static_assert((kBS * C::ROW_BYTES / 4) == (1 << kTileShift), "tile bytes must be a power of two");
+  const uint32_t scale_row_bytes = (uint32_t)p.num_kv_heads * 4;
+  // the scales of this head in every block (num_blocks * Hkv * 4 < 2^31,
+  // checked on the host); an empty pool reads nothing
+  const int sbytes = kCodes && p.num_blocks > 0 ? p.num_blocks * (int)scale_row_bytes - kvh * 4 : 0;
+  const __amdgpu_buffer_rsrc_t ks_r = make_rsrc(p.k_scales + kvh, sbytes);
+  const __amdgpu_buffer_rsrc_t vs_r = make_rsrc(p.v_scales + kvh, sbytes);
   int v_off[VCH], v_row[VCH];
 #pragma unroll
   for (int ps = 0; ps < VCH; ++ps) {
     v_row[ps] = ps * C::ROWS_PER_PASS + lane / C::LANES_PER_ROW;
     v_off[ps] = v_row[ps] * row_stride + (lane % C::LANES_PER_ROW) * 16;
   }
-  const int tile_bytes = (kBS - 1) * row_stride + C::ROW_BYTES;
+  const int tile_bytes = p.num_blocks > 0 ? (kBS - 1) * row_stride + C::ROW_BYTES : 0;
 
   // e: list entry of the block, ent: its (physical, logical) block
   auto load_tile = [&](Tile& t, const int2& ent, const int4& e) {
     const bool valid = e.w != kEndKey;
-    int pb = __builtin_amdgcn_readfirstlane(ent.x);
-    pb = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the cache arrays
-    const size_t tile = ((size_t)pb * kBS * p.num_kv_heads + kvh) * C::ROW_BYTES;
+    uint32_t pb = __builtin_amdgcn_readfirstlane(ent.x);
+    pb = pb < (uint32_t)p.num_blocks ? pb : 0u;   // a bad table must not leave the cache arrays
+    const uint32_t so = pb * scale_row_bytes;    // < 2^31: checked on the host
+    const uint64_t tile = (uint64_t)so << kTileShift;
     const int nbytes = valid ? tile_bytes : 0;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const uint8_t*>(p.k_cache) + tile, nbytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const uint8_t*>(p.v_cache) + tile, nbytes);
-    const int t0 = SEL ? __builtin_amdgcn_readfirstlane(ent.y) * kBS : e.y;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_head + tile, nbytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_head + tile, nbytes);
+    const int t0 = block_start(ent, e);
     const int L = e.z;
     t.t0 = t0;
-    const bool full = block_full(t0, L);
-    const int ko = (full | kept(t0 + krow, L, p.sink, p.window)) ? k_off : kOutOfRange;
+    // K rows that are not kept load as they are: their scores are masked
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) t.k[c] = buf_load16<STREAM ? kPolicyStream : 0>(kr, ko + (kCodes ? 16 : 64) * c);
+    for (int c = 0; c < KCH; ++c)
+      t.k[c] = buf_load16<STREAM ? kPolicyStream : 0>(kr, k_off + (kCodes ? 16 : 64) * c);
+    // V rows that are not kept read as zeros (a zero weight times a NaN row
+    // would still poison the product)
+    int vo[VCH];
 #pragma unroll
-    for (int ps = 0; ps < VCH; ++ps) {
-      const int vo = (full | kept(t0 + v_row[ps], L, p.sink, p.window)) ? v_off[ps] : kOutOfRange;
-      t.v[ps] = buf_load16<STREAM ? kPolicyStream : 0>(vr, vo);
+    for (int ps = 0; ps < VCH; ++ps) vo[ps] = v_off[ps];
+    if (block_masked(t0, e)) {
+#pragma unroll
+      for (int ps = 0; ps < VCH; ++ps)
+        if (!kept(t0 + v_row[ps], L, p.sink, p.window)) vo[ps] = kOutOfRange;
     }
+#pragma unroll
+    for (int ps = 0; ps < VCH; ++ps) t.v[ps] = buf_load16<STREAM ? kPolicyStream : 0>(vr, vo[ps]);
     if constexpr (kCodes) {
-      // the scale row of this block: a 4-byte window at its own address
-      const size_t si = (size_t)pb * p.num_kv_heads + kvh;
-      t.ks = buf_load4(make_rsrc(p.k_scales + si, valid ? 4 : 0), 0);
-      t.vs = buf_load4(make_rsrc(p.v_scales + si, valid ? 4 : 0), 0);
+      t.ks = buf_load4(ks_r, 0, (int)so);
+      t.vs = buf_load4(vs_r, 0, (int)so);
     } else {
       t.ks = t.vs = 1.f;
     }
@@ -696,7 +724,6 @@ void paged_attn_wave_kernel(AttnParams p) {
       cur_key = e.w;
     }
     const int t0 = t.t0, L = e.z;
-    const bool full = block_full(t0, L);
 
     // ---- V rows -> LDS (masked rows arrive as zeros) -----------------------
 #pragma unroll
@@ -747,7 +774,7 @@ void paged_attn_wave_kernel(AttnParams p) {
     for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * factor;
     // query token t sees positions up to L - T + t: blocks reaching past
     // L - T are masked per column
-    if (!full | (t0 + kBS - 1 > L - T)) {
+    if (block_masked(t0, e)) {
       const int lim = L - T + lane_t;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
