@@ -23,14 +23,16 @@ Sources (cited by page title and section):
 
 Modules:
 
-* ``codecs``    - exact decoders of bf16 / fp16 / FP8-e4m3 storage, and the
-                  brute-force FP8-e4m3 round-to-nearest-even encoder.
+* ``codecs``    - exact decoders of bf16 / fp16 / FP8-e4m3 / FP8-e5m2 /
+                  packed INT4 storage, and the brute-force FP8
+                  round-to-nearest-even encoders.
 * ``paging``    - slot addressing, gather in logical order, the slot write
                   (reshape_and_cache) and whole-block copy (copy-on-write).
 * ``attention`` - textbook softmax attention in float64 over the gathered
                   sequence, GQA head mapping, StreamingLLM keep-mask, and the
                   split-K partial/merge formulation.
-* ``quant``     - the symmetric absmax quantiser (INT-n and FP8-e4m3 codes).
+* ``quant``     - the symmetric absmax quantiser (INT8, INT4, FP8-e4m3 and
+                  FP8-e5m2 codes) and the requantisation of a growing block.
 * ``pool``      - FIFO free-block pool with reference counts and
                   copy-on-write append.
 * ``sizes``     - the KV cache-size formula.
@@ -43,7 +45,7 @@ Modules:
 Every function here is pinned by tests in ``tests/test_oracle_*.py`` against
 values the pages print, closed forms, invariants, library routines
 (``torch.nn.functional.scaled_dot_product_attention`` on CPU, torch's
-``float8_e4m3fn`` cast) or brute force.  No function is "parity unpinned".
+``float8_e4m3fn`` and ``float8_e5m2`` casts) or brute force.  No function is "parity unpinned".
 """
 
 from . import attention, codecs, paging, pool, quant, quest, reuse, sizes  # noqa: F401

@@ -84,7 +84,7 @@ def decoded_cache_rows(cache, table_row, length, block_size, dtype, scales=None)
     cache holds quantised codes.  Returns [L, Hkv, D] float32."""
     raw = paging.gather_sequence(cache, table_row, length, block_size)
     vals = codecs.decode(raw, dtype)
-    if dtype in ("i8", "i4", "fp8e4m3"):
+    if dtype in quant.CODE_DTYPES:
         if scales is None:
             raise ValueError("quantised cache needs scales")
         L = int(length)

@@ -9,9 +9,11 @@ also the INT4 cache's rule (two codes per byte, ``codecs.i4_pack``); the
 INT8 cache uses bits = 8 (largest code 127).  "Chapter 18", section "KV-Cache
 Quantization", lists INT8 storage at one byte per value.
 
-FP8-E4M3 storage follows the same rule with the largest finite E4M3 magnitude
-(448) as the largest code and FP8 round-to-nearest-even in place of integer
-rounding.
+FP8 storage follows the same rule with the format's largest finite magnitude
+as the largest code (448 for E4M3, 57344 for E5M2) and FP8
+round-to-nearest-even in place of integer rounding.  (The pages' vLLM example
+names an ``fp8_e5m2`` cache without saying how it is scaled; this takes the
+same per-tile absmax scale as the other formats.)
 
 Group: one scale per (physical block, KV head) over the ``[block_size, d_k]``
 tile, separately for K and V.
@@ -38,6 +40,8 @@ from . import codecs
 INT8_QMAX = 127
 INT4_QMAX = 7
 FP8E4M3_QMAX = 448.0
+FP8E5M2_QMAX = 57344.0
+CODE_DTYPES = ("i8", "i4", "fp8e4m3", "fp8e5m2")
 
 
 def largest_code(bits):
@@ -67,14 +71,16 @@ def quantize_int(x, bits):
     return codes, sc
 
 
-def quantize_fp8(x):
-    """FP8-E4M3 codes and scale for one group (float32 arithmetic)."""
+def quantize_fp8(x, fmt="e4m3"):
+    """FP8 codes (``fmt`` "e4m3" or "e5m2") and scale for one group
+    (float32 arithmetic)."""
     x = np.asarray(x, dtype=np.float32)
-    sc = absmax_scale(x, FP8E4M3_QMAX)
+    qmax, encode = (FP8E4M3_QMAX, codecs.e4m3_encode) if fmt == "e4m3" else (FP8E5M2_QMAX, codecs.e5m2_encode)
+    sc = absmax_scale(x, qmax)
     if sc == 0:
         return np.zeros(x.shape, dtype=np.uint8), np.float32(0)
     y = (x / sc).astype(np.float32)
-    return codecs.e4m3_encode(y), sc
+    return encode(y), sc
 
 
 def dequantize(code_values, scale):
@@ -89,8 +95,8 @@ def quantize_cache_blocks(cache_vals, code_dtype, block_ids=None):
     ``cache_vals``: [NB, BS, Hkv, D] float32 values.  For every block in
     ``block_ids`` (all blocks if None) and every KV head, the
     ``[BS, D]`` tile gets its own scale.  Returns (codes, scales) where
-    ``codes`` has the cache's shape (int8 for "i8", uint8 for "fp8e4m3",
-    packed uint8 with D / 2 bytes per row for "i4") and
+    ``codes`` has the cache's shape (int8 for "i8", uint8 for "fp8e4m3" and
+    "fp8e5m2", packed uint8 with D / 2 bytes per row for "i4") and
     ``scales`` is [NB, Hkv] float32; blocks not listed keep code 0 / scale 0.
     """
     NB, BS, Hkv, D = cache_vals.shape
@@ -99,7 +105,7 @@ def quantize_cache_blocks(cache_vals, code_dtype, block_ids=None):
         codes = np.zeros(cache_vals.shape, dtype=np.int8)
     elif code_dtype == "i4":
         codes = np.zeros(cache_vals.shape[:-1] + (D // 2,), dtype=np.uint8)
-    elif code_dtype == "fp8e4m3":
+    elif code_dtype in ("fp8e4m3", "fp8e5m2"):
         codes = np.zeros(cache_vals.shape, dtype=np.uint8)
     else:
         raise ValueError(code_dtype)
@@ -114,7 +120,7 @@ def quantize_cache_blocks(cache_vals, code_dtype, block_ids=None):
                 c, sc = quantize_int(tile, 4)
                 codes[b, :, h, :] = codecs.i4_pack(c)
             else:
-                c, sc = quantize_fp8(tile)
+                c, sc = quantize_fp8(tile, code_dtype[3:])
                 codes[b, :, h, :] = c
             scales[b, h] = sc
     return codes, scales
@@ -125,24 +131,9 @@ def requantize_tail(tail_vals, rows, code_dtype):
     rows, the others taken as zeros.
 
     ``tail_vals``: [BS, Hkv, D] float32 source values (rows >= ``rows`` are
-    ignored).  Returns (codes [BS, Hkv, D] - int8 for "i8", uint8 for
-    "fp8e4m3" - and scales [Hkv] float32)."""
+    ignored).  Returns (codes of one block as ``quantize_cache_blocks``
+    stores them, and scales [Hkv] float32)."""
     t = np.array(tail_vals, dtype=np.float32)
     t[rows:] = 0.0
-    BS, Hkv, D = t.shape
-    if code_dtype == "i4":
-        codes, scales = quantize_cache_blocks(t[None], "i4")
-        return codes[0], scales[0]
-    codes = np.zeros(t.shape, dtype=np.int8 if code_dtype == "i8" else np.uint8)
-    scales = np.zeros(Hkv, dtype=np.float32)
-    for h in range(Hkv):
-        if code_dtype == "i8":
-            c, sc = quantize_int(t[:, h, :], 8)
-            codes[:, h, :] = c.astype(np.int8)
-        elif code_dtype == "fp8e4m3":
-            c, sc = quantize_fp8(t[:, h, :])
-            codes[:, h, :] = c
-        else:
-            raise ValueError(code_dtype)
-        scales[h] = sc
-    return codes, scales
+    codes, scales = quantize_cache_blocks(t[None], code_dtype)
+    return codes[0], scales[0]

@@ -228,6 +228,67 @@ def test_fp8_quantizer_properties():
         assert (np.abs(restored / sc - x / sc) <= ulp / 2 * (1 + 1e-6) + 1e-7).all()
 
 
+# --------------------------------------------------------------------------
+# FP8 E5M2 codec against torch's float8_e5m2 (a library routine)
+# --------------------------------------------------------------------------
+
+def test_e5m2_decode_matches_torch():
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).float().numpy()
+    ours = codecs.E5M2_TABLE.astype(np.float32)
+    nan = np.isnan(t)
+    assert (np.isnan(ours) == nan).all()
+    assert nan.sum() == 6                       # exponent 31 with a nonzero mantissa
+    assert (ours[~nan] == t[~nan]).all()        # infinities included
+    assert ours[0x7C] == np.inf and ours[0xFC] == -np.inf
+    assert codecs.E5M2_TABLE[0x7B] == 57344.0
+    assert codecs.E5M2_TABLE[0x01] == 2.0 ** -16
+    assert codecs.E5M2_TABLE[0x3C] == 1.0
+    # an E5M2 byte is the high byte of the binary16 number of the same value
+    f16 = (np.arange(256, dtype=np.uint16) << 8).view(np.float16).astype(np.float32)
+    assert (f16[~nan] == ours[~nan]).all()
+
+
+def test_e5m2_encode_matches_torch_in_range():
+    rng = np.random.default_rng(3)
+    mags = codecs.E5M2_TABLE[:0x7C]
+    mids = (mags[:-1] + mags[1:]) / 2           # exact ties
+    x = np.concatenate([
+        rng.uniform(-57344, 57344, 20000),
+        rng.standard_normal(20000) * 0.001,
+        mags, -mags, mids, -mids,
+        np.nextafter(mids, 0), np.nextafter(mids, 1e6),
+        [0.0, -0.0, 2.0 ** -17, -2.0 ** -17, 2.0 ** -18, 57344.0, -57344.0],
+    ]).astype(np.float32)
+    ours = codecs.e5m2_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert (ours == ref).all(), np.nonzero(ours != ref)[0][:10]
+
+
+def test_e5m2_roundtrip_and_saturation():
+    finite = [c for c in range(256) if np.isfinite(codecs.E5M2_TABLE[c])]
+    vals = codecs.E5M2_TABLE[finite].astype(np.float32)
+    assert codecs.e5m2_encode(vals).tolist() == finite
+    # past the largest finite value the quantiser saturates instead of
+    # rounding to infinity
+    assert codecs.e5m2_encode(np.array([61440.0, 1e30, -1e30], np.float32)).tolist() == [0x7B, 0x7B, 0xFB]
+    assert codecs.e5m2_encode(np.array([-1e-30], np.float32)).tolist() == [0x80]
+
+
+def test_e5m2_quantizer_properties():
+    rng = np.random.default_rng(4)
+    for trial in range(20):
+        x = (rng.standard_normal((16, 128)) * rng.uniform(0.01, 100)).astype(np.float32)
+        codes, sc = quant.quantize_fp8(x, "e5m2")
+        assert sc == np.float32(np.float32(np.abs(x).max()) / np.float32(57344))
+        i = np.unravel_index(np.abs(x).argmax(), x.shape)
+        assert codes[i] & 0x7F == 0x7B
+        restored = codecs.e5m2_to_f32(codes).astype(np.float64) * sc
+        # within half an e5m2 ulp of the scaled value's binade (2 mantissa bits)
+        y = np.abs(x.astype(np.float64) / sc)
+        ulp = np.where(y < 2.0 ** -14, 2.0 ** -16, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -14))) - 2))
+        assert (np.abs(restored / sc - x / sc) <= ulp / 2 * (1 + 1e-6) + 1e-7).all()
+
+
 def test_bf16_decode_matches_torch():
     x = torch.randn(10000).to(torch.bfloat16)
     bits = x.view(torch.int16).numpy().view(np.uint16)
@@ -288,7 +349,7 @@ def test_copy_on_write_only_when_shared():
 # appending to a quantised cache
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("code", ["i8", "fp8e4m3"])
+@pytest.mark.parametrize("code", ["i8", "fp8e4m3", "fp8e5m2", "i4"])
 def test_token_by_token_requantisation_ends_at_the_whole_block_codes(code):
     """A block filled one token at a time, quantised again from its tail after
     each token, ends with exactly the codes and scales of quantising the
