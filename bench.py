@@ -31,8 +31,8 @@ sys.path.insert(0, ROOT)
 sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBPS = 8000.0
-BYTES = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "fp8e4m3": 1, "i4": 0.5}
-CODES = ("i8", "fp8e4m3", "i4")
+BYTES = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "fp8e4m3": 1, "fp8e5m2": 1, "i4": 0.5}
+CODES = ("i8", "fp8e4m3", "fp8e5m2", "i4")
 
 DESCRIPTIONS = {
     "llama3_8b_b64": "Llama-3-8B-shaped single-layer paged decode, bf16, batch 64, 32q/8kv heads, d 128, "
@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_b64")
-    ap.add_argument("--kv-dtype", default=None, help="override: i8 / fp8e4m3 / i4 for the quantised workload")
+    ap.add_argument("--kv-dtype", default=None, help="override: i8 / fp8e4m3 / fp8e5m2 / i4 for the quantised workload")
     ap.add_argument("--streaming", action="store_true", help="4 sink + 4092 window keep-mask")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--copies", type=int, default=2,

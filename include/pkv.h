@@ -86,9 +86,10 @@ typedef enum pkv_dtype {
   PKV_F16 = 2,     /* IEEE binary16 */
   PKV_I8 = 3,      /* signed 8-bit integer code, value = code * scale */
   PKV_FP8E4M3 = 4, /* OCP FP8 E4M3 ("fn": no inf, NaN = S.1111.111) code, value = code * scale */
-  PKV_I4 = 5       /* signed 4-bit integer code in -7..7, two per byte (element 2i in the low
+  PKV_I4 = 5,      /* signed 4-bit integer code in -7..7, two per byte (element 2i in the low
                       nibble, 2i + 1 in the high nibble, two's complement); a cache row holds
                       head_dim / 2 bytes; value = code * scale */
+  PKV_FP8E5M2 = 6  /* OCP FP8 E5M2 (bias 15; inf/NaN in the top exponent) code, value = code * scale */
 } pkv_dtype;
 
 /* Thread-local text of the last error on this thread ("" if none). */
@@ -160,9 +161,11 @@ size_t pkv_paged_attn_workspace_bytes(int kv_dtype, int num_seqs, int num_q_head
  * q_dtype (nearest even).  A sequence with no kept position gets zeros.
  *
  * q_dtype:  PKV_F32, PKV_BF16 or PKV_F16; out has the same dtype.
- * kv_dtype: equal to q_dtype, or PKV_I8 / PKV_FP8E4M3 with a bf16 or f16
- *           query (dequantised in registers with k_scales / v_scales,
- *           [P2] s.8).  k_scales/v_scales are ignored (may be NULL) otherwise.
+ * kv_dtype: equal to q_dtype, or a code type (PKV_I8, PKV_FP8E4M3,
+ *           PKV_FP8E5M2, PKV_I4) with a bf16 or f16 query, dequantised in
+ *           registers with k_scales / v_scales ([P2] s.8); k_scales /
+ *           v_scales are ignored (may be NULL) otherwise.  PKV_I4 caches
+ *           are built for head_dim 128.
  * head_dim: 64 or 128.  block_size: 16.  num_q_heads % num_kv_heads == 0.
  * partition_size: 0 = library's choice, else a positive multiple of
  *           block_size, at most 128 * min(num_kv_heads, 8) blocks for 16-bit
@@ -370,14 +373,15 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float*
  * [P1] "KV-Cache Quantization"), one scale per (block, KV head) over its
  * [block_size, head_dim] tile:
  *   a = max |x|;  scale = fp32(a / qmax)  (IEEE division; qmax = 127 for
- *   PKV_I8, 448 for PKV_FP8E4M3);
- *   code = round_half_even(fp32(x / scale)) clipped to [-127, 127]   (I8)
- *   code = FP8-E4M3 round-to-nearest-even of fp32(x / scale), saturating at
- *          +-448, sign of zero kept                                     (FP8)
+ *   PKV_I8, 7 for PKV_I4, 448 for PKV_FP8E4M3, 57344 for PKV_FP8E5M2);
+ *   code = round_half_even(fp32(x / scale)) clipped to [-qmax, qmax]  (I8, I4)
+ *   code = FP8 round-to-nearest-even of fp32(x / scale), saturating at
+ *          +-qmax, sign of zero kept                                  (FP8)
  *   a == 0 gives scale 0 and all codes 0.
  * src_cache: [num_blocks][block_size][num_kv_heads][head_dim] of src_dtype
- * (PKV_F32, PKV_BF16, PKV_F16); dst_codes: same shape of code_dtype
- * (PKV_I8 or PKV_FP8E4M3); dst_scales: [num_blocks][num_kv_heads] fp32.
+ * (PKV_F32, PKV_BF16, PKV_F16); dst_codes: the same shape in code_dtype
+ * (PKV_I8, PKV_I4 - head_dim / 2 bytes per row -, PKV_FP8E4M3 or
+ * PKV_FP8E5M2); dst_scales: [num_blocks][num_kv_heads] fp32.
  * block_ids: device int32 [n_blocks] of blocks to quantise, or NULL for
  * blocks 0..n_blocks-1.  Call once for K and once for V.  Every slot of a
  * quantised block must hold data.  Bit-exact.

@@ -29,12 +29,12 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 # pkv_dtype
-F32, BF16, F16, I8, FP8E4M3, I4 = 0, 1, 2, 3, 4, 5
+F32, BF16, F16, I8, FP8E4M3, I4, FP8E5M2 = 0, 1, 2, 3, 4, 5, 6
 # decode flags
 DECODE_STREAM_KV = 1
-DTYPES = {"f32": F32, "bf16": BF16, "f16": F16, "i8": I8, "fp8e4m3": FP8E4M3, "i4": I4}
+DTYPES = {"f32": F32, "bf16": BF16, "f16": F16, "i8": I8, "fp8e4m3": FP8E4M3, "i4": I4, "fp8e5m2": FP8E5M2}
 _TORCH_TO_PKV = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8,
-                 torch.float8_e4m3fn: FP8E4M3}
+                 torch.float8_e4m3fn: FP8E4M3, torch.float8_e5m2: FP8E5M2}
 _STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP",
            5: "PKV_ENOMEM"}
 
@@ -206,7 +206,7 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens, sm_s
 
     query/out [S, Hq, D]; caches [NB, 16, Hkv, D]; block_tables [S, MBS] int32;
     seq_lens [S] int32.  A workspace is taken from torch when none is given.
-    ``kv_dtype`` ("i8" / "fp8e4m3" / "i4") names the code type when the caches are
+    ``kv_dtype`` ("i8" / "fp8e4m3" / "fp8e5m2" / "i4") names the code type when the caches are
     uint8 tensors.  ``stream_kv`` sets PKV_DECODE_STREAM_KV (no block is
     shared between the batch's sequences).
     """
@@ -404,7 +404,7 @@ def copy_blocks(k_cache, v_cache, src_dst, k_scales=None, v_scales=None, dtype=N
 
 def quantize_kv(src_cache, dst_codes, dst_scales, code_dtype, block_ids=None, n_blocks=None):
     """Absmax block quantisation (``pkv_quantize_kv``).  code_dtype "i8",
-    "fp8e4m3" or "i4"; dst_codes has the cache's shape (int8 / uint8), with
+    "fp8e4m3", "fp8e5m2" or "i4"; dst_codes has the cache's shape (int8 / uint8), with
     D / 2 bytes per row for "i4" (element 2i in the low nibble of byte i)."""
     _contig(src_cache, dst_codes, dst_scales, block_ids)
     NB, BS, Hkv, D = src_cache.shape

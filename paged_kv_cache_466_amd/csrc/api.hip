@@ -217,7 +217,7 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
     const bool same = a.kv_dtype == a.q_dtype;
     const bool codes = is_code_storage(a.kv_dtype) && (a.q_dtype == PKV_BF16 || a.q_dtype == PKV_F16);
     if (!same && !codes)
-      return fail(PKV_EUNSUPPORTED, "%s: kv dtype must equal the query dtype, or be i8/i4/fp8e4m3 with a 16-bit query",
+      return fail(PKV_EUNSUPPORTED, "%s: kv dtype must equal the query dtype, or be a code type with a 16-bit query",
                   who);
     if (codes && (!a.k_scales || !a.v_scales)) return fail(PKV_EINVAL, "%s: quantised cache needs k/v scales", who);
     if (a.kv_dtype == PKV_I4 && a.head_dim != 128)
@@ -539,7 +539,8 @@ extern "C" pkv_status pkv_append_kv_quantized(const void* key, const void* value
   pkv_status st = check_cache_shape(who, block_size, num_kv_heads, head_dim);
   if (st != PKV_OK) return st;
   if (!is_float_storage(src_dtype)) return fail(PKV_EUNSUPPORTED, "%s: source must be f32/bf16/f16", who);
-  if (!is_code_storage(code_dtype)) return fail(PKV_EUNSUPPORTED, "%s: codes must be i8, i4 or fp8e4m3", who);
+  if (!is_code_storage(code_dtype))
+    return fail(PKV_EUNSUPPORTED, "%s: codes must be i8, i4, fp8e4m3 or fp8e5m2", who);
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0) return fail(PKV_EINVAL, "%s: negative size", who);
   if (num_seqs == 0) return PKV_OK;
   if (num_seqs > 2147483647 / 1 || num_kv_heads > 65535) return fail(PKV_EUNSUPPORTED, "%s: shape too large", who);
@@ -559,7 +560,7 @@ extern "C" pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void
   if (st != PKV_OK) return st;
   if (!is_float_storage(src_dtype)) return fail(PKV_EUNSUPPORTED, "pkv_quantize_kv: source must be f32/bf16/f16");
   if (!is_code_storage(code_dtype))
-    return fail(PKV_EUNSUPPORTED, "pkv_quantize_kv: codes must be i8, i4 or fp8e4m3");
+    return fail(PKV_EUNSUPPORTED, "pkv_quantize_kv: codes must be i8, i4, fp8e4m3 or fp8e5m2");
   if (n_blocks < 0 || num_blocks < 0) return fail(PKV_EINVAL, "pkv_quantize_kv: negative size");
   if (!block_ids && n_blocks > num_blocks) return fail(PKV_EINVAL, "pkv_quantize_kv: n_blocks > num_blocks");
   if (n_blocks == 0) return PKV_OK;

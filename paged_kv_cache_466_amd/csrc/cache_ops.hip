@@ -168,11 +168,12 @@ int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_s
 }
 
 // Code type of the quantisers: INT8, FP8-E4M3 or packed INT4.
-enum CodeKind { kCodeI8 = 0, kCodeFP8 = 1, kCodeI4 = 2 };
+enum CodeKind { kCodeI8 = 0, kCodeFP8 = 1, kCodeI4 = 2, kCodeBF8 = 3 };
 
 template <int CODE> struct CodeTraits;
 template <> struct CodeTraits<kCodeI8> { static constexpr float qmax = 127.f; static constexpr int bits = 8; };
 template <> struct CodeTraits<kCodeFP8> { static constexpr float qmax = 448.f; static constexpr int bits = 8; };
+template <> struct CodeTraits<kCodeBF8> { static constexpr float qmax = 57344.f; static constexpr int bits = 8; };
 template <> struct CodeTraits<kCodeI4> { static constexpr float qmax = 7.f; static constexpr int bits = 4; };
 
 // Codes of N values x with scale sc ("KV Cache Engineering", section 8:
@@ -191,6 +192,8 @@ __device__ __forceinline__ void encode_store(const float* x, float sc, uint8_t* 
       const float y = __fdiv_rn(x[i], sc);
       if constexpr (CODE == kCodeFP8) {
         codes[i] = (uint8_t)f32_to_e4m3(y);
+      } else if constexpr (CODE == kCodeBF8) {
+        codes[i] = (uint8_t)f32_to_e5m2(y);
       } else {
         float r = rintf(y);
         r = fminf(fmaxf(r, -qmax), qmax);
@@ -267,6 +270,9 @@ static int launch_q(const void* src, void* dst, int code_dtype, float* scales, c
   typedef typename SRC::raw R;
   if (code_dtype == PKV_FP8E4M3)
     quantize_kv_kernel<SRC, D, kCodeFP8><<<grid, 64, 0, st>>>((const R*)src, dst, scales, ids, num_blocks,
+                                                              num_kv_heads);
+  else if (code_dtype == PKV_FP8E5M2)
+    quantize_kv_kernel<SRC, D, kCodeBF8><<<grid, 64, 0, st>>>((const R*)src, dst, scales, ids, num_blocks,
                                                               num_kv_heads);
   else if (code_dtype == PKV_I4)
     quantize_kv_kernel<SRC, D, kCodeI4><<<grid, 64, 0, st>>>((const R*)src, dst, scales, ids, num_blocks,
@@ -365,6 +371,7 @@ static int launch_aq(const void* key, const void* value, void* k_tail, void* v_t
       (const R*)key, (const R*)value, (R*)k_tail, (R*)v_tail, (uint8_t*)k_codes, (uint8_t*)v_codes, k_scales, \
       v_scales, tables, mbs, positions, num_blocks, num_kv_heads)
   if (code_dtype == PKV_FP8E4M3) PKV_AQK(kCodeFP8);
+  else if (code_dtype == PKV_FP8E5M2) PKV_AQK(kCodeBF8);
   else if (code_dtype == PKV_I4) PKV_AQK(kCodeI4);
   else PKV_AQK(kCodeI8);
 #undef PKV_AQK

@@ -125,6 +125,9 @@ template <> struct Mfma<BF16> {
   template <bool HI> __device__ static uint32_t fp8x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   }
+  template <bool HI> __device__ static uint32_t bf8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+  }
   __device__ static shortx4 tr_read(const void* lds) {
     bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
         (__attribute__((address_space(3))) bf16x4*)(lds));
@@ -147,6 +150,9 @@ template <> struct Mfma<F16> {
   __device__ static float sum2(uint32_t w) { return f16_to_f32(w & 0xFFFFu) + f16_to_f32(w >> 16); }
   template <bool HI> __device__ static uint32_t fp8x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+  template <bool HI> __device__ static uint32_t bf8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, HI));
   }
   __device__ static shortx4 tr_read(const void* lds) {
     fp16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4*)(lds));
@@ -194,13 +200,16 @@ __device__ __forceinline__ uint4 i4x8_f16(uint32_t w) {
 }
 
 // 8 codes -> 8 elements of the MFMA type, exactly (every INT8 value is an f16
-// value; every FP8-E4M3 value is a bf16 and an f16 value).
+// value; every finite FP8-E4M3 and FP8-E5M2 value is a bf16 and an f16 value).
 template <typename MT, typename KVT>
 __device__ __forceinline__ uint4 to16(uint32_t w0, uint32_t w1) {
   typedef Mfma<MT> M;
   if constexpr (std::is_same<KVT, I8>::value) {
     const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
     return make_uint4(i8x2_f16<0>(u0), i8x2_f16<1>(u0), i8x2_f16<0>(u1), i8x2_f16<1>(u1));
+  } else if constexpr (std::is_same<KVT, BF8>::value) {
+    return make_uint4(M::template bf8x2<false>(w0), M::template bf8x2<true>(w0), M::template bf8x2<false>(w1),
+                      M::template bf8x2<true>(w1));
   } else {
     return make_uint4(M::template fp8x2<false>(w0), M::template fp8x2<true>(w0), M::template fp8x2<false>(w1),
                       M::template fp8x2<true>(w1));
@@ -1266,6 +1275,7 @@ int launch_paged_attn_partition(const AttnArgs& a) {
       case PKV_BF16: return launch_wave_d<BF16, BF16>(p, K, D, stream, st);
       case PKV_I8: return launch_wave_d<BF16, I8>(p, K, D, stream, st);
       case PKV_I4: return launch_wave_i4<BF16>(p, K, stream, st);
+      case PKV_FP8E5M2: return launch_wave_d<BF16, BF8>(p, K, D, stream, st);
       default: return launch_wave_d<BF16, FP8>(p, K, D, stream, st);
     }
   }
@@ -1273,6 +1283,7 @@ int launch_paged_attn_partition(const AttnArgs& a) {
     case PKV_F16: return launch_wave_d<F16, F16>(p, K, D, stream, st);
     case PKV_I8: return launch_wave_d<F16, I8>(p, K, D, stream, st);
     case PKV_I4: return launch_wave_i4<F16>(p, K, stream, st);
+    case PKV_FP8E5M2: return launch_wave_d<F16, BF8>(p, K, D, stream, st);
     default: return launch_wave_d<F16, FP8>(p, K, D, stream, st);
   }
 }

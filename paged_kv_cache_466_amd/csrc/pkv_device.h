@@ -22,6 +22,8 @@ struct BF16 { typedef uint16_t raw; static constexpr int bytes = 2; static const
 struct F16 { typedef uint16_t raw; static constexpr int bytes = 2; static constexpr int bits = 16; };
 struct I8 { typedef int8_t raw; static constexpr int bytes = 1; static constexpr int bits = 8; };
 struct FP8 { typedef uint8_t raw; static constexpr int bytes = 1; static constexpr int bits = 8; };
+// OCP FP8 E5M2 codes
+struct BF8 { typedef uint8_t raw; static constexpr int bytes = 1; static constexpr int bits = 8; };
 // two signed 4-bit codes per byte: element 2i in the low nibble
 struct I4 { typedef uint8_t raw; static constexpr int bytes = 1; static constexpr int bits = 4; };
 
@@ -149,6 +151,31 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   } else {                               // subnormal: value = m * 2^-9
     const float y = __uint_as_float(a) * 512.0f;   // exact power-of-two scaling
     code = (uint32_t)rintf(y);                     // 0..8; 8 is the smallest normal
+  }
+  return code | sign;
+}
+
+// ---------------------------------------------------------------------------
+// FP8-E5M2 (OCP) encoder: round to nearest, ties to even, saturating at
+// +-57344 (no infinity is produced), sign of zero kept.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e5m2(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a > 0x47600000u) {                 // |x| > 57344: saturate
+    code = 0x7B;
+  } else if (a >= 0x38800000u) {         // |x| >= 2^-14: normal range
+    // keep exponent and top 2 mantissa bits, round the 21 dropped bits
+    uint32_t q = a >> 21;
+    const uint32_t rem = a & 0x1FFFFFu;
+    if (rem > 0x100000u || (rem == 0x100000u && (q & 1u))) q += 1;
+    code = q - (112u << 2);              // rebias exponent 127 -> 15
+    if (code > 0x7B) code = 0x7B;
+  } else {                               // subnormal: value = m * 2^-16
+    const float y = __uint_as_float(a) * 65536.0f;   // exact power-of-two scaling
+    code = (uint32_t)rintf(y);                       // 0..4; 4 is the smallest normal
   }
   return code | sign;
 }

@@ -21,13 +21,16 @@ inline int dtype_bytes(int dt) {
     case PKV_F16: return 2;
     case PKV_I8:
     case PKV_FP8E4M3:
+    case PKV_FP8E5M2:
     case PKV_I4: return 1;   // INT4: a byte holds two elements (see row_bytes)
     default: return 0;
   }
 }
 
 inline bool is_float_storage(int dt) { return dt == PKV_F32 || dt == PKV_BF16 || dt == PKV_F16; }
-inline bool is_code_storage(int dt) { return dt == PKV_I8 || dt == PKV_FP8E4M3 || dt == PKV_I4; }
+inline bool is_code_storage(int dt) {
+  return dt == PKV_I8 || dt == PKV_FP8E4M3 || dt == PKV_FP8E5M2 || dt == PKV_I4;
+}
 // Bytes of one cache row (one token, one KV head) of head_dim elements.
 inline int row_bytes(int dt, int head_dim) { return dt == PKV_I4 ? head_dim / 2 : head_dim * dtype_bytes(dt); }
 

@@ -15,9 +15,10 @@ import paged_kv_cache_466_amd as pkv
 from plan import build_tables
 
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
-            "i8": torch.int8, "fp8e4m3": torch.uint8, "i4": torch.uint8}
-POISON_BITS = {"f32": 0x7FC00000, "bf16": 0x7FC0, "f16": 0x7E00, "i8": -128, "fp8e4m3": 0x7F, "i4": 0x88}
-CODES = ("i8", "fp8e4m3", "i4")
+            "i8": torch.int8, "fp8e4m3": torch.uint8, "fp8e5m2": torch.uint8, "i4": torch.uint8}
+POISON_BITS = {"f32": 0x7FC00000, "bf16": 0x7FC0, "f16": 0x7E00, "i8": -128, "fp8e4m3": 0x7F, "fp8e5m2": 0x7F,
+               "i4": 0x88}
+CODES = ("i8", "fp8e4m3", "fp8e5m2", "i4")
 
 
 def cache_shape(w, dtype):
@@ -27,13 +28,13 @@ def cache_shape(w, dtype):
 
 def uint8_kind(dtype):
     """The kv_dtype argument for caches held in uint8 tensors."""
-    return dtype if dtype in ("fp8e4m3", "i4") else None
+    return dtype if dtype in ("fp8e4m3", "fp8e5m2", "i4") else None
 
 
 def poisoned(shape, dtype, device):
     """A tensor whose every element is the dtype's poison pattern (NaN for
-    floats, code -128 for INT8, 0x7F = NaN for FP8-E4M3, code -8 in both
-    nibbles for INT4)."""
+    floats, code -128 for INT8, 0x7F = NaN for both FP8 formats, code -8 in
+    both nibbles for INT4)."""
     if dtype == "f32":
         return torch.full(shape, float("nan"), dtype=torch.float32, device=device)
     if dtype in ("bf16", "f16"):

@@ -18,9 +18,9 @@ from oracle import attention, paging, quant
 from plan import build_tables
 
 POISON = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "f16": np.uint16(0x7E00),
-          "i8": np.int8(-128), "fp8e4m3": np.uint8(0x7F), "i4": np.uint8(0x88)}
+          "i8": np.int8(-128), "fp8e4m3": np.uint8(0x7F), "fp8e5m2": np.uint8(0x7F), "i4": np.uint8(0x88)}
 RAW_NP = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "i8": np.int8, "fp8e4m3": np.uint8,
-          "i4": np.uint8}
+          "fp8e5m2": np.uint8, "i4": np.uint8}
 
 
 def to_raw(t, dtype):
@@ -32,7 +32,7 @@ def to_raw(t, dtype):
         return t.numpy().astype(np.float32)
     if dtype == "i8":
         return t.numpy().astype(np.int8)
-    if dtype in ("fp8e4m3", "i4"):
+    if dtype in ("fp8e4m3", "fp8e5m2", "i4"):
         return t.view(torch.uint8).numpy()
     raise ValueError(dtype)
 
@@ -63,7 +63,7 @@ class OracleRun:
         paging.reshape_and_cache(self.v_cache, to_raw(tensors["value"], src), self.prompt_slots, w.BS)
         self.k_scales = self.v_scales = None
         self.lens = w.seq_lens.astype(np.int64).copy()
-        if w.kv_dtype in ("i8", "fp8e4m3", "i4"):
+        if w.kv_dtype in quant.CODE_DTYPES:
             used = sorted({b for t in self.tables for b in t})
             kv = oracle.codecs.decode(self.k_cache, src)
             vv = oracle.codecs.decode(self.v_cache, src)

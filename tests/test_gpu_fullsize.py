@@ -34,6 +34,7 @@ CASES = {
     "quant_kv_32k_b16_i8": ("quant_kv_32k_b16", {}, [5], [0, 7]),
     "quant_kv_32k_b16_fp8": ("quant_kv_32k_b16", {"kv_dtype": "fp8e4m3"}, [11], [3]),
     "quant_kv_32k_b16_i4": ("quant_kv_32k_b16", {"kv_dtype": "i4"}, [2], [1, 6]),
+    "quant_kv_32k_b16_e5m2": ("quant_kv_32k_b16", {"kv_dtype": "fp8e5m2"}, [9], [4]),
     "ctx128k_b4": ("ctx128k_b4", {}, [1, 3], None),
     "ctx128k_b4_streaming": ("ctx128k_b4", {"streaming": True}, [2], None),
 }
@@ -91,7 +92,7 @@ def quantised_tiles(vals, kv_dtype, heads):
                 c, sc = quant.quantize_int(tiles[b], 4)
                 c_all[b] = codecs.i4_pack(c)
             else:
-                c, sc = quant.quantize_fp8(tiles[b])
+                c, sc = quant.quantize_fp8(tiles[b], kv_dtype[3:])
                 c_all[b] = c
             scales[b, h] = sc
         codes[h] = c_all
@@ -130,7 +131,7 @@ def test_full_size_sampled(case):
         # cache contents of sequence s, read through the GPU's own table
         nb = -(-L // 16)
         blocks = torch.as_tensor(bt[s, :nb].astype(np.int64), device="cuda")
-        if w.kv_dtype in ("i8", "fp8e4m3", "i4"):
+        if w.kv_dtype in quant.CODE_DTYPES:
             kv = codecs.decode(k_raw, w.src_dtype)
             vv = codecs.decode(v_raw, w.src_dtype)
             kc, ks, K = quantised_tiles(kv, w.kv_dtype, kv_heads)

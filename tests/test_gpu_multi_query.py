@@ -23,9 +23,10 @@ CASES = {
     "i8": ("quant_kv_32k_b16", dict(S=3, fixed_len=704)),
     "fp8": ("quant_kv_32k_b16", dict(S=2, fixed_len=512, kv_dtype="fp8e4m3")),
     "i4": ("quant_kv_32k_b16", dict(S=2, fixed_len=576, kv_dtype="i4")),
+    "e5m2": ("quant_kv_32k_b16", dict(S=2, fixed_len=512, kv_dtype="fp8e5m2", q_dtype="f16", src_dtype="f16")),
     "d64_g8": ("llama3_8b_b64", dict(S=3, Hq=8, Hkv=1, D=64, len_lo=5, len_hi=300)),
 }
-TOKENS = {"llama_shape": [1, 2, 4], "g8_f16": [2], "i8": [4], "fp8": [3], "i4": [2], "d64_g8": [2]}
+TOKENS = {"llama_shape": [1, 2, 4], "g8_f16": [2], "i8": [4], "fp8": [3], "i4": [2], "e5m2": [3], "d64_g8": [2]}
 
 _runs = {}
 

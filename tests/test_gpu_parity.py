@@ -32,6 +32,9 @@ CASES = {
     "quant_fp8_f16q": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16",
                                                  kv_dtype="fp8e4m3")),
     "quant_i4_small": ("quant_kv_32k_b16", dict(S=3, fixed_len=1024, kv_dtype="i4")),
+    "quant_e5m2_small": ("quant_kv_32k_b16", dict(S=3, fixed_len=1024, kv_dtype="fp8e5m2")),
+    "quant_e5m2_f16q_d64": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16",
+                                                      D=64, Hq=8, Hkv=2, kv_dtype="fp8e5m2")),
     "quant_i4_f16q": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16",
                                                 kv_dtype="i4")),
     "ctx_small": ("ctx128k_b4", dict(S=2, fixed_len=5000)),
@@ -208,7 +211,7 @@ def test_partition_and_merge_entry_points_compose(sink, window):
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("kv", ["i8", "fp8e4m3", "i4"])
+@pytest.mark.parametrize("kv", ["i8", "fp8e4m3", "fp8e5m2", "i4"])
 @pytest.mark.parametrize("k", [20, -30])
 def test_code_cache_with_out_of_f16_range_query(kv, k):
     """bf16 queries scaled by 2^k with sm_scale scaled by 2^-k (same scores):
@@ -217,7 +220,8 @@ def test_code_cache_with_out_of_f16_range_query(kv, k):
     Results must match the oracle on the same dequantised values."""
     import paged_kv_cache_466_amd as pkv
     from oracle import attention
-    w, t, g, o = run_case({"i8": "quant_i8_small", "fp8e4m3": "quant_fp8_small", "i4": "quant_i4_small"}[kv])
+    w, t, g, o = run_case({"i8": "quant_i8_small", "fp8e4m3": "quant_fp8_small", "fp8e5m2": "quant_e5m2_small",
+                           "i4": "quant_i4_small"}[kv])
     q = (t["query"].float() * 2.0 ** k).to(torch.bfloat16)
     sm = float(np.float32(w.sm_scale) * np.float32(2.0 ** -k))
     out = torch.empty_like(q)
@@ -277,3 +281,28 @@ def test_int4_decoder_reads_every_code(qdt):
     out = torch.empty_like(q)
     pkv.paged_attn_decode(out, q, kc, vc, bt, lens, 0.1, one, one, kv_dtype="i4")
     assert (out.float().cpu().numpy().reshape(2, D) == rows).all()
+
+
+@pytest.mark.parametrize("qdt", [torch.float16, torch.bfloat16])
+def test_e5m2_decoder_matches_format_table(qdt):
+    """Every finite FP8-E5M2 code read by the attention kernel decodes to the
+    value the oracle's format table gives: a one-token sequence returns V[0]."""
+    import paged_kv_cache_466_amd as pkv
+    from oracle import codecs
+    D, Hkv = 128, 1
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    table = codecs.E5M2_TABLE
+    finite = torch.from_numpy(np.isfinite(table))
+    codes[~finite] = 0                  # the quantiser never stores inf or NaN
+    vc = codes.view(2, 1, 1, D).repeat(1, 16, 1, 1).contiguous().cuda()
+    kc = torch.zeros_like(vc)
+    q = torch.ones(2, 1, D, dtype=qdt, device="cuda")
+    bt = torch.tensor([[0], [1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([1, 1], dtype=torch.int32, device="cuda")
+    one = torch.ones(2, Hkv, device="cuda")
+    out = torch.empty_like(q)
+    pkv.paged_attn_decode(out, q, kc, vc, bt, lens, 0.1, one, one, kv_dtype="fp8e5m2")
+    expect = table[codes.numpy()].reshape(2, D)
+    got = out.float().cpu().numpy().reshape(2, D)
+    # every finite e5m2 value is exactly representable in f16 and in bf16
+    assert (got == expect).all()

@@ -1,4 +1,4 @@
-"""GPU parity of appending to an INT8 / FP8 / INT4 cache one token at a time
+"""GPU parity of appending to an INT8 / FP8 (E4M3, E5M2) / INT4 cache one token at a time
 (``pkv_append_kv_quantized``) against the oracle's ``requantize_tail``:
 codes and scales of every written block bit-exact after each checked step,
 and decode attention over the growing sequences within 2e-2 of the oracle
@@ -31,7 +31,8 @@ def src_values(rng, shape, dtype, outliers=False):
 
 @pytest.mark.parametrize("code,src,D,Hkv", [("i8", "bf16", 128, 4), ("fp8e4m3", "bf16", 128, 2),
                                             ("i8", "f16", 64, 2), ("fp8e4m3", "f16", 64, 1),
-                                            ("i4", "bf16", 128, 4), ("i4", "f16", 128, 1)])
+                                            ("i4", "bf16", 128, 4), ("i4", "f16", 128, 1),
+                                            ("fp8e5m2", "bf16", 128, 2), ("fp8e5m2", "f16", 64, 2)])
 def test_append_token_by_token(code, src, D, Hkv):
     import paged_kv_cache_466_amd as pkv
     rng = np.random.default_rng(31)
@@ -43,7 +44,7 @@ def test_append_token_by_token(code, src, D, Hkv):
     tables = order[: S * mbs].reshape(S, mbs)
     bt = torch.from_numpy(tables.copy()).cuda()
     cdt = torch.int8 if code == "i8" else torch.uint8
-    poison = {"i8": -128, "fp8e4m3": 0x7F, "i4": 0x88}[code]
+    poison = {"i8": -128, "fp8e4m3": 0x7F, "fp8e5m2": 0x7F, "i4": 0x88}[code]
     row_bytes = D // 2 if code == "i4" else D
     kc = torch.full((NB, BS, Hkv, row_bytes), poison, dtype=cdt, device="cuda")
     vc = torch.full_like(kc, poison)

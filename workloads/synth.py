@@ -17,8 +17,10 @@ Five workloads, named for what they are:
 ``quant_kv_32k_b16``     batch 16, 32 query / 8 KV heads, head dim 128, 32768
                          tokens each, bf16 source values with 1% of the
                          (KV head, channel) pairs of K scaled by 8, stored as
-                         INT8 (``kv_dtype="i8"``) or FP8-E4M3 codes with one
-                         scale per (block, KV head); bf16 queries.
+                         INT8 (``kv_dtype="i8"``), FP8-E4M3 (``"fp8e4m3"``),
+                         FP8-E5M2 (``"fp8e5m2"``) or packed INT4 (``"i4"``)
+                         codes with one scale per (block, KV head); bf16
+                         queries.
 ``ctx128k_b4``           batch 4, Llama-3.1-70B attention shape (64 query / 8 KV
                          heads, head dim 128), bf16, 131072 tokens each,
                          512-token split-K partitions; ``streaming=True`` keeps
