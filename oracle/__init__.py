@@ -32,7 +32,9 @@ Modules:
                   sequence, GQA head mapping, StreamingLLM keep-mask, and the
                   split-K partial/merge formulation.
 * ``quant``     - the symmetric absmax quantiser (INT8, INT4, FP8-e4m3 and
-                  FP8-e5m2 codes) and the requantisation of a growing block.
+                  FP8-e5m2 codes) with one scale per block tile or grouped
+                  scales (K per channel, V per token), and the
+                  requantisation of a growing block.
 * ``pool``      - FIFO free-block pool with reference counts and
                   copy-on-write append.
 * ``sizes``     - the KV cache-size formula.

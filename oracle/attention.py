@@ -15,6 +15,9 @@ StreamingLLM keep-mask ("Chapter 18 - KV-Cache Optimization Strategies",
 section "Token Eviction and Pruning"): the first ``sink`` tokens plus the most
 recent ``window`` tokens (4 + 4092 = 4096 entries in the page's layout).
 
+Grouped scales (``paged_decode_grouped``): keys dequantised with one scale
+per (block, KV head, channel), values with one per (block, KV head, token).
+
 Arithmetic: every value is decoded exactly to float32 (``codecs.decode``,
 ``quant.dequantize``) and the attention itself runs in float64.  The result is
 stored as float32.  A sequence of length 0 yields a zero output row.
@@ -92,6 +95,41 @@ def decoded_cache_rows(cache, table_row, length, block_size, dtype, scales=None)
         sc = np.asarray(scales, dtype=np.float32)[blocks] if L else np.zeros((0, vals.shape[1]), np.float32)
         vals = quant.dequantize(vals, sc[:, :, None])
     return vals
+
+
+def decoded_cache_rows_grouped(cache, table_row, length, block_size, dtype, group_scales, group):
+    """One sequence's rows in logical order, dequantised with grouped scales
+    (``quant.quantize_cache_blocks_grouped``): ``group_scales`` [NB, Hkv, D]
+    for "channel", [NB, Hkv, BS] for "token".  Returns [L, Hkv, D] float32."""
+    L = int(length)
+    Hkv = cache.shape[2]
+    out = []
+    for lb in range((L + block_size - 1) // block_size):
+        b = int(table_row[lb])
+        vals = codecs.decode(cache[b], dtype)                        # [BS, Hkv, D]
+        tile = np.stack([quant.dequantize_grouped(vals[:, h, :], group_scales[b, h], group)
+                         for h in range(Hkv)], axis=1)
+        out.append(tile[: min(block_size, L - lb * block_size)])
+    D = vals.shape[-1] if out else cache.shape[3] * (2 if dtype == "i4" else 1)
+    return np.concatenate(out) if out else np.zeros((0, Hkv, D), np.float32)
+
+
+def paged_decode_grouped(query, q_dtype, k_cache, v_cache, kv_dtype, block_tables, seq_lens, block_size,
+                         sm_scale, k_channel_scales, v_token_scales):
+    """``paged_decode`` over a cache quantised with grouped scales: keys with
+    one scale per (block, KV head, channel), values with one per (block, KV
+    head, token).  Returns float32 [S, Hq, D]."""
+    qv = codecs.decode(query, q_dtype)
+    S, Hq, D = qv.shape
+    out = np.zeros((S, Hq, D), dtype=np.float32)
+    for s in range(S):
+        L = int(seq_lens[s])
+        K = decoded_cache_rows_grouped(k_cache, block_tables[s], L, block_size, kv_dtype, k_channel_scales,
+                                       "channel")
+        V = decoded_cache_rows_grouped(v_cache, block_tables[s], L, block_size, kv_dtype, v_token_scales,
+                                       "token")
+        out[s] = decode_sequence(qv[s], K, V, sm_scale)
+    return out
 
 
 def paged_decode(query, q_dtype, k_cache, v_cache, kv_dtype, block_tables, seq_lens,

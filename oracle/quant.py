@@ -18,6 +18,14 @@ same per-tile absmax scale as the other formats.)
 Group: one scale per (physical block, KV head) over the ``[block_size, d_k]``
 tile, separately for K and V.
 
+Grouped scales (section 8's KIVI paragraph: keys grouped by channel, values
+by token, smaller groups fitting their own ranges): here a group stays
+inside one block tile, so K gets one scale per (block, KV head, channel)
+over the block's rows and V one per (block, KV head, token row) over the
+channels (``quantize_grouped``).  The tile's largest channel scale is kept
+beside the channel scales; it equals the tile scale of the one-scale rule
+(rounding a quotient by the same positive divisor is monotonic).
+
 Appending to a quantised cache (the pages do not say how): a sequence keeps
 the source values of its partial last block (its "tail"); each new token is
 added to the tail and the whole block is quantised again from the tail, with
@@ -137,3 +145,61 @@ def requantize_tail(tail_vals, rows, code_dtype):
     t[rows:] = 0.0
     codes, scales = quantize_cache_blocks(t[None], code_dtype)
     return codes[0], scales[0]
+
+
+def quantize_group_rows(tile, code_dtype):
+    """Codes and scales of a [n, m] array quantised row by row: each row is
+    one group with its own absmax scale.  Returns (codes [n, m] - packed to
+    [n, m / 2] bytes for "i4" -, scales [n] float32)."""
+    t = np.asarray(tile, dtype=np.float32)
+    n, m = t.shape
+    out = quantize_cache_blocks(t.reshape(n, 1, 1, m), code_dtype)
+    return out[0][:, 0, 0, :], out[1][:, 0]
+
+
+def quantize_grouped(tile, code_dtype, group):
+    """One block tile [BS, D] quantised with grouped scales.
+
+    ``group`` "channel": one scale per column (a channel across the block's
+    tokens); "token": one scale per row.  Returns (codes [BS, D] as
+    ``quantize_cache_blocks`` stores them, scales [D] or [BS] float32)."""
+    t = np.asarray(tile, dtype=np.float32)
+    if group == "token":
+        return quantize_group_rows(t, code_dtype)
+    if group != "channel":
+        raise ValueError(group)
+    if code_dtype == "i4":
+        # quantise the columns as rows (integer codes), then pack the rows
+        c, sc = quantize_group_rows(t.T, "i4")
+        vals = codecs.decode(c, "i4").astype(np.int64)            # [D, BS] code values
+        return codecs.i4_pack(vals.T), sc
+    c, sc = quantize_group_rows(t.T, code_dtype)
+    return np.ascontiguousarray(c.T), sc
+
+
+def quantize_cache_blocks_grouped(cache_vals, code_dtype, group, block_ids=None):
+    """Grouped-scale quantisation of whole blocks of a decoded cache
+    [NB, BS, Hkv, D] float32.  Returns (codes in the cache's layout, group
+    scales [NB, Hkv, D] for "channel" or [NB, Hkv, BS] for "token", tile
+    scales [NB, Hkv] = the largest group scale of each tile).  Blocks not
+    listed keep code 0 and scales 0."""
+    NB, BS, Hkv, D = cache_vals.shape
+    ids = range(NB) if block_ids is None else [int(b) for b in block_ids]
+    codes, _ = quantize_cache_blocks(np.zeros((NB, BS, Hkv, D), np.float32), code_dtype, [])
+    gs = np.zeros((NB, Hkv, D if group == "channel" else BS), dtype=np.float32)
+    ts = np.zeros((NB, Hkv), dtype=np.float32)
+    for b in ids:
+        for h in range(Hkv):
+            c, sc = quantize_grouped(cache_vals[b, :, h, :], code_dtype, group)
+            codes[b, :, h, :] = c
+            gs[b, h] = sc
+            ts[b, h] = sc.max() if sc.size else 0
+    return codes, gs, ts
+
+
+def dequantize_grouped(code_values, scales, group):
+    """Restored tile ``fp32(code * scale)`` for a [BS, D] tile of code values
+    (float32) and its group scales ([D] for "channel", [BS] for "token")."""
+    cv = np.asarray(code_values, dtype=np.float32)
+    sc = np.asarray(scales, dtype=np.float32)
+    return dequantize(cv, sc[None, :] if group == "channel" else sc[:, None])

@@ -409,3 +409,101 @@ def test_i4_cache_blocks_follow_the_page_example_rule():
     back = quant.dequantize(vals[0, 0, 0, :6], scales[0, 0]).astype(np.float64)
     assert np.round(back, 3).tolist() == g["restored_3dp"]
     assert (vals[0, 1:] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# grouped scales (section 8, KIVI paragraph): K per channel, V per token,
+# each group inside one block tile
+# --------------------------------------------------------------------------
+
+def test_grouped_page_example_as_one_channel_and_as_one_token():
+    """The section-8 example's six values form one group either way: as the
+    single channel of a [6, 1] tile or as the single token of a [1, 6] tile
+    they give the page's codes and restored values."""
+    g = golden("quant4_example.json")
+    vals = np.array(g["values"], dtype=np.float32)
+    c, sc = quant.quantize_grouped(vals[:, None], "i8", "channel")     # 8-bit first: shape only
+    assert c.shape == (6, 1) and sc.shape == (1,)
+    col = np.zeros((6, 2), np.float32)
+    col[:, 0] = vals                                                   # second channel all zero
+    c4, sc4 = quant.quantize_grouped(col, "i4", "channel")
+    codes = codecs.decode(c4, "i4")[:, 0]
+    assert codes.astype(int).tolist() == g["codes"]
+    assert sc4[1] == 0 and not codecs.decode(c4, "i4")[:, 1].any()
+    restored = quant.dequantize_grouped(codecs.decode(c4, "i4"), sc4, "channel")[:, 0]
+    assert np.round(restored.astype(np.float64), 3).tolist() == g["restored_3dp"]
+    row = np.zeros((2, 6), np.float32)
+    row[1] = vals
+    t4, ts4 = quant.quantize_grouped(row, "i4", "token")
+    assert codecs.decode(t4, "i4")[1].astype(int).tolist() == g["codes"]
+    assert ts4[0] == 0 and ts4[1] == sc4[0]
+
+
+@pytest.mark.parametrize("code", ["i8", "fp8e4m3", "fp8e5m2", "i4"])
+def test_token_groups_are_channel_groups_of_the_transpose(code):
+    rng = np.random.default_rng(41)
+    t = rng.standard_normal((16, 32)).astype(np.float32) * rng.uniform(0.1, 10, size=(16, 1)).astype(np.float32)
+    ct, st = quant.quantize_grouped(t, code, "token")
+    cc, sc = quant.quantize_grouped(np.ascontiguousarray(t.T), code, "channel")
+    assert (st.view(np.uint32) == sc.view(np.uint32)).all()
+    assert (codecs.decode(ct, code) == codecs.decode(cc, code).T).all()
+
+
+@pytest.mark.parametrize("code,qmax", [("i8", 127), ("i4", 7)])
+def test_channel_groups_fit_their_own_range(code, qmax):
+    """Each channel's largest magnitude takes the largest code, every value
+    is restored within half a step of its own channel's scale, and the
+    largest channel scale is the one-scale tile rule's scale."""
+    rng = np.random.default_rng(42)
+    t = rng.standard_normal((16, 64)).astype(np.float32)
+    t[:, 5] *= 8.0
+    t[:, 9] *= 0.01
+    c, sc = quant.quantize_grouped(t, code, "channel")
+    vals = codecs.decode(c, code)
+    for d in range(64):
+        i = np.abs(t[:, d]).argmax()
+        assert abs(vals[i, d]) == qmax
+        assert sc[d] == np.float32(np.float32(np.abs(t[:, d]).max()) / np.float32(qmax))
+    back = quant.dequantize_grouped(vals, sc, "channel")
+    assert (np.abs(back - t) <= sc[None, :] * 0.5 * (1 + 1e-6)).all()
+    _, tile_sc = quant.quantize_int(t, 4 if code == "i4" else 8)
+    assert sc.max() == tile_sc
+
+
+def test_channel_groups_shrink_the_error_of_outlier_tiles():
+    """With one channel x8 (config 4's outliers), the other channels' worst
+    rounding error under per-channel scales is far below the one-scale
+    tile's (the page: smaller groups fit their own ranges)."""
+    rng = np.random.default_rng(43)
+    t = rng.standard_normal((16, 128)).astype(np.float32)
+    t[:, 3] *= 8.0
+    c, sc = quant.quantize_grouped(t, "i8", "channel")
+    err_g = np.abs(quant.dequantize_grouped(codecs.decode(c, "i8"), sc, "channel") - t)
+    ct, tsc = quant.quantize_int(t, 8)
+    err_t = np.abs(quant.dequantize(ct, tsc) - t)
+    others = np.arange(128) != 3
+    assert err_g[:, others].max() < err_t[:, others].max() / 4
+
+
+def test_grouped_decode_reduces_to_tile_decode_when_all_groups_share_the_range():
+    """Tiles whose every channel (for K) and every token (for V) reaches the
+    same magnitude get group scales equal to the tile scale, the codes of
+    the one-scale rule, and the same attention output."""
+    rng = np.random.default_rng(44)
+    NB, BS, Hkv, D, Hq = 6, 16, 2, 32, 4
+    k = rng.uniform(-1, 1, (NB, BS, Hkv, D)).astype(np.float32)
+    v = rng.uniform(-1, 1, (NB, BS, Hkv, D)).astype(np.float32)
+    k[:, 0] = 2.0                       # every channel reaches 2 in row 0
+    v[:, :, :, 0] = -2.0                # every token reaches 2 in channel 0
+    kc, kg, kt = quant.quantize_cache_blocks_grouped(k, "i8", "channel")
+    vc, vg, vt = quant.quantize_cache_blocks_grouped(v, "i8", "token")
+    kc1, ks1 = quant.quantize_cache_blocks(k, "i8")
+    vc1, vs1 = quant.quantize_cache_blocks(v, "i8")
+    assert (kc == kc1).all() and (vc == vc1).all()
+    assert (kg == ks1[:, :, None]).all() and (vg == vs1[:, :, None]).all() and (kt == ks1).all()
+    q = rng.standard_normal((2, Hq, D)).astype(np.float32)
+    tables = np.array([[0, 3, 5], [4, 1, 2]], dtype=np.int32)
+    lens = [40, 33]
+    a = attention.paged_decode_grouped(q, "f32", kc, vc, "i8", tables, lens, BS, 0.2, kg, vg)
+    b = attention.paged_decode(q, "f32", kc1, vc1, "i8", tables, lens, BS, 0.2, ks1, vs1)
+    assert (a == b).all()
