@@ -391,6 +391,54 @@ pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes
                            int num_blocks, int block_size, int num_kv_heads, int head_dim,
                            void* stream);
 
+/* Scale groups of the grouped quantiser and decode. */
+typedef enum pkv_scale_group {
+  PKV_GROUP_CHANNEL = 0, /* one scale per (block, KV head, channel) over the block's rows (keys) */
+  PKV_GROUP_TOKEN = 1    /* one scale per (block, KV head, token row) over the channels (values) */
+} pkv_scale_group;
+
+/*
+ * Absmax quantisation with grouped scales ([P2] s.8, the KIVI paragraph:
+ * keys grouped by channel, values by token; here every group stays inside
+ * one block tile).  Per (block, KV head) tile [block_size][head_dim], each
+ * group g (a column for PKV_GROUP_CHANNEL, a row for PKV_GROUP_TOKEN) gets
+ * scale_g = fp32(max |x_g| / qmax) and its elements the codes of
+ * pkv_quantize_kv with that scale (qmax and rounding as there).
+ * dst_codes: cache layout of code_dtype; dst_group_scales: fp32
+ * [num_blocks][num_kv_heads][head_dim] (channel) or
+ * [num_blocks][num_kv_heads][block_size] (token); dst_tile_scales: fp32
+ * [num_blocks][num_kv_heads], each tile's largest group scale (the
+ * one-scale tile rule's scale), or NULL to skip.  block_ids / n_blocks as
+ * in pkv_quantize_kv.  Bit-exact.
+ */
+pkv_status pkv_quantize_kv_grouped(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
+                                   float* dst_tile_scales, float* dst_group_scales, int group,
+                                   const int32_t* block_ids, int n_blocks, int num_blocks, int block_size,
+                                   int num_kv_heads, int head_dim, void* stream);
+
+/*
+ * pkv_paged_attn_decode over a cache quantised with grouped scales: keys
+ * by channel (k_channel_scales [num_blocks][num_kv_heads][head_dim] and
+ * k_tile_scales [num_blocks][num_kv_heads] from pkv_quantize_kv_grouped
+ * with PKV_GROUP_CHANNEL), values by token (v_token_scales
+ * [num_blocks][num_kv_heads][block_size], PKV_GROUP_TOKEN).  A key is
+ * code * channel scale, a value code * token scale.  kv_dtype PKV_I8
+ * (head_dim 64 or 128) or PKV_I4 (head_dim 128); bf16 or f16 query; no
+ * keep-mask.  The channel scales enter the products as f16 factors
+ * scale / tile scale in (0, 1] (the tile scale joins the fp32 score
+ * factor), so a channel below 2^-24 of its tile's largest reads as zero.
+ * num_blocks * num_kv_heads < 2^25.  Workspace, partition_size and flags as
+ * in pkv_paged_attn_decode (size it with the kv_dtype).
+ */
+pkv_status pkv_paged_attn_decode_grouped(void* out, const void* query, int q_dtype, const void* k_cache,
+                                         const void* v_cache, int kv_dtype, const float* k_tile_scales,
+                                         const float* k_channel_scales, const float* v_token_scales,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                         float sm_scale, int partition_size, unsigned flags, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
 /*
  * Appends one token per sequence to a quantised cache (the pages leave the
  * how open; this is the reading taken).  Each sequence keeps the source

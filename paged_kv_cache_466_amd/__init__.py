@@ -16,6 +16,7 @@ __all__ = [
     "paged_attn_decode", "paged_attn_partition", "paged_attn_merge",
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
     "paged_attn_decode_multi", "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
+    "paged_attn_decode_grouped", "quantize_kv_grouped", "GROUP_CHANNEL", "GROUP_TOKEN",
     "slot_mapping", "reshape_and_cache", "append_kv", "append_kv_quantized", "copy_blocks", "quantize_kv",
     "validate_tables", "BlockPool", "PrefixCache", "h2o_retain", "DTYPES",
 ]
@@ -32,6 +33,8 @@ lib = ctypes.CDLL(LIB_PATH)
 F32, BF16, F16, I8, FP8E4M3, I4, FP8E5M2 = 0, 1, 2, 3, 4, 5, 6
 # decode flags
 DECODE_STREAM_KV = 1
+# scale groups of the grouped quantiser / decode
+GROUP_CHANNEL, GROUP_TOKEN = 0, 1
 DTYPES = {"f32": F32, "bf16": BF16, "f16": F16, "i8": I8, "fp8e4m3": FP8E4M3, "i4": I4, "fp8e5m2": FP8E5M2}
 _TORCH_TO_PKV = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8,
                  torch.float8_e4m3fn: FP8E4M3, torch.float8_e5m2: FP8E5M2}
@@ -56,6 +59,9 @@ _SIGS = {
                                      ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_selected": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                         ctypes.c_uint, _p, _sz, _p], _i),
+    "pkv_paged_attn_decode_grouped": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
+                                       _i, ctypes.c_uint, _p, _sz, _p], _i),
+    "pkv_quantize_kv_grouped": ([_p, _i, _p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_quest_summarize": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p], _i),
     "pkv_quest_scratch_bytes": ([_i, _i, _i], _sz),
     "pkv_quest_select": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p], _i),
@@ -415,6 +421,53 @@ def quantize_kv(src_cache, dst_codes, dst_scales, code_dtype, block_ids=None, n_
     _check(lib.pkv_quantize_kv(_ptr(src_cache), _dtype(src_cache), _ptr(dst_codes), DTYPES[code_dtype],
                                _ptr(dst_scales), _ptr(block_ids), n_blocks, NB, BS, Hkv, D,
                                _stream(src_cache)))
+
+
+def quantize_kv_grouped(src_cache, dst_codes, dst_group_scales, code_dtype, group, dst_tile_scales=None,
+                        block_ids=None, n_blocks=None):
+    """Absmax quantisation with grouped scales (``pkv_quantize_kv_grouped``):
+    ``group`` GROUP_CHANNEL (dst_group_scales [NB, Hkv, D]) or GROUP_TOKEN
+    ([NB, Hkv, 16]); dst_tile_scales [NB, Hkv] receives each tile's largest
+    group scale when given."""
+    _contig(src_cache, dst_codes, dst_group_scales, dst_tile_scales, block_ids)
+    NB, BS, Hkv, D = src_cache.shape
+    if _head_dim(dst_codes, DTYPES[code_dtype]) != D or tuple(dst_codes.shape[:3]) != (NB, BS, Hkv):
+        raise ValueError("dst_codes must be [NB, block_size, Hkv, D] (D / 2 bytes for i4)")
+    want = (NB, Hkv, D if group == GROUP_CHANNEL else BS)
+    if tuple(dst_group_scales.shape) != want or dst_group_scales.dtype != torch.float32:
+        raise ValueError(f"dst_group_scales must be float32 {want}")
+    if n_blocks is None:
+        n_blocks = block_ids.numel() if block_ids is not None else NB
+    _check(lib.pkv_quantize_kv_grouped(_ptr(src_cache), _dtype(src_cache), _ptr(dst_codes), DTYPES[code_dtype],
+                                       _ptr(dst_tile_scales), _ptr(dst_group_scales), int(group), _ptr(block_ids),
+                                       n_blocks, NB, BS, Hkv, D, _stream(src_cache)))
+
+
+def paged_attn_decode_grouped(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_tile_scales,
+                              k_channel_scales, v_token_scales, partition_size=0, workspace=None, kv_dtype=None,
+                              stream_kv=False):
+    """Decode over a cache quantised with grouped scales
+    (``pkv_paged_attn_decode_grouped``): keys per channel, values per token."""
+    _contig(out, query, k_cache, v_cache, block_tables, seq_lens, k_tile_scales, k_channel_scales,
+            v_token_scales, workspace)
+    S, Hq, D = query.shape
+    NB, BS, Hkv = k_cache.shape[:3]
+    kvdt = _dtype(k_cache, kv_dtype)
+    if _head_dim(k_cache, kvdt) != D or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("shape mismatch between query, caches and out")
+    if tuple(k_channel_scales.shape) != (NB, Hkv, D) or tuple(v_token_scales.shape) != (NB, Hkv, BS) \
+            or tuple(k_tile_scales.shape) != (NB, Hkv):
+        raise ValueError("scales must be [NB, Hkv] (tile), [NB, Hkv, D] (channel) and [NB, Hkv, 16] (token)")
+    workspace = _workspace_for(query, k_cache, block_tables, partition_size, workspace, kvdt)
+    mbs = block_tables.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attn_decode_grouped(
+        _ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), kvdt, _ptr(k_tile_scales),
+        _ptr(k_channel_scales), _ptr(v_token_scales), _ptr(block_tables), mbs, _ptr(seq_lens), S, Hq, Hkv, D, BS, NB,
+        float(sm_scale), int(partition_size), DECODE_STREAM_KV if stream_kv else 0, _ptr(workspace), ws_bytes,
+        _stream(query)))
+    return out
 
 
 def validate_tables(block_tables, seq_lens, num_blocks, slot_mapping=None, block_size=16):

@@ -392,6 +392,37 @@ extern "C" pkv_status pkv_paged_attn_decode_selected(
   return hip_status(launch_paged_attn_merge(a), who);
 }
 
+extern "C" pkv_status pkv_paged_attn_decode_grouped(
+    void* out, const void* query, int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_tile_scales, const float* k_channel_scales, const float* v_token_scales,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
+    int num_kv_heads, int head_dim, int block_size, int num_blocks, float sm_scale, int partition_size,
+    unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "pkv_paged_attn_decode_grouped";
+  if (kv_dtype != PKV_I8 && kv_dtype != PKV_I4)
+    return fail(PKV_EUNSUPPORTED, "%s: grouped scales are built for i8 and i4 codes", who);
+  if (q_dtype != PKV_BF16 && q_dtype != PKV_F16) return fail(PKV_EUNSUPPORTED, "%s: query must be bf16 or f16", who);
+  if (num_seqs > 0 && (!k_tile_scales || !k_channel_scales || !v_token_scales))
+    return fail(PKV_EINVAL, "%s: null scale pointer", who);
+  // token scales are addressed as num_blocks * num_kv_heads * 64 bytes in 31 bits
+  if ((long long)num_blocks * num_kv_heads >= (1LL << 25))
+    return fail(PKV_EUNSUPPORTED, "%s: pool too large (num_blocks * num_kv_heads >= 2^25)", who);
+  AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, k_tile_scales, v_token_scales,
+                         block_tables, max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                         block_size, num_blocks, sm_scale, partition_size, 0, 0, flags, stream);
+  a.k_chan = k_channel_scales;
+  pkv_status st = prepare_attn(a, who, workspace, workspace_bytes, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if (check_env()) {
+    st = device_check(block_tables, max_blocks_per_seq, seq_lens, num_seqs, block_size, num_blocks, nullptr, 0,
+                      stream);
+    if (st != PKV_OK) return st;
+  }
+  st = hip_status(launch_paged_attn_partition(a), who);
+  if (st != PKV_OK) return st;
+  return hip_status(launch_paged_attn_merge(a), who);
+}
+
 extern "C" size_t pkv_quest_scratch_bytes(int num_seqs, int num_kv_heads, int max_blocks_per_seq) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
   return align256((size_t)num_seqs * num_kv_heads * max_blocks_per_seq * 8);
@@ -550,6 +581,27 @@ extern "C" pkv_status pkv_append_kv_quantized(const void* key, const void* value
   return hip_status(launch_append_quantized(key, value, src_dtype, k_tail, v_tail, k_codes, v_codes, code_dtype,
                                             k_scales, v_scales, block_tables, max_blocks_per_seq, positions,
                                             num_seqs, num_blocks, num_kv_heads, head_dim, stream),
+                    who);
+}
+
+extern "C" pkv_status pkv_quantize_kv_grouped(const void* src_cache, int src_dtype, void* dst_codes,
+                                              int code_dtype, float* dst_tile_scales, float* dst_group_scales,
+                                              int group, const int32_t* block_ids, int n_blocks, int num_blocks,
+                                              int block_size, int num_kv_heads, int head_dim, void* stream) {
+  const char* who = "pkv_quantize_kv_grouped";
+  pkv_status st = check_cache_shape(who, block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (!is_float_storage(src_dtype)) return fail(PKV_EUNSUPPORTED, "%s: source must be f32/bf16/f16", who);
+  if (!is_code_storage(code_dtype))
+    return fail(PKV_EUNSUPPORTED, "%s: codes must be i8, i4, fp8e4m3 or fp8e5m2", who);
+  if (group != PKV_GROUP_CHANNEL && group != PKV_GROUP_TOKEN) return fail(PKV_EINVAL, "%s: unknown group %d", who, group);
+  if (n_blocks < 0 || num_blocks < 0) return fail(PKV_EINVAL, "%s: negative size", who);
+  if (!block_ids && n_blocks > num_blocks) return fail(PKV_EINVAL, "%s: n_blocks > num_blocks", who);
+  if (n_blocks == 0) return PKV_OK;
+  if (!src_cache || !dst_codes || !dst_group_scales) return fail(PKV_EINVAL, "%s: null pointer", who);
+  return hip_status(launch_quantize_kv_grouped(src_cache, src_dtype, dst_codes, code_dtype, dst_tile_scales,
+                                               dst_group_scales, group, block_ids, n_blocks, num_blocks, num_kv_heads,
+                                               head_dim, stream),
                     who);
 }
 

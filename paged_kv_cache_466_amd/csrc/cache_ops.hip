@@ -181,15 +181,15 @@ template <> struct CodeTraits<kCodeI4> { static constexpr float qmax = 7.f; stat
 // rounds to the E4M3 grid), stored at dst as N * bits / 8 bytes (INT4:
 // element 2i in the low nibble of byte i).
 template <int CODE, int N>
-__device__ __forceinline__ void encode_store(const float* x, float sc, uint8_t* dst) {
+__device__ __forceinline__ void encode_store(const float* x, const float* sc, uint8_t* dst) {
   constexpr float qmax = CodeTraits<CODE>::qmax;
   uint8_t codes[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    if (sc == 0.f) {
+    if (sc[i] == 0.f) {
       codes[i] = 0;
     } else {
-      const float y = __fdiv_rn(x[i], sc);
+      const float y = __fdiv_rn(x[i], sc[i]);
       if constexpr (CODE == kCodeFP8) {
         codes[i] = (uint8_t)f32_to_e4m3(y);
       } else if constexpr (CODE == kCodeBF8) {
@@ -259,8 +259,95 @@ __global__ __launch_bounds__(64) void quantize_kv_kernel(
   for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
   a = wave_max(a);
   const float sc = __fdiv_rn(a, CodeTraits<CODE>::qmax);
-  encode_store<CODE, ELEMS>(x, sc, reinterpret_cast<uint8_t*>(dst) + row * ROWB + q * (ROWB / 4));
+  float scv[ELEMS];
+#pragma unroll
+  for (int i = 0; i < ELEMS; ++i) scv[i] = sc;
+  encode_store<CODE, ELEMS>(x, scv, reinterpret_cast<uint8_t*>(dst) + row * ROWB + q * (ROWB / 4));
   if (lane == 0) scales[(size_t)b * num_kv_heads + h] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// Grouped scales ("KV Cache Engineering", section 8, the KIVI paragraph:
+// keys grouped by channel, values by token), each group inside one block
+// tile: with quantize_kv's lane layout (lane l: token row t = l/4, quarter
+// q = l%4 of the head dimension), channel q * D/4 + i of a tile lives in
+// lanes q, q + 4, ..., q + 60, and token row t in lanes 4t .. 4t + 3.
+// Sets each element's group scale (group absmax / largest code) and returns
+// the tile's largest group scale (uniform).
+// ---------------------------------------------------------------------------
+enum GroupKind { kGroupChannel = 0, kGroupToken = 1 };
+
+template <int CODE, int GROUP, int ELEMS>
+__device__ __forceinline__ float group_scales(const float* x, float* sc) {
+  constexpr float qmax = CodeTraits<CODE>::qmax;
+  float smax;
+  if constexpr (GROUP == kGroupChannel) {
+    smax = 0.f;
+#pragma unroll
+    for (int i = 0; i < ELEMS; ++i) {
+      float a = fabsf(x[i]);
+#pragma unroll
+      for (int o = 4; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+      sc[i] = __fdiv_rn(a, qmax);
+      smax = fmaxf(smax, sc[i]);
+    }
+    smax = fmaxf(smax, __shfl_xor(smax, 1, 64));
+    smax = fmaxf(smax, __shfl_xor(smax, 2, 64));
+  } else {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));
+    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    const float st = __fdiv_rn(a, qmax);
+#pragma unroll
+    for (int i = 0; i < ELEMS; ++i) sc[i] = st;
+    smax = wave_max(st);
+  }
+  return smax;
+}
+
+// Writes the group scales of one tile: channel scales [D] (row-0 lanes, a
+// quarter each) or token scales [16] (one lane per row).
+template <int GROUP, int D>
+__device__ __forceinline__ void store_group_scales(float* gs_tile, const float* sc, int t, int q) {
+  constexpr int ELEMS = D / 4;
+  if constexpr (GROUP == kGroupChannel) {
+    if (t == 0) {
+#pragma unroll
+      for (int i = 0; i < ELEMS; i += 4)
+        *reinterpret_cast<float4*>(gs_tile + q * ELEMS + i) = make_float4(sc[i], sc[i + 1], sc[i + 2], sc[i + 3]);
+    }
+  } else {
+    if (q == 0) gs_tile[t] = sc[0];
+  }
+}
+
+template <typename SRC, int D, int CODE, int GROUP>
+__global__ __launch_bounds__(64) void quantize_kv_grouped_kernel(
+    const typename SRC::raw* __restrict__ src, void* __restrict__ dst, float* __restrict__ tile_scales,
+    float* __restrict__ gscales, const int32_t* __restrict__ block_ids, int num_blocks, int num_kv_heads) {
+  constexpr int BS = 16;
+  constexpr int ELEMS = D / 4;                 // per lane
+  constexpr int SRC_CHUNKS = ELEMS * SRC::bytes / 16;
+  constexpr int EL16 = 16 / SRC::bytes;
+  constexpr int ROWB = D * CodeTraits<CODE>::bits / 8;   // code bytes per row
+  constexpr int GS = GROUP == kGroupChannel ? D : BS;    // group scales per tile
+  const int b = block_ids ? block_ids[blockIdx.x] : (int)blockIdx.x;
+  const int h = blockIdx.y;
+  if (b < 0 || b >= num_blocks) return;
+  const int lane = threadIdx.x;
+  const int t = lane >> 2, q = lane & 3;
+  const size_t row = ((size_t)b * BS + t) * num_kv_heads + h;   // element row index
+  const uint4* p = reinterpret_cast<const uint4*>(src + row * D + q * ELEMS);
+  float x[ELEMS];
+#pragma unroll
+  for (int c = 0; c < SRC_CHUNKS; ++c) decode16<SRC>(p[c], x + c * EL16);
+  float sc[ELEMS];
+  const float smax = group_scales<CODE, GROUP, ELEMS>(x, sc);
+  encode_store<CODE, ELEMS>(x, sc, reinterpret_cast<uint8_t*>(dst) + row * ROWB + q * (ROWB / 4));
+  store_group_scales<GROUP, D>(gscales + ((size_t)b * num_kv_heads + h) * GS, sc, t, q);
+  if (lane == 0 && tile_scales) tile_scales[(size_t)b * num_kv_heads + h] = smax;
 }
 
 template <typename SRC, int D>
@@ -281,6 +368,47 @@ static int launch_q(const void* src, void* dst, int code_dtype, float* scales, c
     quantize_kv_kernel<SRC, D, kCodeI8><<<grid, 64, 0, st>>>((const R*)src, dst, scales, ids, num_blocks,
                                                              num_kv_heads);
   return hipGetLastError();
+}
+
+template <typename SRC, int D, int GROUP>
+static int launch_qg(const void* src, void* dst, int code_dtype, float* tile_scales, float* gscales,
+                     const int32_t* ids, int n_blocks, int num_blocks, int num_kv_heads, hipStream_t st) {
+  dim3 grid(n_blocks, num_kv_heads);
+  typedef typename SRC::raw R;
+#define PKV_QG(CODE)                                                                                   \
+  quantize_kv_grouped_kernel<SRC, D, CODE, GROUP><<<grid, 64, 0, st>>>((const R*)src, dst, tile_scales, \
+                                                                      gscales, ids, num_blocks, num_kv_heads)
+  switch (code_dtype) {
+    case PKV_FP8E4M3: PKV_QG(kCodeFP8); break;
+    case PKV_FP8E5M2: PKV_QG(kCodeBF8); break;
+    case PKV_I4: PKV_QG(kCodeI4); break;
+    default: PKV_QG(kCodeI8); break;
+  }
+#undef PKV_QG
+  return hipGetLastError();
+}
+
+int launch_quantize_kv_grouped(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
+                               float* tile_scales, float* group_scales, int group, const int32_t* block_ids,
+                               int n_blocks, int num_blocks, int num_kv_heads, int head_dim, void* stream) {
+  if (n_blocks == 0) return hipSuccess;
+  hipStream_t st = (hipStream_t)stream;
+#define PKV_QGD(SRC, D)                                                                                    \
+  return group == PKV_GROUP_CHANNEL                                                                        \
+             ? launch_qg<SRC, D, kGroupChannel>(src_cache, dst_codes, code_dtype, tile_scales, group_scales, \
+                                                block_ids, n_blocks, num_blocks, num_kv_heads, st)          \
+             : launch_qg<SRC, D, kGroupToken>(src_cache, dst_codes, code_dtype, tile_scales, group_scales,   \
+                                              block_ids, n_blocks, num_blocks, num_kv_heads, st)
+#define PKV_QGS(SRC)                 \
+  if (head_dim == 64) PKV_QGD(SRC, 64); \
+  PKV_QGD(SRC, 128)
+  switch (src_dtype) {
+    case PKV_F32: { PKV_QGS(F32); }
+    case PKV_BF16: { PKV_QGS(BF16); }
+    default: { PKV_QGS(F16); }
+  }
+#undef PKV_QGS
+#undef PKV_QGD
 }
 
 int launch_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
@@ -355,8 +483,11 @@ __global__ __launch_bounds__(64) void append_quantized_kernel(
   for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
   a = wave_max(a);
   const float sc = __fdiv_rn(a, CodeTraits<CODE>::qmax);
+  float scv[ELEMS];
+#pragma unroll
+  for (int i = 0; i < ELEMS; ++i) scv[i] = sc;
   uint8_t* dst = is_v ? v_codes : k_codes;
-  encode_store<CODE, ELEMS>(x, sc, dst + (((size_t)b * BS + t) * num_kv_heads + h) * ROWB + q * (ROWB / 4));
+  encode_store<CODE, ELEMS>(x, scv, dst + (((size_t)b * BS + t) * num_kv_heads + h) * ROWB + q * (ROWB / 4));
   if (lane == 0) (is_v ? v_scales : k_scales)[(size_t)b * num_kv_heads + h] = sc;
 }
 

@@ -65,6 +65,7 @@ struct AttnParams {
   const int32_t* selected;   // selected decode: [S][Hkv][budget] (physical, logical block)
   int budget;                // selected decode: pages per (sequence, KV head)
   int qtok;                  // query tokens per sequence (the last qtok positions, causal)
+  const float* k_chan;       // grouped scales: K per (block, KV head, channel); v_scales per token
   float scale_log2;     // sm_scale * log2(e)
 };
 
@@ -216,7 +217,9 @@ __device__ __forceinline__ uint4 to16(uint32_t w0, uint32_t w1) {
   }
 }
 
-template <typename KVT, int D>
+// GRP: grouped scales (K per channel, V per token), whose per-lane scale
+// loads ride in the ring too.
+template <typename KVT, int D, bool GRP = false>
 struct WaveCfg {
   static constexpr bool kCodes = KVT::bits < 16;
   static constexpr int NC = D / 32;                    // q.K MFMAs per block (k = 32)
@@ -228,8 +231,9 @@ struct WaveCfg {
   static constexpr int LANES_PER_ROW = ROW_BYTES / 16;
   static constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
   static constexpr int VCH = kBS / ROWS_PER_PASS;      // 16-byte V loads per lane per block
-  static constexpr int STAGE_VGPRS = 4 * (KCH + VCH);
-  static constexpr int DEPTH = STAGE_VGPRS >= 32 ? 4 : 8;   // ring of register tiles
+  static constexpr int KCS = GRP ? D / 16 : 1;         // 16-byte channel-scale loads per lane (a quarter row)
+  static constexpr int STAGE_VGPRS = 4 * (KCH + VCH) + (GRP ? 4 * KCS + 4 : 0);
+  static constexpr int DEPTH = GRP ? 2 : (STAGE_VGPRS >= 32 ? 4 : 8);   // ring of register tiles
   static constexpr int VROW = D * 2 + 16;              // LDS bytes per staged V row (16-bit, padded)
   static constexpr int VSTAGE = kBS * VROW;            // one staged V block
 };
@@ -459,10 +463,12 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
   }
 }
 
-template <typename QT, typename KVT, int D, bool STREAM, bool SEL>
+template <typename QT, typename KVT, int D, bool STREAM, bool SEL, bool GRP>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_attn_wave_kernel(AttnParams p) {
-  typedef WaveCfg<KVT, D> C;
+  typedef WaveCfg<KVT, D, GRP> C;
+  static_assert(!GRP || (C::kCodes && std::is_same<typename MmaType<QT, KVT>::type, F16>::value && !SEL),
+                "grouped scales are built for integer codes, without a selection");
   typedef typename MmaType<QT, KVT>::type MT;
   typedef Mfma<MT> M;     // operands of both products
   typedef Mfma<QT> MO;    // the output type
@@ -543,6 +549,8 @@ void paged_attn_wave_kernel(AttnParams p) {
     uint4 k[KCH];
     uint4 v[VCH];
     float ks, vs;
+    floatx4 kcs[C::KCS];   // grouped: channel scales of this lane's quarter row
+    floatx4 vts;           // grouped: token scales of rows 4 kg .. 4 kg + 3
     int t0;   // first token of the block
   };
   const int row_stride = p.num_kv_heads * C::ROW_BYTES;        // bytes between token rows
@@ -561,7 +569,12 @@ void paged_attn_wave_kernel(AttnParams p) {
   // checked on the host); an empty pool reads nothing
   const int sbytes = kCodes && p.num_blocks > 0 ? p.num_blocks * (int)scale_row_bytes - kvh * 4 : 0;
   const __amdgpu_buffer_rsrc_t ks_r = make_rsrc(p.k_scales + kvh, sbytes);
-  const __amdgpu_buffer_rsrc_t vs_r = make_rsrc(p.v_scales + kvh, sbytes);
+  // grouped: token scales [block][head][16] (num_blocks * Hkv * 64 < 2^31,
+  // checked on the host), channel scales [block][head][D]
+  const __amdgpu_buffer_rsrc_t vs_r =
+      GRP ? make_rsrc(p.v_scales + kvh * kBS, p.num_blocks > 0 ? (p.num_blocks * p.num_kv_heads - kvh) * kBS * 4 : 0)
+          : make_rsrc(p.v_scales + kvh, sbytes);
+  const uint8_t* kchan_head = reinterpret_cast<const uint8_t*>(p.k_chan + (size_t)kvh * D);
   int v_off[VCH], v_row[VCH];
 #pragma unroll
   for (int ps = 0; ps < VCH; ++ps) {
@@ -599,7 +612,14 @@ void paged_attn_wave_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int ps = 0; ps < VCH; ++ps) t.v[ps] = buf_load16<STREAM ? kPolicyStream : 0>(vr, vo[ps]);
-    if constexpr (kCodes) {
+    if constexpr (GRP) {
+      t.ks = buf_load4(ks_r, 0, (int)so);
+      const __amdgpu_buffer_rsrc_t cr = make_rsrc(kchan_head + (uint64_t)so * D, valid ? D * 4 : 0);
+#pragma unroll
+      for (int j = 0; j < C::KCS; ++j)
+        t.kcs[j] = __builtin_bit_cast(floatx4, buf_load16(cr, (D / 4) * 4 * kg + 16 * j));
+      t.vts = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(vs_r, 16 * kg, (int)so * kBS, 0));
+    } else if constexpr (kCodes) {
       t.ks = buf_load4(ks_r, 0, (int)so);
       t.vs = buf_load4(vs_r, 0, (int)so);
     } else {
@@ -756,6 +776,30 @@ void paged_attn_wave_kernel(AttnParams p) {
 
     // ---- S^T = K Q^T --------------------------------------------------------
     floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+    // grouped: channel factors s_d / s_tile in (0, 1] as f16 pairs (the tile
+    // scale goes into the score factor): 8 channels of k-chunk c per uint4
+    uint32_t kf[GRP ? 4 * NC : 1];
+    if constexpr (GRP) {
+      const float r = t.ks > 0.f ? __builtin_amdgcn_rcpf(t.ks) : 0.f;
+#pragma unroll
+      for (int j = 0; j < C::KCS; ++j) {
+        kf[2 * j] = M::pack2(t.kcs[j][0] * r, t.kcs[j][1] * r);
+        kf[2 * j + 1] = M::pack2(t.kcs[j][2] * r, t.kcs[j][3] * r);
+      }
+    }
+    auto kscale = [&](uint4 k8, int c) {
+      if constexpr (GRP) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const uint32_t w[4] = {k8.x, k8.y, k8.z, k8.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, w[i]) * __builtin_bit_cast(h2, kf[4 * c + i]));
+        return make_uint4(o[0], o[1], o[2], o[3]);
+      } else {
+        return k8;
+      }
+    };
     if constexpr (!kCodes) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::vec8, t.k[c]), qop[c], sacc);
@@ -766,14 +810,15 @@ void paged_attn_wave_kernel(AttnParams p) {
         const uint32_t w[4] = {t.k[c2].x, t.k[c2].y, t.k[c2].z, t.k[c2].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          sacc = M::qk(__builtin_bit_cast(typename M::vec8, i4x8_f16(w[j])), qop[4 * c2 + j], sacc);
+          sacc = M::qk(__builtin_bit_cast(typename M::vec8, kscale(i4x8_f16(w[j]), 4 * c2 + j)), qop[4 * c2 + j], sacc);
       }
     } else {
 #pragma unroll
       for (int c2 = 0; c2 < KCH; ++c2) {
-        sacc = M::qk(__builtin_bit_cast(typename M::vec8, to16<MT, KVT>(t.k[c2].x, t.k[c2].y)), qop[2 * c2], sacc);
-        sacc = M::qk(__builtin_bit_cast(typename M::vec8, to16<MT, KVT>(t.k[c2].z, t.k[c2].w)), qop[2 * c2 + 1],
-                     sacc);
+        sacc = M::qk(__builtin_bit_cast(typename M::vec8, kscale(to16<MT, KVT>(t.k[c2].x, t.k[c2].y), 2 * c2)),
+                     qop[2 * c2], sacc);
+        sacc = M::qk(__builtin_bit_cast(typename M::vec8, kscale(to16<MT, KVT>(t.k[c2].z, t.k[c2].w), 2 * c2 + 1)),
+                     qop[2 * c2 + 1], sacc);
       }
     }
     const float factor = qfactor * t.ks;
@@ -807,8 +852,11 @@ void paged_attn_wave_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m2);
     // P^T as the B operand (tokens 4kg..4kg+3 of head g), V scale folded in
-    const uint32_t p01 = M::pack2(pr[0] * t.vs, pr[1] * t.vs);
-    const uint32_t p23 = M::pack2(pr[2] * t.vs, pr[3] * t.vs);
+    float vsc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vsc[i] = GRP ? t.vts[i] : t.vs;
+    const uint32_t p01 = M::pack2(pr[0] * vsc[0], pr[1] * vsc[1]);
+    const uint32_t p23 = M::pack2(pr[2] * vsc[2], pr[3] * vsc[3]);
     // the denominator sums the weights the MFMA uses (16-bit rounded), so
     // they add up to one; with codes the V scale is not part of the weight
     if constexpr (!kCodes) lsum += M::sum2(p01) + M::sum2(p23);
@@ -1208,17 +1256,18 @@ static AttnParams make_params(const AttnArgs& a) {
   p.qtok = a.qtok > 0 ? a.qtok : 1;
   p.table_bytes = a.selected ? (int)((long long)a.num_seqs * a.num_kv_heads * a.budget * 8)
                              : (int)((long long)a.num_seqs * a.max_blocks_per_seq * 4);
+  p.k_chan = a.k_chan;
   p.scale_log2 = a.sm_scale * kLog2e;
   return p;
 }
 
-template <typename QT, typename KVT, int D, bool STREAM, bool SEL>
+template <typename QT, typename KVT, int D, bool STREAM, bool SEL, bool GRP = false>
 static int launch_wave(const AttnParams& p, int num_slots, hipStream_t st) {
   // (workgroup slot, group of up to 8 KV heads); one wave per KV head
   const int per_group = wave_group_size(p.num_kv_heads);
   const int groups = (p.num_kv_heads + per_group - 1) / per_group;
   const int lds = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, per_group, p.list_cap);
-  auto kernel = paged_attn_wave_kernel<QT, KVT, D, STREAM, SEL>;
+  auto kernel = paged_attn_wave_kernel<QT, KVT, D, STREAM, SEL, GRP>;
   static bool lds_set = false;
   if (!lds_set) {
     // above the default dynamic-LDS limit: the largest group needs ~100 KB
@@ -1259,9 +1308,29 @@ static int launch_simple(const AttnParams& p, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Grouped scales: INT8 (head_dim 64 or 128) and INT4 (head_dim 128) codes.
+template <typename QT>
+static int launch_wave_grouped(const AttnParams& p, int num_slots, int kv_dtype, int D, bool stream,
+                               hipStream_t st) {
+  if (kv_dtype == PKV_I4)
+    return stream ? launch_wave<QT, I4, 128, true, false, true>(p, num_slots, st)
+                  : launch_wave<QT, I4, 128, false, false, true>(p, num_slots, st);
+  if (D == 64)
+    return stream ? launch_wave<QT, I8, 64, true, false, true>(p, num_slots, st)
+                  : launch_wave<QT, I8, 64, false, false, true>(p, num_slots, st);
+  return stream ? launch_wave<QT, I8, 128, true, false, true>(p, num_slots, st)
+                : launch_wave<QT, I8, 128, false, false, true>(p, num_slots, st);
+}
+
 int launch_paged_attn_partition(const AttnArgs& a) {
   if (a.num_seqs == 0) return hipSuccess;
   AttnParams p = make_params(a);
+  if (a.k_chan) {
+    const bool stream = (a.flags & PKV_DECODE_STREAM_KV) != 0;
+    return a.q_dtype == PKV_BF16
+               ? launch_wave_grouped<BF16>(p, a.num_slots, a.kv_dtype, a.head_dim, stream, (hipStream_t)a.stream)
+               : launch_wave_grouped<F16>(p, a.num_slots, a.kv_dtype, a.head_dim, stream, (hipStream_t)a.stream);
+  }
   hipStream_t st = (hipStream_t)a.stream;
   const int D = a.head_dim;
   if (a.kv_dtype == PKV_F32) {

@@ -70,6 +70,9 @@ struct AttnArgs {
   const int32_t* selected;
   int budget;
   int qtok;    // query tokens per sequence (0 or 1: one)
+  // grouped scales: K channel scales [NB][Hkv][D] (k_scales then holds each
+  // tile's largest channel scale) and v_scales per token [NB][Hkv][16]
+  const float* k_chan;
   void* stream;
 };
 
@@ -132,6 +135,9 @@ int launch_quest_select(const void* query, int q_dtype, const void* k_summary, c
                         int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
                         int num_kv_heads, int head_dim, int num_blocks, int budget, int32_t* selected,
                         void* scratch, void* stream);
+int launch_quantize_kv_grouped(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
+                               float* tile_scales, float* group_scales, int group, const int32_t* block_ids,
+                               int n_blocks, int num_blocks, int num_kv_heads, int head_dim, void* stream);
 int launch_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
                        float* dst_scales, const int32_t* block_ids, int n_blocks, int num_blocks,
                        int block_size, int num_kv_heads, int head_dim, void* stream);
