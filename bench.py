@@ -21,6 +21,7 @@ Default workload: Llama-3-8B attention shape (32 query / 8 KV heads, head dim
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -34,13 +35,25 @@ HBM_PEAK_GBPS = 8000.0
 BYTES = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "fp8e4m3": 1, "fp8e5m2": 1, "i4": 0.5}
 CODES = ("i8", "fp8e4m3", "fp8e5m2", "i4")
 
+CODE_NAMES = {"i8": "INT8", "i4": "INT4", "fp8e4m3": "FP8-E4M3", "fp8e5m2": "FP8-E5M2"}
+
+
+def describe(w, grouped=False):
+    """Workload text for the JSON line: the code type and scale layout of
+    quantised workloads filled in."""
+    d = DESCRIPTIONS.get(w.name, w.name)
+    scales = ("keys scaled per (block, kv head, channel), values per (block, kv head, token)" if grouped
+              else "one fp32 scale per (block, kv head)")
+    return d.format(codes=CODE_NAMES.get(w.kv_dtype, w.kv_dtype), scales=scales)
+
+
 DESCRIPTIONS = {
     "llama3_8b_b64": "Llama-3-8B-shaped single-layer paged decode, bf16, batch 64, 32q/8kv heads, d 128, "
                      "block 16, lengths U[512,4096]",
     "shared_prefix_b128": "shared-prefix copy-on-write decode, bf16, batch 128, 64q/8kv, d 128, 1024-token "
                           "shared prefix + suffix U[64,2048]",
-    "quant_kv_32k_b16": "INT8-KV long-context decode, batch 16, 32q/8kv, d 128, 32768 tokens each, "
-                        "one fp32 scale per (block, kv head)",
+    "quant_kv_32k_b16": "{codes}-KV long-context decode, batch 16, 32q/8kv, d 128, 32768 tokens each, "
+                        "{scales}",
     "ctx128k_b4": "128K-context split-K decode, bf16, batch 4, 64q/8kv, d 128, 131072 tokens each, "
                   "512-token partitions",
     "tiny_fp32": "tiny fp32 paged decode, 4 sequences {40,17,64,1}, 8q/2kv, d 64",
@@ -66,6 +79,8 @@ def parse():
                     help="T query tokens per sequence in one pass (checking speculative drafts)")
     ap.add_argument("--quest", type=int, default=0, metavar="PAGES",
                     help="time query-aware page selection reading PAGES pages per (sequence, KV head) instead")
+    ap.add_argument("--grouped", action="store_true",
+                    help="quantised workload with keys scaled per channel and values per token (i8 / i4)")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the secondary 128K-context split-K measurement")
     return ap.parse_args()
@@ -290,7 +305,7 @@ def measure_quest(w, steps, warmup, copies, budget):
         "ms_per_step": round(total_ms / steps, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype,
         "data": "synthetic (seeded N(0,1) keys/values/queries, random block placement)",
-        "config": {"workload": DESCRIPTIONS.get(w.name, w.name) + f", {budget} pages per (sequence, KV head)",
+        "config": {"workload": describe(w) + f", {budget} pages per (sequence, KV head)",
                    "budget_pages": budget, "kv_bytes_read_per_step": int(kv_bytes),
                    "kv_bytes_full_step": int(full_bytes), "summary_bytes_scored": summary_bytes},
         "steps_per_s": round(1000.0 * steps / total_ms, 1),
@@ -371,10 +386,82 @@ def measure_multi(w, steps, warmup, copies, T):
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype,
         "data": "synthetic (seeded N(0,1) keys/values/queries, random block placement)",
-        "config": {"workload": DESCRIPTIONS.get(w.name, w.name) + f", {T} query tokens per sequence",
+        "config": {"workload": describe(w) + f", {T} query tokens per sequence",
                    "query_tokens": T, "kv_bytes_per_step": int(kv_bytes)},
         "attn_us": round(attn_ms * 1e3, 2),
         "attn_kv_gbps": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 2),
+    }
+
+
+def measure_grouped(w, steps, warmup, copies):
+    """Times `steps` decode steps over a cache quantised with grouped scales
+    (keys per channel, values per token): KV-read GB/s, the bytes counting
+    the codes and every scale the step reads."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_466_amd as pkv
+    from gpu_pipeline import GpuRun, cache_shape, uint8_kind
+    from workloads import draw_tensors
+
+    code = w.kv_dtype
+    src_w = dataclasses.replace(w, kv_dtype=w.src_dtype)
+    print(f"[bench] grouped-scale workload={w.name} S={w.S} codes={code}", file=sys.stderr, flush=True)
+    t = draw_tensors(src_w, "cuda")
+    g = GpuRun(src_w, t)
+    used = torch.tensor(sorted({b for tb in g.tables for b in tb}), dtype=torch.int32, device="cuda")
+    shape = cache_shape(w, code)
+    cdt = torch.int8 if code == "i8" else torch.uint8
+
+    def quantised():
+        kc = torch.zeros(shape, dtype=cdt, device="cuda")
+        vc = torch.zeros(shape, dtype=cdt, device="cuda")
+        kg = torch.zeros(w.num_blocks, w.Hkv, w.D, device="cuda")
+        kt = torch.zeros(w.num_blocks, w.Hkv, device="cuda")
+        vg = torch.zeros(w.num_blocks, w.Hkv, 16, device="cuda")
+        pkv.quantize_kv_grouped(g.k_cache, kc, kg, code, pkv.GROUP_CHANNEL, dst_tile_scales=kt, block_ids=used)
+        pkv.quantize_kv_grouped(g.v_cache, vc, vg, code, pkv.GROUP_TOKEN, block_ids=used)
+        return kc, vc, kt, kg, vg
+
+    runs = [quantised() for _ in range(copies)]
+    del g.k_cache, g.v_cache
+    torch.cuda.synchronize()
+    lens = g.lens.cpu().numpy()
+    blocks = int(sum(-(-int(L) // 16) for L in lens))
+    kv_bytes = kv_bytes_per_step(w, lens) - blocks * w.Hkv * 4 * 2 + blocks * w.Hkv * (4 + 4 * w.D + 4 * 16)
+    S, Hq, D = t["query"].shape
+    max_len = g.mbs * 16
+    psize = w.partition_size or pkv.paged_attn_partition_size(code, max_len)
+    nbytes = pkv.paged_attn_workspace_bytes(code, S, Hq, w.Hkv, D, max_len, psize)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["query"])
+    kvdt = uint8_kind(code)
+
+    def step(r):
+        kc, vc, kt, kg, vg = r
+        pkv.paged_attn_decode_grouped(out, t["query"], kc, vc, g.block_tables, g.lens, w.sm_scale, kt, kg, vg,
+                                      partition_size=psize, workspace=ws, kv_dtype=kvdt, stream_kv=True)
+
+    for i in range(warmup):
+        step(runs[i % len(runs)])
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(runs[i % len(runs)])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    return {
+        "metric": "grouped-scale paged decode: KV-read GB/s (codes and scales)",
+        "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": code,
+        "data": "synthetic (seeded N(0,1) keys/values/queries, x8 outlier key channels, random block placement)",
+        "config": {"workload": describe(w, grouped=True),
+                   "kv_bytes_per_step": int(kv_bytes), "partition_size": psize},
+        "frac_of_hbm_peak": round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
     }
 
 
@@ -414,7 +501,8 @@ def main():
     # the 128K split-K measurement runs first, in a child process of its own,
     # so that its multi-GiB allocations start from a fresh device heap
     long_ctx = None
-    if not args.no_long_context and not args.quest and args.query_tokens == 1 and args.workload != "ctx128k_b4":
+    if not args.no_long_context and not args.quest and not args.grouped and args.query_tokens == 1 \
+            and args.workload != "ctx128k_b4":
         long_ctx = long_context_entry(min(args.steps, 50), min(args.warmup, 20))
 
     from workloads import get_workload
@@ -425,6 +513,9 @@ def main():
     if args.partition_size:
         ov["partition_size"] = args.partition_size
     w = get_workload(args.workload, streaming=args.streaming, **ov)
+    if args.grouped:
+        print(json.dumps(measure_grouped(w, args.steps, args.warmup, args.copies)), flush=True)
+        return
     if args.quest:
         print(json.dumps(measure_quest(w, args.steps, args.warmup, args.copies, args.quest)), flush=True)
         return
@@ -449,7 +540,7 @@ def main():
         "dtype": w.kv_dtype,
         "data": "synthetic (seeded N(0,1) keys/values/queries, random block placement)",
         "config": {
-            "workload": DESCRIPTIONS.get(w.name, w.name) + (" + StreamingLLM 4+4092 mask" if w.sink else ""),
+            "workload": describe(w) + (" + StreamingLLM 4+4092 mask" if w.sink else ""),
             "num_seqs": m["S"], "num_q_heads": m["Hq"], "num_kv_heads": w.Hkv, "head_dim": m["D"],
             "block_size": 16, "seq_len_mean": float(lens.mean()), "seq_len_max": int(lens.max()),
             "kv_dtype": w.kv_dtype, "partition_size": m["psize"], "kv_bytes_per_step": int(kv_bytes),

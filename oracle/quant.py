@@ -203,3 +203,14 @@ def dequantize_grouped(code_values, scales, group):
     cv = np.asarray(code_values, dtype=np.float32)
     sc = np.asarray(scales, dtype=np.float32)
     return dequantize(cv, sc[None, :] if group == "channel" else sc[:, None])
+
+
+def requantize_tail_grouped(tail_vals, rows, code_dtype, group):
+    """``requantize_tail`` with grouped scales: the block quantised from its
+    first ``rows`` written rows (the others taken as zeros) with one scale
+    per channel ("channel") or per token row ("token").  Returns (codes of
+    one block, group scales [Hkv, D] or [Hkv, BS], tile scales [Hkv])."""
+    t = np.array(tail_vals, dtype=np.float32)
+    t[rows:] = 0.0
+    codes, gs, ts = quantize_cache_blocks_grouped(t[None], code_dtype, group)
+    return codes[0], gs[0], ts[0]

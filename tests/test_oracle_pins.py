@@ -507,3 +507,35 @@ def test_grouped_decode_reduces_to_tile_decode_when_all_groups_share_the_range()
     a = attention.paged_decode_grouped(q, "f32", kc, vc, "i8", tables, lens, BS, 0.2, kg, vg)
     b = attention.paged_decode(q, "f32", kc1, vc1, "i8", tables, lens, BS, 0.2, ks1, vs1)
     assert (a == b).all()
+
+
+@pytest.mark.parametrize("code", ["i8", "i4"])
+@pytest.mark.parametrize("group", ["channel", "token"])
+def test_grouped_requantisation_ends_at_the_whole_block(code, group):
+    """A block filled one token at a time with grouped scales ends with the
+    codes and scales of quantising it whole.  Token groups: appending a row
+    never changes an earlier row's codes or scale.  Channel groups: each
+    channel's scale is the running absmax of its written rows over the
+    largest code."""
+    rng = np.random.default_rng(45)
+    tile = rng.standard_normal((16, 2, 32)).astype(np.float32)
+    tile[:, 0, 7] *= 8.0
+    qmax = 127 if code == "i8" else 7
+    prev = None
+    for rows in range(1, 17):
+        codes, gs, ts = quant.requantize_tail_grouped(tile, rows, code, group)
+        assert not codecs.decode(codes[rows:], code).any()
+        assert (ts == gs.max(axis=1)).all()
+        if group == "token":
+            assert not gs[:, rows:].any()
+            if prev is not None:
+                pc, pg = prev
+                assert (codecs.decode(codes[:rows - 1], code) == codecs.decode(pc[:rows - 1], code)).all()
+                assert (gs[:, :rows - 1] == pg[:, :rows - 1]).all()
+        else:
+            run_max = np.abs(tile[:rows]).max(axis=0)                         # [Hkv, D]
+            assert (gs == (run_max / np.float32(qmax)).astype(np.float32)).all()
+        prev = (codes, gs)
+    whole, wgs, wts = quant.quantize_cache_blocks_grouped(tile[None], code, group)
+    assert codes.tobytes() == whole[0].tobytes()
+    assert (gs.view(np.uint32) == wgs[0].view(np.uint32)).all() and (ts == wts[0]).all()
