@@ -463,6 +463,23 @@ pkv_status pkv_append_kv_quantized(const void* key, const void* value, int src_d
                                    const int32_t* positions, int num_seqs, int num_blocks, int block_size,
                                    int num_kv_heads, int head_dim, void* stream);
 
+/*
+ * pkv_append_kv_quantized for a cache with grouped scales (the layout of
+ * pkv_quantize_kv_grouped): the block is quantised again from the tail with
+ * keys scaled per channel (k_channel_scales [num_blocks][num_kv_heads]
+ * [head_dim], their largest into k_tile_scales [num_blocks][num_kv_heads])
+ * and values per token (v_token_scales [num_blocks][num_kv_heads]
+ * [block_size]).  A token group depends on its own row only, so appending
+ * leaves earlier rows' value codes and scales as they were.  Bit-exact.
+ */
+pkv_status pkv_append_kv_quantized_grouped(const void* key, const void* value, int src_dtype,
+                                           void* k_tail, void* v_tail, void* k_codes, void* v_codes,
+                                           int code_dtype, float* k_tile_scales, float* k_channel_scales,
+                                           float* v_token_scales, const int32_t* block_tables,
+                                           int max_blocks_per_seq, const int32_t* positions, int num_seqs,
+                                           int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                                           void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host-side checks                                                          */
 /* ------------------------------------------------------------------------ */

@@ -16,7 +16,8 @@ __all__ = [
     "paged_attn_decode", "paged_attn_partition", "paged_attn_merge",
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
     "paged_attn_decode_multi", "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
-    "paged_attn_decode_grouped", "quantize_kv_grouped", "GROUP_CHANNEL", "GROUP_TOKEN",
+    "paged_attn_decode_grouped", "quantize_kv_grouped", "append_kv_quantized_grouped", "GROUP_CHANNEL",
+    "GROUP_TOKEN",
     "slot_mapping", "reshape_and_cache", "append_kv", "append_kv_quantized", "copy_blocks", "quantize_kv",
     "validate_tables", "BlockPool", "PrefixCache", "h2o_retain", "DTYPES",
 ]
@@ -61,6 +62,8 @@ _SIGS = {
                                         ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_grouped": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                        _i, ctypes.c_uint, _p, _sz, _p], _i),
+    "pkv_append_kv_quantized_grouped": ([_p, _p, _i, _p, _p, _p, _p, _i, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i,
+                                         _p], _i),
     "pkv_quantize_kv_grouped": ([_p, _i, _p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p], _i),
     "pkv_quest_summarize": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p], _i),
     "pkv_quest_scratch_bytes": ([_i, _i, _i], _sz),
@@ -396,6 +399,27 @@ def append_kv_quantized(key, value, k_tail, v_tail, k_codes, v_codes, k_scales, 
                                        _ptr(k_codes), _ptr(v_codes), DTYPES[code_dtype], _ptr(k_scales),
                                        _ptr(v_scales), _ptr(block_tables), block_tables.shape[1], _ptr(positions),
                                        S, NB, BS, Hkv, D, _stream(key)))
+
+
+def append_kv_quantized_grouped(key, value, k_tail, v_tail, k_codes, v_codes, k_tile_scales, k_channel_scales,
+                                v_token_scales, block_tables, positions, code_dtype):
+    """``append_kv_quantized`` for a grouped-scale cache
+    (``pkv_append_kv_quantized_grouped``): keys per channel, values per token."""
+    _contig(key, value, k_tail, v_tail, k_codes, v_codes, k_tile_scales, k_channel_scales, v_token_scales,
+            block_tables, positions)
+    S, Hkv, D = key.shape
+    NB, BS = k_codes.shape[:2]
+    if tuple(k_tail.shape) != (S, BS, Hkv, D) or k_tail.dtype != key.dtype or value.shape != key.shape:
+        raise ValueError("tails must be [S, block_size, Hkv, D] of the key dtype")
+    if _head_dim(k_codes, DTYPES[code_dtype]) != D or k_codes.shape != v_codes.shape:
+        raise ValueError("codes must be [NB, block_size, Hkv, D] (D / 2 bytes for i4)")
+    if tuple(k_channel_scales.shape) != (NB, Hkv, D) or tuple(v_token_scales.shape) != (NB, Hkv, BS) \
+            or tuple(k_tile_scales.shape) != (NB, Hkv):
+        raise ValueError("scales must be [NB, Hkv] (tile), [NB, Hkv, D] (channel) and [NB, Hkv, 16] (token)")
+    _check(lib.pkv_append_kv_quantized_grouped(
+        _ptr(key), _ptr(value), _dtype(key), _ptr(k_tail), _ptr(v_tail), _ptr(k_codes), _ptr(v_codes),
+        DTYPES[code_dtype], _ptr(k_tile_scales), _ptr(k_channel_scales), _ptr(v_token_scales), _ptr(block_tables),
+        block_tables.shape[1], _ptr(positions), S, NB, BS, Hkv, D, _stream(key)))
 
 
 def copy_blocks(k_cache, v_cache, src_dst, k_scales=None, v_scales=None, dtype=None):

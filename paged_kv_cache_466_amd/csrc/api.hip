@@ -579,8 +579,32 @@ extern "C" pkv_status pkv_append_kv_quantized(const void* key, const void* value
       !positions)
     return fail(PKV_EINVAL, "%s: null pointer", who);
   return hip_status(launch_append_quantized(key, value, src_dtype, k_tail, v_tail, k_codes, v_codes, code_dtype,
-                                            k_scales, v_scales, block_tables, max_blocks_per_seq, positions,
-                                            num_seqs, num_blocks, num_kv_heads, head_dim, stream),
+                                            k_scales, v_scales, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                                            positions, num_seqs, num_blocks, num_kv_heads, head_dim, stream),
+                    who);
+}
+
+extern "C" pkv_status pkv_append_kv_quantized_grouped(
+    const void* key, const void* value, int src_dtype, void* k_tail, void* v_tail, void* k_codes, void* v_codes,
+    int code_dtype, float* k_tile_scales, float* k_channel_scales, float* v_token_scales,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions, int num_seqs, int num_blocks,
+    int block_size, int num_kv_heads, int head_dim, void* stream) {
+  const char* who = "pkv_append_kv_quantized_grouped";
+  pkv_status st = check_cache_shape(who, block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (!is_float_storage(src_dtype)) return fail(PKV_EUNSUPPORTED, "%s: source must be f32/bf16/f16", who);
+  if (!is_code_storage(code_dtype))
+    return fail(PKV_EUNSUPPORTED, "%s: codes must be i8, i4, fp8e4m3 or fp8e5m2", who);
+  if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0) return fail(PKV_EINVAL, "%s: negative size", who);
+  if (num_seqs == 0) return PKV_OK;
+  if (num_kv_heads > 65535) return fail(PKV_EUNSUPPORTED, "%s: shape too large", who);
+  if (!key || !value || !k_tail || !v_tail || !k_codes || !v_codes || !k_tile_scales || !k_channel_scales ||
+      !v_token_scales || !block_tables || !positions)
+    return fail(PKV_EINVAL, "%s: null pointer", who);
+  return hip_status(launch_append_quantized(key, value, src_dtype, k_tail, v_tail, k_codes, v_codes, code_dtype,
+                                            k_tile_scales, nullptr, k_channel_scales, v_token_scales, block_tables,
+                                            max_blocks_per_seq, positions, num_seqs, num_blocks, num_kv_heads,
+                                            head_dim, stream),
                     who);
 }
 

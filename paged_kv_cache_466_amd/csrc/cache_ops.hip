@@ -437,14 +437,16 @@ int launch_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes, in
 // zeros.  One wave per (sequence, KV head, K or V), with quantize_kv's lane
 // layout (lane l: token row l/4, quarter l%4 of the head dimension) and the
 // same arithmetic, so a full block ends with exactly quantize_kv's codes.
+// GRP: grouped scales (keys per channel into k_group and their largest into
+// k_scales, values per token into v_group), quantize_kv_grouped's arithmetic.
 // ---------------------------------------------------------------------------
-template <typename SRC, int D, int CODE>
+template <typename SRC, int D, int CODE, bool GRP>
 __global__ __launch_bounds__(64) void append_quantized_kernel(
     const typename SRC::raw* __restrict__ key, const typename SRC::raw* __restrict__ value,
     typename SRC::raw* __restrict__ k_tail, typename SRC::raw* __restrict__ v_tail, uint8_t* __restrict__ k_codes,
     uint8_t* __restrict__ v_codes, float* __restrict__ k_scales, float* __restrict__ v_scales,
-    const int32_t* __restrict__ tables, int mbs, const int32_t* __restrict__ positions, int num_blocks,
-    int num_kv_heads) {
+    float* __restrict__ k_group, float* __restrict__ v_group, const int32_t* __restrict__ tables, int mbs,
+    const int32_t* __restrict__ positions, int num_blocks, int num_kv_heads) {
   constexpr int BS = 16;
   constexpr int ELEMS = D / 4;                 // per lane
   constexpr int SRC_CHUNKS = ELEMS * SRC::bytes / 16;
@@ -478,29 +480,43 @@ __global__ __launch_bounds__(64) void append_quantized_kernel(
 #pragma unroll
     for (int i = 0; i < ELEMS; ++i) x[i] = 0.f;
   }
-  float a = 0.f;
-#pragma unroll
-  for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
-  a = wave_max(a);
-  const float sc = __fdiv_rn(a, CodeTraits<CODE>::qmax);
-  float scv[ELEMS];
-#pragma unroll
-  for (int i = 0; i < ELEMS; ++i) scv[i] = sc;
   uint8_t* dst = is_v ? v_codes : k_codes;
-  encode_store<CODE, ELEMS>(x, scv, dst + (((size_t)b * BS + t) * num_kv_heads + h) * ROWB + q * (ROWB / 4));
-  if (lane == 0) (is_v ? v_scales : k_scales)[(size_t)b * num_kv_heads + h] = sc;
+  float scv[ELEMS];
+  if constexpr (GRP) {
+    const size_t tile = (size_t)b * num_kv_heads + h;
+    if (is_v) {
+      (void)group_scales<CODE, kGroupToken, ELEMS>(x, scv);
+      store_group_scales<kGroupToken, D>(v_group + tile * BS, scv, t, q);
+    } else {
+      const float smax = group_scales<CODE, kGroupChannel, ELEMS>(x, scv);
+      store_group_scales<kGroupChannel, D>(k_group + tile * D, scv, t, q);
+      if (lane == 0) k_scales[tile] = smax;
+    }
+    encode_store<CODE, ELEMS>(x, scv, dst + (((size_t)b * BS + t) * num_kv_heads + h) * ROWB + q * (ROWB / 4));
+  } else {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < ELEMS; ++i) a = fmaxf(a, fabsf(x[i]));
+    a = wave_max(a);
+    const float sc = __fdiv_rn(a, CodeTraits<CODE>::qmax);
+#pragma unroll
+    for (int i = 0; i < ELEMS; ++i) scv[i] = sc;
+    encode_store<CODE, ELEMS>(x, scv, dst + (((size_t)b * BS + t) * num_kv_heads + h) * ROWB + q * (ROWB / 4));
+    if (lane == 0) (is_v ? v_scales : k_scales)[(size_t)b * num_kv_heads + h] = sc;
+  }
 }
 
-template <typename SRC, int D>
+template <typename SRC, int D, bool GRP>
 static int launch_aq(const void* key, const void* value, void* k_tail, void* v_tail, void* k_codes, void* v_codes,
-                     int code_dtype, float* k_scales, float* v_scales, const int32_t* tables, int mbs,
-                     const int32_t* positions, int num_seqs, int num_blocks, int num_kv_heads, hipStream_t st) {
+                     int code_dtype, float* k_scales, float* v_scales, float* k_group, float* v_group,
+                     const int32_t* tables, int mbs, const int32_t* positions, int num_seqs, int num_blocks,
+                     int num_kv_heads, hipStream_t st) {
   typedef typename SRC::raw R;
   const dim3 grid(num_seqs, num_kv_heads, 2);
 #define PKV_AQK(CODE)                                                                                      \
-  append_quantized_kernel<SRC, D, CODE><<<grid, 64, 0, st>>>(                                              \
+  append_quantized_kernel<SRC, D, CODE, GRP><<<grid, 64, 0, st>>>(                                         \
       (const R*)key, (const R*)value, (R*)k_tail, (R*)v_tail, (uint8_t*)k_codes, (uint8_t*)v_codes, k_scales, \
-      v_scales, tables, mbs, positions, num_blocks, num_kv_heads)
+      v_scales, k_group, v_group, tables, mbs, positions, num_blocks, num_kv_heads)
   if (code_dtype == PKV_FP8E4M3) PKV_AQK(kCodeFP8);
   else if (code_dtype == PKV_FP8E5M2) PKV_AQK(kCodeBF8);
   else if (code_dtype == PKV_I4) PKV_AQK(kCodeI4);
@@ -509,25 +525,32 @@ static int launch_aq(const void* key, const void* value, void* k_tail, void* v_t
   return hipGetLastError();
 }
 
+// k_group / v_group non-null: grouped scales (k_scales takes the tiles'
+// largest channel scales, v_scales is unused).
 int launch_append_quantized(const void* key, const void* value, int src_dtype, void* k_tail, void* v_tail,
                             void* k_codes, void* v_codes, int code_dtype, float* k_scales, float* v_scales,
-                            const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
-                            int num_seqs, int num_blocks, int num_kv_heads, int head_dim, void* stream) {
+                            float* k_group, float* v_group, const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* positions, int num_seqs, int num_blocks, int num_kv_heads, int head_dim,
+                            void* stream) {
   hipStream_t st = (hipStream_t)stream;
-#define PKV_AQ(SRC)                                                                                          \
-  return head_dim == 64                                                                                      \
-             ? launch_aq<SRC, 64>(key, value, k_tail, v_tail, k_codes, v_codes, code_dtype, k_scales,        \
-                                  v_scales, block_tables, max_blocks_per_seq, positions, num_seqs, num_blocks, \
-                                  num_kv_heads, st)                                                          \
-             : launch_aq<SRC, 128>(key, value, k_tail, v_tail, k_codes, v_codes, code_dtype, k_scales,       \
-                                   v_scales, block_tables, max_blocks_per_seq, positions, num_seqs,          \
-                                   num_blocks, num_kv_heads, st)
+#define PKV_AQD(SRC, D, GRP)                                                                                  \
+  return launch_aq<SRC, D, GRP>(key, value, k_tail, v_tail, k_codes, v_codes, code_dtype, k_scales, v_scales, \
+                                k_group, v_group, block_tables, max_blocks_per_seq, positions, num_seqs,      \
+                                num_blocks, num_kv_heads, st)
+#define PKV_AQ(SRC)                                  \
+  if (k_group) {                                     \
+    if (head_dim == 64) PKV_AQD(SRC, 64, true);      \
+    PKV_AQD(SRC, 128, true);                         \
+  }                                                  \
+  if (head_dim == 64) PKV_AQD(SRC, 64, false);       \
+  PKV_AQD(SRC, 128, false)
   switch (src_dtype) {
-    case PKV_F32: PKV_AQ(F32);
-    case PKV_BF16: PKV_AQ(BF16);
-    default: PKV_AQ(F16);
+    case PKV_F32: { PKV_AQ(F32); }
+    case PKV_BF16: { PKV_AQ(BF16); }
+    default: { PKV_AQ(F16); }
   }
 #undef PKV_AQ
+#undef PKV_AQD
 }
 
 }  // namespace pkv

@@ -126,8 +126,9 @@ int launch_copy_blocks(void* k_cache, void* v_cache, float* k_scales, float* v_s
                        int num_kv_heads, int head_dim, void* stream);
 int launch_append_quantized(const void* key, const void* value, int src_dtype, void* k_tail, void* v_tail,
                             void* k_codes, void* v_codes, int code_dtype, float* k_scales, float* v_scales,
-                            const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
-                            int num_seqs, int num_blocks, int num_kv_heads, int head_dim, void* stream);
+                            float* k_group, float* v_group, const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* positions, int num_seqs, int num_blocks, int num_kv_heads, int head_dim,
+                            void* stream);
 int launch_quest_summarize(const void* k_cache, int kv_dtype, void* k_summary, const int32_t* block_tables,
                            int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_blocks,
                            int num_kv_heads, int head_dim, int last_only, void* stream);

@@ -6,7 +6,10 @@ against ``oracle/quant.py`` and ``oracle/attention.py``:
   used block bit-exact against ``quant.quantize_cache_blocks_grouped``;
 * ``pkv_paged_attn_decode_grouped``: within 2e-2 of the oracle's float64
   attention over the same dequantised values, with the last blocks partly
-  masked (lengths cut below the written rows) and with the split decode.
+  masked (lengths cut below the written rows) and with the split decode;
+* ``pkv_append_kv_quantized_grouped``: codes and scales of every written
+  block bit-exact against ``quant.requantize_tail_grouped`` after checked
+  steps of a token-by-token fill, and the decode over the growing cache.
 """
 
 import numpy as np
@@ -14,6 +17,7 @@ import pytest
 import torch
 
 from oracle import attention, codecs, quant
+from test_gpu_quant_append import src_values
 from oracle_pipeline import OracleRun, to_raw
 from workloads import draw_tensors, get_workload
 
@@ -122,3 +126,65 @@ def test_grouped_scales_track_the_source_closer_than_one_scale():
     e_tile = float(np.abs(out1.float().cpu().numpy() - src).mean())
     print(f"[grouped] mean |error| vs source values: grouped {e_grouped:.4e}, one scale {e_tile:.4e}")
     assert e_grouped < e_tile
+
+
+@pytest.mark.parametrize("code,src,D,Hkv", [("i8", "bf16", 128, 4), ("i4", "f16", 128, 2), ("i8", "f16", 64, 2)])
+def test_grouped_append_token_by_token(code, src, D, Hkv):
+    import paged_kv_cache_466_amd as pkv
+    TORCH = {"bf16": torch.bfloat16, "f16": torch.float16}
+    rng = np.random.default_rng(47)
+    S, G, T, BS = 3, 4, 37, 16
+    Hq = Hkv * G
+    mbs = (T + BS - 1) // BS
+    NB = S * mbs + 2
+    tables = rng.permutation(NB).astype(np.int32)[: S * mbs].reshape(S, mbs)
+    bt = torch.from_numpy(tables.copy()).cuda()
+    row_bytes = D // 2 if code == "i4" else D
+    cdt = torch.int8 if code == "i8" else torch.uint8
+    poison = -128 if code == "i8" else 0x88
+    kc = torch.full((NB, BS, Hkv, row_bytes), poison, dtype=cdt, device="cuda")
+    vc = torch.full_like(kc, poison)
+    kt = torch.full((NB, Hkv), float("nan"), device="cuda")
+    kg = torch.full((NB, Hkv, D), float("nan"), device="cuda")
+    vg = torch.full((NB, Hkv, BS), float("nan"), device="cuda")
+    k_tail = torch.full((S, BS, Hkv, D), float("nan"), dtype=TORCH[src], device="cuda")
+    v_tail = torch.full_like(k_tail, float("nan"))
+    o_kc = np.full((NB, BS, Hkv, row_bytes), poison, dtype=np.int8 if code == "i8" else np.uint8)
+    o_vc = o_kc.copy()
+    o_kt = np.zeros((NB, Hkv), np.float32)
+    o_kg = np.zeros((NB, Hkv, D), np.float32)
+    o_vg = np.zeros((NB, Hkv, BS), np.float32)
+    o_ktail = np.zeros((S, BS, Hkv, D), np.float32)
+    o_vtail = np.zeros((S, BS, Hkv, D), np.float32)
+    sm = np.float32(1.0 / np.sqrt(D))
+    worst = 0.0
+    for step in range(T):
+        k_new, k_val = src_values(rng, (S, Hkv, D), src, outliers=True)
+        v_new, v_val = src_values(rng, (S, Hkv, D), src)
+        pos = torch.full((S,), step, dtype=torch.int32, device="cuda")
+        pkv.append_kv_quantized_grouped(k_new, v_new, k_tail, v_tail, kc, vc, kt, kg, vg, bt, pos, code)
+        row, lb = step % BS, step // BS
+        for s_ in range(S):
+            b = tables[s_, lb]
+            o_ktail[s_, row], o_vtail[s_, row] = k_val[s_], v_val[s_]
+            o_kc[b], o_kg[b], o_kt[b] = quant.requantize_tail_grouped(o_ktail[s_], row + 1, code, "channel")
+            o_vc[b], o_vg[b], _ = quant.requantize_tail_grouped(o_vtail[s_], row + 1, code, "token")
+        if step not in (0, 6, 15, 16, T - 1):
+            continue
+        used = tables[:, : lb + 1].reshape(-1)
+        assert to_raw(kc, code)[used].tobytes() == o_kc[used].tobytes(), step
+        assert to_raw(vc, code)[used].tobytes() == o_vc[used].tobytes(), step
+        assert (kt.cpu().numpy()[used].view(np.uint32) == o_kt[used].view(np.uint32)).all(), step
+        assert (kg.cpu().numpy()[used].view(np.uint32) == o_kg[used].view(np.uint32)).all(), step
+        assert (vg.cpu().numpy()[used].view(np.uint32) == o_vg[used].view(np.uint32)).all(), step
+        q, _ = src_values(rng, (S, Hq, D), src)
+        lens = torch.full((S,), step + 1, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(q)
+        pkv.paged_attn_decode_grouped(out, q, kc, vc, bt, lens, float(sm), kt, kg, vg,
+                                      kv_dtype=None if code == "i8" else code)
+        ref = attention.paged_decode_grouped(to_raw(q, src), src, o_kc, o_vc, code, tables, [step + 1] * S, BS, sm,
+                                             o_kg, o_vg)
+        err = float(np.abs(out.float().cpu().numpy() - ref).max())
+        worst = max(worst, err)
+        assert err <= TOL, (step, err)
+    print(f"[grouped-append] {code} {src} D={D} Hkv={Hkv} max_abs_err={worst:.3e}")
