@@ -79,6 +79,8 @@ def parse():
                     help="T query tokens per sequence in one pass (checking speculative drafts)")
     ap.add_argument("--quest", type=int, default=0, metavar="PAGES",
                     help="time query-aware page selection reading PAGES pages per (sequence, KV head) instead")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from HIP graphs (reported as graph_ms_per_step)")
     ap.add_argument("--grouped", action="store_true",
                     help="quantised workload with keys scaled per channel and values per token (i8 / i4)")
     ap.add_argument("--no-long-context", action="store_true",
@@ -86,16 +88,19 @@ def parse():
     return ap.parse_args()
 
 
+# the sources the decode kernels are built from
+KERNEL_SOURCES = ("paged_attn.hip", "pkv_device.h", "pkv_internal.h")
+
+
 def csrc_hash():
-    """sha1 (first 12 hex digits) of the kernel sources, in sorted file order:
-    the key under which profiles/traffic.json stores HBM traffic."""
+    """sha1 (first 12 hex digits) of the decode kernels' sources, in this
+    order: the key under which profiles/traffic.json stores HBM traffic."""
     import hashlib
     d = os.path.join(ROOT, "paged_kv_cache_466_amd", "csrc")
     h = hashlib.sha1()
-    for fn in sorted(os.listdir(d)):
-        if fn.endswith((".hip", ".h", ".cpp")):
-            h.update(fn.encode())
-            h.update(open(os.path.join(d, fn), "rb").read())
+    for fn in KERNEL_SOURCES:
+        h.update(fn.encode())
+        h.update(open(os.path.join(d, fn), "rb").read())
     return h.hexdigest()[:12]
 
 
@@ -134,7 +139,7 @@ def kv_bytes_per_step(w, lens):
     return total
 
 
-def measure(w, steps, warmup, copies):
+def measure(w, steps, warmup, copies, graph=False):
     """Times `steps` decode steps of workload `w` (inputs resident in HBM,
     `copies` cache copies rotated so the last-level cache cannot hold them).
     Returns the timings and the state the CPU baseline needs."""
@@ -209,11 +214,36 @@ def measure(w, steps, warmup, copies):
     total_ms = start.elapsed_time(stop)
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    # the same steps replayed from HIP graphs, one per cache copy (a serving
+    # loop captures its decode step once); the library enqueues no memset,
+    # allocation or synchronisation, so a step captures as its kernels
+    graph_ms = None
+    if graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in runs:
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=side):
+                    step(r)
+                graphs.append(gr)
+        torch.cuda.current_stream().wait_stream(side)
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        stop.record()
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(stop) / steps
     return {
         "w": w, "t": t, "lens": lens, "kv_bytes": kv_bytes, "psize": psize, "S": S, "Hq": Hq, "D": D,
         "ms_per_step": total_ms / steps, "part_ms": float(part_ms.mean()), "merge_ms": float(merge_ms.mean()),
         "attn_ms": float((part_ms + merge_ms).mean()), "wall": wall, "copies": len(runs),
-        "stream_kv": stream_kv,
+        "stream_kv": stream_kv, "graph_ms": graph_ms,
     }
 
 
@@ -522,7 +552,7 @@ def main():
     if args.query_tokens > 1:
         print(json.dumps(measure_multi(w, args.steps, args.warmup, args.copies, args.query_tokens)), flush=True)
         return
-    m = measure(w, args.steps, args.warmup, args.copies)
+    m = measure(w, args.steps, args.warmup, args.copies, graph=args.graph)
     kv_bytes, ms = m["kv_bytes"], m["ms_per_step"]
     value = kv_bytes / (ms * 1e-3) / 1e9
     lens = m["lens"]
@@ -553,6 +583,7 @@ def main():
         "merge_us": round(m["merge_ms"] * 1e3, 2),
         "attn_kv_gbps": round(kv_bytes / (m["attn_ms"] * 1e-3) / 1e9, 2),
         "wall_s": round(m["wall"], 3),
+        "graph_ms_per_step": None if m["graph_ms"] is None else round(m["graph_ms"], 5),
         "roofline": roofline(m),
     }
     if not args.no_cpu_baseline:
