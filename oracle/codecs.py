@@ -6,9 +6,9 @@ Serving", section "The cache formula", fixes two bytes per value for BF16 and
 one for FP8; section 8 "Quantization" describes storing a small code plus a
 scale.  The FP8 flavours here are OCP E4M3 (the "fn" variant: no infinities,
 one NaN pattern per sign) and OCP E5M2 (IEEE-like: infinities and NaNs in
-the top exponent), the two FP8 formats the gfx950 converts in hardware;
-"LLM Inference Optimization", section "vLLM", stores the cache as
-``fp8_e5m2``.
+the top exponent), the two FP8 formats the gfx950 converts in hardware; "Chapter 18 -
+KV-Cache Optimization Strategies", section "vLLM with PagedAttention + KV
+Quantization", stores the cache as ``fp8_e5m2``.
 
 Nothing here rounds except the two FP8 encoders; every decoder is exact.
 """

@@ -11,9 +11,10 @@ Quantization", lists INT8 storage at one byte per value.
 
 FP8 storage follows the same rule with the format's largest finite magnitude
 as the largest code (448 for E4M3, 57344 for E5M2) and FP8
-round-to-nearest-even in place of integer rounding.  (The pages' vLLM example
-names an ``fp8_e5m2`` cache without saying how it is scaled; this takes the
-same per-tile absmax scale as the other formats.)
+round-to-nearest-even in place of integer rounding.  ("Chapter 18", section
+"vLLM with PagedAttention + KV Quantization", names an ``fp8_e5m2`` cache
+without saying how it is scaled; this takes the same per-tile absmax scale
+as the other formats.)
 
 Group: one scale per (physical block, KV head) over the ``[block_size, d_k]``
 tile, separately for K and V.

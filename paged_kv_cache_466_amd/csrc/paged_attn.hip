@@ -200,6 +200,29 @@ __device__ __forceinline__ uint4 i4x8_f16(uint32_t w) {
   return make_uint4(pair(a, 0x04010400u), pair(a, 0x04030402u), pair(b, 0x04010400u), pair(b, 0x04030402u));
 }
 
+// Eight INT4 codes -> eight f16 values, exactly, in the interleaved order
+// (0, 4, 1, 5, 2, 6, 3, 7): the nibbles at bits s and s + 16 of w >> s
+// (s = 0, 4, 8, 12) are elements s/4 and s/4 + 4.  Masking them to the low
+// bits of each half, flipping bit 3 (u = code + 8) and setting the 0x64
+// byte is one three-input bit operation; the f16 1024 + u minus 1032 is the
+// code.  Three operations per pair fewer than the in-order conversion; the
+// query's elements and the staged V rows use the same order.
+__device__ __forceinline__ uint4 i4x8_f16_il(uint32_t w) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  auto pair = [](uint32_t x) {
+    const uint32_t b = (x & 0x000F000Fu) ^ 0x64086408u;
+    const h2 v = __builtin_bit_cast(h2, b) - h2{(_Float16)1032.0f, (_Float16)1032.0f};
+    return __builtin_bit_cast(uint32_t, v);
+  };
+  return make_uint4(pair(w), pair(w >> 4), pair(w >> 8), pair(w >> 12));
+}
+
+// (q0..q7) -> (q0, q4, q1, q5, q2, q6, q3, q7): 16-bit elements of a uint4
+__device__ __forceinline__ uint4 interleave8(uint4 q) {
+  return make_uint4(__builtin_amdgcn_perm(q.z, q.x, 0x05040100u), __builtin_amdgcn_perm(q.z, q.x, 0x07060302u),
+                    __builtin_amdgcn_perm(q.w, q.y, 0x05040100u), __builtin_amdgcn_perm(q.w, q.y, 0x07060302u));
+}
+
 // 8 codes -> 8 elements of the MFMA type, exactly (every INT8 value is an f16
 // value; every finite FP8-E4M3 and FP8-E5M2 value is a bf16 and an f16 value).
 template <typename MT, typename KVT>
@@ -474,6 +497,11 @@ void paged_attn_wave_kernel(AttnParams p) {
   typedef Mfma<QT> MO;    // the output type
   constexpr int NC = C::NC, NN = C::NN, KCH = C::KCH, VCH = C::VCH, DEPTH = C::DEPTH;
   constexpr bool kCodes = C::kCodes;
+  // INT4: key and value elements come out of the conversion interleaved
+  // within each group of 8 (i4x8_f16_il): the query operand is interleaved to
+  // match, and the staged V rows hold interleaved columns, put back in order
+  // when the results leave LDS
+  constexpr bool kIL = KVT::bits == 4;
   // the query is rescaled into f16 (INT8 caches with a bf16 query)
   constexpr bool kRescaleQ = !std::is_same<MT, QT>::value;
   // Scores may exceed the running max by this much (log2 units) before the
@@ -682,6 +710,11 @@ void paged_attn_wave_kernel(AttnParams p) {
         qop[c] = __builtin_bit_cast(typename M::vec8, w);
       }
     }
+    if constexpr (kIL) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        qop[c] = __builtin_bit_cast(typename M::vec8, interleave8(__builtin_bit_cast(uint4, qop[c])));
+    }
     m2 = -INFINITY;
     lsum = 0.f;
 #pragma unroll
@@ -728,15 +761,30 @@ void paged_attn_wave_kernel(AttnParams p) {
           const float* src = rl + (c / CPR) * RSTRIDE + (c % CPR) * 8;
           const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
           const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
+          // interleaved columns: positions (0..7) hold elements (0, 4, 1, 5, 2, 6, 3, 7)
           *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + qrow(seq, h0 + c / CPR) * D + (c % CPR) * 8) =
-              make_uint4(MO::pack2(lo[0], lo[1]), MO::pack2(lo[2], lo[3]), MO::pack2(hi[0], hi[1]),
-                         MO::pack2(hi[2], hi[3]));
+              kIL ? make_uint4(MO::pack2(lo[0], lo[2]), MO::pack2(hi[0], hi[2]), MO::pack2(lo[1], lo[3]),
+                               MO::pack2(hi[1], hi[3]))
+                  : make_uint4(MO::pack2(lo[0], lo[1]), MO::pack2(lo[2], lo[3]), MO::pack2(hi[0], hi[1]),
+                               MO::pack2(hi[2], hi[3]));
         }
       } else if (p.ws) {
-        constexpr int CPR = D / 4;
-        for (int c = lane; c < nh * CPR; c += 64)
-          *reinterpret_cast<floatx4*>(rec + (size_t)h0 * D + 4 * c) =
-              *reinterpret_cast<const floatx4*>(rl + (c / CPR) * RSTRIDE + (c % CPR) * 4);
+        if constexpr (kIL) {
+          constexpr int CPR = D / 8;
+          for (int c = lane; c < nh * CPR; c += 64) {
+            const float* src = rl + (c / CPR) * RSTRIDE + (c % CPR) * 8;
+            const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
+            const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
+            float* dst = rec + (size_t)h0 * D + 8 * c;
+            *reinterpret_cast<floatx4*>(dst) = floatx4{lo[0], lo[2], hi[0], hi[2]};
+            *reinterpret_cast<floatx4*>(dst + 4) = floatx4{lo[1], lo[3], hi[1], hi[3]};
+          }
+        } else {
+          constexpr int CPR = D / 4;
+          for (int c = lane; c < nh * CPR; c += 64)
+            *reinterpret_cast<floatx4*>(rec + (size_t)h0 * D + 4 * c) =
+                *reinterpret_cast<const floatx4*>(rl + (c / CPR) * RSTRIDE + (c % CPR) * 4);
+        }
         if (h0 == 0 && lane < 8)
           *reinterpret_cast<floatx4*>(rec + (size_t)NCOL * D + 4 * lane) =
               *reinterpret_cast<const floatx4*>(rl + 8 * RSTRIDE + 4 * lane);
@@ -763,10 +811,10 @@ void paged_attn_wave_kernel(AttnParams p) {
       } else if constexpr (KVT::bits == 4) {
         // 32 codes -> 64 bytes of f16
         uint8_t* dst = vst + v_row[ps] * C::VROW + cchunk * 64;
-        *reinterpret_cast<uint4*>(dst) = i4x8_f16(t.v[ps].x);
-        *reinterpret_cast<uint4*>(dst + 16) = i4x8_f16(t.v[ps].y);
-        *reinterpret_cast<uint4*>(dst + 32) = i4x8_f16(t.v[ps].z);
-        *reinterpret_cast<uint4*>(dst + 48) = i4x8_f16(t.v[ps].w);
+        *reinterpret_cast<uint4*>(dst) = i4x8_f16_il(t.v[ps].x);
+        *reinterpret_cast<uint4*>(dst + 16) = i4x8_f16_il(t.v[ps].y);
+        *reinterpret_cast<uint4*>(dst + 32) = i4x8_f16_il(t.v[ps].z);
+        *reinterpret_cast<uint4*>(dst + 48) = i4x8_f16_il(t.v[ps].w);
       } else {
         *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32) = to16<MT, KVT>(t.v[ps].x, t.v[ps].y);
         *reinterpret_cast<uint4*>(vst + v_row[ps] * C::VROW + cchunk * 32 + 16) =
@@ -781,10 +829,18 @@ void paged_attn_wave_kernel(AttnParams p) {
     uint32_t kf[GRP ? 4 * NC : 1];
     if constexpr (GRP) {
       const float r = t.ks > 0.f ? __builtin_amdgcn_rcpf(t.ks) : 0.f;
+      if constexpr (kIL) {
+        // chunk c: channels 8c..8c+7 in loads 2c, 2c + 1, paired (i, i + 4)
 #pragma unroll
-      for (int j = 0; j < C::KCS; ++j) {
-        kf[2 * j] = M::pack2(t.kcs[j][0] * r, t.kcs[j][1] * r);
-        kf[2 * j + 1] = M::pack2(t.kcs[j][2] * r, t.kcs[j][3] * r);
+        for (int c = 0; c < C::KCS / 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kf[4 * c + i] = M::pack2(t.kcs[2 * c][i] * r, t.kcs[2 * c + 1][i] * r);
+      } else {
+#pragma unroll
+        for (int j = 0; j < C::KCS; ++j) {
+          kf[2 * j] = M::pack2(t.kcs[j][0] * r, t.kcs[j][1] * r);
+          kf[2 * j + 1] = M::pack2(t.kcs[j][2] * r, t.kcs[j][3] * r);
+        }
       }
     }
     auto kscale = [&](uint4 k8, int c) {
@@ -810,7 +866,8 @@ void paged_attn_wave_kernel(AttnParams p) {
         const uint32_t w[4] = {t.k[c2].x, t.k[c2].y, t.k[c2].z, t.k[c2].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          sacc = M::qk(__builtin_bit_cast(typename M::vec8, kscale(i4x8_f16(w[j]), 4 * c2 + j)), qop[4 * c2 + j], sacc);
+          sacc = M::qk(__builtin_bit_cast(typename M::vec8, kscale(i4x8_f16_il(w[j]), 4 * c2 + j)), qop[4 * c2 + j],
+                       sacc);
       }
     } else {
 #pragma unroll
