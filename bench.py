@@ -177,9 +177,24 @@ def measure(w, steps, warmup, copies, graph=False):
     # sequences that share no block are read with the streaming load policy
     stream_kv = not (w.prefix_tokens or w.fork)
 
-    def step(r, ev=None):
-        # the slot write of the new token (code caches are written whole by
-        # the quantiser at prefill, so their step is attention only)
+    fused = not quant and not w.sink and not w.window
+
+    def step(r):
+        """One decode step as the library runs it in production: the slot
+        write inside the decode (pkv_paged_attn_decode_append) for 16-bit
+        caches without a keep-mask; otherwise the slot write (none for code
+        caches, written whole by the quantiser at prefill), the partition
+        pass and the merge."""
+        if fused:
+            pkv.paged_attn_decode_append(out, t["query"], r.k_cache, r.v_cache, t["new_key"], t["new_value"],
+                                         positions, r.block_tables, r.lens, w.sm_scale, slot_mapping=slots,
+                                         partition_size=psize, workspace=ws, stream_kv=stream_kv)
+        else:
+            step_split(r)
+
+    def step_split(r, ev=None):
+        """The same step as separate launches (slot write, partition, merge),
+        with HIP events around the partition kernel when ``ev`` is given."""
         if not quant:
             pkv.append_kv(t["new_key"], t["new_value"], r.k_cache, r.v_cache, r.block_tables, positions,
                           slot_mapping=slots)
@@ -195,27 +210,46 @@ def measure(w, steps, warmup, copies, graph=False):
         if ev is not None:
             ev[2].record()
 
-    for i in range(warmup):
-        step(runs[i % len(runs)])
-    torch.cuda.synchronize()
-    # events are recorded on torch's current stream, the stream every kernel
-    # is launched on (the binding passes it to the library)
+    def timed(fn):
+        """ms per step over `steps` steps after `warmup` untimed ones, cache
+        copies rotated; synchronised on both sides."""
+        for i in range(warmup):
+            fn(runs[i % len(runs)])
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            fn(runs[i % len(runs)])
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    # 1. the separate launches with HIP events on the launch stream (torch's
+    # current stream, which the binding passes to the library) around the
+    # partition kernel and the merge: the roofline's kernel time
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(warmup):
+        step_split(runs[i % len(runs)])
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     start.record()
     for i in range(steps):
-        step(runs[i % len(runs)], evs[i])
+        step_split(runs[i % len(runs)], evs[i])
     stop.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(stop)
+    split_ms = start.elapsed_time(stop) / steps
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
 
-    # the same steps replayed from HIP graphs, one per cache copy (a serving
+    # 2. the step, as the bench line's ms_per_step (after loop 1, so that the
+    # GPU runs at its working clocks)
+    t0 = time.perf_counter()
+    total_ms = timed(step)
+    wall = time.perf_counter() - t0
+
+    # 3. the step replayed from HIP graphs, one per cache copy (a serving
     # loop captures its decode step once); the library enqueues no memset,
     # allocation or synchronisation, so a step captures as its kernels
     graph_ms = None
@@ -230,20 +264,12 @@ def measure(w, steps, warmup, copies, graph=False):
                     step(r)
                 graphs.append(gr)
         torch.cuda.current_stream().wait_stream(side)
-        for i in range(warmup):
-            graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
-        start.record()
-        for i in range(steps):
-            graphs[i % len(graphs)].replay()
-        stop.record()
-        torch.cuda.synchronize()
-        graph_ms = start.elapsed_time(stop) / steps
+        graph_ms = timed(lambda r: graphs[runs.index(r)].replay())
     return {
         "w": w, "t": t, "lens": lens, "kv_bytes": kv_bytes, "psize": psize, "S": S, "Hq": Hq, "D": D,
-        "ms_per_step": total_ms / steps, "part_ms": float(part_ms.mean()), "merge_ms": float(merge_ms.mean()),
+        "ms_per_step": total_ms, "part_ms": float(part_ms.mean()), "merge_ms": float(merge_ms.mean()),
         "attn_ms": float((part_ms + merge_ms).mean()), "wall": wall, "copies": len(runs),
-        "stream_kv": stream_kv, "graph_ms": graph_ms,
+        "stream_kv": stream_kv, "graph_ms": graph_ms, "split_ms": split_ms, "fused": fused,
     }
 
 
@@ -584,6 +610,10 @@ def main():
         "attn_kv_gbps": round(kv_bytes / (m["attn_ms"] * 1e-3) / 1e9, 2),
         "wall_s": round(m["wall"], 3),
         "graph_ms_per_step": None if m["graph_ms"] is None else round(m["graph_ms"], 5),
+        "step": ("slot write fused into the decode (pkv_paged_attn_decode_append), then the merge" if m["fused"]
+                 else "partition pass and merge" if w.kv_dtype in CODES
+                 else "slot write (pkv_append_kv), partition pass, merge"),
+        "split_launches_ms_per_step": round(m["split_ms"], 5),
         "roofline": roofline(m),
     }
     if not args.no_cpu_baseline:

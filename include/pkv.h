@@ -391,6 +391,31 @@ pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes
                            int num_blocks, int block_size, int num_kv_heads, int head_dim,
                            void* stream);
 
+/*
+ * pkv_paged_attn_decode with the step's slot write fused into it: for each
+ * sequence s with positions[s] = p >= 0, key[s] / value[s]
+ * ([num_seqs][num_kv_heads][head_dim] in the cache dtype) are written to
+ * slot block_tables[s][p / block_size] * block_size + p % block_size, as
+ * pkv_reshape_and_cache would, and the decode attends over seq_lens[s]
+ * tokens with that row included.  The slot goes to slot_mapping_out[s] when
+ * it is not NULL.  Precondition: p = seq_lens[s] - 1 (the new token is the
+ * last one) and its block is in the table; the write is done by the
+ * workgroup that reads that block, before it reads it, so with any other p
+ * the attention may or may not see the new row.  Rows of sequences with
+ * p < 0, or whose table entry is outside [0, num_blocks), are not written.
+ * bf16 or f16 caches of the query dtype; no keep-mask.  Workspace,
+ * partition_size and flags as in pkv_paged_attn_decode.  One launch fewer
+ * per decode step than pkv_append_kv followed by the decode.
+ */
+pkv_status pkv_paged_attn_decode_append(void* out, const void* query, int q_dtype, void* k_cache, void* v_cache,
+                                        int kv_dtype, const void* key, const void* value,
+                                        const int32_t* positions, int32_t* slot_mapping_out,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int num_blocks, float sm_scale,
+                                        int partition_size, unsigned flags, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Scale groups of the grouped quantiser and decode. */
 typedef enum pkv_scale_group {
   PKV_GROUP_CHANNEL = 0, /* one scale per (block, KV head, channel) over the block's rows (keys) */

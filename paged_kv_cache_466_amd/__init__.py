@@ -16,7 +16,7 @@ __all__ = [
     "paged_attn_decode", "paged_attn_partition", "paged_attn_merge",
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
     "paged_attn_decode_multi", "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
-    "paged_attn_decode_grouped", "quantize_kv_grouped", "append_kv_quantized_grouped", "GROUP_CHANNEL",
+    "paged_attn_decode_append", "paged_attn_decode_grouped", "quantize_kv_grouped", "append_kv_quantized_grouped", "GROUP_CHANNEL",
     "GROUP_TOKEN",
     "slot_mapping", "reshape_and_cache", "append_kv", "append_kv_quantized", "copy_blocks", "quantize_kv",
     "validate_tables", "BlockPool", "PrefixCache", "h2o_retain", "DTYPES",
@@ -60,6 +60,8 @@ _SIGS = {
                                      ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_selected": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                         ctypes.c_uint, _p, _sz, _p], _i),
+    "pkv_paged_attn_decode_append": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
+                                      _i, ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_grouped": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                        _i, ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_append_kv_quantized_grouped": ([_p, _p, _i, _p, _p, _p, _p, _i, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i,
@@ -465,6 +467,29 @@ def quantize_kv_grouped(src_cache, dst_codes, dst_group_scales, code_dtype, grou
     _check(lib.pkv_quantize_kv_grouped(_ptr(src_cache), _dtype(src_cache), _ptr(dst_codes), DTYPES[code_dtype],
                                        _ptr(dst_tile_scales), _ptr(dst_group_scales), int(group), _ptr(block_ids),
                                        n_blocks, NB, BS, Hkv, D, _stream(src_cache)))
+
+
+def paged_attn_decode_append(out, query, k_cache, v_cache, key, value, positions, block_tables, seq_lens, sm_scale,
+                             slot_mapping=None, partition_size=0, workspace=None, stream_kv=False):
+    """Decode with the step's slot write fused in (``pkv_paged_attn_decode_append``):
+    key/value [S, Hkv, D] of each sequence's new token go to position
+    positions[s] (= seq_lens[s] - 1, or < 0 for none), then attention over
+    seq_lens tokens; the slots go to ``slot_mapping`` when given."""
+    _contig(out, query, k_cache, v_cache, key, value, positions, block_tables, seq_lens, slot_mapping, workspace)
+    S, Hq, D = query.shape
+    NB, BS, Hkv = k_cache.shape[:3]
+    if k_cache.shape[3] != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("shape mismatch between query, caches and out")
+    if tuple(key.shape) != (S, Hkv, D) or value.shape != key.shape or key.dtype != k_cache.dtype:
+        raise ValueError("key/value must be [S, Hkv, D] of the cache's dtype")
+    workspace = _workspace_for(query, k_cache, block_tables, partition_size, workspace, None)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attn_decode_append(
+        _ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache), _ptr(key), _ptr(value),
+        _ptr(positions), _ptr(slot_mapping), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, Hq, Hkv, D,
+        BS, NB, float(sm_scale), int(partition_size), DECODE_STREAM_KV if stream_kv else 0, _ptr(workspace),
+        ws_bytes, _stream(query)))
+    return out
 
 
 def paged_attn_decode_grouped(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_tile_scales,

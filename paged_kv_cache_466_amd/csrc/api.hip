@@ -392,6 +392,35 @@ extern "C" pkv_status pkv_paged_attn_decode_selected(
   return hip_status(launch_paged_attn_merge(a), who);
 }
 
+extern "C" pkv_status pkv_paged_attn_decode_append(
+    void* out, const void* query, int q_dtype, void* k_cache, void* v_cache, int kv_dtype, const void* key,
+    const void* value, const int32_t* positions, int32_t* slot_mapping_out, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, float sm_scale, int partition_size, unsigned flags, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* who = "pkv_paged_attn_decode_append";
+  if (kv_dtype != q_dtype || (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16))
+    return fail(PKV_EUNSUPPORTED, "%s: the fused write is built for bf16 / f16 caches of the query dtype", who);
+  if (num_seqs > 0 && (!key || !value || !positions)) return fail(PKV_EINVAL, "%s: null pointer argument", who);
+  AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, nullptr, nullptr, block_tables,
+                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         num_blocks, sm_scale, partition_size, 0, 0, flags, stream);
+  a.new_k = key;
+  a.new_v = value;
+  a.positions = positions;
+  a.slots_out = slot_mapping_out;
+  pkv_status st = prepare_attn(a, who, workspace, workspace_bytes, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if (check_env()) {
+    st = device_check(block_tables, max_blocks_per_seq, seq_lens, num_seqs, block_size, num_blocks, nullptr, 0,
+                      stream);
+    if (st != PKV_OK) return st;
+  }
+  st = hip_status(launch_paged_attn_partition(a), who);
+  if (st != PKV_OK) return st;
+  return hip_status(launch_paged_attn_merge(a), who);
+}
+
 extern "C" pkv_status pkv_paged_attn_decode_grouped(
     void* out, const void* query, int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
     const float* k_tile_scales, const float* k_channel_scales, const float* v_token_scales,

@@ -66,6 +66,13 @@ struct AttnParams {
   int budget;                // selected decode: pages per (sequence, KV head)
   int qtok;                  // query tokens per sequence (the last qtok positions, causal)
   const float* k_chan;       // grouped scales: K per (block, KV head, channel); v_scales per token
+  // fused slot write (new_k != null): the new token of sequence s, key/value
+  // [S][Hkv][D], goes to position positions[s] (< 0: none) before it is read;
+  // its slot goes to slots_out[s] when slots_out != null
+  const void* new_k;
+  const void* new_v;
+  const int32_t* positions;
+  int32_t* slots_out;
   float scale_log2;     // sm_scale * log2(e)
 };
 
@@ -383,9 +390,10 @@ constexpr int kEndKey = -1;            // key of the list entry after the last b
 
 // LDS of a workgroup of `waves` waves: per wave a V staging area and a query
 // area, then the block list (list_cap entries and the end entry), the
-// sequences of the first segments and two counters.
+// sequences of the first segments, four counters, and the sequences whose
+// last unit the workgroup holds (at most one per list entry).
 __host__ __device__ constexpr int wave_group_lds(int vstage, int waves, int list_cap) {
-  return waves * (vstage + kQueryLds) + (list_cap + 1) * 16 + kMaxQuerySegs * 4 + 16;
+  return waves * (vstage + kQueryLds) + (list_cap + 1) * 16 + kMaxQuerySegs * 4 + 16 + list_cap * 4;
 }
 
 // Writes the workgroup's block list into LDS (one wave calls it).  Entry k:
@@ -399,7 +407,7 @@ __host__ __device__ constexpr int wave_group_lds(int vstage, int waves, int list
 // entries of the sequences that start here.
 template <bool SEL>
 __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_dim, int lane, int4* list, int* segs,
-                                                 int* counts) {
+                                                 int* counts, int* ends) {
   const int S = p.num_seqs;
   const int w = blockIdx.x;
   // workgroup s of the first head group zeroes sequence s when it is empty
@@ -414,7 +422,7 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
   SeqWindow win = load_window<SEL>(p, 0, 0, lane);
   int U = win.total;
   for (int s0 = 64; s0 < S; s0 += 64) U += load_window<SEL>(p, s0, U, lane).total;
-  int nb = 0, nseg = 0;
+  int nb = 0, nseg = 0, nend = 0;
   if (U > 0) {
     const int K = gridDim.x;
     const int Q = max(p.min_units, (U + K - 1) / K);
@@ -468,6 +476,11 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
                                : make_int4((s * p.mbs + lb) * 4, t0 | (masked ? (int)0x80000000u : 0), L, key);
           }
           if (lane == 0 && nseg < kMaxQuerySegs) segs[nseg] = s;
+          // the workgroup holding a sequence's last unit writes its new token
+          if (p.new_k && i1 == n && cnt > 0) {
+            if (lane == 0) ends[nend] = s;
+            ++nend;
+          }
           if (i0 == 0 && p.plan && blockIdx.y == 0 && lane == 0) {
             const int w_last = (int)(((long long)(P + n) * k_eff - 1) / U);
             reinterpret_cast<int4*>(p.plan)[s] = make_int4(2 * w + upper, w, w_last, 0);
@@ -483,6 +496,7 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
     list[nb] = make_int4(kOutOfRange, 0, 0, kEndKey);
     counts[0] = nb;
     counts[1] = nseg;
+    counts[2] = nend;
   }
 }
 
@@ -534,12 +548,42 @@ void paged_attn_wave_kernel(AttnParams p) {
   int4* list = reinterpret_cast<int4*>(lds + waves * (C::VSTAGE + kQueryLds));
   int* segs = reinterpret_cast<int*>(list + p.list_cap + 1);
   int* counts = segs + kMaxQuerySegs;
+  int* ends = counts + 4;
 
-  if (wave == 0) build_block_list<SEL>(p, D, lane, list, segs, counts);
+  if (wave == 0) build_block_list<SEL>(p, D, lane, list, segs, counts, ends);
   __syncthreads();
   if (kvh >= p.num_kv_heads) return;
   const int nb = __builtin_amdgcn_readfirstlane(counts[0]);
   const int nseg = __builtin_amdgcn_readfirstlane(counts[1]);
+
+  if (!SEL && !kCodes && p.new_k) {
+    // Fused slot write: the new token of every sequence whose last unit this
+    // workgroup holds (the only workgroup reading that block).  Each wave
+    // writes its own head's key and value rows, and its stores complete
+    // before it loads any block.
+    const int nend = __builtin_amdgcn_readfirstlane(counts[2]);
+    constexpr int CH = D / 8;   // 16-byte pieces of a 16-bit row
+    for (int j = 0; j < nend; ++j) {
+      const int s = __builtin_amdgcn_readfirstlane(ends[j]);
+      const int pos = p.positions[s];
+      if (pos < 0 || pos / kBS >= p.mbs) continue;
+      const int pb = p.block_tables[(size_t)s * p.mbs + pos / kBS];
+      if (pb < 0 || pb >= p.num_blocks) continue;
+      const size_t slot = (size_t)pb * kBS + pos % kBS;
+      if (lane < 2 * CH) {
+        const bool isv = lane >= CH;
+        const int c = isv ? lane - CH : lane;
+        const uint4 v =
+            reinterpret_cast<const uint4*>(isv ? p.new_v : p.new_k)[((size_t)s * p.num_kv_heads + kvh) * CH + c];
+        uint4* cache = reinterpret_cast<uint4*>(const_cast<void*>(isv ? p.v_cache : p.k_cache));
+        cache[(slot * p.num_kv_heads + kvh) * CH + c] = v;
+      }
+      if (p.slots_out && blockIdx.y == 0 && wave == 0 && lane == 0) p.slots_out[s] = (int)slot;
+    }
+    // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone): the rows are in
+    // memory before this wave issues its first block load
+    if (nend > 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
 
   // queries of the first segments, copied to LDS at the start of the ring
   const int q_chunks = NCOL * D / 8;                   // 16-byte pieces of one segment's query columns
@@ -1314,6 +1358,10 @@ static AttnParams make_params(const AttnArgs& a) {
   p.table_bytes = a.selected ? (int)((long long)a.num_seqs * a.num_kv_heads * a.budget * 8)
                              : (int)((long long)a.num_seqs * a.max_blocks_per_seq * 4);
   p.k_chan = a.k_chan;
+  p.new_k = a.new_k;
+  p.new_v = a.new_v;
+  p.positions = a.positions;
+  p.slots_out = a.slots_out;
   p.scale_log2 = a.sm_scale * kLog2e;
   return p;
 }

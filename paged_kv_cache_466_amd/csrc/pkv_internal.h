@@ -73,6 +73,11 @@ struct AttnArgs {
   // grouped scales: K channel scales [NB][Hkv][D] (k_scales then holds each
   // tile's largest channel scale) and v_scales per token [NB][Hkv][16]
   const float* k_chan;
+  // fused slot write of each sequence's new token (16-bit caches)
+  const void* new_k;
+  const void* new_v;
+  const int32_t* positions;
+  int32_t* slots_out;
   void* stream;
 };
 

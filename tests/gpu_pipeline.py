@@ -82,10 +82,12 @@ class GpuRun:
         if do_step and w.append:
             self.decode_step(tensors)
 
-    def decode_step(self, tensors, fused=False):
+    def decode_step(self, tensors, fused=False, attend=None):
         """Host pool append -> copy-on-write copies -> device slot mapping ->
         slot write (``fused``: both in one pkv_append_kv launch).  Also keeps
-        the host pool's slots for comparison."""
+        the host pool's slots for comparison.  ``attend`` = (query, out,
+        partition_size): the slot write goes into the decode instead
+        (pkv_paged_attn_decode_append), which leaves its output in out."""
         w = self.w
         host_slots = []
         lens = self.lens.cpu().numpy()
@@ -101,6 +103,15 @@ class GpuRun:
                             dtype=w.kv_dtype if w.kv_dtype in CODES else None)
         positions = self.lens.clone()
         self.host_step_slots = np.asarray(host_slots, dtype=np.int64)
+        if attend is not None:
+            query, out, psize = attend
+            self.step_slots = torch.empty(w.S, dtype=torch.int32, device=self.device)
+            self.lens += 1
+            pkv.paged_attn_decode_append(out, query, self.k_cache, self.v_cache, tensors["new_key"],
+                                         tensors["new_value"], positions, self.block_tables, self.lens, w.sm_scale,
+                                         slot_mapping=self.step_slots, partition_size=psize,
+                                         stream_kv=not (w.prefix_tokens or w.fork))
+            return
         if fused:
             self.step_slots = torch.empty(w.S, dtype=torch.int32, device=self.device)
             pkv.append_kv(tensors["new_key"], tensors["new_value"], self.k_cache, self.v_cache, self.block_tables,

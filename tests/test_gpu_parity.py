@@ -126,6 +126,29 @@ def test_fused_append_matches_oracle(name):
     assert raw_cpu(g.v_cache, w.kv_dtype).tobytes() == o.v_cache.tobytes()
 
 
+@pytest.mark.parametrize("name", ["llama_small", "prefix_small", "llama_small_f16", "many_short", "one_long",
+                                  "hkv16", "mqa_d64", "g16"])
+@pytest.mark.parametrize("psize", [0, 64, 512])
+def test_decode_with_fused_slot_write(name, psize):
+    """pkv_paged_attn_decode_append (the slot write inside the decode) leaves
+    the oracle's caches and slots, copy-on-write included, and outputs bit
+    for bit what the separate slot write followed by the decode outputs."""
+    from gpu_pipeline import GpuRun
+    w, t, g0, o = run_case(name)
+    g = GpuRun(w, t, do_step=False)
+    out = torch.empty_like(t["query"])
+    g.decode_step(t, attend=(t["query"], out, psize))
+    torch.cuda.synchronize()
+    assert (g.step_slots.cpu().numpy().astype(np.int64) == o.step_slots).all()
+    assert g.cow == o.cow and g.tables == o.tables
+    assert raw_cpu(g.k_cache, w.kv_dtype).tobytes() == o.k_cache.tobytes()
+    assert raw_cpu(g.v_cache, w.kv_dtype).tobytes() == o.v_cache.tobytes()
+    ref = g0.decode(t["query"], partition_size=psize, stream_kv=not (w.prefix_tokens or w.fork))
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    err = np.abs(out.float().cpu().numpy() - o.decode(to_raw(t["query"], w.q_dtype))).max()
+    assert err <= TOL[w.q_dtype], err
+
+
 @pytest.mark.parametrize("name", [n for n in CASES if n != "tiny_fp32"])
 def test_decode_streaming_policy_is_bit_identical(name):
     """PKV_DECODE_STREAM_KV only changes the cache policy of the loads: the
