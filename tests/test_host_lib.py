@@ -186,6 +186,24 @@ def test_argument_errors_return_before_launch():
                                  0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 2 and "INT4" in pkv.last_error()
     assert L.pkv_reshape_and_cache(None, None, None, None, 5, None, 4, 10, 16, 8, 128, None) == 2
+    # fused slot write: 16-bit caches of the query dtype only
+    st = L.pkv_paged_attn_decode_append(None, None, 1, None, None, 3, None, None, None, None, None, 4, None, 2, 32, 8,
+                                        128, 16, 10, 0.1, 0, 0, None, 0, None)
+    assert st == 2 and "fused" in pkv.last_error()
+    st = L.pkv_paged_attn_decode_append(None, None, 1, None, None, 1, None, None, None, None, None, 4, None, 2, 32, 8,
+                                        128, 16, 10, 0.1, 0, 0, None, 0, None)
+    assert st == 1 and "null" in pkv.last_error()
+    # grouped scales: i8 / i4 codes; scale pointers; scale group kind
+    st = L.pkv_paged_attn_decode_grouped(None, None, 1, None, None, 4, 1, 1, 1, None, 4, None, 2, 32, 8, 128, 16, 10,
+                                         0.1, 0, 0, None, 0, None)
+    assert st == 2 and "grouped" in pkv.last_error()
+    st = L.pkv_paged_attn_decode_grouped(None, None, 1, None, None, 3, None, 1, 1, None, 4, None, 2, 32, 8, 128, 16,
+                                         10, 0.1, 0, 0, None, 0, None)
+    assert st == 1 and "scale" in pkv.last_error()
+    assert L.pkv_quantize_kv_grouped(1, 1, 1, 3, None, 1, 7, None, 4, 10, 16, 8, 128, None) == 1
+    assert L.pkv_quantize_kv_grouped(1, 1, 1, 1, None, 1, 0, None, 4, 10, 16, 8, 128, None) == 2
+    assert L.pkv_append_kv_quantized_grouped(1, 1, 1, 1, 1, 1, 1, 3, 1, None, 1, 1, 4, 1, 2, 10, 16, 8, 128,
+                                             None) == 1
     # empty batches are no-ops
     assert L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 0, 32, 8, 128, 16, 10,
                                    0.1, 0, 0, 0, 0, None, 0, None) == 0
