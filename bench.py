@@ -139,6 +139,53 @@ def kv_bytes_per_step(w, lens):
     return total
 
 
+def kv_bytes_unique(w, tables, lens):
+    """KV bytes of the distinct physical blocks one step reads (a block
+    shared by several sequences counted once, with the most rows any of them
+    reads), plus the scales of code caches."""
+    b = BYTES[w.kv_dtype]
+    masked = bool(w.sink or w.window)
+    rows = {}
+    for tb, L in zip(tables, lens):
+        L = int(L)
+        for lb in range(-(-L // 16)):
+            lo, hi = 16 * lb, min(16 * lb + 16, L)
+            if masked:
+                # kept positions: [0, sink) and [max(sink, L - window), L)
+                n = max(0, min(hi, w.sink) - lo) + max(0, hi - max(lo, w.sink, L - w.window))
+            else:
+                n = hi - lo
+            rows[tb[lb]] = max(rows.get(tb[lb], 0), n)
+    total = int(sum(rows.values()) * w.Hkv * w.D * b * 2)
+    if w.kv_dtype in CODES:
+        total += sum(1 for n in rows.values() if n) * w.Hkv * 4 * 2
+    return total
+
+
+def stream_read_ceiling(nbytes=2 << 30, reps=20):
+    """GB/s of the library's streaming-read probe over a fresh device buffer
+    of nbytes (read once per launch)."""
+    import torch
+
+    import paged_kv_cache_466_amd as pkv
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(pkv.lib.pkv_stream_read_sink_words(), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pkv.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        pkv.stream_read(buf, sink)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    del buf
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def measure(w, steps, warmup, copies, graph=False):
     """Times `steps` decode steps of workload `w` (inputs resident in HBM,
     `copies` cache copies rotated so the last-level cache cannot hold them).
@@ -194,7 +241,9 @@ def measure(w, steps, warmup, copies, graph=False):
 
     def step_split(r, ev=None):
         """The same step as separate launches (slot write, partition, merge),
-        with HIP events around the partition kernel when ``ev`` is given."""
+        with HIP events around each when ``ev`` is given."""
+        if ev is not None:
+            ev[3].record()
         if not quant:
             pkv.append_kv(t["new_key"], t["new_value"], r.k_cache, r.v_cache, r.block_tables, positions,
                           slot_mapping=slots)
@@ -228,7 +277,7 @@ def measure(w, steps, warmup, copies, graph=False):
     # 1. the separate launches with HIP events on the launch stream (torch's
     # current stream, which the binding passes to the library) around the
     # partition kernel and the merge: the roofline's kernel time
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(warmup):
         step_split(runs[i % len(runs)])
     torch.cuda.synchronize()
@@ -242,6 +291,7 @@ def measure(w, steps, warmup, copies, graph=False):
     split_ms = start.elapsed_time(stop) / steps
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    write_ms = np.array([e[3].elapsed_time(e[0]) for e in evs])
 
     # 2. the step, as the bench line's ms_per_step (after loop 1, so that the
     # GPU runs at its working clocks)
@@ -268,6 +318,9 @@ def measure(w, steps, warmup, copies, graph=False):
     return {
         "w": w, "t": t, "lens": lens, "kv_bytes": kv_bytes, "psize": psize, "S": S, "Hq": Hq, "D": D,
         "ms_per_step": total_ms, "part_ms": float(part_ms.mean()), "merge_ms": float(merge_ms.mean()),
+        "part_pct": [float(np.percentile(part_ms, q)) for q in (10, 50, 90)],
+        "write_ms": None if quant else float(write_ms.mean()),
+        "kv_bytes_unique": kv_bytes_unique(w, g0.tables, lens),
         "attn_ms": float((part_ms + merge_ms).mean()), "wall": wall, "copies": len(runs),
         "stream_kv": stream_kv, "graph_ms": graph_ms, "split_ms": split_ms, "fused": fused,
     }
@@ -522,7 +575,9 @@ def measure_grouped(w, steps, warmup, copies):
 
 
 def roofline(m):
-    achieved = m["kv_bytes"] / (m["part_ms"] * 1e-3) / 1e9
+    # algorithmic HBM bytes: a block shared by several sequences is read from
+    # HBM once per step (equal to the KV bytes when nothing is shared)
+    achieved = m["kv_bytes_unique"] / (m["part_ms"] * 1e-3) / 1e9
     return {
         "bound": "hbm",
         "kernel": "paged_attn_wave_kernel" if m["w"].kv_dtype != "f32" else "paged_attn_simple_kernel",
@@ -601,12 +656,15 @@ def main():
             "block_size": 16, "seq_len_mean": float(lens.mean()), "seq_len_max": int(lens.max()),
             "kv_dtype": w.kv_dtype, "partition_size": m["psize"], "kv_bytes_per_step": int(kv_bytes),
             "cache_copies_rotated": m["copies"], "stream_kv": m["stream_kv"],
+            "kv_bytes_unique_per_step": int(m["kv_bytes_unique"]),
         },
         "steps_per_s": round(1000.0 / ms, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "attn_us": round(m["attn_ms"] * 1e3, 2),
         "partition_us": round(m["part_ms"] * 1e3, 2),
+        "partition_us_p10_p50_p90": [round(x * 1e3, 2) for x in m["part_pct"]],
         "merge_us": round(m["merge_ms"] * 1e3, 2),
+        "write_us": None if m["write_ms"] is None else round(m["write_ms"] * 1e3, 2),
         "attn_kv_gbps": round(kv_bytes / (m["attn_ms"] * 1e-3) / 1e9, 2),
         "wall_s": round(m["wall"], 3),
         "graph_ms_per_step": None if m["graph_ms"] is None else round(m["graph_ms"], 5),
@@ -616,6 +674,13 @@ def main():
         "split_launches_ms_per_step": round(m["split_ms"], 5),
         "roofline": roofline(m),
     }
+    if m["kv_bytes_unique"] != kv_bytes:
+        # shared blocks: the bytes that have to come from HBM once per step
+        result["value_unique_gbps"] = round(m["kv_bytes_unique"] / (ms * 1e-3) / 1e9, 2)
+        result["pct_hbm_peak_unique"] = round(100.0 * result["value_unique_gbps"] / HBM_PEAK_GBPS, 2)
+    ceiling = stream_read_ceiling()
+    result["stream_read_ceiling_gbps"] = round(ceiling, 1)
+    result["pct_stream_read_ceiling"] = round(100.0 * result["roofline"]["achieved"] / ceiling, 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, m["t"], lens, args.cpu_seconds)
     if long_ctx is not None:

@@ -624,6 +624,22 @@ int pkv_prefix_cache_size(const pkv_prefix_cache* cache);
 pkv_status pkv_h2o_retain(const float* scores, int n, int budget, int recent_count, int32_t* kept_out,
                           int* n_kept);
 
+/* ------------------------------------------------------------------------
+ * Measurement
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Streaming-read probe: reads `bytes` bytes from device memory at src once
+ * (16-byte non-temporal loads, every CU busy) and stores one 32-bit fold of
+ * the data per workgroup into sink (device, at least
+ * pkv_stream_read_sink_words() words), so that nothing is skipped.  Timed
+ * around it, it gives the box's streaming-read ceiling that the decode's
+ * HBM figures are set against.  bytes must be a multiple of 16 and src
+ * 16-byte aligned.
+ */
+int pkv_stream_read_sink_words(void);
+pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

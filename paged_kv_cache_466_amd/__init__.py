@@ -19,7 +19,7 @@ __all__ = [
     "paged_attn_decode_append", "paged_attn_decode_grouped", "quantize_kv_grouped", "append_kv_quantized_grouped", "GROUP_CHANNEL",
     "GROUP_TOKEN",
     "slot_mapping", "reshape_and_cache", "append_kv", "append_kv_quantized", "copy_blocks", "quantize_kv",
-    "validate_tables", "BlockPool", "PrefixCache", "h2o_retain", "DTYPES",
+    "stream_read", "validate_tables", "BlockPool", "PrefixCache", "h2o_retain", "DTYPES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +67,8 @@ _SIGS = {
     "pkv_append_kv_quantized_grouped": ([_p, _p, _i, _p, _p, _p, _p, _i, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i,
                                          _p], _i),
     "pkv_quantize_kv_grouped": ([_p, _i, _p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p], _i),
+    "pkv_stream_read_sink_words": ([], _i),
+    "pkv_stream_read": ([_p, _sz, _p, _p], _i),
     "pkv_quest_summarize": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p], _i),
     "pkv_quest_scratch_bytes": ([_i, _i, _i], _sz),
     "pkv_quest_select": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz, _p], _i),
@@ -517,6 +519,16 @@ def paged_attn_decode_grouped(out, query, k_cache, v_cache, block_tables, seq_le
         float(sm_scale), int(partition_size), DECODE_STREAM_KV if stream_kv else 0, _ptr(workspace), ws_bytes,
         _stream(query)))
     return out
+
+
+def stream_read(src, sink=None):
+    """Streaming-read probe (``pkv_stream_read``): reads all of ``src`` (a
+    device tensor, size a multiple of 16 bytes) once; returns the sink."""
+    _contig(src)
+    if sink is None:
+        sink = torch.empty(lib.pkv_stream_read_sink_words(), dtype=torch.int32, device=src.device)
+    _check(lib.pkv_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src)))
+    return sink
 
 
 def validate_tables(block_tables, seq_lens, num_blocks, slot_mapping=None, block_size=16):

@@ -111,6 +111,16 @@ using namespace pkv;
 extern "C" const char* pkv_last_error(void) { return g_err; }
 extern "C" const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 
+extern "C" int pkv_stream_read_sink_words(void) { return kStreamReadBlocks; }
+
+extern "C" pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes % 16) return fail(PKV_EINVAL, "pkv_stream_read: bytes must be a multiple of 16");
+  if (bytes == 0) return PKV_OK;
+  if (!src || !sink) return fail(PKV_EINVAL, "pkv_stream_read: null pointer");
+  if (((uintptr_t)src) & 15) return fail(PKV_EINVAL, "pkv_stream_read: src must be 16-byte aligned");
+  return hip_status(launch_stream_read(src, bytes, sink, stream), "pkv_stream_read");
+}
+
 extern "C" int pkv_paged_attn_partition_size(int kv_dtype, int max_seq_len, int block_size) {
   if (block_size <= 0 || max_seq_len < 0) return 0;
   return resolve_partition(kv_dtype, max_seq_len, block_size, 0);

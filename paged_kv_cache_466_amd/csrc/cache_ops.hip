@@ -553,4 +553,44 @@ int launch_append_quantized(const void* key, const void* value, int src_dtype, v
 #undef PKV_AQD
 }
 
+// ---------------------------------------------------------------------------
+// Streaming-read probe: workgroup w reads the w-th contiguous chunk of the
+// buffer, each thread keeping 8 16-byte non-temporal loads in flight, and
+// folds what it read into one word per workgroup.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  uint32_t acc = 0;
+  size_t i = lo + threadIdx.x;
+  for (; i + (U - 1) * 256 < hi; i += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < hi; i += 256) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] ^= red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
+}
+
+int launch_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  stream_read_kernel<<<kStreamReadBlocks, 256, 0, (hipStream_t)stream>>>((const u32x4*)src, bytes / 16, sink);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -141,6 +141,9 @@ int launch_quest_select(const void* query, int q_dtype, const void* k_summary, c
                         int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
                         int num_kv_heads, int head_dim, int num_blocks, int budget, int32_t* selected,
                         void* scratch, void* stream);
+// streaming-read probe: workgroups (4 per CU) and their launcher
+constexpr int kStreamReadBlocks = 1024;
+int launch_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 int launch_quantize_kv_grouped(const void* src_cache, int src_dtype, void* dst_codes, int code_dtype,
                                float* tile_scales, float* group_scales, int group, const int32_t* block_ids,
                                int n_blocks, int num_blocks, int num_kv_heads, int head_dim, void* stream);
