@@ -1373,15 +1373,11 @@ static int launch_wave(const AttnParams& p, int num_slots, hipStream_t st) {
   const int groups = (p.num_kv_heads + per_group - 1) / per_group;
   const int lds = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, per_group, p.list_cap);
   auto kernel = paged_attn_wave_kernel<QT, KVT, D, STREAM, SEL, GRP>;
-  static bool lds_set = false;
-  if (!lds_set) {
-    // above the default dynamic-LDS limit: the largest group needs ~100 KB
-    const int most = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, kMaxWavesPerGroup, 128 * kMaxWavesPerGroup);
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, most);
-    if (e != hipSuccess) return e;
-    lds_set = true;
-  }
+  // above the default dynamic-LDS limit: the largest group needs ~105 KB
+  static std::atomic<bool> lds_set[64];
+  const int most = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, kMaxWavesPerGroup, 128 * kMaxWavesPerGroup);
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kernel), most, lds_set);
+  if (e != hipSuccess) return e;
   kernel<<<dim3(num_slots, groups), 64 * per_group, lds, st>>>(p);
   return hipGetLastError();
 }

@@ -4,6 +4,8 @@
 #define PKV_DEVICE_H_
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 namespace pkv {
@@ -178,6 +180,19 @@ __device__ __forceinline__ uint32_t f32_to_e5m2(float x) {
     code = (uint32_t)rintf(y);                       // 0..4; 4 is the smallest normal
   }
   return code | sign;
+}
+
+// Raises a kernel's dynamic-LDS limit to `bytes` once per device (the
+// attribute is set with the device current; devices up to 64 are tracked,
+// others set it on every call).  `done` is the kernel's own flag array.
+inline hipError_t set_lds_limit_once(const void* kernel, int bytes, std::atomic<bool>* done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev].store(true, std::memory_order_release);
+  return e;
 }
 
 }  // namespace pkv

@@ -387,13 +387,10 @@ int launch_quest_select(const void* query, int q_dtype, const void* k_summary, c
   constexpr int kMaxLdsKeys = 16384;
   const dim3 grid(num_seqs * num_kv_heads);
   if (max_blocks_per_seq <= kMaxLdsKeys) {
-    static bool lds_set = false;
-    if (!lds_set) {
-      const hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(quest_select_kernel<true>),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsKeys * 8);
-      if (e2 != hipSuccess) return e2;
-      lds_set = true;
-    }
+    static std::atomic<bool> lds_set[64];
+    const hipError_t e2 =
+        set_lds_limit_once(reinterpret_cast<const void*>(quest_select_kernel<true>), kMaxLdsKeys * 8, lds_set);
+    if (e2 != hipSuccess) return e2;
     quest_select_kernel<true><<<grid, kSelThreads, (size_t)max_blocks_per_seq * 8, st>>>(
         keys, block_tables, max_blocks_per_seq, seq_lens, num_blocks, num_kv_heads, budget, selected);
   } else {
