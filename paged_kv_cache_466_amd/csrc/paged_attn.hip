@@ -190,30 +190,14 @@ __device__ __forceinline__ uint32_t i8x2_f16(uint32_t u) {
 }
 
 // Eight INT4 codes (the nibbles of w, element 2i in the low nibble of byte
-// i) -> eight f16 values, exactly: with u = code + 8, bytes 0x64, u are the
-// f16 1024 + u, and subtracting 1032 leaves the code.
-__device__ __forceinline__ uint4 i4x8_f16(uint32_t w) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t lo = u & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
-  const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
-  const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // elements 0..3, one per byte
-  const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // elements 4..7
-  auto pair = [](uint32_t x, uint32_t sel) {
-    const h2 v = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, sel)) -
-                 h2{(_Float16)1032.0f, (_Float16)1032.0f};
-    return __builtin_bit_cast(uint32_t, v);
-  };
-  return make_uint4(pair(a, 0x04010400u), pair(a, 0x04030402u), pair(b, 0x04010400u), pair(b, 0x04030402u));
-}
-
-// Eight INT4 codes -> eight f16 values, exactly, in the interleaved order
+// i, two's complement) -> eight f16 values, exactly, in the interleaved order
 // (0, 4, 1, 5, 2, 6, 3, 7): the nibbles at bits s and s + 16 of w >> s
 // (s = 0, 4, 8, 12) are elements s/4 and s/4 + 4.  Masking them to the low
 // bits of each half, flipping bit 3 (u = code + 8) and setting the 0x64
 // byte is one three-input bit operation; the f16 1024 + u minus 1032 is the
-// code.  Three operations per pair fewer than the in-order conversion; the
-// query's elements and the staged V rows use the same order.
+// code.  Eleven operations per eight codes (an in-order conversion needs
+// byte permutes on top); the query's elements and the staged V rows use the
+// same order.
 __device__ __forceinline__ uint4 i4x8_f16_il(uint32_t w) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   auto pair = [](uint32_t x) {
