@@ -37,6 +37,10 @@ CASES = {
     "quant_kv_32k_b16_e5m2": ("quant_kv_32k_b16", {"kv_dtype": "fp8e5m2"}, [9], [4]),
     "ctx128k_b4": ("ctx128k_b4", {}, [1, 3], None),
     "ctx128k_b4_streaming": ("ctx128k_b4", {"streaming": True}, [2], None),
+    # the step as the bench runs it: the slot write fused into the decode
+    "llama3_8b_b64_fused_write": ("llama3_8b_b64", {"fused": True}, [3, 40, 62], None),
+    "shared_prefix_b128_fused_write": ("shared_prefix_b128", {"fused": True}, [0, 1, 100], None),
+    "ctx128k_b4_fused_write": ("ctx128k_b4", {"fused": True}, [0], [2, 5]),
 }
 
 
@@ -107,15 +111,21 @@ def test_full_size_sampled(case):
     name, ov, seqs, heads = CASES[case]
     ov = dict(ov)
     streaming = ov.pop("streaming", False)
+    fused = ov.pop("fused", False)
     w = get_workload(name, streaming=streaming, **ov)
     print(f"[fullsize] case={case} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} kv={w.kv_dtype} blocks={w.num_blocks}",
           flush=True)
     t = draw_tensors(w, "cuda")
-    g = GpuRun(w, t)
+    g = GpuRun(w, t, do_step=not fused)
     S, Hq, D = t["query"].shape
     psize = w.partition_size or pkv.paged_attn_partition_size(w.kv_dtype, g.mbs * 16)
     stream_kv = not (w.prefix_tokens or w.fork)
-    out = g.decode(t["query"], partition_size=psize, stream_kv=stream_kv).float().cpu().numpy()
+    if fused:
+        out = torch.empty_like(t["query"])
+        g.decode_step(t, attend=(t["query"], out, psize))
+        out = out.float().cpu().numpy()
+    else:
+        out = g.decode(t["query"], partition_size=psize, stream_kv=stream_kv).float().cpu().numpy()
     torch.cuda.synchronize()
     assert np.isfinite(out).all()
     q_all = codecs.decode(to_raw(t["query"], w.q_dtype), w.q_dtype)
