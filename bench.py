@@ -657,6 +657,9 @@ def main():
             "kv_dtype": w.kv_dtype, "partition_size": m["psize"], "kv_bytes_per_step": int(kv_bytes),
             "cache_copies_rotated": m["copies"], "stream_kv": m["stream_kv"],
             "kv_bytes_unique_per_step": int(m["kv_bytes_unique"]),
+            # slots allocated but unused in each sequence's last block
+            "block_waste_pct": round(100.0 * float(sum(-(-int(L) // 16) * 16 - int(L) for L in lens))
+                                     / max(1, sum(-(-int(L) // 16) * 16 for L in lens)), 3),
         },
         "steps_per_s": round(1000.0 / ms, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
