@@ -477,7 +477,7 @@ extern "C" pkv_status pkv_quest_summarize(const void* k_cache, int kv_dtype, voi
   if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16) return fail(PKV_EUNSUPPORTED, "%s: cache must be bf16 or f16", who);
   if (num_seqs < 0 || max_blocks_per_seq < 0 || num_blocks < 0) return fail(PKV_EINVAL, "%s: negative size", who);
   if (num_seqs == 0 || max_blocks_per_seq == 0) return PKV_OK;
-  if (num_seqs > 2147483647 / 1 || (!last_only && max_blocks_per_seq > 65535))
+  if (!last_only && max_blocks_per_seq > 65535)
     return fail(PKV_EUNSUPPORTED, "%s: max_blocks_per_seq above 65535 needs last_only", who);
   if (!k_cache || !k_summary || !block_tables || !seq_lens) return fail(PKV_EINVAL, "%s: null pointer", who);
   return hip_status(launch_quest_summarize(k_cache, kv_dtype, k_summary, block_tables, max_blocks_per_seq, seq_lens,
@@ -613,7 +613,7 @@ extern "C" pkv_status pkv_append_kv_quantized(const void* key, const void* value
     return fail(PKV_EUNSUPPORTED, "%s: codes must be i8, i4, fp8e4m3 or fp8e5m2", who);
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0) return fail(PKV_EINVAL, "%s: negative size", who);
   if (num_seqs == 0) return PKV_OK;
-  if (num_seqs > 2147483647 / 1 || num_kv_heads > 65535) return fail(PKV_EUNSUPPORTED, "%s: shape too large", who);
+  if (num_kv_heads > 65535) return fail(PKV_EUNSUPPORTED, "%s: shape too large", who);
   if (!key || !value || !k_tail || !v_tail || !k_codes || !v_codes || !k_scales || !v_scales || !block_tables ||
       !positions)
     return fail(PKV_EINVAL, "%s: null pointer", who);
@@ -679,7 +679,6 @@ extern "C" pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void
   if (n_blocks < 0 || num_blocks < 0) return fail(PKV_EINVAL, "pkv_quantize_kv: negative size");
   if (!block_ids && n_blocks > num_blocks) return fail(PKV_EINVAL, "pkv_quantize_kv: n_blocks > num_blocks");
   if (n_blocks == 0) return PKV_OK;
-  if (n_blocks > 2147483647 / 1) return fail(PKV_EINVAL, "pkv_quantize_kv: too many blocks");
   if (!src_cache || !dst_codes || !dst_scales) return fail(PKV_EINVAL, "pkv_quantize_kv: null pointer");
   return hip_status(launch_quantize_kv(src_cache, src_dtype, dst_codes, code_dtype, dst_scales, block_ids, n_blocks,
                                        num_blocks, block_size, num_kv_heads, head_dim, stream),
