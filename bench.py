@@ -85,6 +85,8 @@ def parse():
                     help="quantised workload with keys scaled per channel and values per token (i8 / i4)")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the secondary 128K-context split-K measurement")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="with a shared prefix, time the plain decode instead of the shared-prefix decode")
     return ap.parse_args()
 
 
@@ -186,10 +188,12 @@ def stream_read_ceiling(nbytes=2 << 30, reps=20):
     return nbytes / (ms * 1e-3) / 1e9
 
 
-def measure(w, steps, warmup, copies, graph=False):
+def measure(w, steps, warmup, copies, graph=False, cascade=False):
     """Times `steps` decode steps of workload `w` (inputs resident in HBM,
     `copies` cache copies rotated so the last-level cache cannot hold them).
-    Returns the timings and the state the CPU baseline needs."""
+    ``cascade``: a workload whose sequences share prefix blocks runs the
+    shared-prefix decode (the shared blocks attended once for the whole
+    batch).  Returns the timings and the state the CPU baseline needs."""
     import numpy as np
     import torch
 
@@ -213,16 +217,25 @@ def measure(w, steps, warmup, copies, graph=False):
     kv_bytes = kv_bytes_per_step(w, lens)
     S, Hq, D = t["query"].shape
     max_len = g0.mbs * 16
-    psize = w.partition_size or pkv.paged_attn_partition_size(w.kv_dtype, max_len)
-    nbytes = pkv.paged_attn_workspace_bytes(w.kv_dtype, S, Hq, w.Hkv, D, max_len, psize)
+    cascade = cascade and bool(w.prefix_tokens)
+    P = w.prefix_tokens // 16
+    if cascade:
+        # the partition size applies to the tokens past the prefix
+        psize = w.partition_size or pkv.paged_attn_partition_size(w.kv_dtype, max_len - 16 * P)
+        nbytes = pkv.paged_attn_shared_prefix_workspace_bytes(w.kv_dtype, S, Hq, w.Hkv, D, max_len, P, psize)
+    else:
+        psize = w.partition_size or pkv.paged_attn_partition_size(w.kv_dtype, max_len)
+        nbytes = pkv.paged_attn_workspace_bytes(w.kv_dtype, S, Hq, w.Hkv, D, max_len, psize)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(t["query"])
     positions = (g0.lens - 1).contiguous()
     slots = torch.empty(S, dtype=torch.int32, device="cuda")
     kvdt = uint8_kind(w.kv_dtype)
     quant = w.kv_dtype in CODES
-    # sequences that share no block are read with the streaming load policy
-    stream_kv = not (w.prefix_tokens or w.fork)
+    # sequences that share no block are read with the streaming load policy;
+    # the shared-prefix decode reads the prefix apart, and past it only a
+    # fork's two sequences share blocks
+    stream_kv = cascade or not (w.prefix_tokens or w.fork)
 
     fused = not quant and not w.sink and not w.window
 
@@ -232,7 +245,12 @@ def measure(w, steps, warmup, copies, graph=False):
         caches without a keep-mask; otherwise the slot write (none for code
         caches, written whole by the quantiser at prefill), the partition
         pass and the merge."""
-        if fused:
+        if cascade:
+            pkv.paged_attn_decode_shared_prefix(out, t["query"], r.k_cache, r.v_cache, r.block_tables, r.lens,
+                                                w.sm_scale, P, key=t["new_key"], value=t["new_value"],
+                                                positions=positions, slot_mapping=slots, partition_size=psize,
+                                                workspace=ws, stream_kv=stream_kv)
+        elif fused:
             pkv.paged_attn_decode_append(out, t["query"], r.k_cache, r.v_cache, t["new_key"], t["new_value"],
                                          positions, r.block_tables, r.lens, w.sm_scale, slot_mapping=slots,
                                          partition_size=psize, workspace=ws, stream_kv=stream_kv)
@@ -249,6 +267,15 @@ def measure(w, steps, warmup, copies, graph=False):
                           slot_mapping=slots)
         if ev is not None:
             ev[0].record()
+        if cascade:
+            # the prefix pass, the partition pass and the merge: one call
+            pkv.paged_attn_decode_shared_prefix(out, t["query"], r.k_cache, r.v_cache, r.block_tables, r.lens,
+                                                w.sm_scale, P, partition_size=psize, workspace=ws,
+                                                stream_kv=stream_kv)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
         pkv.paged_attn_partition(out, t["query"], r.k_cache, r.v_cache, r.block_tables, r.lens, w.sm_scale, ws,
                                  r.k_scales, r.v_scales, partition_size=psize, sink_tokens=w.sink,
                                  window_tokens=w.window, kv_dtype=kvdt, stream_kv=stream_kv)
@@ -322,7 +349,7 @@ def measure(w, steps, warmup, copies, graph=False):
         "write_ms": None if quant else float(write_ms.mean()),
         "kv_bytes_unique": kv_bytes_unique(w, g0.tables, lens),
         "attn_ms": float((part_ms + merge_ms).mean()), "wall": wall, "copies": len(runs),
-        "stream_kv": stream_kv, "graph_ms": graph_ms, "split_ms": split_ms, "fused": fused,
+        "stream_kv": stream_kv, "graph_ms": graph_ms, "split_ms": split_ms, "fused": fused, "cascade": cascade,
     }
 
 
@@ -576,16 +603,20 @@ def measure_grouped(w, steps, warmup, copies):
 
 def roofline(m):
     # algorithmic HBM bytes: a block shared by several sequences is read from
-    # HBM once per step (equal to the KV bytes when nothing is shared)
+    # HBM once per step (equal to the KV bytes when nothing is shared).  The
+    # shared-prefix decode is one call of three kernels, timed together.
     achieved = m["kv_bytes_unique"] / (m["part_ms"] * 1e-3) / 1e9
+    kernel = "paged_attn_wave_kernel" if m["w"].kv_dtype != "f32" else "paged_attn_simple_kernel"
+    if m.get("cascade"):
+        kernel = "prefix_attn_kernel + paged_attn_wave_kernel + paged_attn_merge_kernel (one call)"
     return {
         "bound": "hbm",
-        "kernel": "paged_attn_wave_kernel" if m["w"].kv_dtype != "f32" else "paged_attn_simple_kernel",
+        "kernel": kernel,
         "achieved": round(achieved, 2),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": measured_traffic(m["w"].name),
+        "traffic": None if m.get("cascade") else measured_traffic(m["w"].name),
     }
 
 
@@ -633,7 +664,7 @@ def main():
     if args.query_tokens > 1:
         print(json.dumps(measure_multi(w, args.steps, args.warmup, args.copies, args.query_tokens)), flush=True)
         return
-    m = measure(w, args.steps, args.warmup, args.copies, graph=args.graph)
+    m = measure(w, args.steps, args.warmup, args.copies, graph=args.graph, cascade=not args.no_shared_prefix)
     kv_bytes, ms = m["kv_bytes"], m["ms_per_step"]
     value = kv_bytes / (ms * 1e-3) / 1e9
     lens = m["lens"]
@@ -664,14 +695,16 @@ def main():
         "steps_per_s": round(1000.0 / ms, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "attn_us": round(m["attn_ms"] * 1e3, 2),
-        "partition_us": round(m["part_ms"] * 1e3, 2),
+        "partition_us": None if m["cascade"] else round(m["part_ms"] * 1e3, 2),
         "partition_us_p10_p50_p90": [round(x * 1e3, 2) for x in m["part_pct"]],
-        "merge_us": round(m["merge_ms"] * 1e3, 2),
+        "merge_us": None if m["cascade"] else round(m["merge_ms"] * 1e3, 2),
         "write_us": None if m["write_ms"] is None else round(m["write_ms"] * 1e3, 2),
         "attn_kv_gbps": round(kv_bytes / (m["attn_ms"] * 1e-3) / 1e9, 2),
         "wall_s": round(m["wall"], 3),
         "graph_ms_per_step": None if m["graph_ms"] is None else round(m["graph_ms"], 5),
-        "step": ("slot write fused into the decode (pkv_paged_attn_decode_append), then the merge" if m["fused"]
+        "step": ("prefix pass, then the decode past the prefix with the slot write fused in, then the merge "
+                 "(pkv_paged_attn_decode_shared_prefix)" if m["cascade"]
+                 else "slot write fused into the decode (pkv_paged_attn_decode_append), then the merge" if m["fused"]
                  else "partition pass and merge" if w.kv_dtype in CODES
                  else "slot write (pkv_append_kv), partition pass, merge"),
         "split_launches_ms_per_step": round(m["split_ms"], 5),

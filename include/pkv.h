@@ -103,11 +103,13 @@ const char* pkv_version(void);
 
 /* Decode flags (bit set). */
 enum {
-  /* Every physical block is read by one sequence of the batch only (no
-   * shared prefix blocks).  The caches are then read with the non-temporal
-   * (streaming) load policy, so the stream does not evict data that is
-   * reused; leave it off when sequences share blocks, whose reuse it would
-   * defeat.  Results are identical either way. */
+  /* A hint: the blocks the decode reads are (nearly) all read by one
+   * sequence of the batch only.  The caches are then read with the
+   * non-temporal (streaming) load policy, so the stream does not evict data
+   * that is reused; leave it off when many sequences share blocks, whose
+   * reuse it would defeat.  For pkv_paged_attn_decode_shared_prefix it
+   * concerns the blocks past the shared prefix, which that call reads apart.
+   * Results are identical either way. */
   PKV_DECODE_STREAM_KV = 1
 };
 
@@ -415,6 +417,60 @@ pkv_status pkv_paged_attn_decode_append(void* out, const void* query, int q_dtyp
                                         int head_dim, int block_size, int num_blocks, float sm_scale,
                                         int partition_size, unsigned flags, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/*
+ * Decode over a batch whose sequences all begin with the same prefix_blocks
+ * physical blocks (a prompt stored once and shared through the block tables:
+ * [P2] s.11 prefix reuse, [P1] "Prefix Caching", [P3] copy-on-write).  The
+ * result is pkv_paged_attn_decode's (softmax attention of each query over
+ * its seq_lens[s] tokens; the shared blocks are ordinary logical blocks
+ * 0..prefix_blocks-1 of every sequence); only the order of the work
+ * differs.  One pass attends every query row of the batch to the shared
+ * blocks, reading each block once per 32 rows (a dense
+ * [num_seqs * G, head_dim] x [head_dim, 16 * prefix_blocks] product on the
+ * matrix cores), and leaves per (sequence, query head) fp32 acc[head_dim],
+ * m, l at the start of the workspace.  The decode then reads each
+ * sequence's blocks past the prefix and folds those records in by
+ * log-sum-exp.
+ * The shared blocks are sequence 0's first prefix_blocks table entries.
+ * Preconditions (checked under PKV_CHECK=1, or by
+ * pkv_validate_shared_prefix): every sequence has the same first
+ * prefix_blocks entries and seq_lens[s] >= 16 * prefix_blocks; otherwise
+ * the result is undefined (no access leaves the caches).  A sequence with
+ * nothing past the prefix gets the prefix's attention.
+ * key / value / positions / slot_mapping_out: optional fused slot write, as
+ * in pkv_paged_attn_decode_append (key NULL: none; the new token must lie
+ * past the prefix, a shared block is never written).
+ * bf16 or f16 caches of the query dtype, head_dim 64 or 128, block_size 16,
+ * query group size <= 16.  workspace: at least
+ * pkv_paged_attn_shared_prefix_workspace_bytes bytes, 128-byte aligned;
+ * partition_size and flags as in pkv_paged_attn_decode (they apply to the
+ * blocks past the prefix).  Errors: PKV_EINVAL (bad sizes, null pointers,
+ * prefix_blocks outside [1, max_blocks_per_seq]), PKV_EUNSUPPORTED (dtype,
+ * head_dim, group size), PKV_EWORKSPACE, PKV_EHIP.
+ */
+pkv_status pkv_paged_attn_decode_shared_prefix(void* out, const void* query, int q_dtype, void* k_cache,
+                                               void* v_cache, int kv_dtype, const void* key, const void* value,
+                                               const int32_t* positions, int32_t* slot_mapping_out,
+                                               const int32_t* block_tables, int max_blocks_per_seq,
+                                               const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                               float sm_scale, int prefix_blocks, int partition_size,
+                                               unsigned flags, void* workspace, size_t workspace_bytes,
+                                               void* stream);
+
+/* Workspace bytes of pkv_paged_attn_decode_shared_prefix for sequences of
+ * at most max_seq_len tokens (0 when num_seqs <= 0). */
+size_t pkv_paged_attn_shared_prefix_workspace_bytes(int kv_dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                                                    int head_dim, int max_seq_len, int prefix_blocks,
+                                                    int partition_size);
+
+/* Host check of the shared-prefix preconditions on HOST copies of the
+ * tables: every row's first prefix_blocks entries equal row 0's, and
+ * seq_lens[s] >= prefix_blocks * block_size.  PKV_EINVAL with the first
+ * violation in pkv_last_error(). */
+pkv_status pkv_validate_shared_prefix(const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+                                      int num_seqs, int block_size, int prefix_blocks);
 
 /* Scale groups of the grouped quantiser and decode. */
 typedef enum pkv_scale_group {

@@ -16,7 +16,8 @@ __all__ = [
     "paged_attn_decode", "paged_attn_partition", "paged_attn_merge",
     "paged_attn_workspace_bytes", "paged_attn_num_partitions", "paged_attn_partition_size",
     "paged_attn_decode_multi", "paged_attn_decode_selected", "quest_summarize", "quest_summary_like", "quest_select",
-    "paged_attn_decode_append", "paged_attn_decode_grouped", "quantize_kv_grouped", "append_kv_quantized_grouped", "GROUP_CHANNEL",
+    "paged_attn_decode_append", "paged_attn_decode_shared_prefix", "paged_attn_shared_prefix_workspace_bytes",
+    "validate_shared_prefix", "paged_attn_decode_grouped", "quantize_kv_grouped", "append_kv_quantized_grouped", "GROUP_CHANNEL",
     "GROUP_TOKEN",
     "slot_mapping", "reshape_and_cache", "append_kv", "append_kv_quantized", "copy_blocks", "quantize_kv",
     "stream_read", "validate_tables", "BlockPool", "PrefixCache", "h2o_retain", "DTYPES",
@@ -62,6 +63,10 @@ _SIGS = {
                                         ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_append": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                       _i, ctypes.c_uint, _p, _sz, _p], _i),
+    "pkv_paged_attn_decode_shared_prefix": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i,
+                                             _i, _f, _i, _i, ctypes.c_uint, _p, _sz, _p], _i),
+    "pkv_paged_attn_shared_prefix_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i, _i], _sz),
+    "pkv_validate_shared_prefix": ([_p, _i, _p, _i, _i, _i], _i),
     "pkv_paged_attn_decode_grouped": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                        _i, ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_append_kv_quantized_grouped": ([_p, _p, _i, _p, _p, _p, _p, _i, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i,
@@ -492,6 +497,55 @@ def paged_attn_decode_append(out, query, k_cache, v_cache, key, value, positions
         BS, NB, float(sm_scale), int(partition_size), DECODE_STREAM_KV if stream_kv else 0, _ptr(workspace),
         ws_bytes, _stream(query)))
     return out
+
+
+def paged_attn_shared_prefix_workspace_bytes(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                            prefix_blocks, partition_size=0):
+    return lib.pkv_paged_attn_shared_prefix_workspace_bytes(_dtype_code(kv_dtype), num_seqs, num_q_heads,
+                                                            num_kv_heads, head_dim, max_seq_len, prefix_blocks,
+                                                            partition_size)
+
+
+def paged_attn_decode_shared_prefix(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, prefix_blocks,
+                                    key=None, value=None, positions=None, slot_mapping=None, partition_size=0,
+                                    workspace=None, stream_kv=False):
+    """Decode over a batch whose sequences all start with the same
+    ``prefix_blocks`` physical blocks (``pkv_paged_attn_decode_shared_prefix``):
+    the result of ``paged_attn_decode``, with the shared blocks read once per
+    32 query rows.  key/value/positions/slot_mapping: the optional fused slot
+    write of ``paged_attn_decode_append`` (the new token lies past the prefix)."""
+    _contig(out, query, k_cache, v_cache, key, value, positions, block_tables, seq_lens, slot_mapping, workspace)
+    S, Hq, D = query.shape
+    NB, BS, Hkv = k_cache.shape[:3]
+    if k_cache.shape[3] != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("shape mismatch between query, caches and out")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and seq_lens [num_seqs]")
+    if key is not None and (tuple(key.shape) != (S, Hkv, D) or value is None or value.shape != key.shape
+                            or key.dtype != k_cache.dtype or positions is None):
+        raise ValueError("key/value must be [S, Hkv, D] of the cache's dtype, with positions")
+    mbs = block_tables.shape[1]
+    if workspace is None:
+        nbytes = paged_attn_shared_prefix_workspace_bytes(_dtype(k_cache), S, Hq, Hkv, D, mbs * BS,
+                                                          int(prefix_blocks), partition_size)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=query.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.pkv_paged_attn_decode_shared_prefix(
+        _ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache), _ptr(key),
+        _ptr(value), _ptr(positions), _ptr(slot_mapping), _ptr(block_tables), mbs, _ptr(seq_lens), S, Hq, Hkv, D,
+        BS, NB, float(sm_scale), int(prefix_blocks), int(partition_size), DECODE_STREAM_KV if stream_kv else 0,
+        _ptr(workspace), ws_bytes, _stream(query)))
+    return out
+
+
+def validate_shared_prefix(block_tables, seq_lens, prefix_blocks, block_size=16):
+    """Host check of the shared-prefix preconditions (``pkv_validate_shared_prefix``)."""
+    bt = block_tables.detach().cpu().contiguous().to(torch.int32)
+    sl = seq_lens.detach().cpu().contiguous().to(torch.int32)
+    _check(lib.pkv_validate_shared_prefix(_ptr(bt), bt.shape[1], _ptr(sl), sl.shape[0], block_size,
+                                          int(prefix_blocks)))
 
 
 def paged_attn_decode_grouped(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_tile_scales,

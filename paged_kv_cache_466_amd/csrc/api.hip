@@ -462,6 +462,109 @@ extern "C" pkv_status pkv_paged_attn_decode_grouped(
   return hip_status(launch_paged_attn_merge(a), who);
 }
 
+// ---------------------------------------------------------------------------
+// shared-prefix decode
+// ---------------------------------------------------------------------------
+extern "C" size_t pkv_paged_attn_shared_prefix_workspace_bytes(int kv_dtype, int num_seqs, int num_q_heads,
+                                                               int num_kv_heads, int head_dim, int max_seq_len,
+                                                               int prefix_blocks, int partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || prefix_blocks < 0) return 0;
+  const int suffix = max_seq_len - prefix_blocks * 16;
+  return prefix_area_bytes(num_seqs, num_q_heads, head_dim) +
+         pkv_paged_attn_workspace_bytes(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        suffix > 0 ? suffix : 0, partition_size);
+}
+
+extern "C" pkv_status pkv_validate_shared_prefix(const int32_t* block_tables, int max_blocks_per_seq,
+                                                 const int32_t* seq_lens, int num_seqs, int block_size,
+                                                 int prefix_blocks) {
+  const char* who = "pkv_validate_shared_prefix";
+  if (num_seqs < 0 || block_size <= 0 || prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq)
+    return fail(PKV_EINVAL, "%s: bad sizes", who);
+  if (num_seqs > 0 && (!block_tables || !seq_lens)) return fail(PKV_EINVAL, "%s: null table", who);
+  for (int s = 0; s < num_seqs; ++s) {
+    if ((long long)seq_lens[s] < (long long)prefix_blocks * block_size)
+      return fail(PKV_EINVAL, "%s: seq_lens[%d] = %d is shorter than the %d-token prefix", who, s, seq_lens[s],
+                  prefix_blocks * block_size);
+    for (int i = 0; i < prefix_blocks; ++i)
+      if (block_tables[(size_t)s * max_blocks_per_seq + i] != block_tables[i])
+        return fail(PKV_EINVAL, "%s: block_tables[%d][%d] = %d differs from sequence 0's %d", who, s, i,
+                    block_tables[(size_t)s * max_blocks_per_seq + i], block_tables[i]);
+  }
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_shared_prefix(
+    void* out, const void* query, int q_dtype, void* k_cache, void* v_cache, int kv_dtype, const void* key,
+    const void* value, const int32_t* positions, int32_t* slot_mapping_out, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int block_size, int num_blocks, float sm_scale, int prefix_blocks, int partition_size, unsigned flags,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "pkv_paged_attn_decode_shared_prefix";
+  if (kv_dtype != q_dtype || (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16))
+    return fail(PKV_EUNSUPPORTED, "%s: built for bf16 / f16 caches of the query dtype", who);
+  if (prefix_blocks < 1 || prefix_blocks > max_blocks_per_seq)
+    return fail(PKV_EINVAL, "%s: prefix_blocks must lie in [1, max_blocks_per_seq]", who);
+  if (key && (!value || !positions)) return fail(PKV_EINVAL, "%s: key given without value or positions", who);
+  if (num_seqs > 0 && (long long)num_seqs * max_blocks_per_seq >= (1LL << 29))
+    return fail(PKV_EUNSUPPORTED, "%s: batch too large (num_seqs * max_blocks_per_seq >= 2^29)", who);
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_EINVAL, "%s: negative or zero size", who);
+  pkv_status st = check_cache_shape(who, block_size, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if (num_q_heads % num_kv_heads) return fail(PKV_EINVAL, "%s: num_q_heads %% num_kv_heads != 0", who);
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(PKV_EUNSUPPORTED, "%s: query group size above 16 is not built", who);
+  if (flags & ~(unsigned)PKV_DECODE_STREAM_KV) return fail(PKV_EINVAL, "%s: unknown flags 0x%x", who, flags);
+  const size_t pre_bytes = num_seqs > 0 ? prefix_area_bytes(num_seqs, num_q_heads, head_dim) : 0;
+  if (num_seqs > 0) {
+    if (!workspace || workspace_bytes < pre_bytes)
+      return fail(PKV_EWORKSPACE, "%s: workspace of at least %zu bytes needed, %zu given", who, pre_bytes,
+                  workspace_bytes);
+    if (((uintptr_t)workspace) & 127) return fail(PKV_EINVAL, "%s: workspace must be 128-byte aligned", who);
+    if (!block_tables) return fail(PKV_EINVAL, "%s: null pointer argument", who);
+  }
+  // the suffix decode: tables from entry prefix_blocks on, lengths past the prefix
+  AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, nullptr, nullptr,
+                         block_tables ? block_tables + prefix_blocks : nullptr, max_blocks_per_seq - prefix_blocks,
+                         seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sm_scale,
+                         partition_size, 0, 0, flags, stream);
+  a.table_stride = max_blocks_per_seq;
+  a.len_off = prefix_blocks * block_size;
+  a.prefix = (const float*)workspace;
+  if (key) {
+    a.new_k = key;
+    a.new_v = value;
+    a.positions = positions;
+    a.slots_out = slot_mapping_out;
+  }
+  st = prepare_attn(a, who, workspace ? (char*)workspace + pre_bytes : nullptr,
+                               workspace_bytes > pre_bytes ? workspace_bytes - pre_bytes : 0, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if (check_env()) {
+    st = device_check(block_tables, max_blocks_per_seq, seq_lens, num_seqs, block_size, num_blocks, nullptr, 0,
+                      stream);
+    if (st != PKV_OK) return st;
+    std::vector<int32_t> bt((size_t)num_seqs * max_blocks_per_seq), sl(num_seqs);
+    hipStream_t hs = (hipStream_t)stream;
+    int e = hipMemcpyAsync(bt.data(), block_tables, bt.size() * 4, hipMemcpyDeviceToHost, hs);
+    e |= hipMemcpyAsync(sl.data(), seq_lens, sl.size() * 4, hipMemcpyDeviceToHost, hs);
+    e |= hipStreamSynchronize(hs);
+    if (e != hipSuccess) return fail(PKV_EHIP, "PKV_CHECK: copying tables to the host failed");
+    st = pkv_validate_shared_prefix(bt.data(), max_blocks_per_seq, sl.data(), num_seqs, block_size, prefix_blocks);
+    if (st != PKV_OK) return st;
+  }
+  // the shared blocks are sequence 0's first prefix_blocks entries
+  st = hip_status(launch_prefix_attn(query, q_dtype, k_cache, v_cache, block_tables, prefix_blocks,
+                                     (float*)workspace, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                     sm_scale, stream),
+                  who);
+  if (st != PKV_OK) return st;
+  st = hip_status(launch_paged_attn_partition(a), who);
+  if (st != PKV_OK) return st;
+  return hip_status(launch_paged_attn_merge(a), who);
+}
+
 extern "C" size_t pkv_quest_scratch_bytes(int num_seqs, int num_kv_heads, int max_blocks_per_seq) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
   return align256((size_t)num_seqs * num_kv_heads * max_blocks_per_seq * 8);

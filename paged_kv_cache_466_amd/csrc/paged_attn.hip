@@ -73,6 +73,13 @@ struct AttnParams {
   const void* new_v;
   const int32_t* positions;
   int32_t* slots_out;
+  // Shared-prefix decode: block_tables starts at the first suffix entry of
+  // row 0, rows are tstride entries apart (tstride = mbs otherwise), and a
+  // sequence's length counts from token len_off.  prefix: per (sequence,
+  // query head) acc[D], m, l of the shared blocks, folded into the result.
+  int tstride;
+  int len_off;
+  const float* prefix;
   float scale_log2;     // sm_scale * log2(e)
 };
 
@@ -88,8 +95,13 @@ __device__ __forceinline__ bool kept(int t, int L, int sink, int window) {
   return (t < L) & (all | (t < sink) | (t >= L - window));
 }
 
+// Kept length of sequence s: its tokens past len_off, at most mbs blocks.
+__device__ __forceinline__ int seq_len_at(const AttnParams& p, int s) {
+  return clamp_len(p.seq_lens[s] - p.len_off, p.mbs);
+}
+
 __device__ __forceinline__ int table_entry(const AttnParams& p, int s, int lb) {
-  int pb = p.block_tables[(size_t)s * p.mbs + lb];
+  int pb = p.block_tables[(size_t)s * p.tstride + lb];
   // a bad table must not make the kernel leave the cache arrays
   return (pb < 0 || pb >= p.num_blocks) ? 0 : pb;
 }
@@ -332,7 +344,7 @@ __device__ __forceinline__ SeqWindow load_window(const AttnParams& p, int s0, in
   w.s0 = s0;
   w.base = base;
   const int s = s0 + lane;
-  w.L = s < p.num_seqs ? clamp_len(p.seq_lens[s], p.mbs) : 0;
+  w.L = s < p.num_seqs ? seq_len_at(p, s) : 0;
   if constexpr (SEL) w.n = min(p.budget, (w.L + kBS - 1) / kBS);
   else w.n = seq_units(w.L, p.partition_size, p.sink, p.window).n;
   const int incl = lane_scan_incl(w.n, lane);
@@ -395,11 +407,15 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
   const int S = p.num_seqs;
   const int w = blockIdx.x;
   // workgroup s of the first head group zeroes sequence s when it is empty
-  // (16-bit outputs: zero bits are zero)
-  if (blockIdx.y == 0 && w < S && clamp_len(p.seq_lens[w], p.mbs) == 0) {
-    const int n16 = p.num_q_heads * p.qtok * head_dim / 8;
-    uint4* o = reinterpret_cast<uint4*>(p.out) + (size_t)w * n16;
-    for (int i = lane; i < n16; i += 64) o[i] = make_uint4(0, 0, 0, 0);
+  // (16-bit outputs: zero bits are zero); with a shared prefix its output is
+  // the prefix's, written by the kernel
+  if (blockIdx.y == 0 && w < S && seq_len_at(p, w) == 0) {
+    if (!p.prefix) {
+      const int n16 = p.num_q_heads * p.qtok * head_dim / 8;
+      uint4* o = reinterpret_cast<uint4*>(p.out) + (size_t)w * n16;
+      for (int i = lane; i < n16; i += 64) o[i] = make_uint4(0, 0, 0, 0);
+    }
+    // nothing for the merge to do
     if (p.plan && lane == 0) reinterpret_cast<int4*>(p.plan)[w] = make_int4(0, 0, 0, 0);
   }
 
@@ -457,7 +473,7 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
             // SEL: offset of the selection entry (KV head 0); the block's
             // first token comes with the entry
             list[nb + j] = SEL ? make_int4((s * p.num_kv_heads * p.budget + lb) * 8, 0, L, key)
-                               : make_int4((s * p.mbs + lb) * 4, t0 | (masked ? (int)0x80000000u : 0), L, key);
+                               : make_int4((s * p.tstride + lb) * 4, t0 | (masked ? (int)0x80000000u : 0), L, key);
           }
           if (lane == 0 && nseg < kMaxQuerySegs) segs[nseg] = s;
           // the workgroup holding a sequence's last unit writes its new token
@@ -537,6 +553,24 @@ void paged_attn_wave_kernel(AttnParams p) {
   if (wave == 0) build_block_list<SEL>(p, D, lane, list, segs, counts, ends);
   __syncthreads();
   if (kvh >= p.num_kv_heads) return;
+  // shared prefix: built for 16-bit caches read through the block table
+  constexpr bool kPrefixFold = !kCodes && !SEL && !GRP;
+  if constexpr (kPrefixFold) {
+    if (p.prefix && (int)blockIdx.x < p.num_seqs && seq_len_at(p, blockIdx.x) == 0) {
+      // nothing past the shared blocks: the output of this head group is
+      // the prefix's, acc / l
+      const size_t s = blockIdx.x;
+      constexpr int CPR = D / 4;
+      for (int i = lane; i < G * CPR; i += 64) {
+        const size_t row = s * p.num_q_heads + kvh * G + i / CPR;
+        const float* pr = p.prefix + row * (D + 4);
+        const float l = pr[D + 1];
+        const floatx4 a = *reinterpret_cast<const floatx4*>(pr + 4 * (i % CPR)) * (l > 0.f ? 1.f / l : 0.f);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + 4 * (i % CPR)) =
+            make_uint2(MO::pack2(a[0], a[1]), MO::pack2(a[2], a[3]));
+      }
+    }
+  }
   const int nb = __builtin_amdgcn_readfirstlane(counts[0]);
   const int nseg = __builtin_amdgcn_readfirstlane(counts[1]);
 
@@ -549,9 +583,11 @@ void paged_attn_wave_kernel(AttnParams p) {
     constexpr int CH = D / 8;   // 16-byte pieces of a 16-bit row
     for (int j = 0; j < nend; ++j) {
       const int s = __builtin_amdgcn_readfirstlane(ends[j]);
-      const int pos = p.positions[s];
+      const int pos_abs = p.positions[s];
+      if (pos_abs < 0) continue;
+      const int pos = pos_abs - p.len_off;   // len_off is whole blocks
       if (pos < 0 || pos / kBS >= p.mbs) continue;
-      const int pb = p.block_tables[(size_t)s * p.mbs + pos / kBS];
+      const int pb = p.block_tables[(size_t)s * p.tstride + pos / kBS];
       if (pb < 0 || pb >= p.num_blocks) continue;
       const size_t slot = (size_t)pb * kBS + pos % kBS;
       if (lane < 2 * CH) {
@@ -758,6 +794,20 @@ void paged_attn_wave_kernel(AttnParams p) {
     const size_t seq = (size_t)(key >> 8);
     float l = lsum + __shfl_xor(lsum, 16, 64);
     l += __shfl_xor(l, 32, 64);
+    if constexpr (kPrefixFold) {
+      // a whole sequence after a shared prefix: fold in the prefix's record
+      // (acc_p, m_p, l_p) of this lane's head by log-sum-exp
+      if (whole && p.prefix && g < NCOL) {
+        const float* pr = p.prefix + (seq * p.num_q_heads + kvh * G + g) * (D + 4);
+        const float pm = pr[D], pl = pr[D + 1];
+        const float mx = fmaxf(m2, pm);
+        const float wsuf = __builtin_amdgcn_exp2f(m2 - mx), wpre = __builtin_amdgcn_exp2f(pm - mx);
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+          acc[n] = acc[n] * wsuf + *reinterpret_cast<const floatx4*>(pr + 16 * n + 4 * kg) * wpre;
+        l = l * wsuf + pl * wpre;
+      }
+    }
     constexpr int RSTRIDE = D + 4;                      // floats per padded LDS row
     static_assert((8 * RSTRIDE + 32) * 4 <= C::VSTAGE, "result staging must fit the V staging area");
     float* rl = reinterpret_cast<float*>(vstage);
@@ -1029,7 +1079,7 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
   const int kvh = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int G = p.num_q_heads / p.num_kv_heads;
-  const int L = clamp_len(p.seq_lens[s], p.mbs);
+  const int L = seq_len_at(p, s);
   const bool single = p.num_partitions == 1;
   const int t_begin = part * p.partition_size;
   const size_t head0 = (size_t)s * p.num_q_heads + kvh * G;
@@ -1136,30 +1186,35 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 }
 
 // ===========================================================================
-// Merge of the wave kernel's records: for each (query head, sequence) cut
-// over several workgroups, out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M)
-// l_i over its records, one per workgroup it reaches.  Whole sequences were
-// finished by their waves and empty ones zeroed: their plan entries name one
-// workgroup.  8 record rows at a time are read by D/4 threads with 16-byte
-// loads, 4 rows per thread in flight.
+// Merge of the wave kernel's records.  For each sequence cut over several
+// workgroups and each record column (query head of a group, times query
+// token), out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i over its
+// records, one per workgroup it reaches; after a shared prefix, the
+// prefix's record of the head (acc[D], m, l at `prefix`) is one more term.
+// Whole sequences were finished by their waves and empty ones zeroed: their
+// plan entries name one workgroup, and their workgroups return at once.
+// One workgroup per (sequence, KV head, group of cpw columns): the columns of
+// one record sit next to each other, so a workgroup reads whole record rows.
+// Its 256 threads take (column, 16-byte piece of the row) outputs; when
+// those are fewer than 256, the records are shared out among `parts` thread
+// groups whose partial sums meet in LDS.  cpw is chosen on the host so that
+// the grid has about a thousand workgroups: most of a workgroup's time is
+// the latency of a few dependent loads, hidden by having many in flight.
 // ===========================================================================
 template <typename QT, int D>
 __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const float* ws, const int* plan,
                                                                int rec_floats, int num_q_heads, int num_kv_heads,
-                                                               int qtok) {
-  constexpr int TPR = D / 4;               // threads per record row
-  constexpr int ROWS = 256 / TPR;
-  constexpr int U = 4;
+                                                               int qtok, int cpw, const float* prefix) {
+  constexpr int V4 = D / 4;   // 16-byte pieces of an output row
   __shared__ float red[256];
-  __shared__ floatx4 part_num[ROWS][TPR];
-  __shared__ float part_den[ROWS];
-  // x: (query token, query head); y: sequence
-  const int t = blockIdx.x / num_q_heads, h = blockIdx.x % num_q_heads, s = blockIdx.y;
+  __shared__ float mcol[16];
+  __shared__ floatx4 pnum[256];
+  __shared__ float pden[256];
+  const int s = blockIdx.x, kvh = blockIdx.y, col0 = blockIdx.z * cpw;
   const int tid = threadIdx.x;
   const int G = num_q_heads / num_kv_heads;
-  const int kvh = h / G;
-  const int g = t * G + h % G;             // the record column
   const int NCOL = G * qtok;
+  const int ncols = min(cpw, NCOL - col0);
   // (slot of the first record, first workgroup, last workgroup)
   const int4 e = reinterpret_cast<const int4*>(plan)[s];
   if (e.z <= e.y) return;
@@ -1169,29 +1224,49 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
     const int slot = i == 0 ? e.x : 2 * (e.y + i);
     return ws + ((size_t)slot * num_kv_heads + kvh) * rec_floats;
   };
-  float mx = -INFINITY;
-  for (int i = tid; i < np; i += 256) mx = fmaxf(mx, rec_of(i)[NCOL * D + g]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
+  // the prefix record of column c (a shared prefix goes with one query token)
+  auto pre_of = [&](int c) { return prefix + ((size_t)s * num_q_heads + kvh * G + c) * (D + 4); };
+
+  // 1. M of each column: thread (column tid % 16, records tid / 16 + 16 k)
+  {
+    const int c = tid & 15;
+    float mx = -INFINITY;
+    if (c < ncols)
+      for (int i = tid >> 4; i < np; i += 16) mx = fmaxf(mx, rec_of(i)[NCOL * D + col0 + c]);
+    red[tid] = mx;
   }
-  const float M = red[0];
-  const int row = tid / TPR, c = tid % TPR;
+  __syncthreads();
+  if (tid < 16) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, red[16 * j + tid]);
+    if (prefix && tid < ncols) mx = fmaxf(mx, pre_of(col0 + tid)[D]);
+    mcol[tid] = mx;
+  }
+  __syncthreads();
+
+  // 2. thread (output o, part): records part, part + parts, ...
+  const int outs = cpw * V4;          // <= 256 (cpw <= 256 / V4, checked on the host)
+  const int parts = 256 / outs;
+  const int o = tid % outs, part = tid / outs;
+  const int c = o / V4, d4 = o % V4;
+  const bool act = part < parts && c < ncols;
+  const int col = col0 + c;
   floatx4 num = floatx4{0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  if (M != -INFINITY) {
-    int i = row;
-    for (; i + (U - 1) * ROWS < np; i += U * ROWS) {
+  const float M = act ? mcol[c] : -INFINITY;
+  if (act && M != -INFINITY) {
+    constexpr int U = 4;   // records in flight per thread
+    int i = part;
+    for (; i + (U - 1) * parts < np; i += U * parts) {
       float mi[U], li[U];
       floatx4 a[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float* r = rec_of(i + u * ROWS);
-        mi[u] = r[NCOL * D + g];
-        li[u] = r[NCOL * D + 16 + g];
-        a[u] = *reinterpret_cast<const floatx4*>(r + g * D + 4 * c);
+        const float* r = rec_of(i + u * parts);
+        mi[u] = r[NCOL * D + col];
+        li[u] = r[NCOL * D + 16 + col];
+        a[u] = *reinterpret_cast<const floatx4*>(r + col * D + 4 * d4);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -1200,27 +1275,35 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
         den += w * li[u];
       }
     }
-    for (; i < np; i += ROWS) {
+    for (; i < np; i += parts) {
       const float* r = rec_of(i);
-      const float w = exp2f(r[NCOL * D + g] - M);
-      num += w * *reinterpret_cast<const floatx4*>(r + g * D + 4 * c);
-      den += w * r[NCOL * D + 16 + g];
+      const float w = exp2f(r[NCOL * D + col] - M);
+      num += w * *reinterpret_cast<const floatx4*>(r + col * D + 4 * d4);
+      den += w * r[NCOL * D + 16 + col];
     }
   }
-  part_num[row][c] = num;
-  if (c == 0) part_den[row] = den;
-  __syncthreads();
-  if (tid < TPR) {
-    floatx4 n = floatx4{0.f, 0.f, 0.f, 0.f};
-    float dn = 0.f;
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      n += part_num[r][tid];
-      dn += part_den[r];
+  if (parts > 1) {
+    pnum[tid] = num;
+    pden[tid] = den;
+    __syncthreads();
+    if (part == 0) {
+      for (int j = 1; j < parts; ++j) {
+        num += pnum[j * outs + o];
+        den += pden[j * outs + o];
+      }
     }
-    const size_t o = (((size_t)s * qtok + t) * num_q_heads + h) * D + 4 * tid;
+  }
+  if (part == 0 && act) {
+    if (prefix) {
+      const float* pre = pre_of(col);
+      const float w = exp2f(pre[D] - M);
+      num += w * *reinterpret_cast<const floatx4*>(pre + 4 * d4);
+      den += w * pre[D + 1];
+    }
+    const int t = col / G, h = kvh * G + col % G;
+    const size_t oi = (((size_t)s * qtok + t) * num_q_heads + h) * D + 4 * d4;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) store_out<QT>(out, o + k, dn > 0.f ? n[k] / dn : 0.f);
+    for (int k = 0; k < 4; ++k) store_out<QT>(out, oi + k, den > 0.f ? num[k] / den : 0.f);
   }
 }
 
@@ -1309,6 +1392,289 @@ __global__ __launch_bounds__(256) void paged_attn_merge_units_kernel(void* out, 
 }
 
 // ===========================================================================
+// Shared-prefix pass
+//
+// When every sequence of a batch starts with the same P physical blocks (a
+// prompt stored once and shared through the block tables: prefix caching,
+// "KV Cache Engineering" section 11; copy-on-write forks, Learning-AI topic
+// t13_4), the scores of the batch's S*G query rows of one KV head against
+// those blocks are one dense product, Q [S*G, D] x K^T [D, 16 P], followed
+// by P.V over the same blocks.  This pass reads each shared block once per
+// 32 rows instead of once per sequence.  A workgroup of four waves takes 32
+// rows of one KV head (row r is sequence r / G, head r % G of the group) and
+// each wave a quarter of the blocks.  Workgroup n takes KV head n % Hkv:
+// consecutive workgroups go to the eight XCDs in turn, so with Hkv dividing
+// or a multiple of 8 every XCD serves whole heads and one head's shared
+// blocks stay in one XCD's L2 for all of its row tiles.  Per block a wave computes S^T = K Q^T
+// for both of its 16-row column groups from one K tile in registers
+// (v_mfma_f32_16x16x32), and out^T += V^T P^T for both from one transposed
+// read of the V tile (v_mfma_f32_16x16x16).  The four waves' online-softmax
+// states are combined in LDS by log-sum-exp into one record per (sequence,
+// query head): acc[D] (unnormalised), m (log2 domain), l.  The suffix decode
+// folds these records into its own results.
+// ===========================================================================
+constexpr int kPrefixWaves = 4;
+constexpr int kPrefixCG = 2;                  // 16-row column groups per wave
+constexpr int kPrefixRows = 16 * kPrefixCG;   // rows of a workgroup (every wave takes all of them)
+constexpr int kPrefixTable = 2048;            // shared-block entries staged in LDS at a time
+
+template <int D>
+__host__ __device__ constexpr int prefix_lds_bytes() {
+  return kPrefixWaves * kBS * (2 * D + 16) + kPrefixTable * 4 + kPrefixWaves * kPrefixRows * (D + 4) * 4;
+}
+
+struct PrefixParams {
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* table;   // the shared physical blocks, in logical order
+  float* rec;             // [S][Hq][D + 4]
+  int num_prefix_blocks, num_seqs, num_q_heads, num_kv_heads, num_blocks;
+  float scale_log2;
+};
+
+template <typename QT, int D>
+__global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixParams p) {
+  typedef Mfma<QT> M;
+  constexpr int NC = D / 32, NN = D / 16;
+  constexpr int ROW_BYTES = 2 * D;
+  constexpr int LANES_PER_ROW = ROW_BYTES / 16;
+  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+  constexpr int VCH = kBS / ROWS_PER_PASS;
+  constexpr int VROW = 2 * D + 16;   // LDS bytes per staged V row (padded)
+  constexpr int DEPTH = 4;           // register tiles in the ring
+  constexpr float kSlack = 8.0f;     // rescale only when a score passes the max by 2^8
+  constexpr int RS = D + 4;          // floats per state row in LDS
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int nrows = p.num_seqs * G;
+  const int r0 = (blockIdx.x / p.num_kv_heads) * kPrefixRows;
+  const int g = lane & 15;    // column of S^T / out^T
+  const int kg = lane >> 4;   // lane group: k-chunk of the operands, 4-row slab of the outputs
+  uint8_t* vst = lds + wave * kBS * VROW;
+  int* tab = reinterpret_cast<int*>(lds + kPrefixWaves * kBS * VROW);
+  float* states = reinterpret_cast<float*>(tab + kPrefixTable);
+  // query / record row of row r
+  auto qrow = [&](int r) { return (size_t)(r / G) * p.num_q_heads + kvh * G + r % G; };
+
+  // the B operands: column g of group cg is row r0 + 16 cg + g (zeros past the last row)
+  typename M::vec8 qop[kPrefixCG][NC];
+#pragma unroll
+  for (int cg = 0; cg < kPrefixCG; ++cg) {
+    const int r = r0 + 16 * cg + g;
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.query) + qrow(r < nrows ? r : 0) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 v = r < nrows ? *reinterpret_cast<const uint4*>(q + 32 * c + 8 * kg) : make_uint4(0, 0, 0, 0);
+      qop[cg][c] = __builtin_bit_cast(typename M::vec8, v);
+    }
+  }
+  float m2[kPrefixCG], lsum[kPrefixCG];
+  floatx4 acc[kPrefixCG][NN];
+#pragma unroll
+  for (int cg = 0; cg < kPrefixCG; ++cg) {
+    m2[cg] = -INFINITY;
+    lsum[cg] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) acc[cg][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int row_stride = p.num_kv_heads * ROW_BYTES;   // bytes between token rows
+  const int tile_bytes = (kBS - 1) * row_stride + ROW_BYTES;
+  const uint8_t* k_head = reinterpret_cast<const uint8_t*>(p.k_cache) + (size_t)kvh * ROW_BYTES;
+  const uint8_t* v_head = reinterpret_cast<const uint8_t*>(p.v_cache) + (size_t)kvh * ROW_BYTES;
+  // K: lane (row g, group kg) reads elements 32c + 8kg .. +7 of its row, the
+  // A operand of MFMA c; V: whole rows, LANES_PER_ROW lanes per row
+  const int k_off = g * row_stride + 16 * kg;
+  int v_off[VCH], v_row[VCH];
+#pragma unroll
+  for (int ps = 0; ps < VCH; ++ps) {
+    v_row[ps] = ps * ROWS_PER_PASS + lane / LANES_PER_ROW;
+    v_off[ps] = v_row[ps] * row_stride + (lane % LANES_PER_ROW) * 16;
+  }
+
+  struct Tile {
+    uint4 k[NC];
+    uint4 v[VCH];
+  };
+  // entry j of the staged table; j >= end reads nothing (zero-size resource)
+  auto load_tile = [&](Tile& t, int j, int end) {
+    const bool valid = j < end;
+    const int pb = __builtin_amdgcn_readfirstlane(tab[valid ? j : 0]);
+    const size_t tile = (size_t)pb * kBS * row_stride;
+    const int nbytes = valid ? tile_bytes : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_head + tile, nbytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_head + tile, nbytes);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) t.k[c] = buf_load16(kr, k_off + 64 * c);
+#pragma unroll
+    for (int ps = 0; ps < VCH; ++ps) t.v[ps] = buf_load16(vr, v_off[ps]);
+  };
+
+  auto process = [&](const Tile& t) {
+#pragma unroll
+    for (int ps = 0; ps < VCH; ++ps)
+      *reinterpret_cast<uint4*>(vst + v_row[ps] * VROW + (lane % LANES_PER_ROW) * 16) = t.v[ps];
+    shortx4 pop[kPrefixCG];
+#pragma unroll
+    for (int cg = 0; cg < kPrefixCG; ++cg) {
+      floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::vec8, t.k[c]), qop[cg][c], sacc);
+      // lane holds tokens 4 kg + i of the block for column g
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * p.scale_log2;
+      const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (__ballot(lm > m2[cg] + kSlack)) {
+        float bmax = fmaxf(lm, __shfl_xor(lm, 16, 64));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        const float mnew = fmaxf(m2[cg], bmax);
+        const float alpha = __builtin_amdgcn_exp2f(m2[cg] - mnew);   // 0 while m2 = -inf
+        lsum[cg] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) acc[cg][n] *= alpha;
+        m2[cg] = mnew;
+      }
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m2[cg]);
+      const uint32_t p01 = M::pack2(pr[0], pr[1]);
+      const uint32_t p23 = M::pack2(pr[2], pr[3]);
+      // the denominator sums the 16-bit weights the MFMA uses
+      lsum[cg] += M::sum2(p01) + M::sum2(p23);
+      pop[cg] = __builtin_bit_cast(shortx4, make_uint2(p01, p23));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane i of each 16-lane group reads row 4kg + i/4, columns 4(i%4)..+3
+    const uint8_t* rd = vst + (4 * kg + (g >> 2)) * VROW + (g & 3) * 8;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) {
+      const shortx4 vt = M::tr_read(rd + n * 32);
+#pragma unroll
+      for (int cg = 0; cg < kPrefixCG; ++cg) acc[cg][n] = M::pv(vt, pop[cg], acc[cg][n]);
+    }
+  };
+
+  const int P = p.num_prefix_blocks;
+  for (int c0 = 0; c0 < P; c0 += kPrefixTable) {
+    const int cn = min(kPrefixTable, P - c0);
+    __syncthreads();   // the previous chunk's entries are no longer read
+    for (int i = threadIdx.x; i < cn; i += 64 * kPrefixWaves) {
+      const int pb = p.table[c0 + i];
+      tab[i] = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the caches
+    }
+    __syncthreads();
+    // this wave's blocks: entries [j0, j1) of the chunk, from a starting
+    // point that differs between the row tiles of a head (the softmax does
+    // not depend on the order): the tiles then ask for different blocks at
+    // once instead of all waiting on the same one, and the head's blocks
+    // reach L2 in one round of memory latency rather than one per block
+    const int j0 = wave * cn / kPrefixWaves, j1 = (wave + 1) * cn / kPrefixWaves;
+    const int n = j1 - j0;
+    const int rot = n > 0 ? (int)((blockIdx.x / p.num_kv_heads) % n) : 0;
+    auto entry = [&](int k) { return k < n ? j0 + (k + rot < n ? k + rot : k + rot - n) : j1; };
+    Tile ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], entry(d), j1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int k0 = 0; k0 < n; k0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int k = k0 + d;
+        if (k < n) process(ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(ring[d], entry(k + DEPTH), j1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // the waves' states -> LDS, then one record per row
+#pragma unroll
+  for (int cg = 0; cg < kPrefixCG; ++cg) {
+    float l = lsum[cg] + __shfl_xor(lsum[cg], 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    float* st = states + (size_t)(wave * kPrefixRows + 16 * cg + g) * RS;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) *reinterpret_cast<floatx4*>(st + 16 * n + 4 * kg) = acc[cg][n];
+    if (kg == 0) {
+      st[D] = m2[cg];
+      st[D + 1] = l;
+    }
+  }
+  __syncthreads();
+  // thread -> (row rr, eighth ch of its D elements); a wave that took no
+  // block has m = -inf and weighs nothing
+  const int rr = threadIdx.x >> 3, ch = threadIdx.x & 7;
+  const int r = r0 + rr;
+  if (r < nrows) {
+    float mw[kPrefixWaves], mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kPrefixWaves; ++w) {
+      mw[w] = states[(w * kPrefixRows + rr) * RS + D];
+      mx = fmaxf(mx, mw[w]);
+    }
+    float wt[kPrefixWaves], l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPrefixWaves; ++w) {
+      wt[w] = __builtin_amdgcn_exp2f(mw[w] - mx);
+      l += wt[w] * states[(w * kPrefixRows + rr) * RS + D + 1];
+    }
+    float* dst = p.rec + qrow(r) * RS;
+    constexpr int E = D / 8;   // elements per thread
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      floatx4 a = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kPrefixWaves; ++w)
+        a += wt[w] * *reinterpret_cast<const floatx4*>(states + (w * kPrefixRows + rr) * RS + ch * E + e);
+      *reinterpret_cast<floatx4*>(dst + ch * E + e) = a;
+    }
+    if (ch == 0) *reinterpret_cast<floatx4*>(dst + D) = floatx4{mx, l, 0.f, 0.f};
+  }
+}
+
+template <typename QT, int D>
+static int launch_prefix_d(const PrefixParams& p, hipStream_t st) {
+  auto kernel = prefix_attn_kernel<QT, D>;
+  static std::atomic<bool> lds_set[64];
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kernel), prefix_lds_bytes<D>(), lds_set);
+  if (e != hipSuccess) return e;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const dim3 grid(((p.num_seqs * G + kPrefixRows - 1) / kPrefixRows) * p.num_kv_heads);
+  kernel<<<grid, 64 * kPrefixWaves, prefix_lds_bytes<D>(), st>>>(p);
+  return hipGetLastError();
+}
+
+int launch_prefix_attn(const void* query, int q_dtype, const void* k_cache, const void* v_cache,
+                       const int32_t* table, int prefix_blocks, float* records, int num_seqs, int num_q_heads,
+                       int num_kv_heads, int head_dim, int num_blocks, float sm_scale, void* stream) {
+  if (num_seqs == 0 || prefix_blocks == 0) return hipSuccess;
+  PrefixParams p;
+  p.query = query;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.table = table;
+  p.rec = records;
+  p.num_prefix_blocks = prefix_blocks;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.scale_log2 = sm_scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  if (q_dtype == PKV_BF16) return head_dim == 64 ? launch_prefix_d<BF16, 64>(p, st) : launch_prefix_d<BF16, 128>(p, st);
+  return head_dim == 64 ? launch_prefix_d<F16, 64>(p, st) : launch_prefix_d<F16, 128>(p, st);
+}
+
+// ===========================================================================
 // launchers
 // ===========================================================================
 static AttnParams make_params(const AttnArgs& a) {
@@ -1327,6 +1693,9 @@ static AttnParams make_params(const AttnArgs& a) {
   p.num_seqs = a.num_seqs;
   // a selected decode takes lengths as they are (its pages come with the selection)
   p.mbs = a.selected ? (1 << 27) - 1 : a.max_blocks_per_seq;
+  p.tstride = a.table_stride > 0 ? a.table_stride : p.mbs;
+  p.len_off = a.len_off;
+  p.prefix = a.prefix;
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.num_blocks = a.num_blocks;
@@ -1340,7 +1709,7 @@ static AttnParams make_params(const AttnArgs& a) {
   p.budget = a.budget;
   p.qtok = a.qtok > 0 ? a.qtok : 1;
   p.table_bytes = a.selected ? (int)((long long)a.num_seqs * a.num_kv_heads * a.budget * 8)
-                             : (int)((long long)a.num_seqs * a.max_blocks_per_seq * 4);
+                             : (int)(((long long)(a.num_seqs - 1) * p.tstride + a.max_blocks_per_seq) * 4);
   p.k_chan = a.k_chan;
   p.new_k = a.new_k;
   p.new_v = a.new_v;
@@ -1462,8 +1831,17 @@ int launch_paged_attn_merge(const AttnArgs& a) {
     return hipGetLastError();
   }
   if (!a.may_split) return hipSuccess;
-#define PKV_MERGE(QT, D) \
-  paged_attn_merge_kernel<QT, D><<<grid, 256, 0, st>>>(a.out, a.ws, a.plan, rec, a.num_q_heads, a.num_kv_heads, T)
+  // columns per workgroup: halved from a whole record row (at most 256
+  // threads' worth of 16-byte pieces) while the grid is under ~1024
+  // workgroups
+  const int NCOL = a.num_q_heads / a.num_kv_heads * T;
+  int cpw = NCOL < 1024 / a.head_dim ? NCOL : 1024 / a.head_dim;
+  const long long pairs = (long long)a.num_seqs * a.num_kv_heads;
+  while (cpw > 1 && pairs * ((NCOL + cpw - 1) / cpw) < 1024) cpw = (cpw + 1) / 2;
+  const dim3 mgrid(a.num_seqs, a.num_kv_heads, (NCOL + cpw - 1) / cpw);
+#define PKV_MERGE(QT, D)                                                                                   \
+  paged_attn_merge_kernel<QT, D><<<mgrid, 256, 0, st>>>(a.out, a.ws, a.plan, rec, a.num_q_heads, a.num_kv_heads, \
+                                                        T, cpw, a.prefix)
   if (a.head_dim == 64) {
     if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 64);
     else PKV_MERGE(F16, 64);

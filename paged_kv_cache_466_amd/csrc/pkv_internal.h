@@ -78,11 +78,26 @@ struct AttnArgs {
   const void* new_v;
   const int32_t* positions;
   int32_t* slots_out;
+  // shared-prefix decode: block_tables points at entry prefix_blocks of row
+  // 0, rows are table_stride entries apart (0: max_blocks_per_seq) and
+  // lengths count from token len_off; prefix holds one record per
+  // (sequence, query head) of the shared blocks (prefix_record_floats)
+  int table_stride;
+  int len_off;
+  const float* prefix;
   void* stream;
 };
 
 // Floats in one partial record for group size G and head_dim D.
 inline size_t partial_record_floats(int G, int D) { return (size_t)G * D + 32; }
+
+// Floats in one shared-prefix record: acc[D] (unnormalised), m (log2
+// domain), l, two unused.
+inline size_t prefix_record_floats(int D) { return (size_t)D + 4; }
+// Bytes of the shared-prefix records of a batch (256-byte aligned).
+inline size_t prefix_area_bytes(int num_seqs, int num_q_heads, int D) {
+  return ((size_t)num_seqs * num_q_heads * prefix_record_floats(D) * 4 + 255) & ~(size_t)255;
+}
 
 // KV heads (one wave each) per workgroup of the 16-bit / code-cache decode.
 inline int wave_group_size(int num_kv_heads) { return num_kv_heads < 8 ? num_kv_heads : 8; }
@@ -115,6 +130,11 @@ size_t workspace_total(int kv_dtype, int num_seqs, int num_q_heads, int num_kv_h
 // arguments and return a hipError_t cast to int.
 int launch_paged_attn_partition(const AttnArgs& a);
 int launch_paged_attn_merge(const AttnArgs& a);
+// Shared-prefix pass: one record per (sequence, query head) of attention
+// over the prefix_blocks blocks listed at `table`.
+int launch_prefix_attn(const void* query, int q_dtype, const void* k_cache, const void* v_cache,
+                       const int32_t* table, int prefix_blocks, float* records, int num_seqs, int num_q_heads,
+                       int num_kv_heads, int head_dim, int num_blocks, float sm_scale, void* stream);
 int launch_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int max_blocks_per_seq,
                         const int32_t* seq_ids, const int32_t* positions, int num_tokens,
                         int num_seqs, int block_size, int num_blocks, void* stream);

@@ -86,8 +86,10 @@ class GpuRun:
         """Host pool append -> copy-on-write copies -> device slot mapping ->
         slot write (``fused``: both in one pkv_append_kv launch).  Also keeps
         the host pool's slots for comparison.  ``attend`` = (query, out,
-        partition_size): the slot write goes into the decode instead
-        (pkv_paged_attn_decode_append), which leaves its output in out."""
+        partition_size[, prefix_blocks]): the slot write goes into the decode
+        instead (pkv_paged_attn_decode_append, or
+        pkv_paged_attn_decode_shared_prefix when prefix_blocks is given), which
+        leaves its output in out."""
         w = self.w
         host_slots = []
         lens = self.lens.cpu().numpy()
@@ -104,9 +106,16 @@ class GpuRun:
         positions = self.lens.clone()
         self.host_step_slots = np.asarray(host_slots, dtype=np.int64)
         if attend is not None:
-            query, out, psize = attend
+            query, out, psize = attend[:3]
             self.step_slots = torch.empty(w.S, dtype=torch.int32, device=self.device)
             self.lens += 1
+            if len(attend) > 3:
+                pkv.paged_attn_decode_shared_prefix(out, query, self.k_cache, self.v_cache, self.block_tables,
+                                                    self.lens, w.sm_scale, attend[3], key=tensors["new_key"],
+                                                    value=tensors["new_value"], positions=positions,
+                                                    slot_mapping=self.step_slots, partition_size=psize,
+                                                    stream_kv=not w.fork)
+                return
             pkv.paged_attn_decode_append(out, query, self.k_cache, self.v_cache, tensors["new_key"],
                                          tensors["new_value"], positions, self.block_tables, self.lens, w.sm_scale,
                                          slot_mapping=self.step_slots, partition_size=psize,

@@ -41,6 +41,11 @@ CASES = {
     "llama3_8b_b64_fused_write": ("llama3_8b_b64", {"fused": True}, [3, 40, 62], None),
     "shared_prefix_b128_fused_write": ("shared_prefix_b128", {"fused": True}, [0, 1, 100], None),
     "ctx128k_b4_fused_write": ("ctx128k_b4", {"fused": True}, [0], [2, 5]),
+    # the shared blocks read once for the whole batch
+    # (pkv_paged_attn_decode_shared_prefix), with and without the fused write
+    "shared_prefix_b128_cascade": ("shared_prefix_b128", {"cascade": True}, [0, 1, 42, 127], None),
+    "shared_prefix_b128_cascade_fused_write": ("shared_prefix_b128", {"cascade": True, "fused": True},
+                                               [0, 1, 99], None),
 }
 
 
@@ -112,6 +117,7 @@ def test_full_size_sampled(case):
     ov = dict(ov)
     streaming = ov.pop("streaming", False)
     fused = ov.pop("fused", False)
+    cascade = ov.pop("cascade", False)
     w = get_workload(name, streaming=streaming, **ov)
     print(f"[fullsize] case={case} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} kv={w.kv_dtype} blocks={w.num_blocks}",
           flush=True)
@@ -120,9 +126,18 @@ def test_full_size_sampled(case):
     S, Hq, D = t["query"].shape
     psize = w.partition_size or pkv.paged_attn_partition_size(w.kv_dtype, g.mbs * 16)
     stream_kv = not (w.prefix_tokens or w.fork)
+    P = w.prefix_tokens // 16
+    if cascade:
+        psize = 0
     if fused:
         out = torch.empty_like(t["query"])
-        g.decode_step(t, attend=(t["query"], out, psize))
+        g.decode_step(t, attend=(t["query"], out, psize) + ((P,) if cascade else ()))
+        out = out.float().cpu().numpy()
+    elif cascade:
+        out = torch.empty_like(t["query"])
+        pkv.validate_shared_prefix(g.block_tables, g.lens, P)
+        pkv.paged_attn_decode_shared_prefix(out, t["query"], g.k_cache, g.v_cache, g.block_tables, g.lens,
+                                            w.sm_scale, P, stream_kv=not w.fork)
         out = out.float().cpu().numpy()
     else:
         out = g.decode(t["query"], partition_size=psize, stream_kv=stream_kv).float().cpu().numpy()

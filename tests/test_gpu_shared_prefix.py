@@ -1,0 +1,117 @@
+"""GPU parity of the shared-prefix decode (pkv_paged_attn_decode_shared_prefix)
+against the CPU oracle.
+
+The shared-prefix decode computes the plain decode's softmax attention; only
+the order of the work differs (the shared blocks once for every query row of
+the batch, then each sequence's own blocks, combined by log-sum-exp).  So the
+oracle is the plain one, run on the same seeded inputs, and outputs must be
+within 2e-2 of it (bf16 / f16).  Cases cover: several 32-row tiles with a
+ragged last one, a one-block prefix, a prefix longer than the kernel's
+2048-entry table chunk, sequences with nothing past the prefix, group sizes
+1, 4, 8 and 16, head dim 64, more KV heads than one workgroup holds, f16,
+over 64 sequences, every sequence finished in one piece (partition_size 0
+on short suffixes) and sequences cut over workgroups (partition_size 16,
+merged with the prefix in the merge kernel), and the fused slot write (cache
+bits equal to the oracle's).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle_pipeline import OracleRun, to_raw
+from workloads import draw_tensors, get_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+# name -> overrides of the shared-prefix workload (suffix lengths drawn or fixed)
+CASES = {
+    "small": dict(S=6, len_lo=20, len_hi=200, prefix_tokens=64),
+    "one_block_prefix": dict(S=5, len_lo=1, len_hi=100, prefix_tokens=16),
+    "prefix_past_table_chunk": dict(S=2, len_lo=10, len_hi=50, prefix_tokens=16 * 2100, fork=()),
+    "prefix_only_rows": dict(S=4, fixed_lens=(0, 7, 0, 33), prefix_tokens=128, fork=(), append=False),
+    "g4": dict(S=9, Hq=32, Hkv=8, len_lo=1, len_hi=400, prefix_tokens=256),
+    "g1_d64": dict(S=7, Hq=4, Hkv=4, D=64, len_lo=5, len_hi=300, prefix_tokens=48),
+    "g16": dict(S=3, Hq=32, Hkv=2, len_lo=100, len_hi=700, prefix_tokens=160),
+    "hkv16": dict(S=3, Hq=32, Hkv=16, len_lo=50, len_hi=400, prefix_tokens=96),
+    "f16": dict(S=5, q_dtype="f16", kv_dtype="f16", src_dtype="f16", len_lo=30, len_hi=300, prefix_tokens=80),
+    "many_seqs": dict(S=70, len_lo=1, len_hi=60, prefix_tokens=32),
+}
+
+_runs = {}
+
+
+def run_case(name):
+    if name not in _runs:
+        from gpu_pipeline import GpuRun
+        w = get_workload("shared_prefix_b128", **CASES[name])
+        print(f"[shared-prefix] case={name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} kv={w.kv_dtype} "
+              f"prefix={w.prefix_tokens} lens={w.seq_lens.tolist()[:8]}", flush=True)
+        t = draw_tensors(w, "cuda")
+        g = GpuRun(w, t)
+        torch.cuda.synchronize()
+        o = OracleRun(w, t)
+        ref = o.decode(to_raw(t["query"], w.q_dtype))
+        _runs[name] = (w, t, g, o, ref)
+    return _runs[name]
+
+
+@pytest.mark.parametrize("psize", [0, 16])
+@pytest.mark.parametrize("name", list(CASES))
+def test_shared_prefix_matches_oracle(name, psize):
+    import paged_kv_cache_466_amd as pkv
+    w, t, g, o, ref = run_case(name)
+    P = w.prefix_tokens // 16
+    pkv.validate_shared_prefix(g.block_tables, g.lens, P)
+    out = torch.full_like(t["query"], float("nan"))
+    pkv.paged_attn_decode_shared_prefix(out, t["query"], g.k_cache, g.v_cache, g.block_tables, g.lens, w.sm_scale,
+                                        P, partition_size=psize, stream_kv=not w.fork)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref).max())
+    print(f"[shared-prefix] {name} psize={psize} max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("name", ["small", "g4", "hkv16", "prefix_only_rows"])
+def test_shared_prefix_reused_workspace(name):
+    """A workspace whose every 16 bytes read as a live merge-plan entry
+    (records in slot 0, workgroups 0 to 1) before the first call, then
+    reused by a second: both results match the oracle, bit-identical to each
+    other."""
+    import paged_kv_cache_466_amd as pkv
+    w, t, g, o, ref = run_case(name)
+    P = w.prefix_tokens // 16
+    S, Hq, D = t["query"].shape
+    nbytes = pkv.paged_attn_shared_prefix_workspace_bytes(w.kv_dtype, S, Hq, w.Hkv, D, g.mbs * 16, P, 16)
+    ws = torch.tensor([0, 0, 1, 0], dtype=torch.int32).repeat(nbytes // 16 + 1).to("cuda").view(torch.uint8)
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(t["query"])
+        pkv.paged_attn_decode_shared_prefix(out, t["query"], g.k_cache, g.v_cache, g.block_tables, g.lens,
+                                            w.sm_scale, P, partition_size=16, workspace=ws)
+        torch.cuda.synchronize()
+        err = float(np.abs(out.float().cpu().numpy() - ref).max())
+        assert err <= TOL, err
+        outs.append(out.view(torch.int16).cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("name", ["small", "g1_d64", "many_seqs"])
+def test_shared_prefix_fused_write(name):
+    """The step's slot write inside the shared-prefix decode: cache bits and
+    slots equal the oracle's, attention within tolerance."""
+    from gpu_pipeline import GpuRun
+    w, t, _, o, ref = run_case(name)
+    g = GpuRun(w, t, do_step=False)
+    out = torch.empty_like(t["query"])
+    g.decode_step(t, attend=(t["query"], out, 0, w.prefix_tokens // 16))
+    torch.cuda.synchronize()
+    assert to_raw(g.k_cache, w.kv_dtype).tobytes() == o.k_cache.tobytes()
+    assert to_raw(g.v_cache, w.kv_dtype).tobytes() == o.v_cache.tobytes()
+    assert (g.step_slots.cpu().numpy().astype(np.int64) == o.step_slots).all()
+    err = float(np.abs(out.float().cpu().numpy() - ref).max())
+    assert err <= TOL, err

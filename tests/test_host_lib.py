@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import paged_kv_cache_466_amd as pkv
@@ -208,6 +209,60 @@ def test_argument_errors_return_before_launch():
     assert L.pkv_paged_attn_decode(None, None, 1, None, None, 1, None, None, None, 4, None, 0, 32, 8, 128, 16, 10,
                                    0.1, 0, 0, 0, 0, None, 0, None) == 0
     assert L.pkv_reshape_and_cache(None, None, None, None, 1, None, 0, 10, 16, 8, 128, None) == 0
+
+
+def test_shared_prefix_host_side():
+    """pkv_paged_attn_decode_shared_prefix rejects bad arguments on the host;
+    pkv_validate_shared_prefix checks its preconditions; the workspace is the
+    prefix records plus the suffix decode's workspace."""
+    L = pkv.lib
+    f = L.pkv_paged_attn_decode_shared_prefix
+    # (out, query, q_dtype, k, v, kv_dtype, key, value, positions, slots, tables, mbs, lens, S, Hq, Hkv, D, BS,
+    #  NB, scale, prefix_blocks, psize, flags, ws, ws_bytes, stream)
+    st = f(None, None, 0, None, None, 0, None, None, None, None, None, 8, None, 2, 32, 8, 128, 16, 10, 0.1, 2, 0, 0,
+           None, 0, None)
+    assert st == 2 and "bf16" in pkv.last_error()
+    st = f(None, None, 1, None, None, 3, None, None, None, None, None, 8, None, 2, 32, 8, 128, 16, 10, 0.1, 2, 0, 0,
+           None, 0, None)
+    assert st == 2
+    for pb in (0, 9):
+        st = f(None, None, 1, None, None, 1, None, None, None, None, None, 8, None, 2, 32, 8, 128, 16, 10, 0.1, pb, 0,
+               0, None, 0, None)
+        assert st == 1 and "prefix_blocks" in pkv.last_error()
+    st = f(None, None, 1, None, None, 1, 1, None, None, None, None, 8, None, 2, 32, 8, 128, 16, 10, 0.1, 2, 0, 0,
+           None, 0, None)
+    assert st == 1 and "key" in pkv.last_error()
+    st = f(1, 1, 1, 1, 1, 1, None, None, None, None, 1, 8, 1, 2, 32, 8, 128, 16, 10, 0.1, 2, 0, 0, None, 0, None)
+    assert st == 3 and "workspace" in pkv.last_error()
+    st = f(None, None, 1, None, None, 1, None, None, None, None, None, 8, None, 2, 32, 8, 96, 16, 10, 0.1, 2, 0, 0,
+           1 << 20, 1 << 20, None)
+    assert st == 2 and "head_dim" in pkv.last_error()
+    st = f(None, None, 1, None, None, 1, None, None, None, None, None, 8, None, 2, 32, 8, 128, 16, 10, 0.1, 2, 0, 4,
+           1 << 20, 1 << 20, None)
+    assert st == 1 and "flags" in pkv.last_error()
+    # an empty batch is a no-op
+    assert f(None, None, 1, None, None, 1, None, None, None, None, None, 8, None, 0, 32, 8, 128, 16, 10, 0.1, 2, 0, 0,
+             None, 0, None) == 0
+
+    # preconditions
+    bt = torch.tensor([[3, 5, 7, 0], [3, 5, 9, 1], [3, 5, 2, 4]], dtype=torch.int32)
+    lens = torch.tensor([50, 49, 64], dtype=torch.int32)
+    pkv.validate_shared_prefix(bt, lens, 2)
+    with pytest.raises(pkv.PkvError, match="differs"):
+        pkv.validate_shared_prefix(bt, lens, 3)
+    with pytest.raises(pkv.PkvError, match="shorter"):
+        pkv.validate_shared_prefix(bt, torch.tensor([50, 31, 64], dtype=torch.int32), 2)
+    with pytest.raises(pkv.PkvError):
+        pkv.validate_shared_prefix(bt, lens, 5)
+
+    # workspace: records of (acc[D], m, l, 2 unused) fp32 per (sequence, query head), 256-byte aligned, then
+    # the decode's workspace for the tokens past the prefix
+    S, Hq, Hkv, D = 128, 64, 8, 128
+    rec = -(-(S * Hq * (D + 4) * 4) // 256) * 256
+    for max_len, P in ((3100, 64), (1024, 64), (5000, 1)):
+        got = pkv.paged_attn_shared_prefix_workspace_bytes("bf16", S, Hq, Hkv, D, max_len, P)
+        assert got == rec + pkv.paged_attn_workspace_bytes("bf16", S, Hq, Hkv, D, max(max_len - 16 * P, 0))
+    assert pkv.paged_attn_shared_prefix_workspace_bytes("bf16", 0, Hq, Hkv, D, 3100, 64) == 0
 
 
 # --------------------------------------------------------------------------
