@@ -107,8 +107,10 @@ def csrc_hash():
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch of the partition kernel from the committed
-    rocprofv3 counter runs, or None when the kernels changed since."""
+    """HBM bytes per launch of the partition kernel (for the shared-prefix
+    decode, ``<workload>_shared_prefix``: per call of its three kernels) from
+    the committed rocprofv3 counter runs, or None when the kernels changed
+    since."""
     try:
         t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     except (OSError, ValueError):
@@ -616,7 +618,7 @@ def roofline(m):
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": None if m.get("cascade") else measured_traffic(m["w"].name),
+        "traffic": measured_traffic(m["w"].name + ("_shared_prefix" if m.get("cascade") else "")),
     }
 
 

@@ -1571,18 +1571,12 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixPa
       tab[i] = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the caches
     }
     __syncthreads();
-    // this wave's blocks: entries [j0, j1) of the chunk, from a starting
-    // point that differs between the row tiles of a head (the softmax does
-    // not depend on the order): the tiles then ask for different blocks at
-    // once instead of all waiting on the same one, and the head's blocks
-    // reach L2 in one round of memory latency rather than one per block
+    // this wave's blocks: entries [j0, j1) of the chunk
     const int j0 = wave * cn / kPrefixWaves, j1 = (wave + 1) * cn / kPrefixWaves;
     const int n = j1 - j0;
-    const int rot = n > 0 ? (int)((blockIdx.x / p.num_kv_heads) % n) : 0;
-    auto entry = [&](int k) { return k < n ? j0 + (k + rot < n ? k + rot : k + rot - n) : j1; };
     Tile ring[DEPTH];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], entry(d), j1);
+    for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], j0 + d, j1);
     __builtin_amdgcn_sched_barrier(0);
     for (int k0 = 0; k0 < n; k0 += DEPTH) {
 #pragma unroll
@@ -1590,7 +1584,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixPa
         const int k = k0 + d;
         if (k < n) process(ring[d]);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(ring[d], entry(k + DEPTH), j1);
+        load_tile(ring[d], j0 + k + DEPTH, j1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
