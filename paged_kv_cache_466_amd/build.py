@@ -24,9 +24,11 @@ SOURCES = ["api.hip", "cache_ops.hip", "paged_attn.hip", "quest.hip", "pool.cpp"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
-# gfx950 code: no packed-fp32 instructions (see the header of paged_attn.hip)
+# gfx950 code: no packed-fp32 instructions (see the header of paged_attn.hip);
+# MFMA results in ordinary VGPRs, so that accumulators the softmax rescales
+# are not copied between accumulation and vector registers every block
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-fno-gpu-rdc", "-munsafe-fp-atomics"]
+             "-fno-gpu-rdc", "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
 def _compile(src):
