@@ -264,10 +264,14 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
   a.may_split = a.num_partitions > 1;
   a.ws = nullptr;
   a.plan = nullptr;
-  if (a.may_split) {
+  // the shared-prefix decode merges every sequence: it needs the plan area
+  // even when no sequence can be cut
+  if (a.may_split || (a.srec && wave_path)) {
     // records hold one row per (query token, query head) of a group
-    const size_t total = workspace_total(a.kv_dtype, a.num_seqs, a.num_q_heads * a.qtok, a.num_kv_heads,
-                                         a.head_dim, a.num_partitions, a.partition_size);
+    const size_t total = a.may_split ? workspace_total(a.kv_dtype, a.num_seqs, a.num_q_heads * a.qtok,
+                                                       a.num_kv_heads, a.head_dim, a.num_partitions,
+                                                       a.partition_size)
+                                     : plan_area_bytes(a.num_seqs);
     if (!workspace || workspace_bytes < total)
       return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, total, workspace_bytes);
     if (((uintptr_t)workspace) & 127) return fail(PKV_EINVAL, "%s: workspace must be 128-byte aligned", who);
@@ -275,7 +279,7 @@ static pkv_status prepare_attn(AttnArgs& a, const char* who, void* workspace, si
       a.ws = (float*)workspace;
     } else {
       a.plan = (int*)workspace;
-      a.ws = (float*)((char*)workspace + plan_area_bytes(a.num_seqs));
+      a.ws = a.may_split ? (float*)((char*)workspace + plan_area_bytes(a.num_seqs)) : nullptr;
     }
   }
   return PKV_OK;
@@ -469,10 +473,15 @@ extern "C" size_t pkv_paged_attn_shared_prefix_workspace_bytes(int kv_dtype, int
                                                                int num_kv_heads, int head_dim, int max_seq_len,
                                                                int prefix_blocks, int partition_size) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || prefix_blocks < 0) return 0;
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return 0;
   const int suffix = max_seq_len - prefix_blocks * 16;
+  const size_t split = pkv_paged_attn_workspace_bytes(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                      suffix > 0 ? suffix : 0, partition_size);
+  // prefix records, whole-sequence records, then the decode's plan area and
+  // split records (the plan area alone when no sequence can be cut)
   return prefix_area_bytes(num_seqs, num_q_heads, head_dim) +
-         pkv_paged_attn_workspace_bytes(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                        suffix > 0 ? suffix : 0, partition_size);
+         whole_record_area_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim) +
+         (split > 0 ? split : plan_area_bytes(num_seqs));
 }
 
 extern "C" pkv_status pkv_validate_shared_prefix(const int32_t* block_tables, int max_blocks_per_seq,
@@ -516,7 +525,9 @@ extern "C" pkv_status pkv_paged_attn_decode_shared_prefix(
   if (num_q_heads / num_kv_heads > 16)
     return fail(PKV_EUNSUPPORTED, "%s: query group size above 16 is not built", who);
   if (flags & ~(unsigned)PKV_DECODE_STREAM_KV) return fail(PKV_EINVAL, "%s: unknown flags 0x%x", who, flags);
-  const size_t pre_bytes = num_seqs > 0 ? prefix_area_bytes(num_seqs, num_q_heads, head_dim) : 0;
+  const size_t pre_bytes = num_seqs > 0 ? prefix_area_bytes(num_seqs, num_q_heads, head_dim) +
+                                              whole_record_area_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim)
+                                        : 0;
   if (num_seqs > 0) {
     if (!workspace || workspace_bytes < pre_bytes)
       return fail(PKV_EWORKSPACE, "%s: workspace of at least %zu bytes needed, %zu given", who, pre_bytes,
@@ -532,6 +543,7 @@ extern "C" pkv_status pkv_paged_attn_decode_shared_prefix(
   a.table_stride = max_blocks_per_seq;
   a.len_off = prefix_blocks * block_size;
   a.prefix = (const float*)workspace;
+  a.srec = workspace ? (float*)((char*)workspace + prefix_area_bytes(num_seqs, num_q_heads, head_dim)) : nullptr;
   if (key) {
     a.new_k = key;
     a.new_v = value;

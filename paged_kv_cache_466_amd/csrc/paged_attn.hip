@@ -75,11 +75,13 @@ struct AttnParams {
   int32_t* slots_out;
   // Shared-prefix decode: block_tables starts at the first suffix entry of
   // row 0, rows are tstride entries apart (tstride = mbs otherwise), and a
-  // sequence's length counts from token len_off.  prefix: per (sequence,
-  // query head) acc[D], m, l of the shared blocks, folded into the result.
+  // sequence's length counts from token len_off.  srec (non-null only
+  // then): one record per (sequence, KV head), where a sequence finished in
+  // one piece leaves its record instead of its output; the merge combines
+  // every sequence's records with the prefix's.
   int tstride;
   int len_off;
-  const float* prefix;
+  float* srec;
   float scale_log2;     // sm_scale * log2(e)
 };
 
@@ -410,7 +412,7 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
   // (16-bit outputs: zero bits are zero); with a shared prefix its output is
   // the prefix's, written by the kernel
   if (blockIdx.y == 0 && w < S && seq_len_at(p, w) == 0) {
-    if (!p.prefix) {
+    if (!p.srec) {
       const int n16 = p.num_q_heads * p.qtok * head_dim / 8;
       uint4* o = reinterpret_cast<uint4*>(p.out) + (size_t)w * n16;
       for (int i = lane; i < n16; i += 64) o[i] = make_uint4(0, 0, 0, 0);
@@ -483,7 +485,8 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
           }
           if (i0 == 0 && p.plan && blockIdx.y == 0 && lane == 0) {
             const int w_last = (int)(((long long)(P + n) * k_eff - 1) / U);
-            reinterpret_cast<int4*>(p.plan)[s] = make_int4(2 * w + upper, w, w_last, 0);
+            // w: 1 when a whole sequence left its record in srec
+            reinterpret_cast<int4*>(p.plan)[s] = make_int4(2 * w + upper, w, w_last, p.srec && w_last == w ? 1 : 0);
           }
           nb += cnt;
           ++nseg;
@@ -553,24 +556,6 @@ void paged_attn_wave_kernel(AttnParams p) {
   if (wave == 0) build_block_list<SEL>(p, D, lane, list, segs, counts, ends);
   __syncthreads();
   if (kvh >= p.num_kv_heads) return;
-  // shared prefix: built for 16-bit caches read through the block table
-  constexpr bool kPrefixFold = !kCodes && !SEL && !GRP;
-  if constexpr (kPrefixFold) {
-    if (p.prefix && (int)blockIdx.x < p.num_seqs && seq_len_at(p, blockIdx.x) == 0) {
-      // nothing past the shared blocks: the output of this head group is
-      // the prefix's, acc / l
-      const size_t s = blockIdx.x;
-      constexpr int CPR = D / 4;
-      for (int i = lane; i < G * CPR; i += 64) {
-        const size_t row = s * p.num_q_heads + kvh * G + i / CPR;
-        const float* pr = p.prefix + row * (D + 4);
-        const float l = pr[D + 1];
-        const floatx4 a = *reinterpret_cast<const floatx4*>(pr + 4 * (i % CPR)) * (l > 0.f ? 1.f / l : 0.f);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + 4 * (i % CPR)) =
-            make_uint2(MO::pack2(a[0], a[1]), MO::pack2(a[2], a[3]));
-      }
-    }
-  }
   const int nb = __builtin_amdgcn_readfirstlane(counts[0]);
   const int nseg = __builtin_amdgcn_readfirstlane(counts[1]);
 
@@ -794,26 +779,18 @@ void paged_attn_wave_kernel(AttnParams p) {
     const size_t seq = (size_t)(key >> 8);
     float l = lsum + __shfl_xor(lsum, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    if constexpr (kPrefixFold) {
-      // a whole sequence after a shared prefix: fold in the prefix's record
-      // (acc_p, m_p, l_p) of this lane's head by log-sum-exp
-      if (whole && p.prefix && g < NCOL) {
-        const float* pr = p.prefix + (seq * p.num_q_heads + kvh * G + g) * (D + 4);
-        const float pm = pr[D], pl = pr[D + 1];
-        const float mx = fmaxf(m2, pm);
-        const float wsuf = __builtin_amdgcn_exp2f(m2 - mx), wpre = __builtin_amdgcn_exp2f(pm - mx);
-#pragma unroll
-        for (int n = 0; n < NN; ++n)
-          acc[n] = acc[n] * wsuf + *reinterpret_cast<const floatx4*>(pr + 16 * n + 4 * kg) * wpre;
-        l = l * wsuf + pl * wpre;
-      }
-    }
     constexpr int RSTRIDE = D + 4;                      // floats per padded LDS row
     static_assert((8 * RSTRIDE + 32) * 4 <= C::VSTAGE, "result staging must fit the V staging area");
     float* rl = reinterpret_cast<float*>(vstage);
-    const float scale_out = whole ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
+    // a whole sequence writes its output, or after a shared prefix its
+    // record for the merge; a piece writes a record
+    const bool to_out = whole && !p.srec;
+    const float scale_out = to_out ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
     // acc[NCOL][D], then m[16], l[16]
-    float* rec = p.ws + ((size_t)(2 * blockIdx.x + ((key >> 1) & 1)) * p.num_kv_heads + kvh) * p.rec_floats;
+    float* rec = whole ? (p.srec ? p.srec + (seq * p.num_kv_heads + kvh) * p.rec_floats : nullptr)
+                       : (p.ws ? p.ws + ((size_t)(2 * blockIdx.x + ((key >> 1) & 1)) * p.num_kv_heads + kvh) *
+                                            p.rec_floats
+                               : nullptr);
     for (int h0 = 0; h0 < NCOL; h0 += 8) {
       const int nh = min(8, NCOL - h0);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -831,7 +808,7 @@ void paged_attn_wave_kernel(AttnParams p) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (whole) {
+      if (to_out) {
         // nh output rows of D elements (rows of one query token are
         // contiguous): 8 elements per lane-store
         constexpr int CPR = D / 8;
@@ -846,7 +823,7 @@ void paged_attn_wave_kernel(AttnParams p) {
                   : make_uint4(MO::pack2(lo[0], lo[1]), MO::pack2(lo[2], lo[3]), MO::pack2(hi[0], hi[1]),
                                MO::pack2(hi[2], hi[3]));
         }
-      } else if (p.ws) {
+      } else if (whole || p.ws) {
         if constexpr (kIL) {
           constexpr int CPR = D / 8;
           for (int c = lane; c < nh * CPR; c += 64) {
@@ -1189,10 +1166,12 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 // Merge of the wave kernel's records.  For each sequence cut over several
 // workgroups and each record column (query head of a group, times query
 // token), out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i over its
-// records, one per workgroup it reaches; after a shared prefix, the
-// prefix's record of the head (acc[D], m, l at `prefix`) is one more term.
-// Whole sequences were finished by their waves and empty ones zeroed: their
-// plan entries name one workgroup, and their workgroups return at once.
+// records, one per workgroup it reaches.  Whole sequences were finished by
+// their waves and empty ones zeroed: their plan entries name one workgroup,
+// and their workgroups return at once.  After a shared prefix every
+// sequence is merged here: the prefix's record of the head (acc[D], m, l at
+// `prefix`) is one more term, a whole sequence's record is in `srec`
+// (plan entry w = 1), and an empty one has the prefix's term alone.
 // One workgroup per (sequence, KV head, group of cpw columns): the columns of
 // one record sit next to each other, so a workgroup reads whole record rows.
 // Its 256 threads take (column, 16-byte piece of the row) outputs; when
@@ -1204,7 +1183,8 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 template <typename QT, int D>
 __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const float* ws, const int* plan,
                                                                int rec_floats, int num_q_heads, int num_kv_heads,
-                                                               int qtok, int cpw, const float* prefix) {
+                                                               int qtok, int cpw, const float* prefix,
+                                                               const float* srec) {
   constexpr int V4 = D / 4;   // 16-byte pieces of an output row
   __shared__ float red[256];
   __shared__ float mcol[16];
@@ -1217,10 +1197,14 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
   const int ncols = min(cpw, NCOL - col0);
   // (slot of the first record, first workgroup, last workgroup)
   const int4 e = reinterpret_cast<const int4*>(plan)[s];
-  if (e.z <= e.y) return;
-  const int np = e.z - e.y + 1;
+  const bool cut = e.z > e.y;
+  if (!cut && !prefix) return;
+  // records: cut, e.z - e.y + 1 of them; after a shared prefix, whole (one,
+  // in srec) or empty (none)
+  const int np = cut ? e.z - e.y + 1 : e.w;
   // record i: slot e.x for i = 0, then slot 2 (e.y + i) of each later workgroup
   auto rec_of = [&](int i) {
+    if (!cut) return srec + ((size_t)s * num_kv_heads + kvh) * rec_floats;
     const int slot = i == 0 ? e.x : 2 * (e.y + i);
     return ws + ((size_t)slot * num_kv_heads + kvh) * rec_floats;
   };
@@ -1689,7 +1673,7 @@ static AttnParams make_params(const AttnArgs& a) {
   p.mbs = a.selected ? (1 << 27) - 1 : a.max_blocks_per_seq;
   p.tstride = a.table_stride > 0 ? a.table_stride : p.mbs;
   p.len_off = a.len_off;
-  p.prefix = a.prefix;
+  p.srec = a.srec;
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.num_blocks = a.num_blocks;
@@ -1824,7 +1808,7 @@ int launch_paged_attn_merge(const AttnArgs& a) {
                                                                      a.partition_size, max_len);
     return hipGetLastError();
   }
-  if (!a.may_split) return hipSuccess;
+  if (!a.may_split && !a.srec) return hipSuccess;
   // columns per workgroup: halved from a whole record row (at most 256
   // threads' worth of 16-byte pieces) while the grid is under ~1024
   // workgroups
@@ -1835,7 +1819,7 @@ int launch_paged_attn_merge(const AttnArgs& a) {
   const dim3 mgrid(a.num_seqs, a.num_kv_heads, (NCOL + cpw - 1) / cpw);
 #define PKV_MERGE(QT, D)                                                                                   \
   paged_attn_merge_kernel<QT, D><<<mgrid, 256, 0, st>>>(a.out, a.ws, a.plan, rec, a.num_q_heads, a.num_kv_heads, \
-                                                        T, cpw, a.prefix)
+                                                        T, cpw, a.prefix, a.srec)
   if (a.head_dim == 64) {
     if (a.q_dtype == PKV_BF16) PKV_MERGE(BF16, 64);
     else PKV_MERGE(F16, 64);

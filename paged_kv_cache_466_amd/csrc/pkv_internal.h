@@ -81,15 +81,23 @@ struct AttnArgs {
   // shared-prefix decode: block_tables points at entry prefix_blocks of row
   // 0, rows are table_stride entries apart (0: max_blocks_per_seq) and
   // lengths count from token len_off; prefix holds one record per
-  // (sequence, query head) of the shared blocks (prefix_record_floats)
+  // (sequence, query head) of the shared blocks (prefix_record_floats);
+  // srec one partial record per (sequence, KV head) for sequences the
+  // decode finishes in one piece (their output is written by the merge,
+  // which then runs for every sequence and needs the plan area)
   int table_stride;
   int len_off;
   const float* prefix;
+  float* srec;
   void* stream;
 };
 
 // Floats in one partial record for group size G and head_dim D.
 inline size_t partial_record_floats(int G, int D) { return (size_t)G * D + 32; }
+inline size_t whole_record_area_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int D) {
+  return ((size_t)num_seqs * num_kv_heads * partial_record_floats(num_q_heads / num_kv_heads, D) * 4 + 255) &
+         ~(size_t)255;
+}
 
 // Floats in one shared-prefix record: acc[D] (unnormalised), m (log2
 // domain), l, two unused.
@@ -98,6 +106,9 @@ inline size_t prefix_record_floats(int D) { return (size_t)D + 4; }
 inline size_t prefix_area_bytes(int num_seqs, int num_q_heads, int D) {
   return ((size_t)num_seqs * num_q_heads * prefix_record_floats(D) * 4 + 255) & ~(size_t)255;
 }
+// Bytes of the shared-prefix decode's per-(sequence, KV head) records of
+// whole sequences (256-byte aligned); defined after partial_record_floats.
+inline size_t whole_record_area_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int D);
 
 // KV heads (one wave each) per workgroup of the 16-bit / code-cache decode.
 inline int wave_group_size(int num_kv_heads) { return num_kv_heads < 8 ? num_kv_heads : 8; }

@@ -255,13 +255,17 @@ def test_shared_prefix_host_side():
     with pytest.raises(pkv.PkvError):
         pkv.validate_shared_prefix(bt, lens, 5)
 
-    # workspace: records of (acc[D], m, l, 2 unused) fp32 per (sequence, query head), 256-byte aligned, then
-    # the decode's workspace for the tokens past the prefix
+    # workspace: the prefix records, (acc[D], m, l, 2 unused) fp32 per (sequence, query head); the records of
+    # sequences finished in one piece, (acc[G][D], m[16], l[16]) per (sequence, KV head); each 256-byte
+    # aligned; then the decode's workspace for the tokens past the prefix, or its plan area (16 bytes per
+    # sequence, 256-byte aligned) when no sequence can be cut
     S, Hq, Hkv, D = 128, 64, 8, 128
-    rec = -(-(S * Hq * (D + 4) * 4) // 256) * 256
-    for max_len, P in ((3100, 64), (1024, 64), (5000, 1)):
+    align = lambda n: -(-n // 256) * 256
+    pre = align(S * Hq * (D + 4) * 4) + align(S * Hkv * ((Hq // Hkv) * D + 32) * 4)
+    for max_len, P in ((3100, 64), (1024, 64), (1100, 64), (5000, 1)):
         got = pkv.paged_attn_shared_prefix_workspace_bytes("bf16", S, Hq, Hkv, D, max_len, P)
-        assert got == rec + pkv.paged_attn_workspace_bytes("bf16", S, Hq, Hkv, D, max(max_len - 16 * P, 0))
+        split = pkv.paged_attn_workspace_bytes("bf16", S, Hq, Hkv, D, max(max_len - 16 * P, 0))
+        assert got == pre + (split if split else align(16 * S)), (max_len, P)
     assert pkv.paged_attn_shared_prefix_workspace_bytes("bf16", 0, Hq, Hkv, D, 3100, 64) == 0
 
 
