@@ -44,7 +44,8 @@ def describe(w, grouped=False):
     d = DESCRIPTIONS.get(w.name, w.name)
     scales = ("keys scaled per (block, kv head, channel), values per (block, kv head, token)" if grouped
               else "one fp32 scale per (block, kv head)")
-    return d.format(codes=CODE_NAMES.get(w.kv_dtype, w.kv_dtype), scales=scales)
+    parts = f"{w.partition_size}-token partitions" if w.partition_size else "the library's partitions"
+    return d.format(codes=CODE_NAMES.get(w.kv_dtype, w.kv_dtype), scales=scales, parts=parts)
 
 
 DESCRIPTIONS = {
@@ -55,7 +56,7 @@ DESCRIPTIONS = {
     "quant_kv_32k_b16": "{codes}-KV long-context decode, batch 16, 32q/8kv, d 128, 32768 tokens each, "
                         "{scales}",
     "ctx128k_b4": "128K-context split-K decode, bf16, batch 4, 64q/8kv, d 128, 131072 tokens each, "
-                  "512-token partitions",
+                  "{parts}",
     "tiny_fp32": "tiny fp32 paged decode, 4 sequences {40,17,64,1}, 8q/2kv, d 64",
 }
 
@@ -85,6 +86,9 @@ def parse():
                     help="quantised workload with keys scaled per channel and values per token (i8 / i4)")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the secondary 128K-context split-K measurement")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the secondary measurements of the other workloads (shared prefix, INT8 / FP8 "
+                         "32K, StreamingLLM 128K)")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="with a shared prefix, time the plain decode instead of the shared-prefix decode")
     return ap.parse_args()
@@ -106,11 +110,25 @@ def csrc_hash():
     return h.hexdigest()[:12]
 
 
+def traffic_key(w, cascade=False):
+    """The key of a measured configuration in profiles/traffic.json: the
+    workload's name, then its code type for code caches, ``_streaming`` for
+    the keep-mask and ``_shared_prefix`` for the shared-prefix decode."""
+    key = w.name
+    if w.kv_dtype in CODES:
+        key += "_" + w.kv_dtype
+    if w.sink or w.window:
+        key += "_streaming"
+    if cascade:
+        key += "_shared_prefix"
+    return key
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the partition kernel (for the shared-prefix
-    decode, ``<workload>_shared_prefix``: per call of its three kernels) from
-    the committed rocprofv3 counter runs, or None when the kernels changed
-    since."""
+    decode: per call of its three kernels) from the committed rocprofv3
+    counter runs, keyed by ``traffic_key``, or None when the kernels changed
+    since or the configuration was not measured."""
     try:
         t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     except (OSError, ValueError):
@@ -618,7 +636,7 @@ def roofline(m):
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": measured_traffic(m["w"].name + ("_shared_prefix" if m.get("cascade") else "")),
+        "traffic": measured_traffic(traffic_key(m["w"], m.get("cascade"))),
     }
 
 
@@ -645,9 +663,13 @@ def main():
     # the 128K split-K measurement runs first, in a child process of its own,
     # so that its multi-GiB allocations start from a fresh device heap
     long_ctx = None
-    if not args.no_long_context and not args.quest and not args.grouped and args.query_tokens == 1 \
-            and args.workload != "ctx128k_b4":
+    primary = not args.quest and not args.grouped and args.query_tokens == 1
+    if not args.no_long_context and primary and args.workload != "ctx128k_b4":
         long_ctx = long_context_entry(min(args.steps, 50), min(args.warmup, 20))
+    others = None
+    if not args.no_other_configs and primary and args.workload == "llama3_8b_b64" and not args.kv_dtype \
+            and not args.streaming and not args.partition_size:
+        others = other_config_entries(min(args.steps, 50), min(args.warmup, 20))
 
     from workloads import get_workload
 
@@ -723,20 +745,51 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, m["t"], lens, args.cpu_seconds)
     if long_ctx is not None:
         result["long_context"] = long_ctx
+    if others is not None:
+        result["other_configs"] = others
     print(json.dumps(result), flush=True)
+
+
+def child_bench(extra, steps, warmup):
+    """The bench's JSON line for one other workload, measured in a child
+    process of its own (a fresh device heap)."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), *extra, "--no-cpu-baseline", "--no-long-context",
+           "--no-other-configs", "--steps", str(steps), "--warmup", str(warmup)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr[-2000:])
+        raise RuntimeError(f"measurement of {' '.join(extra)} failed ({r.returncode})")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def other_config_entries(steps, warmup):
+    """Summaries of the other workloads at their full sizes: the shared-prefix
+    decode, INT8 and FP8-E4M3 codes at 32K, and the StreamingLLM mask at
+    128K.  KV bytes are algorithmic (distinct blocks for the shared prefix)."""
+    out = []
+    for extra in (["--workload", "shared_prefix_b128"],
+                  ["--workload", "quant_kv_32k_b16", "--kv-dtype", "i8"],
+                  ["--workload", "quant_kv_32k_b16", "--kv-dtype", "fp8e4m3"],
+                  ["--workload", "ctx128k_b4", "--streaming"]):
+        print(f"[bench] other config: {' '.join(extra)}", file=sys.stderr, flush=True)
+        d = child_bench(extra, steps, warmup)
+        unique = d["config"]["kv_bytes_unique_per_step"]
+        gbps = unique / (d["ms_per_step"] * 1e-3) / 1e9
+        out.append({
+            "workload": d["config"]["workload"], "kv_dtype": d["config"]["kv_dtype"],
+            "kv_bytes_per_step": d["config"]["kv_bytes_per_step"], "kv_bytes_unique_per_step": unique,
+            "ms_per_step": d["ms_per_step"], "steps_per_s": d["steps_per_s"],
+            "kv_read_gbps_unique": round(gbps, 2), "pct_hbm_peak_unique": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+            "step": d["step"], "roofline": d["roofline"], "steps": steps, "warmup": warmup,
+        })
+    return out
 
 
 def long_context_entry(steps, warmup):
     """Measures the 128K-context split-K workload in a child process and
     returns its summary for the long_context field."""
-    import subprocess
-    cmd = [sys.executable, os.path.abspath(__file__), "--workload", "ctx128k_b4", "--no-cpu-baseline",
-           "--no-long-context", "--steps", str(steps), "--warmup", str(warmup)]
-    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
-    if r.returncode != 0:
-        sys.stderr.write(r.stderr[-2000:])
-        raise RuntimeError(f"long-context measurement failed ({r.returncode})")
-    d = json.loads(r.stdout.strip().splitlines()[-1])
+    d = child_bench(["--workload", "ctx128k_b4"], steps, warmup)
     return {
         "workload": d["config"]["workload"],
         "partition_size": d["config"]["partition_size"], "kv_bytes_per_step": d["config"]["kv_bytes_per_step"],
