@@ -68,3 +68,51 @@ def test_graph_replay_matches_eager_step(base, ov):
                               g.k_scales, g.v_scales, kv_dtype=kvdt)
         torch.cuda.synchronize()
         assert torch.equal(other.view(torch.int16), ref_out.view(torch.int16))
+
+
+def test_graph_replay_shared_prefix_step():
+    """The shared-prefix decode step (prefix pass, decode past the prefix
+    with the slot write fused in, merge) captured once and replayed: every
+    replay equals the eager step bit for bit, with the workspace scribbled
+    over and eager work between replays."""
+    import paged_kv_cache_466_amd as pkv
+    from gpu_pipeline import GpuRun
+    w = get_workload("shared_prefix_b128", S=40, len_lo=20, len_hi=600, prefix_tokens=256)
+    print(f"[graph] shared prefix S={w.S}", flush=True)
+    t = draw_tensors(w, "cuda")
+    g = GpuRun(w, t)
+    P = w.prefix_tokens // 16
+    positions = (g.lens - 1).contiguous()
+    nbytes = pkv.paged_attn_shared_prefix_workspace_bytes(w.kv_dtype, w.S, w.Hq, w.Hkv, w.D, g.mbs * 16, P)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    slots = torch.empty(w.S, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(t["query"])
+
+    def step():
+        pkv.paged_attn_decode_shared_prefix(out, t["query"], g.k_cache, g.v_cache, g.block_tables, g.lens,
+                                            w.sm_scale, P, key=t["new_key"], value=t["new_value"],
+                                            positions=positions, slot_mapping=slots, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    ref_k = g.k_cache.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gr, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"replay {i}"
+        assert torch.equal(g.k_cache.view(torch.uint8), ref_k.view(torch.uint8)), f"replay {i}"
+        other = torch.empty_like(out)
+        pkv.paged_attn_decode_shared_prefix(other, t["query"], g.k_cache, g.v_cache, g.block_tables, g.lens,
+                                            w.sm_scale, P)
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int16), ref_out.view(torch.int16))
