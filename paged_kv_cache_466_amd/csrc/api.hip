@@ -63,10 +63,14 @@ int decode_slots(int num_seqs, int num_kv_heads, int num_partitions, int partiti
   constexpr int kWavesPerCU = 8;   // two waves per SIMD: the wave kernel's register budget
   long long k = ((long long)kWavesPerCU * device_cu_count() + num_kv_heads - 1) / num_kv_heads;
   if (k < num_seqs) k = num_seqs;
-  // a workgroup takes at most ceil(units / k) partitions (or the minimum):
-  // both must fit its block list
-  const long long blocks_per_unit = partition_size / 16;
-  const long long units_cap = decode_list_cap(num_kv_heads) / (blocks_per_unit > 0 ? blocks_per_unit : 1);
+  // a workgroup takes at most ceil(units / k) partitions (or the minimum),
+  // or, when the split balances blocks, its share of the blocks plus up to
+  // one partition less a block: both must fit its block list
+  const long long blocks_per_unit = partition_size / 16 > 0 ? partition_size / 16 : 1;
+  const long long cap = decode_list_cap(num_kv_heads);
+  // (the decode balances blocks only when 3 blocks_per_unit <= cap)
+  const long long units_cap = 3 * blocks_per_unit <= cap ? (cap - blocks_per_unit + 1) / blocks_per_unit
+                                                         : cap / blocks_per_unit;
   if (units_cap > 0) {
     const long long need = ((long long)num_seqs * num_partitions + units_cap - 1) / units_cap;
     if (k < need) k = need;

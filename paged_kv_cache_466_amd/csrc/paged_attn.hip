@@ -329,19 +329,23 @@ __device__ __forceinline__ int lane_scan_incl(int x, int lane) {
 }
 
 // 64 consecutive sequences, lane i describing sequence s0 + i.
+// Positions in the split are measured in units, or in blocks (`weighted`):
+// then a workgroup's share is a run of blocks, and it takes the units that
+// start inside it (see build_block_list).
 struct SeqWindow {
   int s0;      // first sequence (uniform)
-  int base;    // global number of its first unit (uniform)
-  int total;   // units in the window (uniform)
+  int base;    // position of its first unit (uniform)
+  int total;   // units (blocks when weighted) in the window (uniform)
   int L;       // this lane's clamped length
   int n;       // its units
-  int P;       // global number of its first unit
+  int P;       // position of its first unit
 };
 
 // SEL: a selected decode, whose units are the selected pages (at most
 // `budget` blocks of the sequence).
 template <bool SEL>
-__device__ __forceinline__ SeqWindow load_window(const AttnParams& p, int s0, int base, int lane) {
+__device__ __forceinline__ SeqWindow load_window(const AttnParams& p, int s0, int base, int lane,
+                                                 bool weighted) {
   SeqWindow w;
   w.s0 = s0;
   w.base = base;
@@ -349,8 +353,9 @@ __device__ __forceinline__ SeqWindow load_window(const AttnParams& p, int s0, in
   w.L = s < p.num_seqs ? seq_len_at(p, s) : 0;
   if constexpr (SEL) w.n = min(p.budget, (w.L + kBS - 1) / kBS);
   else w.n = seq_units(w.L, p.partition_size, p.sink, p.window).n;
-  const int incl = lane_scan_incl(w.n, lane);
-  w.P = base + incl - w.n;
+  const int wt = weighted ? (w.L + kBS - 1) / kBS : w.n;
+  const int incl = lane_scan_incl(wt, lane);
+  w.P = base + incl - wt;
   w.total = __builtin_amdgcn_readlane(incl, 63);
   return w;
 }
@@ -421,34 +426,56 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
     if (p.plan && lane == 0) reinterpret_cast<int4*>(p.plan)[w] = make_int4(0, 0, 0, 0);
   }
 
-  SeqWindow win = load_window<SEL>(p, 0, 0, lane);
+  // Weighted split: a full-attention decode whose partitions span several
+  // blocks balances blocks rather than partitions.  The units of a 128K
+  // sequence and one appended token are 256 partitions of 32 blocks and one
+  // of 1 block; counted as units, 4 such sequences over 256 workgroups give
+  // some workgroups 5 partitions (160 blocks), counted in blocks none gets
+  // more than 129.  A unit starting inside a workgroup's run of blocks
+  // belongs to it whole, so a workgroup reads at most step - 1 blocks past
+  // its run: the host sizes the grid for that, and step is kept small
+  // enough next to the block list (3 step <= list_cap).
+  const int bpp = p.partition_size / kBS;
+  const bool weighted = !SEL && (p.sink | p.window) == 0 && bpp > 1 && 3 * bpp <= p.list_cap;
+  const int step = weighted ? bpp : 1;   // position step between a sequence's units
+  SeqWindow win = load_window<SEL>(p, 0, 0, lane, weighted);
   int U = win.total;
-  for (int s0 = 64; s0 < S; s0 += 64) U += load_window<SEL>(p, s0, U, lane).total;
+  for (int s0 = 64; s0 < S; s0 += 64) U += load_window<SEL>(p, s0, U, lane, weighted).total;
   int nb = 0, nseg = 0, nend = 0;
   if (U > 0) {
     const int K = gridDim.x;
-    const int Q = max(p.min_units, (U + K - 1) / K);
-    const int k_eff = (U + Q - 1) / Q;
+    int k_eff;
+    if (weighted) {
+      // every run at least one unit long (so that every workgroup between a
+      // sequence's first and last holds a unit of it) and min_units long
+      k_eff = max(1, min(K, min(U / (p.min_units * step), U / step)));
+    } else {
+      const int Q = max(p.min_units, (U + K - 1) / K);
+      k_eff = (U + Q - 1) / Q;
+    }
     if (w < k_eff) {
       const int u0 = (int)((long long)w * U / k_eff);
       const int u1 = (int)((long long)(w + 1) * U / k_eff);
       if (S > 64) {
-        win = load_window<SEL>(p, 0, 0, lane);
+        win = load_window<SEL>(p, 0, 0, lane, weighted);
         while (win.base + win.total <= u0 && win.s0 + 64 < S)
-          win = load_window<SEL>(p, win.s0 + 64, win.base + win.total, lane);
+          win = load_window<SEL>(p, win.s0 + 64, win.base + win.total, lane, weighted);
       }
-      // the sequence holding unit u0: the first with units past it
-      const unsigned long long hit = __ballot(win.n > 0 && win.P + win.n > u0);
-      int s = hit ? win.s0 + (int)__ffsll((long long)hit) - 1 : S;
+      // the first sequence with a unit starting at or past u0 (weighted, it
+      // may lie in the next window)
+      const unsigned long long hit = __ballot(win.n > 0 && win.P + (win.n - 1) * step >= u0);
+      int s = hit ? win.s0 + (int)__ffsll((long long)hit) - 1 : min(win.s0 + 64, S);
       while (s < S) {
-        if (s >= win.s0 + 64) win = load_window<SEL>(p, win.s0 + 64, win.base + win.total, lane);
+        if (s >= win.s0 + 64) win = load_window<SEL>(p, win.s0 + 64, win.base + win.total, lane, weighted);
         const int l = s - win.s0;
         const int n = __builtin_amdgcn_readlane(win.n, l);
         const int P = __builtin_amdgcn_readlane(win.P, l);
         const int L = __builtin_amdgcn_readlane(win.L, l);
         if (P >= u1) break;
-        if (n > 0) {
-          const int i0 = max(u0 - P, 0), i1 = min(u1 - P, n);
+        // the units starting in [u0, u1): unit i starts at P + i step
+        const int i0 = min(n, u0 > P ? (u0 - P + step - 1) / step : 0);
+        const int i1 = min(n, (u1 - P + step - 1) / step);
+        if (i0 < i1) {
           SegBlocks sb;
           if constexpr (SEL) {
             // units are entries i0 .. i1-1 of the sequence's selection
@@ -459,7 +486,7 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
             sb = segment_blocks(p, L, i0, i1);
           }
           const int whole = (i0 == 0 && i1 == n) ? 1 : 0;
-          const int upper = (P + i0 == u0) ? 0 : 1;   // not the workgroup's first segment
+          const int upper = nseg > 0 ? 1 : 0;   // not the workgroup's first segment
           const int key = (s << 8) | (min(nseg, 63) << 2) | (upper << 1) | whole;
           // the grid is sized so that every range fits; the bound only
           // keeps a wrong size from writing past the list
@@ -484,7 +511,8 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
             ++nend;
           }
           if (i0 == 0 && p.plan && blockIdx.y == 0 && lane == 0) {
-            const int w_last = (int)(((long long)(P + n) * k_eff - 1) / U);
+            // the workgroup whose run holds the start of the last unit
+            const int w_last = (int)(((long long)(P + (n - 1) * step + 1) * k_eff - 1) / U);
             // w: 1 when a whole sequence left its record in srec
             reinterpret_cast<int4*>(p.plan)[s] = make_int4(2 * w + upper, w, w_last, p.srec && w_last == w ? 1 : 0);
           }
