@@ -11,11 +11,12 @@
 // (m, l, acc) that a merge kernel combines by log-sum-exp.
 //
 // Kernels:
-//  * paged_attn_wave_kernel - bf16 / f16 caches and INT8 / FP8-E4M3 codes
-//    (converted to the query's 16-bit type in registers).  Each workgroup
-//    takes an equal run of the batch's partitions (stream-K style, crossing
-//    sequence boundaries) and runs one wave per KV head over the same list
-//    of physical blocks.  Per 16-token block: S^T = K Q^T on
+//  * paged_attn_wave_kernel - bf16 / f16 caches and INT8, INT4, FP8-E4M3 and
+//    FP8-E5M2 codes (converted to a 16-bit type in registers).  Each
+//    workgroup takes an equal run of the batch's partitions, or of its
+//    blocks when partitions span several (stream-K style, crossing sequence
+//    boundaries), and runs one wave per KV head over the same list of
+//    physical blocks.  Per 16-token block: S^T = K Q^T on
 //    v_mfma_f32_16x16x32 (K rows go straight from HBM into the A operand;
 //    the query group, padded to 16 heads, is the B operand), then out^T +=
 //    V^T P^T on v_mfma_f32_16x16x16, where the score tile already has the
@@ -28,7 +29,11 @@
 //    0 * NaN in the MFMA) and keeps the ring branch-free.
 //  * paged_attn_simple_kernel - fp32 caches (and any group size): scores in
 //    LDS, plain fp32 FMAs.  Exact fp32 arithmetic, for the fp32 path.
-//  * paged_attn_merge_kernel - log-sum-exp combine of the partials.
+//  * paged_attn_merge_kernel - log-sum-exp combine of the partials (and,
+//    after a shared prefix, of the prefix's record).
+//  * prefix_attn_kernel - blocks every sequence of the batch shares,
+//    attended once for all query rows (a dense product on the matrix cores),
+//    leaving one record per (sequence, query head) for the merge.
 //
 // Scores are kept in the log2 domain: s2 = (q.k) * sm_scale * log2(e), so
 // exp(s - m) = exp2(s2 - m2).
