@@ -257,14 +257,13 @@ def measure(w, steps, warmup, copies, graph=False, cascade=False):
     # fork's two sequences share blocks
     stream_kv = cascade or not (w.prefix_tokens or w.fork)
 
-    fused = not quant and not w.sink and not w.window
+    fused = not quant
 
     def step(r):
         """One decode step as the library runs it in production: the slot
         write inside the decode (pkv_paged_attn_decode_append) for 16-bit
-        caches without a keep-mask; otherwise the slot write (none for code
-        caches, written whole by the quantiser at prefill), the partition
-        pass and the merge."""
+        caches; for code caches (written whole by the quantiser at prefill)
+        the partition pass and the merge."""
         if cascade:
             pkv.paged_attn_decode_shared_prefix(out, t["query"], r.k_cache, r.v_cache, r.block_tables, r.lens,
                                                 w.sm_scale, P, key=t["new_key"], value=t["new_value"],
@@ -273,7 +272,8 @@ def measure(w, steps, warmup, copies, graph=False, cascade=False):
         elif fused:
             pkv.paged_attn_decode_append(out, t["query"], r.k_cache, r.v_cache, t["new_key"], t["new_value"],
                                          positions, r.block_tables, r.lens, w.sm_scale, slot_mapping=slots,
-                                         partition_size=psize, workspace=ws, stream_kv=stream_kv)
+                                         partition_size=psize, sink_tokens=w.sink, window_tokens=w.window,
+                                         workspace=ws, stream_kv=stream_kv)
         else:
             step_split(r)
 

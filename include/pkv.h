@@ -405,9 +405,11 @@ pkv_status pkv_quantize_kv(const void* src_cache, int src_dtype, void* dst_codes
  * workgroup that reads that block, before it reads it, so with any other p
  * the attention may or may not see the new row.  Rows of sequences with
  * p < 0, or whose table entry is outside [0, num_blocks), are not written.
- * bf16 or f16 caches of the query dtype; no keep-mask.  Workspace,
- * partition_size and flags as in pkv_paged_attn_decode.  One launch fewer
- * per decode step than pkv_append_kv followed by the decode.
+ * bf16 or f16 caches of the query dtype.  Workspace, partition_size,
+ * sink_tokens / window_tokens (the keep-mask; the new row is written
+ * whether or not the mask keeps it) and flags as in pkv_paged_attn_decode.
+ * One launch fewer per decode step than pkv_append_kv followed by the
+ * decode.
  */
 pkv_status pkv_paged_attn_decode_append(void* out, const void* query, int q_dtype, void* k_cache, void* v_cache,
                                         int kv_dtype, const void* key, const void* value,
@@ -415,8 +417,8 @@ pkv_status pkv_paged_attn_decode_append(void* out, const void* query, int q_dtyp
                                         const int32_t* block_tables, int max_blocks_per_seq,
                                         const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                                         int head_dim, int block_size, int num_blocks, float sm_scale,
-                                        int partition_size, unsigned flags, void* workspace,
-                                        size_t workspace_bytes, void* stream);
+                                        int partition_size, int sink_tokens, int window_tokens, unsigned flags,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Decode over a batch whose sequences all begin with the same prefix_blocks

@@ -62,7 +62,7 @@ _SIGS = {
     "pkv_paged_attn_decode_selected": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                         ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_append": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
-                                      _i, ctypes.c_uint, _p, _sz, _p], _i),
+                                      _i, _i, _i, ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_shared_prefix": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i,
                                              _i, _f, _i, _i, ctypes.c_uint, _p, _sz, _p], _i),
     "pkv_paged_attn_shared_prefix_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i, _i], _sz),
@@ -477,7 +477,8 @@ def quantize_kv_grouped(src_cache, dst_codes, dst_group_scales, code_dtype, grou
 
 
 def paged_attn_decode_append(out, query, k_cache, v_cache, key, value, positions, block_tables, seq_lens, sm_scale,
-                             slot_mapping=None, partition_size=0, workspace=None, stream_kv=False):
+                             slot_mapping=None, partition_size=0, sink_tokens=0, window_tokens=0, workspace=None,
+                             stream_kv=False):
     """Decode with the step's slot write fused in (``pkv_paged_attn_decode_append``):
     key/value [S, Hkv, D] of each sequence's new token go to position
     positions[s] (= seq_lens[s] - 1, or < 0 for none), then attention over
@@ -494,8 +495,8 @@ def paged_attn_decode_append(out, query, k_cache, v_cache, key, value, positions
     _check(lib.pkv_paged_attn_decode_append(
         _ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache), _ptr(key), _ptr(value),
         _ptr(positions), _ptr(slot_mapping), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, Hq, Hkv, D,
-        BS, NB, float(sm_scale), int(partition_size), DECODE_STREAM_KV if stream_kv else 0, _ptr(workspace),
-        ws_bytes, _stream(query)))
+        BS, NB, float(sm_scale), int(partition_size), int(sink_tokens), int(window_tokens),
+        DECODE_STREAM_KV if stream_kv else 0, _ptr(workspace), ws_bytes, _stream(query)))
     return out
 
 

@@ -414,15 +414,15 @@ extern "C" pkv_status pkv_paged_attn_decode_append(
     void* out, const void* query, int q_dtype, void* k_cache, void* v_cache, int kv_dtype, const void* key,
     const void* value, const int32_t* positions, int32_t* slot_mapping_out, const int32_t* block_tables,
     int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-    int block_size, int num_blocks, float sm_scale, int partition_size, unsigned flags, void* workspace,
-    size_t workspace_bytes, void* stream) {
+    int block_size, int num_blocks, float sm_scale, int partition_size, int sink_tokens, int window_tokens,
+    unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   const char* who = "pkv_paged_attn_decode_append";
   if (kv_dtype != q_dtype || (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16))
     return fail(PKV_EUNSUPPORTED, "%s: the fused write is built for bf16 / f16 caches of the query dtype", who);
   if (num_seqs > 0 && (!key || !value || !positions)) return fail(PKV_EINVAL, "%s: null pointer argument", who);
   AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, nullptr, nullptr, block_tables,
                          max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                         num_blocks, sm_scale, partition_size, 0, 0, flags, stream);
+                         num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, flags, stream);
   a.new_k = key;
   a.new_v = value;
   a.positions = positions;

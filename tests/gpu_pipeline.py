@@ -118,8 +118,8 @@ class GpuRun:
                 return
             pkv.paged_attn_decode_append(out, query, self.k_cache, self.v_cache, tensors["new_key"],
                                          tensors["new_value"], positions, self.block_tables, self.lens, w.sm_scale,
-                                         slot_mapping=self.step_slots, partition_size=psize,
-                                         stream_kv=not (w.prefix_tokens or w.fork))
+                                         slot_mapping=self.step_slots, partition_size=psize, sink_tokens=w.sink,
+                                         window_tokens=w.window, stream_kv=not (w.prefix_tokens or w.fork))
             return
         if fused:
             self.step_slots = torch.empty(w.S, dtype=torch.int32, device=self.device)

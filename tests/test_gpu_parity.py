@@ -38,6 +38,8 @@ CASES = {
     "quant_i4_f16q": ("quant_kv_32k_b16", dict(S=2, fixed_len=704, q_dtype="f16", src_dtype="f16",
                                                 kv_dtype="i4")),
     "ctx_small": ("ctx128k_b4", dict(S=2, fixed_len=5000)),
+    # the keep-mask (4 sinks + a 1000-token window) with the slot write fused in
+    "ctx_small_streaming": ("ctx128k_b4", dict(S=3, fixed_len=5000, sink=4, window=1000, partition_size=0)),
     "mqa_d64": ("llama3_8b_b64", dict(S=4, Hq=8, Hkv=1, D=64, len_lo=1, len_hi=700)),
     "mha_d64": ("llama3_8b_b64", dict(S=4, Hq=4, Hkv=4, D=64, len_lo=1, len_hi=300)),
     "g16": ("llama3_8b_b64", dict(S=3, Hq=32, Hkv=2, len_lo=100, len_hi=700)),
@@ -127,7 +129,7 @@ def test_fused_append_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["llama_small", "prefix_small", "llama_small_f16", "many_short", "one_long",
-                                  "hkv16", "mqa_d64", "g16"])
+                                  "hkv16", "mqa_d64", "g16", "ctx_small_streaming"])
 @pytest.mark.parametrize("psize", [0, 64, 512])
 def test_decode_with_fused_slot_write(name, psize):
     """pkv_paged_attn_decode_append (the slot write inside the decode) leaves

@@ -189,10 +189,10 @@ def test_argument_errors_return_before_launch():
     assert L.pkv_reshape_and_cache(None, None, None, None, 5, None, 4, 10, 16, 8, 128, None) == 2
     # fused slot write: 16-bit caches of the query dtype only
     st = L.pkv_paged_attn_decode_append(None, None, 1, None, None, 3, None, None, None, None, None, 4, None, 2, 32, 8,
-                                        128, 16, 10, 0.1, 0, 0, None, 0, None)
+                                        128, 16, 10, 0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 2 and "fused" in pkv.last_error()
     st = L.pkv_paged_attn_decode_append(None, None, 1, None, None, 1, None, None, None, None, None, 4, None, 2, 32, 8,
-                                        128, 16, 10, 0.1, 0, 0, None, 0, None)
+                                        128, 16, 10, 0.1, 0, 0, 0, 0, None, 0, None)
     assert st == 1 and "null" in pkv.last_error()
     # grouped scales: i8 / i4 codes; scale pointers; scale group kind
     st = L.pkv_paged_attn_decode_grouped(None, None, 1, None, None, 4, 1, 1, 1, None, 4, None, 2, 32, 8, 128, 16, 10,
