@@ -665,7 +665,10 @@ def main():
     long_ctx = None
     primary = not args.quest and not args.grouped and args.query_tokens == 1
     if not args.no_long_context and primary and args.workload != "ctx128k_b4":
-        long_ctx = long_context_entry(min(args.steps, 50), min(args.warmup, 20))
+        try:
+            long_ctx = long_context_entry(min(args.steps, 50), min(args.warmup, 20))
+        except Exception as e:   # reported in the line, not fatal to it
+            long_ctx = {"error": str(e)[:500]}
     others = None
     if not args.no_other_configs and primary and args.workload == "llama3_8b_b64" and not args.kv_dtype \
             and not args.streaming and not args.partition_size:
@@ -773,7 +776,11 @@ def other_config_entries(steps, warmup):
                   ["--workload", "quant_kv_32k_b16", "--kv-dtype", "fp8e4m3"],
                   ["--workload", "ctx128k_b4", "--streaming"]):
         print(f"[bench] other config: {' '.join(extra)}", file=sys.stderr, flush=True)
-        d = child_bench(extra, steps, warmup)
+        try:
+            d = child_bench(extra, steps, warmup)
+        except Exception as e:   # a failed secondary entry is reported, not fatal to the line
+            out.append({"args": " ".join(extra), "error": str(e)[:500]})
+            continue
         unique = d["config"]["kv_bytes_unique_per_step"]
         gbps = unique / (d["ms_per_step"] * 1e-3) / 1e9
         out.append({
