@@ -185,6 +185,14 @@ def paged_attn_workspace_bytes(kv_dtype, num_seqs, num_q_heads, num_kv_heads, he
                                               head_dim, max_seq_len, partition_size)
 
 
+def _check_tables(block_tables, seq_lens, S):
+    """block_tables [S, max_blocks] and seq_lens [S], both int32."""
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(seq_lens.shape) != (S,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and seq_lens [num_seqs]")
+
+
 def _attn_call(fn, out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_scales, v_scales,
                partition_size, sink_tokens, window_tokens, workspace, kv_dtype, stream_kv):
     _contig(out, query, k_cache, v_cache, block_tables, seq_lens, k_scales, v_scales, workspace)
@@ -193,10 +201,7 @@ def _attn_call(fn, out, query, k_cache, v_cache, block_tables, seq_lens, sm_scal
     if _head_dim(k_cache, _dtype(k_cache, kv_dtype)) != D or tuple(v_cache.shape) != tuple(k_cache.shape) \
             or tuple(out.shape) != tuple(query.shape):
         raise ValueError("shape mismatch between query, caches and out")
-    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise TypeError("block_tables and seq_lens must be int32")
-    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
-        raise ValueError("block_tables must be [num_seqs, max_blocks] and seq_lens [num_seqs]")
+    _check_tables(block_tables, seq_lens, S)
     mbs = block_tables.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(fn(_ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache, kv_dtype),
@@ -255,6 +260,7 @@ def paged_attn_decode_multi(out, query, k_cache, v_cache, block_tables, seq_lens
     if _head_dim(k_cache, kvdt) != D or tuple(out.shape) != tuple(query.shape) \
             or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("shape mismatch between query, caches and out")
+    _check_tables(block_tables, seq_lens, S)
     mbs = block_tables.shape[1]
     if workspace is None:
         nbytes = paged_attn_workspace_bytes(kvdt, S, Hq * T, Hkv, D, mbs * BS, partition_size)
@@ -490,6 +496,7 @@ def paged_attn_decode_append(out, query, k_cache, v_cache, key, value, positions
         raise ValueError("shape mismatch between query, caches and out")
     if tuple(key.shape) != (S, Hkv, D) or value.shape != key.shape or key.dtype != k_cache.dtype:
         raise ValueError("key/value must be [S, Hkv, D] of the cache's dtype")
+    _check_tables(block_tables, seq_lens, S)
     workspace = _workspace_for(query, k_cache, block_tables, partition_size, workspace, None)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pkv_paged_attn_decode_append(
@@ -520,10 +527,7 @@ def paged_attn_decode_shared_prefix(out, query, k_cache, v_cache, block_tables, 
     NB, BS, Hkv = k_cache.shape[:3]
     if k_cache.shape[3] != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(query.shape):
         raise ValueError("shape mismatch between query, caches and out")
-    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise TypeError("block_tables and seq_lens must be int32")
-    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
-        raise ValueError("block_tables must be [num_seqs, max_blocks] and seq_lens [num_seqs]")
+    _check_tables(block_tables, seq_lens, S)
     if key is not None and (tuple(key.shape) != (S, Hkv, D) or value is None or value.shape != key.shape
                             or key.dtype != k_cache.dtype or positions is None):
         raise ValueError("key/value must be [S, Hkv, D] of the cache's dtype, with positions")
@@ -565,6 +569,7 @@ def paged_attn_decode_grouped(out, query, k_cache, v_cache, block_tables, seq_le
     if tuple(k_channel_scales.shape) != (NB, Hkv, D) or tuple(v_token_scales.shape) != (NB, Hkv, BS) \
             or tuple(k_tile_scales.shape) != (NB, Hkv):
         raise ValueError("scales must be [NB, Hkv] (tile), [NB, Hkv, D] (channel) and [NB, Hkv, 16] (token)")
+    _check_tables(block_tables, seq_lens, S)
     workspace = _workspace_for(query, k_cache, block_tables, partition_size, workspace, kvdt)
     mbs = block_tables.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -973,7 +973,8 @@ void paged_attn_wave_kernel(AttnParams p) {
     for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * factor;
     // query token t sees positions up to L - T + t: blocks reaching past
     // L - T are masked per column
-    if (block_masked(t0, e)) {
+    const bool msk = block_masked(t0, e);
+    if (msk) {
       const int lim = L - T + lane_t;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -983,19 +984,26 @@ void paged_attn_wave_kernel(AttnParams p) {
     }
     const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     // ---- online softmax, rescaling only when a score passes m2 + slack -----
+    // A column may have seen no visible position yet (m2 = -inf) and see
+    // none in this block either: with several query tokens, a segment can
+    // start at a block past a column's causal limit.  Such a column keeps
+    // alpha = 1 and weights 0 (exp2(-inf - -inf) would be NaN), as an empty
+    // partition does in the log-sum-exp merge.
     if (__ballot(lm > m2 + kSlack)) {
       float bmax = fmaxf(lm, __shfl_xor(lm, 16, 64));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
       const float mnew = fmaxf(m2, bmax);
-      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);   // 0 while m2 = -inf
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2 - mnew);   // 0 while m2 = -inf
       lsum *= alpha;
 #pragma unroll
       for (int n = 0; n < NN; ++n) acc[n] *= alpha;
       m2 = mnew;
     }
+    // only a masked block can hold a column whose scores are all -inf
+    const float mb = (msk & (m2 == -INFINITY)) ? 0.f : m2;
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m2);
+    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - mb);
     // P^T as the B operand (tokens 4kg..4kg+3 of head g), V scale folded in
     float vsc[4];
 #pragma unroll

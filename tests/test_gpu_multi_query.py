@@ -10,6 +10,7 @@ import torch
 
 from oracle import attention
 from oracle_pipeline import OracleRun, to_raw
+from split_model import causal_tail_starts, cdiv, tail_cut_lens
 from workloads import draw_tensors, get_workload
 
 pytestmark = pytest.mark.gpu
@@ -31,6 +32,43 @@ TOKENS = {"llama_shape": [1, 2, 4], "g8_f16": [2], "i8": [4], "fp8": [3], "i4": 
 _runs = {}
 
 
+def device_cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+# Cases whose split starts a workgroup's segment past the first query
+# token's causal limit (a block holding fewer than T of a cut sequence's
+# tokens), plus a sequence shorter than T: lengths from the CPU model of the
+# split with the device's compute-unit count (split_model.tail_cut_lens).
+# Such a block is partly filled, so the cases are 16-bit caches (the code
+# workloads quantise whole blocks only).
+TAIL = [("llama_shape", T, ps) for T in (2, 3, 4) for ps in (0, 64)] + [("g8_f16", 2, ps) for ps in (0, 64)]
+HKV = 8
+
+
+def tail_case(name, T, psize):
+    key = ("tail", name, T, psize)
+    if key not in _runs:
+        base, ov = CASES[name]
+        ov = {k: v for k, v in ov.items() if k not in ("S", "len_lo", "len_hi", "fixed_len", "prefix_tokens")}
+        if base == "shared_prefix_b128":
+            ov.update(prefix_tokens=0, fork=())
+        prompt = tail_cut_lens(T, psize, HKV, S=4, cus=device_cus())
+        ov.update(S=len(prompt), fixed_lens=tuple(prompt))
+        _runs[key] = make_run(base, ov)
+    return _runs[key]
+
+
+def make_run(base, ov):
+    from gpu_pipeline import GpuRun
+    w = get_workload(base, **ov)
+    t = draw_tensors(w, "cuda")
+    g = GpuRun(w, t)
+    torch.cuda.synchronize()
+    o = OracleRun(w, t)
+    return w, t, g, o
+
+
 def run_case(name):
     if name not in _runs:
         from gpu_pipeline import GpuRun
@@ -47,9 +85,26 @@ def run_case(name):
 @pytest.mark.parametrize("name,T", [(n, T) for n in CASES for T in TOKENS[n]])
 @pytest.mark.parametrize("psize", [0, 64])
 def test_multi_query_parity(name, T, psize):
+    check_multi(run_case(name), name, T, psize)
+
+
+@pytest.mark.parametrize("name,T,psize", TAIL)
+def test_multi_query_segment_in_causal_tail(name, T, psize):
+    """A workgroup's segment starts at a block past token 0's causal limit,
+    and one sequence is shorter than T: outputs finite and within 2e-2 of
+    the oracle (zeros for a token that sees no position)."""
+    run = tail_case(name, T, psize)
+    w, t, g, o = run
+    lens = g.lens.tolist()
+    cuts = causal_tail_starts(lens, psize, T, w.Hkv, g.mbs, device_cus())
+    assert any(t0 > 0 for _, t0 in cuts) and min(lens) < T, (lens, cuts)
+    check_multi(run, name, T, psize)
+
+
+def check_multi(run, name, T, psize):
     import paged_kv_cache_466_amd as pkv
     from gpu_pipeline import uint8_kind
-    w, t, g, o = run_case(name)
+    w, t, g, o = run
     print(f"[multi] case={name} T={T} psize={psize} lens={g.lens.tolist()}", flush=True)
     gen = torch.Generator(device="cuda").manual_seed(1000 + T)
     qdt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.q_dtype]

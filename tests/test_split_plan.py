@@ -22,57 +22,7 @@ import random
 
 import pytest
 
-
-def cdiv(a, b):
-    return -(-a // b)
-
-
-def grid_slots(S, hkv, num_partitions, psize, cus=256):
-    """Workgroups along the sequence axis, as the host sizes the grid."""
-    list_cap = 128 * min(hkv, 8)
-    k = max(cdiv(8 * cus, hkv), S)
-    bpu = max(psize // 16, 1)
-    cap = (list_cap - bpu + 1) // bpu if 3 * bpu <= list_cap else list_cap // bpu
-    if cap > 0:
-        k = max(k, cdiv(S * num_partitions, cap))
-    return k, list_cap
-
-
-def plan(lens, psize, K, list_cap):
-    """Owner workgroup of every (sequence, unit), blocks per workgroup and the
-    last workgroup of each sequence, by the kernel's rules (full attention)."""
-    bpp = psize // 16
-    min_units = max(1, 128 // psize)
-    weighted = bpp > 1 and 3 * bpp <= list_cap
-    step = bpp if weighted else 1
-    seqs, P = [], 0
-    for L in lens:
-        nb, n = cdiv(L, 16), cdiv(L, psize)
-        seqs.append((P, n, nb))
-        P += nb if weighted else n
-    U = P
-    if U == 0:
-        return {}, [], {}
-    if weighted:
-        k_eff = max(1, min(K, min(U // (min_units * step), U // step)))
-    else:
-        Q = max(min_units, cdiv(U, K))
-        k_eff = cdiv(U, Q)
-    owner, blocks, last = {}, [0] * k_eff, {}
-    for w in range(k_eff):
-        u0, u1 = w * U // k_eff, (w + 1) * U // k_eff
-        for s, (P, n, nb) in enumerate(seqs):
-            if P >= u1:
-                break
-            i0 = min(n, cdiv(u0 - P, step) if u0 > P else 0)
-            i1 = min(n, cdiv(u1 - P, step))
-            for u in range(i0, i1):
-                assert (s, u) not in owner
-                owner[(s, u)] = w
-                blocks[w] += min((u + 1) * bpp, nb) - u * bpp
-            if i0 == 0 and i1 > 0:
-                last[s] = ((P + (n - 1) * step + 1) * k_eff - 1) // U
-    return owner, blocks, last
+from split_model import cdiv, grid_slots, plan
 
 
 def check(lens, psize, hkv):
@@ -115,3 +65,22 @@ def test_block_balanced_split_at_128k():
 @pytest.mark.parametrize("psize", [16, 64, 512])
 def test_one_sequence_many_workgroups(psize):
     check([20000], psize, 8)
+
+
+@pytest.mark.parametrize("T", [2, 3, 4])
+@pytest.mark.parametrize("psize", [0, 64])
+def test_tail_cut_generator_reaches_the_causal_tail(T, psize):
+    """The multi-token parity cases' lengths put a workgroup boundary at a
+    unit past position L - T of a cut sequence (a block holding fewer than T
+    of its tokens) and include a sequence shorter than T."""
+    from split_model import causal_tail_starts, tail_cut_lens
+    for append in (True, False):
+        prompt = tail_cut_lens(T, psize, 8, append=append)
+        lens = [L + (1 if append else 0) for L in prompt]
+        mbs = max(cdiv(L, 16) for L in lens) + 1
+        cuts = causal_tail_starts(lens, psize, T, 8, mbs)
+        assert any(t0 > 0 for _, t0 in cuts)
+        assert min(lens) < T
+        # the start is a true cut: inside the sequence, past token 0's limit
+        for s, t0 in cuts:
+            assert t0 == 0 or lens[s] - T < t0 < lens[s]
