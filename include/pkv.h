@@ -196,6 +196,33 @@ pkv_status pkv_paged_attn_decode(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same kernels and the same result,
+ * bit for bit; the scratch (merge plan and partial records) is a fixed
+ * device array of pkv_paged_attn_noalloc_scratch_bytes() bytes (64 MiB) that
+ * the library holds on every GPU it runs on until the process ends.  The
+ * call allocates nothing: no hipMalloc, no hipFree.
+ * Errors: PKV_EWORKSPACE when pkv_paged_attn_workspace_bytes(...) for these
+ * arguments exceeds that size (nothing is launched); otherwise as
+ * pkv_paged_attn_decode.  The PKV_CHECK=1 host check is not run (it copies
+ * the tables to the host); call pkv_validate_tables instead.
+ * Every call on one GPU shares that GPU's array, and each call overwrites
+ * what it needs before reading it: calls that overlap on one GPU (on
+ * different streams, or from several threads) race and must not be issued.
+ */
+size_t pkv_paged_attn_noalloc_scratch_bytes(void);
+pkv_status pkv_paged_attn_decode_noalloc(
+    void* out, const void* query, int q_dtype,
+    const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_scales, const float* v_scales,
+    const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* seq_lens, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+    float sm_scale, int partition_size, int sink_tokens, int window_tokens, unsigned flags,
+    void* stream);
+
+/*
  * The two kernels pkv_paged_attn_decode launches, exposed so that each can be
  * timed on its own.  pkv_paged_attn_partition takes the same arguments and
  * writes the partials to the workspace (or `out` directly when one partition

@@ -56,6 +56,8 @@ _SIGS = {
     "pkv_paged_attn_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "pkv_paged_attn_decode": (_ATTN, _i),
     "pkv_paged_attn_partition": (_ATTN, _i),
+    "pkv_paged_attn_noalloc_scratch_bytes": ([], _sz),
+    "pkv_paged_attn_decode_noalloc": (_ATTN[:-3] + [_p], _i),
     "pkv_paged_attn_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
     "pkv_paged_attn_decode_multi": ([_p, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                                      ctypes.c_uint, _p, _sz, _p], _i),
@@ -237,6 +239,27 @@ def paged_attn_decode(out, query, k_cache, v_cache, block_tables, seq_lens, sm_s
     return _attn_call(lib.pkv_paged_attn_decode, out, query, k_cache, v_cache, block_tables, seq_lens,
                       sm_scale, k_scales, v_scales, partition_size, sink_tokens, window_tokens, workspace,
                       kv_dtype, stream_kv)
+
+
+def paged_attn_decode_noalloc(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, k_scales=None,
+                              v_scales=None, partition_size=0, sink_tokens=0, window_tokens=0, kv_dtype=None,
+                              stream_kv=False):
+    """``paged_attn_decode`` without a workspace (``pkv_paged_attn_decode_noalloc``):
+    the library's fixed device scratch array stands in for it, so the call
+    allocates nothing.  Calls that overlap on one GPU race on that array."""
+    _contig(out, query, k_cache, v_cache, block_tables, seq_lens, k_scales, v_scales)
+    S, Hq, D = query.shape
+    NB, BS, Hkv = k_cache.shape[:3]
+    if _head_dim(k_cache, _dtype(k_cache, kv_dtype)) != D or tuple(v_cache.shape) != tuple(k_cache.shape) \
+            or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("shape mismatch between query, caches and out")
+    _check_tables(block_tables, seq_lens, S)
+    _check(lib.pkv_paged_attn_decode_noalloc(
+        _ptr(out), _ptr(query), _dtype(query), _ptr(k_cache), _ptr(v_cache), _dtype(k_cache, kv_dtype),
+        _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, Hq, Hkv, D, BS,
+        NB, float(sm_scale), int(partition_size), int(sink_tokens), int(window_tokens),
+        DECODE_STREAM_KV if stream_kv else 0, _stream(query)))
+    return out
 
 
 def paged_attn_partition(out, query, k_cache, v_cache, block_tables, seq_lens, sm_scale, workspace,

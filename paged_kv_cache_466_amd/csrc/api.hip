@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "pkv.h"
@@ -356,6 +357,74 @@ extern "C" pkv_status pkv_paged_attn_decode(PKV_ATTN_ARGS) {
                   max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                   num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, flags, workspace,
                   workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// decode without a caller workspace: the scratch is a fixed device array
+// ---------------------------------------------------------------------------
+namespace pkv {
+
+// The decode's scratch (merge plan and partial records) for callers that
+// cannot allocate.  Every GPU the library runs on holds its own copy of this
+// array until the process ends.  Host code must never pass `scratch` itself to
+// a kernel: on the host the name stands for a host-side shadow, not the device
+// copy.  Its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];   // device address of `scratch`, per device
+
+static pkv_status scratch_address(void** out, const char* who) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PKV_EHIP, "%s: hipGetDevice failed", who);
+  if (dev < 0 || dev >= 64) return fail(PKV_EUNSUPPORTED, "%s: device %d above 63", who, dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PKV_EHIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" size_t pkv_paged_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" pkv_status pkv_paged_attn_decode_noalloc(
+    void* out, const void* query, int q_dtype, const void* k_cache, const void* v_cache, int kv_dtype,
+    const float* k_scales, const float* v_scales, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* seq_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int num_blocks, float sm_scale, int partition_size, int sink_tokens, int window_tokens, unsigned flags,
+    void* stream) {
+  const char* who = "pkv_paged_attn_decode_noalloc";
+  AttnArgs a = fill_args(out, query, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, block_tables,
+                         max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         num_blocks, sm_scale, partition_size, sink_tokens, window_tokens, flags, stream);
+  // the same size rule as pkv_paged_attn_workspace_bytes, checked against
+  // the fixed array before anything is launched
+  if (num_seqs > 0 && num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+      max_blocks_per_seq >= 0 && block_size == 16 && partition_size >= 0) {
+    const size_t need = pkv_paged_attn_workspace_bytes(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                       max_blocks_per_seq * block_size, partition_size);
+    if (need > kNoAllocScratchBytes)
+      return fail(PKV_EWORKSPACE, "%s: the decode needs %zu bytes of scratch, above the fixed %zu", who, need,
+                  kNoAllocScratchBytes);
+  }
+  void* ws = nullptr;
+  if (num_seqs > 0) {
+    const pkv_status st = scratch_address(&ws, who);
+    if (st != PKV_OK) return st;
+  }
+  pkv_status st = prepare_attn(a, who, ws, kNoAllocScratchBytes, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  st = hip_status(launch_paged_attn_partition(a), who);
+  if (st != PKV_OK) return st;
+  return hip_status(launch_paged_attn_merge(a), who);
 }
 
 extern "C" pkv_status pkv_paged_attn_partition(PKV_ATTN_ARGS) {
