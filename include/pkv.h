@@ -632,6 +632,26 @@ pkv_status pkv_pool_decref(pkv_pool* pool, int32_t block);
 int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t block);
 
 /*
+ * Sequence-level operations ([P2] s.10 free-list example; [P1] "Prefix
+ * Caching"; [P3] copy-on-write), each all-or-nothing: on an error nothing
+ * changes.
+ * pkv_pool_allocate_sequence: blocks for a new sequence of num_tokens tokens,
+ *   ceil(num_tokens / block_size) of them taken from the front of the free
+ *   list in order into table_out[0 .. *n_out).  PKV_ENOMEM if too few are
+ *   free, PKV_EINVAL if table_capacity is smaller.
+ * pkv_pool_fork: a new sequence shares every block of table[0 .. n): each
+ *   gains one reference.  PKV_EINVAL if an entry is free or out of range.
+ * pkv_pool_release: a finished sequence drops one reference per entry of
+ *   table[0 .. n), in table order; blocks reaching 0 go to the back of the
+ *   free list in that order.  PKV_EINVAL if an entry is free, out of range,
+ *   or listed more often than it is referenced.
+ */
+pkv_status pkv_pool_allocate_sequence(pkv_pool* pool, int32_t num_tokens, int block_size,
+                                      int32_t* table_out, int32_t table_capacity, int32_t* n_out);
+pkv_status pkv_pool_fork(pkv_pool* pool, const int32_t* table, int32_t n);
+pkv_status pkv_pool_release(pkv_pool* pool, const int32_t* table, int32_t n);
+
+/*
  * Reserves the slot of token number seq_len of a sequence whose host table
  * table[0 .. *table_len) covers seq_len tokens.  If seq_len % block_size == 0
  * a new block is appended to the table (table_capacity bounds it).

@@ -101,6 +101,9 @@ _SIGS = {
     "pkv_pool_refcount": ([_p, ctypes.c_int32], ctypes.c_int32),
     "pkv_pool_append": ([_p, _p, ctypes.c_int32, _i32p, ctypes.c_int32, _i, _i32p, _i32p, _i32p], _i),
     "pkv_pool_stats": ([_p, _i32p, _i32p, _i32p], _i),
+    "pkv_pool_allocate_sequence": ([_p, ctypes.c_int32, _i, _p, ctypes.c_int32, _i32p], _i),
+    "pkv_pool_fork": ([_p, _p, ctypes.c_int32], _i),
+    "pkv_pool_release": ([_p, _p, ctypes.c_int32], _i),
     "pkv_pool_free_list": ([_p, _p, ctypes.c_int32, _i32p], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -686,18 +689,27 @@ class BlockPool:
         _check(lib.pkv_pool_free_list(self._h, ctypes.cast(arr, ctypes.c_void_p), n.value, ctypes.byref(n)))
         return list(arr[: n.value])
 
-    # sequence-level helpers
+    # sequence-level operations (pkv_pool_allocate_sequence / _fork / _release)
     def allocate_sequence(self, length, block_size=16):
-        return [self.alloc() for _ in range(-(-int(length) // block_size))]
+        cap = self.num_blocks
+        arr = (ctypes.c_int32 * max(cap, 1))()
+        n = ctypes.c_int32()
+        _check(lib.pkv_pool_allocate_sequence(self._h, int(length), int(block_size),
+                                              ctypes.cast(arr, ctypes.c_void_p), cap, ctypes.byref(n)))
+        return list(arr[: n.value])
+
+    @staticmethod
+    def _array(table):
+        return (ctypes.c_int32 * max(len(table), 1))(*[int(b) for b in table])
 
     def fork(self, table):
-        for b in table:
-            self.incref(b)
+        arr = self._array(table)
+        _check(lib.pkv_pool_fork(self._h, ctypes.cast(arr, ctypes.c_void_p), len(table)))
         return list(table)
 
     def release(self, table):
-        for b in table:
-            self.decref(b)
+        arr = self._array(table)
+        _check(lib.pkv_pool_release(self._h, ctypes.cast(arr, ctypes.c_void_p), len(table)))
 
 
 class PrefixCache:

@@ -19,7 +19,11 @@ LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libpkv.so")
 OBJDIR = os.path.join(ROOT, "_build", "pkv")
 
-SOURCES = ["api.hip", "cache_ops.hip", "paged_attn.hip", "quest.hip", "pool.cpp", "reuse.cpp"]
+SOURCES = ["api.hip", "cache_ops.hip", "paged_attn.hip", "quest.hip", "host.cpp", "pool.cpp", "reuse.cpp"]
+# the host-only sources, also built on their own under the address and
+# undefined-behaviour sanitizers (build_host_sanitized)
+HOST_SOURCES = ["host.cpp", "pool.cpp", "reuse.cpp"]
+SAN_LIB = os.path.join(ROOT, "_build", "san", "libpkv_host_san.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -61,6 +65,21 @@ def build(verbose=False):
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
     shutil.move(tmp, LIB)
     return LIB
+
+
+def build_host_sanitized():
+    """The host-only sources as one shared library built by g++ with
+    -fsanitize=address,undefined (every error fatal).  No GPU code is in it;
+    tests load it in a process of their own with the sanitizer runtime
+    preloaded.  Returns its path."""
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", f"-I{INCLUDE}", f"-I{CSRC}",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           *[os.path.join(CSRC, s) for s in HOST_SOURCES], "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized host build failed: {' '.join(cmd)}\n{r.stderr}")
+    return SAN_LIB
 
 
 if __name__ == "__main__":

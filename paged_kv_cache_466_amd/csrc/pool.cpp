@@ -8,6 +8,7 @@
 // when one of them writes into it.
 #include <deque>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "pkv.h"
@@ -80,6 +81,61 @@ extern "C" pkv_status pkv_pool_decref(pkv_pool* pool, int32_t block) {
 extern "C" int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t block) {
   if (!pool || block < 0 || block >= (int32_t)pool->refcount.size()) return -1;
   return pool->refcount[block];
+}
+
+extern "C" pkv_status pkv_pool_allocate_sequence(pkv_pool* pool, int32_t num_tokens, int block_size,
+                                                 int32_t* table_out, int32_t table_capacity, int32_t* n_out) {
+  if (!pool || !n_out) return pkv::fail(PKV_EINVAL, "pkv_pool_allocate_sequence: null argument");
+  if (block_size <= 0 || num_tokens < 0 || table_capacity < 0)
+    return pkv::fail(PKV_EINVAL, "pkv_pool_allocate_sequence: bad block_size, num_tokens or capacity");
+  const int64_t n = ((int64_t)num_tokens + block_size - 1) / block_size;
+  if (n > table_capacity) return pkv::fail(PKV_EINVAL, "pkv_pool_allocate_sequence: table capacity exceeded");
+  if (n > 0 && !table_out) return pkv::fail(PKV_EINVAL, "pkv_pool_allocate_sequence: null table");
+  if (n > (int64_t)pool->free_list.size())
+    return pkv::fail(PKV_ENOMEM, "pkv_pool_allocate_sequence: %lld blocks needed, %zu free", (long long)n,
+                     pool->free_list.size());
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t b = pool->free_list.front();
+    pool->free_list.pop_front();
+    pool->refcount[b] = 1;
+    table_out[i] = b;
+  }
+  *n_out = (int32_t)n;
+  return PKV_OK;
+}
+
+// Occurrences of each block in table[0 .. n) that is in use; false when some
+// entry is free or out of range.
+static bool count_in_use(const pkv_pool* pool, const int32_t* table, int32_t n,
+                         std::unordered_map<int32_t, int32_t>& uses) {
+  for (int32_t i = 0; i < n; ++i) {
+    if (!in_use(pool, table[i])) return false;
+    ++uses[table[i]];
+  }
+  return true;
+}
+
+extern "C" pkv_status pkv_pool_fork(pkv_pool* pool, const int32_t* table, int32_t n) {
+  if (!pool || n < 0 || (n > 0 && !table)) return pkv::fail(PKV_EINVAL, "pkv_pool_fork: bad argument");
+  std::unordered_map<int32_t, int32_t> uses;
+  if (!count_in_use(pool, table, n, uses)) return pkv::fail(PKV_EINVAL, "pkv_pool_fork: table names a free block");
+  for (int32_t i = 0; i < n; ++i) pool->refcount[table[i]] += 1;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_pool_release(pkv_pool* pool, const int32_t* table, int32_t n) {
+  if (!pool || n < 0 || (n > 0 && !table)) return pkv::fail(PKV_EINVAL, "pkv_pool_release: bad argument");
+  std::unordered_map<int32_t, int32_t> uses;
+  if (!count_in_use(pool, table, n, uses))
+    return pkv::fail(PKV_EINVAL, "pkv_pool_release: table names a free block");
+  for (const auto& kv : uses)
+    if (pool->refcount[kv.first] < kv.second)
+      return pkv::fail(PKV_EINVAL, "pkv_pool_release: block %d listed more often than it is referenced", kv.first);
+  // in table order, so that blocks freed here reach the back of the free
+  // list in that order
+  for (int32_t i = 0; i < n; ++i)
+    if (--pool->refcount[table[i]] == 0) pool->free_list.push_back(table[i]);
+  return PKV_OK;
 }
 
 extern "C" pkv_status pkv_pool_append(pkv_pool* pool, int32_t* table, int32_t table_capacity,

@@ -350,3 +350,27 @@ def test_h2o_matches_page_and_oracle():
         assert pkv.h2o_retain(scores, budget, recent) == oracle.reuse.h2o_retain(scores, budget, recent)
     with pytest.raises(pkv.PkvError):
         pkv.h2o_retain([1.0, float("nan")], 1, 0)
+
+
+def test_pool_sequence_operations_are_all_or_nothing():
+    """pkv_pool_allocate_sequence / _fork / _release change nothing on an
+    error: too few free blocks, a free or out-of-range block, a block listed
+    more often than it is referenced."""
+    p = pkv.BlockPool(5)
+    a = p.allocate_sequence(40)                   # 3 blocks, the last partial
+    assert a == [0, 1, 2] and p.free_list() == [3, 4]
+    with pytest.raises(pkv.PkvError, match="needed"):
+        p.allocate_sequence(48)                   # 3 more blocks, 2 free
+    assert p.free_list() == [3, 4]
+    f = p.fork(a)
+    assert [p.refcount(b) for b in f] == [2, 2, 2]
+    with pytest.raises(pkv.PkvError):
+        p.fork([0, 3])                            # 3 is free
+    assert [p.refcount(b) for b in (0, 3)] == [2, 0]
+    with pytest.raises(pkv.PkvError):
+        p.release([0, 0, 0])                      # 3 references asked, 2 held
+    assert p.refcount(0) == 2
+    p.release(f)
+    p.release(a[::-1])                            # freed in table order
+    assert p.free_list() == [3, 4, 2, 1, 0]
+    assert p.allocate_sequence(0) == []
