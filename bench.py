@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 / f16 matrix peak (AMD public spec)
 BYTES = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1, "fp8e4m3": 1, "fp8e5m2": 1, "i4": 0.5}
 CODES = ("i8", "fp8e4m3", "fp8e5m2", "i4")
 
@@ -502,7 +503,8 @@ def measure_multi(w, steps, warmup, copies, T):
     out = torch.empty_like(q)
     mbs = g.block_tables.shape[1]
     psize = w.partition_size
-    nbytes = pkv.paged_attn_workspace_bytes(w.kv_dtype, S, Hq * T, w.Hkv, D, mbs * 16, psize)
+    chunk = w.G * T > 16          # the query-tile pass: no workspace
+    nbytes = 0 if chunk else pkv.paged_attn_workspace_bytes(w.kv_dtype, S, Hq * T, w.Hkv, D, mbs * 16, psize)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
     positions = (g.lens - 1).contiguous()
     slots = torch.empty(S, dtype=torch.int32, device="cuda")
@@ -536,6 +538,26 @@ def measure_multi(w, steps, warmup, copies, T):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
     attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    # algorithmic work of the attention call: token t of a sequence of length
+    # L scores and weighs L - T + t + 1 positions, 4 D flops per position and
+    # query head; bytes: every K/V row once, the queries and the outputs
+    vis = sum(max(0, int(L) - T + i + 1) for L in lens for i in range(T))
+    flops = 4.0 * vis * Hq * D
+    qo_bytes = 2 * q.numel() * q.element_size()
+    hbm_bytes = kv_bytes + qo_bytes
+    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    intensity = flops / hbm_bytes
+    sec = attn_ms * 1e-3
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": round(hbm_bytes / sec / 1e9, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(hbm_bytes / sec / 1e9 / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / sec / 1e12, 2), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / sec / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+    roof.update({"kernel": "chunk_attn_kernel" if chunk else "paged_attn_wave_kernel + paged_attn_merge_kernel",
+                 "flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
+                 "tflops": round(flops / sec / 1e12, 2), "hbm_gbps": round(hbm_bytes / sec / 1e9, 2),
+                 "traffic": None})
     return {
         "metric": "multi-token paged decode: query tokens/s + KV-read GB/s",
         "value": round(S * T / (ms * 1e-3), 1), "unit": "tokens/s",
@@ -546,6 +568,7 @@ def measure_multi(w, steps, warmup, copies, T):
                    "query_tokens": T, "kv_bytes_per_step": int(kv_bytes)},
         "attn_us": round(attn_ms * 1e3, 2),
         "attn_kv_gbps": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 2),
+        "roofline": roof,
     }
 
 

@@ -393,6 +393,27 @@ extern "C" pkv_status pkv_paged_attn_decode_multi(
                          max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                          num_blocks, sm_scale, partition_size, 0, 0, flags, stream);
   a.qtok = num_query_tokens;
+  if (num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+      (long long)(num_q_heads / num_kv_heads) * num_query_tokens > 16) {
+    // more query rows per KV head than the decode's 16 MFMA columns: the
+    // query-tile pass (a chunk of prefill), which needs no workspace
+    if (num_seqs < 0 || max_blocks_per_seq < 0 || num_blocks < 0) return fail(PKV_EINVAL, "%s: negative size", who);
+    if (q_dtype != PKV_BF16 && q_dtype != PKV_F16)
+      return fail(PKV_EUNSUPPORTED, "%s: more than 16 query rows per KV head need a bf16 or f16 query", who);
+    if (kv_dtype != q_dtype)
+      return fail(PKV_EUNSUPPORTED, "%s: more than 16 query rows per KV head are built for 16-bit caches", who);
+    pkv_status st = check_cache_shape(who, block_size, num_kv_heads, head_dim);
+    if (st != PKV_OK) return st;
+    if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
+      return fail(PKV_EINVAL, "%s: partition_size must be 0 or a positive multiple of block_size", who);
+    if (flags & ~(unsigned)PKV_DECODE_STREAM_KV) return fail(PKV_EINVAL, "%s: unknown flags 0x%x", who, flags);
+    if (num_seqs > 65535 || num_kv_heads > 65535 || (long long)num_query_tokens * num_q_heads >= (1LL << 24))
+      return fail(PKV_EUNSUPPORTED, "%s: grid too large (num_seqs or num_kv_heads above 65535)", who);
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens)
+      return fail(PKV_EINVAL, "%s: null pointer argument", who);
+    return hip_status(launch_chunk_attn(a), who);
+  }
   pkv_status st = prepare_attn(a, who, workspace, workspace_bytes, true);
   if (st != PKV_OK || num_seqs == 0) return st;
   st = hip_status(launch_paged_attn_partition(a), who);

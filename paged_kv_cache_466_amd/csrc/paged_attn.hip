@@ -1694,6 +1694,339 @@ int launch_prefix_attn(const void* query, int q_dtype, const void* k_cache, cons
 }
 
 // ===========================================================================
+// Query-tile pass: many query tokens of one sequence (a chunk of prefill)
+//
+// With T new tokens per sequence whose keys and values are already in the
+// cache at positions L - T .. L - 1, token t attends to positions
+// 0 .. L - T + t (the causal reading of several new tokens; the pages stop
+// at one token per step).  For one (sequence, KV head) the T * G query rows
+// (row r is token r / G, head r % G of the group) against the sequence's
+// blocks are a dense product, Q [T G, D] x K^T [D, L], followed by P.V: the
+// matrix cores' work, with every K/V block loaded once per 32 rows instead
+// of once per 16 columns of the one-token decode.
+//
+// A workgroup of four waves takes 32 rows (two 16-row column groups) of one
+// (sequence, KV head) and the blocks some row of the tile can see; each wave
+// takes a quarter of those blocks.  Per block a wave computes S^T = K Q^T
+// for both column groups from one K tile in registers (v_mfma_f32_16x16x32)
+// and out^T += V^T P^T for both from one transposed read of the V tile
+// (v_mfma_f32_16x16x16).  Blocks reaching past the tile's first row's limit
+// are masked per row.  The four online-softmax states are combined pairwise
+// in LDS by log-sum-exp and the normalised rows leave as whole-line stores.
+// ===========================================================================
+constexpr int kChunkWaves = 4;
+constexpr int kChunkCG = 2;                 // 16-row column groups per wave
+constexpr int kChunkRows = 16 * kChunkCG;   // rows of a workgroup
+constexpr int kChunkTable = 1024;           // table entries staged in LDS at a time
+
+template <int D>
+__host__ __device__ constexpr int chunk_lds_bytes() {
+  // V staging per wave, the staged table, two waves' states (the combine is
+  // pairwise), which also hold the output rows at the end
+  return kChunkWaves * kBS * (2 * D + 16) + kChunkTable * 4 + 2 * kChunkRows * (D + 4) * 4;
+}
+
+struct ChunkParams {
+  void* out;              // [S][T][Hq][D]
+  const void* query;      // [S][T][Hq][D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  int mbs, num_seqs, qtok, num_q_heads, num_kv_heads, num_blocks;
+  float scale_log2;
+};
+
+template <typename QT, int D>
+__global__ __launch_bounds__(64 * kChunkWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void chunk_attn_kernel(ChunkParams p) {
+  typedef Mfma<QT> M;
+  constexpr int NC = D / 32, NN = D / 16;
+  constexpr int ROW_BYTES = 2 * D;
+  constexpr int LANES_PER_ROW = ROW_BYTES / 16;
+  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+  constexpr int VCH = kBS / ROWS_PER_PASS;
+  constexpr int VROW = 2 * D + 16;   // LDS bytes per staged V row (padded)
+  constexpr int DEPTH = D > 64 ? 3 : 4;   // register tiles in the ring
+  constexpr float kSlack = 8.0f;     // rescale only when a score passes the max by 2^8
+  constexpr int RS = D + 4;          // floats per state row in LDS
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kvh = blockIdx.y, s = blockIdx.z;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int T = p.qtok;
+  const int nrows = T * G;
+  const int r0 = blockIdx.x * kChunkRows;
+  const int g = lane & 15;    // column of S^T / out^T
+  const int kg = lane >> 4;   // lane group: k-chunk of the operands, 4-row slab of the outputs
+  uint8_t* vst = lds + wave * kBS * VROW;
+  int* tab = reinterpret_cast<int*>(lds + kChunkWaves * kBS * VROW);
+  float* states = reinterpret_cast<float*>(tab + kChunkTable);
+  // query / output element offset of row r
+  auto qrow = [&](int r) {
+    const int t = r / G;
+    return (((size_t)s * T + t) * p.num_q_heads + kvh * G + (r - t * G)) * D;
+  };
+
+  int L = p.seq_lens[s];
+  L = L < 0 ? 0 : (L > p.mbs * kBS ? p.mbs * kBS : L);
+  // token t sees positions 0 .. L - T + t; the tile's rows see up to lim_hi,
+  // all of them up to lim_lo
+  const int lim_lo = L - T + r0 / G;
+  const int lim_hi = L - T + min(r0 + kChunkRows - 1, nrows - 1) / G;
+  const int nvis = lim_hi < 0 ? 0 : min((L + kBS - 1) / kBS, lim_hi / kBS + 1);
+
+  // the B operands: column g of group cg is row r0 + 16 cg + g (zeros past the last row)
+  typename M::vec8 qop[kChunkCG][NC];
+  int lim[kChunkCG];
+#pragma unroll
+  for (int cg = 0; cg < kChunkCG; ++cg) {
+    const int r = r0 + 16 * cg + g;
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p.query) + qrow(r < nrows ? r : 0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 v = r < nrows ? *reinterpret_cast<const uint4*>(q + 32 * c + 8 * kg) : make_uint4(0, 0, 0, 0);
+      qop[cg][c] = __builtin_bit_cast(typename M::vec8, v);
+    }
+    lim[cg] = L - T + (r < nrows ? r : nrows - 1) / G;
+  }
+  float m2[kChunkCG], lsum[kChunkCG];
+  floatx4 acc[kChunkCG][NN];
+#pragma unroll
+  for (int cg = 0; cg < kChunkCG; ++cg) {
+    m2[cg] = -INFINITY;
+    lsum[cg] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) acc[cg][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int row_stride = p.num_kv_heads * ROW_BYTES;   // bytes between token rows
+  const int tile_bytes = (kBS - 1) * row_stride + ROW_BYTES;
+  const uint8_t* k_head = reinterpret_cast<const uint8_t*>(p.k_cache) + (size_t)kvh * ROW_BYTES;
+  const uint8_t* v_head = reinterpret_cast<const uint8_t*>(p.v_cache) + (size_t)kvh * ROW_BYTES;
+  // K: lane (row g, group kg) reads elements 32c + 8kg .. +7 of its row, the
+  // A operand of MFMA c; V: whole rows, LANES_PER_ROW lanes per row
+  const int k_off = g * row_stride + 16 * kg;
+  int v_off[VCH], v_row[VCH];
+#pragma unroll
+  for (int ps = 0; ps < VCH; ++ps) {
+    v_row[ps] = ps * ROWS_PER_PASS + lane / LANES_PER_ROW;
+    v_off[ps] = v_row[ps] * row_stride + (lane % LANES_PER_ROW) * 16;
+  }
+
+  struct Tile {
+    uint4 k[NC];
+    uint4 v[VCH];
+  };
+  // block j of the chunk staged at tab (logical block c0 + j); j >= end reads
+  // nothing (zero-size resource).  V rows at or past L read as zeros: the
+  // unwritten slots of the last block may hold anything, and a zero weight
+  // times a NaN would still poison the product.
+  auto load_tile = [&](Tile& t, int j, int end, int c0) {
+    const bool valid = j < end;
+    const int pb = __builtin_amdgcn_readfirstlane(tab[valid ? j : 0]);
+    const size_t tile = (size_t)pb * kBS * row_stride;
+    const int nbytes = valid ? tile_bytes : 0;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_head + tile, nbytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_head + tile, nbytes);
+    const int t0 = (c0 + j) * kBS;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) t.k[c] = buf_load16(kr, k_off + 64 * c);
+#pragma unroll
+    for (int ps = 0; ps < VCH; ++ps) t.v[ps] = buf_load16(vr, t0 + v_row[ps] < L ? v_off[ps] : kOutOfRange);
+  };
+
+  auto process = [&](const Tile& t, int t0) {
+#pragma unroll
+    for (int ps = 0; ps < VCH; ++ps)
+      *reinterpret_cast<uint4*>(vst + v_row[ps] * VROW + (lane % LANES_PER_ROW) * 16) = t.v[ps];
+    // some position of the block lies past some row's limit
+    const bool msk = t0 + kBS - 1 > lim_lo;
+    shortx4 pop[kChunkCG];
+#pragma unroll
+    for (int cg = 0; cg < kChunkCG; ++cg) {
+      floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::vec8, t.k[c]), qop[cg][c], sacc);
+      // lane holds tokens 4 kg + i of the block for column g
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * p.scale_log2;
+      if (msk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 4 * kg + i > lim[cg]) sc[i] = -INFINITY;
+      }
+      const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      // a row that has seen no visible position yet and sees none here keeps
+      // alpha = 1 and weights 0 (exp2(-inf - -inf) would be NaN)
+      if (__ballot(lm > m2[cg] + kSlack)) {
+        float bmax = fmaxf(lm, __shfl_xor(lm, 16, 64));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        const float mnew = fmaxf(m2[cg], bmax);
+        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2[cg] - mnew);
+        lsum[cg] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) acc[cg][n] *= alpha;
+        m2[cg] = mnew;
+      }
+      const float mb = (msk & (m2[cg] == -INFINITY)) ? 0.f : m2[cg];
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - mb);
+      const uint32_t p01 = M::pack2(pr[0], pr[1]);
+      const uint32_t p23 = M::pack2(pr[2], pr[3]);
+      // the denominator sums the 16-bit weights the MFMA uses
+      lsum[cg] += M::sum2(p01) + M::sum2(p23);
+      pop[cg] = __builtin_bit_cast(shortx4, make_uint2(p01, p23));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane i of each 16-lane group reads row 4kg + i/4, columns 4(i%4)..+3
+    const uint8_t* rd = vst + (4 * kg + (g >> 2)) * VROW + (g & 3) * 8;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) {
+      const shortx4 vt = M::tr_read(rd + n * 32);
+#pragma unroll
+      for (int cg = 0; cg < kChunkCG; ++cg) acc[cg][n] = M::pv(vt, pop[cg], acc[cg][n]);
+    }
+  };
+
+  for (int c0 = 0; c0 < nvis; c0 += kChunkTable) {
+    const int cn = min(kChunkTable, nvis - c0);
+    __syncthreads();   // the previous chunk's entries are no longer read
+    const int32_t* row = p.block_tables + (size_t)s * p.mbs + c0;
+    for (int i = threadIdx.x; i < cn; i += 64 * kChunkWaves) {
+      const int pb = row[i];
+      tab[i] = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the caches
+    }
+    __syncthreads();
+    // this wave's blocks: entries [j0, j1) of the chunk
+    const int j0 = wave * cn / kChunkWaves, j1 = (wave + 1) * cn / kChunkWaves;
+    const int n = j1 - j0;
+    Tile ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], j0 + d, j1, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int k0 = 0; k0 < n; k0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int k = k0 + d;
+        if (k < n) process(ring[d], (c0 + j0 + k) * kBS);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(ring[d], j0 + k + DEPTH, j1, c0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- combine the four waves' states: (2, 3) into (0, 1), then 1 into 0 --
+  float l[kChunkCG];
+#pragma unroll
+  for (int cg = 0; cg < kChunkCG; ++cg) {
+    l[cg] = lsum[cg] + __shfl_xor(lsum[cg], 16, 64);
+    l[cg] += __shfl_xor(l[cg], 32, 64);
+  }
+  // state slot `slot`: rows [32][RS], row = 16 cg + g: acc, then m at D, l at D + 1
+  auto put = [&](int slot) {
+#pragma unroll
+    for (int cg = 0; cg < kChunkCG; ++cg) {
+      float* st = states + (size_t)(slot * kChunkRows + 16 * cg + g) * RS;
+#pragma unroll
+      for (int n = 0; n < NN; ++n) *reinterpret_cast<floatx4*>(st + 16 * n + 4 * kg) = acc[cg][n];
+      if (kg == 0) {
+        st[D] = m2[cg];
+        st[D + 1] = l[cg];
+      }
+    }
+  };
+  auto take = [&](int slot) {
+#pragma unroll
+    for (int cg = 0; cg < kChunkCG; ++cg) {
+      const float* st = states + (size_t)(slot * kChunkRows + 16 * cg + g) * RS;
+      const float mo = st[D], lo = st[D + 1];
+      const float mn = fmaxf(m2[cg], mo);
+      // an empty state (m = -inf) weighs nothing
+      const float wa = m2[cg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2[cg] - mn);
+      const float wb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+#pragma unroll
+      for (int n = 0; n < NN; ++n)
+        acc[cg][n] = acc[cg][n] * wa + *reinterpret_cast<const floatx4*>(st + 16 * n + 4 * kg) * wb;
+      l[cg] = l[cg] * wa + lo * wb;
+      m2[cg] = mn;
+    }
+  };
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) take(wave);
+  __syncthreads();
+  if (wave == 1) put(0);
+  __syncthreads();
+  if (wave == 0) {
+    take(0);
+    // normalised rows -> LDS (slot 0, row-major), then whole-line stores
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int cg = 0; cg < kChunkCG; ++cg) {
+      const float inv = l[cg] > 0.f ? 1.f / l[cg] : 0.f;
+      float* st = states + (size_t)(16 * cg + g) * RS;
+#pragma unroll
+      for (int n = 0; n < NN; ++n) *reinterpret_cast<floatx4*>(st + 16 * n + 4 * kg) = acc[cg][n] * inv;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int CPR = D / 8;   // 16-byte pieces of an output row
+    const int rows = min(kChunkRows, nrows - r0);
+    for (int c = lane; c < rows * CPR; c += 64) {
+      const float* src = states + (size_t)(c / CPR) * RS + (c % CPR) * 8;
+      const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
+      const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + qrow(r0 + c / CPR) + (c % CPR) * 8) =
+          make_uint4(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]), M::pack2(hi[0], hi[1]), M::pack2(hi[2], hi[3]));
+    }
+  }
+}
+
+template <typename QT, int D>
+static int launch_chunk_d(const ChunkParams& p, hipStream_t st) {
+  auto kernel = chunk_attn_kernel<QT, D>;
+  static std::atomic<bool> lds_set[64];
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kernel), chunk_lds_bytes<D>(), lds_set);
+  if (e != hipSuccess) return e;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const dim3 grid((p.qtok * G + kChunkRows - 1) / kChunkRows, p.num_kv_heads, p.num_seqs);
+  kernel<<<grid, 64 * kChunkWaves, chunk_lds_bytes<D>(), st>>>(p);
+  return hipGetLastError();
+}
+
+int launch_chunk_attn(const AttnArgs& a) {
+  if (a.num_seqs == 0) return hipSuccess;
+  ChunkParams p;
+  p.out = a.out;
+  p.query = a.query;
+  p.k_cache = a.k_cache;
+  p.v_cache = a.v_cache;
+  p.block_tables = a.block_tables;
+  p.seq_lens = a.seq_lens;
+  p.mbs = a.max_blocks_per_seq;
+  p.num_seqs = a.num_seqs;
+  p.qtok = a.qtok;
+  p.num_q_heads = a.num_q_heads;
+  p.num_kv_heads = a.num_kv_heads;
+  p.num_blocks = a.num_blocks;
+  p.scale_log2 = a.sm_scale * kLog2e;
+  hipStream_t st = (hipStream_t)a.stream;
+  if (a.q_dtype == PKV_BF16) return a.head_dim == 64 ? launch_chunk_d<BF16, 64>(p, st) : launch_chunk_d<BF16, 128>(p, st);
+  return a.head_dim == 64 ? launch_chunk_d<F16, 64>(p, st) : launch_chunk_d<F16, 128>(p, st);
+}
+
+// ===========================================================================
 // launchers
 // ===========================================================================
 static AttnParams make_params(const AttnArgs& a) {

@@ -141,6 +141,9 @@ size_t workspace_total(int kv_dtype, int num_seqs, int num_q_heads, int num_kv_h
 // arguments and return a hipError_t cast to int.
 int launch_paged_attn_partition(const AttnArgs& a);
 int launch_paged_attn_merge(const AttnArgs& a);
+// Several query tokens per sequence with more than 16 query rows per KV head
+// (a chunk of prefill): the query-tile pass, written straight to `out`.
+int launch_chunk_attn(const AttnArgs& a);
 // Shared-prefix pass: one record per (sequence, query head) of attention
 // over the prefix_blocks blocks listed at `table`.
 int launch_prefix_attn(const void* query, int q_dtype, const void* k_cache, const void* v_cache,

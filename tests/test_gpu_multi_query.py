@@ -123,6 +123,31 @@ def check_multi(run, name, T, psize):
     assert err <= TOL, err
 
 
+# More than 16 query rows per KV head (T * G > 16): the query-tile pass of a
+# prefill chunk.  Lengths include sequences shorter than T (rows that see
+# nothing get zeros) and just above it, and one case spans more than one
+# staged chunk of 1024 table entries.
+CHUNK_CASES = {
+    "llama_shape": CASES["llama_shape"],
+    "short_rows": ("llama3_8b_b64", dict(S=5, fixed_lens=(2, 20, 37, 63, 64))),
+    "g8_f16": CASES["g8_f16"],
+    "d64_g8": CASES["d64_g8"],
+    "long": ("llama3_8b_b64", dict(S=2, fixed_lens=(16450, 300))),
+}
+CHUNK = [("llama_shape", T) for T in (5, 8, 16, 33, 64)] + [("short_rows", T) for T in (17, 40)] + \
+        [("g8_f16", T) for T in (3, 8, 40)] + [("d64_g8", 17), ("long", 20)]
+
+
+@pytest.mark.parametrize("name,T", CHUNK)
+def test_multi_query_chunk_parity(name, T):
+    """T * G > 16 rows per KV head: within 2e-2 of the oracle's causal
+    multi_query_decode, zeros for tokens that see no position."""
+    key = ("chunk", name)
+    if key not in _runs:
+        _runs[key] = make_run(*CHUNK_CASES[name])
+    check_multi(_runs[key], name, T, 0)
+
+
 def test_one_token_is_the_decode():
     """T = 1 gives bit for bit the output of pkv_paged_attn_decode."""
     import paged_kv_cache_466_amd as pkv
@@ -136,10 +161,12 @@ def test_one_token_is_the_decode():
     assert torch.equal(out[:, 0].view(torch.int16), ref.view(torch.int16))
 
 
-def test_too_many_columns_is_refused():
+def test_code_cache_chunk_is_refused():
+    """The query-tile pass is built for 16-bit caches: more than 16 rows per
+    KV head over an INT8 cache is refused."""
     import paged_kv_cache_466_amd as pkv
-    w, t, g, o = run_case("g8_f16")           # G = 8: at most 2 tokens
-    q = torch.zeros((w.S, 3, w.Hq, w.D), dtype=torch.float16, device="cuda")
-    with pytest.raises(pkv.PkvError, match="16"):
+    w, t, g, o = run_case("i8")               # G = 4: at most 4 tokens on codes
+    q = torch.zeros((w.S, 5, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(pkv.PkvError, match="16-bit caches"):
         pkv.paged_attn_decode_multi(torch.empty_like(q), q, g.k_cache, g.v_cache, g.block_tables, g.lens,
-                                    w.sm_scale)
+                                    w.sm_scale, g.k_scales, g.v_scales)
