@@ -407,8 +407,11 @@ extern "C" pkv_status pkv_paged_attn_decode_multi(
     if (partition_size < 0 || (partition_size > 0 && partition_size % block_size))
       return fail(PKV_EINVAL, "%s: partition_size must be 0 or a positive multiple of block_size", who);
     if (flags & ~(unsigned)PKV_DECODE_STREAM_KV) return fail(PKV_EINVAL, "%s: unknown flags 0x%x", who, flags);
-    if (num_seqs > 65535 || num_kv_heads > 65535 || (long long)num_query_tokens * num_q_heads >= (1LL << 24))
-      return fail(PKV_EUNSUPPORTED, "%s: grid too large (num_seqs or num_kv_heads above 65535)", who);
+    // one workgroup per 32 query rows of each (sequence, KV head), the pairs
+    // padded to a multiple of 8
+    const long long tiles = ((long long)num_query_tokens * (num_q_heads / num_kv_heads) + 31) / 32;
+    if (((long long)num_seqs * num_kv_heads + 7) / 8 * 8 * tiles >= (1LL << 31))
+      return fail(PKV_EUNSUPPORTED, "%s: grid too large (2^31 workgroups or more)", who);
     if (num_seqs == 0) return PKV_OK;
     if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens)
       return fail(PKV_EINVAL, "%s: null pointer argument", who);

@@ -143,11 +143,16 @@ template <> struct Mfma<BF16> {
   __device__ static floatx4 pv(const shortx4& a, const shortx4& b, const floatx4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
   }
+  // two values rounded to nearest even, packed (one v_cvt_pk_bf16_f32)
   __device__ static uint32_t pack2(float x, float y) {
-    return (uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(y) << 16);
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){x, y}, b2));
   }
-  // sum of the two packed values
-  __device__ static float sum2(uint32_t w) { return __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u); }
+  // c plus the two packed values (one v_dot2_f32_bf16 against (1, 1))
+  __device__ static float acc2(uint32_t w, float c) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), (b2){(__bf16)1.0f, (__bf16)1.0f}, c, false);
+  }
   // two FP8-E4M3 codes (byte pair `hi` of w) -> two values, exactly
   template <bool HI> __device__ static uint32_t fp8x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
@@ -172,9 +177,13 @@ template <> struct Mfma<F16> {
                                                  0, 0);
   }
   __device__ static uint32_t pack2(float x, float y) {
-    return (uint32_t)f32_to_f16(x) | ((uint32_t)f32_to_f16(y) << 16);
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){x, y}, h2));
   }
-  __device__ static float sum2(uint32_t w) { return f16_to_f32(w & 0xFFFFu) + f16_to_f32(w >> 16); }
+  __device__ static float acc2(uint32_t w, float c) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), (h2){(_Float16)1.0f, (_Float16)1.0f}, c, false);
+  }
   template <bool HI> __device__ static uint32_t fp8x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
@@ -1012,7 +1021,7 @@ void paged_attn_wave_kernel(AttnParams p) {
     const uint32_t p23 = M::pack2(pr[2] * vsc[2], pr[3] * vsc[3]);
     // the denominator sums the weights the MFMA uses (16-bit rounded), so
     // they add up to one; with codes the V scale is not part of the weight
-    if constexpr (!kCodes) lsum += M::sum2(p01) + M::sum2(p23);
+    if constexpr (!kCodes) lsum = M::acc2(p23, M::acc2(p01, lsum));
     else lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const shortx4 pop = __builtin_bit_cast(shortx4, make_uint2(p01, p23));
 
@@ -1217,7 +1226,9 @@ __global__ __launch_bounds__(256) void paged_attn_simple_kernel(AttnParams p) {
 // one record sit next to each other, so a workgroup reads whole record rows.
 // Its 256 threads take (column, 16-byte piece of the row) outputs; when
 // those are fewer than 256, the records are shared out among `parts` thread
-// groups whose partial sums meet in LDS.  cpw is chosen on the host so that
+// groups whose partial sums meet in LDS.  Each thread folds its records in
+// one pass with a running max, so that all its record loads are issued
+// together right after the plan entry's.  cpw is chosen on the host so that
 // the grid has about a thousand workgroups: most of a workgroup's time is
 // the latency of a few dependent loads, hidden by having many in flight.
 // ===========================================================================
@@ -1228,7 +1239,6 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
                                                                const float* srec) {
   constexpr int V4 = D / 4;   // 16-byte pieces of an output row
   __shared__ float red[256];
-  __shared__ float mcol[16];
   __shared__ floatx4 pnum[256];
   __shared__ float pden[256];
   const int s = blockIdx.x, kvh = blockIdx.y, col0 = blockIdx.z * cpw;
@@ -1252,25 +1262,9 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
   // the prefix record of column c (a shared prefix goes with one query token)
   auto pre_of = [&](int c) { return prefix + ((size_t)s * num_q_heads + kvh * G + c) * (D + 4); };
 
-  // 1. M of each column: thread (column tid % 16, records tid / 16 + 16 k)
-  {
-    const int c = tid & 15;
-    float mx = -INFINITY;
-    if (c < ncols)
-      for (int i = tid >> 4; i < np; i += 16) mx = fmaxf(mx, rec_of(i)[NCOL * D + col0 + c]);
-    red[tid] = mx;
-  }
-  __syncthreads();
-  if (tid < 16) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, red[16 * j + tid]);
-    if (prefix && tid < ncols) mx = fmaxf(mx, pre_of(col0 + tid)[D]);
-    mcol[tid] = mx;
-  }
-  __syncthreads();
-
-  // 2. thread (output o, part): records part, part + parts, ...
+  // thread (output o, part): records part, part + parts, ..., combined in one
+  // pass with a running max (one round of loads after the plan entry); the
+  // parts then meet in LDS
   const int outs = cpw * V4;          // <= 256 (cpw <= 256 / V4, checked on the host)
   const int parts = 256 / outs;
   const int o = tid % outs, part = tid / outs;
@@ -1278,9 +1272,18 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
   const bool act = part < parts && c < ncols;
   const int col = col0 + c;
   floatx4 num = floatx4{0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  const float M = act ? mcol[c] : -INFINITY;
-  if (act && M != -INFINITY) {
+  float den = 0.f, mrun = -INFINITY;
+  // folds a term (m, l, acc) into (mrun, den, num); a term with m = -inf
+  // (an empty piece) weighs nothing
+  auto fold = [&](float mi, float li, const floatx4& a) {
+    const float mn = fmaxf(mrun, mi);
+    const float keep = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
+    const float w = mi == -INFINITY ? 0.f : exp2f(mi - mn);
+    num = num * keep + w * a;
+    den = den * keep + w * li;
+    mrun = mn;
+  };
+  if (act) {
     constexpr int U = 4;   // records in flight per thread
     int i = part;
     for (; i + (U - 1) * parts < np; i += U * parts) {
@@ -1294,36 +1297,26 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
         a[u] = *reinterpret_cast<const floatx4*>(r + col * D + 4 * d4);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = exp2f(mi[u] - M);
-        num += w * a[u];
-        den += w * li[u];
-      }
+      for (int u = 0; u < U; ++u) fold(mi[u], li[u], a[u]);
     }
     for (; i < np; i += parts) {
       const float* r = rec_of(i);
-      const float w = exp2f(r[NCOL * D + col] - M);
-      num += w * *reinterpret_cast<const floatx4*>(r + col * D + 4 * d4);
-      den += w * r[NCOL * D + 16 + col];
+      fold(r[NCOL * D + col], r[NCOL * D + 16 + col], *reinterpret_cast<const floatx4*>(r + col * D + 4 * d4));
     }
   }
   if (parts > 1) {
     pnum[tid] = num;
     pden[tid] = den;
+    red[tid] = mrun;
     __syncthreads();
     if (part == 0) {
-      for (int j = 1; j < parts; ++j) {
-        num += pnum[j * outs + o];
-        den += pden[j * outs + o];
-      }
+      for (int j = 1; j < parts; ++j) fold(red[j * outs + o], pden[j * outs + o], pnum[j * outs + o]);
     }
   }
   if (part == 0 && act) {
     if (prefix) {
       const float* pre = pre_of(col);
-      const float w = exp2f(pre[D] - M);
-      num += w * *reinterpret_cast<const floatx4*>(pre + 4 * d4);
-      den += w * pre[D + 1];
+      fold(pre[D], pre[D + 1], *reinterpret_cast<const floatx4*>(pre + 4 * d4));
     }
     const int t = col / G, h = kvh * G + col % G;
     const size_t oi = (((size_t)s * qtok + t) * num_q_heads + h) * D + 4 * d4;
@@ -1571,7 +1564,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixPa
       const uint32_t p01 = M::pack2(pr[0], pr[1]);
       const uint32_t p23 = M::pack2(pr[2], pr[3]);
       // the denominator sums the 16-bit weights the MFMA uses
-      lsum[cg] += M::sum2(p01) + M::sum2(p23);
+      lsum[cg] = M::acc2(p23, M::acc2(p01, lsum[cg]));
       pop[cg] = __builtin_bit_cast(shortx4, make_uint2(p01, p23));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1702,29 +1695,35 @@ int launch_prefix_attn(const void* query, int q_dtype, const void* k_cache, cons
 // at one token per step).  For one (sequence, KV head) the T * G query rows
 // (row r is token r / G, head r % G of the group) against the sequence's
 // blocks are a dense product, Q [T G, D] x K^T [D, L], followed by P.V: the
-// matrix cores' work, with every K/V block loaded once per 32 rows instead
-// of once per 16 columns of the one-token decode.
+// matrix cores' work.
 //
-// A workgroup of four waves takes 32 rows (two 16-row column groups) of one
-// (sequence, KV head) and the blocks some row of the tile can see; each wave
-// takes a quarter of those blocks.  Per block a wave computes S^T = K Q^T
-// for both column groups from one K tile in registers (v_mfma_f32_16x16x32)
-// and out^T += V^T P^T for both from one transposed read of the V tile
-// (v_mfma_f32_16x16x16).  Blocks reaching past the tile's first row's limit
-// are masked per row.  The four online-softmax states are combined pairwise
-// in LDS by log-sum-exp and the normalised rows leave as whole-line stores.
+// A workgroup of NW waves takes 32 * NW rows of one (sequence, KV head); each
+// wave owns 32 of them (two 16-row column groups) outright.  The workgroup
+// walks the blocks some row of the tile can see through a ring of NBUF block
+// slots in LDS: each block's K and V tiles are loaded once for all waves,
+// straight from memory into LDS (buffer loads with the LDS destination),
+// each wave fetching its share of the tile's 1 KB pieces.  A tile's 16-byte
+// chunk c of row r sits at position c ^ (r mod chunks-per-row) of its LDS
+// row, so that the key reads of the q.K operand (16 rows, one chunk) and the
+// transposing reads of V (4 rows, 32 bytes each, per 16 lanes) spread over
+// the banks.  V rows at or past L load with an out-of-range offset, which
+// writes zeros: the unwritten slots of a last block may hold anything.
+// Per block a wave computes S^T = K Q^T for both column groups
+// (v_mfma_f32_16x16x32, the key operand read from LDS) and out^T += V^T P^T
+// for both from one transposed read of V (v_mfma_f32_16x16x16), with a
+// causal limit per row in the blocks past its first row's.  One barrier per
+// block: after it, the block is complete in LDS and every wave is done with
+// the slot the next load overwrites.  Rows leave normalised, staged through
+// LDS as whole-line stores.
 // ===========================================================================
-constexpr int kChunkWaves = 4;
+// s_waitcnt immediate: vmcnt(n) (bits 3:0 and 15:14), lgkmcnt(0), expcnt left alone
+constexpr int waitcnt_vmcnt(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | 0x0070; }
+
 constexpr int kChunkCG = 2;                 // 16-row column groups per wave
-constexpr int kChunkRows = 16 * kChunkCG;   // rows of a workgroup
+constexpr int kChunkWaveRows = 16 * kChunkCG;
+constexpr int kChunkNBuf = 6;               // block slots in the LDS ring (three pairs)
 constexpr int kChunkTable = 1024;           // table entries staged in LDS at a time
 
-template <int D>
-__host__ __device__ constexpr int chunk_lds_bytes() {
-  // V staging per wave, the staged table, two waves' states (the combine is
-  // pairwise), which also hold the output rows at the end
-  return kChunkWaves * kBS * (2 * D + 16) + kChunkTable * 4 + 2 * kChunkRows * (D + 4) * 4;
-}
 
 struct ChunkParams {
   void* out;              // [S][T][Hq][D]
@@ -1737,33 +1736,51 @@ struct ChunkParams {
   float scale_log2;
 };
 
-template <typename QT, int D>
-__global__ __launch_bounds__(64 * kChunkWaves) __attribute__((amdgpu_waves_per_eu(2)))
-void chunk_attn_kernel(ChunkParams p) {
+template <typename QT, int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void chunk_attn_kernel(ChunkParams p) {
   typedef Mfma<QT> M;
   constexpr int NC = D / 32, NN = D / 16;
-  constexpr int ROW_BYTES = 2 * D;
-  constexpr int LANES_PER_ROW = ROW_BYTES / 16;
-  constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
-  constexpr int VCH = kBS / ROWS_PER_PASS;
-  constexpr int VROW = 2 * D + 16;   // LDS bytes per staged V row (padded)
-  constexpr int DEPTH = D > 64 ? 3 : 4;   // register tiles in the ring
-  constexpr float kSlack = 8.0f;     // rescale only when a score passes the max by 2^8
-  constexpr int RS = D + 4;          // floats per state row in LDS
+  constexpr int ROWB = 2 * D;              // bytes of one token row of one head
+  constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+  constexpr int TILE = kBS * ROWB;         // one K or V tile
+  constexpr int SLOT = 2 * TILE;
+  constexpr int PIECES = 2 * TILE / 1024;  // 1 KB pieces (one wave-wide load each) of a block
+  static_assert(PIECES % NW == 0, "every wave loads the same number of pieces");
+  constexpr int LPW = PIECES / NW;         // loads per wave per block
+  constexpr int RPP = 1024 / ROWB;         // rows per piece
+  constexpr float kSlack = 8.0f;           // rescale only when a score passes the max by 2^8
+  constexpr int RS = D + 4;                // floats per staged output row
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  // The ring's slots are separate LDS objects, and the block loop is unrolled
+  // so that each step names the slot it reads and the slot it loads into:
+  // the compiler then knows that the reads do not touch what the loads in
+  // flight write, and waits for the loads only where this code does.
+  static_assert(kChunkNBuf == 6, "six ring slots");
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[SLOT], ring1[SLOT], ring2[SLOT], ring3[SLOT], ring4[SLOT],
+      ring5[SLOT];
+  __shared__ int tab[kChunkTable];
+  auto ring = [&](int i) -> uint8_t* {
+    return i == 0 ? ring0 : i == 1 ? ring1 : i == 2 ? ring2 : i == 3 ? ring3 : i == 4 ? ring4 : ring5;
+  };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kvh = blockIdx.y, s = blockIdx.z;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int T = p.qtok;
   const int nrows = T * G;
-  const int r0 = blockIdx.x * kChunkRows;
+  // Workgroup n runs on XCD n % 8.  The row tiles of one (sequence, KV
+  // head) read the same blocks, so they all go to one XCD, whose L2 then
+  // serves the tiles after the first: pair xcd + 8 (j / R), tile j % R for
+  // the j-th workgroup of XCD xcd (R tiles per pair; the grid is padded to
+  // whole groups of 8 pairs).
+  const int R = (nrows + 32 * NW - 1) / (32 * NW);
+  const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+  const int pair = xcd + 8 * (jw / R);
+  if (pair >= p.num_seqs * p.num_kv_heads) return;
+  const int s = pair / p.num_kv_heads, kvh = pair % p.num_kv_heads;
+  const int r0 = (jw % R) * 32 * NW;          // the workgroup's first row
+  const int w0 = r0 + wave * kChunkWaveRows;  // this wave's first row
   const int g = lane & 15;    // column of S^T / out^T
   const int kg = lane >> 4;   // lane group: k-chunk of the operands, 4-row slab of the outputs
-  uint8_t* vst = lds + wave * kBS * VROW;
-  int* tab = reinterpret_cast<int*>(lds + kChunkWaves * kBS * VROW);
-  float* states = reinterpret_cast<float*>(tab + kChunkTable);
   // query / output element offset of row r
   auto qrow = [&](int r) {
     const int t = r / G;
@@ -1772,18 +1789,19 @@ void chunk_attn_kernel(ChunkParams p) {
 
   int L = p.seq_lens[s];
   L = L < 0 ? 0 : (L > p.mbs * kBS ? p.mbs * kBS : L);
-  // token t sees positions 0 .. L - T + t; the tile's rows see up to lim_hi,
-  // all of them up to lim_lo
-  const int lim_lo = L - T + r0 / G;
-  const int lim_hi = L - T + min(r0 + kChunkRows - 1, nrows - 1) / G;
+  // token t sees positions 0 .. L - T + t: the workgroup's rows up to
+  // lim_hi, all of this wave's up to wlim_lo
+  const int lim_hi = L - T + min(r0 + 32 * NW - 1, nrows - 1) / G;
+  const int wlim_lo = L - T + min(w0, nrows - 1) / G;
   const int nvis = lim_hi < 0 ? 0 : min((L + kBS - 1) / kBS, lim_hi / kBS + 1);
+  const bool has_rows = w0 < nrows;
 
-  // the B operands: column g of group cg is row r0 + 16 cg + g (zeros past the last row)
+  // the B operands: column g of group cg is row w0 + 16 cg + g (zeros past the last row)
   typename M::vec8 qop[kChunkCG][NC];
   int lim[kChunkCG];
 #pragma unroll
   for (int cg = 0; cg < kChunkCG; ++cg) {
-    const int r = r0 + 16 * cg + g;
+    const int r = w0 + 16 * cg + g;
     const uint16_t* q = reinterpret_cast<const uint16_t*>(p.query) + qrow(r < nrows ? r : 0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -1802,30 +1820,25 @@ void chunk_attn_kernel(ChunkParams p) {
     for (int n = 0; n < NN; ++n) acc[cg][n] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int row_stride = p.num_kv_heads * ROW_BYTES;   // bytes between token rows
-  const int tile_bytes = (kBS - 1) * row_stride + ROW_BYTES;
-  const uint8_t* k_head = reinterpret_cast<const uint8_t*>(p.k_cache) + (size_t)kvh * ROW_BYTES;
-  const uint8_t* v_head = reinterpret_cast<const uint8_t*>(p.v_cache) + (size_t)kvh * ROW_BYTES;
-  // K: lane (row g, group kg) reads elements 32c + 8kg .. +7 of its row, the
-  // A operand of MFMA c; V: whole rows, LANES_PER_ROW lanes per row
-  const int k_off = g * row_stride + 16 * kg;
-  int v_off[VCH], v_row[VCH];
+  const int row_stride = p.num_kv_heads * ROWB;   // bytes between token rows
+  const int tile_bytes = (kBS - 1) * row_stride + ROWB;
+  const uint8_t* k_head = reinterpret_cast<const uint8_t*>(p.k_cache) + (size_t)kvh * ROWB;
+  const uint8_t* v_head = reinterpret_cast<const uint8_t*>(p.v_cache) + (size_t)kvh * ROWB;
+  // this lane's chunk of each piece it loads: LDS chunk q = 64 * piece + lane
+  // of the tile is row q / CPR, position q % CPR, which holds the row's chunk
+  // (q % CPR) ^ (row % CPR)
+  int ld_row[LPW], ld_off[LPW];
 #pragma unroll
-  for (int ps = 0; ps < VCH; ++ps) {
-    v_row[ps] = ps * ROWS_PER_PASS + lane / LANES_PER_ROW;
-    v_off[ps] = v_row[ps] * row_stride + (lane % LANES_PER_ROW) * 16;
+  for (int u = 0; u < LPW; ++u) {
+    const int piece = (wave * LPW + u) % (PIECES / 2);
+    const int q = 64 * piece + lane;
+    ld_row[u] = q / CPR;
+    ld_off[u] = ld_row[u] * row_stride + (((q % CPR) ^ (ld_row[u] % CPR)) * 16);
   }
-
-  struct Tile {
-    uint4 k[NC];
-    uint4 v[VCH];
-  };
-  // block j of the chunk staged at tab (logical block c0 + j); j >= end reads
-  // nothing (zero-size resource).  V rows at or past L read as zeros: the
-  // unwritten slots of the last block may hold anything, and a zero weight
-  // times a NaN would still poison the product.
-  auto load_tile = [&](Tile& t, int j, int end, int c0) {
-    const bool valid = j < end;
+  // block j of the staged table chunk (logical block c0 + j) into slot
+  // `slot`; j >= cn loads nothing (zero-size resource)
+  auto issue = [&](uint8_t* slot, int j, int cn, int c0) {
+    const bool valid = j < cn;
     const int pb = __builtin_amdgcn_readfirstlane(tab[valid ? j : 0]);
     const size_t tile = (size_t)pb * kBS * row_stride;
     const int nbytes = valid ? tile_bytes : 0;
@@ -1833,37 +1846,74 @@ void chunk_attn_kernel(ChunkParams p) {
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_head + tile, nbytes);
     const int t0 = (c0 + j) * kBS;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) t.k[c] = buf_load16(kr, k_off + 64 * c);
-#pragma unroll
-    for (int ps = 0; ps < VCH; ++ps) t.v[ps] = buf_load16(vr, t0 + v_row[ps] < L ? v_off[ps] : kOutOfRange);
+    for (int u = 0; u < LPW; ++u) {
+      const int pc = wave * LPW + u;            // piece of the block: K pieces, then V pieces
+      const bool isv = pc >= PIECES / 2;
+      const int piece = isv ? pc - PIECES / 2 : pc;
+      uint8_t* dst = slot + (isv ? TILE : 0) + piece * 1024;
+      const int off = isv && t0 + ld_row[u] >= L ? kOutOfRange : ld_off[u];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vr : kr, (__attribute__((address_space(3))) void*)dst, 16, off,
+                                               0, 0, 0);
+    }
   };
 
-  auto process = [&](const Tile& t, int t0) {
+  // per-lane LDS offsets of the operand reads (swizzled chunk positions)
+  int k_rd[NC];
 #pragma unroll
-    for (int ps = 0; ps < VCH; ++ps)
-      *reinterpret_cast<uint4*>(vst + v_row[ps] * VROW + (lane % LANES_PER_ROW) * 16) = t.v[ps];
-    // some position of the block lies past some row's limit
-    const bool msk = t0 + kBS - 1 > lim_lo;
-    shortx4 pop[kChunkCG];
+  for (int c = 0; c < NC; ++c) k_rd[c] = g * ROWB + (((4 * c + kg) ^ (g % CPR)) * 16);
+  const int vr_row = 4 * kg + (g >> 2);
+  int v_rd[NN];
+#pragma unroll
+  for (int n = 0; n < NN; ++n)
+    v_rd[n] = TILE + vr_row * ROWB + (((2 * n + ((g & 3) >> 1)) ^ (vr_row % CPR)) * 16) + (g & 1) * 8;
+
+  // Two blocks a, b (tokens t0 .. t0 + 31) per step: one softmax update per
+  // 32 tokens, and P.V over both blocks as one v_mfma_f32_16x16x32 per 16
+  // channels.  Its k index 8 kg + i is token 4 kg + i of block a for i < 4
+  // and of block b for i >= 4: the score tiles of a and b give P^T in that
+  // order, and the transposed reads of a's and b's V give V^T in it.
+  auto process2 = [&](const uint8_t* sa, const uint8_t* sb, int t0) {
+    // some position of a block lies past some of this wave's rows' limits
+    const bool msk_a = t0 + kBS - 1 > wlim_lo, msk_b = t0 + 2 * kBS - 1 > wlim_lo;
+    floatx4 sacc[2][kChunkCG];
+#pragma unroll
+    for (int cg = 0; cg < kChunkCG; ++cg) sacc[0][cg] = sacc[1][cg] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 ka = *reinterpret_cast<const uint4*>(sa + k_rd[c]);
+      const uint4 kb = *reinterpret_cast<const uint4*>(sb + k_rd[c]);
+#pragma unroll
+      for (int cg = 0; cg < kChunkCG; ++cg) {
+        sacc[0][cg] = M::qk(__builtin_bit_cast(typename M::vec8, ka), qop[cg][c], sacc[0][cg]);
+        sacc[1][cg] = M::qk(__builtin_bit_cast(typename M::vec8, kb), qop[cg][c], sacc[1][cg]);
+      }
+    }
+    // lane holds tokens 4 kg + i of each block for column g; raw scores, the
+    // factor is applied inside the exponent (positive, so maxima commute)
+    float lm[kChunkCG];
 #pragma unroll
     for (int cg = 0; cg < kChunkCG; ++cg) {
-      floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) sacc = M::qk(__builtin_bit_cast(typename M::vec8, t.k[c]), qop[cg][c], sacc);
-      // lane holds tokens 4 kg + i of the block for column g
-      float sc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * p.scale_log2;
-      if (msk) {
+      if (msk_a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (t0 + 4 * kg + i > lim[cg]) sc[i] = -INFINITY;
+          if (t0 + 4 * kg + i > lim[cg]) sacc[0][cg][i] = -INFINITY;
       }
-      const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (msk_b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + kBS + 4 * kg + i > lim[cg]) sacc[1][cg][i] = -INFINITY;
+      }
+      const float ma = fmaxf(fmaxf(sacc[0][cg][0], sacc[0][cg][1]), fmaxf(sacc[0][cg][2], sacc[0][cg][3]));
+      const float mbk = fmaxf(fmaxf(sacc[1][cg][0], sacc[1][cg][1]), fmaxf(sacc[1][cg][2], sacc[1][cg][3]));
+      lm[cg] = fmaxf(ma, mbk) * p.scale_log2;
+    }
+    typename M::vec8 pop[kChunkCG];
+#pragma unroll
+    for (int cg = 0; cg < kChunkCG; ++cg) {
       // a row that has seen no visible position yet and sees none here keeps
       // alpha = 1 and weights 0 (exp2(-inf - -inf) would be NaN)
-      if (__ballot(lm > m2[cg] + kSlack)) {
-        float bmax = fmaxf(lm, __shfl_xor(lm, 16, 64));
+      if (__ballot(lm[cg] > m2[cg] + kSlack)) {
+        float bmax = fmaxf(lm[cg], __shfl_xor(lm[cg], 16, 64));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
         const float mnew = fmaxf(m2[cg], bmax);
         const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m2[cg] - mnew);
@@ -1872,137 +1922,126 @@ void chunk_attn_kernel(ChunkParams p) {
         for (int n = 0; n < NN; ++n) acc[cg][n] *= alpha;
         m2[cg] = mnew;
       }
-      const float mb = (msk & (m2[cg] == -INFINITY)) ? 0.f : m2[cg];
-      float pr[4];
+      const float mb = (msk_b & (m2[cg] == -INFINITY)) ? 0.f : m2[cg];
+      float pr[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - mb);
-      const uint32_t p01 = M::pack2(pr[0], pr[1]);
-      const uint32_t p23 = M::pack2(pr[2], pr[3]);
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(fmaf(sacc[0][cg][i], p.scale_log2, -mb));
+        pr[4 + i] = __builtin_amdgcn_exp2f(fmaf(sacc[1][cg][i], p.scale_log2, -mb));
+      }
+      const uint4 pw = make_uint4(M::pack2(pr[0], pr[1]), M::pack2(pr[2], pr[3]), M::pack2(pr[4], pr[5]),
+                                  M::pack2(pr[6], pr[7]));
       // the denominator sums the 16-bit weights the MFMA uses
-      lsum[cg] += M::sum2(p01) + M::sum2(p23);
-      pop[cg] = __builtin_bit_cast(shortx4, make_uint2(p01, p23));
+      lsum[cg] = M::acc2(pw.w, M::acc2(pw.z, M::acc2(pw.y, M::acc2(pw.x, lsum[cg]))));
+      pop[cg] = __builtin_bit_cast(typename M::vec8, pw);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // lane i of each 16-lane group reads row 4kg + i/4, columns 4(i%4)..+3
-    const uint8_t* rd = vst + (4 * kg + (g >> 2)) * VROW + (g & 3) * 8;
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
-      const shortx4 vt = M::tr_read(rd + n * 32);
+      const shortx4 va = M::tr_read(sa + v_rd[n]);
+      const shortx4 vb = M::tr_read(sb + v_rd[n]);
+      const typename M::vec8 vt = __builtin_bit_cast(
+          typename M::vec8, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
+                                       __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
 #pragma unroll
-      for (int cg = 0; cg < kChunkCG; ++cg) acc[cg][n] = M::pv(vt, pop[cg], acc[cg][n]);
+      for (int cg = 0; cg < kChunkCG; ++cg) acc[cg][n] = M::qk(vt, pop[cg], acc[cg][n]);
     }
   };
 
   for (int c0 = 0; c0 < nvis; c0 += kChunkTable) {
     const int cn = min(kChunkTable, nvis - c0);
-    __syncthreads();   // the previous chunk's entries are no longer read
-    const int32_t* row = p.block_tables + (size_t)s * p.mbs + c0;
-    for (int i = threadIdx.x; i < cn; i += 64 * kChunkWaves) {
-      const int pb = row[i];
+    __syncthreads();   // every wave is done with the ring and the previous entries
+    const int32_t* trow = p.block_tables + (size_t)s * p.mbs + c0;
+    for (int i = threadIdx.x; i < cn; i += 64 * NW) {
+      const int pb = trow[i];
       tab[i] = (pb < 0 || pb >= p.num_blocks) ? 0 : pb;   // a bad table must not leave the caches
     }
     __syncthreads();
-    // this wave's blocks: entries [j0, j1) of the chunk
-    const int j0 = wave * cn / kChunkWaves, j1 = (wave + 1) * cn / kChunkWaves;
-    const int n = j1 - j0;
-    Tile ring[DEPTH];
+    // The ring holds three pairs of blocks; block b sits in slot b mod 6.
+    // Step k waits for its own pair (pair k + 1 may still be in flight),
+    // then, after the barrier (every wave's pieces have landed and every wave
+    // is done with pair k - 1), loads pair k + 2 into the slots pair k - 1
+    // used and works on pair k.  Past the end the loads are zero-size: the
+    // rows of such a block read as zeros and its scores are masked (its
+    // positions lie past every row's limit).
+    issue(ring0, 0, cn, c0);
+    issue(ring1, 1, cn, c0);
+    issue(ring2, 2, cn, c0);
+    issue(ring3, 3, cn, c0);
+    for (int j = 0; j < cn; j += 6) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], j0 + d, j1, c0);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int k0 = 0; k0 < n; k0 += DEPTH) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        const int k = k0 + d;
-        if (k < n) process(ring[d], (c0 + j0 + k) * kBS);
-        __builtin_amdgcn_sched_barrier(0);
-        load_tile(ring[d], j0 + k + DEPTH, j1, c0);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int h = 0; h < 3; ++h) {
+        const int jj = j + 2 * h;
+        // A plain s_barrier: __syncthreads()'s release fence would also wait
+        // for the loads of the next pair, which this step does not need.  The
+        // clobber keeps the compiler from moving memory accesses across it.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(2 * LPW));
+        asm volatile("s_barrier" ::: "memory");
+        issue(ring((2 * h + 4) % 6), jj + 4, cn, c0);
+        issue(ring((2 * h + 5) % 6), jj + 5, cn, c0);
+        if (has_rows && jj < cn) process2(ring(2 * h), ring(2 * h + 1), (c0 + jj) * kBS);
       }
     }
   }
+  // the last issued pieces (zero-size, past the chunk) land before the ring
+  // is reused for the output rows
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __syncthreads();
+  if (!has_rows) return;
 
-  // ---- combine the four waves' states: (2, 3) into (0, 1), then 1 into 0 --
-  float l[kChunkCG];
+  // ---- normalised rows through this wave's share of the ring -------------
+  float inv[kChunkCG];
 #pragma unroll
   for (int cg = 0; cg < kChunkCG; ++cg) {
-    l[cg] = lsum[cg] + __shfl_xor(lsum[cg], 16, 64);
-    l[cg] += __shfl_xor(l[cg], 32, 64);
+    float l = lsum[cg] + __shfl_xor(lsum[cg], 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    inv[cg] = l > 0.f ? 1.f / l : 0.f;
   }
-  // state slot `slot`: rows [32][RS], row = 16 cg + g: acc, then m at D, l at D + 1
-  auto put = [&](int slot) {
+  float* st = reinterpret_cast<float*>(ring(wave));
+  static_assert(8 * RS * 4 <= SLOT, "eight staged rows fit a ring slot");
+  constexpr int CPO = D / 8;   // 16-byte pieces of an output row
 #pragma unroll
-    for (int cg = 0; cg < kChunkCG; ++cg) {
-      float* st = states + (size_t)(slot * kChunkRows + 16 * cg + g) * RS;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) *reinterpret_cast<floatx4*>(st + 16 * n + 4 * kg) = acc[cg][n];
-      if (kg == 0) {
-        st[D] = m2[cg];
-        st[D + 1] = l[cg];
-      }
-    }
-  };
-  auto take = [&](int slot) {
-#pragma unroll
-    for (int cg = 0; cg < kChunkCG; ++cg) {
-      const float* st = states + (size_t)(slot * kChunkRows + 16 * cg + g) * RS;
-      const float mo = st[D], lo = st[D + 1];
-      const float mn = fmaxf(m2[cg], mo);
-      // an empty state (m = -inf) weighs nothing
-      const float wa = m2[cg] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2[cg] - mn);
-      const float wb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+  for (int q = 0; q < 4; ++q) {   // rows 8q .. 8q + 7 of the wave's 32
+    const int cg = q >> 1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if ((g >> 3) == (q & 1)) {
 #pragma unroll
       for (int n = 0; n < NN; ++n)
-        acc[cg][n] = acc[cg][n] * wa + *reinterpret_cast<const floatx4*>(st + 16 * n + 4 * kg) * wb;
-      l[cg] = l[cg] * wa + lo * wb;
-      m2[cg] = mn;
-    }
-  };
-  if (wave >= 2) put(wave - 2);
-  __syncthreads();
-  if (wave < 2) take(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
-  __syncthreads();
-  if (wave == 0) {
-    take(0);
-    // normalised rows -> LDS (slot 0, row-major), then whole-line stores
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int cg = 0; cg < kChunkCG; ++cg) {
-      const float inv = l[cg] > 0.f ? 1.f / l[cg] : 0.f;
-      float* st = states + (size_t)(16 * cg + g) * RS;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) *reinterpret_cast<floatx4*>(st + 16 * n + 4 * kg) = acc[cg][n] * inv;
+        *reinterpret_cast<floatx4*>(st + (g & 7) * RS + 16 * n + 4 * kg) = acc[cg][n] * inv[cg];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    constexpr int CPR = D / 8;   // 16-byte pieces of an output row
-    const int rows = min(kChunkRows, nrows - r0);
-    for (int c = lane; c < rows * CPR; c += 64) {
-      const float* src = states + (size_t)(c / CPR) * RS + (c % CPR) * 8;
+    const int rbase = w0 + 8 * q;
+    const int rows = min(8, nrows - rbase);
+    for (int c = lane; c < rows * CPO; c += 64) {
+      const float* src = st + (c / CPO) * RS + (c % CPO) * 8;
       const floatx4 lo = *reinterpret_cast<const floatx4*>(src);
       const floatx4 hi = *reinterpret_cast<const floatx4*>(src + 4);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + qrow(r0 + c / CPR) + (c % CPR) * 8) =
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + qrow(rbase + c / CPO) + (c % CPO) * 8) =
           make_uint4(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]), M::pack2(hi[0], hi[1]), M::pack2(hi[2], hi[3]));
     }
   }
 }
 
+template <typename QT, int D, int NW>
+static int launch_chunk_nw(const ChunkParams& p, hipStream_t st) {
+  auto kernel = chunk_attn_kernel<QT, D, NW>;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const long long tiles = (p.qtok * G + 32 * NW - 1) / (32 * NW);
+  const long long pairs8 = ((long long)p.num_seqs * p.num_kv_heads + 7) / 8 * 8;
+  kernel<<<dim3((unsigned)(pairs8 * tiles)), 64 * NW, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+// waves per workgroup: enough for the rows (32 each), at most 4
 template <typename QT, int D>
 static int launch_chunk_d(const ChunkParams& p, hipStream_t st) {
-  auto kernel = chunk_attn_kernel<QT, D>;
-  static std::atomic<bool> lds_set[64];
-  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kernel), chunk_lds_bytes<D>(), lds_set);
-  if (e != hipSuccess) return e;
-  const int G = p.num_q_heads / p.num_kv_heads;
-  const dim3 grid((p.qtok * G + kChunkRows - 1) / kChunkRows, p.num_kv_heads, p.num_seqs);
-  kernel<<<grid, 64 * kChunkWaves, chunk_lds_bytes<D>(), st>>>(p);
-  return hipGetLastError();
+  const int rows = p.qtok * (p.num_q_heads / p.num_kv_heads);
+  if (rows <= 32) return launch_chunk_nw<QT, D, 1>(p, st);
+  if (rows <= 64) return launch_chunk_nw<QT, D, 2>(p, st);
+  return launch_chunk_nw<QT, D, 4>(p, st);
 }
 
 int launch_chunk_attn(const AttnArgs& a) {
