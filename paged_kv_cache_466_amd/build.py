@@ -19,7 +19,8 @@ LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libpkv.so")
 OBJDIR = os.path.join(ROOT, "_build", "pkv")
 
-SOURCES = ["api.hip", "cache_ops.hip", "paged_attn.hip", "quest.hip", "host.cpp", "pool.cpp", "reuse.cpp"]
+SOURCES = ["api.hip", "cache_ops.hip", "paged_attn.hip", "query_tile.hip", "quest.hip", "host.cpp", "pool.cpp",
+           "reuse.cpp"]
 # the host-only sources, also built on their own under the address and
 # undefined-behaviour sanitizers (build_host_sanitized)
 HOST_SOURCES = ["host.cpp", "pool.cpp", "reuse.cpp"]

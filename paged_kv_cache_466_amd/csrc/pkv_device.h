@@ -182,6 +182,89 @@ __device__ __forceinline__ uint32_t f32_to_e5m2(float x) {
   return code | sign;
 }
 
+// ---------------------------------------------------------------------------
+// buffer loads and the 16-bit MFMA operand helpers shared by the attention
+// kernels
+// ---------------------------------------------------------------------------
+// Raw buffer resource over `nbytes` bytes from `base` (gfx9 descriptor word 3).
+// A load whose offset + size exceeds nbytes returns zeros and reads nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+}
+// POL: cache-policy bits of the load (gfx950: 2 = nt, non-temporal).
+template <int POL = 0>
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, POL));
+}
+constexpr int kPolicyStream = 2;   // non-temporal: streamed data does not evict reused data
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff = 0) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+constexpr int kOutOfRange = 0x40000000;    // buffer offset that is always out of range
+
+// 16-bit MFMA element type of the query (bf16 or f16) and the converted KV.
+template <typename QT> struct Mfma;
+template <> struct Mfma<BF16> {
+  typedef bf16x8 vec8;
+  __device__ static floatx4 qk(const vec8& a, const vec8& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static floatx4 pv(const shortx4& a, const shortx4& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // two values rounded to nearest even, packed (one v_cvt_pk_bf16_f32)
+  __device__ static uint32_t pack2(float x, float y) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){x, y}, b2));
+  }
+  // c plus the two packed values (one v_dot2_f32_bf16 against (1, 1))
+  __device__ static float acc2(uint32_t w, float c) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), (b2){(__bf16)1.0f, (__bf16)1.0f}, c, false);
+  }
+  // two FP8-E4M3 codes (byte pair `hi` of w) -> two values, exactly
+  template <bool HI> __device__ static uint32_t fp8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
+  template <bool HI> __device__ static uint32_t bf8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+  }
+  __device__ static shortx4 tr_read(const void* lds) {
+    bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(lds));
+    return __builtin_bit_cast(shortx4, v);
+  }
+};
+template <> struct Mfma<F16> {
+  typedef f16x8 vec8;
+  __device__ static floatx4 qk(const vec8& a, const vec8& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static floatx4 pv(const shortx4& a, const shortx4& b, const floatx4& c) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b), c, 0,
+                                                 0, 0);
+  }
+  __device__ static uint32_t pack2(float x, float y) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){x, y}, h2));
+  }
+  __device__ static float acc2(uint32_t w, float c) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), (h2){(_Float16)1.0f, (_Float16)1.0f}, c, false);
+  }
+  template <bool HI> __device__ static uint32_t fp8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+  template <bool HI> __device__ static uint32_t bf8x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, HI));
+  }
+  __device__ static shortx4 tr_read(const void* lds) {
+    fp16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4*)(lds));
+    return __builtin_bit_cast(shortx4, v);
+  }
+};
+
 // Raises a kernel's dynamic-LDS limit to `bytes` once per device (the
 // attribute is set with the device current; devices up to 64 are tracked,
 // others set it on every call).  `done` is the kernel's own flag array.
