@@ -9,15 +9,18 @@
 //  * quest_summarize_kernel - minimum / maximum per (block, KV head, dim)
 //    over the block's written rows, stored in the cache's 16-bit type (exact:
 //    both are stored values).  Layout [NB][Hkv][2][D].
+//  * quest_qprep_kernel - the query group of each (sequence, KV head) split
+//    into its positive and negative parts, as doubles.
 //  * quest_score_kernel - the score of every page of every (sequence, KV
 //    head): the largest over the group's query heads, in fp64 (each product
 //    of two 16-bit values is exact there), stored as an order-preserving
-//    64-bit key.  16 lanes per page, 8 (or 4) dimensions per lane, 64
-//    pages per workgroup.
+//    64-bit key.  One lane per page, 64 pages per wave; the query parts are
+//    read by scalar loads, the summaries staged through LDS.
 //  * quest_select_kernel - per (sequence, KV head), the `budget` largest
-//    keys by a 6-pass radix select (11-bit digits) over the keys held in LDS
-//    (LDS histograms), ties to the lower page, written in logical order as
-//    (physical block, logical block).
+//    keys by a radix select (11-bit digits from the highest bit where keys
+//    differ, stopping once a digit's bin is kept whole) over the keys held
+//    in LDS (LDS histograms), ties to the lower page, written in logical
+//    order as (physical block, logical block).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -84,128 +87,257 @@ __global__ __launch_bounds__(256) void quest_summarize_kernel(const uint16_t* __
   }
 }
 
-// x of the lane `o` places further along its row of 16 lanes (DPP row
-// rotation), for a double.
-__device__ __forceinline__ double row_ror(double x, int o) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, x);
-  int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
-  switch (o) {
-    case 8:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x128, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x128, 0xF, 0xF, false);
-      break;
-    case 4:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x124, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x124, 0xF, 0xF, false);
-      break;
-    case 2:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x122, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x122, 0xF, 0xF, false);
-      break;
-    default:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x121, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x121, 0xF, 0xF, false);
-      break;
-  }
-  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
 // Order-preserving map of a double onto uint64 (larger value, larger key).
 __device__ __forceinline__ uint64_t order_key(double x) {
   const uint64_t b = __builtin_bit_cast(uint64_t, x);
   return (b >> 63) ? ~b : (b | (1ull << 63));
 }
 
-constexpr int kScorePagesPerGroup = 64;   // pages per scoring workgroup: 4 rounds of 16
+// Query heads of a group padded to a power of two (at most 16); the padded
+// heads repeat the last one, so the largest score over them is unchanged.
+__host__ __device__ constexpr int padded_group(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
 
-// grid (S * Hkv, ceil(mbs / 64)), 256 threads: 16 lanes per page, 16 pages
-// a round, 4 rounds.  The table entries of all rounds are requested
-// together, then all summaries together with the query group.  With
-// q+ = max(q, 0) and q- = min(q, 0), max(q * min, q * max) = q+ * max +
-// q- * min (min <= max), so a head's score is two fp64 dot products; every
-// product is exact, and the 16-lane sums of 4 heads are reduced together
-// by DPP row rotations.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void quest_score_kernel(const uint16_t* __restrict__ query,
-                                                          const uint16_t* __restrict__ summ,
-                                                          const int32_t* __restrict__ bt, int mbs,
-                                                          const int32_t* __restrict__ lens, int num_blocks,
-                                                          int Hq, int Hkv, uint64_t* __restrict__ keys) {
-  constexpr int DPL = D / 16;   // dimensions per lane: 16 bytes of 16-bit values at D = 128
-  constexpr int R = kScorePagesPerGroup / 16;
-  typedef uint16_t u16xN __attribute__((ext_vector_type(DPL)));
-  __shared__ float qp[16 * D], qn[16 * D];   // q+ and q- of the group's heads (exact)
-  const int s = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+// The query parts of one (sequence, KV head) as doubles: value f = d * 2GP
+// + j (j < GP: q+ = max(q, 0) of head j; j >= GP: q- = min(q, 0) of head
+// j - GP; both exact) is entry f % 16 of register pair f / 16 of a 16-lane
+// row.  Pairs are stored two at a time per row position: pair v, position
+// n at byte ((v / 2) * 16 + n) * 16 + (v % 2) * 8, so that lane n of a row
+// reads pairs v and v + 1 with one 16-byte load.
+__host__ __device__ constexpr int quest_q_bytes(int D, int GP) { return D * 2 * GP * 8; }
+__device__ __forceinline__ int quest_q_offset(int f) { return (((f >> 5) * 16 + (f & 15)) * 16 + ((f >> 4) & 1) * 8) / 8; }
+
+// grid (S * Hkv), 256 threads: the query parts of each (sequence, KV head)
+// in the layout above, qd + (s * Hkv + kvh) * quest_q_bytes(D, GP).
+template <typename T>
+__global__ __launch_bounds__(256) void quest_qprep_kernel(const uint16_t* __restrict__ query, int Hq, int Hkv, int D,
+                                                          int GP, double* __restrict__ qd) {
+  const int sk = blockIdx.x, s = sk / Hkv, kvh = sk - s * Hkv;
   const int G = Hq / Hkv;
+  double* o = qd + (size_t)sk * quest_q_bytes(D, GP) / 8;
+  for (int f = threadIdx.x; f < D * 2 * GP; f += 256) {
+    const int d = f / (2 * GP), j = f - d * 2 * GP;
+    const int g = j < GP ? j : j - GP;
+    const float x = ld16<T>(query, ((size_t)s * Hq + kvh * G + min(g, G - 1)) * D + d);
+    o[quest_q_offset(f)] = j < GP ? (x > 0.f ? (double)x : 0.0) : (x < 0.f ? (double)x : 0.0);
+  }
+}
+
+// acc[i] += (entry B + i of q's row) * x for i < N: v_fmac_f64 with a DPP
+// row broadcast of its first operand.  The leading s_nop covers the two
+// wait states a DPP read needs after a VALU write of its source.
+template <int N, int B>
+__device__ __forceinline__ void fmac_row_bcast(double* acc, double q, double x);
+template <int B>
+__device__ __forceinline__ void fmac_row_bcast1(double* a, double q, double x) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(a[0])
+      : "v"(q), "v"(x), "n"(B));
+}
+template <int B>
+__device__ __forceinline__ void fmac_row_bcast2(double* a, double q, double x) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f64_dpp %0, %2, %3 row_newbcast:%4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %1, %2, %3 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+      : "+v"(a[0]), "+v"(a[1])
+      : "v"(q), "v"(x), "n"(B), "n"(B + 1));
+}
+template <int B>
+__device__ __forceinline__ void fmac_row_bcast4(double* a, double q, double x) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f64_dpp %0, %4, %5 row_newbcast:%6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %1, %4, %5 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %2, %4, %5 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %3, %4, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf"
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+      : "v"(q), "v"(x), "n"(B), "n"(B + 1), "n"(B + 2), "n"(B + 3));
+}
+template <int B>
+__device__ __forceinline__ void fmac_row_bcast8(double* a, double q, double x) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f64_dpp %0, %8, %9 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %1, %8, %9 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %2, %8, %9 row_newbcast:%12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %3, %8, %9 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %4, %8, %9 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %5, %8, %9 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %6, %8, %9 row_newbcast:%16 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %7, %8, %9 row_newbcast:%17 row_mask:0xf bank_mask:0xf"
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+      : "v"(q), "v"(x), "n"(B), "n"(B + 1), "n"(B + 2), "n"(B + 3), "n"(B + 4), "n"(B + 5), "n"(B + 6),
+        "n"(B + 7));
+}
+template <int N, int B>
+__device__ __forceinline__ void fmac_row_bcast(double* acc, double q, double x) {
+  if constexpr (N == 1) fmac_row_bcast1<B>(acc, q, x);
+  else if constexpr (N == 2) fmac_row_bcast2<B>(acc, q, x);
+  else if constexpr (N == 4) fmac_row_bcast4<B>(acc, q, x);
+  else fmac_row_bcast8<B>(acc, q, x);
+}
+
+constexpr int kScorePages = 64;                                  // pages per scoring wave: one per lane
+constexpr int kScoreWaves = 4;                                   // waves per scoring workgroup
+constexpr int kScoreDims = 32;                                   // dimensions per stage
+constexpr int kScoreStage = kScorePages * 2 * kScoreDims * 2;    // (minimum, maximum) x 16 bits: 8 KiB
+
+// Position of a page's 16-byte units in a stage: page p's unit u sits at
+// p * 128 + 16 * (u ^ swz(p)).  Any 8 lanes reading unit u of pages p..p+7
+// (or 16 lanes, of pages p..p+15 with p a multiple of 16) meet distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int score_swz(int p) { return (p ^ (p >> 3)) & 7; }
+
+template <typename T>
+__device__ __forceinline__ double cvt_d(uint32_t w, int upper) {
+  if constexpr (std::is_same<T, BF16>::value)
+    return (double)__builtin_bit_cast(float, upper ? (w & 0xffff0000u) : (w << 16));
+  else
+    return (double)f16_to_f32((uint16_t)(upper ? w >> 16 : w));
+}
+
+// The 2 * GP products of dimension d (dim: its index within the head) into
+// ap (q+ * maximum) and an (q- * minimum); qv: the register pairs of the
+// stage's query parts, pair v at qv[v - v0].
+template <int GP>
+__device__ __forceinline__ void score_dim(double* ap, double* an, const double* qv, int v0, int dim, double mx,
+                                          double mn);
+
+// grid (S * Hkv, ceil(mbs / 256)), 4 waves: lane i of wave w scores page
+// lb0 + 64 w + i.  With q+ = max(q, 0) and q- = min(q, 0), max(q * min, q *
+// max) = q+ * max + q- * min (min <= max), so a head's score is two fp64
+// dot products of exact products.  The query parts are copied once into
+// LDS and reach the FMAs by DPP row broadcasts; the summaries are taken 32
+// dimensions at a time: the wave's 64 pages' minima and maxima of a stage
+// (8 KiB) are copied by 8 direct-to-LDS loads of 8 pages each, two stages
+// in flight.
+template <typename T, int D, int GP>
+__global__ __launch_bounds__(64 * kScoreWaves) void quest_score_kernel(const double* __restrict__ qd,
+                                                                       const uint16_t* __restrict__ summ,
+                                                                       const int32_t* __restrict__ bt, int mbs,
+                                                                       const int32_t* __restrict__ lens,
+                                                                       int num_blocks, int Hkv,
+                                                                       uint64_t* __restrict__ keys) {
+  constexpr int NST = D / kScoreDims;
+  constexpr int QB = quest_q_bytes(D, GP);
+  constexpr int PPS = kScoreDims * 2 * GP / 16;   // register pairs of query parts per stage
+  __shared__ __attribute__((aligned(16))) uint8_t qs[QB];
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[kScoreWaves][kScoreStage], stage1[kScoreWaves][kScoreStage];
+  const int sk = blockIdx.x, s = sk / Hkv, kvh = sk - s * Hkv;
   const int L = clamp_len_q(lens[s], mbs);
   const int nb = (L + kBS - 1) / kBS;
-  const int lb0 = blockIdx.y * kScorePagesPerGroup;
-  if (lb0 >= nb) return;
-  const int j = threadIdx.x & 15;
-  int pb[R];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lb0 = (blockIdx.y * kScoreWaves + wave) * kScorePages;
+  if (blockIdx.y * kScoreWaves * kScorePages >= nb) return;
+  const int pb = table_pb(bt, mbs, s, min(lb0 + lane, nb - 1), num_blocks);
+  // load k of a stage: lane i copies unit (i % 8) ^ swz(p) of page p = 8k + i / 8
+  // (units 0-3: minima of the stage's dimensions, 4-7: maxima)
+  const uint16_t* src[8];
 #pragma unroll
-  for (int r = 0; r < R; ++r) pb[r] = table_pb(bt, mbs, s, min(lb0 + r * 16 + (int)threadIdx.x / 16, nb - 1), num_blocks);
-  u16xN mn[R], mx[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint16_t* o = summ + ((size_t)pb[r] * Hkv + kvh) * 2 * D + j * DPL;
-    mn[r] = *reinterpret_cast<const u16xN*>(o);
-    mx[r] = *reinterpret_cast<const u16xN*>(o + D);
+  for (int k = 0; k < 8; ++k) {
+    const int p = 8 * k + (lane >> 3);
+    const int pbk = __shfl(pb, p, 64);
+    const int u = (lane & 7) ^ score_swz(p);
+    src[k] = summ + ((size_t)pbk * Hkv + kvh) * 2 * D + (u >= 4 ? D : 0) + 8 * (u & 3);
   }
+  // the query parts: QB / 1024 direct-to-LDS loads shared by the waves, the
+  // same count in every wave (below 4 KiB some pieces are loaded twice, with
+  // the same bytes)
   {
-    // the group's G * D query values as 8-element pieces (index clamped)
-    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-    constexpr int PPT = (16 * D / 8 + 255) / 256;   // pieces per thread
-    const u16x8* q8 = reinterpret_cast<const u16x8*>(query + ((size_t)s * Hq + kvh * G) * D);
-    u16x8 qv[PPT];
+    constexpr int NQ = QB / 1024, NQW = NQ >= kScoreWaves ? NQ / kScoreWaves : 1;
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(qd) + (size_t)sk * QB;
 #pragma unroll
-    for (int u = 0; u < PPT; ++u) qv[u] = q8[min(u * 256 + (int)threadIdx.x, G * D / 8 - 1)];
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int piece = u * 256 + threadIdx.x;
-      if (piece < 16 * D / 8) {   // within the arrays (pieces past G * D repeat the last)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = cvt16<T>(qv[u][e]);
-          qp[piece * 8 + e] = fmaxf(x, 0.f);
-          qn[piece * 8 + e] = fminf(x, 0.f);
-        }
-      }
+    for (int i = 0; i < NQW; ++i) {
+      const int k = (wave + kScoreWaves * i) % NQ;
+      __builtin_amdgcn_global_load_lds((const void*)(qsrc + k * 1024 + lane * 16),
+                                       (__attribute__((address_space(3))) void*)(qs + k * 1024), 16, 0, 0);
     }
   }
-  __syncthreads();
+  uint8_t* buf0 = stage0[wave];
+  uint8_t* buf1 = stage1[wave];
+  // a wave past the last page scores copies of it (nothing is stored)
+  auto issue = [&](uint8_t* buf, int st) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    double lo[DPL], hi[DPL];
+    for (int k = 0; k < 8; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(src[k] + st * kScoreDims),
+                                       (__attribute__((address_space(3))) void*)(buf + k * 1024), 16, 0, 0);
+  };
+  issue(buf0, 0);
+  if constexpr (NST > 1) issue(buf1, 1);
+  // the wave's own query loads are the oldest: vmcnt(16) leaves only the
+  // stage loads outstanding; after the barrier every wave's copies are in LDS
+  static_assert(NST > 1, "two stages in flight");
+  __builtin_amdgcn_s_waitcnt(0x4070);   // vmcnt(16), lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+  const int xr = (lane * 128) | (score_swz(lane) << 4);   // unit u of this lane's page: xr ^ (u << 4)
+  const int qrow = (lane & 15) * 16;                       // this lane's row position in qs
+  double ap[GP], an[GP];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-      lo[k] = cvt16<T>(mn[r][k]);
-      hi[k] = cvt16<T>(mx[r][k]);
+  for (int h = 0; h < GP; ++h) ap[h] = an[h] = 0.0;
+  auto compute = [&](const uint8_t* buf, int st) {
+    double qv[PPS];
+#pragma unroll
+    for (int i = 0; i < PPS; i += 2) {
+      const double2 t = *reinterpret_cast<const double2*>(qs + ((st * PPS + i) / 2) * 256 + qrow);
+      qv[i] = t.x;
+      qv[i + 1] = t.y;
     }
-    double best = -INFINITY;
-    for (int g0 = 0; g0 < G; g0 += 4) {
-      double acc[4];
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int g = min(g0 + gg, G - 1);   // heads past G repeat the last one
-        const float* a = qp + g * D + j * DPL;
-        const float* b = qn + g * D + j * DPL;
-        double t = 0.0;
+    for (int c = 0; c < 4; ++c) {
+      const uint4 mnv = *reinterpret_cast<const uint4*>(buf + (xr ^ (c << 4)));
+      const uint4 mxv = *reinterpret_cast<const uint4*>(buf + (xr ^ ((4 + c) << 4)));
+      const uint32_t mnw[4] = {mnv.x, mnv.y, mnv.z, mnv.w}, mxw[4] = {mxv.x, mxv.y, mxv.z, mxv.w};
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) t = fma((double)a[k], hi[k], fma((double)b[k], lo[k], t));
-        acc[gg] = t;
-      }
-      // sum over the page's 16 lanes: rotations within a row of 16 lanes
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) {
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) acc[gg] += row_ror(acc[gg], o);
-      }
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) best = fmax(best, acc[gg]);
+      for (int e = 0; e < 8; ++e)
+        score_dim<GP>(ap, an, qv, st * PPS, st * kScoreDims + 8 * c + e, cvt_d<T>(mxw[e >> 1], e & 1),
+                      cvt_d<T>(mnw[e >> 1], e & 1));
     }
-    const int lb = lb0 + r * 16 + threadIdx.x / 16;
-    if (lb < nb && j == 0) keys[((size_t)s * Hkv + kvh) * mbs + lb] = order_key(best);
+  };
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    // s_waitcnt vmcnt(8) while the next stage is still in flight, else
+    // vmcnt(0) (lgkmcnt(0), expcnt left alone)
+    if (st + 1 < NST) __builtin_amdgcn_s_waitcnt(0x0078);
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    compute((st & 1) ? buf1 : buf0, st);
+    if (st + 2 < NST) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this stage's LDS reads are done
+      issue((st & 1) ? buf1 : buf0, st + 2);
+    }
+  }
+  double best = ap[0] + an[0];
+#pragma unroll
+  for (int h = 1; h < GP; ++h) best = fmax(best, ap[h] + an[h]);
+  if (lb0 + lane < nb) keys[(size_t)sk * mbs + lb0 + lane] = order_key(best);
+}
+
+// value f = dim * 2GP + j sits at entry f % 16 of pair f / 16
+template <int GP>
+__device__ __forceinline__ void score_dim(double* ap, double* an, const double* qv, int v0, int dim, double mx,
+                                          double mn) {
+  if constexpr (GP == 16) {
+    const double qp = qv[2 * dim - v0], qn = qv[2 * dim + 1 - v0];
+    fmac_row_bcast<8, 0>(ap, qp, mx);
+    fmac_row_bcast<8, 8>(ap + 8, qp, mx);
+    fmac_row_bcast<8, 0>(an, qn, mn);
+    fmac_row_bcast<8, 8>(an + 8, qn, mn);
+  } else {
+    constexpr int PER = 16 / (2 * GP);   // dimensions per pair
+    const double q = qv[dim / PER - v0];
+    switch (dim % PER) {   // a constant after unrolling
+#define PKV_SCORE_DIM(R)                                   \
+  case R:                                                  \
+    if constexpr (R < PER) {                               \
+      fmac_row_bcast<GP, R * 2 * GP>(ap, q, mx);           \
+      fmac_row_bcast<GP, R * 2 * GP + GP>(an, q, mn);      \
+    }                                                      \
+    break;
+      PKV_SCORE_DIM(0) PKV_SCORE_DIM(1) PKV_SCORE_DIM(2) PKV_SCORE_DIM(3)
+      PKV_SCORE_DIM(4) PKV_SCORE_DIM(5) PKV_SCORE_DIM(6) PKV_SCORE_DIM(7)
+#undef PKV_SCORE_DIM
+    }
   }
 }
 
@@ -238,13 +370,28 @@ __device__ __forceinline__ int block_scan(int x, int* tmp, int* total) {
   return base + incl - x;
 }
 
+// OR of x over a kSelThreads-thread workgroup.
+__device__ __forceinline__ uint64_t block_or(uint64_t x, uint64_t* tmp64) {
+  constexpr int W = kSelThreads / 64;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x |= __shfl_xor(x, o, 64);
+  if ((threadIdx.x & 63) == 0) tmp64[threadIdx.x >> 6] = x;
+  __syncthreads();
+  uint64_t all = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) all |= tmp64[w];
+  __syncthreads();
+  return all;
+}
+
 // grid (S * Hkv), kSelThreads threads.  IN_LDS: the keys of the (sequence,
 // KV head) are first copied to LDS; otherwise every pass reads them from
 // global memory.  Thread t owns the contiguous run of keys [t * per,
 // (t + 1) * per).  Radix select of the budget-th largest key, 11 bits at a
-// time from the top, with LDS histogram atomics; then every larger key is
-// kept, and the first keys equal to it in page order until the budget is
-// met.
+// time from the highest bit where the keys differ, with LDS histogram
+// atomics, stopping early once the digit's whole bin is kept; then every
+// larger key is kept, and the first keys equal to it in page order until
+// the budget is met.
 template <bool IN_LDS>
 __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint64_t* __restrict__ keys,
                                                                    const int32_t* __restrict__ bt, int mbs,
@@ -253,8 +400,9 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint64_
                                                                    int32_t* __restrict__ selected) {
   extern __shared__ uint64_t kl[];
   __shared__ int hist[kBins];
-  __shared__ int pick[2];
+  __shared__ int pick[3];
   __shared__ int tmp[kSelThreads / 64];
+  __shared__ uint64_t tmp64[kSelThreads / 64];
   const int tid = threadIdx.x;
   const int s = blockIdx.x / Hkv;
   const int L = clamp_len_q(lens[s], mbs);
@@ -279,9 +427,17 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint64_
   auto key_at = [&](int i) { return IN_LDS ? kl[i] : kg[i]; };
   const int per = (nb + kSelThreads - 1) / kSelThreads;
   const int r0 = min(nb, tid * per), r1 = min(nb, r0 + per);
-  uint64_t prefix = 0, mask = 0;
-  int remaining = budget;   // keys still to take at or below the current prefix
-  for (int top = 64; top > 0; top -= kDigitBits) {
+  // bits every key shares need no pass (their digits would all fall in one
+  // bin): start below the highest bit where two keys differ
+  const uint64_t k0 = key_at(0);
+  uint64_t dif = 0;
+  for (int i = r0; i < r1; ++i) dif |= key_at(i) ^ k0;
+  dif = block_or(dif, tmp64);
+  int top = dif ? 64 - __clzll((long long)dif) : 0;
+  uint64_t mask = top >= 64 ? 0 : ~0ull << top;
+  uint64_t prefix = k0 & mask;
+  int remaining = budget;   // keys still to take among those whose masked bits equal prefix
+  while (top > 0) {
     const int bits = top < kDigitBits ? top : kDigitBits;
     const int shift = top - bits;
     const int dmask = (1 << bits) - 1;
@@ -313,6 +469,7 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint64_
       if (above < remaining && above + c[u] >= remaining) {
         pick[0] = kBins - 1 - (tid * BPT + u);
         pick[1] = remaining - above;
+        pick[2] = c[u];
       }
       above += c[u];
     }
@@ -320,22 +477,27 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint64_
     prefix |= (uint64_t)pick[0] << shift;
     mask |= (uint64_t)dmask << shift;
     remaining = pick[1];
+    top = shift;
+    const bool whole_bin = pick[2] == remaining;   // every key in the digit's bin is kept
     __syncthreads();
+    if (whole_bin) break;
   }
+  // kept: keys whose masked bits exceed prefix, and the first `remaining`
+  // (in page order) of those equal to it
   int eq = 0;
-  for (int i = r0; i < r1; ++i) eq += key_at(i) == prefix;
+  for (int i = r0; i < r1; ++i) eq += (key_at(i) & mask) == prefix;
   int unused;
   int eq_seen = block_scan(eq, tmp, &unused);
   int nsel = 0;
   for (int i = r0; i < r1; ++i) {
-    const uint64_t key = key_at(i);
+    const uint64_t key = key_at(i) & mask;
     if (key > prefix) ++nsel;
     else if (key == prefix) nsel += (eq_seen++ < remaining);
   }
   int pos = block_scan(nsel, tmp, &unused);
   eq_seen -= eq;
   for (int i = r0; i < r1; ++i) {
-    const uint64_t key = key_at(i);
+    const uint64_t key = key_at(i) & mask;
     bool sel = key > prefix;
     if (key == prefix) sel = eq_seen++ < remaining;
     if (sel) out[pos++] = make_int2(table_pb(bt, mbs, s, i, num_blocks), i);
@@ -368,17 +530,33 @@ int launch_quest_select(const void* query, int q_dtype, const void* k_summary, c
   auto q = reinterpret_cast<const uint16_t*>(query);
   auto sm = reinterpret_cast<const uint16_t*>(k_summary);
   auto keys = reinterpret_cast<uint64_t*>(scratch);
-  const dim3 sgrid(num_seqs * num_kv_heads, (max_blocks_per_seq + kScorePagesPerGroup - 1) / kScorePagesPerGroup);
-#define PKV_SCORE(T, D)                                                                                        \
-  quest_score_kernel<T, D><<<sgrid, 256, 0, st>>>(q, sm, block_tables, max_blocks_per_seq, seq_lens, num_blocks, \
-                                                 num_q_heads, num_kv_heads, keys)
-  if (q_dtype == PKV_BF16) {
-    if (head_dim == 64) PKV_SCORE(BF16, 64);
-    else PKV_SCORE(BF16, 128);
-  } else {
-    if (head_dim == 64) PKV_SCORE(F16, 64);
-    else PKV_SCORE(F16, 128);
+  // the query halves follow the keys (pkv_quest_scratch_bytes reserves both)
+  auto qd = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(scratch) +
+                                      quest_keys_bytes(num_seqs, num_kv_heads, max_blocks_per_seq));
+  const int GP = padded_group(num_q_heads / num_kv_heads);
+  if (q_dtype == PKV_BF16)
+    quest_qprep_kernel<BF16><<<num_seqs * num_kv_heads, 256, 0, st>>>(q, num_q_heads, num_kv_heads, head_dim, GP, qd);
+  else
+    quest_qprep_kernel<F16><<<num_seqs * num_kv_heads, 256, 0, st>>>(q, num_q_heads, num_kv_heads, head_dim, GP, qd);
+  constexpr int kWgPages = kScorePages * kScoreWaves;
+  const dim3 sgrid(num_seqs * num_kv_heads, (max_blocks_per_seq + kWgPages - 1) / kWgPages);
+#define PKV_SCORE(T, D, G)                                                                              \
+  quest_score_kernel<T, D, G><<<sgrid, 64 * kScoreWaves, 0, st>>>(qd, sm, block_tables, max_blocks_per_seq, \
+                                                                  seq_lens, num_blocks, num_kv_heads, keys)
+#define PKV_SCORE_G(T, D)              \
+  switch (GP) {                        \
+    case 1: PKV_SCORE(T, D, 1); break; \
+    case 2: PKV_SCORE(T, D, 2); break; \
+    case 4: PKV_SCORE(T, D, 4); break; \
+    case 8: PKV_SCORE(T, D, 8); break; \
+    default: PKV_SCORE(T, D, 16); break; \
   }
+  if (q_dtype == PKV_BF16) {
+    if (head_dim == 64) PKV_SCORE_G(BF16, 64) else PKV_SCORE_G(BF16, 128)
+  } else {
+    if (head_dim == 64) PKV_SCORE_G(F16, 64) else PKV_SCORE_G(F16, 128)
+  }
+#undef PKV_SCORE_G
 #undef PKV_SCORE
   const int e = hipGetLastError();
   if (e != hipSuccess) return e;

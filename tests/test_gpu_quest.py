@@ -27,6 +27,11 @@ CASES = {
     "g8_f16": ("shared_prefix_b128", dict(S=3, len_lo=200, len_hi=900, prefix_tokens=64, q_dtype="f16",
                                           kv_dtype="f16", src_dtype="f16")),
     "d64_mqa": ("llama3_8b_b64", dict(S=3, Hq=8, Hkv=1, D=64, len_lo=100, len_hi=600)),
+    # several 64-page scoring waves per sequence with a ragged last one
+    "g2_long": ("llama3_8b_b64", dict(S=2, Hq=16, Hkv=8, len_lo=3000, len_hi=5000)),
+    # a group size that is not a power of two (padded to 4 heads)
+    "g3": ("llama3_8b_b64", dict(S=3, Hq=6, Hkv=2, len_lo=300, len_hi=1500)),
+    "g16": ("llama3_8b_b64", dict(S=2, Hq=32, Hkv=2, len_lo=500, len_hi=1200)),
 }
 
 _runs = {}
@@ -143,3 +148,70 @@ def test_full_budget_equals_full_decode():
     pkv.paged_attn_decode_selected(out, t["query"], g.k_cache, g.v_cache, sel, g.lens, w.sm_scale)
     ref = o.decode(to_raw(t["query"], w.q_dtype))
     assert np.abs(out.float().cpu().numpy() - ref).max() <= TOL
+
+
+def _oracle_scores_from_summaries(w, summ_raw, q_all, tables, lens):
+    """Oracle page scores per (sequence, KV head) from stored summaries."""
+    G = w.Hq // w.Hkv
+    out = {}
+    for s in range(w.S):
+        nb = (int(lens[s]) + 15) // 16
+        for h in range(w.Hkv):
+            qg = q_all[s, h * G:(h + 1) * G]
+            sc = []
+            for lb in range(nb):
+                pb = tables[s][lb]
+                mn = codecs.decode(summ_raw[pb, h, 0], w.kv_dtype)
+                mx = codecs.decode(summ_raw[pb, h, 1], w.kv_dtype)
+                sc.append(quest.group_page_score(qg, mn, mx))
+            out[s, h] = sc
+    return out
+
+
+@pytest.mark.parametrize("name", ["g3", "llama_shape"])
+def test_every_budget_matches_the_oracle_ranking(name):
+    """Each budget from 1 to the page count selects the oracle's pages: the
+    selection agrees with the oracle's whole ranking of every (sequence,
+    KV head)."""
+    import paged_kv_cache_466_amd as pkv
+    w, t, g, o = run_case(name)
+    summ = pkv.quest_summary_like(g.k_cache)
+    pkv.quest_summarize(g.k_cache, summ, g.block_tables, g.lens)
+    torch.cuda.synchronize()
+    q_all = codecs.decode(to_raw(t["query"], w.q_dtype), w.q_dtype)
+    scores = _oracle_scores_from_summaries(w, to_raw(summ, w.kv_dtype), q_all, o.tables, o.lens)
+    nmax = max((int(L) + 15) // 16 for L in o.lens)
+    for budget in range(1, nmax + 1):
+        sel = pkv.quest_select(t["query"], summ, g.block_tables, g.lens, budget).cpu().numpy()
+        for (s, h), sc in scores.items():
+            want = quest.select_pages(sc, budget)
+            assert sel[s, h, :len(want), 1].tolist() == want, (budget, s, h)
+
+
+def test_ties_at_the_cut_keep_the_lower_pages():
+    """Copies of one page's summary give equal scores; budgets that cut
+    through the equal pages keep the lower ones (checked against the
+    oracle's ranking of the same summaries)."""
+    import paged_kv_cache_466_amd as pkv
+    w, t, g, o = run_case("g2_long")
+    summ = pkv.quest_summary_like(g.k_cache)
+    pkv.quest_summarize(g.k_cache, summ, g.block_tables, g.lens)
+    torch.cuda.synchronize()
+    for s in range(w.S):
+        nb = (int(o.lens[s]) + 15) // 16
+        src = int(o.tables[s][5])
+        dst = torch.tensor([int(o.tables[s][lb]) for lb in range(7, nb, 3)], dtype=torch.long, device=summ.device)
+        summ[dst] = summ[src].clone()
+    torch.cuda.synchronize()
+    q_all = codecs.decode(to_raw(t["query"], w.q_dtype), w.q_dtype)
+    scores = _oracle_scores_from_summaries(w, to_raw(summ, w.kv_dtype), q_all, o.tables, o.lens)
+    budgets = set()
+    for (s, h), sc in scores.items():
+        order = sorted(range(len(sc)), key=lambda i: (-sc[i], i))
+        rank = order.index(5)            # the copied page and its copies sit together
+        budgets.update({rank + 1, rank + 2, rank + 10})
+    for budget in sorted(budgets):
+        sel = pkv.quest_select(t["query"], summ, g.block_tables, g.lens, budget).cpu().numpy()
+        for (s, h), sc in scores.items():
+            want = quest.select_pages(sc, budget)
+            assert sel[s, h, :len(want), 1].tolist() == want, (budget, s, h)
