@@ -299,9 +299,7 @@ pkv_status pkv_quest_summarize(const void* k_cache, int kv_dtype, void* k_summar
                                const int32_t* seq_lens, int num_seqs, int num_blocks, int block_size,
                                int num_kv_heads, int head_dim, int last_only, void* stream);
 
-/* Bytes of scratch pkv_quest_select needs: 8 per (sequence, KV head, block)
- * for the page keys, rounded up to 256, plus 32 KiB per (sequence, KV head)
- * for the query group as doubles. */
+/* Bytes of scratch pkv_quest_select needs (8 per (sequence, KV head, block)). */
 size_t pkv_quest_scratch_bytes(int num_seqs, int num_kv_heads, int max_blocks_per_seq);
 
 /*

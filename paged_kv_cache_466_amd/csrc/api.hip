@@ -604,8 +604,7 @@ extern "C" pkv_status pkv_paged_attn_decode_shared_prefix(
 
 extern "C" size_t pkv_quest_scratch_bytes(int num_seqs, int num_kv_heads, int max_blocks_per_seq) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 0;
-  return quest_keys_bytes(num_seqs, num_kv_heads, max_blocks_per_seq) +
-         (size_t)num_seqs * num_kv_heads * kQuestQueryBytes;
+  return align256((size_t)num_seqs * num_kv_heads * max_blocks_per_seq * 8);
 }
 
 extern "C" pkv_status pkv_quest_summarize(const void* k_cache, int kv_dtype, void* k_summary,

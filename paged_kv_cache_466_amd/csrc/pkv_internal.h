@@ -171,13 +171,6 @@ int launch_append_quantized(const void* key, const void* value, int src_dtype, v
 int launch_quest_summarize(const void* k_cache, int kv_dtype, void* k_summary, const int32_t* block_tables,
                            int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_blocks,
                            int num_kv_heads, int head_dim, int last_only, void* stream);
-// Quest selection scratch: the page keys (8 bytes per (sequence, KV head,
-// block), rounded up to 256 bytes), then the query halves as doubles
-// ([S * Hkv][D <= 128][2][padded group <= 16], 32 KiB per (sequence, KV head)).
-constexpr size_t kQuestQueryBytes = 128 * 2 * 16 * sizeof(double);
-inline size_t quest_keys_bytes(int num_seqs, int num_kv_heads, int max_blocks_per_seq) {
-  return ((size_t)num_seqs * num_kv_heads * max_blocks_per_seq * 8 + 255) & ~(size_t)255;
-}
 int launch_quest_select(const void* query, int q_dtype, const void* k_summary, const int32_t* block_tables,
                         int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_q_heads,
                         int num_kv_heads, int head_dim, int num_blocks, int budget, int32_t* selected,

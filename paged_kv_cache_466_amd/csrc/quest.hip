@@ -9,13 +9,11 @@
 //  * quest_summarize_kernel - minimum / maximum per (block, KV head, dim)
 //    over the block's written rows, stored in the cache's 16-bit type (exact:
 //    both are stored values).  Layout [NB][Hkv][2][D].
-//  * quest_qprep_kernel - the query group of each (sequence, KV head) split
-//    into its positive and negative parts, as doubles.
 //  * quest_score_kernel - the score of every page of every (sequence, KV
 //    head): the largest over the group's query heads, in fp64 (each product
 //    of two 16-bit values is exact there), stored as an order-preserving
-//    64-bit key.  One lane per page, 64 pages per wave; the query parts are
-//    read by scalar loads, the summaries staged through LDS.
+//    64-bit key.  One lane per page, 64 pages per wave; the query parts
+//    are held in LDS and reach the FMAs by DPP row broadcasts.
 //  * quest_select_kernel - per (sequence, KV head), the `budget` largest
 //    keys by a radix select (11-bit digits from the highest bit where keys
 //    differ, stopping once a digit's bin is kept whole) over the keys held
@@ -97,30 +95,14 @@ __device__ __forceinline__ uint64_t order_key(double x) {
 // heads repeat the last one, so the largest score over them is unchanged.
 __host__ __device__ constexpr int padded_group(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
 
-// The query parts of one (sequence, KV head) as doubles: value f = d * 2GP
-// + j (j < GP: q+ = max(q, 0) of head j; j >= GP: q- = min(q, 0) of head
-// j - GP; both exact) is entry f % 16 of register pair f / 16 of a 16-lane
-// row.  Pairs are stored two at a time per row position: pair v, position
-// n at byte ((v / 2) * 16 + n) * 16 + (v % 2) * 8, so that lane n of a row
-// reads pairs v and v + 1 with one 16-byte load.
+// The query parts of one (sequence, KV head) as doubles in LDS: value f =
+// d * 2GP + j (j < GP: q+ = max(q, 0) of head j; j >= GP: q- = min(q, 0)
+// of head j - GP; both exact) is entry f % 16 of register pair f / 16 of a
+// 16-lane row.  Pairs are stored two at a time per row position: pair v,
+// position n at byte ((v / 2) * 16 + n) * 16 + (v % 2) * 8, so that lane n
+// of a row reads pairs v and v + 1 with one 16-byte load.
 __host__ __device__ constexpr int quest_q_bytes(int D, int GP) { return D * 2 * GP * 8; }
-__device__ __forceinline__ int quest_q_offset(int f) { return (((f >> 5) * 16 + (f & 15)) * 16 + ((f >> 4) & 1) * 8) / 8; }
-
-// grid (S * Hkv), 256 threads: the query parts of each (sequence, KV head)
-// in the layout above, qd + (s * Hkv + kvh) * quest_q_bytes(D, GP).
-template <typename T>
-__global__ __launch_bounds__(256) void quest_qprep_kernel(const uint16_t* __restrict__ query, int Hq, int Hkv, int D,
-                                                          int GP, double* __restrict__ qd) {
-  const int sk = blockIdx.x, s = sk / Hkv, kvh = sk - s * Hkv;
-  const int G = Hq / Hkv;
-  double* o = qd + (size_t)sk * quest_q_bytes(D, GP) / 8;
-  for (int f = threadIdx.x; f < D * 2 * GP; f += 256) {
-    const int d = f / (2 * GP), j = f - d * 2 * GP;
-    const int g = j < GP ? j : j - GP;
-    const float x = ld16<T>(query, ((size_t)s * Hq + kvh * G + min(g, G - 1)) * D + d);
-    o[quest_q_offset(f)] = j < GP ? (x > 0.f ? (double)x : 0.0) : (x < 0.f ? (double)x : 0.0);
-  }
-}
+__device__ __forceinline__ int quest_q_offset(int f) { return ((f >> 5) * 16 + (f & 15)) * 16 + ((f >> 4) & 1) * 8; }
 
 // acc[i] += (entry B + i of q's row) * x for i < N: v_fmac_f64 with a DPP
 // row broadcast of its first operand.  The leading s_nop covers the two
@@ -179,16 +161,9 @@ __device__ __forceinline__ void fmac_row_bcast(double* acc, double q, double x) 
   else fmac_row_bcast8<B>(acc, q, x);
 }
 
-constexpr int kScorePages = 64;                                  // pages per scoring wave: one per lane
-constexpr int kScoreWaves = 4;                                   // waves per scoring workgroup
-constexpr int kScoreDims = 32;                                   // dimensions per stage
-constexpr int kScoreStage = kScorePages * 2 * kScoreDims * 2;    // (minimum, maximum) x 16 bits: 8 KiB
-
-// Position of a page's 16-byte units in a stage: page p's unit u sits at
-// p * 128 + 16 * (u ^ swz(p)).  Any 8 lanes reading unit u of pages p..p+7
-// (or 16 lanes, of pages p..p+15 with p a multiple of 16) meet distinct
-// 16-byte bank groups.
-__device__ __forceinline__ int score_swz(int p) { return (p ^ (p >> 3)) & 7; }
+constexpr int kScorePages = 64;   // pages per scoring wave: one per lane
+constexpr int kScoreWaves = 4;    // waves per scoring workgroup
+constexpr int kScoreDims = 32;    // dimensions per stage
 
 template <typename T>
 __device__ __forceinline__ double cvt_d(uint32_t w, int upper) {
@@ -198,9 +173,9 @@ __device__ __forceinline__ double cvt_d(uint32_t w, int upper) {
     return (double)f16_to_f32((uint16_t)(upper ? w >> 16 : w));
 }
 
-// The 2 * GP products of dimension d (dim: its index within the head) into
-// ap (q+ * maximum) and an (q- * minimum); qv: the register pairs of the
-// stage's query parts, pair v at qv[v - v0].
+// The 2 * GP products of dimension `dim` into ap (q+ * maximum) and an
+// (q- * minimum); qv: the register pairs of the stage's query parts, pair
+// v at qv[v - v0].
 template <int GP>
 __device__ __forceinline__ void score_dim(double* ap, double* an, const double* qv, int v0, int dim, double mx,
                                           double mn);
@@ -208,75 +183,71 @@ __device__ __forceinline__ void score_dim(double* ap, double* an, const double* 
 // grid (S * Hkv, ceil(mbs / 256)), 4 waves: lane i of wave w scores page
 // lb0 + 64 w + i.  With q+ = max(q, 0) and q- = min(q, 0), max(q * min, q *
 // max) = q+ * max + q- * min (min <= max), so a head's score is two fp64
-// dot products of exact products.  The query parts are copied once into
-// LDS and reach the FMAs by DPP row broadcasts; the summaries are taken 32
-// dimensions at a time: the wave's 64 pages' minima and maxima of a stage
-// (8 KiB) are copied by 8 direct-to-LDS loads of 8 pages each, two stages
-// in flight.
+// dot products of exact products.  The workgroup first writes its query
+// group's parts to LDS (layout above); they reach the FMAs by DPP row
+// broadcasts.  Each lane reads its own page's minima and maxima, 32
+// dimensions (128 bytes) a stage, two stages in flight.
 template <typename T, int D, int GP>
-__global__ __launch_bounds__(64 * kScoreWaves) void quest_score_kernel(const double* __restrict__ qd,
+__global__ __launch_bounds__(64 * kScoreWaves) void quest_score_kernel(const uint16_t* __restrict__ query,
                                                                        const uint16_t* __restrict__ summ,
                                                                        const int32_t* __restrict__ bt, int mbs,
                                                                        const int32_t* __restrict__ lens,
-                                                                       int num_blocks, int Hkv,
+                                                                       int num_blocks, int Hq, int Hkv,
                                                                        uint64_t* __restrict__ keys) {
   constexpr int NST = D / kScoreDims;
-  constexpr int QB = quest_q_bytes(D, GP);
   constexpr int PPS = kScoreDims * 2 * GP / 16;   // register pairs of query parts per stage
-  __shared__ __attribute__((aligned(16))) uint8_t qs[QB];
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[kScoreWaves][kScoreStage], stage1[kScoreWaves][kScoreStage];
+  constexpr int QPIECES = GP * D / 8;             // 8-dimension pieces of the (padded) query group
+  static_assert(NST >= 2 && QPIECES <= 64 * kScoreWaves, "shape");
+  __shared__ __attribute__((aligned(16))) uint8_t qs[quest_q_bytes(D, GP)];
   const int sk = blockIdx.x, s = sk / Hkv, kvh = sk - s * Hkv;
   const int L = clamp_len_q(lens[s], mbs);
   const int nb = (L + kBS - 1) / kBS;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lb0 = (blockIdx.y * kScoreWaves + wave) * kScorePages;
   if (blockIdx.y * kScoreWaves * kScorePages >= nb) return;
+  // thread t < QPIECES: dimensions 8 (t % (D / 8)) .. +7 of (padded) head
+  // t / (D / 8); heads past the group repeat its last one
+  const int G = Hq / Hkv;
+  const int qg = threadIdx.x / (D / 8), qd8 = threadIdx.x % (D / 8);
+  uint4 qraw = make_uint4(0, 0, 0, 0);
+  if (threadIdx.x < QPIECES)
+    qraw = *reinterpret_cast<const uint4*>(query + ((size_t)s * Hq + kvh * G + min(qg, G - 1)) * D + 8 * qd8);
+  // a wave past the last page scores copies of it (nothing is stored)
   const int pb = table_pb(bt, mbs, s, min(lb0 + lane, nb - 1), num_blocks);
-  // load k of a stage: lane i copies unit (i % 8) ^ swz(p) of page p = 8k + i / 8
-  // (units 0-3: minima of the stage's dimensions, 4-7: maxima)
-  const uint16_t* src[8];
+  if (threadIdx.x < QPIECES) {
+    const uint32_t w[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int p = 8 * k + (lane >> 3);
-    const int pbk = __shfl(pb, p, 64);
-    const int u = (lane & 7) ^ score_swz(p);
-    src[k] = summ + ((size_t)pbk * Hkv + kvh) * 2 * D + (u >= 4 ? D : 0) + 8 * (u & 3);
-  }
-  // the query parts: QB / 1024 direct-to-LDS loads shared by the waves, the
-  // same count in every wave (below 4 KiB some pieces are loaded twice, with
-  // the same bytes)
-  {
-    constexpr int NQ = QB / 1024, NQW = NQ >= kScoreWaves ? NQ / kScoreWaves : 1;
-    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(qd) + (size_t)sk * QB;
-#pragma unroll
-    for (int i = 0; i < NQW; ++i) {
-      const int k = (wave + kScoreWaves * i) % NQ;
-      __builtin_amdgcn_global_load_lds((const void*)(qsrc + k * 1024 + lane * 16),
-                                       (__attribute__((address_space(3))) void*)(qs + k * 1024), 16, 0, 0);
+    for (int e = 0; e < 8; ++e) {
+      const double x = cvt_d<T>(w[e >> 1], e & 1);
+      const int f = (8 * qd8 + e) * 2 * GP + qg;
+      *reinterpret_cast<double*>(qs + quest_q_offset(f)) = x > 0.0 ? x : 0.0;
+      *reinterpret_cast<double*>(qs + quest_q_offset(f + GP)) = x < 0.0 ? x : 0.0;
     }
   }
-  uint8_t* buf0 = stage0[wave];
-  uint8_t* buf1 = stage1[wave];
-  // a wave past the last page scores copies of it (nothing is stored)
-  auto issue = [&](uint8_t* buf, int st) {
+  const uint4* pmin = reinterpret_cast<const uint4*>(summ + ((size_t)pb * Hkv + kvh) * 2 * D);
+  const uint4* pmax = pmin + D / 8;
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 ra[8], rb[8];   // a stage: minima of its 32 dimensions, then maxima
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      __builtin_amdgcn_global_load_lds((const void*)(src[k] + st * kScoreDims),
-                                       (__attribute__((address_space(3))) void*)(buf + k * 1024), 16, 0, 0);
-  };
-  issue(buf0, 0);
-  if constexpr (NST > 1) issue(buf1, 1);
-  // the wave's own query loads are the oldest: vmcnt(16) leaves only the
-  // stage loads outstanding; after the barrier every wave's copies are in LDS
-  static_assert(NST > 1, "two stages in flight");
-  __builtin_amdgcn_s_waitcnt(0x4070);   // vmcnt(16), lgkmcnt(0)
+  for (int c = 0; c < 4; ++c) {
+    ra[c] = pmin[c];
+    ra[4 + c] = pmax[c];
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    rb[c] = pmin[4 + c];
+    rb[4 + c] = pmax[4 + c];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // lgkmcnt(0): this wave's query stores are done (the stage loads stay in
+  // flight; __syncthreads() would wait for them too)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("s_barrier" ::: "memory");
-  const int xr = (lane * 128) | (score_swz(lane) << 4);   // unit u of this lane's page: xr ^ (u << 4)
-  const int qrow = (lane & 15) * 16;                       // this lane's row position in qs
+  const int qrow = (lane & 15) * 16;   // this lane's row position in qs
   double ap[GP], an[GP];
 #pragma unroll
   for (int h = 0; h < GP; ++h) ap[h] = an[h] = 0.0;
-  auto compute = [&](const uint8_t* buf, int st) {
+  auto compute = [&](const uint4* r, int st) {
     double qv[PPS];
 #pragma unroll
     for (int i = 0; i < PPS; i += 2) {
@@ -286,9 +257,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void quest_score_kernel(const dou
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 mnv = *reinterpret_cast<const uint4*>(buf + (xr ^ (c << 4)));
-      const uint4 mxv = *reinterpret_cast<const uint4*>(buf + (xr ^ ((4 + c) << 4)));
-      const uint32_t mnw[4] = {mnv.x, mnv.y, mnv.z, mnv.w}, mxw[4] = {mxv.x, mxv.y, mxv.z, mxv.w};
+      const uint32_t mnw[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
+      const uint32_t mxw[4] = {r[4 + c].x, r[4 + c].y, r[4 + c].z, r[4 + c].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         score_dim<GP>(ap, an, qv, st * PPS, st * kScoreDims + 8 * c + e, cvt_d<T>(mxw[e >> 1], e & 1),
@@ -297,15 +267,17 @@ __global__ __launch_bounds__(64 * kScoreWaves) void quest_score_kernel(const dou
   };
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
-    // s_waitcnt vmcnt(8) while the next stage is still in flight, else
-    // vmcnt(0) (lgkmcnt(0), expcnt left alone)
-    if (st + 1 < NST) __builtin_amdgcn_s_waitcnt(0x0078);
-    else __builtin_amdgcn_s_waitcnt(0x0070);
-    compute((st & 1) ? buf1 : buf0, st);
+    compute((st & 1) ? rb : ra, st);
+    __builtin_amdgcn_sched_barrier(0);
     if (st + 2 < NST) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this stage's LDS reads are done
-      issue((st & 1) ? buf1 : buf0, st + 2);
+      uint4* r = (st & 1) ? rb : ra;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        r[c] = pmin[4 * (st + 2) + c];
+        r[4 + c] = pmax[4 * (st + 2) + c];
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   double best = ap[0] + an[0];
 #pragma unroll
@@ -530,19 +502,12 @@ int launch_quest_select(const void* query, int q_dtype, const void* k_summary, c
   auto q = reinterpret_cast<const uint16_t*>(query);
   auto sm = reinterpret_cast<const uint16_t*>(k_summary);
   auto keys = reinterpret_cast<uint64_t*>(scratch);
-  // the query halves follow the keys (pkv_quest_scratch_bytes reserves both)
-  auto qd = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(scratch) +
-                                      quest_keys_bytes(num_seqs, num_kv_heads, max_blocks_per_seq));
   const int GP = padded_group(num_q_heads / num_kv_heads);
-  if (q_dtype == PKV_BF16)
-    quest_qprep_kernel<BF16><<<num_seqs * num_kv_heads, 256, 0, st>>>(q, num_q_heads, num_kv_heads, head_dim, GP, qd);
-  else
-    quest_qprep_kernel<F16><<<num_seqs * num_kv_heads, 256, 0, st>>>(q, num_q_heads, num_kv_heads, head_dim, GP, qd);
   constexpr int kWgPages = kScorePages * kScoreWaves;
   const dim3 sgrid(num_seqs * num_kv_heads, (max_blocks_per_seq + kWgPages - 1) / kWgPages);
 #define PKV_SCORE(T, D, G)                                                                              \
-  quest_score_kernel<T, D, G><<<sgrid, 64 * kScoreWaves, 0, st>>>(qd, sm, block_tables, max_blocks_per_seq, \
-                                                                  seq_lens, num_blocks, num_kv_heads, keys)
+  quest_score_kernel<T, D, G><<<sgrid, 64 * kScoreWaves, 0, st>>>(q, sm, block_tables, max_blocks_per_seq, \
+                                                                  seq_lens, num_blocks, num_q_heads, num_kv_heads, keys)
 #define PKV_SCORE_G(T, D)              \
   switch (GP) {                        \
     case 1: PKV_SCORE(T, D, 1); break; \
