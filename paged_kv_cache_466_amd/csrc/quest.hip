@@ -95,12 +95,15 @@ __device__ __forceinline__ uint64_t order_key(double x) {
 // heads repeat the last one, so the largest score over them is unchanged.
 __host__ __device__ constexpr int padded_group(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
 
-// The query parts of one (sequence, KV head) as doubles in LDS: value f =
-// d * 2GP + j (j < GP: q+ = max(q, 0) of head j; j >= GP: q- = min(q, 0)
-// of head j - GP; both exact) is entry f % 16 of register pair f / 16 of a
-// 16-lane row.  Pairs are stored two at a time per row position: pair v,
-// position n at byte ((v / 2) * 16 + n) * 16 + (v % 2) * 8, so that lane n
-// of a row reads pairs v and v + 1 with one 16-byte load.
+// The query parts of one (sequence, KV head) as doubles in LDS, in the
+// order the scoring stages use them: stage st pairs the minima (st even,
+// with q- = min(q, 0)) or the maxima (st odd, with q+ = max(q, 0)) of
+// dimensions 64 (st / 2) .. +63 with the parts of all GP (padded) heads;
+// value f = st * 64 GP + i GP + g (dimension 64 (st / 2) + i, head g, both
+// parts exact) is entry f % 16 of register pair f / 16 of a 16-lane row.
+// Pairs are stored two at a time per row position: pair v, position n at
+// byte ((v / 2) * 16 + n) * 16 + (v % 2) * 8, so that lane n of a row
+// reads pairs v and v + 1 with one 16-byte load.
 __host__ __device__ constexpr int quest_q_bytes(int D, int GP) { return D * 2 * GP * 8; }
 __device__ __forceinline__ int quest_q_offset(int f) { return ((f >> 5) * 16 + (f & 15)) * 16 + ((f >> 4) & 1) * 8; }
 
@@ -163,7 +166,7 @@ __device__ __forceinline__ void fmac_row_bcast(double* acc, double q, double x) 
 
 constexpr int kScorePages = 64;   // pages per scoring wave: one per lane
 constexpr int kScoreWaves = 4;    // waves per scoring workgroup
-constexpr int kScoreDims = 32;    // dimensions per stage
+constexpr int kScoreStageDims = 64;   // dimensions of a stage (one 128-byte line of minima or maxima)
 
 template <typename T>
 __device__ __forceinline__ double cvt_d(uint32_t w, int upper) {
@@ -173,20 +176,38 @@ __device__ __forceinline__ double cvt_d(uint32_t w, int upper) {
     return (double)f16_to_f32((uint16_t)(upper ? w >> 16 : w));
 }
 
-// The 2 * GP products of dimension `dim` into ap (q+ * maximum) and an
-// (q- * minimum); qv: the register pairs of the stage's query parts, pair
-// v at qv[v - v0].
+// acc[g] += (part of head g for dimension i) * x for the GP heads; qv: the
+// register pairs of query parts from the one holding dimension 0 on.
 template <int GP>
-__device__ __forceinline__ void score_dim(double* ap, double* an, const double* qv, int v0, int dim, double mx,
-                                          double mn);
+__device__ __forceinline__ void score_dim(double* acc, const double* qv, int i, double x) {
+  if constexpr (GP == 16) {
+    fmac_row_bcast<8, 0>(acc, qv[i], x);
+    fmac_row_bcast<8, 8>(acc + 8, qv[i], x);
+  } else {
+    constexpr int PER = 16 / GP;   // dimensions per register pair
+    const double q = qv[i / PER];
+    switch (i % PER) {   // a constant after unrolling
+#define PKV_SCORE_DIM(R)                                        \
+  case R:                                                       \
+    if constexpr (R < PER) fmac_row_bcast<GP, R * GP>(acc, q, x); \
+    break;
+      PKV_SCORE_DIM(0) PKV_SCORE_DIM(1) PKV_SCORE_DIM(2) PKV_SCORE_DIM(3)
+      PKV_SCORE_DIM(4) PKV_SCORE_DIM(5) PKV_SCORE_DIM(6) PKV_SCORE_DIM(7)
+      PKV_SCORE_DIM(8) PKV_SCORE_DIM(9) PKV_SCORE_DIM(10) PKV_SCORE_DIM(11)
+      PKV_SCORE_DIM(12) PKV_SCORE_DIM(13) PKV_SCORE_DIM(14) PKV_SCORE_DIM(15)
+#undef PKV_SCORE_DIM
+    }
+  }
+}
 
 // grid (S * Hkv, ceil(mbs / 256)), 4 waves: lane i of wave w scores page
 // lb0 + 64 w + i.  With q+ = max(q, 0) and q- = min(q, 0), max(q * min, q *
 // max) = q+ * max + q- * min (min <= max), so a head's score is two fp64
-// dot products of exact products.  The workgroup first writes its query
-// group's parts to LDS (layout above); they reach the FMAs by DPP row
-// broadcasts.  Each lane reads its own page's minima and maxima, 32
-// dimensions (128 bytes) a stage, two stages in flight.
+// dot products of exact products, one over the page's minima and one over
+// its maxima.  The workgroup first writes its query group's parts to LDS
+// (layout above); they reach the FMAs by DPP row broadcasts.  Each lane
+// reads its own page's summary in stages of one 128-byte line (64 minima
+// or 64 maxima), two stages in flight.
 template <typename T, int D, int GP>
 __global__ __launch_bounds__(64 * kScoreWaves) void quest_score_kernel(const uint16_t* __restrict__ query,
                                                                        const uint16_t* __restrict__ summ,
@@ -194,9 +215,9 @@ __global__ __launch_bounds__(64 * kScoreWaves) void quest_score_kernel(const uin
                                                                        const int32_t* __restrict__ lens,
                                                                        int num_blocks, int Hq, int Hkv,
                                                                        uint64_t* __restrict__ keys) {
-  constexpr int NST = D / kScoreDims;
-  constexpr int PPS = kScoreDims * 2 * GP / 16;   // register pairs of query parts per stage
-  constexpr int QPIECES = GP * D / 8;             // 8-dimension pieces of the (padded) query group
+  constexpr int NST = 2 * D / kScoreStageDims;     // stages: minima and maxima of each 64 dimensions
+  constexpr int PPS = kScoreStageDims * GP / 16;   // register pairs of query parts per stage
+  constexpr int QPIECES = GP * D / 8;              // 8-dimension pieces of the (padded) query group
   static_assert(NST >= 2 && QPIECES <= 64 * kScoreWaves, "shape");
   __shared__ __attribute__((aligned(16))) uint8_t qs[quest_q_bytes(D, GP)];
   const int sk = blockIdx.x, s = sk / Hkv, kvh = sk - s * Hkv;
@@ -219,98 +240,68 @@ __global__ __launch_bounds__(64 * kScoreWaves) void quest_score_kernel(const uin
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const double x = cvt_d<T>(w[e >> 1], e & 1);
-      const int f = (8 * qd8 + e) * 2 * GP + qg;
-      *reinterpret_cast<double*>(qs + quest_q_offset(f)) = x > 0.0 ? x : 0.0;
-      *reinterpret_cast<double*>(qs + quest_q_offset(f + GP)) = x < 0.0 ? x : 0.0;
+      const int d = 8 * qd8 + e;
+      const int fmin = 2 * (d / kScoreStageDims) * kScoreStageDims * GP + (d % kScoreStageDims) * GP + qg;
+      *reinterpret_cast<double*>(qs + quest_q_offset(fmin)) = x < 0.0 ? x : 0.0;
+      *reinterpret_cast<double*>(qs + quest_q_offset(fmin + kScoreStageDims * GP)) = x > 0.0 ? x : 0.0;
     }
   }
-  const uint4* pmin = reinterpret_cast<const uint4*>(summ + ((size_t)pb * Hkv + kvh) * 2 * D);
-  const uint4* pmax = pmin + D / 8;
+  // stage st: 8 pieces of 16 bytes of the minima (st even) or maxima (st odd)
+  const uint4* page = reinterpret_cast<const uint4*>(summ + ((size_t)pb * Hkv + kvh) * 2 * D);
+  auto piece = [&](int st, int c) { return page[(st & 1) * (D / 8) + (st >> 1) * 8 + c]; };
   __builtin_amdgcn_sched_barrier(0);
-  uint4 ra[8], rb[8];   // a stage: minima of its 32 dimensions, then maxima
+  uint4 ra[8], rb[8];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    ra[c] = pmin[c];
-    ra[4 + c] = pmax[c];
-  }
+  for (int c = 0; c < 8; ++c) ra[c] = piece(0, c);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    rb[c] = pmin[4 + c];
-    rb[4 + c] = pmax[4 + c];
-  }
+  for (int c = 0; c < 8; ++c) rb[c] = piece(1, c);
   __builtin_amdgcn_sched_barrier(0);
   // lgkmcnt(0): this wave's query stores are done (the stage loads stay in
   // flight; __syncthreads() would wait for them too)
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("s_barrier" ::: "memory");
   const int qrow = (lane & 15) * 16;   // this lane's row position in qs
-  double ap[GP], an[GP];
+  // one sum per head over both parts (every product is exact, so the order
+  // of the additions does not change it)
+  double acc[GP];
 #pragma unroll
-  for (int h = 0; h < GP; ++h) ap[h] = an[h] = 0.0;
-  auto compute = [&](const uint4* r, int st) {
-    double qv[PPS];
-#pragma unroll
-    for (int i = 0; i < PPS; i += 2) {
-      const double2 t = *reinterpret_cast<const double2*>(qs + ((st * PPS + i) / 2) * 256 + qrow);
-      qv[i] = t.x;
-      qv[i + 1] = t.y;
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t mnw[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
-      const uint32_t mxw[4] = {r[4 + c].x, r[4 + c].y, r[4 + c].z, r[4 + c].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        score_dim<GP>(ap, an, qv, st * PPS, st * kScoreDims + 8 * c + e, cvt_d<T>(mxw[e >> 1], e & 1),
-                      cvt_d<T>(mnw[e >> 1], e & 1));
-    }
-  };
+  for (int h = 0; h < GP; ++h) acc[h] = 0.0;
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
-    compute((st & 1) ? rb : ra, st);
-    __builtin_amdgcn_sched_barrier(0);
-    if (st + 2 < NST) {
-      uint4* r = (st & 1) ? rb : ra;
+    const uint4* r = (st & 1) ? rb : ra;
+    // the stage's query parts half at a time (32 dimensions), so that four
+    // waves fit on a SIMD
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      constexpr int HP = PPS / 2;   // register pairs per half stage
+      double qv[HP];
+#pragma unroll
+      for (int i = 0; i < HP; i += 2) {
+        const double2 t = *reinterpret_cast<const double2*>(qs + ((st * PPS + half * HP + i) / 2) * 256 + qrow);
+        qv[i] = t.x;
+        qv[i + 1] = t.y;
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        r[c] = pmin[4 * (st + 2) + c];
-        r[4 + c] = pmax[4 * (st + 2) + c];
+        const uint4 p4 = r[4 * half + c];
+        const uint32_t w[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) score_dim<GP>(acc, qv, 8 * c + e, cvt_d<T>(w[e >> 1], e & 1));
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the next stage into this stage's registers (kept in this order)
+    if (st + 2 < NST) {
+      uint4* rr = (st & 1) ? rb : ra;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) rr[c] = piece(st + 2, c);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  double best = ap[0] + an[0];
+  double best = acc[0];
 #pragma unroll
-  for (int h = 1; h < GP; ++h) best = fmax(best, ap[h] + an[h]);
+  for (int h = 1; h < GP; ++h) best = fmax(best, acc[h]);
   if (lb0 + lane < nb) keys[(size_t)sk * mbs + lb0 + lane] = order_key(best);
-}
-
-// value f = dim * 2GP + j sits at entry f % 16 of pair f / 16
-template <int GP>
-__device__ __forceinline__ void score_dim(double* ap, double* an, const double* qv, int v0, int dim, double mx,
-                                          double mn) {
-  if constexpr (GP == 16) {
-    const double qp = qv[2 * dim - v0], qn = qv[2 * dim + 1 - v0];
-    fmac_row_bcast<8, 0>(ap, qp, mx);
-    fmac_row_bcast<8, 8>(ap + 8, qp, mx);
-    fmac_row_bcast<8, 0>(an, qn, mn);
-    fmac_row_bcast<8, 8>(an + 8, qn, mn);
-  } else {
-    constexpr int PER = 16 / (2 * GP);   // dimensions per pair
-    const double q = qv[dim / PER - v0];
-    switch (dim % PER) {   // a constant after unrolling
-#define PKV_SCORE_DIM(R)                                   \
-  case R:                                                  \
-    if constexpr (R < PER) {                               \
-      fmac_row_bcast<GP, R * 2 * GP>(ap, q, mx);           \
-      fmac_row_bcast<GP, R * 2 * GP + GP>(an, q, mn);      \
-    }                                                      \
-    break;
-      PKV_SCORE_DIM(0) PKV_SCORE_DIM(1) PKV_SCORE_DIM(2) PKV_SCORE_DIM(3)
-      PKV_SCORE_DIM(4) PKV_SCORE_DIM(5) PKV_SCORE_DIM(6) PKV_SCORE_DIM(7)
-#undef PKV_SCORE_DIM
-    }
-  }
 }
 
 constexpr int kSelThreads = 1024;   // threads of a selection workgroup (16 waves)

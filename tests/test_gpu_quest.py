@@ -215,3 +215,29 @@ def test_ties_at_the_cut_keep_the_lower_pages():
         for (s, h), sc in scores.items():
             want = quest.select_pages(sc, budget)
             assert sel[s, h, :len(want), 1].tolist() == want, (budget, s, h)
+
+
+@pytest.mark.parametrize("budget", [100, 5000])
+def test_long_table_keys_from_global_memory(budget):
+    """A block table wider than 16384 blocks: the selection reads its keys
+    from global memory instead of LDS.  One sequence of 16500 pages with
+    random stored summaries, against the oracle's ranking of them."""
+    import paged_kv_cache_466_amd as pkv
+    g = torch.Generator().manual_seed(7)
+    S, Hq, Hkv, D, nbk, mbs = 1, 8, 1, 64, 16500, 16600
+    print(f"[quest] long table S={S} Hq={Hq} Hkv={Hkv} D={D} pages={nbk} width={mbs} budget={budget}", flush=True)
+    a = torch.randn(nbk, Hkv, D, generator=g).to(torch.bfloat16)
+    b = torch.randn(nbk, Hkv, D, generator=g).to(torch.bfloat16)
+    summ = torch.stack([torch.minimum(a, b), torch.maximum(a, b)], dim=2).contiguous()
+    perm = torch.randperm(nbk, generator=g).to(torch.int32)
+    bt = torch.zeros(S, mbs, dtype=torch.int32)
+    bt[0, :nbk] = perm
+    lens = torch.tensor([nbk * 16 - 5], dtype=torch.int32)
+    q = torch.randn(S, Hq, D, generator=g).to(torch.bfloat16)
+    sel = pkv.quest_select(q.cuda(), summ.cuda(), bt.cuda(), lens.cuda(), budget).cpu().numpy()
+    qf = q.float().numpy().astype(np.float64)
+    sf = summ.float().numpy().astype(np.float64)
+    scores = [quest.group_page_score(qf[0], sf[int(perm[lb]), 0, 0], sf[int(perm[lb]), 0, 1]) for lb in range(nbk)]
+    want = quest.select_pages(scores, budget)
+    assert sel[0, 0, :, 1].tolist() == want
+    assert sel[0, 0, :, 0].tolist() == [int(perm[lb]) for lb in want]
