@@ -23,7 +23,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Compute units of the current device (256 when none can be queried, e.g.
 // on a host without a GPU, so that sizes computed there match MI355X).
-static int device_cu_count() {
+int device_cu_count() {
   static int cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
@@ -41,9 +41,10 @@ static int device_cu_count() {
   return cache[dev];
 }
 
-int decode_slots(int num_seqs, int num_kv_heads, int num_partitions, int partition_size) {
+int decode_slots(int num_seqs, int num_kv_heads, int num_partitions, int partition_size, int cus) {
   constexpr int kWavesPerCU = 8;   // two waves per SIMD: the wave kernel's register budget
-  long long k = ((long long)kWavesPerCU * device_cu_count() + num_kv_heads - 1) / num_kv_heads;
+  if (cus <= 0) cus = device_cu_count();
+  long long k = ((long long)kWavesPerCU * cus + num_kv_heads - 1) / num_kv_heads;
   if (k < num_seqs) k = num_seqs;
   // a workgroup takes at most ceil(units / k) partitions (or the minimum),
   // or, when the split balances blocks, its share of the blocks plus up to
@@ -591,13 +592,22 @@ extern "C" pkv_status pkv_paged_attn_decode_shared_prefix(
     st = pkv_validate_shared_prefix(bt.data(), max_blocks_per_seq, sl.data(), num_seqs, block_size, prefix_blocks);
     if (st != PKV_OK) return st;
   }
-  // the shared blocks are sequence 0's first prefix_blocks entries
-  st = hip_status(launch_prefix_attn(query, q_dtype, k_cache, v_cache, block_tables, prefix_blocks,
-                                     (float*)workspace, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
-                                     sm_scale, stream),
-                  who);
-  if (st != PKV_OK) return st;
-  st = hip_status(launch_paged_attn_partition(a), who);
+  // The shared blocks are sequence 0's first prefix_blocks entries.  The
+  // prefix items run in the decode's own launch, on workgroups dispatched
+  // after its slots, in the compute units its workgroups leave; without
+  // four waves per workgroup (fewer than 4 KV heads) the prefix pass runs
+  // first on its own.
+  const int pfx_wgs = prefix_workgroups(num_seqs, num_q_heads, num_kv_heads, device_cu_count());
+  if (pfx_wgs > 0) {
+    st = hip_status(launch_shared_prefix_decode(a, block_tables, prefix_blocks, (float*)workspace, pfx_wgs), who);
+  } else {
+    st = hip_status(launch_prefix_attn(query, q_dtype, k_cache, v_cache, block_tables, prefix_blocks,
+                                       (float*)workspace, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                                       sm_scale, stream),
+                    who);
+    if (st != PKV_OK) return st;
+    st = hip_status(launch_paged_attn_partition(a), who);
+  }
   if (st != PKV_OK) return st;
   return hip_status(launch_paged_attn_merge(a), who);
 }

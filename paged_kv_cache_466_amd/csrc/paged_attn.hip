@@ -49,6 +49,28 @@ namespace pkv {
 constexpr int kBS = 16;                     // tokens per block
 constexpr float kLog2e = 1.4426950408889634f;
 
+constexpr int kPrefixWaves = 4;                // waves of a prefix item
+constexpr int kPrefixCG = 2;                  // 16-row column groups per wave
+constexpr int kPrefixRows = 16 * kPrefixCG;   // rows of a workgroup (every wave takes all of them)
+constexpr int kPrefixTable = 2048;            // shared-block entries staged in LDS at a time
+
+template <int D>
+__host__ __device__ constexpr int prefix_lds_bytes() {
+  return kPrefixWaves * kBS * (2 * D + 16) + kPrefixTable * 4 + kPrefixWaves * kPrefixRows * (D + 4) * 4;
+}
+
+// Shared-prefix pass: see prefix_attn_kernel.
+struct PrefixParams {
+  const void* query;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* table;   // the shared physical blocks, in logical order
+  float* rec;             // [S][Hq][D + 4]
+  int num_prefix_blocks, num_seqs, num_q_heads, num_kv_heads, num_blocks;
+  float scale_log2;
+  int items;              // (32-row tile, KV head) items: row tiles x num_kv_heads
+};
+
 struct AttnParams {
   void* out;
   const void* query;
@@ -88,6 +110,10 @@ struct AttnParams {
   int len_off;
   float* srec;
   float scale_log2;     // sm_scale * log2(e)
+  // combined shared-prefix launch: the first pfx_wgs workgroups along x
+  // take the prefix items of pfx, the decode's workgroup slots follow them
+  int pfx_wgs;
+  PrefixParams pfx;
 };
 
 __device__ __forceinline__ int clamp_len(int L, int mbs) {
@@ -344,7 +370,7 @@ __host__ __device__ constexpr int wave_group_lds(int vstage, int waves, int list
 // record goes to slot 2w + 1 (bit 1) and whether it is the whole sequence
 // (bit 0).  Also zeroes an empty sequence's output and writes the plan
 // entries of the sequences that start here.
-template <bool SEL>
+template <bool SEL, bool PFX>
 __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_dim, int lane, int4* list, int* segs,
                                                  int* counts, int* ends) {
   const int S = p.num_seqs;
@@ -379,7 +405,8 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
   for (int s0 = 64; s0 < S; s0 += 64) U += load_window<SEL>(p, s0, U, lane, weighted).total;
   int nb = 0, nseg = 0, nend = 0;
   if (U > 0) {
-    const int K = gridDim.x;
+    // a combined launch's prefix workgroups follow the decode's slots
+    const int K = PFX ? (int)gridDim.x - p.pfx_wgs : (int)gridDim.x;
     int k_eff;
     if (weighted) {
       // every run at least one unit long (so that every workgroup between a
@@ -467,9 +494,26 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
   }
 }
 
-template <typename QT, typename KVT, int D, bool STREAM, bool SEL, bool GRP>
+template <typename QT, int D, int DEPTH>
+__device__ __forceinline__ void prefix_item(const PrefixParams& p, int item);
+
+// PFX: the combined shared-prefix launch.  The last pfx_wgs workgroups
+// along x take the prefix items (prefix_item, on their first four waves,
+// items strided over all of them).  They are dispatched after every decode
+// slot, so they take the compute units the decode's workgroups leave.
+template <typename QT, typename KVT, int D, bool STREAM, bool SEL, bool GRP, bool PFX = false>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_attn_wave_kernel(AttnParams p) {
+  if constexpr (PFX) {
+    const int first = (int)gridDim.x - p.pfx_wgs;
+    if ((int)blockIdx.x >= first) {
+      if (threadIdx.x >= 64 * kPrefixWaves) return;   // the barriers count the waves still running
+      const int stride = p.pfx_wgs * (int)gridDim.y;
+      for (int item = (int)blockIdx.x - first + p.pfx_wgs * (int)blockIdx.y; item < p.pfx.items; item += stride)
+        prefix_item<QT, D, 3>(p.pfx, item);   // a shorter ring: the decode's register budget
+      return;
+    }
+  }
   typedef WaveCfg<KVT, D, GRP> C;
   static_assert(!GRP || (C::kCodes && std::is_same<typename MmaType<QT, KVT>::type, F16>::value && !SEL),
                 "grouped scales are built for integer codes, without a selection");
@@ -517,7 +561,7 @@ void paged_attn_wave_kernel(AttnParams p) {
   int* counts = segs + kMaxQuerySegs;
   int* ends = counts + 4;
 
-  if (wave == 0) build_block_list<SEL>(p, D, lane, list, segs, counts, ends);
+  if (wave == 0) build_block_list<SEL, PFX>(p, D, lane, list, segs, counts, ends);
   __syncthreads();
   if (kvh >= p.num_kv_heads) return;
   const int nb = __builtin_amdgcn_readfirstlane(counts[0]);
@@ -1353,28 +1397,12 @@ __global__ __launch_bounds__(256) void paged_attn_merge_units_kernel(void* out, 
 // query head): acc[D] (unnormalised), m (log2 domain), l.  The suffix decode
 // folds these records into its own results.
 // ===========================================================================
-constexpr int kPrefixWaves = 4;
-constexpr int kPrefixCG = 2;                  // 16-row column groups per wave
-constexpr int kPrefixRows = 16 * kPrefixCG;   // rows of a workgroup (every wave takes all of them)
-constexpr int kPrefixTable = 2048;            // shared-block entries staged in LDS at a time
 
-template <int D>
-__host__ __device__ constexpr int prefix_lds_bytes() {
-  return kPrefixWaves * kBS * (2 * D + 16) + kPrefixTable * 4 + kPrefixWaves * kPrefixRows * (D + 4) * 4;
-}
 
-struct PrefixParams {
-  const void* query;
-  const void* k_cache;
-  const void* v_cache;
-  const int32_t* table;   // the shared physical blocks, in logical order
-  float* rec;             // [S][Hq][D + 4]
-  int num_prefix_blocks, num_seqs, num_q_heads, num_kv_heads, num_blocks;
-  float scale_log2;
-};
-
-template <typename QT, int D>
-__global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixParams p) {
+// One item: 32 rows of one KV head against every shared block, on the
+// first four waves of the workgroup, DEPTH block tiles in flight per wave.
+template <typename QT, int D, int DEPTH>
+__device__ __forceinline__ void prefix_item(const PrefixParams& p, int item) {
   typedef Mfma<QT> M;
   constexpr int NC = D / 32, NN = D / 16;
   constexpr int ROW_BYTES = 2 * D;
@@ -1382,17 +1410,16 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixPa
   constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
   constexpr int VCH = kBS / ROWS_PER_PASS;
   constexpr int VROW = 2 * D + 16;   // LDS bytes per staged V row (padded)
-  constexpr int DEPTH = 4;           // register tiles in the ring
   constexpr float kSlack = 8.0f;     // rescale only when a score passes the max by 2^8
   constexpr int RS = D + 4;          // floats per state row in LDS
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int kvh = item % p.num_kv_heads;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int nrows = p.num_seqs * G;
-  const int r0 = (blockIdx.x / p.num_kv_heads) * kPrefixRows;
+  const int r0 = (item / p.num_kv_heads) * kPrefixRows;
   const int g = lane & 15;    // column of S^T / out^T
   const int kg = lane >> 4;   // lane group: k-chunk of the operands, 4-row slab of the outputs
   uint8_t* vst = lds + wave * kBS * VROW;
@@ -1576,6 +1603,11 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixPa
 }
 
 template <typename QT, int D>
+__global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixParams p) {
+  prefix_item<QT, D, 4>(p, blockIdx.x);
+}
+
+template <typename QT, int D>
 static int launch_prefix_d(const PrefixParams& p, hipStream_t st) {
   auto kernel = prefix_attn_kernel<QT, D>;
   static std::atomic<bool> lds_set[64];
@@ -1585,6 +1617,22 @@ static int launch_prefix_d(const PrefixParams& p, hipStream_t st) {
   const dim3 grid(((p.num_seqs * G + kPrefixRows - 1) / kPrefixRows) * p.num_kv_heads);
   kernel<<<grid, 64 * kPrefixWaves, prefix_lds_bytes<D>(), st>>>(p);
   return hipGetLastError();
+}
+
+int prefix_item_count(int num_seqs, int num_q_heads, int num_kv_heads) {
+  const long long rows = (long long)num_seqs * (num_q_heads / num_kv_heads);
+  return (int)((rows + kPrefixRows - 1) / kPrefixRows) * num_kv_heads;
+}
+
+int prefix_workgroups(int num_seqs, int num_q_heads, int num_kv_heads, int cus) {
+  // the prefix role needs four waves per workgroup
+  const int per_group = wave_group_size(num_kv_heads);
+  if (per_group < kPrefixWaves) return 0;
+  const int groups = (num_kv_heads + per_group - 1) / per_group;
+  const int items = prefix_item_count(num_seqs, num_q_heads, num_kv_heads);
+  // one item per workgroup, at most one per compute unit
+  const int along_x = (items + groups - 1) / groups;
+  return along_x * groups <= cus ? along_x : 0;
 }
 
 int launch_prefix_attn(const void* query, int q_dtype, const void* k_cache, const void* v_cache,
@@ -1603,6 +1651,7 @@ int launch_prefix_attn(const void* query, int q_dtype, const void* k_cache, cons
   p.num_kv_heads = num_kv_heads;
   p.num_blocks = num_blocks;
   p.scale_log2 = sm_scale * kLog2e;
+  p.items = prefix_item_count(num_seqs, num_q_heads, num_kv_heads);
   hipStream_t st = (hipStream_t)stream;
   if (q_dtype == PKV_BF16) return head_dim == 64 ? launch_prefix_d<BF16, 64>(p, st) : launch_prefix_d<BF16, 128>(p, st);
   return head_dim == 64 ? launch_prefix_d<F16, 64>(p, st) : launch_prefix_d<F16, 128>(p, st);
@@ -1650,6 +1699,8 @@ static AttnParams make_params(const AttnArgs& a) {
   p.positions = a.positions;
   p.slots_out = a.slots_out;
   p.scale_log2 = a.sm_scale * kLog2e;
+  p.pfx_wgs = 0;
+  p.pfx = PrefixParams{};
   return p;
 }
 
@@ -1743,6 +1794,52 @@ int launch_paged_attn_partition(const AttnArgs& a) {
     case PKV_FP8E5M2: return launch_wave_d<F16, BF8>(p, K, D, stream, st);
     default: return launch_wave_d<F16, FP8>(p, K, D, stream, st);
   }
+}
+
+// The combined shared-prefix launch (16-bit caches of the query's type):
+// pfx_wgs workgroups along x of prefix items, then the decode's slots.
+template <typename QT, int D, bool STREAM>
+static int launch_wave_pfx(const AttnParams& p, int num_slots, hipStream_t st) {
+  const int per_group = wave_group_size(p.num_kv_heads);
+  const int groups = (p.num_kv_heads + per_group - 1) / per_group;
+  const int wave_lds = wave_group_lds(WaveCfg<QT, D>::VSTAGE, per_group, p.list_cap);
+  const int lds = wave_lds > prefix_lds_bytes<D>() ? wave_lds : prefix_lds_bytes<D>();
+  auto kernel = paged_attn_wave_kernel<QT, QT, D, STREAM, false, false, true>;
+  static std::atomic<bool> lds_set[64];
+  const int wmost = wave_group_lds(WaveCfg<QT, D>::VSTAGE, kMaxWavesPerGroup, 128 * kMaxWavesPerGroup);
+  const int most = wmost > prefix_lds_bytes<D>() ? wmost : prefix_lds_bytes<D>();
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kernel), most, lds_set);
+  if (e != hipSuccess) return e;
+  kernel<<<dim3(p.pfx_wgs + num_slots, groups), 64 * per_group, lds, st>>>(p);
+  return hipGetLastError();
+}
+
+int launch_shared_prefix_decode(const AttnArgs& a, const int32_t* prefix_table, int prefix_blocks, float* prefix_rec,
+                                int pfx_wgs) {
+  if (a.num_seqs == 0) return hipSuccess;
+  AttnParams p = make_params(a);
+  p.pfx_wgs = pfx_wgs;
+  p.pfx.query = a.query;
+  p.pfx.k_cache = a.k_cache;
+  p.pfx.v_cache = a.v_cache;
+  p.pfx.table = prefix_table;
+  p.pfx.rec = prefix_rec;
+  p.pfx.num_prefix_blocks = prefix_blocks;
+  p.pfx.num_seqs = a.num_seqs;
+  p.pfx.num_q_heads = a.num_q_heads;
+  p.pfx.num_kv_heads = a.num_kv_heads;
+  p.pfx.num_blocks = a.num_blocks;
+  p.pfx.scale_log2 = a.sm_scale * kLog2e;
+  p.pfx.items = prefix_item_count(a.num_seqs, a.num_q_heads, a.num_kv_heads);
+  hipStream_t st = (hipStream_t)a.stream;
+  const bool stream = (a.flags & PKV_DECODE_STREAM_KV) != 0;
+  const int K = a.num_slots;
+  if (a.q_dtype == PKV_BF16) {
+    if (a.head_dim == 64) return stream ? launch_wave_pfx<BF16, 64, true>(p, K, st) : launch_wave_pfx<BF16, 64, false>(p, K, st);
+    return stream ? launch_wave_pfx<BF16, 128, true>(p, K, st) : launch_wave_pfx<BF16, 128, false>(p, K, st);
+  }
+  if (a.head_dim == 64) return stream ? launch_wave_pfx<F16, 64, true>(p, K, st) : launch_wave_pfx<F16, 64, false>(p, K, st);
+  return stream ? launch_wave_pfx<F16, 128, true>(p, K, st) : launch_wave_pfx<F16, 128, false>(p, K, st);
 }
 
 int launch_paged_attn_merge(const AttnArgs& a) {

@@ -117,7 +117,9 @@ inline int decode_list_cap(int num_kv_heads) { return 128 * wave_group_size(num_
 // Workgroups along the sequence axis of that decode: enough to fill every
 // compute unit at two waves per SIMD, at least one per sequence, and enough
 // that no workgroup's share of the partitions exceeds its block list.
-int decode_slots(int num_seqs, int num_kv_heads, int num_partitions, int partition_size);
+// cus: compute units the decode runs on (0: all of the device's)
+int decode_slots(int num_seqs, int num_kv_heads, int num_partitions, int partition_size, int cus = 0);
+int device_cu_count();
 // Bytes at the start of the wave path's workspace that hold, per sequence,
 // the slot of its first partial record and the first and last workgroups it
 // reaches (four int32), written by the decode for the merge; the records
@@ -168,6 +170,15 @@ int launch_append_quantized(const void* key, const void* value, int src_dtype, v
                             float* k_group, float* v_group, const int32_t* block_tables, int max_blocks_per_seq,
                             const int32_t* positions, int num_seqs, int num_blocks, int num_kv_heads, int head_dim,
                             void* stream);
+// Shared-prefix decode: (32-row tile, KV head) items of the prefix pass,
+// and the prefix workgroups of a combined launch on a device of `cus`
+// compute units (0: launch the prefix pass on its own).
+int prefix_item_count(int num_seqs, int num_q_heads, int num_kv_heads);
+int prefix_workgroups(int num_seqs, int num_q_heads, int num_kv_heads, int cus);
+// The combined launch: the decode past the prefix (a.num_slots slots), then
+// pfx_wgs workgroups along x of prefix items.
+int launch_shared_prefix_decode(const AttnArgs& a, const int32_t* prefix_table, int prefix_blocks, float* prefix_rec,
+                                int pfx_wgs);
 int launch_quest_summarize(const void* k_cache, int kv_dtype, void* k_summary, const int32_t* block_tables,
                            int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs, int num_blocks,
                            int num_kv_heads, int head_dim, int last_only, void* stream);
