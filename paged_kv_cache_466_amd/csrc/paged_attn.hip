@@ -168,20 +168,27 @@ __device__ __forceinline__ uint32_t i8x2_f16(uint32_t u) {
 // Eight INT4 codes (the nibbles of w, element 2i in the low nibble of byte
 // i, two's complement) -> eight f16 values, exactly, in the interleaved order
 // (0, 4, 1, 5, 2, 6, 3, 7): the nibbles at bits s and s + 16 of w >> s
-// (s = 0, 4, 8, 12) are elements s/4 and s/4 + 4.  Masking them to the low
-// bits of each half, flipping bit 3 (u = code + 8) and setting the 0x64
-// byte is one three-input bit operation; the f16 1024 + u minus 1032 is the
-// code.  Eleven operations per eight codes (an in-order conversion needs
-// byte permutes on top); the query's elements and the staged V rows use the
-// same order.
+// (s = 0, 4, 8, 12) are elements s/4 and s/4 + 4.  With u = code + 8 (bit 3
+// of the nibble flipped), masking a pair of nibbles to bits 0-3 of each half,
+// flipping bit 3 and setting the 0x64 byte is one three-input bit operation
+// that leaves the f16 1024 + u; minus 1032 is the code.  The nibbles at bits
+// 4-7 need no shift: in place they give 1024 + 16 u, and (1024 + 16 u) / 16 -
+// 72 is the code, one packed FMA, exact.  Nine operations per eight codes;
+// the query's elements and the staged V rows use the same order.
 __device__ __forceinline__ uint4 i4x8_f16_il(uint32_t w) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  auto pair = [](uint32_t x) {
+  auto low = [](uint32_t x) {
     const uint32_t b = (x & 0x000F000Fu) ^ 0x64086408u;
-    const h2 v = __builtin_bit_cast(h2, b) - h2{(_Float16)1032.0f, (_Float16)1032.0f};
-    return __builtin_bit_cast(uint32_t, v);
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, b) - h2{(_Float16)1032.0f, (_Float16)1032.0f});
   };
-  return make_uint4(pair(w), pair(w >> 4), pair(w >> 8), pair(w >> 12));
+  auto high = [](uint32_t x) {
+    const uint32_t b = (x & 0x00F000F0u) ^ 0x64806480u;
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(h2, b),
+                                                                  h2{(_Float16)0.0625f, (_Float16)0.0625f},
+                                                                  h2{(_Float16)-72.0f, (_Float16)-72.0f}));
+  };
+  const uint32_t w8 = w >> 8;
+  return make_uint4(low(w), high(w), low(w8), high(w8));
 }
 
 // (q0..q7) -> (q0, q4, q1, q5, q2, q6, q3, q7): 16-bit elements of a uint4
@@ -221,11 +228,12 @@ struct WaveCfg {
   static constexpr int LANES_PER_ROW = ROW_BYTES / 16;
   static constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
   static constexpr int VCH = kBS / ROWS_PER_PASS;      // 16-byte V loads per lane per block
-  static constexpr int KCS = GRP ? D / 16 : 1;         // 16-byte channel-scale loads per lane (a quarter row)
-  static constexpr int STAGE_VGPRS = 4 * (KCH + VCH) + (GRP ? 4 * KCS + 4 : 0);
-  static constexpr int DEPTH = GRP ? 2 : (STAGE_VGPRS >= 32 ? 4 : 8);   // ring of register tiles
+  // grouped: per lane two channel scales, 4 token scales and the tile's largest
+  static constexpr int STAGE_VGPRS = 4 * (KCH + VCH) + (GRP ? 7 : 0);
+  static constexpr int DEPTH = GRP ? (STAGE_VGPRS >= 20 ? 4 : 8) : (STAGE_VGPRS >= 32 ? 4 : 8);   // ring of register tiles
   static constexpr int VROW = D * 2 + 16;              // LDS bytes per staged V row (16-bit, padded)
-  static constexpr int VSTAGE = kBS * VROW;            // one staged V block
+  // one staged V block, then (grouped) the D / 2 f16 pairs of channel factors
+  static constexpr int VSTAGE = kBS * VROW + (GRP ? 2 * D : 0);
 };
 
 // d-offset (elements) of the 8-element k-chunk that lane group `kg` feeds to
@@ -634,7 +642,7 @@ void paged_attn_wave_kernel(AttnParams p) {
     uint4 k[KCH];
     uint4 v[VCH];
     float ks, vs;
-    floatx4 kcs[C::KCS];   // grouped: channel scales of this lane's quarter row
+    float kc[2];           // grouped: the two channel scales of this lane's factor pair
     floatx4 vts;           // grouped: token scales of rows 4 kg .. 4 kg + 3
     int t0;   // first token of the block
   };
@@ -660,6 +668,20 @@ void paged_attn_wave_kernel(AttnParams p) {
       GRP ? make_rsrc(p.v_scales + kvh * kBS, p.num_blocks > 0 ? (p.num_blocks * p.num_kv_heads - kvh) * kBS * 4 : 0)
           : make_rsrc(p.v_scales + kvh, sbytes);
   const uint8_t* kchan_head = reinterpret_cast<const uint8_t*>(p.k_chan + (size_t)kvh * D);
+  // grouped: lane l < D / 2 turns two channel scales (bytes kc_off and
+  // kc_off + kc_step of the tile's row) into f16 factor pair l.  A lane group's pairs (D / 8 of them, from pair D / 8 * kg)
+  // are the factors of its quarter row in the order the key operand uses:
+  // channels (2m, 2m + 1) of the quarter, or, with INT4's interleaved
+  // elements, (8c + i, 8c + i + 4) for pair m = 4c + i.
+  int kc_off = kOutOfRange, kc_step = 4;
+  if constexpr (GRP) {
+    if (lane < D / 2) {
+      const int quarter = lane / (D / 8), m = lane % (D / 8);
+      const int ch = kIL ? quarter * (D / 4) + 8 * (m / 4) + (m % 4) : 2 * lane;
+      kc_off = 4 * ch;
+      kc_step = kIL ? 16 : 4;
+    }
+  }
   int v_off[VCH], v_row[VCH];
 #pragma unroll
   for (int ps = 0; ps < VCH; ++ps) {
@@ -667,6 +689,11 @@ void paged_attn_wave_kernel(AttnParams p) {
     v_off[ps] = v_row[ps] * row_stride + (lane % C::LANES_PER_ROW) * 16;
   }
   const int tile_bytes = p.num_blocks > 0 ? (kBS - 1) * row_stride + C::ROW_BYTES : 0;
+  // Rows shorter than a 128-byte line (INT4 at head_dim 128, 8-bit codes at
+  // 64) put two KV heads in each line, read by two waves of the workgroup:
+  // they keep the default policy (a non-temporal line may be gone before
+  // the second read)
+  constexpr int kPol = (STREAM && C::ROW_BYTES % 128 == 0) ? kPolicyStream : 0;
 
   // e: list entry of the block, ent: its (physical, logical) block
   auto load_tile = [&](Tile& t, const int2& ent, const int4& e) {
@@ -684,7 +711,7 @@ void paged_attn_wave_kernel(AttnParams p) {
     // K rows that are not kept load as they are: their scores are masked
 #pragma unroll
     for (int c = 0; c < KCH; ++c)
-      t.k[c] = buf_load16<STREAM ? kPolicyStream : 0>(kr, k_off + (kCodes ? 16 : 64) * c);
+      t.k[c] = buf_load16<kPol>(kr, k_off + (kCodes ? 16 : 64) * c);
     // V rows that are not kept read as zeros (a zero weight times a NaN row
     // would still poison the product)
     int vo[VCH];
@@ -696,13 +723,12 @@ void paged_attn_wave_kernel(AttnParams p) {
         if (!kept(t0 + v_row[ps], L, p.sink, p.window)) vo[ps] = kOutOfRange;
     }
 #pragma unroll
-    for (int ps = 0; ps < VCH; ++ps) t.v[ps] = buf_load16<STREAM ? kPolicyStream : 0>(vr, vo[ps]);
+    for (int ps = 0; ps < VCH; ++ps) t.v[ps] = buf_load16<kPol>(vr, vo[ps]);
     if constexpr (GRP) {
       t.ks = buf_load4(ks_r, 0, (int)so);
       const __amdgpu_buffer_rsrc_t cr = make_rsrc(kchan_head + (uint64_t)so * D, valid ? D * 4 : 0);
-#pragma unroll
-      for (int j = 0; j < C::KCS; ++j)
-        t.kcs[j] = __builtin_bit_cast(floatx4, buf_load16(cr, (D / 4) * 4 * kg + 16 * j));
+      t.kc[0] = buf_load4(cr, kc_off);
+      t.kc[1] = buf_load4(cr, kc_off + kc_step);
       t.vts = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(vs_r, 16 * kg, (int)so * kBS, 0));
     } else if constexpr (kCodes) {
       t.ks = buf_load4(ks_r, 0, (int)so);
@@ -865,6 +891,11 @@ void paged_attn_wave_kernel(AttnParams p) {
     }
     const int t0 = t.t0, L = e.z;
 
+    if constexpr (GRP) {
+      const float r = t.ks > 0.f ? __builtin_amdgcn_rcpf(t.ks) : 0.f;
+      if (lane < D / 2)
+        *reinterpret_cast<uint32_t*>(vst + kBS * C::VROW + 4 * lane) = M::pack2(t.kc[0] * r, t.kc[1] * r);
+    }
     // ---- V rows -> LDS (masked rows arrive as zeros) -----------------------
 #pragma unroll
     for (int ps = 0; ps < VCH; ++ps) {
@@ -888,22 +919,17 @@ void paged_attn_wave_kernel(AttnParams p) {
     // ---- S^T = K Q^T --------------------------------------------------------
     floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
     // grouped: channel factors s_d / s_tile in (0, 1] as f16 pairs (the tile
-    // scale goes into the score factor): 8 channels of k-chunk c per uint4
+    // scale goes into the score factor), written to LDS before the V rows and
+    // read back after them: 8 channels of k-chunk c per 4 pairs
     uint32_t kf[GRP ? 4 * NC : 1];
     if constexpr (GRP) {
-      const float r = t.ks > 0.f ? __builtin_amdgcn_rcpf(t.ks) : 0.f;
-      if constexpr (kIL) {
-        // chunk c: channels 8c..8c+7 in loads 2c, 2c + 1, paired (i, i + 4)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int c = 0; c < C::KCS / 2; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) kf[4 * c + i] = M::pack2(t.kcs[2 * c][i] * r, t.kcs[2 * c + 1][i] * r);
-      } else {
-#pragma unroll
-        for (int j = 0; j < C::KCS; ++j) {
-          kf[2 * j] = M::pack2(t.kcs[j][0] * r, t.kcs[j][1] * r);
-          kf[2 * j + 1] = M::pack2(t.kcs[j][2] * r, t.kcs[j][3] * r);
-        }
+      for (int m = 0; m < 4 * NC; m += 4) {
+        const uint4 f = *reinterpret_cast<const uint4*>(vst + kBS * C::VROW + 4 * ((D / 8) * kg + m));
+        kf[m] = f.x, kf[m + 1] = f.y, kf[m + 2] = f.z, kf[m + 3] = f.w;
       }
     }
     auto kscale = [&](uint4 k8, int c) {
@@ -1709,11 +1735,11 @@ static int launch_wave(const AttnParams& p, int num_slots, hipStream_t st) {
   // (workgroup slot, group of up to 8 KV heads); one wave per KV head
   const int per_group = wave_group_size(p.num_kv_heads);
   const int groups = (p.num_kv_heads + per_group - 1) / per_group;
-  const int lds = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, per_group, p.list_cap);
+  const int lds = wave_group_lds(WaveCfg<KVT, D, GRP>::VSTAGE, per_group, p.list_cap);
   auto kernel = paged_attn_wave_kernel<QT, KVT, D, STREAM, SEL, GRP>;
   // above the default dynamic-LDS limit: the largest group needs ~105 KB
   static std::atomic<bool> lds_set[64];
-  const int most = wave_group_lds(WaveCfg<KVT, D>::VSTAGE, kMaxWavesPerGroup, 128 * kMaxWavesPerGroup);
+  const int most = wave_group_lds(WaveCfg<KVT, D, GRP>::VSTAGE, kMaxWavesPerGroup, 128 * kMaxWavesPerGroup);
   const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kernel), most, lds_set);
   if (e != hipSuccess) return e;
   kernel<<<dim3(num_slots, groups), 64 * per_group, lds, st>>>(p);
