@@ -23,7 +23,7 @@
 //    B-operand layout and V^T is read from an LDS copy of the block with the
 //    transposing ds_read_b64_tr_b16.  Blocks are loaded with buffer loads
 //    into a ring of DEPTH register tiles, so DEPTH-1 blocks are in flight
-//    while one computes.  Rows outside the kept range and tiles past the end
+//    per wave while one computes.  Rows outside the kept range and tiles past the end
 //    are given an out-of-range buffer offset: the hardware returns zeros for
 //    them without touching memory, which both masks poisoned slots (no
 //    0 * NaN in the MFMA) and keeps the ring branch-free.
@@ -228,9 +228,12 @@ struct WaveCfg {
   static constexpr int LANES_PER_ROW = ROW_BYTES / 16;
   static constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
   static constexpr int VCH = kBS / ROWS_PER_PASS;      // 16-byte V loads per lane per block
-  // grouped: per lane two channel scales, 4 token scales and the tile's largest
-  static constexpr int STAGE_VGPRS = 4 * (KCH + VCH) + (GRP ? 7 : 0);
-  static constexpr int DEPTH = GRP ? (STAGE_VGPRS >= 20 ? 4 : 8) : (STAGE_VGPRS >= 32 ? 4 : 8);   // ring of register tiles
+  // Ring of register tiles: one block in flight per wave while one computes,
+  // eight waves per compute unit.  Deeper rings (3, 4, 6, 8) measured slower
+  // for every cache type on the Llama-3-8B and 32K shapes and no faster at
+  // 128K: a launch's first burst of loads, DEPTH blocks from every wave at
+  // once, queues in front of the blocks the waves need first.
+  static constexpr int DEPTH = 2;
   static constexpr int VROW = D * 2 + 16;              // LDS bytes per staged V row (16-bit, padded)
   // one staged V block, then (grouped) the D / 2 f16 pairs of channel factors
   static constexpr int VSTAGE = kBS * VROW + (GRP ? 2 * D : 0);
@@ -669,10 +672,11 @@ void paged_attn_wave_kernel(AttnParams p) {
           : make_rsrc(p.v_scales + kvh, sbytes);
   const uint8_t* kchan_head = reinterpret_cast<const uint8_t*>(p.k_chan + (size_t)kvh * D);
   // grouped: lane l < D / 2 turns two channel scales (bytes kc_off and
-  // kc_off + kc_step of the tile's row) into f16 factor pair l.  A lane group's pairs (D / 8 of them, from pair D / 8 * kg)
-  // are the factors of its quarter row in the order the key operand uses:
-  // channels (2m, 2m + 1) of the quarter, or, with INT4's interleaved
-  // elements, (8c + i, 8c + i + 4) for pair m = 4c + i.
+  // kc_off + kc_step of the tile's row) into f16 factor pair l.  A lane
+  // group's pairs (D / 8 of them, from pair D / 8 * kg) are the factors of
+  // its quarter row in the order the key operand uses: channels (2m, 2m + 1)
+  // of the quarter, or, with INT4's interleaved elements, (8c + i, 8c + i + 4)
+  // for pair m = 4c + i.
   int kc_off = kOutOfRange, kc_step = 4;
   if constexpr (GRP) {
     if (lane < D / 2) {
