@@ -521,7 +521,7 @@ void paged_attn_wave_kernel(AttnParams p) {
       if (threadIdx.x >= 64 * kPrefixWaves) return;   // the barriers count the waves still running
       const int stride = p.pfx_wgs * (int)gridDim.y;
       for (int item = (int)blockIdx.x - first + p.pfx_wgs * (int)blockIdx.y; item < p.pfx.items; item += stride)
-        prefix_item<QT, D, 3>(p.pfx, item);   // a shorter ring: the decode's register budget
+        prefix_item<QT, D, 2>(p.pfx, item);   // a shorter ring: the decode's register budget
       return;
     }
   }
@@ -1242,6 +1242,25 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
   const int G = num_q_heads / num_kv_heads;
   const int NCOL = G * qtok;
   const int ncols = min(cpw, NCOL - col0);
+  // thread (output o, part): records part, part + parts, ..., combined in one
+  // pass with a running max (one round of loads after the plan entry); the
+  // parts then meet in LDS
+  const int outs = cpw * V4;          // <= 256 (cpw <= 256 / V4, checked on the host)
+  const int parts = 256 / outs;
+  const int o = tid % outs, part = tid / outs;
+  const int c = o / V4, d4 = o % V4;
+  const bool act = part < parts && c < ncols;
+  const int col = col0 + c;
+  // the prefix record of column c (a shared prefix goes with one query
+  // token), loaded with the plan entry rather than after the records
+  float pm = -INFINITY, pl = 0.f;
+  floatx4 pa = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (prefix && part == 0 && act) {
+    const float* pre = prefix + ((size_t)s * num_q_heads + kvh * G + col) * (D + 4);
+    pm = pre[D];
+    pl = pre[D + 1];
+    pa = *reinterpret_cast<const floatx4*>(pre + 4 * d4);
+  }
   // (slot of the first record, first workgroup, last workgroup)
   const int4 e = reinterpret_cast<const int4*>(plan)[s];
   const bool cut = e.z > e.y;
@@ -1255,18 +1274,7 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
     const int slot = i == 0 ? e.x : 2 * (e.y + i);
     return ws + ((size_t)slot * num_kv_heads + kvh) * rec_floats;
   };
-  // the prefix record of column c (a shared prefix goes with one query token)
-  auto pre_of = [&](int c) { return prefix + ((size_t)s * num_q_heads + kvh * G + c) * (D + 4); };
 
-  // thread (output o, part): records part, part + parts, ..., combined in one
-  // pass with a running max (one round of loads after the plan entry); the
-  // parts then meet in LDS
-  const int outs = cpw * V4;          // <= 256 (cpw <= 256 / V4, checked on the host)
-  const int parts = 256 / outs;
-  const int o = tid % outs, part = tid / outs;
-  const int c = o / V4, d4 = o % V4;
-  const bool act = part < parts && c < ncols;
-  const int col = col0 + c;
   floatx4 num = floatx4{0.f, 0.f, 0.f, 0.f};
   float den = 0.f, mrun = -INFINITY;
   // folds a term (m, l, acc) into (mrun, den, num); a term with m = -inf
@@ -1310,10 +1318,7 @@ __global__ __launch_bounds__(256) void paged_attn_merge_kernel(void* out, const 
     }
   }
   if (part == 0 && act) {
-    if (prefix) {
-      const float* pre = pre_of(col);
-      fold(pre[D], pre[D + 1], *reinterpret_cast<const floatx4*>(pre + 4 * d4));
-    }
+    if (prefix) fold(pm, pl, pa);
     const int t = col / G, h = kvh * G + col % G;
     const size_t oi = (((size_t)s * qtok + t) * num_q_heads + h) * D + 4 * d4;
 #pragma unroll
@@ -1634,7 +1639,7 @@ __device__ __forceinline__ void prefix_item(const PrefixParams& p, int item) {
 
 template <typename QT, int D>
 __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_attn_kernel(PrefixParams p) {
-  prefix_item<QT, D, 4>(p, blockIdx.x);
+  prefix_item<QT, D, 2>(p, blockIdx.x);
 }
 
 template <typename QT, int D>

@@ -78,7 +78,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   constexpr int PIECES = 2 * TILE / 1024;  // 1 KB pieces (one wave-wide load each) of a block
   static_assert(PIECES % NW == 0, "every wave loads the same number of pieces");
   constexpr int LPW = PIECES / NW;         // loads per wave per block
-  constexpr int RPP = 1024 / ROWB;         // rows per piece
   constexpr float kSlack = 8.0f;           // rescale only when a score passes the max by 2^8
   constexpr int RS = D + 4;                // floats per staged output row
 
