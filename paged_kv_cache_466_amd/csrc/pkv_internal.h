@@ -125,11 +125,12 @@ int device_cu_count();
 // reaches (four int32), written by the decode for the merge; the records
 // follow.
 inline size_t plan_area_bytes(int num_seqs) { return ((size_t)num_seqs * 16 + 255) & ~(size_t)255; }
-// Fewest partitions a workgroup takes: enough for 128 tokens (8 blocks), so
+// Fewest partitions a workgroup takes: enough for 80 tokens (5 blocks), so
 // that its fixed costs stay small next to its stream, while small batches
-// still spread over many compute units.
+// still spread over many compute units (a 4 + 4092 StreamingLLM window over
+// four sequences keeps 207 workgroups busy, against 129 at 8 blocks).
 inline int min_units_per_wave(int partition_size) {
-  const int m = 128 / partition_size;
+  const int m = 80 / partition_size;
   return m < 1 ? 1 : m;
 }
 // Bytes of workspace the split decode needs for a cache of kv_dtype: fp32

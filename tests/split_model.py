@@ -29,7 +29,7 @@ def plan(lens, psize, K, list_cap):
     last workgroup of each sequence, by the kernel's rules (full attention).
     A unit is a partition of ``psize`` tokens holding at least one token."""
     bpp = psize // 16
-    min_units = max(1, 128 // psize)
+    min_units = max(1, 80 // psize)
     weighted = bpp > 1 and 3 * bpp <= list_cap
     step = bpp if weighted else 1
     seqs, P = [], 0
