@@ -647,11 +647,11 @@ def measure_grouped(w, steps, warmup, copies):
 def roofline(m):
     # algorithmic HBM bytes: a block shared by several sequences is read from
     # HBM once per step (equal to the KV bytes when nothing is shared).  The
-    # shared-prefix decode is one call of three kernels, timed together.
+    # shared-prefix decode is one call of two kernels, timed together.
     achieved = m["kv_bytes_unique"] / (m["part_ms"] * 1e-3) / 1e9
     kernel = "paged_attn_wave_kernel" if m["w"].kv_dtype != "f32" else "paged_attn_simple_kernel"
     if m.get("cascade"):
-        kernel = "prefix_attn_kernel + paged_attn_wave_kernel + paged_attn_merge_kernel (one call)"
+        kernel = "paged_attn_wave_kernel (decode + prefix items) + paged_attn_merge_kernel (one call)"
     return {
         "bound": "hbm",
         "kernel": kernel,
