@@ -427,9 +427,15 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
       const int Q = max(p.min_units, (U + K - 1) / K);
       k_eff = (U + Q - 1) / Q;
     }
+    // floor(a * b / c) for a * b <= K * U: in 32 bits when that fits (every
+    // shape but the largest; a 64-bit division is several times longer)
+    const bool narrow = (unsigned long long)K * (unsigned)U < (1ull << 32);
+    auto muldiv = [&](int a, int b, int c) {
+      return narrow ? (int)((unsigned)a * (unsigned)b / (unsigned)c) : (int)((long long)a * b / c);
+    };
     if (w < k_eff) {
-      const int u0 = (int)((long long)w * U / k_eff);
-      const int u1 = (int)((long long)(w + 1) * U / k_eff);
+      const int u0 = muldiv(w, U, k_eff);
+      const int u1 = muldiv(w + 1, U, k_eff);
       if (S > 64) {
         win = load_window<SEL>(p, 0, 0, lane, weighted);
         while (win.base + win.total <= u0 && win.s0 + 64 < S)
@@ -447,8 +453,9 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
         const int L = __builtin_amdgcn_readlane(win.L, l);
         if (P >= u1) break;
         // the units starting in [u0, u1): unit i starts at P + i step
-        const int i0 = min(n, u0 > P ? (u0 - P + step - 1) / step : 0);
-        const int i1 = min(n, (u1 - P + step - 1) / step);
+        // (one-block units, step 1, skip the divisions)
+        const int i0 = min(n, u0 > P ? (step == 1 ? u0 - P : (u0 - P + step - 1) / step) : 0);
+        const int i1 = min(n, step == 1 ? u1 - P : (u1 - P + step - 1) / step);
         if (i0 < i1) {
           SegBlocks sb;
           if constexpr (SEL) {
@@ -486,7 +493,8 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
           }
           if (i0 == 0 && p.plan && blockIdx.y == 0 && lane == 0) {
             // the workgroup whose run holds the start of the last unit
-            const int w_last = (int)(((long long)(P + (n - 1) * step + 1) * k_eff - 1) / U);
+            const int w_last = narrow ? (int)(((unsigned)(P + (n - 1) * step + 1) * (unsigned)k_eff - 1u) / (unsigned)U)
+                                      : (int)(((long long)(P + (n - 1) * step + 1) * k_eff - 1) / U);
             // w: 1 when a whole sequence left its record in srec
             reinterpret_cast<int4*>(p.plan)[s] = make_int4(2 * w + upper, w, w_last, p.srec && w_last == w ? 1 : 0);
           }
