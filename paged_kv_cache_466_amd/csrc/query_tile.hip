@@ -67,8 +67,12 @@ struct ChunkParams {
   float scale_log2;
 };
 
+// Three waves per SIMD for the 4-wave workgroups (160 VGPRs at head_dim 128).
+// The 2-wave ones need a few registers more and run at two; a 1-wave
+// workgroup's LDS ring leaves room for at most one wave per SIMD.
 template <typename QT, int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void chunk_attn_kernel(ChunkParams p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 3 : NW))) void chunk_attn_kernel(
+    ChunkParams p) {
   typedef Mfma<QT> M;
   constexpr int NC = D / 32, NN = D / 16;
   constexpr int ROWB = 2 * D;              // bytes of one token row of one head
