@@ -1047,12 +1047,18 @@ void paged_attn_wave_kernel(AttnParams p) {
   {
     Tile ring[DEPTH];
     int2 tab_ent[DEPTH];
+    // entries k and k + DEPTH of slot d's next iteration: each list entry is
+    // read from LDS once, for its table load, and carried to its tile load and
+    // its processing
+    int4 c0[DEPTH], c1[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) c0[d] = entry_at(d), c1[d] = entry_at(DEPTH + d);
     {
       int2 first[DEPTH];
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) first[d] = load_table(entry_at(d).x);
+      for (int d = 0; d < DEPTH; ++d) first[d] = load_table(c0[d].x);
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) tab_ent[d] = load_table(entry_at(DEPTH + d).x);
+      for (int d = 0; d < DEPTH; ++d) tab_ent[d] = load_table(c1[d].x);
       // The queries' loads overlap the table entries' (no wait comes between
       // them).  Branch-free, so that the waits stay counted: pieces past the
       // end load sequence 0's query and land in unused LDS.
@@ -1076,14 +1082,16 @@ void paged_attn_wave_kernel(AttnParams p) {
 #pragma unroll
       for (int r = 0; r < kQRegs; ++r) *reinterpret_cast<u32x4*>(qlds + (r * 64 + lane) * 16) = qv[r];
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], first[d], entry_at(d));
+      for (int d = 0; d < DEPTH; ++d) load_tile(ring[d], first[d], c0[d]);
     }
     __builtin_amdgcn_sched_barrier(0);
     for (int k0 = 0; k0 < nb; k0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
         const int k = k0 + d;
-        const int4 e0 = entry_at(k), e1 = entry_at(k + DEPTH), e2 = entry_at(k + 2 * DEPTH);
+        const int4 e0 = c0[d], e1 = c1[d], e2 = entry_at(k + 2 * DEPTH);
+        c0[d] = e1;
+        c1[d] = e2;
         if (k < nb) process(ring[d], e0, vstage);
         __builtin_amdgcn_sched_barrier(0);
         load_tile(ring[d], tab_ent[d], e1);
