@@ -50,7 +50,7 @@ constexpr int kBS = 16;                     // tokens per block
 constexpr float kLog2e = 1.4426950408889634f;
 
 constexpr int kPrefixWaves = 4;                // waves of a prefix item
-constexpr int kPrefixCG = 2;                  // 16-row column groups per wave
+constexpr int kPrefixCG = 3;                  // 16-row column groups per wave
 constexpr int kPrefixRows = 16 * kPrefixCG;   // rows of a workgroup (every wave takes all of them)
 constexpr int kPrefixTable = 2048;            // shared-block entries staged in LDS at a time
 
@@ -68,7 +68,7 @@ struct PrefixParams {
   float* rec;             // [S][Hq][D + 4]
   int num_prefix_blocks, num_seqs, num_q_heads, num_kv_heads, num_blocks;
   float scale_log2;
-  int items;              // (32-row tile, KV head) items: row tiles x num_kv_heads
+  int items;              // (row tile, KV head) items: row tiles x num_kv_heads
 };
 
 struct AttnParams {
@@ -1435,22 +1435,23 @@ __global__ __launch_bounds__(256) void paged_attn_merge_units_kernel(void* out, 
 // t13_4), the scores of the batch's S*G query rows of one KV head against
 // those blocks are one dense product, Q [S*G, D] x K^T [D, 16 P], followed
 // by P.V over the same blocks.  This pass reads each shared block once per
-// 32 rows instead of once per sequence.  A workgroup of four waves takes 32
+// 48 rows instead of once per sequence.  A workgroup of four waves takes 48
 // rows of one KV head (row r is sequence r / G, head r % G of the group) and
-// each wave a quarter of the blocks.  Workgroup n takes KV head n % Hkv:
+// each wave a quarter of the blocks (48 rows do the pass in about a quarter
+// fewer CU-microseconds than 32: an item's time is mostly per block).  Workgroup n takes KV head n % Hkv:
 // consecutive workgroups go to the eight XCDs in turn, so with Hkv dividing
 // or a multiple of 8 every XCD serves whole heads and one head's shared
-// blocks stay in one XCD's L2 for all of its row tiles.  Per block a wave computes S^T = K Q^T
-// for both of its 16-row column groups from one K tile in registers
-// (v_mfma_f32_16x16x32), and out^T += V^T P^T for both from one transposed
-// read of the V tile (v_mfma_f32_16x16x16).  The four waves' online-softmax
+// blocks stay in one XCD's L2 for all of its row tiles.  Per block a wave
+// computes S^T = K Q^T for each of its three 16-row column groups from one K
+// tile in registers (v_mfma_f32_16x16x32), and out^T += V^T P^T for all
+// three from one transposed read of the V tile (v_mfma_f32_16x16x16).  The four waves' online-softmax
 // states are combined in LDS by log-sum-exp into one record per (sequence,
 // query head): acc[D] (unnormalised), m (log2 domain), l.  The suffix decode
 // folds these records into its own results.
 // ===========================================================================
 
 
-// One item: 32 rows of one KV head against every shared block, on the
+// One item: 48 rows of one KV head against every shared block, on the
 // first four waves of the workgroup, DEPTH block tiles in flight per wave.
 template <typename QT, int D, int DEPTH>
 __device__ __forceinline__ void prefix_item(const PrefixParams& p, int item) {
@@ -1622,11 +1623,12 @@ __device__ __forceinline__ void prefix_item(const PrefixParams& p, int item) {
     }
   }
   __syncthreads();
-  // thread -> (row rr, eighth ch of its D elements); a wave that took no
-  // block has m = -inf and weighs nothing
-  const int rr = threadIdx.x >> 3, ch = threadIdx.x & 7;
-  const int r = r0 + rr;
-  if (r < nrows) {
+  // thread -> (row rr, eighth ch of its D elements), 32 rows per pass; a
+  // wave that took no block has m = -inf and weighs nothing
+  const int ch = threadIdx.x & 7;
+  for (int rr = threadIdx.x >> 3; rr < kPrefixRows; rr += 64 * kPrefixWaves / 8) {
+    const int r = r0 + rr;
+    if (r >= nrows) break;
     float mw[kPrefixWaves], mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kPrefixWaves; ++w) {
