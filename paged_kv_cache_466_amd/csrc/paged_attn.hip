@@ -373,8 +373,10 @@ __host__ __device__ constexpr int wave_group_lds(int vstage, int waves, int list
 }
 
 // Writes the workgroup's block list into LDS (one wave calls it).  Entry k:
-// (byte offset of the block's table entry - of its selection entry for a
-// selected decode -, first token of the block with bit 31 set when some
+// (the block's physical number, gathered from the table in one round of
+// loads once the list is written - for a selected decode the byte offset of
+// its selection entry, which differs per KV head -, first token of the block
+// with bit 31 set when some
 // token of the block is masked for some query, length of its sequence,
 // segment key); the key packs the sequence (bits 8+), the
 // segment's number in the workgroup (bits 2-7, saturating), whether its
@@ -505,6 +507,22 @@ __device__ __forceinline__ void build_block_list(const AttnParams& p, int head_d
       }
     }
   }
+  if constexpr (!SEL) {
+    // the table entries of the whole list in one round of loads: entry .x
+    // becomes the physical block (the same for every KV head)
+    const __amdgpu_buffer_rsrc_t tabr = make_rsrc(p.block_tables, p.table_bytes);
+    for (int j0 = lane; j0 < nb; j0 += 4 * 64) {
+      int pbv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + 64 * q;
+        pbv[q] = (int)__builtin_amdgcn_raw_buffer_load_b32(tabr, j < nb ? list[j].x : kOutOfRange, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j0 + 64 * q < nb) list[j0 + 64 * q].x = pbv[q];
+    }
+  }
   if (lane == 0) {
     list[nb] = make_int4(kOutOfRange, 0, 0, kEndKey);
     counts[0] = nb;
@@ -627,8 +645,9 @@ void paged_attn_wave_kernel(AttnParams p) {
     return make_int4(__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
                      __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w));
   };
-  // (physical block, logical block) of a list entry: the table entry, or
-  // this head's selection entry for a selected decode
+  // (physical block, logical block) of a list entry: the physical block the
+  // list already holds, or this head's selection entry for a selected decode
+  // (per head, so loaded here)
   const __amdgpu_buffer_rsrc_t tab = make_rsrc(SEL ? (const void*)p.selected : (const void*)p.block_tables,
                                                p.table_bytes);
   const int sel_head = kvh * p.budget * 8;
@@ -638,7 +657,7 @@ void paged_attn_wave_kernel(AttnParams p) {
       const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(tab, off + sel_head, 0, 0));
       return make_int2((int)v[0], (int)v[1]);
     } else {
-      return make_int2((int)__builtin_amdgcn_raw_buffer_load_b32(tab, off, 0, 0), 0);
+      return make_int2(off, 0);   // the list entry holds the physical block
     }
   };
   // first token of an entry's block, and whether some token of it is
@@ -1040,9 +1059,9 @@ void paged_attn_wave_kernel(AttnParams p) {
   };
 
   // ---- main loop: a ring of DEPTH tiles; block k + DEPTH is requested as
-  // soon as block k's registers are free, with its table entry fetched
-  // DEPTH steps earlier, so that by the time a tile load needs an entry it
-  // is older than every load still in flight and no wait stalls the ring.
+  // soon as block k's registers are free.  A selected decode fetches each
+  // selection entry DEPTH steps before its tile load, so that the entry is
+  // older than every load still in flight and no wait stalls the ring.
   // Loads past the end of the list read nothing.
   {
     Tile ring[DEPTH];
