@@ -1067,8 +1067,8 @@ void paged_attn_wave_kernel(AttnParams p) {
     Tile ring[DEPTH];
     int2 tab_ent[DEPTH];
     // entries k and k + DEPTH of slot d's next iteration: each list entry is
-    // read from LDS once, for its table load, and carried to its tile load and
-    // its processing
+    // read from LDS once, 2 DEPTH blocks ahead (where a selected decode loads
+    // its selection entry), and carried to its tile load and its processing
     int4 c0[DEPTH], c1[DEPTH];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) c0[d] = entry_at(d), c1[d] = entry_at(DEPTH + d);
@@ -1078,9 +1078,10 @@ void paged_attn_wave_kernel(AttnParams p) {
       for (int d = 0; d < DEPTH; ++d) first[d] = load_table(c0[d].x);
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) tab_ent[d] = load_table(c1[d].x);
-      // The queries' loads overlap the table entries' (no wait comes between
-      // them).  Branch-free, so that the waits stay counted: pieces past the
-      // end load sequence 0's query and land in unused LDS.
+      // The queries' loads overlap a selected decode's first selection
+      // entries (no wait comes between them).  Branch-free, so that the
+      // waits stay counted: pieces past the end load sequence 0's query and
+      // land in unused LDS.
       // c / q_chunks as (c * inv) >> 16: exact for c < 6 * 64 and every
       // q_chunks = NCOL * D / 8 built (checked exhaustively on the host)
       const int inv = 0x10000 / q_chunks + 1;
