@@ -299,12 +299,19 @@ pkv_status pkv_quest_summarize(const void* k_cache, int kv_dtype, void* k_summar
                                const int32_t* seq_lens, int num_seqs, int num_blocks, int block_size,
                                int num_kv_heads, int head_dim, int last_only, void* stream);
 
-/* Bytes of scratch pkv_quest_select needs (8 per (sequence, KV head, block)). */
+/* Bytes of scratch pkv_quest_select needs (8 per (sequence, KV head, block)).
+ * For tables up to 8704 blocks wide, after a call that did not keep every
+ * page, scratch[s][h][lb] holds two uint32 order keys (larger float, larger
+ * key: the bits of a non-negative value with the top bit set, of a negative
+ * one inverted): a lower and an upper bound of block lb's score, each a
+ * float32.  Wider tables hold the exact scores there instead. */
 size_t pkv_quest_scratch_bytes(int num_seqs, int num_kv_heads, int max_blocks_per_seq);
 
 /*
  * Scores every page of every (sequence, KV head) against the query group
- * (fp64; each product of two 16-bit values is exact) and writes, for each
+ * (fp64; each product of two 16-bit values is exact; for tables up to 8704
+ * blocks wide, bounds from a float32 pass first settle most pages and only
+ * the others are scored in fp64, with the same result) and writes, for each
  * (s, kvh), the budget_blocks highest-scoring pages in logical order to
  * selected[S][num_kv_heads][budget_blocks][2] as (physical block, logical
  * block) int32 pairs.  Equal scores keep the lower logical block.  A

@@ -241,3 +241,42 @@ def test_long_table_keys_from_global_memory(budget):
     want = quest.select_pages(scores, budget)
     assert sel[0, 0, :, 1].tolist() == want
     assert sel[0, 0, :, 0].tolist() == [int(perm[lb]) for lb in want]
+
+
+def _bound_floats(keys):
+    """Order keys (larger value, larger key) back to float32 values."""
+    k = keys.astype(np.uint32)
+    bits = np.where(k & np.uint32(0x80000000), k & np.uint32(0x7FFFFFFF), ~k)
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["llama_shape", "g8_f16", "d64_mqa", "g16", "g2_long"])
+def test_score_bounds_hold(name):
+    """For tables up to 12288 blocks wide the selection first bounds every
+    page's score on the matrix cores (fp32 sums); scratch then holds, per
+    (sequence, KV head, logical block), the (lower, upper) bound as order
+    keys.  Every exact score (the oracle's, exactly rounded) lies inside
+    its bounds, and the bounds are narrow (a few parts in 10^4 of the
+    score's scale)."""
+    import paged_kv_cache_466_amd as pkv
+    w, t, g, o = run_case(name)
+    summ = pkv.quest_summary_like(g.k_cache)
+    pkv.quest_summarize(g.k_cache, summ, g.block_tables, g.lens)
+    S, mbs = g.block_tables.shape
+    scratch = torch.zeros(pkv.lib.pkv_quest_scratch_bytes(S, w.Hkv, mbs), dtype=torch.uint8, device="cuda")
+    pkv.quest_select(t["query"], summ, g.block_tables, g.lens, 1, scratch=scratch)
+    torch.cuda.synchronize()
+    bounds = scratch[: S * w.Hkv * mbs * 8].view(torch.int32).cpu().numpy().reshape(S, w.Hkv, mbs, 2)
+    q_all = codecs.decode(to_raw(t["query"], w.q_dtype), w.q_dtype)
+    scores = _oracle_scores_from_summaries(w, to_raw(summ, w.kv_dtype), q_all, o.tables, o.lens)
+    widest = 0.0
+    for (s, h), sc in scores.items():
+        n = len(sc)
+        lo = _bound_floats(bounds[s, h, :n, 0])
+        hi = _bound_floats(bounds[s, h, :n, 1])
+        sc = np.asarray(sc)
+        assert np.all(lo <= sc) and np.all(sc <= hi), (s, h, np.flatnonzero((lo > sc) | (sc > hi))[:5])
+        scale = np.abs(sc).max()
+        widest = max(widest, float(np.max(hi - lo)) / scale)
+    print(f"[quest] {name} widest bound / score scale = {widest:.3e}")
+    assert widest < 1e-3
