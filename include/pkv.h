@@ -300,7 +300,7 @@ pkv_status pkv_quest_summarize(const void* k_cache, int kv_dtype, void* k_summar
                                int num_kv_heads, int head_dim, int last_only, void* stream);
 
 /* Bytes of scratch pkv_quest_select needs (8 per (sequence, KV head, block)).
- * For tables up to 8704 blocks wide, after a call that did not keep every
+ * For tables up to 9216 blocks wide, after a call that did not keep every
  * page, scratch[s][h][lb] holds two uint32 order keys (larger float, larger
  * key: the bits of a non-negative value with the top bit set, of a negative
  * one inverted): a lower and an upper bound of block lb's score, each a
@@ -309,7 +309,7 @@ size_t pkv_quest_scratch_bytes(int num_seqs, int num_kv_heads, int max_blocks_pe
 
 /*
  * Scores every page of every (sequence, KV head) against the query group
- * (fp64; each product of two 16-bit values is exact; for tables up to 8704
+ * (fp64; each product of two 16-bit values is exact; for tables up to 9216
  * blocks wide, bounds from a float32 pass first settle most pages and only
  * the others are scored in fp64, with the same result) and writes, for each
  * (s, kvh), the budget_blocks highest-scoring pages in logical order to

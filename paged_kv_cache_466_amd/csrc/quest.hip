@@ -546,8 +546,8 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint64_
 constexpr int kBoundWaves = 4;      // waves per bounding workgroup
 constexpr int kBoundGroups = 2;   // 16-page groups per wave, all loads issued first
 constexpr int kBoundPages = 16 * kBoundGroups * kBoundWaves;   // pages per workgroup
-constexpr int kPickThreads = 512;                             // threads of a picking workgroup (8 waves)
-constexpr int kPickMaxPages = 8704;                           // widest table taken here
+constexpr int kPickMaxPages = 9216;                           // widest table taken here
+constexpr int kPickWide = 4096;   // tables wider than this are picked by 1024 threads, others by 512
 
 // Order-preserving map of a float onto uint32 (larger value, larger key).
 __device__ __forceinline__ uint32_t order_key32(float x) {
@@ -674,20 +674,21 @@ __global__ __launch_bounds__(64 * kBoundWaves) void quest_bound_kernel(const uin
 constexpr int kPairMax = 256;   // open pages ranked pairwise; more take a radix select
 constexpr int kPickBin = 8;     // keys a threshold's bin may keep before the digits stop
 
-// grid (S * Hkv), kPickThreads threads: the budget pages of the largest
-// exact scores from the bounds.  theta, at most the budget-th largest
-// lower bound, and ucut, at least the (budget + 1)-th largest upper bound,
-// are narrowed down together one radix digit at a time (from the highest
-// bit where two bounds differ) until the bin holding each has at most
-// kPickBin keys: theta is the lower edge of its bin, ucut the upper edge of
-// its.  At least budget pages have lower bounds >= theta, so a page whose
-// upper bound is below theta is not among the budget best; at most budget
-// pages have upper bounds > ucut, so a page whose lower bound is above ucut
-// is (at most budget - 1 others can reach its score).  The others ("open"
-// pages) get their exact fp64 score, as the scoring kernel computes it, and
-// the budget - (sure pages) largest of those are kept, equal scores to the
-// lower page; all written in page order.  A query the bounds do not hold
-// for (a denormal element, or for bf16 one above 2^18) opens every page.
+// grid (S * Hkv), kPickThreads threads (512, or 1024 for tables wider than
+// kPickWide): the budget pages of the largest exact scores from the bounds.
+// theta, at most the budget-th largest lower bound, and ucut, at least the
+// (budget + 1)-th largest upper bound, are narrowed down together one radix
+// digit at a time (from the highest bit where two bounds differ) until the
+// bin holding each has at most kPickBin keys: theta is the lower edge of its
+// bin, ucut the upper edge of its.  At least budget pages have lower bounds
+// >= theta, so a page whose upper bound is below theta is not among the
+// budget best; at most budget pages have upper bounds > ucut, so a page
+// whose lower bound is above ucut is (at most budget - 1 others can reach
+// its score).  The others ("open" pages) get their exact fp64 score, as the
+// scoring kernel computes it, and the budget - (sure pages) largest of those
+// are kept, equal scores to the lower page; all written in page order.  A
+// query the bounds do not hold for (a denormal element, or for bf16 one
+// above 2^18) opens every page.
 //
 // Wave w owns pages [w * per, (w + 1) * per), lane l of it pages w * per + l
 // + 64 j for j < per / 64 <= JMAX; the sweeps are unrolled to JMAX with
@@ -696,13 +697,13 @@ constexpr int kPickBin = 8;     // keys a threshold's bin may keep before the di
 // physical blocks and then their exact keys (by rank in page order), then
 // the kept pages in page order (16-bit); [mbs] 16-bit open pages (bit 15
 // set once a page is chosen).
-template <typename T, int D, int GP>
+template <typename T, int D, int GP, int kPickThreads>
 __global__ __launch_bounds__(kPickThreads) __attribute__((amdgpu_waves_per_eu(4))) void quest_pick_kernel(
     const uint16_t* __restrict__ query, const uint16_t* __restrict__ summ, const int32_t* __restrict__ bt, int mbs,
     const int32_t* __restrict__ lens, int num_blocks, int Hq, int Hkv, int budget, const uint2* __restrict__ bounds,
     int32_t* __restrict__ selected) {
   constexpr int W = kPickThreads / 64;
-  constexpr int JMAX = kPickMaxPages / kPickThreads;
+  constexpr int JMAX = (kPickThreads == 512 ? kPickWide : kPickMaxPages) / kPickThreads;
   constexpr bool kBF = std::is_same<T, BF16>::value;
   extern __shared__ uint64_t pk_lds[];
   __shared__ int hist[2][kBins];
@@ -1025,14 +1026,20 @@ int launch_quest_select(const void* query, int q_dtype, const void* k_summary, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)mbs * 10 + 8;
-    static std::atomic<bool> lds_set[2][2][5][64];
-#define PKV_PICK(T, D, G, TI, DI, GI)                                                                           \
+    static std::atomic<bool> lds_set[2][2][5][2][64];
+    const bool wide = mbs > kPickWide;
+#define PKV_PICK_N(T, D, G, TI, DI, GI, NT, NI)                                                                  \
   do {                                                                                                          \
-    e = set_lds_limit_once(reinterpret_cast<const void*>(quest_pick_kernel<T, D, G>), kPickMaxPages * 10 + 8,   \
-                           lds_set[TI][DI][GI]);                                                                \
+    e = set_lds_limit_once(reinterpret_cast<const void*>(quest_pick_kernel<T, D, G, NT>), kPickMaxPages * 10 + 8, \
+                           lds_set[TI][DI][GI][NI]);                                                            \
     if (e != hipSuccess) return e;                                                                              \
-    quest_pick_kernel<T, D, G><<<num_seqs * num_kv_heads, kPickThreads, lds, st>>>(                             \
+    quest_pick_kernel<T, D, G, NT><<<num_seqs * num_kv_heads, NT, lds, st>>>(                                    \
         q, sm, block_tables, mbs, seq_lens, num_blocks, num_q_heads, num_kv_heads, budget, bounds, selected);   \
+  } while (0)
+#define PKV_PICK(T, D, G, TI, DI, GI)                        \
+  do {                                                       \
+    if (wide) PKV_PICK_N(T, D, G, TI, DI, GI, 1024, 1);      \
+    else PKV_PICK_N(T, D, G, TI, DI, GI, 512, 0);            \
   } while (0)
 #define PKV_PICK_G(T, D, TI, DI)                     \
   switch (GP) {                                      \
@@ -1049,6 +1056,7 @@ int launch_quest_select(const void* query, int q_dtype, const void* k_summary, c
     }
 #undef PKV_PICK_G
 #undef PKV_PICK
+#undef PKV_PICK_N
     return hipGetLastError();
   }
   auto keys = reinterpret_cast<uint64_t*>(scratch);

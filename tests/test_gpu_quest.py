@@ -280,3 +280,32 @@ def test_score_bounds_hold(name):
         widest = max(widest, float(np.max(hi - lo)) / scale)
     print(f"[quest] {name} widest bound / score scale = {widest:.3e}")
     assert widest < 1e-3
+
+
+@pytest.mark.parametrize("budget", [1, 100, 2999, 5999])
+def test_wide_table_bounded_path(budget):
+    """A block table 6100 blocks wide (the bounded selection with its wider
+    picking workgroup): one sequence of 6000 pages, two KV heads of four
+    query heads, random stored summaries, against the oracle's ranking."""
+    import paged_kv_cache_466_amd as pkv
+    g = torch.Generator().manual_seed(11)
+    S, Hq, Hkv, D, nbk, mbs = 1, 8, 2, 128, 6000, 6100
+    print(f"[quest] wide table S={S} Hq={Hq} Hkv={Hkv} D={D} pages={nbk} width={mbs} budget={budget}", flush=True)
+    a = torch.randn(nbk, Hkv, D, generator=g).to(torch.bfloat16)
+    b = torch.randn(nbk, Hkv, D, generator=g).to(torch.bfloat16)
+    summ = torch.stack([torch.minimum(a, b), torch.maximum(a, b)], dim=2).contiguous()
+    perm = torch.randperm(nbk, generator=g).to(torch.int32)
+    bt = torch.zeros(S, mbs, dtype=torch.int32)
+    bt[0, :nbk] = perm
+    lens = torch.tensor([nbk * 16 - 3], dtype=torch.int32)
+    q = torch.randn(S, Hq, D, generator=g).to(torch.bfloat16)
+    sel = pkv.quest_select(q.cuda(), summ.cuda(), bt.cuda(), lens.cuda(), budget).cpu().numpy()
+    qf = q.float().numpy().astype(np.float64)
+    sf = summ.float().numpy().astype(np.float64)
+    G = Hq // Hkv
+    for h in range(Hkv):
+        scores = [quest.group_page_score(qf[0, h * G:(h + 1) * G], sf[int(perm[lb]), h, 0], sf[int(perm[lb]), h, 1])
+                  for lb in range(nbk)]
+        want = quest.select_pages(scores, budget)
+        assert sel[0, h, :, 1].tolist() == want, h
+        assert sel[0, h, :, 0].tolist() == [int(perm[lb]) for lb in want], h
