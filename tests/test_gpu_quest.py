@@ -309,3 +309,45 @@ def test_wide_table_bounded_path(budget):
         want = quest.select_pages(scores, budget)
         assert sel[0, h, :, 1].tolist() == want, h
         assert sel[0, h, :, 0].tolist() == [int(perm[lb]) for lb in want], h
+
+
+@pytest.mark.parametrize("case", ["bf16_large_query", "bf16_denormal_query", "f16_denormal_query", "all_equal"])
+@pytest.mark.parametrize("budget", [5, 300])
+def test_every_page_open(case, budget):
+    """Cases where the float bounds settle no page, so that every page is
+    scored exactly and the open pages outnumber the pairwise ranking (600
+    pages): a query element the bounds do not cover (bf16 above 2^18, a
+    denormal bf16 or f16 value), and pages with equal summaries (all tied:
+    the lowest pages are kept).  Against the oracle's ranking."""
+    import paged_kv_cache_466_amd as pkv
+    g = torch.Generator().manual_seed(13)
+    dt = torch.float16 if case.startswith("f16") else torch.bfloat16
+    S, Hq, Hkv, D, nbk, mbs = 1, 4, 1, 64, 600, 640
+    print(f"[quest] every page open: {case} pages={nbk} budget={budget}", flush=True)
+    a = torch.randn(nbk, Hkv, D, generator=g)
+    b = torch.randn(nbk, Hkv, D, generator=g)
+    if case == "all_equal":
+        a[:] = a[0]
+        b[:] = b[0]
+    summ = torch.stack([torch.minimum(a, b), torch.maximum(a, b)], dim=2).to(dt).contiguous()
+    q = torch.randn(S, Hq, D, generator=g)
+    if case == "bf16_large_query":
+        q[0, 1, 3] = 1.0e6
+    elif case == "bf16_denormal_query":
+        q[0, 2, 5] = 3.0e-39
+    elif case == "f16_denormal_query":
+        q[0, 0, 7] = 1.0e-6
+    q = q.to(dt)
+    perm = torch.randperm(nbk, generator=g).to(torch.int32)
+    bt = torch.zeros(S, mbs, dtype=torch.int32)
+    bt[0, :nbk] = perm
+    lens = torch.tensor([nbk * 16 - 7], dtype=torch.int32)
+    sel = pkv.quest_select(q.cuda(), summ.cuda(), bt.cuda(), lens.cuda(), budget).cpu().numpy()
+    qf = q.float().numpy().astype(np.float64)
+    sf = summ.float().numpy().astype(np.float64)
+    scores = [quest.group_page_score(qf[0], sf[int(perm[lb]), 0, 0], sf[int(perm[lb]), 0, 1]) for lb in range(nbk)]
+    want = quest.select_pages(scores, budget)
+    if case == "all_equal":
+        assert want == list(range(budget))
+    assert sel[0, 0, :, 1].tolist() == want
+    assert sel[0, 0, :, 0].tolist() == [int(perm[lb]) for lb in want]
