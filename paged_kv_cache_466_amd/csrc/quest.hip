@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint64_
 // The pages chosen are those of the exact scores (the same as above).
 // ---------------------------------------------------------------------------
 
-constexpr int kBoundWaves = 4;      // waves per bounding workgroup
+constexpr int kBoundWaves = 4;    // waves per bounding workgroup
 constexpr int kBoundGroups = 2;   // 16-page groups per wave, all loads issued first
 constexpr int kBoundPages = 16 * kBoundGroups * kBoundWaves;   // pages per workgroup
 constexpr int kPickMaxPages = 9216;                           // widest table taken here
