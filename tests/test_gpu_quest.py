@@ -282,23 +282,20 @@ def test_score_bounds_hold(name):
     assert widest < 1e-3
 
 
-@pytest.mark.parametrize("budget", [1, 100, 2999, 5999])
-def test_wide_table_bounded_path(budget):
-    """A block table 6100 blocks wide (the bounded selection with its wider
-    picking workgroup): one sequence of 6000 pages, two KV heads of four
-    query heads, random stored summaries, against the oracle's ranking."""
+def _random_table_case(seed, dt, Hq, Hkv, D, nbk, mbs, budget):
+    """One sequence of nbk pages (random stored summaries, a random block
+    order) in a table mbs blocks wide; the selection against the oracle's
+    ranking for every KV head."""
     import paged_kv_cache_466_amd as pkv
-    g = torch.Generator().manual_seed(11)
-    S, Hq, Hkv, D, nbk, mbs = 1, 8, 2, 128, 6000, 6100
-    print(f"[quest] wide table S={S} Hq={Hq} Hkv={Hkv} D={D} pages={nbk} width={mbs} budget={budget}", flush=True)
-    a = torch.randn(nbk, Hkv, D, generator=g).to(torch.bfloat16)
-    b = torch.randn(nbk, Hkv, D, generator=g).to(torch.bfloat16)
-    summ = torch.stack([torch.minimum(a, b), torch.maximum(a, b)], dim=2).contiguous()
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randn(nbk, Hkv, D, generator=g)
+    b = torch.randn(nbk, Hkv, D, generator=g)
+    summ = torch.stack([torch.minimum(a, b), torch.maximum(a, b)], dim=2).to(dt).contiguous()
     perm = torch.randperm(nbk, generator=g).to(torch.int32)
-    bt = torch.zeros(S, mbs, dtype=torch.int32)
+    bt = torch.zeros(1, mbs, dtype=torch.int32)
     bt[0, :nbk] = perm
     lens = torch.tensor([nbk * 16 - 3], dtype=torch.int32)
-    q = torch.randn(S, Hq, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(1, Hq, D, generator=g).to(dt)
     sel = pkv.quest_select(q.cuda(), summ.cuda(), bt.cuda(), lens.cuda(), budget).cpu().numpy()
     qf = q.float().numpy().astype(np.float64)
     sf = summ.float().numpy().astype(np.float64)
@@ -309,6 +306,26 @@ def test_wide_table_bounded_path(budget):
         want = quest.select_pages(scores, budget)
         assert sel[0, h, :, 1].tolist() == want, h
         assert sel[0, h, :, 0].tolist() == [int(perm[lb]) for lb in want], h
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64)])
+@pytest.mark.parametrize("budget", [1, 100, 2999, 5999])
+def test_wide_table_bounded_path(dtype, D, budget):
+    """A block table 6100 blocks wide (the bounded selection with its wider
+    picking workgroup): one sequence of 6000 pages, two KV heads of four
+    query heads, random stored summaries, against the oracle's ranking."""
+    print(f"[quest] wide table {dtype} D={D} pages=6000 width=6100 budget={budget}", flush=True)
+    dt = torch.float16 if dtype == "f16" else torch.bfloat16
+    _random_table_case(11, dt, 8, 2, D, 6000, 6100, budget)
+
+
+@pytest.mark.parametrize("mbs", [4096, 4097, 9216, 9217])
+def test_table_width_boundaries(mbs):
+    """Tables on either side of the widths where the selection changes road:
+    4096 / 4097 blocks (512 or 1024 picking threads), 9216 / 9217 (the
+    bounded road or the exact one).  A sequence of mbs - 10 pages."""
+    print(f"[quest] table width {mbs}", flush=True)
+    _random_table_case(17, torch.bfloat16, 4, 1, 64, mbs - 10, mbs, 97)
 
 
 @pytest.mark.parametrize("case", ["bf16_large_query", "bf16_denormal_query", "f16_denormal_query", "all_equal"])
